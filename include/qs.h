@@ -1,0 +1,261 @@
+/*
+ * qs.h -- C ABI of the Q-Sparse inference hot path for AMD Instinct MI355X
+ * (gfx950).  Library: libqs.so.
+ *
+ * Sources of the operations (cited by page title and section):
+ *   [QS-TopK]   Q-Sparse news article (zxwl-tech.com, July 2024), section
+ *               "Sparsification with the Top-K function": Y = X . W^T for every
+ *               attention/FFN projection; keep the K entries of largest |x|
+ *               (K a preset hyperparameter), mask M with X's shape, X (.) M
+ *               replaces X in the product; squared-ReLU FFN; activations
+ *               quantised before top-K with an epsilon-guarded denominator;
+ *               1-bit (ternary) weights with alpha = mean |W|.
+ *   [QS-Adv]    Q-Sparse aibase report (aibase.com, pt), section on the
+ *               advantages of sparsity: top-K on every linear projection,
+ *               I/O as the main inference bottleneck.
+ *   [TS-Eq2]    Turbo Sparse summary (blog.csdn.net), Eq. 2: dReLU, ReLU
+ *               after both the gate and the up projection.
+ *   [TS-Eq3-4]  Turbo Sparse summary, Eq. 3-4: top-k% of the FFN
+ *               intermediate by absolute value before W_down.
+ *   [TS-Fig]    Turbo Sparse summary, per-layer zero-activation figure
+ *               (about 90% of FFN neurons inactive).
+ *
+ * Readings where the pages are silent (each is part of the contract):
+ *   - top-K is per row (token); among equal |x| the lower index wins, so the
+ *     selected set is unique; every row gets exactly min(K, D) selected
+ *     entries, zero-valued ones included when a row has fewer nonzeros;
+ *   - |x| is ordered through its bit pattern: fp32 key = bits & 0x7FFFFFFF,
+ *     bf16 key = bits & 0x7FFF, int8 key = |q|; +0 and -0 tie; inputs are
+ *     finite (NaN/Inf are outside the contract);
+ *   - activation quantiser: gamma = max|x|, s = 127 / (gamma + 1e-5),
+ *     q = clamp(rint(x * s), -128, 127), IEEE binary32, round-to-nearest-even
+ *     at every step; top-K then runs on |q|;
+ *   - ternary weights: alpha = mean |W| over the whole tensor,
+ *     t = clamp(rint(W / (alpha + 1e-5)), -1, 1);
+ *   - squared ReLU is un-gated: h = relu(u)^2; the FFN intermediate stays
+ *     fp32 between the up and the down projection.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned (allocate them however you like,
+ *     e.g. through torch).  The library allocates no device memory, keeps no
+ *     pointer after the call returns, and may access the buffers until the
+ *     stream reaches the end of the enqueued work.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous and never synchronise the host.
+ *   - Arguments are validated before anything is enqueued; on any error the
+ *     call enqueues nothing, leaves every output untouched and returns a
+ *     nonzero qs_status; qs_last_error() then describes it.  No C++
+ *     exception crosses the ABI.  rows == 0 is a valid no-op.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Results are bitwise deterministic for fixed inputs, shapes and stream
+ *     (no floating-point atomics; every reduction has a fixed order).
+ *   - A workspace (`ws`, `ws_bytes`) is device memory of at least the size
+ *     qs_workspace_bytes() reports for the same op and shape; its contents
+ *     are scratch and need no initialisation (qs_gather_linear excepted, see
+ *     there).  Two calls that may run at the same time must not share a
+ *     workspace.
+ */
+#ifndef QS_H
+#define QS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qs_status {
+    QS_OK = 0,
+    QS_ERR_INVALID_ARG = 1,   /* null pointer, negative size, K outside [0, D], ... */
+    QS_ERR_UNSUPPORTED = 2,   /* valid but not implemented: dtype/layout combo, misalignment */
+    QS_ERR_WORKSPACE = 3,     /* ws NULL or ws_bytes below qs_workspace_bytes() */
+    QS_ERR_HIP = 4            /* a HIP runtime call failed; qs_last_error() has its text */
+} qs_status;
+
+typedef enum qs_dtype {
+    QS_F32 = 0,
+    QS_BF16 = 1,
+    QS_I8 = 2
+} qs_dtype;
+
+typedef enum qs_layout {
+    QS_LAYOUT_WT = 0,   /* feature-major W^T [d_in, n_out], row j = weights of input feature j */
+    QS_LAYOUT_W = 1     /* neuron-major W [n_out, d_in] (nn.Linear layout) */
+} qs_layout;
+
+typedef enum qs_act {
+    QS_ACT_RELU2 = 0,   /* h = relu(u)^2                       [QS-TopK]  */
+    QS_ACT_DRELU = 1    /* h = relu(x W_gate^T + b_g) * relu(x W_up^T + b_u)   [TS-Eq2] */
+} qs_act;
+
+typedef enum qs_op {
+    QS_OP_TOPK_MASK = 0,
+    QS_OP_SPARSE_LINEAR = 1,
+    QS_OP_SPARSE_LINEAR_I8T = 2,
+    QS_OP_SPARSE_FFN_RELU2 = 3,
+    QS_OP_SPARSE_FFN_DRELU = 4,
+    QS_OP_GATHER_LINEAR = 5
+} qs_op;
+
+/*
+ * qs_topk_mask -- per-row top-K by |x| with ties to the lower index  [QS-TopK]
+ *
+ *   x       device, [rows, d] row-major, dtype xt (QS_F32, QS_BF16 or QS_I8).
+ *   k       0 <= k <= d.
+ *   mask    device u8 [rows, d] or NULL: 1 at the selected entries, else 0.
+ *   idx     device i32 [rows, k] or NULL: selected indices, ascending.
+ *   tau     device u32 [rows] or NULL: key of the K-th largest entry
+ *           (0xFFFFFFFF when k == 0).
+ *   cutoff  device i32 [rows] or NULL: one past the index of the last
+ *           selected entry whose key equals tau (0 when k == 0); entry j is
+ *           selected iff key_j > tau or (key_j == tau and j < cutoff).
+ *   xs      device fp32 [rows, d] or NULL: the sparsified activation X (.) M
+ *           (exact conversion of x at the selected entries, +0 elsewhere).
+ *   Limits: d <= 1<<24.
+ */
+qs_status qs_topk_mask(const void* x, qs_dtype xt, int64_t rows, int64_t d, int64_t k,
+                       uint8_t* mask, int32_t* idx, uint32_t* tau, int32_t* cutoff,
+                       float* xs, void* stream);
+
+/*
+ * qs_sparse_linear -- Y = (X (.) M) . W^T with M the per-row top-K mask of X
+ * [QS-TopK], [QS-Adv].
+ *
+ *   x       device [rows, d_in], dtype xt (QS_F32 or QS_BF16).
+ *   k       0 <= k <= d_in.
+ *   w       device weights, dtype wt_t (QS_F32 or QS_BF16), layout w_layout:
+ *           QS_LAYOUT_WT  W^T [d_in, n_out]: the gather path, which reads only
+ *                         the rows of W^T selected by some token of the batch
+ *                         (any rows; meant for decode batches);
+ *           QS_LAYOUT_W   W [n_out, d_in]: the masked dense MFMA path for large
+ *                         token batches; needs xt == wt_t == QS_BF16.
+ *   y       device [rows, n_out], dtype yt (QS_F32 or QS_BF16, bf16 rounded
+ *           to nearest-even from the fp32 sum).
+ *   Arithmetic: products of the exact input values, fp32 accumulation.
+ *   Alignment: n_out % 8 == 0 (bf16 weights) or n_out % 4 == 0 (fp32), and
+ *   d_in % 8 == 0 for QS_LAYOUT_W.
+ */
+qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_in, int64_t k,
+                           const void* w, qs_dtype wt_t, qs_layout w_layout, int64_t n_out,
+                           void* y, qs_dtype yt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qs_gather_linear -- Y = Xs . W^T for an already sparsified Xs (for example
+ * the xs output of qs_topk_mask), reading only the rows of W^T whose input
+ * feature is nonzero for some row of Xs  [QS-TopK], [QS-Adv].
+ *
+ *   xs      device fp32 [rows, d_in].
+ *   wt      device W^T [d_in, n_out], dtype wt_t (QS_F32 or QS_BF16).
+ *   y       device [rows, n_out], dtype yt (QS_F32 or QS_BF16).
+ *   Arithmetic and alignment as qs_sparse_linear with QS_LAYOUT_WT.
+ *   Workspace: sized by qs_workspace_bytes(QS_OP_GATHER_LINEAR, ...); unlike
+ *   the other entry points it must be zero-filled once before its first use
+ *   (its first 16 KiB hold split-K counters that every call leaves zero), so
+ *   that the call is a single kernel launch.
+ */
+qs_status qs_gather_linear(const float* xs, int64_t rows, int64_t d_in, const void* wt,
+                           qs_dtype wt_t, int64_t n_out, void* y, qs_dtype yt,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qs_sparse_linear_i8t -- quantised Q-Sparse linear  [QS-TopK]
+ *
+ *   q = absmax int8 quantisation of x per row (see the readings above),
+ *   M = top-K of |q| (ties to the lower index),
+ *   acc[r,o] = sum_{j in M_r} q[r,j] * t[o,j]   (exact int32),
+ *   y[r,o]   = fl32(fl32(acc[r,o]) * fl32(alpha / s_r)).
+ *
+ *   x          device fp32 [rows, d_in].
+ *   wt_packed  device u8 [d_in, n_out/4]: ternary W^T, 2 bits per weight as
+ *              two's complement (00 = 0, 01 = +1, 11 = -1); byte c/4 of row j
+ *              holds columns c..c+3, column c+i in bits 2i..2i+1 (see
+ *              qs_pack_ternary).
+ *   alpha      the weight scale (mean |W|, see qs_ternarize).
+ *   acc        device i32 [rows, n_out] or NULL.
+ *   y          device fp32 [rows, n_out] or NULL.
+ *   xq         device i8 [rows, d_in] or NULL: the quantised activations.
+ *   xscale     device fp32 [rows] or NULL: s_r.
+ *   idx        device i32 [rows, k] or NULL: the selected indices, ascending.
+ *   Limits: n_out % 16 == 0; d_in <= 1<<24 (|acc| <= 128 d_in must fit int32).
+ */
+qs_status qs_sparse_linear_i8t(const float* x, int64_t rows, int64_t d_in, int64_t k,
+                               const uint8_t* wt_packed, float alpha, int64_t n_out,
+                               int32_t* acc, float* y, int8_t* xq, float* xscale, int32_t* idx,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qs_sparse_ffn -- sparse FFN: input top-K, up (and gate) projection,
+ * activation, optional top-K of the intermediate, gathered down projection.
+ *
+ *   x        device [rows, d], dtype dt.
+ *   act == QS_ACT_RELU2   [QS-TopK], [TS-Eq3-4]
+ *       dt QS_F32 or QS_BF16 (weights in the same dtype);
+ *       u = (x (.) M1) . W_up^T with M1 = top-k_in of |x|;  h = relu(u)^2;
+ *       M2 = top-k_mid of |h| (k_mid < 0: M2 = all of h);
+ *       y = (h (.) M2) . W_down^T.
+ *       w_gate = NULL; w_up = W_up^T [d, ffn]; w_down_t = W_down^T [ffn, d];
+ *       b_gate, b_up must be NULL.
+ *   act == QS_ACT_DRELU   [TS-Eq2], [TS-Fig]
+ *       dt QS_BF16 only;  xm = x (.) M1 (k_in == d: no selection);
+ *       g = xm . W_gate^T + b_gate; u = xm . W_up^T + b_up;
+ *       h = relu(g) * relu(u); rows of W_up are read only for neurons with
+ *       g > 0 for some token of the batch;
+ *       M2 = top-k_mid of |h|, or (k_mid < 0) the nonzero entries of h;
+ *       y = (h (.) M2) . W_down^T, reading only the rows of W_down^T that
+ *       some token selects.
+ *       w_gate = W_gate [ffn, d]; w_up = W_up [ffn, d]; w_down_t = W_down^T
+ *       [ffn, d]; b_gate, b_up: device fp32 [ffn] or NULL (= 0).
+ *   y        device [rows, d], dtype yt (QS_F32 or QS_BF16).
+ *   h        device fp32 [rows, ffn] or NULL: the intermediate before M2.
+ *   mid_idx  device i32 [rows, ffn] or NULL: for each row the entries of M2,
+ *            ascending, in the first mid_cnt[r] slots (the rest is untouched).
+ *   mid_cnt  device i32 [rows] or NULL.
+ *   Arithmetic: exact products, fp32 accumulation, fp32 intermediate.
+ *   Alignment: d % 8 == 0 and ffn % 8 == 0.
+ */
+qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int64_t ffn,
+                        qs_act act, int64_t k_in, int64_t k_mid,
+                        const void* w_gate, const void* w_up, const void* w_down_t,
+                        const float* b_gate, const float* b_up,
+                        void* y, qs_dtype yt, float* h, int32_t* mid_idx, int32_t* mid_cnt,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qs_workspace_bytes -- device workspace needed by `op` at this shape.
+ *   d = d_in (or the FFN model dimension), n = n_out (or ffn).  The size does
+ *   not depend on K, dtypes or layout.  *bytes receives the size (0 for ops
+ *   that need none).  Host-only; enqueues nothing.
+ */
+qs_status qs_workspace_bytes(qs_op op, int64_t rows, int64_t d, int64_t n, size_t* bytes);
+
+/*
+ * qs_ternarize -- offline ternary quantisation of a weight matrix  [QS-TopK]
+ *   w_host   host fp32 [n_out, d_in] (nn.Linear layout).
+ *   t_host   host i8 [n_out, d_in] receives t in {-1, 0, +1}.
+ *   alpha    host fp32 receives mean |W|: the exact sum of |w| rounded to
+ *            binary64, divided by n_out*d_in in binary64, rounded to binary32.
+ *   t = clamp(rint(fl32(w / fl32(alpha + 1e-5))), -1, 1).  Host-only.
+ */
+qs_status qs_ternarize(const float* w_host, int64_t n_out, int64_t d_in, int8_t* t_host,
+                       float* alpha);
+
+/*
+ * qs_pack_ternary -- pack t [n_out, d_in] (host, values in {-1,0,1}) into the
+ * feature-major 2-bit layout that qs_sparse_linear_i8t reads (host u8
+ * [d_in, n_out/4]).  n_out % 4 == 0.  Host-only.
+ */
+qs_status qs_pack_ternary(const int8_t* t_host, int64_t n_out, int64_t d_in, uint8_t* packed_host);
+
+/* Text of the last error on the calling thread ("" if none); valid until the
+ * next qs_* call on this thread. */
+const char* qs_last_error(void);
+
+/* Library version string. */
+const char* qs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QS_H */

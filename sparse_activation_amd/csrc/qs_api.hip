@@ -1,0 +1,457 @@
+// C ABI of libqs.so: argument validation, workspace layout and dispatch to
+// the HIP kernels.  Every check runs before anything is enqueued, so a call
+// that fails leaves the outputs untouched.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/qs.h"
+#include "qs_error.h"
+#include "qs_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+qs_status fail(qs_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+qs_status ok() {
+    g_err.clear();
+    return QS_OK;
+}
+
+qs_status hip_fail(hipError_t e, const char* where) {
+    return fail(QS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Bump allocator over the caller's workspace (256-byte aligned regions).
+struct Carve {
+    size_t off = 0;
+    char* base = nullptr;
+    void* take(size_t bytes) {
+        void* p = base ? base + off : nullptr;
+        off += (bytes + 255) & ~size_t(255);
+        return p;
+    }
+};
+
+// ----------------------------------------------------------------- layouts
+// Each layout is computed twice: once with base == nullptr to size it, once
+// with the caller's pointer to carve it.  Sizes depend on shapes only.
+
+struct LinearWs {
+    int32_t* counters;
+    float* xs;
+    float* partial;
+    uint32_t* tau;
+    int32_t* cutoff;
+    size_t bytes;
+};
+
+size_t max_sz(size_t a, size_t b) { return a > b ? a : b; }
+
+LinearWs linear_ws(char* base, int64_t rows, int64_t d_in, int64_t n_out) {
+    qs::GemvPlan pb = qs::plan_gemv(rows, d_in, n_out, 1);
+    qs::GemvPlan pf = qs::plan_gemv(rows, d_in, n_out, 0);
+    Carve c;
+    c.base = base;
+    LinearWs w{};
+    w.counters = (int32_t*)c.take(sizeof(int32_t) * (size_t)(pb.n_counters > pf.n_counters ? pb.n_counters : pf.n_counters));
+    w.xs = (float*)c.take(sizeof(float) * (size_t)rows * d_in);
+    w.partial = (float*)c.take(sizeof(float) * max_sz(pb.partial_floats, pf.partial_floats));
+    w.tau = (uint32_t*)c.take(sizeof(uint32_t) * (size_t)rows);
+    w.cutoff = (int32_t*)c.take(sizeof(int32_t) * (size_t)rows);
+    w.bytes = c.off;
+    return w;
+}
+
+struct GatherWs {
+    int32_t* counters;
+    float* partial;
+    size_t bytes;
+};
+
+// qs_gather_linear keeps its split-K counters in a fixed header at the start
+// of the workspace, which the caller zeroes once and every call leaves zero.
+constexpr int kGatherCounters = 4096;
+
+GatherWs gather_ws(char* base, int64_t rows, int64_t d_in, int64_t n_out) {
+    qs::GemvPlan pb = qs::plan_gemv(rows, d_in, n_out, 1);
+    qs::GemvPlan pf = qs::plan_gemv(rows, d_in, n_out, 0);
+    Carve c;
+    c.base = base;
+    GatherWs w{};
+    w.counters = (int32_t*)c.take(sizeof(int32_t) * kGatherCounters);
+    w.partial = (float*)c.take(sizeof(float) * max_sz(pb.partial_floats, pf.partial_floats));
+    w.bytes = c.off;
+    return w;
+}
+
+struct I8tWs {
+    int32_t* counters;
+    int8_t* qs;
+    float* scale;
+    int32_t* partial;
+    size_t bytes;
+};
+
+I8tWs i8t_ws(char* base, int64_t rows, int64_t d_in, int64_t n_out) {
+    qs::I8tPlan p = qs::plan_i8t(rows, d_in, n_out);
+    Carve c;
+    c.base = base;
+    I8tWs w{};
+    w.counters = (int32_t*)c.take(sizeof(int32_t) * (size_t)p.n_counters);
+    w.qs = (int8_t*)c.take((size_t)rows * d_in);
+    w.scale = (float*)c.take(sizeof(float) * (size_t)rows);
+    w.partial = (int32_t*)c.take(sizeof(int32_t) * p.partial_ints);
+    w.bytes = c.off;
+    return w;
+}
+
+struct FfnWs {
+    int32_t* ctr_up;
+    int32_t* ctr_down;
+    int n_ctr;             // ctr_up and ctr_down are contiguous: n_ctr ints in total
+    float* xs1;            // relu2: X (.) M1 (fp32)
+    uint16_t* xm;          // drelu: X (.) M1 (bf16)
+    float* h;
+    float* hs;
+    float* partial;
+    size_t bytes;
+};
+
+FfnWs ffn_ws(char* base, int64_t rows, int64_t d, int64_t ffn, bool drelu) {
+    Carve c;
+    c.base = base;
+    FfnWs w{};
+    size_t up_ctr = 0, up_part = 0;
+    if (!drelu) {
+        qs::GemvPlan ub = qs::plan_gemv(rows, d, ffn, 1), uf = qs::plan_gemv(rows, d, ffn, 0);
+        up_ctr = (size_t)(ub.n_counters > uf.n_counters ? ub.n_counters : uf.n_counters);
+        up_part = max_sz(ub.partial_floats, uf.partial_floats);
+    }
+    qs::GemvPlan db = qs::plan_gemv(rows, ffn, d, 1), df = qs::plan_gemv(rows, ffn, d, 0);
+    size_t down_ctr = (size_t)(db.n_counters > df.n_counters ? db.n_counters : df.n_counters);
+    size_t down_part = max_sz(db.partial_floats, df.partial_floats);
+    w.n_ctr = (int)(up_ctr + down_ctr);
+    w.ctr_up = (int32_t*)c.take(sizeof(int32_t) * (up_ctr + down_ctr));
+    w.ctr_down = w.ctr_up ? w.ctr_up + up_ctr : nullptr;
+    if (!drelu) w.xs1 = (float*)c.take(sizeof(float) * (size_t)rows * d);
+    else w.xm = (uint16_t*)c.take(sizeof(uint16_t) * (size_t)rows * d);
+    w.h = (float*)c.take(sizeof(float) * (size_t)rows * ffn);
+    w.hs = (float*)c.take(sizeof(float) * (size_t)rows * ffn);
+    w.partial = (float*)c.take(sizeof(float) * max_sz(up_part, down_part));
+    w.bytes = c.off;
+    return w;
+}
+
+bool valid_float_dtype(qs_dtype t) { return t == QS_F32 || t == QS_BF16; }
+
+}  // namespace
+
+qs_status qs::set_error(qs_status st, const char* msg) {
+    g_err = msg;
+    return st;
+}
+
+extern "C" {
+
+const char* qs_last_error(void) { return g_err.c_str(); }
+
+const char* qs_version(void) { return "qsparse-mi355x 0.1 (gfx950)"; }
+
+qs_status qs_workspace_bytes(qs_op op, int64_t rows, int64_t d, int64_t n, size_t* bytes) {
+    if (bytes == nullptr) return fail(QS_ERR_INVALID_ARG, "qs_workspace_bytes: bytes is NULL");
+    if (rows < 0 || d <= 0 || n < 0) return fail(QS_ERR_INVALID_ARG, "qs_workspace_bytes: bad shape");
+    switch (op) {
+    case QS_OP_TOPK_MASK: *bytes = 0; break;
+    case QS_OP_SPARSE_LINEAR: *bytes = linear_ws(nullptr, rows, d, n).bytes; break;
+    case QS_OP_SPARSE_LINEAR_I8T: *bytes = i8t_ws(nullptr, rows, d, n).bytes; break;
+    case QS_OP_SPARSE_FFN_RELU2: *bytes = ffn_ws(nullptr, rows, d, n, false).bytes; break;
+    case QS_OP_SPARSE_FFN_DRELU: *bytes = ffn_ws(nullptr, rows, d, n, true).bytes; break;
+    case QS_OP_GATHER_LINEAR: *bytes = gather_ws(nullptr, rows, d, n).bytes; break;
+    default: return fail(QS_ERR_INVALID_ARG, "qs_workspace_bytes: unknown op %d", (int)op);
+    }
+    return ok();
+}
+
+qs_status qs_topk_mask(const void* x, qs_dtype xt, int64_t rows, int64_t d, int64_t k,
+                       uint8_t* mask, int32_t* idx, uint32_t* tau, int32_t* cutoff,
+                       float* xs, void* stream) {
+    if (rows < 0 || d <= 0 || d > (int64_t(1) << 24))
+        return fail(QS_ERR_INVALID_ARG, "qs_topk_mask: need rows >= 0 and 0 < d <= 2^24");
+    if (k < 0 || k > d) return fail(QS_ERR_INVALID_ARG, "qs_topk_mask: need 0 <= k <= d");
+    if (xt != QS_F32 && xt != QS_BF16 && xt != QS_I8)
+        return fail(QS_ERR_UNSUPPORTED, "qs_topk_mask: dtype must be QS_F32, QS_BF16 or QS_I8");
+    if (rows > 0x7FFFFFFF) return fail(QS_ERR_UNSUPPORTED, "qs_topk_mask: too many rows");
+    if (rows == 0) return ok();
+    if (x == nullptr) return fail(QS_ERR_INVALID_ARG, "qs_topk_mask: x is NULL");
+    const void* ptrs[] = {x, mask, idx, tau, cutoff, xs};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(QS_ERR_UNSUPPORTED, "qs_topk_mask: pointer not 16-byte aligned");
+    if (xs && xt == QS_I8) return fail(QS_ERR_UNSUPPORTED, "qs_topk_mask: xs needs QS_F32 or QS_BF16 x");
+    qs::TopkArgs a{};
+    a.x = x;
+    a.d = d;
+    a.k = k;
+    a.mask = mask;
+    a.idx = idx;
+    a.idx_stride = k;
+    a.tau = tau;
+    a.cutoff = cutoff;
+    a.xs = xs;
+    const int kk = xt == QS_F32 ? qs::KEY_F32 : xt == QS_BF16 ? qs::KEY_BF16 : qs::KEY_I8;
+    hipError_t e = qs::launch_topk(kk, xs ? qs::XS_F32 : qs::XS_NONE, rows, a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "qs_topk_mask");
+    return ok();
+}
+
+qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_in, int64_t k,
+                           const void* w, qs_dtype wt_t, qs_layout w_layout, int64_t n_out,
+                           void* y, qs_dtype yt, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "qs_sparse_linear";
+    if (rows < 0 || d_in <= 0 || n_out <= 0 || d_in > (int64_t(1) << 24))
+        return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
+    if (k < 0 || k > d_in) return fail(QS_ERR_INVALID_ARG, "%s: need 0 <= k <= d_in", fn);
+    if (!valid_float_dtype(xt) || !valid_float_dtype(wt_t) || !valid_float_dtype(yt))
+        return fail(QS_ERR_UNSUPPORTED, "%s: dtypes must be QS_F32 or QS_BF16", fn);
+    if (w_layout != QS_LAYOUT_WT && w_layout != QS_LAYOUT_W)
+        return fail(QS_ERR_INVALID_ARG, "%s: unknown weight layout", fn);
+    if (rows > 0x7FFFFFFF) return fail(QS_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    if (w_layout == QS_LAYOUT_W) {
+        if (xt != QS_BF16 || wt_t != QS_BF16)
+            return fail(QS_ERR_UNSUPPORTED, "%s: QS_LAYOUT_W (MFMA path) needs bf16 x and w", fn);
+        if (d_in % 8 != 0) return fail(QS_ERR_UNSUPPORTED, "%s: QS_LAYOUT_W needs d_in %% 8 == 0", fn);
+    } else {
+        if (n_out % (wt_t == QS_BF16 ? 8 : 4) != 0)
+            return fail(QS_ERR_UNSUPPORTED, "%s: n_out must be a multiple of %d", fn,
+                        wt_t == QS_BF16 ? 8 : 4);
+    }
+    if (rows == 0) return ok();
+    if (!x || !w || !y) return fail(QS_ERR_INVALID_ARG, "%s: x, w and y must be non-NULL", fn);
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (ws && !aligned16(ws)))
+        return fail(QS_ERR_UNSUPPORTED, "%s: pointer not 16-byte aligned", fn);
+    LinearWs need = linear_ws(nullptr, rows, d_in, n_out);
+    if (ws == nullptr || ws_bytes < need.bytes)
+        return fail(QS_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need.bytes);
+    LinearWs wsp = linear_ws((char*)ws, rows, d_in, n_out);
+    hipStream_t st = (hipStream_t)stream;
+    const int kk = xt == QS_F32 ? qs::KEY_F32 : qs::KEY_BF16;
+    hipError_t e;
+    if (w_layout == QS_LAYOUT_W) {
+        qs::TopkArgs t{};
+        t.x = x; t.d = d_in; t.k = k; t.idx_stride = k;
+        t.tau = wsp.tau; t.cutoff = wsp.cutoff;
+        e = qs::launch_topk(kk, qs::XS_NONE, rows, t, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        qs::MfmaArgs m{};
+        m.x = (const uint16_t*)x; m.tau = wsp.tau; m.cutoff = wsp.cutoff;
+        m.w = (const uint16_t*)w; m.m = rows; m.n = n_out; m.k = d_in;
+        m.y = y; m.y_bf16 = yt == QS_BF16;
+        e = qs::launch_masked_gemm(m, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return ok();
+    }
+    const int wb = wt_t == QS_BF16;
+    qs::GemvPlan plan = qs::plan_gemv(rows, d_in, n_out, wb);
+    qs::TopkArgs t{};
+    t.x = x; t.d = d_in; t.k = k; t.idx_stride = k;
+    t.xs = wsp.xs;
+    t.zero_ptr = wsp.counters; t.n_zero = plan.n_counters;
+    e = qs::launch_topk(kk, qs::XS_F32, rows, t, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    qs::GemvArgs g{};
+    g.xs = wsp.xs; g.rows = rows; g.d_in = d_in; g.n_out = n_out; g.w = w;
+    g.partial = wsp.partial; g.counters = wsp.counters; g.y = y; g.y_bf16 = yt == QS_BF16;
+    g.epilogue = qs::EPI_STORE;
+    e = qs::launch_gemv(plan, wb, g, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+qs_status qs_gather_linear(const float* xs, int64_t rows, int64_t d_in, const void* wt,
+                           qs_dtype wt_t, int64_t n_out, void* y, qs_dtype yt,
+                           void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "qs_gather_linear";
+    if (rows < 0 || d_in <= 0 || n_out <= 0 || d_in > (int64_t(1) << 24))
+        return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
+    if (!valid_float_dtype(wt_t) || !valid_float_dtype(yt))
+        return fail(QS_ERR_UNSUPPORTED, "%s: dtypes must be QS_F32 or QS_BF16", fn);
+    if (n_out % (wt_t == QS_BF16 ? 8 : 4) != 0)
+        return fail(QS_ERR_UNSUPPORTED, "%s: n_out must be a multiple of %d", fn,
+                    wt_t == QS_BF16 ? 8 : 4);
+    if (rows > 0x7FFFFFFF) return fail(QS_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    if (rows == 0) return ok();
+    if (!xs || !wt || !y) return fail(QS_ERR_INVALID_ARG, "%s: xs, wt and y must be non-NULL", fn);
+    if (!aligned16(xs) || !aligned16(wt) || !aligned16(y) || (ws && !aligned16(ws)))
+        return fail(QS_ERR_UNSUPPORTED, "%s: pointer not 16-byte aligned", fn);
+    GatherWs need = gather_ws(nullptr, rows, d_in, n_out);
+    if (ws == nullptr || ws_bytes < need.bytes)
+        return fail(QS_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need.bytes);
+    GatherWs wsp = gather_ws((char*)ws, rows, d_in, n_out);
+    hipStream_t st = (hipStream_t)stream;
+    const int wb = wt_t == QS_BF16;
+    qs::GemvPlan plan = qs::plan_gemv(rows, d_in, n_out, wb);
+    if (plan.n_counters > kGatherCounters)
+        return fail(QS_ERR_UNSUPPORTED, "%s: too many output tiles (n_out or rows too large)", fn);
+    qs::GemvArgs g{};
+    g.xs = xs; g.rows = rows; g.d_in = d_in; g.n_out = n_out; g.w = wt;
+    g.partial = wsp.partial; g.counters = wsp.counters; g.y = y; g.y_bf16 = yt == QS_BF16;
+    g.epilogue = qs::EPI_STORE;
+    hipError_t e = qs::launch_gemv(plan, wb, g, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+qs_status qs_sparse_linear_i8t(const float* x, int64_t rows, int64_t d_in, int64_t k,
+                               const uint8_t* wt_packed, float alpha, int64_t n_out,
+                               int32_t* acc, float* y, int8_t* xq, float* xscale, int32_t* idx,
+                               void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "qs_sparse_linear_i8t";
+    if (rows < 0 || d_in <= 0 || n_out <= 0 || d_in > (int64_t(1) << 24))
+        return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
+    if (k < 0 || k > d_in) return fail(QS_ERR_INVALID_ARG, "%s: need 0 <= k <= d_in", fn);
+    if (n_out % 16 != 0) return fail(QS_ERR_UNSUPPORTED, "%s: n_out must be a multiple of 16", fn);
+    if (rows > 0x7FFFFFFF) return fail(QS_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    if (rows == 0) return ok();
+    if (!x || !wt_packed) return fail(QS_ERR_INVALID_ARG, "%s: x and wt_packed must be non-NULL", fn);
+    const void* ptrs[] = {x, wt_packed, acc, y, xq, xscale, idx, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(QS_ERR_UNSUPPORTED, "%s: pointer not 16-byte aligned", fn);
+    I8tWs need = i8t_ws(nullptr, rows, d_in, n_out);
+    if (ws == nullptr || ws_bytes < need.bytes)
+        return fail(QS_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need.bytes);
+    I8tWs wsp = i8t_ws((char*)ws, rows, d_in, n_out);
+    qs::I8tPlan plan = qs::plan_i8t(rows, d_in, n_out);
+    hipStream_t st = (hipStream_t)stream;
+    float* scale = xscale ? xscale : wsp.scale;
+    qs::TopkArgs t{};
+    t.x = x; t.d = d_in; t.k = k; t.idx = idx; t.idx_stride = k;
+    t.xs = wsp.qs; t.xq = xq; t.xscale = scale;
+    t.zero_ptr = wsp.counters; t.n_zero = plan.n_counters;
+    hipError_t e = qs::launch_topk(qs::KEY_Q8, qs::XS_I8, rows, t, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (!acc && !y) return ok();
+    qs::I8tArgs g{};
+    g.qs = wsp.qs; g.xscale = scale; g.rows = rows; g.d_in = d_in; g.n_out = n_out;
+    g.wt = wt_packed; g.alpha = alpha; g.partial = wsp.partial; g.counters = wsp.counters;
+    g.acc = acc; g.y = y;
+    e = qs::launch_i8t(plan, g, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int64_t ffn,
+                        qs_act act, int64_t k_in, int64_t k_mid,
+                        const void* w_gate, const void* w_up, const void* w_down_t,
+                        const float* b_gate, const float* b_up,
+                        void* y, qs_dtype yt, float* h, int32_t* mid_idx, int32_t* mid_cnt,
+                        void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "qs_sparse_ffn";
+    if (rows < 0 || d <= 0 || ffn <= 0 || d > (int64_t(1) << 24) || ffn > (int64_t(1) << 24))
+        return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
+    if (act != QS_ACT_RELU2 && act != QS_ACT_DRELU)
+        return fail(QS_ERR_INVALID_ARG, "%s: unknown activation", fn);
+    if (k_in < 0 || k_in > d) return fail(QS_ERR_INVALID_ARG, "%s: need 0 <= k_in <= d", fn);
+    if (k_mid > ffn) return fail(QS_ERR_INVALID_ARG, "%s: need k_mid <= ffn", fn);
+    if (!valid_float_dtype(dt) || !valid_float_dtype(yt))
+        return fail(QS_ERR_UNSUPPORTED, "%s: dtypes must be QS_F32 or QS_BF16", fn);
+    if (act == QS_ACT_DRELU && dt != QS_BF16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: dReLU path needs bf16 x and weights", fn);
+    if (d % 8 != 0 || ffn % 8 != 0)
+        return fail(QS_ERR_UNSUPPORTED, "%s: d and ffn must be multiples of 8", fn);
+    if (rows > 0x7FFFFFFF) return fail(QS_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    if (rows == 0) return ok();
+    if (!x || !w_up || !w_down_t || !y)
+        return fail(QS_ERR_INVALID_ARG, "%s: x, w_up, w_down_t and y must be non-NULL", fn);
+    if (act == QS_ACT_DRELU && !w_gate) return fail(QS_ERR_INVALID_ARG, "%s: dReLU needs w_gate", fn);
+    if (act == QS_ACT_RELU2 && (w_gate || b_gate || b_up))
+        return fail(QS_ERR_INVALID_ARG, "%s: squared ReLU takes no gate weights or biases", fn);
+    const void* ptrs[] = {x, w_gate, w_up, w_down_t, b_gate, b_up, y, h, mid_idx, mid_cnt, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(QS_ERR_UNSUPPORTED, "%s: pointer not 16-byte aligned", fn);
+    const bool drelu = act == QS_ACT_DRELU;
+    FfnWs need = ffn_ws(nullptr, rows, d, ffn, drelu);
+    if (ws == nullptr || ws_bytes < need.bytes)
+        return fail(QS_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need.bytes);
+    FfnWs wsp = ffn_ws((char*)ws, rows, d, ffn, drelu);
+    hipStream_t st = (hipStream_t)stream;
+    const int wb = dt == QS_BF16;
+    const int kk = wb ? qs::KEY_BF16 : qs::KEY_F32;
+    float* hbuf = h ? h : wsp.h;
+    hipError_t e;
+
+    // Stage 1: the intermediate h.
+    if (!drelu) {
+        qs::GemvPlan pu = qs::plan_gemv(rows, d, ffn, wb);
+        qs::TopkArgs t{};
+        t.x = x; t.d = d; t.k = k_in; t.idx_stride = k_in;
+        t.xs = wsp.xs1;
+        t.zero_ptr = wsp.ctr_up; t.n_zero = wsp.n_ctr;
+        e = qs::launch_topk(kk, qs::XS_F32, rows, t, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        qs::GemvArgs g{};
+        g.xs = wsp.xs1; g.rows = rows; g.d_in = d; g.n_out = ffn; g.w = w_up;
+        g.partial = wsp.partial; g.counters = wsp.ctr_up; g.y = hbuf; g.y_bf16 = 0;
+        g.epilogue = qs::EPI_RELU2;
+        e = qs::launch_gemv(pu, wb, g, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    } else {
+        const uint16_t* xin = (const uint16_t*)x;
+        bool zeroed = false;
+        if (k_in < d) {
+            qs::TopkArgs t{};
+            t.x = x; t.d = d; t.k = k_in; t.idx_stride = k_in;
+            t.xs = wsp.xm;
+            t.zero_ptr = wsp.ctr_up; t.n_zero = wsp.n_ctr;
+            e = qs::launch_topk(qs::KEY_BF16, qs::XS_BF16, rows, t, st);
+            if (e != hipSuccess) return hip_fail(e, fn);
+            xin = wsp.xm;
+            zeroed = true;
+        }
+        qs::DreluArgs g{};
+        g.x = xin; g.rows = rows; g.d = d; g.ffn = ffn;
+        g.wg = (const uint16_t*)w_gate; g.wu = (const uint16_t*)w_up;
+        g.bg = b_gate; g.bu = b_up; g.h = hbuf;
+        g.zero_ptr = zeroed ? nullptr : wsp.ctr_up; g.n_zero = zeroed ? 0 : wsp.n_ctr;
+        e = qs::launch_drelu_gate_up(g, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
+
+    // Stage 2: select the intermediate entries that enter W_down.
+    const float* hsel = hbuf;
+    if (k_mid >= 0) {
+        qs::TopkArgs t{};
+        t.x = hbuf; t.d = ffn; t.k = k_mid;
+        t.idx = mid_idx; t.idx_stride = ffn; t.count = mid_cnt;
+        t.xs = wsp.hs;
+        e = qs::launch_topk(qs::KEY_F32, qs::XS_F32, rows, t, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        hsel = wsp.hs;
+    } else if (mid_idx || mid_cnt) {
+        e = qs::launch_nonzero_lists(hbuf, rows, ffn, mid_idx, mid_cnt, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
+
+    // Stage 3: gathered down projection.
+    qs::GemvPlan pd = qs::plan_gemv(rows, ffn, d, wb);
+    qs::GemvArgs g{};
+    g.xs = hsel; g.rows = rows; g.d_in = ffn; g.n_out = d; g.w = w_down_t;
+    g.partial = wsp.partial; g.counters = wsp.ctr_down; g.y = y; g.y_bf16 = yt == QS_BF16;
+    g.epilogue = qs::EPI_STORE;
+    e = qs::launch_gemv(pd, wb, g, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+}  // extern "C"

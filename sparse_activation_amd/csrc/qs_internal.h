@@ -1,0 +1,132 @@
+// Internal declarations shared by the HIP translation units of libqs.so.
+// Not part of the public ABI (that is include/qs.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qs {
+
+// ---------------------------------------------------------------- element kinds
+enum KeyKind : int {
+    KEY_F32 = 0,   // fp32 input, key = bits & 0x7FFFFFFF
+    KEY_BF16 = 1,  // bf16 input, key = bits & 0x7FFF
+    KEY_I8 = 2,    // int8 input, key = |q|
+    KEY_Q8 = 3     // fp32 input quantised in-kernel to int8 (absmax), key = |q|
+};
+
+// What the selection kernel writes as the "sparsified activation" X (.) M.
+enum XsKind : int {
+    XS_NONE = 0,
+    XS_F32 = 1,    // float [rows, d]
+    XS_BF16 = 2,   // bf16 bits [rows, d]
+    XS_I8 = 3      // int8 [rows, d] (masked q)
+};
+
+struct TopkArgs {
+    const void* x;        // [rows, d]
+    int64_t d;
+    int64_t k;
+    uint8_t* mask;        // [rows, d] or null
+    int32_t* idx;         // [rows, idx_stride] or null (first k entries of each row)
+    int64_t idx_stride;   // row stride of idx (k unless the caller says otherwise)
+    int32_t* count;       // [rows] or null: receives k
+    uint32_t* tau;        // [rows] or null
+    int32_t* cutoff;      // [rows] or null
+    void* xs;             // [rows, d] or null (kind given by xs_kind)
+    int8_t* xq;           // KEY_Q8 only: [rows, d] or null
+    float* xscale;        // KEY_Q8 only: [rows] or null
+    int32_t* zero_ptr;    // block 0 clears zero_ptr[0..n_zero) (split-K counters)
+    int n_zero;
+};
+
+// One workgroup per row.  Returns a HIP error code (hipSuccess = 0).
+hipError_t launch_topk(int key_kind, int xs_kind, int64_t rows, const TopkArgs& a,
+                       hipStream_t stream);
+
+// ---------------------------------------------------------------- gather GEMV
+enum Epilogue : int { EPI_STORE = 0, EPI_RELU2 = 1 };
+
+// Launch plan of the gather GEMV: deterministic function of the shape only.
+struct GemvPlan {
+    int lpr;          // lanes per weight-row segment
+    int ept;          // elements per lane (16 bytes of weights)
+    int ct;           // columns per tile
+    int n_tiles;      // column tiles
+    int bt;           // tokens per tile
+    int n_tok_tiles;
+    int cand;         // candidate input rows per split
+    int nsplit;
+    size_t partial_floats;  // nsplit * rows * n_out (0 if nsplit == 1)
+    int n_counters;         // n_tiles * n_tok_tiles
+};
+GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16);
+
+struct GemvArgs {
+    const float* xs;       // [rows, d_in] fp32, zero where not selected
+    int64_t rows, d_in, n_out;
+    const void* w;         // W^T [d_in, n_out], fp32 or bf16
+    float* partial;        // [nsplit, rows, n_out]
+    int32_t* counters;     // [n_counters], zero on entry, left zero on exit
+    void* y;               // [rows, n_out]
+    int y_bf16;            // output dtype
+    int epilogue;          // EPI_STORE or EPI_RELU2 (then y is fp32 h)
+};
+hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- ternary x int8 gather
+struct I8tPlan {
+    int ct, n_tiles, bt, n_tok_tiles, cand, nsplit;
+    size_t partial_ints;
+    int n_counters;
+};
+I8tPlan plan_i8t(int64_t rows, int64_t d_in, int64_t n_out);
+
+struct I8tArgs {
+    const int8_t* qs;        // [rows, d_in] masked q
+    const float* xscale;     // [rows]
+    int64_t rows, d_in, n_out;
+    const uint8_t* wt;       // [d_in, n_out/4] packed
+    float alpha;
+    int32_t* partial;        // [nsplit, rows, n_out]
+    int32_t* counters;
+    int32_t* acc;            // [rows, n_out] or null
+    float* y;                // [rows, n_out] or null
+};
+hipError_t launch_i8t(const I8tPlan& p, const I8tArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- masked MFMA GEMM
+struct MfmaArgs {
+    const uint16_t* x;       // bf16 [M, K]
+    const uint32_t* tau;     // [M] selection descriptors
+    const int32_t* cutoff;   // [M]
+    const uint16_t* w;       // bf16 W [N, K]
+    int64_t m, n, k;
+    void* y;                 // [M, N]
+    int y_bf16;
+};
+hipError_t launch_masked_gemm(const MfmaArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- dReLU gate/up
+struct DreluArgs {
+    const uint16_t* x;       // bf16 [rows, d] (already masked if k_in < d)
+    int64_t rows, d, ffn;
+    const uint16_t* wg;      // [ffn, d]
+    const uint16_t* wu;      // [ffn, d]
+    const float* bg;         // [ffn] or null
+    const float* bu;         // [ffn] or null
+    float* h;                // [rows, ffn] fp32
+    int32_t* zero_ptr;       // block 0 clears zero_ptr[0..n_zero) (split-K counters)
+    int n_zero;
+};
+hipError_t launch_drelu_gate_up(const DreluArgs& a, hipStream_t stream);
+
+// Nonzero compaction of h rows: idx[r, 0..cnt) ascending, cnt[r].
+hipError_t launch_nonzero_lists(const float* h, int64_t rows, int64_t n, int32_t* idx,
+                                int32_t* cnt, hipStream_t stream);
+
+// Fill an int32 buffer with zeros (a kernel, so graph capture stays clean).
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
+
+}  // namespace qs

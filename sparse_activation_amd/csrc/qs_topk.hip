@@ -1,0 +1,306 @@
+// Per-row top-K selection by |x| with ties to the lower index (gfx950).
+//
+// Q-Sparse news article (zxwl-tech.com), section "Sparsification with the
+// Top-K function": take |X|, find the K entries of largest magnitude, build
+// a mask of X's shape that is 1 there, and use X (.) M in place of X.  Ties
+// (not covered by the pages) go to the lower index.
+//
+// One workgroup per row.  The row's raw words are staged in LDS, then an
+// MSD radix select on the magnitude key (8-bit digits, per-wave-group LDS
+// histograms, a descending block scan over the 256 bins) finds tau, the key
+// of the K-th largest entry, and how many entries equal to tau are taken.
+// A final pass walks the row in index order in chunks of one workgroup: two
+// wavefront ballots (key > tau, key == tau) and mbcnt prefix counts give
+// each tie its rank and each selected entry its slot in the ascending index
+// list, with one barrier per chunk (double-buffered wave totals).
+//
+// The quantised variant (KEY_Q8) first quantises the fp32 row to int8
+// (absmax, IEEE binary32 with round-to-nearest-even at every step; Q-Sparse
+// news article, Top-K section: activations are quantised before top-K with
+// an epsilon-guarded denominator) and then selects on |q|.
+#include "qs_internal.h"
+
+namespace qs {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kNSub = 4;               // LDS sub-histograms (spread atomic contention)
+constexpr int64_t kStageMaxD = 14336;  // raw words staged in LDS up to this row length
+
+__device__ __forceinline__ uint32_t popc_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Raw 32-bit word of element i, and its magnitude key.
+template <int KK> struct Elem;
+
+template <> struct Elem<KEY_F32> {
+    static constexpr int kKeyBits = 31;
+    __device__ static uint32_t load(const void* x, int64_t i, float) {
+        return reinterpret_cast<const uint32_t*>(x)[i];
+    }
+    __device__ static uint32_t key(uint32_t raw) { return raw & 0x7FFFFFFFu; }
+};
+
+template <> struct Elem<KEY_BF16> {
+    static constexpr int kKeyBits = 15;
+    __device__ static uint32_t load(const void* x, int64_t i, float) {
+        return reinterpret_cast<const uint16_t*>(x)[i];
+    }
+    __device__ static uint32_t key(uint32_t raw) { return raw & 0x7FFFu; }
+};
+
+template <> struct Elem<KEY_I8> {
+    static constexpr int kKeyBits = 8;
+    __device__ static uint32_t load(const void* x, int64_t i, float) {
+        return (uint32_t)(int32_t)reinterpret_cast<const int8_t*>(x)[i];
+    }
+    __device__ static uint32_t key(uint32_t raw) {
+        int32_t v = (int32_t)raw;
+        return (uint32_t)(v < 0 ? -v : v);
+    }
+};
+
+template <> struct Elem<KEY_Q8> {
+    static constexpr int kKeyBits = 8;
+    // q = clamp(rint(fl32(x * s)), -128, 127)
+    __device__ static uint32_t load(const void* x, int64_t i, float s) {
+        float v = reinterpret_cast<const float*>(x)[i];
+        float r = rintf(__fmul_rn(v, s));
+        r = fminf(fmaxf(r, -128.0f), 127.0f);
+        return (uint32_t)(int32_t)r;
+    }
+    __device__ static uint32_t key(uint32_t raw) { return Elem<KEY_I8>::key(raw); }
+};
+
+template <int KK, int XK>
+__device__ __forceinline__ void store_xs(void* xs, int64_t i, uint32_t raw, bool sel) {
+    if constexpr (XK == XS_F32) {
+        float v = 0.0f;
+        if (sel) {
+            if constexpr (KK == KEY_F32) v = __uint_as_float(raw);
+            else if constexpr (KK == KEY_BF16) v = __uint_as_float(raw << 16);
+            else v = (float)(int32_t)raw;
+        }
+        reinterpret_cast<float*>(xs)[i] = v;
+    } else if constexpr (XK == XS_BF16) {
+        reinterpret_cast<uint16_t*>(xs)[i] = sel ? (uint16_t)raw : (uint16_t)0;
+    } else if constexpr (XK == XS_I8) {
+        reinterpret_cast<int8_t*>(xs)[i] = sel ? (int8_t)(int32_t)raw : (int8_t)0;
+    }
+}
+
+template <int NT, int KK, int XK, bool STAGED>
+__global__ __launch_bounds__(NT) void topk_rows_kernel(TopkArgs a) {
+    constexpr int NW = NT / kWave;
+    extern __shared__ uint32_t s_raw[];                 // [d] when STAGED
+    __shared__ uint32_t s_hist[kNSub][256];
+    __shared__ uint32_t s_scan[4];
+    __shared__ uint32_t s_gt[2][NW], s_eq[2][NW];
+    __shared__ uint32_t s_digit, s_kr;
+    __shared__ float s_max[NW];
+
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int64_t d = a.d;
+    const int64_t k = a.k;
+    const int64_t row0 = (int64_t)r * d;
+
+    if (r == 0 && a.zero_ptr != nullptr)
+        for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
+
+    // Quantisation scale (KEY_Q8): gamma = max|x| (exact), s = 127 / (gamma + eps).
+    float scale = 0.0f;
+    if constexpr (KK == KEY_Q8) {
+        const float* xr = reinterpret_cast<const float*>(a.x) + row0;
+        float m = 0.0f;
+        for (int64_t j = tid; j < d; j += NT) m = fmaxf(m, fabsf(xr[j]));
+        for (int off = kWave / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if (lane == 0) s_max[wave] = m;
+        __syncthreads();
+        float g = s_max[0];
+        for (int w = 1; w < NW; ++w) g = fmaxf(g, s_max[w]);
+        scale = __fdiv_rn(127.0f, __fadd_rn(g, 1e-5f));
+        if (tid == 0 && a.xscale != nullptr) a.xscale[r] = scale;
+    }
+
+    if constexpr (STAGED) {
+        for (int64_t j = tid; j < d; j += NT) {
+            uint32_t raw = Elem<KK>::load(a.x, row0 + j, scale);
+            s_raw[j] = raw;
+            if constexpr (KK == KEY_Q8)
+                if (a.xq != nullptr) a.xq[row0 + j] = (int8_t)(int32_t)raw;
+        }
+        __syncthreads();
+    } else {
+        if constexpr (KK == KEY_Q8)
+            if (a.xq != nullptr)
+                for (int64_t j = tid; j < d; j += NT)
+                    a.xq[row0 + j] = (int8_t)(int32_t)Elem<KK>::load(a.x, row0 + j, scale);
+    }
+    auto raw_at = [&](int64_t j) -> uint32_t {
+        if constexpr (STAGED) return s_raw[j];
+        else return Elem<KK>::load(a.x, row0 + j, scale);
+    };
+
+    // ---- MSD radix select: tau and the number kr of tau-ties to take.
+    uint32_t prefix = 0, himask = 0, kr = (uint32_t)k;
+    if (k > 0) {
+        constexpr int kPasses = (Elem<KK>::kKeyBits + 7) / 8;
+#pragma unroll 1
+        for (int p = kPasses - 1; p >= 0; --p) {
+            const int shift = 8 * p;
+            for (int i = tid; i < kNSub * 256; i += NT) (&s_hist[0][0])[i] = 0;
+            __syncthreads();
+            uint32_t* hsub = s_hist[wave % kNSub];
+            for (int64_t j = tid; j < d; j += NT) {
+                uint32_t key = Elem<KK>::key(raw_at(j));
+                if ((key & himask) == prefix) atomicAdd(&hsub[(key >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            // Threads 0..255 own bins in descending order; inclusive scan gives
+            // the number of candidates with digit >= bin.
+            uint32_t v = 0, incl = 0;
+            if (tid < 256) {
+                const int b = 255 - tid;
+#pragma unroll
+                for (int q = 0; q < kNSub; ++q) v += s_hist[q][b];
+                incl = v;
+#pragma unroll
+                for (int off = 1; off < kWave; off <<= 1) {
+                    uint32_t n = __shfl_up(incl, off);
+                    if (lane >= off) incl += n;
+                }
+                if (lane == kWave - 1) s_scan[wave] = incl;
+            }
+            __syncthreads();
+            if (tid < 256) {
+                uint32_t base = 0;
+                for (int w = 0; w < wave; ++w) base += s_scan[w];
+                incl += base;
+                const uint32_t excl = incl - v;
+                if (excl < kr && kr <= incl) {
+                    s_digit = (uint32_t)(255 - tid);
+                    s_kr = kr - excl;
+                }
+            }
+            __syncthreads();
+            prefix |= s_digit << shift;
+            himask |= 0xFFu << shift;
+            kr = s_kr;
+        }
+    }
+    const uint32_t tau = (k > 0) ? prefix : 0xFFFFFFFFu;
+
+    // ---- Ordered pass: tie ranks, selection, compaction, outputs.
+    uint32_t eq_run = 0, sel_run = 0;
+    int buf = 0;
+    for (int64_t base = 0; base < d; base += NT) {
+        const int64_t j = base + tid;
+        const bool valid = j < d;
+        const uint32_t raw = valid ? raw_at(j) : 0u;
+        const uint32_t key = Elem<KK>::key(raw);
+        const bool gt = valid && k > 0 && key > tau;
+        const bool eq = valid && k > 0 && key == tau;
+        const uint64_t bgt = __ballot(gt);
+        const uint64_t beq = __ballot(eq);
+        if (lane == 0) {
+            s_gt[buf][wave] = (uint32_t)__popcll(bgt);
+            s_eq[buf][wave] = (uint32_t)__popcll(beq);
+        }
+        __syncthreads();
+        uint32_t eq_before = eq_run, sel_before = sel_run;
+        uint32_t my_eq = 0, my_sel = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const uint32_t g = s_gt[buf][w], e = s_eq[buf][w];
+            const uint32_t take = kr > eq_before ? min(e, kr - eq_before) : 0u;
+            if (w == wave) { my_eq = eq_before; my_sel = sel_before; }
+            eq_before += e;
+            sel_before += g + take;
+        }
+        const uint32_t eq_rank = my_eq + popc_below(beq);
+        const bool sel = gt || (eq && eq_rank < kr);
+        const uint64_t bsel = __ballot(sel);
+        if (valid) {
+            const uint32_t pos = my_sel + popc_below(bsel);
+            if (a.mask != nullptr) a.mask[row0 + j] = sel ? 1 : 0;
+            if constexpr (XK != XS_NONE)
+                if (a.xs != nullptr) store_xs<KK, XK>(a.xs, row0 + j, raw, sel);
+            if (sel && pos < (uint32_t)k && a.idx != nullptr) a.idx[(int64_t)r * a.idx_stride + pos] = (int32_t)j;
+            if (eq && eq_rank + 1 == kr && a.cutoff != nullptr) a.cutoff[r] = (int32_t)(j + 1);
+        }
+        eq_run = eq_before;
+        sel_run = sel_before;
+        buf ^= 1;
+    }
+    if (tid == 0) {
+        if (a.tau != nullptr) a.tau[r] = tau;
+        if (k == 0 && a.cutoff != nullptr) a.cutoff[r] = 0;
+        if (a.count != nullptr) a.count[r] = (int32_t)k;
+    }
+}
+
+template <int NT, int KK, int XK>
+hipError_t launch_kkx(int64_t rows, const TopkArgs& a, hipStream_t stream) {
+    if (a.d <= kStageMaxD) {
+        size_t smem = (size_t)a.d * sizeof(uint32_t);
+        topk_rows_kernel<NT, KK, XK, true><<<dim3((unsigned)rows), dim3(NT), smem, stream>>>(a);
+    } else {
+        topk_rows_kernel<NT, KK, XK, false><<<dim3((unsigned)rows), dim3(NT), 0, stream>>>(a);
+    }
+    return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_nt(int key_kind, int xs_kind, int64_t rows, const TopkArgs& a,
+                     hipStream_t stream) {
+    switch (key_kind) {
+    case KEY_F32:
+        if (xs_kind == XS_NONE) return launch_kkx<NT, KEY_F32, XS_NONE>(rows, a, stream);
+        if (xs_kind == XS_F32) return launch_kkx<NT, KEY_F32, XS_F32>(rows, a, stream);
+        break;
+    case KEY_BF16:
+        if (xs_kind == XS_NONE) return launch_kkx<NT, KEY_BF16, XS_NONE>(rows, a, stream);
+        if (xs_kind == XS_F32) return launch_kkx<NT, KEY_BF16, XS_F32>(rows, a, stream);
+        if (xs_kind == XS_BF16) return launch_kkx<NT, KEY_BF16, XS_BF16>(rows, a, stream);
+        break;
+    case KEY_I8:
+        if (xs_kind == XS_NONE) return launch_kkx<NT, KEY_I8, XS_NONE>(rows, a, stream);
+        break;
+    case KEY_Q8:
+        if (xs_kind == XS_I8) return launch_kkx<NT, KEY_Q8, XS_I8>(rows, a, stream);
+        if (xs_kind == XS_NONE) return launch_kkx<NT, KEY_Q8, XS_NONE>(rows, a, stream);
+        break;
+    }
+    return hipErrorInvalidValue;
+}
+
+__global__ void zero_i32_kernel(int32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_topk(int key_kind, int xs_kind, int64_t rows, const TopkArgs& a,
+                       hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    // Few rows (decode): one big workgroup per row; many rows: smaller ones.
+    if (rows <= 64) return launch_nt<1024>(key_kind, xs_kind, rows, a, stream);
+    return launch_nt<256>(key_kind, xs_kind, rows, a, stream);
+}
+
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    int blocks = (int)((n + 255) / 256);
+    if (blocks > 1024) blocks = 1024;
+    zero_i32_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(p, n);
+    return hipGetLastError();
+}
+
+}  // namespace qs

@@ -1,0 +1,148 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its argument validation, workspace sizing and host-side weight preparation
+behave as include/qs.h states.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import sparse_activation_amd as qs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qs.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qs_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qs.load()
+    names = _declared()
+    assert "qs_sparse_ffn" in names and len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "gfx950" in qs.qs_version()
+
+
+FAKE = ctypes.c_void_p(0x1000)          # never dereferenced: every call below fails validation
+MISALIGNED = ctypes.c_void_p(0x1004)
+
+
+def _status(call):
+    return call
+
+
+def test_topk_validation():
+    lib = qs.load()
+    assert lib.qs_topk_mask(FAKE, qs.F32, 2, 8, 9, None, None, None, None, None, None) == 1
+    assert lib.qs_topk_mask(FAKE, qs.F32, 2, 8, -1, None, None, None, None, None, None) == 1
+    assert lib.qs_topk_mask(FAKE, 7, 2, 8, 3, None, None, None, None, None, None) == 2
+    assert lib.qs_topk_mask(None, qs.F32, 2, 8, 3, None, None, None, None, None, None) == 1
+    assert lib.qs_topk_mask(MISALIGNED, qs.F32, 2, 8, 3, None, None, None, None, None,
+                            None) == 2
+    assert "aligned" in qs.qs_last_error()
+    assert lib.qs_topk_mask(FAKE, qs.I8, 2, 8, 3, None, None, None, None, FAKE, None) == 2
+    # rows == 0 is a no-op that touches nothing
+    assert lib.qs_topk_mask(None, qs.F32, 0, 8, 3, None, None, None, None, None, None) == 0
+    assert qs.qs_last_error() == ""
+
+
+def test_linear_validation_and_workspace():
+    lib = qs.load()
+    need = qs.qs_workspace_bytes(qs.OP_SPARSE_LINEAR, 4, 1024, 512)
+    assert need > 0
+    args = lambda **kw: dict(dict(x=FAKE, xt=qs.BF16, rows=4, d=1024, k=100, w=FAKE,
+                                  wt=qs.BF16, lay=qs.LAYOUT_WT, n=512, y=FAKE, yt=qs.F32,
+                                  ws=FAKE, wsb=need), **kw)
+
+    def call(a):
+        return lib.qs_sparse_linear(a["x"], a["xt"], a["rows"], a["d"], a["k"], a["w"],
+                                    a["wt"], a["lay"], a["n"], a["y"], a["yt"], a["ws"],
+                                    a["wsb"], None)
+    assert call(args(k=1025)) == 1
+    assert call(args(n=500)) == 2                      # n_out % 8 for bf16 weights
+    assert call(args(wsb=need - 1)) == 3
+    assert call(args(ws=None)) == 3
+    assert call(args(y=None)) == 1
+    assert call(args(w=MISALIGNED)) == 2
+    assert call(args(lay=qs.LAYOUT_W, xt=qs.F32, wt=qs.F32, n=512)) == 2
+    assert call(args(xt=qs.I8)) == 2
+    assert call(args(rows=0, x=None, w=None, y=None, ws=None)) == 0
+
+
+def test_gather_linear_validation():
+    lib = qs.load()
+    need = qs.qs_workspace_bytes(qs.OP_GATHER_LINEAR, 2, 512, 256)
+    assert need >= 16384
+    assert lib.qs_gather_linear(FAKE, 2, 512, FAKE, qs.BF16, 252, FAKE, qs.F32, FAKE, need,
+                                None) == 2
+    assert lib.qs_gather_linear(FAKE, 2, 512, FAKE, qs.BF16, 256, FAKE, qs.F32, FAKE, need - 1,
+                                None) == 3
+    assert lib.qs_gather_linear(None, 2, 512, FAKE, qs.BF16, 256, FAKE, qs.F32, FAKE, need,
+                                None) == 1
+
+
+def test_i8t_and_ffn_validation():
+    lib = qs.load()
+    need = qs.qs_workspace_bytes(qs.OP_SPARSE_LINEAR_I8T, 2, 256, 64)
+    assert lib.qs_sparse_linear_i8t(FAKE, 2, 256, 10, FAKE, ctypes.c_float(1.0), 60, None,
+                                    None, None, None, None, FAKE, need, None) == 2
+    assert lib.qs_sparse_linear_i8t(FAKE, 2, 256, 257, FAKE, ctypes.c_float(1.0), 64, None,
+                                    None, None, None, None, FAKE, need, None) == 1
+    need = qs.qs_workspace_bytes(qs.OP_SPARSE_FFN_DRELU, 2, 256, 512)
+    # dReLU needs bf16 and a gate; squared ReLU takes no gate
+    assert lib.qs_sparse_ffn(FAKE, qs.F32, 2, 256, 512, qs.ACT_DRELU, 256, -1, FAKE, FAKE, FAKE,
+                             None, None, FAKE, qs.F32, None, None, None, FAKE, need, None) == 2
+    assert lib.qs_sparse_ffn(FAKE, qs.BF16, 2, 256, 512, qs.ACT_DRELU, 256, -1, None, FAKE, FAKE,
+                             None, None, FAKE, qs.F32, None, None, None, FAKE, need, None) == 1
+    need = qs.qs_workspace_bytes(qs.OP_SPARSE_FFN_RELU2, 2, 256, 512)
+    assert lib.qs_sparse_ffn(FAKE, qs.BF16, 2, 256, 512, qs.ACT_RELU2, 100, 513, None, FAKE,
+                             FAKE, None, None, FAKE, qs.F32, None, None, None, FAKE, need,
+                             None) == 1
+    assert lib.qs_sparse_ffn(FAKE, qs.BF16, 2, 256, 512, qs.ACT_RELU2, 100, 50, FAKE, FAKE,
+                             FAKE, None, None, FAKE, qs.F32, None, None, None, FAKE, need,
+                             None) == 1
+
+
+def test_workspace_sizes_depend_on_shape_only():
+    for op in (qs.OP_SPARSE_LINEAR, qs.OP_SPARSE_LINEAR_I8T, qs.OP_SPARSE_FFN_RELU2,
+               qs.OP_SPARSE_FFN_DRELU):
+        a = qs.qs_workspace_bytes(op, 16, 4096, 11008)
+        b = qs.qs_workspace_bytes(op, 16, 4096, 11008)
+        assert a == b and a % 256 == 0
+    assert qs.qs_workspace_bytes(qs.OP_TOPK_MASK, 16, 4096, 0) == 0
+    with pytest.raises(qs.QSError):
+        qs.qs_workspace_bytes(99, 1, 1, 1)
+
+
+def test_ternarize_matches_oracle_bit_exactly():
+    rng = np.random.default_rng(31)
+    for shape in [(4, 8), (33, 64), (128, 96)]:
+        w = rng.normal(0, 0.02, size=shape).astype(np.float32)
+        w[0, 0] = 0.0
+        t_lib, a_lib = qs.qs_ternarize(w)
+        t_ref, a_ref = oracle.ternarize(w)
+        assert np.float32(a_lib) == a_ref
+        assert np.array_equal(t_lib, t_ref)
+
+
+def test_ternarize_extreme_magnitudes():
+    w = np.array([[1e-40, -3e38, 2.5e-3, 0.0], [7.0, -1e-45, 3e38, 1.0]], dtype=np.float32)
+    t_lib, a_lib = qs.qs_ternarize(w)
+    t_ref, a_ref = oracle.ternarize(w)
+    assert np.float32(a_lib) == a_ref and np.array_equal(t_lib, t_ref)
+
+
+def test_pack_ternary_roundtrip_through_oracle_decoder():
+    rng = np.random.default_rng(37)
+    t = rng.integers(-1, 2, size=(64, 40)).astype(np.int8)
+    packed = qs.qs_pack_ternary(t)
+    assert packed.shape == (40, 16)
+    assert np.array_equal(oracle.unpack_ternary(packed, 64), t)
+    with pytest.raises(qs.QSError):
+        qs.qs_pack_ternary(np.full((4, 4), 2, dtype=np.int8))

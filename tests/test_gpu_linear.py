@@ -1,0 +1,131 @@
+"""GPU parity of the sparse-activation linear Y = (X (.) M) . W^T.
+
+Tolerances (fp32 accumulation of exact products): |y - y_ref| <= 1e-5 * T for
+fp32 inputs and <= 4e-3 * T for bf16 inputs (which also covers a bf16 output
+rounding), T = sum over selected j of |x_j w_j|; T == 0 requires y == 0.
+Integer-valued inputs make every partial sum exact, so there the result must
+be bit-exact whatever the reduction order.
+"""
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+from gpu_util import assert_within, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(gpu_lib, x, k, w, xdt, wdt, ydt, layout=None):
+    import torch
+    qs = gpu_lib
+    layout = qs.LAYOUT_WT if layout is None else layout
+    xd = to_dev(x, xdt)
+    wd = to_dev(np.ascontiguousarray(w.T) if layout == qs.LAYOUT_WT else w, wdt)
+    y = qs.qs_sparse_linear(xd, k, wd, layout=layout, y_dtype=ydt)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy()
+
+
+def _ref(x, k, w):
+    mask, _, _, _ = oracle.topk_select(oracle.magnitude(x), k)
+    return oracle.sparse_linear(x, w, mask)
+
+
+@pytest.mark.parametrize("wtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,d,n", [(1, 64, 8), (3, 300, 264), (8, 1024, 1024),
+                                      (20, 700, 520), (37, 256, 128), (1, 4096, 11008)])
+def test_linear_random(gpu_lib, wtype, rows, d, n):
+    import torch
+    rng = np.random.default_rng(rows * 7 + d + n)
+    x = datagen.student_t(rng, (rows, d))
+    w = datagen.normal(rng, (n, d), 0.02)
+    dt = torch.float32 if wtype == "f32" else torch.bfloat16
+    if wtype == "bf16":
+        x, w = datagen.bf16_round(x), datagen.bf16_round(w)
+    tol = 1e-5 if wtype == "f32" else 4e-3
+    for k in sorted({0, 1, (2 * d) // 5, d}):
+        note(f"linear {wtype} rows={rows} d={d} n={n} k={k}")
+        y = _run(gpu_lib, x, k, w, dt, dt, torch.float32)
+        y_ref, t = _ref(x, k, w)
+        assert_within(y, y_ref, t, tol, f"linear {wtype} k={k}")
+
+
+@pytest.mark.parametrize("wtype", ["f32", "bf16"])
+def test_linear_integer_valued_is_exact(gpu_lib, wtype):
+    import torch
+    rng = np.random.default_rng(41)
+    rows, d, n = 6, 2000, 776
+    x = rng.integers(-30, 31, size=(rows, d)).astype(np.float32)
+    w = rng.integers(-3, 4, size=(n, d)).astype(np.float32)
+    dt = torch.float32 if wtype == "f32" else torch.bfloat16
+    note(f"linear integer-valued {wtype}")
+    y = _run(gpu_lib, x, 900, w, dt, dt, torch.float32)
+    y_ref, _ = _ref(x, 900, w)
+    assert np.array_equal(y, y_ref)
+
+
+def test_linear_bf16_output_and_dense_k(gpu_lib):
+    import torch
+    rng = np.random.default_rng(43)
+    x = datagen.bf16_round(datagen.student_t(rng, (4, 512)))
+    w = datagen.bf16_round(datagen.normal(rng, (256, 512), 0.02))
+    note("linear bf16 output, k = d")
+    y = _run(gpu_lib, x, 512, w, torch.bfloat16, torch.bfloat16, torch.bfloat16)
+    y_ref = x.astype(np.float64) @ w.astype(np.float64).T       # K = D: the dense product
+    t = np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T
+    assert_within(y, y_ref, t, 4e-3, "bf16 out")
+
+
+def test_linear_deterministic(gpu_lib):
+    import torch
+    rng = np.random.default_rng(47)
+    x = datagen.bf16_round(datagen.student_t(rng, (5, 4096)))
+    w = datagen.bf16_round(datagen.normal(rng, (4096, 4096), 0.02))
+    note("linear run-twice determinism")
+    y1 = _run(gpu_lib, x, 1638, w, torch.bfloat16, torch.bfloat16, torch.float32)
+    y2 = _run(gpu_lib, x, 1638, w, torch.bfloat16, torch.bfloat16, torch.float32)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_linear_full_c1(gpu_lib):
+    import torch
+    c = datagen.c1_linear()
+    note("linear full config C1 fp32 [8,1024] x [1024,1024], K=410")
+    y = _run(gpu_lib, c["X"], c["K"], c["W"], torch.float32, torch.float32, torch.float32)
+    y_ref, t = _ref(c["X"], c["K"], c["W"])
+    assert_within(y, y_ref, t, 1e-5, "C1")
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4, 8, 16])
+def test_linear_full_c2_up(gpu_lib, batch):
+    """The Llama-7B FFN up projection at decode batch sizes (bf16, K = 1638)."""
+    import torch
+    c = datagen.c2_relu2_ffn(batch)
+    note(f"linear C2 up projection B={batch}")
+    y = _run(gpu_lib, c["X"], c["K_in"], c["W_up"], torch.bfloat16, torch.bfloat16, torch.float32)
+    y_ref, t = _ref(c["X"], c["K_in"], c["W_up"])
+    assert_within(y, y_ref, t, 4e-3, f"C2 up B={batch}")
+
+
+def test_topk_xs_and_gather_linear(gpu_lib):
+    """qs_topk_mask's xs output is X (.) M, and qs_gather_linear on it gives the
+    same product (workspace reused across calls, counters left zero)."""
+    import torch
+    qs = gpu_lib
+    rng = np.random.default_rng(59)
+    ws = None
+    for rows, d, n, k in [(3, 1000, 520, 400), (16, 4096, 1024, 1638), (1, 300, 64, 7)]:
+        x = datagen.bf16_round(datagen.student_t(rng, (rows, d)))
+        w = datagen.bf16_round(datagen.normal(rng, (n, d), 0.02))
+        note(f"gather_linear rows={rows} d={d} n={n} k={k}")
+        mask, _, _, _, xs = qs.qs_topk_mask(to_dev(x, torch.bfloat16), k, want_xs=True)
+        if ws is None or ws.numel() < qs.qs_workspace_bytes(qs.OP_GATHER_LINEAR, rows, d, n):
+            ws = qs.gather_workspace(16, 4096, 1024)
+        y = qs.qs_gather_linear(xs, to_dev(np.ascontiguousarray(w.T), torch.bfloat16), ws=ws)
+        torch.cuda.synchronize()
+        m_ref, _, _, _ = oracle.topk_select(oracle.magnitude(x), k)
+        assert np.array_equal(xs.cpu().numpy(), np.where(m_ref == 1, x, 0.0).astype(np.float32))
+        y_ref, t = oracle.sparse_linear(x, w, m_ref)
+        assert_within(y.cpu().numpy(), y_ref, t, 4e-3, "gather_linear")
+        assert int(ws[:16384].count_nonzero()) == 0, "split-K counters must be left zero"
