@@ -51,10 +51,9 @@ struct Carve {
 
 struct LinearWs {
     int32_t* counters;
-    float* xs;
+    float* xs;          // gather path: X (.) M in fp32
     float* partial;
-    uint32_t* tau;
-    int32_t* cutoff;
+    uint16_t* xm;       // MFMA path: X (.) M in bf16
     size_t bytes;
 };
 
@@ -69,8 +68,7 @@ LinearWs linear_ws(char* base, int64_t rows, int64_t d_in, int64_t n_out) {
     w.counters = (int32_t*)c.take(sizeof(int32_t) * (size_t)(pb.n_counters > pf.n_counters ? pb.n_counters : pf.n_counters));
     w.xs = (float*)c.take(sizeof(float) * (size_t)rows * d_in);
     w.partial = (float*)c.take(sizeof(float) * max_sz(pb.partial_floats, pf.partial_floats));
-    w.tau = (uint32_t*)c.take(sizeof(uint32_t) * (size_t)rows);
-    w.cutoff = (int32_t*)c.take(sizeof(int32_t) * (size_t)rows);
+    w.xm = (uint16_t*)c.take(sizeof(uint16_t) * (size_t)rows * d_in);
     w.bytes = c.off;
     return w;
 }
@@ -236,6 +234,8 @@ qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_i
         if (n_out % (wt_t == QS_BF16 ? 8 : 4) != 0)
             return fail(QS_ERR_UNSUPPORTED, "%s: n_out must be a multiple of %d", fn,
                         wt_t == QS_BF16 ? 8 : 4);
+        if (d_in * n_out * (wt_t == QS_BF16 ? 2 : 4) >= qs::kMaxGatherWeightBytes)
+            return fail(QS_ERR_UNSUPPORTED, "%s: W^T must be smaller than 1 GiB", fn);
     }
     if (rows == 0) return ok();
     if (!x || !w || !y) return fail(QS_ERR_INVALID_ARG, "%s: x, w and y must be non-NULL", fn);
@@ -249,13 +249,14 @@ qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_i
     const int kk = xt == QS_F32 ? qs::KEY_F32 : qs::KEY_BF16;
     hipError_t e;
     if (w_layout == QS_LAYOUT_W) {
+        // Top-K writes X (.) M in bf16; the dense MFMA GEMM then reads it.
         qs::TopkArgs t{};
         t.x = x; t.d = d_in; t.k = k; t.idx_stride = k;
-        t.tau = wsp.tau; t.cutoff = wsp.cutoff;
-        e = qs::launch_topk(kk, qs::XS_NONE, rows, t, st);
+        t.xs = wsp.xm;
+        e = qs::launch_topk(kk, qs::XS_BF16, rows, t, st);
         if (e != hipSuccess) return hip_fail(e, fn);
         qs::MfmaArgs m{};
-        m.x = (const uint16_t*)x; m.tau = wsp.tau; m.cutoff = wsp.cutoff;
+        m.x = wsp.xm;
         m.w = (const uint16_t*)w; m.m = rows; m.n = n_out; m.k = d_in;
         m.y = y; m.y_bf16 = yt == QS_BF16;
         e = qs::launch_masked_gemm(m, st);
@@ -290,6 +291,8 @@ qs_status qs_gather_linear(const float* xs, int64_t rows, int64_t d_in, const vo
     if (n_out % (wt_t == QS_BF16 ? 8 : 4) != 0)
         return fail(QS_ERR_UNSUPPORTED, "%s: n_out must be a multiple of %d", fn,
                     wt_t == QS_BF16 ? 8 : 4);
+    if (d_in * n_out * (wt_t == QS_BF16 ? 2 : 4) >= qs::kMaxGatherWeightBytes)
+        return fail(QS_ERR_UNSUPPORTED, "%s: W^T must be smaller than 1 GiB", fn);
     if (rows > 0x7FFFFFFF) return fail(QS_ERR_UNSUPPORTED, "%s: too many rows", fn);
     if (rows == 0) return ok();
     if (!xs || !wt || !y) return fail(QS_ERR_INVALID_ARG, "%s: xs, wt and y must be non-NULL", fn);
@@ -322,6 +325,8 @@ qs_status qs_sparse_linear_i8t(const float* x, int64_t rows, int64_t d_in, int64
         return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
     if (k < 0 || k > d_in) return fail(QS_ERR_INVALID_ARG, "%s: need 0 <= k <= d_in", fn);
     if (n_out % 16 != 0) return fail(QS_ERR_UNSUPPORTED, "%s: n_out must be a multiple of 16", fn);
+    if (d_in * (n_out / 4) >= qs::kMaxGatherWeightBytes)
+        return fail(QS_ERR_UNSUPPORTED, "%s: packed W^T must be smaller than 1 GiB", fn);
     if (rows > 0x7FFFFFFF) return fail(QS_ERR_UNSUPPORTED, "%s: too many rows", fn);
     if (rows == 0) return ok();
     if (!x || !wt_packed) return fail(QS_ERR_INVALID_ARG, "%s: x and wt_packed must be non-NULL", fn);
@@ -370,6 +375,8 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
         return fail(QS_ERR_UNSUPPORTED, "%s: dReLU path needs bf16 x and weights", fn);
     if (d % 8 != 0 || ffn % 8 != 0)
         return fail(QS_ERR_UNSUPPORTED, "%s: d and ffn must be multiples of 8", fn);
+    if (d * ffn * (dt == QS_BF16 ? 2 : 4) >= qs::kMaxGatherWeightBytes)
+        return fail(QS_ERR_UNSUPPORTED, "%s: each weight matrix must be smaller than 1 GiB", fn);
     if (rows > 0x7FFFFFFF) return fail(QS_ERR_UNSUPPORTED, "%s: too many rows", fn);
     if (rows == 0) return ok();
     if (!x || !w_up || !w_down_t || !y)

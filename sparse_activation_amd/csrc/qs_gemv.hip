@@ -24,6 +24,8 @@
 //
 // The ternary x int8 variant does the same with 2-bit packed weights and
 // exact int32 accumulation.
+#include <cstdlib>
+
 #include "qs_internal.h"
 
 namespace qs {
@@ -33,13 +35,62 @@ constexpr int kNT = 256;     // threads per workgroup
 constexpr int kLPR = 32;     // lanes per weight-row segment
 constexpr int kRPI = 64 / kLPR;
 constexpr int kNSlot = 4 * kRPI;
-constexpr int kUnroll = 4;
-constexpr int kTargetWG = 1024;
+constexpr int kUnroll = 4;       // rows per pipeline stage per lane (ternary kernel)
+constexpr int kMaxUnroll = 8;    // the fp kernel uses 8 for small token tiles
+
+// Workgroups the split-K plan aims for.  QS_GEMV_TARGET_WG overrides it (read
+// once per process; a tuning knob for measurements).
+int target_wg() {
+    static const int v = [] {
+        const char* e = getenv("QS_GEMV_TARGET_WG");
+        int t = e ? atoi(e) : 0;
+        return t > 0 ? t : 384;
+    }();
+    return v;
+}
 
 __device__ __forceinline__ uint32_t popc_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
+
+// Split-K handoff between workgroups that may sit on different XCDs (each
+// with its own L2): partials are written and read with relaxed agent-scope
+// atomics, which the compiler emits as sc1 stores/loads that bypass the
+// non-coherent L2 state, so no L2 writeback/invalidate fence is needed.
+// s_waitcnt vmcnt(0) (0x0F70) makes this wave's stores complete before the
+// workgroup barrier and the counter increment.
+template <typename T>
+__device__ __forceinline__ void store_agent(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T load_agent(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Returns true in every thread of the last workgroup to finish its split.
+__device__ __forceinline__ bool last_split_arrived(int32_t* counter, int nsplit, int* s_flag) {
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *s_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+    __syncthreads();
+    return *s_flag != 0;
+}
+
+// Raw buffer view of a weight matrix: out-of-range offsets read as zero.
+// Weight matrices are below 1 GiB (checked by the host), so an offset with
+// either part set to kOOB is out of range, and the sum cannot wrap.
+constexpr uint32_t kOOB = 0x40000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const void* p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t b = __float_as_uint(f);
@@ -48,7 +99,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 template <int WBF16>
-__device__ __forceinline__ void unpack(const uint4& v, float* w) {
+__device__ __forceinline__ void unpack(const u32x4& v, float* w) {
     if constexpr (WBF16) {
         const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -79,9 +130,11 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
     constexpr int EPT = WBF16 ? 8 : 4;
     constexpr int CT = kLPR * EPT;
     constexpr int TG = BT < 2 ? BT : 2;
+    constexpr int U = BT <= 4 ? kMaxUnroll : kUnroll;   // rows per stage per lane
+    constexpr int BATCH = kNSlot * U;                    // rows per pipeline stage
     extern __shared__ float smem[];
-    float* s_coef = smem;                                  // [cand][BT]
-    int* s_act = reinterpret_cast<int*>(smem + (size_t)cand * BT);   // [cand]
+    float* s_coef = smem;                                  // [cand + 3 BATCH][BT]
+    uint32_t* s_off = reinterpret_cast<uint32_t*>(smem + (size_t)(cand + 3 * BATCH) * BT);
     __shared__ int s_wcnt[4];
     __shared__ int s_last;
 
@@ -92,19 +145,28 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
     const int64_t j1 = min(d_in, j0 + (int64_t)cand);
     const int64_t tok0 = (int64_t)tt * BT;
 
-    // Phase A: selected candidate rows (union over the token tile), ascending.
+    const int64_t esize = WBF16 ? 2 : 4;
+    const uint32_t rowbytes = (uint32_t)(n_out * esize);
+
+    // Phase A: selected candidate rows (union over the token tile), ascending;
+    // s_off holds their byte offsets in W^T and s_coef their coefficients.
+    // Coefficients come through a buffer view of this token tile's rows of xs,
+    // so the BT loads are issued together (rows past the batch read 0).
+    const int64_t ntok = min((int64_t)BT, rows - tok0);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.xs + tok0 * d_in), (short)0, (int)(ntok * d_in * 4), 0x00020000);
     int nact = 0;
     for (int64_t c0 = j0; c0 < j1; c0 += kNT) {
         const int64_t j = c0 + tid;
+        const bool jin = j < j1;
         float c[BT];
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+            c[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                xr, jin ? (uint32_t)((t * d_in + j) * 4) : kOOB, 0, 0));
         bool any = false;
 #pragma unroll
-        for (int t = 0; t < BT; ++t) {
-            float v = 0.0f;
-            if (j < j1 && tok0 + t < rows) v = a.xs[(tok0 + t) * d_in + j];
-            c[t] = v;
-            any = any || (v != 0.0f);
-        }
+        for (int t = 0; t < BT; ++t) any = any || (c[t] != 0.0f);
         const uint64_t b = __ballot(any);
         if (lane == 0) s_wcnt[wave] = (int)__popcll(b);
         __syncthreads();
@@ -116,21 +178,29 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
         }
         if (any) {
             const int pos = before + (int)popc_below(b);
-            s_act[pos] = (int)j;
+            s_off[pos] = (uint32_t)j * rowbytes;
 #pragma unroll
             for (int t = 0; t < BT; ++t) s_coef[pos * BT + t] = c[t];
         }
         nact = total;
         __syncthreads();
     }
+    // Pad the list with rows that read as zero up to an even number of
+    // pipeline stages plus the one stage that the last iteration prefetches.
+    const int nbatch = (nact + BATCH - 1) / BATCH;
+    const int npad = ((nbatch + 1) / 2 * 2 + 1) * BATCH;
+    for (int i = nact + tid; i < npad; i += kNT) {
+        s_off[i] = kOOB;
+#pragma unroll
+        for (int t = 0; t < BT; ++t) s_coef[i * BT + t] = 0.0f;
+    }
+    __syncthreads();
 
-    // Phase B: stream the selected W^T row segments.
+    // Phase B: stream the selected W^T row segments, one stage ahead.
     const int slot = wave * kRPI + lane / kLPR;
     const int64_t col = (int64_t)tile * CT + (lane % kLPR) * EPT;
-    const bool colok = col < n_out;
-    const int64_t esize = WBF16 ? 2 : 4;
-    const char* wcol = reinterpret_cast<const char*>(a.w) + col * esize;
-    const int64_t rowbytes = n_out * esize;
+    const uint32_t colb = col < n_out ? (uint32_t)(col * esize) : kOOB;
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, a.d_in * (int64_t)rowbytes);
 
     float acc[BT][EPT];
 #pragma unroll
@@ -138,32 +208,45 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
 #pragma unroll
         for (int e = 0; e < EPT; ++e) acc[t][e] = 0.0f;
 
-    for (int a0 = slot; a0 < nact; a0 += kNSlot * kUnroll) {
-        uint4 wv[kUnroll];
+    // Two register buffers in ping-pong (no copies, so the waits on one stage
+    // never cover the loads of the next): 2 * U rows in flight per lane.
+    u32x4 bufa[U], bufb[U];
+    auto load_stage = [&](u32x4* dst, int bi) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int ai = a0 + u * kNSlot;
-            if (ai < nact && colok)
-                wv[u] = *reinterpret_cast<const uint4*>(wcol + (int64_t)s_act[ai] * rowbytes);
-            else
-                wv[u] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int u = 0; u < U; ++u)
+            dst[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, s_off[bi * BATCH + slot + u * kNSlot] + colb, 0, 0);
+    };
+    auto fma_stage = [&](const u32x4* src, int bi) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int ai = a0 + u * kNSlot;
-            if (ai < nact) {
-                float w[EPT];
-                unpack<WBF16>(wv[u], w);
+        for (int u = 0; u < U; ++u) {
+            float w[EPT];
+            unpack<WBF16>(src[u], w);
+            const int ai = bi * BATCH + slot + u * kNSlot;
 #pragma unroll
-                for (int t = 0; t < BT; ++t) {
-                    const float c = s_coef[ai * BT + t];
+            for (int t = 0; t < BT; ++t) {
+                const float c = s_coef[ai * BT + t];
 #pragma unroll
-                    for (int e = 0; e < EPT; ++e) acc[t][e] = fmaf(c, w[e], acc[t][e]);
-                }
+                for (int e = 0; e < EPT; ++e) acc[t][e] = fmaf(c, w[e], acc[t][e]);
             }
         }
+    };
+    // Straight-line body: stages past the list hold out-of-range offsets and
+    // zero coefficients, so their loads return zero without memory traffic.
+    // sched_barrier keeps each stage's loads issued before the previous
+    // stage's arithmetic (the scheduler would otherwise sink them).
+    load_stage(bufa, 0);
+    for (int bi = 0; bi < nbatch; bi += 2) {
+        load_stage(bufb, bi + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        fma_stage(bufa, bi);
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage(bufa, bi + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        fma_stage(bufb, bi + 1);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();   // s_coef / s_act are dead from here: reuse as the reduction buffer
+    __syncthreads();   // s_coef / s_off are dead from here: reuse as the reduction buffer
 
     // Phase C: sum the row slots in slot order, token group by token group.
     float* s_red = smem;   // [kNSlot][TG][CT]
@@ -183,7 +266,7 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
             const int64_t cg = (int64_t)tile * CT + (o % CT);
             if (row < rows && cg < n_out) {
                 if (nsplit == 1) store_final(a, row * n_out + cg, s);
-                else a.partial[((int64_t)split * rows + row) * n_out + cg] = s;
+                else store_agent(&a.partial[((int64_t)split * rows + row) * n_out + cg], s);
             }
         }
         __syncthreads();
@@ -191,24 +274,29 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
 
     // Phase D: the last split of this tile sums the partials in split order.
     if (nsplit > 1) {
-        __threadfence();
-        __syncthreads();
         const int ci = tt * gridDim.x + tile;
-        if (tid == 0) s_last = (atomicAdd(&a.counters[ci], 1) == nsplit - 1);
-        __syncthreads();
-        if (s_last) {
-            __threadfence();
+        if (last_split_arrived(&a.counters[ci], nsplit, &s_last)) {
             for (int o = tid; o < BT * CT; o += kNT) {
                 const int64_t row = tok0 + o / CT;
                 const int64_t cg = (int64_t)tile * CT + (o % CT);
                 if (row < rows && cg < n_out) {
+                    // 16 independent loads in flight, summed in split order.
+                    const float* pp = a.partial + row * n_out + cg;
+                    const int64_t stride = rows * n_out;
                     float s = 0.0f;
-                    for (int sp = 0; sp < nsplit; ++sp)
-                        s += a.partial[((int64_t)sp * rows + row) * n_out + cg];
+                    for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
+                        float v[16];
+#pragma unroll
+                        for (int u = 0; u < 16; ++u)
+                            v[u] = sp0 + u < nsplit ? load_agent(pp + (int64_t)(sp0 + u) * stride) : 0.0f;
+#pragma unroll
+                        for (int u = 0; u < 16; ++u)
+                            if (sp0 + u < nsplit) s += v[u];
+                    }
                     store_final(a, row * n_out + cg, s);
                 }
             }
-            if (tid == 0) a.counters[ci] = 0;
+            if (tid == 0) store_agent(&a.counters[ci], 0);
         }
     }
 }
@@ -229,9 +317,10 @@ constexpr int kI8TargetWG = 512;
 
 template <int BT>
 __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int nsplit) {
+    constexpr int BATCH = kNSlot * kUnroll;
     extern __shared__ int ismem[];
-    int* s_coef = ismem;                        // [cand][BT]
-    int* s_act = ismem + (size_t)cand * BT;     // [cand]
+    int* s_coef = ismem;                                                   // [cand+3 BATCH][BT]
+    uint32_t* s_off = reinterpret_cast<uint32_t*>(ismem + (size_t)(cand + 3 * BATCH) * BT);
     __shared__ int s_wcnt[4];
     __shared__ int s_last;
 
@@ -242,18 +331,22 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
     const int64_t j1 = min(d_in, j0 + (int64_t)cand);
     const int64_t tok0 = (int64_t)tt * BT;
 
+    const uint32_t rowbytes = (uint32_t)(n_out / 4);
+    const int64_t ntok = min((int64_t)BT, rows - tok0);
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(a.qs + tok0 * d_in), (short)0, (int)(ntok * d_in), 0x00020000);
     int nact = 0;
     for (int64_t c0 = j0; c0 < j1; c0 += kNT) {
         const int64_t j = c0 + tid;
+        const bool jin = j < j1;
         int c[BT];
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+            c[t] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(
+                qr, jin ? (uint32_t)(t * d_in + j) : kOOB, 0, 0);
         bool any = false;
 #pragma unroll
-        for (int t = 0; t < BT; ++t) {
-            int v = 0;
-            if (j < j1 && tok0 + t < rows) v = a.qs[(tok0 + t) * d_in + j];
-            c[t] = v;
-            any = any || (v != 0);
-        }
+        for (int t = 0; t < BT; ++t) any = any || (c[t] != 0);
         const uint64_t b = __ballot(any);
         if (lane == 0) s_wcnt[wave] = (int)__popcll(b);
         __syncthreads();
@@ -265,20 +358,29 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
         }
         if (any) {
             const int pos = before + (int)popc_below(b);
-            s_act[pos] = (int)j;
+            s_off[pos] = (uint32_t)j * rowbytes;
 #pragma unroll
             for (int t = 0; t < BT; ++t) s_coef[pos * BT + t] = c[t];
         }
         nact = total;
         __syncthreads();
     }
+    const int nbatch = (nact + BATCH - 1) / BATCH;
+    const int npad = ((nbatch + 1) / 2 * 2 + 1) * BATCH;
+    for (int i = nact + tid; i < npad; i += kNT) {
+        s_off[i] = kOOB;
+#pragma unroll
+        for (int t = 0; t < BT; ++t) s_coef[i * BT + t] = 0;
+    }
+    __syncthreads();
 
     const int slot = wave * kRPI + lane / kLPR;
     const int64_t col = (int64_t)tile * kI8CT + (lane % kLPR) * kI8EPT;
-    const bool colok = col < n_out;
-    const bool col2ok = col + 16 < n_out;     // n_out % 16 == 0: second word present
-    const int64_t rowbytes = n_out / 4;
-    const uint8_t* wcol = a.wt + col / 4;
+    // Rows are only 4-byte aligned when n_out % 32 != 0: two dword loads; the
+    // second is out of range (zero) for the last 16 columns of such a row.
+    const uint32_t colb = col < n_out ? (uint32_t)(col / 4) : kOOB;
+    const uint32_t colb2 = col + 16 < n_out ? (uint32_t)(col / 4 + 4) : kOOB;
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.wt, a.d_in * (int64_t)rowbytes);
 
     int acc[BT][kI8EPT];
 #pragma unroll
@@ -286,37 +388,46 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
 #pragma unroll
         for (int e = 0; e < kI8EPT; ++e) acc[t][e] = 0;
 
-    for (int a0 = slot; a0 < nact; a0 += kNSlot * kUnroll) {
-        uint2 wv[kUnroll];
+    u32x2 bufa[kUnroll], bufb[kUnroll];
+    auto load_stage = [&](u32x2* dst, int bi) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int ai = a0 + u * kNSlot;
-            // Two 4-byte loads: rows are only 4-byte aligned when n_out % 32 != 0.
-            wv[u] = make_uint2(0u, 0u);
-            if (ai < nact && colok) {
-                const uint32_t* p =
-                    reinterpret_cast<const uint32_t*>(wcol + (int64_t)s_act[ai] * rowbytes);
-                wv[u].x = p[0];
-                if (col2ok) wv[u].y = p[1];
-            }
+            const uint32_t ro = s_off[bi * BATCH + slot + u * kNSlot];
+            dst[u].x = __builtin_amdgcn_raw_buffer_load_b32(rs, ro + colb, 0, 0);
+            dst[u].y = __builtin_amdgcn_raw_buffer_load_b32(rs, ro + colb2, 0, 0);
         }
+    };
+    auto mac_stage = [&](const u32x2* src, int bi) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int ai = a0 + u * kNSlot;
-            if (ai < nact) {
-                int c[BT];
+            const int ai = bi * BATCH + slot + u * kNSlot;
+            int c[BT];
 #pragma unroll
-                for (int t = 0; t < BT; ++t) c[t] = s_coef[ai * BT + t];
+            for (int t = 0; t < BT; ++t) c[t] = s_coef[ai * BT + t];
 #pragma unroll
-                for (int e = 0; e < kI8EPT; ++e) {
-                    const uint32_t word = e < 16 ? wv[u].x : wv[u].y;
-                    // 2-bit two's complement field: 00 -> 0, 01 -> +1, 11 -> -1
-                    const int tv = __builtin_amdgcn_sbfe((int)word, (2 * e) & 31, 2);
+            for (int e = 0; e < kI8EPT; ++e) {
+                const uint32_t word = e < 16 ? src[u].x : src[u].y;
+                // 2-bit two's complement field: 00 -> 0, 01 -> +1, 11 -> -1
+                const int tv = __builtin_amdgcn_sbfe((int)word, (2 * e) & 31, 2);
 #pragma unroll
-                    for (int t = 0; t < BT; ++t) acc[t][e] += c[t] * tv;
-                }
+                for (int t = 0; t < BT; ++t) acc[t][e] += c[t] * tv;
             }
         }
+    };
+    // Straight-line body: stages past the list hold out-of-range offsets and
+    // zero coefficients, so their loads return zero without memory traffic.
+    // sched_barrier keeps each stage's loads issued before the previous
+    // stage's arithmetic (the scheduler would otherwise sink them).
+    load_stage(bufa, 0);
+    for (int bi = 0; bi < nbatch; bi += 2) {
+        load_stage(bufb, bi + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mac_stage(bufa, bi);
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage(bufa, bi + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mac_stage(bufb, bi + 1);
+        __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
 
@@ -340,7 +451,7 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
                     if (a.y) a.y[row * n_out + cg] =
                         __fmul_rn((float)s, __fdiv_rn(a.alpha, a.xscale[row]));
                 } else {
-                    a.partial[((int64_t)split * rows + row) * n_out + cg] = s;
+                    store_agent(&a.partial[((int64_t)split * rows + row) * n_out + cg], s);
                 }
             }
         }
@@ -348,26 +459,29 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
     }
 
     if (nsplit > 1) {
-        __threadfence();
-        __syncthreads();
         const int ci = tt * gridDim.x + tile;
-        if (tid == 0) s_last = (atomicAdd(&a.counters[ci], 1) == nsplit - 1);
-        __syncthreads();
-        if (s_last) {
-            __threadfence();
+        if (last_split_arrived(&a.counters[ci], nsplit, &s_last)) {
             for (int o = tid; o < BT * kI8CT; o += kNT) {
                 const int64_t row = tok0 + o / kI8CT;
                 const int64_t cg = (int64_t)tile * kI8CT + (o % kI8CT);
                 if (row < rows && cg < n_out) {
+                    const int32_t* pp = a.partial + row * n_out + cg;
+                    const int64_t stride = rows * n_out;
                     int s = 0;
-                    for (int sp = 0; sp < nsplit; ++sp)
-                        s += a.partial[((int64_t)sp * rows + row) * n_out + cg];
+                    for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
+                        int v[16];
+#pragma unroll
+                        for (int u = 0; u < 16; ++u)
+                            v[u] = sp0 + u < nsplit ? load_agent(pp + (int64_t)(sp0 + u) * stride) : 0;
+#pragma unroll
+                        for (int u = 0; u < 16; ++u) s += v[u];
+                    }
                     if (a.acc) a.acc[row * n_out + cg] = s;
                     if (a.y) a.y[row * n_out + cg] =
                         __fmul_rn((float)s, __fdiv_rn(a.alpha, a.xscale[row]));
                 }
             }
-            if (tid == 0) a.counters[ci] = 0;
+            if (tid == 0) store_agent(&a.counters[ci], 0);
         }
     }
 }
@@ -384,7 +498,7 @@ GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16) {
     p.n_tok_tiles = (int)ceil_div(rows, p.bt);
     const int cand_max = 8192 / p.bt < 2048 ? 8192 / p.bt : 2048;   // <= 32 KB of coefficients
     const int64_t base = (int64_t)p.n_tiles * p.n_tok_tiles;
-    int64_t ns = ceil_div(kTargetWG, base);
+    int64_t ns = ceil_div(target_wg(), base);
     if (ns < 1) ns = 1;
     int64_t cand = ceil_div(ceil_div(d_in, ns), 64) * 64;
     if (cand > cand_max) cand = cand_max;
@@ -402,7 +516,8 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
     const int ept = w_is_bf16 ? 8 : 4;
     const int ct = kLPR * ept;
     const int tg = p.bt < 2 ? p.bt : 2;
-    size_t lds_a = (size_t)p.cand * p.bt * 4 + (size_t)p.cand * 4;
+    const size_t padded = (size_t)p.cand + 3 * kNSlot * kMaxUnroll;
+    size_t lds_a = padded * p.bt * 4 + padded * 4;
     size_t lds_c = (size_t)kNSlot * tg * ct * 4;
     size_t lds = lds_a > lds_c ? lds_a : lds_c;
     dim3 grid(p.n_tiles, p.nsplit, p.n_tok_tiles);
@@ -421,7 +536,7 @@ I8tPlan plan_i8t(int64_t rows, int64_t d_in, int64_t n_out) {
     I8tPlan p{};
     p.ct = kI8CT;
     p.n_tiles = (int)ceil_div(n_out, p.ct);
-    p.bt = pow2_tile(rows, 4);
+    p.bt = pow2_tile(rows, 2);   // 32 int32 accumulators per token per lane
     p.n_tok_tiles = (int)ceil_div(rows, p.bt);
     const int cand_max = 4096 / p.bt;
     const int64_t base = (int64_t)p.n_tiles * p.n_tok_tiles;
@@ -440,7 +555,8 @@ I8tPlan plan_i8t(int64_t rows, int64_t d_in, int64_t n_out) {
 
 hipError_t launch_i8t(const I8tPlan& p, const I8tArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
-    size_t lds_a = (size_t)p.cand * p.bt * 4 + (size_t)p.cand * 4;
+    const size_t padded = (size_t)p.cand + 3 * kNSlot * kUnroll;
+    size_t lds_a = padded * p.bt * 4 + padded * 4;
     size_t lds_c = (size_t)kNSlot * kI8CT * 4;
     size_t lds = lds_a > lds_c ? lds_a : lds_c;
     dim3 grid(p.n_tiles, p.nsplit, p.n_tok_tiles);
@@ -449,7 +565,7 @@ hipError_t launch_i8t(const I8tPlan& p, const I8tArgs& a, hipStream_t stream) {
         i8t_gemv_kernel<BTV><<<grid, dim3(kNT), lds, stream>>>(a, p.cand, p.nsplit);    \
         return hipGetLastError();                                                       \
     }
-    QS_I8T_CASE(1) QS_I8T_CASE(2) QS_I8T_CASE(4)
+    QS_I8T_CASE(1) QS_I8T_CASE(2)
 #undef QS_I8T_CASE
     return hipErrorInvalidValue;
 }

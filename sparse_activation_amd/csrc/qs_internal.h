@@ -46,6 +46,8 @@ hipError_t launch_topk(int key_kind, int xs_kind, int64_t rows, const TopkArgs& 
                        hipStream_t stream);
 
 // ---------------------------------------------------------------- gather GEMV
+// The gather kernels address weights through 32-bit buffer offsets.
+constexpr int64_t kMaxGatherWeightBytes = int64_t(1) << 30;
 enum Epilogue : int { EPI_STORE = 0, EPI_RELU2 = 1 };
 
 // Launch plan of the gather GEMV: deterministic function of the shape only.
@@ -98,9 +100,7 @@ hipError_t launch_i8t(const I8tPlan& p, const I8tArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- masked MFMA GEMM
 struct MfmaArgs {
-    const uint16_t* x;       // bf16 [M, K]
-    const uint32_t* tau;     // [M] selection descriptors
-    const int32_t* cutoff;   // [M]
+    const uint16_t* x;       // bf16 [M, K]: X (.) M
     const uint16_t* w;       // bf16 W [N, K]
     int64_t m, n, k;
     void* y;                 // [M, N]

@@ -74,6 +74,22 @@ template <> struct Elem<KEY_Q8> {
     __device__ static uint32_t key(uint32_t raw) { return Elem<KEY_I8>::key(raw); }
 };
 
+// Raw words of a whole row through one buffer resource: all loads are issued
+// back to back (no per-entry branch), and entries past the row end read 0.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <int KK>
+__device__ __forceinline__ uint32_t buffer_raw(__amdgpu_buffer_rsrc_t rs, uint32_t j) {
+    if constexpr (KK == KEY_BF16)
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, j * 2u, 0, 0);
+    else if constexpr (KK == KEY_I8)
+        return (uint32_t)(int32_t)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(rs, j, 0, 0);
+    else
+        return __builtin_amdgcn_raw_buffer_load_b32(rs, j * 4u, 0, 0);
+}
+template <int KK> constexpr int elem_bytes() {
+    return KK == KEY_BF16 ? 2 : (KK == KEY_I8 ? 1 : 4);
+}
+
 template <int KK, int XK>
 __device__ __forceinline__ void store_xs(void* xs, int64_t i, uint32_t raw, bool sel) {
     if constexpr (XK == XS_F32) {
@@ -244,13 +260,275 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(TopkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident variant for rows of up to EPT * NT entries (the common
+// case), NT = 256.  Thread t keeps entries t, t + NT, ... in registers.  The
+// threshold key is found bit by bit from the most significant key bit: for
+// each bit, one compare per entry, a wavefront ballot and a scalar popcount
+// count the candidates that keep the current prefix with that bit set; the
+// four per-wave counts meet in LDS behind one barrier (double-buffered by bit
+// parity).  No atomics, so skewed key distributions (many equal exponents)
+// cost nothing extra.  The ordered output pass needs three barriers in all:
+// per-(chunk, wave) counts of keys above and equal to tau go to LDS, wave 0
+// turns them into exclusive prefixes (tie ranks and output slots) with two
+// wavefront scans, and every thread then places its entries.  Entries past
+// the row end carry bit 31, which no valid key has, so they never match a
+// prefix or tie with tau.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, int lane) {
+    uint32_t incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t n = __shfl_up(incl, off);
+        if (lane >= off) incl += n;
+    }
+    return incl - v;
+}
+
+template <int NT, int EPT, int KK, int XK>
+__global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
+    constexpr int NW = NT / kWave;
+    constexpr int NE = EPT * NW;                  // (chunk, wave) entries
+    constexpr int PER = (NE + kWave - 1) / kWave; // entries per lane in the scan
+    constexpr uint32_t kInvalid = 0x80000000u;
+    constexpr int kCap = 1024;                    // compacted candidates
+    __shared__ uint32_t s_cnt[2][NW];
+    __shared__ uint32_t s_g[NE], s_e[NE], s_gb[NE], s_eb[NE];
+    __shared__ uint32_t s_cand[kCap];
+    __shared__ uint32_t s_ncand, s_res[2];
+    __shared__ float s_max[NW];
+
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int64_t d = a.d;
+    const int64_t k = a.k;
+    const int64_t row0 = (int64_t)r * d;
+    const int nch = (int)((d + NT - 1) / NT);     // chunks holding entries (<= EPT)
+
+    if (r == 0 && a.zero_ptr != nullptr)
+        for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
+
+    // Load the row: every load issued before any is used.
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(a.x)) + row0 * elem_bytes<KK>(), (short)0,
+        (int)(d * elem_bytes<KK>()), 0x00020000);
+    uint32_t raw[EPT], key[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) raw[i] = buffer_raw<KK>(rs, (uint32_t)(i * NT + tid));
+
+    float scale = 0.0f;
+    if constexpr (KK == KEY_Q8) {
+        // gamma = max |x| (exact), s = 127 / (gamma + eps), q = rint(x s)
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) m = fmaxf(m, fabsf(__uint_as_float(raw[i])));
+        for (int off = kWave / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if (lane == 0) s_max[wave] = m;
+        __syncthreads();
+        float g = s_max[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) g = fmaxf(g, s_max[w]);
+        scale = __fdiv_rn(127.0f, __fadd_rn(g, 1e-5f));
+        if (tid == 0 && a.xscale != nullptr) a.xscale[r] = scale;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            float q = rintf(__fmul_rn(__uint_as_float(raw[i]), scale));
+            q = fminf(fmaxf(q, -128.0f), 127.0f);
+            raw[i] = (uint32_t)(int32_t)q;
+            const int64_t j = (int64_t)i * NT + tid;
+            if (a.xq != nullptr && j < d) a.xq[row0 + j] = (int8_t)(int32_t)q;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+        key[i] = (int64_t)i * NT + tid < d ? Elem<KK>::key(raw[i]) : kInvalid;
+
+    // ---- bitwise MSD select: tau and the number kr of tau-ties to take.
+    // The top kFull key bits are resolved over the whole row; the entries
+    // still matching the prefix (typically ~1% of the row) are then compacted
+    // into LDS and wave 0 resolves the remaining bits alone, without barriers.
+    // If more than kCap entries survive, the whole block keeps going instead.
+    constexpr int KB = Elem<KK>::kKeyBits;
+    constexpr int kFull = KB > 12 ? (KB > 16 ? 12 : 10) : KB;
+    uint32_t prefix = 0, himask = kInvalid, kr = (uint32_t)k;
+    auto full_pass = [&](int b) {
+        const uint32_t bit = 1u << b;
+        const uint32_t mb = himask | bit, cb = prefix | bit;
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) c += (uint32_t)__popcll(__ballot((key[i] & mb) == cb));
+        // readfirstlane is convergent: it keeps the popcounts out of the
+        // lane-0 branch (otherwise every ballot mask stays live in SGPRs).
+        c = __builtin_amdgcn_readfirstlane(c);
+        const int par = b & 1;
+        if (lane == 0) s_cnt[par][wave] = c;
+        __syncthreads();
+        uint32_t total = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) total += s_cnt[par][w];
+        if (total >= kr) prefix = cb;
+        else kr -= total;
+        himask |= bit;
+    };
+    if (k > 0) {
+        int b = KB - 1;
+#pragma unroll 1
+        for (; b >= KB - kFull; --b) full_pass(b);
+        if (b >= 0) {
+            if (tid == 0) s_ncand = 0;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) {
+                const bool m = (key[i] & himask) == prefix;
+                const uint64_t bm = __ballot(m);
+                const uint32_t n = (uint32_t)__popcll(bm);
+                uint32_t base = 0;
+                if (lane == 0 && n != 0) base = atomicAdd(&s_ncand, n);
+                base = __shfl(base, 0);
+                const uint32_t pos = base + popc_below(bm);
+                if (m && pos < (uint32_t)kCap) s_cand[pos] = key[i];
+            }
+            __syncthreads();
+            const uint32_t nc = s_ncand;
+            if (nc <= (uint32_t)kCap) {
+                if (wave == 0) {
+                    uint32_t ck[kCap / kWave];
+#pragma unroll
+                    for (int q = 0; q < kCap / kWave; ++q) {
+                        const uint32_t n = (uint32_t)(q * kWave + lane);
+                        ck[q] = n < nc ? s_cand[n] : kInvalid;
+                    }
+#pragma unroll 1
+                    for (; b >= 0; --b) {
+                        const uint32_t bit = 1u << b;
+                        const uint32_t mb = himask | bit, cb = prefix | bit;
+                        uint32_t c = 0;
+#pragma unroll
+                        for (int q = 0; q < kCap / kWave; ++q)
+                            c += (uint32_t)__popcll(__ballot((ck[q] & mb) == cb));
+                        if (c >= kr) prefix = cb;
+                        else kr -= c;
+                        himask |= bit;
+                    }
+                    if (lane == 0) { s_res[0] = prefix; s_res[1] = kr; }
+                }
+                __syncthreads();
+                prefix = s_res[0];
+                kr = s_res[1];
+            } else {
+#pragma unroll 1
+                for (; b >= 0; --b) full_pass(b);
+            }
+        }
+    }
+    const uint32_t tau = (k > 0) ? prefix : 0xFFFFFFFFu;
+
+    // ---- ordered output.  Phase 1: per-(chunk, wave) counts.
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        if (i < nch) {
+            const bool gt = k > 0 && key[i] != kInvalid && key[i] > tau;
+            const bool eq = k > 0 && key[i] == tau;
+            const uint32_t g = (uint32_t)__popcll(__ballot(gt));
+            const uint32_t e = (uint32_t)__popcll(__ballot(eq));
+            if (lane == 0) { s_g[i * NW + wave] = g; s_e[i * NW + wave] = e; }
+        }
+    }
+    __syncthreads();
+    // Phase 2: wave 0 scans the entries in (chunk, wave) order.  Ties are
+    // taken in index order until kr of them are in; an entry's selected
+    // count is its keys above tau plus the ties it contributes.
+    if (wave == 0) {
+        const int ne = nch * NW;
+        uint32_t e_loc[PER], g_loc[PER], esum = 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int n = lane * PER + q;
+            e_loc[q] = n < ne ? s_e[n] : 0u;
+            g_loc[q] = n < ne ? s_g[n] : 0u;
+            esum += e_loc[q];
+        }
+        uint32_t eb = wave_excl_scan(esum, lane);
+        uint32_t sel_loc[PER], ssum = 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const uint32_t take = kr > eb ? min(e_loc[q], kr - eb) : 0u;
+            const int n = lane * PER + q;
+            if (n < ne) s_eb[n] = eb;
+            eb += e_loc[q];
+            sel_loc[q] = g_loc[q] + take;
+            ssum += sel_loc[q];
+        }
+        uint32_t sb = wave_excl_scan(ssum, lane);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int n = lane * PER + q;
+            if (n < ne) s_gb[n] = sb;
+            sb += sel_loc[q];
+        }
+    }
+    __syncthreads();
+    // Phase 3: place the entries.  The prefixes are read for every chunk up
+    // front (entries past nch are never used), so no LDS round trip sits on
+    // the per-chunk dependency chain.
+    uint32_t ebv[EPT], gbv[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        ebv[i] = s_eb[i * NW + wave];
+        gbv[i] = s_gb[i * NW + wave];
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        if (i < nch) {
+            const int64_t j = (int64_t)i * NT + tid;
+            const bool valid = key[i] != kInvalid;
+            const bool gt = k > 0 && valid && key[i] > tau;
+            const bool eq = k > 0 && key[i] == tau;
+            const uint64_t beq = __ballot(eq);
+            const uint32_t eq_rank = ebv[i] + popc_below(beq);
+            const bool sel = gt || (eq && eq_rank < kr);
+            const uint64_t bsel = __ballot(sel);
+            if (valid) {
+                const uint32_t pos = gbv[i] + popc_below(bsel);
+                if (a.mask != nullptr) a.mask[row0 + j] = sel ? 1 : 0;
+                if constexpr (XK != XS_NONE)
+                    if (a.xs != nullptr) store_xs<KK, XK>(a.xs, row0 + j, raw[i], sel);
+                if (sel && pos < (uint32_t)k && a.idx != nullptr)
+                    a.idx[(int64_t)r * a.idx_stride + pos] = (int32_t)j;
+                if (eq && eq_rank + 1 == kr && a.cutoff != nullptr) a.cutoff[r] = (int32_t)(j + 1);
+            }
+        }
+    }
+    if (tid == 0) {
+        if (a.tau != nullptr) a.tau[r] = tau;
+        if (k == 0 && a.cutoff != nullptr) a.cutoff[r] = 0;
+        if (a.count != nullptr) a.count[r] = (int32_t)k;
+    }
+}
+
 template <int NT, int KK, int XK>
 hipError_t launch_kkx(int64_t rows, const TopkArgs& a, hipStream_t stream) {
-    if (a.d <= kStageMaxD) {
+    const dim3 grid((unsigned)rows), block(NT);
+    constexpr int R = 256;   // the register-resident kernel always runs 4 waves
+    if (a.d <= 4 * R) {
+        topk_reg_kernel<R, 4, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
+    } else if (a.d <= 8 * R) {
+        topk_reg_kernel<R, 8, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
+    } else if (a.d <= 16 * R) {
+        topk_reg_kernel<R, 16, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
+    } else if (a.d <= 32 * R) {
+        topk_reg_kernel<R, 32, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
+    } else if (a.d <= 48 * R) {
+        topk_reg_kernel<R, 48, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
+    } else if (a.d <= 64 * R) {
+        topk_reg_kernel<R, 64, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
+    } else if (a.d <= kStageMaxD) {
         size_t smem = (size_t)a.d * sizeof(uint32_t);
-        topk_rows_kernel<NT, KK, XK, true><<<dim3((unsigned)rows), dim3(NT), smem, stream>>>(a);
+        topk_rows_kernel<NT, KK, XK, true><<<grid, block, smem, stream>>>(a);
     } else {
-        topk_rows_kernel<NT, KK, XK, false><<<dim3((unsigned)rows), dim3(NT), 0, stream>>>(a);
+        topk_rows_kernel<NT, KK, XK, false><<<grid, block, 0, stream>>>(a);
     }
     return hipGetLastError();
 }

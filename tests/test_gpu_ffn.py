@@ -79,3 +79,66 @@ def test_relu2_bf16_output(gpu_lib):
     note("relu2 FFN C2 B=2 bf16 output")
     _relu2_case(gpu_lib, c["X"], c["W_up"], c["W_down"], c["K_in"], c["K_mid"],
                 ydt=torch.bfloat16)
+
+
+# ---------------------------------------------------------------- dReLU
+
+def _drelu_case(gpu_lib, x, wg, bg, wu, bu, wd, k_in=None, k_mid=-1):
+    import torch
+    qs = gpu_lib
+    d = x.shape[1]
+    k_in = d if k_in is None else k_in
+    bf = torch.bfloat16
+    y, h, mid_idx, mid_cnt = qs.qs_sparse_ffn(
+        to_dev(x, bf), qs.ACT_DRELU, k_in, k_mid, to_dev(wu, bf),
+        to_dev(np.ascontiguousarray(wd.T), bf), w_gate=to_dev(wg, bf),
+        b_gate=None if bg is None else to_dev(bg), b_up=None if bu is None else to_dev(bu),
+        want_h=True, want_mid=True)
+    torch.cuda.synchronize()
+    y, h, mid_idx, mid_cnt = (a.cpu().numpy() for a in (y, h, mid_idx, mid_cnt))
+    xm = x
+    if k_in < d:
+        m1, _, _, _ = oracle.topk_select(oracle.magnitude(x), k_in)
+        xm = np.where(m1 == 1, x, 0.0)
+    ref = oracle.ffn_drelu(xm, wg, bg, wu, bu, wd)
+    tol = 4e-3
+    gp, up = np.maximum(ref["g"], 0), np.maximum(ref["u"], 0)
+    bound = tol * (ref["T_g"] * up + ref["T_u"] * gp + tol * ref["T_g"] * ref["T_u"])
+    err = np.abs(h.astype(np.float64) - ref["h"])
+    assert np.all(err <= bound), f"h outside bound: worst {np.max(err - bound)}"
+    if k_mid < 0:
+        down = oracle.ffn_drelu_down_from(h, wd)
+        for r in range(x.shape[0]):
+            assert mid_cnt[r] == down["nz_count"][r]
+            assert np.array_equal(mid_idx[r, :mid_cnt[r]], down["nz_idx"][r])
+    else:
+        down = oracle.ffn_relu2_down_from(h, k_mid, wd)
+        for r in range(x.shape[0]):
+            assert mid_cnt[r] == k_mid and np.array_equal(mid_idx[r, :k_mid], down["idx2"][r])
+    assert_within(y, down["y"], down["T_y"], tol, "drelu y")
+    return float(np.mean(h == 0))
+
+
+@pytest.mark.parametrize("rows,d,f", [(1, 64, 48), (3, 256, 520), (16, 512, 264), (21, 200, 136)])
+def test_drelu_small(gpu_lib, rows, d, f):
+    rng = np.random.default_rng(rows * 5 + d + f)
+    x = datagen.bf16_round(datagen.student_t(rng, (rows, d)))
+    wg = datagen.bf16_round(datagen.normal(rng, (f, d), 0.02))
+    wu = datagen.bf16_round(datagen.normal(rng, (f, d), 0.02))
+    wd = datagen.bf16_round(datagen.normal(rng, (d, f), 0.02))
+    bg = rng.normal(-0.2, 0.1, size=f).astype(np.float32)
+    bu = rng.normal(-0.2, 0.1, size=f).astype(np.float32)
+    note(f"drelu rows={rows} d={d} ffn={f} (biases)")
+    _drelu_case(gpu_lib, x, wg, bg, wu, bu, wd)
+    note(f"drelu rows={rows} d={d} ffn={f} (no biases, top-K on x and on h)")
+    _drelu_case(gpu_lib, x, wg, None, wu, None, wd, k_in=d // 2, k_mid=f // 3)
+
+
+@pytest.mark.parametrize("batch", [1, 4, 16])
+def test_drelu_full_c5(gpu_lib, batch):
+    c = datagen.c5_drelu_ffn(batch)
+    note(f"dReLU FFN full config C5 B={batch}")
+    zero = _drelu_case(gpu_lib, c["X"], c["W_gate"], c["b_gate"], c["W_up"], c["b_up"],
+                       c["W_down"])
+    print(f"C5 B={batch}: zero fraction of h = {zero:.3f}")
+    assert 0.8 < zero < 0.97

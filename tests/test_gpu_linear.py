@@ -129,3 +129,52 @@ def test_topk_xs_and_gather_linear(gpu_lib):
         y_ref, t = oracle.sparse_linear(x, w, m_ref)
         assert_within(y.cpu().numpy(), y_ref, t, 4e-3, "gather_linear")
         assert int(ws[:16384].count_nonzero()) == 0, "split-K counters must be left zero"
+
+
+# ---------------------------------------------------------------- MFMA (batched) path
+
+@pytest.mark.parametrize("rows,d,n", [(1, 64, 40), (37, 200, 300), (256, 512, 256),
+                                      (300, 1000, 520), (513, 128, 777)])
+def test_linear_mfma_random(gpu_lib, rows, d, n):
+    import torch
+    qs = gpu_lib
+    rng = np.random.default_rng(rows + 3 * d + n)
+    x = datagen.bf16_round(datagen.student_t(rng, (rows, d)))
+    w = datagen.bf16_round(datagen.normal(rng, (n, d), 0.02))
+    for k in sorted({0, 1, (7 * d) // 10, d}):
+        note(f"linear MFMA rows={rows} d={d} n={n} k={k}")
+        y = _run(gpu_lib, x, k, w, torch.bfloat16, torch.bfloat16, torch.float32,
+                 layout=qs.LAYOUT_W)
+        y_ref, t = _ref(x, k, w)
+        assert_within(y, y_ref, t, 4e-3, f"mfma k={k}")
+
+
+def test_linear_mfma_integer_valued_is_exact(gpu_lib):
+    import torch
+    qs = gpu_lib
+    rng = np.random.default_rng(61)
+    rows, d, n = 300, 512, 400
+    x = rng.integers(-8, 9, size=(rows, d)).astype(np.float32)
+    w = rng.integers(-2, 3, size=(n, d)).astype(np.float32)
+    note("linear MFMA integer-valued")
+    y = _run(gpu_lib, x, 300, w, torch.bfloat16, torch.bfloat16, torch.float32, layout=qs.LAYOUT_W)
+    y_ref, _ = _ref(x, 300, w)
+    assert np.array_equal(y, y_ref)
+
+
+def test_linear_mfma_full_c4_sampled(gpu_lib):
+    """Fused-QKV prefill: X [2048,4096] bf16, W [12288,4096], K = 2867; the
+    oracle checks 96 sampled rows (all 12288 outputs each) and the output is
+    also produced in bf16."""
+    import torch
+    qs = gpu_lib
+    c = datagen.c4_prefill_qkv()
+    x, w, k = c["X"], c["W"], c["K"]
+    note("linear MFMA full config C4")
+    y = _run(gpu_lib, x, k, w, torch.bfloat16, torch.bfloat16, torch.float32, layout=qs.LAYOUT_W)
+    yb = _run(gpu_lib, x, k, w, torch.bfloat16, torch.bfloat16, torch.bfloat16, layout=qs.LAYOUT_W)
+    rows = np.sort(np.random.default_rng(67).choice(x.shape[0], 96, replace=False))
+    rows[0], rows[-1] = 0, x.shape[0] - 1
+    y_ref, t = _ref(x[rows], k, w)
+    assert_within(y[rows], y_ref, t, 4e-3, "C4 fp32 out")
+    assert_within(yb[rows], y_ref, t, 4e-3, "C4 bf16 out")
