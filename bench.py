@@ -1,23 +1,30 @@
 #!/usr/bin/env python3
 """Throughput of the Q-Sparse decode hot path on one MI355X.
 
-Default workload: the Llama-7B-shaped squared-ReLU sparse FFN at decode
-(d = 4096, ffn = 11008, bf16 weights, top-K 40% of the input features, then
-top-K 40% of relu(u)^2 before the down projection).  One step is one call of
-qs_sparse_ffn over one batch: top-K of x, gathered up projection with the
-squared-ReLU epilogue, top-K of the intermediate, gathered down projection.
+Default workload (the headline line): the Llama-7B-shaped squared-ReLU sparse
+FFN at decode (d = 4096, ffn = 11008, bf16 weights, top-K 40% of the input
+features, then top-K 40% of relu(u)^2 before the down projection), batch 1.
+One step is one call of qs_sparse_ffn over one batch: top-K of x, gathered up
+projection with the squared-ReLU epilogue, top-K of the intermediate,
+gathered down projection.
+
+Other workloads (--workload): c1 (fp32 1024x1024 linear, 8 tokens), c3
+(int8 x ternary 4096x4096 linear), c4 (fused-QKV prefill through the MFMA
+path, 2048 tokens), c5 (Mistral-7B dReLU FFN decode).
 
 Measurement:
-  * inputs are resident in HBM before timing; three copies of the weights
-    (541 MB, more than the 256 MB Infinity Cache) and eight activation batches
-    rotate from step to step, so the selected rows change and are not served
-    from the cache;
+  * inputs are resident in HBM before timing; weight copies rotate so that
+    the footprint exceeds the 256 MB Infinity Cache where the weights are
+    large, and eight activation batches rotate so the selections change;
   * the K timed steps are captured in one HIP graph (no host launch gaps)
     and timed with HIP events on the stream the library launches on;
-  * roofline: the gather GEMV (the dominant kernel) is timed alone, launch by
-    launch in a graph, on the same inputs; achieved = algorithmic bytes
-    (selected weight rows of the batch's union, each read once, plus its
-    activations and outputs) / measured time, against 8 TB/s;
+  * roofline (c2): the gather GEMV, the dominant kernel, is timed alone
+    through qs_gather_linear, launch by launch in a graph, on the same
+    inputs; achieved = algorithmic bytes (selected weight rows of the
+    batch's union, each read once, plus activations and outputs) / time;
+  * traffic: HBM bytes per launch from committed rocprofv3 PMC summaries
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), used
+    only while the kernel source is unchanged since they were taken;
   * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 
 Prints one JSON line.
@@ -25,8 +32,10 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -36,7 +45,7 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-linear tokens/s and HBM GB/s (% of roofline) at 7B FFN decode, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
-N_WCOPIES = 3
+BF16_PEAK_TFLOPS = 2500.0
 N_XROT = 8
 
 
@@ -46,14 +55,328 @@ def parse_args():
     p.add_argument("--steps", type=int, default=480)
     p.add_argument("--warmup", type=int, default=48)
     p.add_argument("--batch", type=int, default=1)
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--roofline-launches", type=int, default=96)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a 256 MiB device copy (for PMC byte calibration)")
     return p.parse_args()
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_graph(torch, stream, fn, steps, warmup):
+    """Warm up eagerly, capture `steps` calls of fn(i) in a graph, time one replay."""
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            fn(i)
+        stream.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                fn(i)
+        graph.replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def committed_traffic(kernel_src: str, name: str):
+    """Traffic per launch from profiles/<name>, if its source hash matches."""
+    path = os.path.join(ROOT, "profiles", name)
+    src = os.path.join(ROOT, "sparse_activation_amd", "csrc", kernel_src)
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    text = open(path).read()
+    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
+    if not (m_sha and m_val) or m_sha.group(1) != sha:
+        return None
+    return float(m_val.group(1))
+
+
+def copy_calibration(torch, dev):
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 x 256 MiB device copies")
+
+
+def bf16_dev(torch, np, a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- c2: relu2 FFN
+
+def run_c2(args, torch, np, qs, datagen, dev, stream):
+    B = args.batch
+    log(f"workload c2: relu2 FFN decode B={B}; generating weights")
+    c = datagen.c2_relu2_ffn(B)
+    d, ffn = c["W_up"].shape[1], c["W_up"].shape[0]
+    k_in, k_mid = c["K_in"], c["K_mid"]
+    n_copies = 3                                   # 3 x 180 MB > 256 MB MALL
+    wup0 = bf16_dev(torch, np, c["W_up"].T, dev)
+    wdn0 = bf16_dev(torch, np, c["W_down"].T, dev)
+    wups = [wup0] + [wup0.clone() for _ in range(n_copies - 1)]
+    wdns = [wdn0] + [wdn0.clone() for _ in range(n_copies - 1)]
+    xs = [bf16_dev(torch, np, datagen.c2_relu2_ffn(B, rotation=i, with_weights=False)["X"], dev)
+          for i in range(N_XROT)]
+    y = torch.empty((B, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(qs.qs_workspace_bytes(qs.OP_SPARSE_FFN_RELU2, B, d, ffn),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i):
+        qs.qs_sparse_ffn(xs[i % N_XROT], qs.ACT_RELU2, k_in, k_mid, wups[i % n_copies],
+                         wdns[i % n_copies], y=y, ws=ws)
+
+    ms_total = time_graph(torch, stream, step, args.steps, args.warmup)
+    ms_step = ms_total / args.steps
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step, {B / (ms_step * 1e-3):.0f} tokens/s")
+
+    # union sizes of the rotated batches (for the algorithmic bytes)
+    u1, u2 = [], []
+    for i in range(N_XROT):
+        _, _, _, _, x1 = qs.qs_topk_mask(xs[i], k_in, want_mask=False, want_idx=False,
+                                          want_desc=False, want_xs=True)
+        _, h, _, _ = qs.qs_sparse_ffn(xs[i], qs.ACT_RELU2, k_in, k_mid, wups[0], wdns[0],
+                                      want_h=True)
+        _, _, _, _, x2 = qs.qs_topk_mask(h, k_mid, want_mask=False, want_idx=False,
+                                          want_desc=False, want_xs=True)
+        u1.append(x1)
+        u2.append(x2)
+    torch.cuda.synchronize()
+    un1 = [int((a != 0).any(0).sum()) for a in u1]
+    un2 = [int((a != 0).any(0).sum()) for a in u2]
+
+    def bytes_up(i):
+        return un1[i] * ffn * 2 + B * d * 4 + B * ffn * 4
+
+    def bytes_dn(i):
+        return un2[i] * d * 2 + B * ffn * 4 + B * d * 4
+
+    step_bytes = sum(bytes_up(i % N_XROT) + bytes_dn(i % N_XROT)
+                     for i in range(args.steps)) / args.steps
+
+    # roofline leg: the gather GEMV alone, launch by launch
+    L = args.roofline_launches
+    yup = torch.empty((B, ffn), dtype=torch.float32, device=dev)
+    ydn = torch.empty((B, d), dtype=torch.float32, device=dev)
+    ws_up = qs.gather_workspace(B, d, ffn, dev)
+    ws_dn = qs.gather_workspace(B, ffn, d, dev)
+
+    def gemv_pair(i):
+        qs.qs_gather_linear(u1[i % N_XROT], wups[i % n_copies], y=yup, ws=ws_up)
+        qs.qs_gather_linear(u2[i % N_XROT], wdns[i % n_copies], y=ydn, ws=ws_dn)
+
+    ms_gemv = time_graph(torch, stream, gemv_pair, L, 4)
+    gemv_bytes = sum(bytes_up(i % N_XROT) + bytes_dn(i % N_XROT) for i in range(L))
+    us_launch = ms_gemv * 1e3 / (2 * L)
+    achieved = gemv_bytes / (ms_gemv * 1e-3) / 1e9
+    log(f"gather GEMV: {us_launch:.2f} us per launch (avg of up and down), {achieved:.0f} GB/s")
+    traffic = committed_traffic("qs_gemv.hip", "gather_gemv_llama7b_relu2_b1_traffic.md")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_c2(c, args.cpu_seconds)
+    return {
+        "metric": METRIC, "value": round(B / (ms_step * 1e-3), 1), "unit": "tokens/s",
+        "ms_per_step": round(ms_step, 6), "dtype": "bf16",
+        "config": {"workload": "llama7b_relu2_ffn_decode", "batch": B, "d": d, "ffn": ffn,
+                   "k_in": k_in, "k_mid": k_mid, "weights": "bf16",
+                   "weight_copies": n_copies, "x_rotations": N_XROT},
+        "hbm_gbps_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "union_rows_up": un1, "union_rows_down": un2,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "gather_gemv_kernel",
+                     "algorithmic_bytes_per_launch": round(gemv_bytes / (2 * L)),
+                     "us_per_launch": round(us_launch, 3)},
+        "cpu_baseline": cpu,
+    }
+
+
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return 1
+
+
+def cpu_baseline_c2(c, seconds):
+    import numpy as np
+
+    import datagen
+    import oracle
+    cores = _cores()
+    w_up = c["W_up"].astype(np.float64)
+    w_dn = c["W_down"].astype(np.float64)
+    n, t0 = 0, time.perf_counter()
+    while n < 64:
+        x = datagen.c2_relu2_ffn(1, rotation=n % N_XROT, with_weights=False)["X"]
+        oracle.ffn_relu2(x, c["K_in"], w_up, c["K_mid"], w_dn)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    log(f"cpu oracle: {n} tokens in {dt:.1f} s")
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} single-token steps of the same workload (B=1), float64 NumPy oracle"}
+
+
+# ---------------------------------------------------------------- other workloads
+
+def run_c5(args, torch, np, qs, datagen, dev, stream):
+    B = args.batch
+    log(f"workload c5: dReLU FFN decode B={B}; generating weights")
+    c = datagen.c5_drelu_ffn(B)
+    ffn, d = c["W_gate"].shape
+    n_copies = 2                                   # 2 x 352 MB > 256 MB MALL
+    wg = [bf16_dev(torch, np, c["W_gate"], dev)]
+    wu = [bf16_dev(torch, np, c["W_up"], dev)]
+    wd = [bf16_dev(torch, np, c["W_down"].T, dev)]
+    for _ in range(n_copies - 1):
+        wg.append(wg[0].clone()); wu.append(wu[0].clone()); wd.append(wd[0].clone())
+    bg = torch.from_numpy(c["b_gate"]).to(dev)
+    bu = torch.from_numpy(c["b_up"]).to(dev)
+    xs = [bf16_dev(torch, np, datagen.c5_drelu_ffn(B, rotation=i, with_weights=False)["X"], dev)
+          for i in range(N_XROT)]
+    y = torch.empty((B, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(qs.qs_workspace_bytes(qs.OP_SPARSE_FFN_DRELU, B, d, ffn),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i):
+        j = i % n_copies
+        qs.qs_sparse_ffn(xs[i % N_XROT], qs.ACT_DRELU, d, -1, wu[j], wd[j], w_gate=wg[j],
+                         b_gate=bg, b_up=bu, y=y, ws=ws)
+
+    ms_step = time_graph(torch, stream, step, args.steps, args.warmup) / args.steps
+    # measured unions: gate read in full, up rows with g > 0 for some token, down rows with h != 0
+    hs = [qs.qs_sparse_ffn(xs[i], qs.ACT_DRELU, d, -1, wu[0], wd[0], w_gate=wg[0], b_gate=bg,
+                           b_up=bu, want_h=True)[1] for i in range(N_XROT)]
+    g_pos = []
+    for i in range(N_XROT):
+        g = xs[i].float() @ wg[0].float().t() + bg
+        g_pos.append(int((g > 0).any(0).sum()))
+    nz = [int((h != 0).any(0).sum()) for h in hs]
+    zero_frac = float(np.mean([float((h == 0).float().mean()) for h in hs]))
+    rb = d * 2
+    step_bytes = np.mean([ffn * rb + g_pos[i] * rb + nz[i] * rb for i in range(N_XROT)])
+    achieved = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"c5: {ms_step * 1e3:.2f} us/step, {achieved:.0f} GB/s, zero fraction of h {zero_frac:.3f}")
+    return {
+        "metric": "dReLU sparse FFN tokens/s at Mistral-7B decode, 1 GPU", "unit": "tokens/s",
+        "value": round(B / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 6), "dtype": "bf16",
+        "config": {"workload": "mistral7b_drelu_ffn_decode", "batch": B, "d": d, "ffn": ffn,
+                   "weight_copies": n_copies, "x_rotations": N_XROT,
+                   "zero_fraction_h": round(zero_frac, 4), "up_rows_read": g_pos,
+                   "down_rows_read": nz},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "whole FFN step (gate/up + down)",
+                     "algorithmic_bytes_per_step": round(float(step_bytes))},
+        "cpu_baseline": None,
+    }
+
+
+def run_c4(args, torch, np, qs, datagen, dev, stream):
+    log("workload c4: fused-QKV prefill through the MFMA path")
+    c = datagen.c4_prefill_qkv()
+    (m, kdim), n = c["X"].shape, c["W"].shape[0]
+    w = bf16_dev(torch, np, c["W"], dev)
+    xs = [bf16_dev(torch, np, datagen.c4_prefill_qkv(rotation=i, with_weights=False)["X"], dev)
+          for i in range(2)]
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(qs.qs_workspace_bytes(qs.OP_SPARSE_LINEAR, m, kdim, n), dtype=torch.uint8,
+                     device=dev)
+
+    def step(i):
+        qs.qs_sparse_linear(xs[i % 2], c["K"], w, layout=qs.LAYOUT_W, y=y, ws=ws)
+
+    steps = max(4, min(args.steps, 40))
+    ms_step = time_graph(torch, stream, step, steps, 4) / steps
+    flops = 2.0 * m * n * kdim
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    log(f"c4: {ms_step * 1e3:.1f} us/step, {tflops:.0f} TFLOP/s (top-K + GEMM)")
+    return {
+        "metric": "masked-MFMA prefill tokens/s (fused QKV 4096->12288), 1 GPU", "unit": "tokens/s",
+        "value": round(m / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 6), "dtype": "bf16",
+        "steps": steps,
+        "config": {"workload": "qkv_prefill_2048x4096x12288", "tokens": m, "d": kdim, "n": n,
+                   "k": c["K"]},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "whole call (top-K + gemm_nt_bf16_kernel)"},
+        "cpu_baseline": None,
+    }
+
+
+def run_c3(args, torch, np, qs, datagen, dev, stream):
+    B = args.batch
+    log(f"workload c3: int8 x ternary linear B={B}")
+    c = datagen.c3_i8t_linear(B)
+    t, alpha = qs.qs_ternarize(c["W"])
+    n, d = c["W"].shape
+    packed = torch.from_numpy(qs.qs_pack_ternary(t)).to(dev)
+    copies = [packed] + [packed.clone() for _ in range(127)]   # 128 x 4 MB > 256 MB MALL
+    xs = [torch.from_numpy(datagen.c3_i8t_linear(B, rotation=i, with_weights=False)["X"]).to(dev)
+          for i in range(N_XROT)]
+    acc = torch.empty((B, n), dtype=torch.int32, device=dev)
+    y = torch.empty((B, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(qs.qs_workspace_bytes(qs.OP_SPARSE_LINEAR_I8T, B, d, n), dtype=torch.uint8,
+                     device=dev)
+
+    def step(i):
+        qs.qs_sparse_linear_i8t(xs[i % N_XROT], c["K"], copies[i % 128], alpha, n, acc=acc, y=y,
+                                ws=ws, want_all=False)
+
+    ms_step = time_graph(torch, stream, step, args.steps, args.warmup) / args.steps
+    log(f"c3: {ms_step * 1e3:.2f} us/step")
+    return {
+        "metric": "int8 x ternary sparse linear tokens/s (4096x4096), 1 GPU", "unit": "tokens/s",
+        "value": round(B / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 6), "dtype": "int8",
+        "config": {"workload": "bitnet_i8t_linear_4096", "batch": B, "k": c["K"]},
+        "roofline": None, "cpu_baseline": None,
+    }
+
+
+def run_c1(args, torch, np, qs, datagen, dev, stream):
+    log("workload c1: fp32 linear [8,1024] x [1024,1024]")
+    c = datagen.c1_linear()
+    wt = torch.from_numpy(np.ascontiguousarray(c["W"].T)).to(dev)
+    copies = [wt] + [wt.clone() for _ in range(127)]
+    xs = [torch.from_numpy(datagen.c1_linear(rotation=i, with_weights=False)["X"]).to(dev)
+          for i in range(N_XROT)]
+    y = torch.empty((8, 1024), dtype=torch.float32, device=dev)
+    ws = torch.empty(qs.qs_workspace_bytes(qs.OP_SPARSE_LINEAR, 8, 1024, 1024), dtype=torch.uint8,
+                     device=dev)
+
+    def step(i):
+        qs.qs_sparse_linear(xs[i % N_XROT], c["K"], copies[i % 128], y=y, ws=ws)
+
+    ms_step = time_graph(torch, stream, step, args.steps, args.warmup) / args.steps
+    log(f"c1: {ms_step * 1e3:.2f} us/step")
+    return {
+        "metric": "fp32 sparse linear tokens/s (1024x1024, 8 tokens), 1 GPU", "unit": "tokens/s",
+        "value": round(8 / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 6), "dtype": "f32",
+        "config": {"workload": "fp32_linear_1024", "batch": 8, "k": c["K"]},
+        "roofline": None, "cpu_baseline": None,
+    }
 
 
 def main():
@@ -72,166 +395,18 @@ def main():
 
     qs.load()
     dev = torch.device("cuda:0")
-    B = args.batch
-    log(f"workload: relu2 FFN decode B={B}; generating weights")
-    c = datagen.c2_relu2_ffn(B)
-    d, ffn = c["W_up"].shape[1], c["W_up"].shape[0]
-    k_in, k_mid = c["K_in"], c["K_mid"]
-
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
-
-    wup0 = bf16(c["W_up"].T)          # W_up^T   [d, ffn]
-    wdn0 = bf16(c["W_down"].T)        # W_down^T [ffn, d]
-    wups = [wup0] + [wup0.clone() for _ in range(N_WCOPIES - 1)]
-    wdns = [wdn0] + [wdn0.clone() for _ in range(N_WCOPIES - 1)]
-    xs = [bf16(datagen.c2_relu2_ffn(B, rotation=i, with_weights=False)["X"])
-          for i in range(N_XROT)]
-    y = torch.empty((B, d), dtype=torch.float32, device=dev)
-    ws = torch.empty(qs.qs_workspace_bytes(qs.OP_SPARSE_FFN_RELU2, B, d, ffn),
-                     dtype=torch.uint8, device=dev)
-
-    def step(i):
-        qs.qs_sparse_ffn(xs[i % N_XROT], qs.ACT_RELU2, k_in, k_mid, wups[i % N_WCOPIES],
-                         wdns[i % N_WCOPIES], y=y, ws=ws)
-
     stream = torch.cuda.Stream(device=dev)
-    torch.cuda.synchronize(dev)
-    with torch.cuda.stream(stream):
-        log(f"warmup {args.warmup} steps")
-        for i in range(args.warmup):
-            step(i)
-        stream.synchronize()
-        log(f"capturing {args.steps} steps in a graph")
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(args.steps):
-                step(i)
-        graph.replay()                       # untimed replay (first-touch of the graph)
-        stream.synchronize()
-
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize(dev)
-        e0.record(stream)
-        graph.replay()
-        e1.record(stream)
-        torch.cuda.synchronize(dev)
-        ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
-    tokens_per_s = B / (ms_step * 1e-3)
-    log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step, {tokens_per_s:.0f} tokens/s")
-
-    # ---- union sizes of the rotated batches (for the algorithmic bytes)
-    u1, u2 = [], []
-    for i in range(N_XROT):
-        _, _, _, _, x1 = qs.qs_topk_mask(xs[i], k_in, want_mask=False, want_idx=False,
-                                          want_desc=False, want_xs=True)
-        _, h, _, _ = qs.qs_sparse_ffn(xs[i], qs.ACT_RELU2, k_in, k_mid, wups[0], wdns[0],
-                                      want_h=True)
-        _, _, _, _, x2 = qs.qs_topk_mask(h, k_mid, want_mask=False, want_idx=False,
-                                          want_desc=False, want_xs=True)
-        u1.append(x1)
-        u2.append(x2)
-    torch.cuda.synchronize(dev)
-    un1 = [int((a != 0).any(0).sum()) for a in u1]
-    un2 = [int((a != 0).any(0).sum()) for a in u2]
-
-    def bytes_up(i):
-        return un1[i] * ffn * 2 + B * d * 4 + B * ffn * 4
-
-    def bytes_dn(i):
-        return un2[i] * d * 2 + B * ffn * 4 + B * d * 4
-
-    step_bytes = sum(bytes_up(i % N_XROT) + bytes_dn(i % N_XROT)
-                     for i in range(args.steps)) / args.steps
-
-    # ---- roofline leg: the gather GEMV alone, launch by launch
-    L = args.roofline_launches
-    yup = torch.empty((B, ffn), dtype=torch.float32, device=dev)
-    ydn = torch.empty((B, d), dtype=torch.float32, device=dev)
-    ws_up = qs.gather_workspace(B, d, ffn, dev)
-    ws_dn = qs.gather_workspace(B, ffn, d, dev)
-    torch.cuda.synchronize(dev)
-    with torch.cuda.stream(stream):
-        for i in range(4):
-            qs.qs_gather_linear(u1[i % N_XROT], wups[i % N_WCOPIES], y=yup, ws=ws_up)
-            qs.qs_gather_linear(u2[i % N_XROT], wdns[i % N_WCOPIES], y=ydn, ws=ws_dn)
-        stream.synchronize()
-        g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g2, stream=stream):
-            for i in range(L):
-                qs.qs_gather_linear(u1[i % N_XROT], wups[i % N_WCOPIES], y=yup, ws=ws_up)
-                qs.qs_gather_linear(u2[i % N_XROT], wdns[i % N_WCOPIES], y=ydn, ws=ws_dn)
-        g2.replay()
-        stream.synchronize()
-        torch.cuda.synchronize(dev)
-        e0.record(stream)
-        g2.replay()
-        e1.record(stream)
-        torch.cuda.synchronize(dev)
-        ms_gemv = e0.elapsed_time(e1)
-    gemv_bytes = sum(bytes_up(i % N_XROT) + bytes_dn(i % N_XROT) for i in range(L))
-    us_launch = ms_gemv * 1e3 / (2 * L)
-    achieved = gemv_bytes / (ms_gemv * 1e-3) / 1e9
-    log(f"gather GEMV: {us_launch:.2f} us per launch (avg of up and down), {achieved:.0f} GB/s")
-
-    # ---- CPU oracle on a bounded sample
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(c, args.cpu_seconds)
-
-    out = {
-        "metric": METRIC,
-        "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded Student-t(4) activations, N(0,0.02) weights; datagen recipe)",
-        "config": {"workload": "llama7b_relu2_ffn_decode", "batch": B, "d": d, "ffn": ffn,
-                   "k_in": k_in, "k_mid": k_mid, "weights": "bf16",
-                   "weight_copies": N_WCOPIES, "x_rotations": N_XROT},
-        "hbm_gbps_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
-        "union_rows_up": un1,
-        "union_rows_down": un2,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": "gather_gemv_kernel",
-                     "us_per_launch": round(us_launch, 3)},
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(out), flush=True)
-
-
-def cpu_baseline(c, seconds):
-    import numpy as np
-
-    import datagen
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
-    w_up = c["W_up"].astype(np.float64)
-    w_dn = c["W_down"].astype(np.float64)
-    n, t0 = 0, time.perf_counter()
-    while n < 64:
-        x = datagen.c2_relu2_ffn(1, rotation=n % N_XROT, with_weights=False)["X"]
-        oracle.ffn_relu2(x, c["K_in"], w_up, c["K_mid"], w_dn)
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    log(f"cpu oracle: {n} tokens in {dt:.1f} s")
-    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} single-token steps of the same workload (B=1), float64 NumPy oracle"}
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+    run = {"c1": run_c1, "c2": run_c2, "c3": run_c3, "c4": run_c4, "c5": run_c5}[args.workload]
+    out = run(args, torch, np, qs, datagen, dev, stream)
+    line = {"metric": out.pop("metric"), "value": out.pop("value"), "unit": out.pop("unit"),
+            "n_gpus": 1, "steps": out.pop("steps", args.steps), "warmup": args.warmup,
+            "ms_per_step": out.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": out.pop("dtype"),
+            "data": "synthetic (seeded Student-t(4) activations, N(0,0.02) weights)"}
+    line.update(out)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

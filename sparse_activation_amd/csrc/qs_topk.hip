@@ -32,6 +32,19 @@ __device__ __forceinline__ uint32_t popc_below(uint64_t m) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Inclusive wavefront sum scan with DPP (in-register cross-lane moves:
+// row_shr 1, 2, 4, 8 inside each 16-lane row, then row_bcast 15 and 31 to
+// carry the row totals; out-of-row sources read zero).
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
 // Raw 32-bit word of element i, and its magnitude key.
 template <int KK> struct Elem;
 
@@ -508,10 +521,386 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Vectorised variant (the main path): rows whose byte length is a multiple of
+// 16 and that fit NQ runs per thread.  Thread t of 256 loads run q, the V
+// entries [q * 256 V + t V, + V) of the row, with one 16-byte buffer load
+// (V = 4 fp32, 8 bf16, 16 int8), so every load instruction of a wavefront
+// reads 1 KiB contiguously.  Index order is (run, thread, entry).
+//
+// Select: 8-bit digits from the top of the key.  The first digit is counted
+// over every entry (LDS histograms, one per wavefront, so that contention on
+// frequent exponents stays inside a wave); a descending block scan of the 256
+// bins finds the digit of the K-th largest key.  The entries that still
+// match the prefix are compacted into LDS (per-wave ballot counts, one
+// barrier, no atomics), and the remaining digits are counted over those
+// candidates only.  Output: the tie ranks and output slots of all runs come
+// from two block-wide scans over (run, thread) order (wave scans of every run
+// at once, one barrier each), after which every thread writes its runs with
+// vector stores.
+// ---------------------------------------------------------------------------
+template <int KK> struct VecOf;
+template <> struct VecOf<KEY_F32> { static constexpr int V = 4; };
+template <> struct VecOf<KEY_Q8> { static constexpr int V = 4; };
+template <> struct VecOf<KEY_BF16> { static constexpr int V = 8; };
+template <> struct VecOf<KEY_I8> { static constexpr int V = 16; };
+
+template <int KK>
+__device__ __forceinline__ void unpack_raw(const u32x4_t& w, uint32_t* raw) {
+    if constexpr (KK == KEY_F32 || KK == KEY_Q8) {
+        raw[0] = w.x; raw[1] = w.y; raw[2] = w.z; raw[3] = w.w;
+    } else if constexpr (KK == KEY_BF16) {
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { raw[2 * i] = u[i] & 0xFFFFu; raw[2 * i + 1] = u[i] >> 16; }
+    } else {
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) raw[i] = (uint32_t)(int32_t)(int8_t)(u[i / 4] >> (8 * (i % 4)));
+    }
+}
+
+// Every wavefront scans the whole 256-bin histogram (summed over the NW
+// sub-histograms) from the top bin down and finds the bin that holds the
+// kr-th largest key, so no second barrier is needed.  Lane l owns bins
+// 255 - 4l - c (c = 0..3).  Returns the digit and the rank of the wanted key
+// inside its bin.
+template <int NW>
+__device__ __forceinline__ void find_digit(const uint32_t (*h)[256], uint32_t kr, int lane,
+                                           uint32_t& digit, uint32_t& kr_out) {
+    uint32_t c4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&h[w][252 - 4 * lane]);   // bins 252+3-4l .. 252-4l
+        c4[0] += v.w; c4[1] += v.z; c4[2] += v.y; c4[3] += v.x;                // descending order
+    }
+    const uint32_t lsum = c4[0] + c4[1] + c4[2] + c4[3];
+    const uint32_t incl = wave_incl_scan_dpp(lsum);
+    const uint32_t excl = incl - lsum;
+    const bool mine = excl < kr && kr <= incl;
+    const uint64_t bm = __ballot(mine);
+    const int src = (int)__builtin_ctzll(bm);
+    uint32_t e = excl, dg = 0, kk = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (dg == 0 && kk == 0 && e < kr && kr <= e + c4[c]) { dg = (uint32_t)(255 - 4 * lane - c); kk = kr - e; }
+        e += c4[c];
+    }
+    digit = (uint32_t)__builtin_amdgcn_readlane((int)dg, src);
+    kr_out = (uint32_t)__builtin_amdgcn_readlane((int)kk, src);
+}
+
+template <int NQ, int KK, int XK>
+__global__ __launch_bounds__(256) void topk_vec_kernel(TopkArgs a) {
+    constexpr int NT = 256, NW = NT / kWave;
+    constexpr int V = VecOf<KK>::V, CS = V * NT, EPT = NQ * V;
+    constexpr int KB = Elem<KK>::kKeyBits;
+    constexpr uint32_t kInvalid = 0x80000000u;
+    constexpr int kCap = 4096;
+    constexpr int ESZ = elem_bytes<KK>();
+    __shared__ uint32_t s_hist[3][NW][256];     // rotating: count, scan, clear
+    __shared__ uint32_t s_cand[kCap];
+    __shared__ uint32_t s_tot[2][NQ][NW];
+    __shared__ uint32_t s_cw[NW];
+    __shared__ float s_max[NW];
+
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int64_t d = a.d, k = a.k, row0 = (int64_t)r * d;
+
+    if (r == 0 && a.zero_ptr != nullptr)
+        for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+        for (int w = 0; w < NW; ++w) s_hist[b][w][tid] = 0;
+
+    // ---- load runs (past the row end the buffer reads zero)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(a.x)) + row0 * ESZ, (short)0,
+        (int)(d * ESZ), 0x00020000);
+    uint32_t raw[EPT], key[EPT];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, (uint32_t)((q * CS + V * tid) * ESZ), 0, 0);
+        unpack_raw<KK>(w, raw + q * V);
+    }
+    auto run_valid = [&](int q) { return (int64_t)q * CS + V * tid < d; };   // d % V == 0
+
+    if constexpr (KK == KEY_Q8) {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) m = fmaxf(m, fabsf(__uint_as_float(raw[i])));
+        for (int off = kWave / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if (lane == 0) s_max[wave] = m;
+        __syncthreads();
+        float g = s_max[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) g = fmaxf(g, s_max[w]);
+        const float scale = __fdiv_rn(127.0f, __fadd_rn(g, 1e-5f));
+        if (tid == 0 && a.xscale != nullptr) a.xscale[r] = scale;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                float qv = rintf(__fmul_rn(__uint_as_float(raw[q * V + e]), scale));
+                qv = fminf(fmaxf(qv, -128.0f), 127.0f);
+                raw[q * V + e] = (uint32_t)(int32_t)qv;
+                packed |= ((uint32_t)(int32_t)qv & 0xFFu) << (8 * e);
+            }
+            if (a.xq != nullptr && run_valid(q))
+                *reinterpret_cast<uint32_t*>(a.xq + row0 + q * CS + V * tid) = packed;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+            key[q * V + e] = run_valid(q) ? Elem<KK>::key(raw[q * V + e]) : kInvalid;
+    __syncthreads();   // histograms cleared
+
+    // ---- select
+    // Level L counts into buffer L % 3 and clears buffer (L + 2) % 3, whose last
+    // reader (level L - 1) finished before level L's barrier and whose next
+    // writer (level L + 2) starts after level L + 1's barrier.
+    uint32_t prefix = 0, himask = kInvalid, kr = (uint32_t)k;
+    if (k > 0) {
+        int shift = KB > 8 ? KB - 8 : 0;
+        int lvl = 0;
+        // level 1 over every entry.  Zero keys (frequent: an FFN intermediate
+        // is often half zeros) are counted with a ballot instead of piling
+        // conflicting atomics onto bin 0.
+        uint32_t nzero = 0;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            nzero += (uint32_t)__popcll(__ballot(key[i] == 0u));
+            if (key[i] != kInvalid && key[i] != 0u) atomicAdd(&s_hist[0][wave][key[i] >> shift], 1u);
+        }
+        nzero = __builtin_amdgcn_readfirstlane(nzero);
+        if (lane == 0 && nzero != 0) atomicAdd(&s_hist[0][wave][0], nzero);
+        __syncthreads();
+        uint32_t dg;
+        find_digit<NW>(s_hist[0], kr, lane, dg, kr);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) s_hist[2][w][tid] = 0;
+        lvl = 1;
+        prefix = dg << shift;
+        himask |= (0xFFu << shift) & ((1u << KB) - 1u);
+        if (shift > 0) {
+            // compact the candidates
+            uint32_t cw = 0;
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) cw += (uint32_t)__popcll(__ballot((key[i] & himask) == prefix));
+            cw = __builtin_amdgcn_readfirstlane(cw);
+            if (lane == 0) s_cw[wave] = cw;
+            __syncthreads();
+            uint32_t run = 0, nc = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) { run += w < wave ? s_cw[w] : 0u; nc += s_cw[w]; }
+            const bool fits = nc <= (uint32_t)kCap;
+            if (fits) {
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) {
+                    const bool m = (key[i] & himask) == prefix;
+                    const uint64_t bm = __ballot(m);
+                    if (m) s_cand[run + popc_below(bm)] = key[i];
+                    run += (uint32_t)__popcll(bm);
+                }
+                __syncthreads();
+            }
+            // Each thread takes candidates tid, tid + NT, ... into registers once.
+            constexpr int CR = kCap / NT;
+            uint32_t cand[CR];
+#pragma unroll
+            for (int i = 0; i < CR; ++i) {
+                const uint32_t c = (uint32_t)(tid + i * NT);
+                cand[i] = kInvalid;
+                if ((uint32_t)(i * NT) < nc && fits && c < nc) cand[i] = s_cand[c];
+            }
+            // remaining levels
+            while (shift > 0) {
+                const int nshift = shift > 8 ? shift - 8 : 0;
+                const uint32_t dmask = (1u << (shift - nshift)) - 1u;
+                uint32_t (*hb)[256] = s_hist[lvl % 3];
+                if (fits) {
+#pragma unroll
+                    for (int i = 0; i < CR; ++i) {
+                        if ((uint32_t)(i * NT) >= nc) break;     // uniform
+                        if ((cand[i] & himask) == prefix)
+                            atomicAdd(&hb[wave][(cand[i] >> nshift) & dmask], 1u);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < EPT; ++i)
+                        if ((key[i] & himask) == prefix)
+                            atomicAdd(&hb[wave][(key[i] >> nshift) & dmask], 1u);
+                }
+                __syncthreads();
+                find_digit<NW>(hb, kr, lane, dg, kr);
+#pragma unroll
+                for (int w = 0; w < NW; ++w) s_hist[(lvl + 2) % 3][w][tid] = 0;
+                ++lvl;
+                prefix |= dg << nshift;
+                himask |= dmask << nshift;
+                shift = nshift;
+            }
+        }
+    }
+    const uint32_t tau = (k > 0) ? prefix : 0xFFFFFFFFu;
+
+    // ---- ordered output: two block scans over (run, thread) order.
+    uint32_t eqc[NQ], gtc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        eqc[q] = 0; gtc[q] = 0;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const uint32_t kk = key[q * V + e];
+            eqc[q] += (k > 0 && kk == tau) ? 1u : 0u;
+            gtc[q] += (k > 0 && kk != kInvalid && kk > tau) ? 1u : 0u;
+        }
+    }
+    // exclusive prefix of cnt[] in (run, thread) order, into out[]
+    auto block_scan = [&](const uint32_t* cnt, uint32_t* out, int buf) {
+        uint32_t inc[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) inc[q] = wave_incl_scan_dpp(cnt[q]);
+        if (lane == kWave - 1)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) s_tot[buf][q][wave] = inc[q];
+        __syncthreads();
+        uint32_t base = 0;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            uint32_t before = 0, tot = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const uint32_t t = s_tot[buf][q][w];
+                before += w < wave ? t : 0u;
+                tot += t;
+            }
+            out[q] = base + before + inc[q] - cnt[q];
+            base += tot;
+        }
+    };
+    uint32_t eqb[NQ], selc[NQ], selb[NQ];
+    block_scan(eqc, eqb, 0);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+        selc[q] = gtc[q] + (kr > eqb[q] ? min(eqc[q], kr - eqb[q]) : 0u);
+    block_scan(selc, selb, 1);
+
+    // Index list and cutoff (optional outputs): a separate pass behind one
+    // uniform branch, so the common path carries no per-entry scatter.
+    if (a.idx != nullptr || a.cutoff != nullptr) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            if (!run_valid(q)) continue;
+            const int64_t j0 = (int64_t)q * CS + V * tid;
+            uint32_t er = eqb[q], sp = selb[q];
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const uint32_t kk = key[q * V + e];
+                const bool gt = k > 0 && kk > tau;
+                const bool eq = k > 0 && kk == tau;
+                const bool sel = gt || (eq && er < kr);
+                if (sel && sp < (uint32_t)k && a.idx != nullptr)
+                    a.idx[(int64_t)r * a.idx_stride + sp] = (int32_t)(j0 + e);
+                if (eq && er + 1 == kr && a.cutoff != nullptr) a.cutoff[r] = (int32_t)(j0 + e + 1);
+                er += eq ? 1u : 0u;
+                sp += sel ? 1u : 0u;
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        if (!run_valid(q)) continue;
+        const int64_t j0 = (int64_t)q * CS + V * tid;
+        uint32_t er = eqb[q];
+        uint32_t mbits[(V + 3) / 4];
+#pragma unroll
+        for (int w = 0; w < (V + 3) / 4; ++w) mbits[w] = 0;
+        uint32_t xsv[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const uint32_t kk = key[q * V + e];
+            const bool gt = k > 0 && kk > tau;      // valid run: no invalid keys here
+            const bool eq = k > 0 && kk == tau;
+            const bool sel = gt || (eq && er < kr);
+            mbits[e / 4] |= (sel ? 1u : 0u) << (8 * (e % 4));
+            uint32_t xv = 0;
+            if constexpr (XK == XS_F32) {
+                float f = 0.0f;
+                if constexpr (KK == KEY_F32) f = __uint_as_float(raw[q * V + e]);
+                else if constexpr (KK == KEY_BF16) f = __uint_as_float(raw[q * V + e] << 16);
+                else f = (float)(int32_t)raw[q * V + e];
+                xv = sel ? __float_as_uint(f) : 0u;
+            } else if constexpr (XK == XS_BF16) {
+                xv = sel ? (raw[q * V + e] & 0xFFFFu) : 0u;
+            } else if constexpr (XK == XS_I8) {
+                xv = sel ? (raw[q * V + e] & 0xFFu) : 0u;
+            }
+            xsv[e] = xv;
+            er += eq ? 1u : 0u;
+        }
+        if (a.mask != nullptr) {
+            uint8_t* mp = a.mask + row0 + j0;
+            if constexpr (V == 4) *reinterpret_cast<uint32_t*>(mp) = mbits[0];
+            else if constexpr (V == 8) *reinterpret_cast<uint2*>(mp) = make_uint2(mbits[0], mbits[1]);
+            else *reinterpret_cast<uint4*>(mp) = make_uint4(mbits[0], mbits[1], mbits[2], mbits[3]);
+        }
+        if constexpr (XK == XS_F32) {
+            if (a.xs != nullptr) {
+                float* xp = reinterpret_cast<float*>(a.xs) + row0 + j0;
+#pragma unroll
+                for (int e = 0; e < V; e += 4)
+                    *reinterpret_cast<uint4*>(xp + e) = make_uint4(xsv[e], xsv[e + 1], xsv[e + 2], xsv[e + 3]);
+            }
+        } else if constexpr (XK == XS_BF16) {
+            if (a.xs != nullptr) {
+                uint16_t* xp = reinterpret_cast<uint16_t*>(a.xs) + row0 + j0;   // V == 8
+                *reinterpret_cast<uint4*>(xp) =
+                    make_uint4(xsv[0] | (xsv[1] << 16), xsv[2] | (xsv[3] << 16),
+                               xsv[4] | (xsv[5] << 16), xsv[6] | (xsv[7] << 16));
+            }
+        } else if constexpr (XK == XS_I8) {
+            if (a.xs != nullptr) {
+                int8_t* xp = reinterpret_cast<int8_t*>(a.xs) + row0 + j0;      // V == 4
+                *reinterpret_cast<uint32_t*>(xp) = xsv[0] | (xsv[1] << 8) | (xsv[2] << 16) | (xsv[3] << 24);
+            }
+        }
+    }
+    if (tid == 0) {
+        if (a.tau != nullptr) a.tau[r] = tau;
+        if (k == 0 && a.cutoff != nullptr) a.cutoff[r] = 0;
+        if (a.count != nullptr) a.count[r] = (int32_t)k;
+    }
+}
+
 template <int NT, int KK, int XK>
 hipError_t launch_kkx(int64_t rows, const TopkArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)rows), block(NT);
-    constexpr int R = 256;   // the register-resident kernel always runs 4 waves
+    constexpr int R = 256;   // the register-resident kernels always run 4 waves
+    constexpr int V = VecOf<KK>::V, CS = V * R;
+    constexpr int kMaxVecD = 16384;               // 64 registers of entries per thread
+    if (a.d % V == 0 && a.d <= kMaxVecD) {
+        const int64_t nq = (a.d + CS - 1) / CS;
+        if (nq <= 1) topk_vec_kernel<1, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
+        else if (nq <= 2) topk_vec_kernel<2, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
+        else if constexpr (kMaxVecD / CS >= 4) {
+            if (nq <= 4) topk_vec_kernel<4, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
+            else if constexpr (kMaxVecD / CS >= 8) {
+                if (nq <= 8) topk_vec_kernel<8, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
+                else if constexpr (kMaxVecD / CS >= 16) {
+                    if (nq <= 12) topk_vec_kernel<12, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
+                    else topk_vec_kernel<16, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
+                }
+            }
+        }
+        return hipGetLastError();
+    }
     if (a.d <= 4 * R) {
         topk_reg_kernel<R, 4, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
     } else if (a.d <= 8 * R) {
