@@ -301,6 +301,198 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA variant for 16-token tiles.  With 16 tokens the gather is an
+// (16 x rows) . (rows x n_out) product, so the multiply-adds go to
+// v_mfma_f32_16x16x4_f32: A = the coefficients of 16 tokens for 4 selected
+// rows (one per lane), B = the 4 rows' weights.  A 16-byte load gives a lane
+// EPT consecutive columns of one row; the EPT values feed EPT MFMAs whose
+// output columns are permuted accordingly (MFMA e, lane column j -> column
+// j * EPT + e), so no LDS transpose is needed.  Each wavefront owns 16 * EPT
+// columns and walks every selected row of the workgroup's candidate range,
+// so the workgroup needs no cross-wave reduction; fp32 products and sums
+// keep the fp32 intermediate exact to fp32 rounding.
+// ---------------------------------------------------------------------------
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int WBF16>
+__global__ __launch_bounds__(kNT) void gather_mfma_kernel(GemvArgs a, int cand, int nsplit) {
+    constexpr int EPT = WBF16 ? 8 : 4;
+    constexpr int CT = 16 * EPT;           // columns per workgroup (128 bf16, 64 fp32)
+    constexpr int BT = 16;
+    constexpr int G = 4;                   // 4-row groups per wave per stage
+    constexpr int BATCH = 4 * 4 * G;       // rows per workgroup stage (4 waves)
+    constexpr int OPT = BT * CT / kNT;     // outputs per thread in the reductions (8)
+    extern __shared__ float smem[];
+    float* s_coef = smem;                                                    // [cand + 3 BATCH][16]
+    uint32_t* s_off = reinterpret_cast<uint32_t*>(smem + (size_t)(cand + 3 * BATCH) * BT);
+    __shared__ int s_wcnt[4];
+    __shared__ int s_last;
+
+    const int tile = blockIdx.x, split = blockIdx.y, tt = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t rows = a.rows, d_in = a.d_in, n_out = a.n_out;
+    const int64_t j0 = (int64_t)split * cand;
+    const int64_t j1 = min(d_in, j0 + (int64_t)cand);
+    const int64_t tok0 = (int64_t)tt * BT;
+    const int64_t esize = WBF16 ? 2 : 4;
+    const uint32_t rowbytes = (uint32_t)(n_out * esize);
+
+    // Phase A: union of the selected rows of this candidate range (as in the
+    // fp32-FMA kernel), with the 16 tokens' coefficients.
+    const int64_t ntok = min((int64_t)BT, rows - tok0);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.xs + tok0 * d_in), (short)0, (int)(ntok * d_in * 4), 0x00020000);
+    int nact = 0;
+    for (int64_t c0 = j0; c0 < j1; c0 += kNT) {
+        const int64_t j = c0 + tid;
+        const bool jin = j < j1;
+        float c[BT];
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+            c[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                xr, jin ? (uint32_t)((t * d_in + j) * 4) : kOOB, 0, 0));
+        bool any = false;
+#pragma unroll
+        for (int t = 0; t < BT; ++t) any = any || (c[t] != 0.0f);
+        const uint64_t b = __ballot(any);
+        if (lane == 0) s_wcnt[wave] = (int)__popcll(b);
+        __syncthreads();
+        int before = nact, total = nact;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if (w < wave) before += s_wcnt[w];
+            total += s_wcnt[w];
+        }
+        if (any) {
+            const int pos = before + (int)popc_below(b);
+            s_off[pos] = (uint32_t)j * rowbytes;
+#pragma unroll
+            for (int t = 0; t < BT; ++t) s_coef[pos * BT + t] = c[t];
+        }
+        nact = total;
+        __syncthreads();
+    }
+    const int nbatch = (nact + BATCH - 1) / BATCH;
+    const int npad = ((nbatch + 1) / 2 * 2 + 1) * BATCH;
+    for (int i = nact + tid; i < npad; i += kNT) {
+        s_off[i] = kOOB;
+#pragma unroll
+        for (int t = 0; t < BT; ++t) s_coef[i * BT + t] = 0.0f;
+    }
+    __syncthreads();
+
+    // Phase B: lane (kq = lane / 16, jl = lane % 16) holds row kq of each
+    // 4-row group and columns jl * EPT .. + EPT of the tile; wave w takes the
+    // groups w, w + 4, w + 8, w + 12 of every 64-row stage.
+    const int kq = lane >> 4, jl = lane & 15;
+    const int64_t col = (int64_t)tile * CT + jl * EPT;
+    const uint32_t colb = col < n_out ? (uint32_t)(col * esize) : kOOB;
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, a.d_in * (int64_t)rowbytes);
+
+    f32x4_t acc[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    u32x4 wa[G], wb[G];
+    float ca[G], cb[G];
+    auto load_stage = [&](u32x4* w, float* c, int bi) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int ai = bi * BATCH + (g * 4 + wave) * 4 + kq;
+            w[g] = __builtin_amdgcn_raw_buffer_load_b128(rs, s_off[ai] + colb, 0, 0);
+            c[g] = s_coef[ai * BT + jl];
+        }
+    };
+    auto mfma_stage = [&](const u32x4* w, const float* c) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float wf[EPT];
+            unpack<WBF16>(w[g], wf);
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                acc[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(c[g], wf[e], acc[e], 0, 0, 0);
+        }
+    };
+    load_stage(wa, ca, 0);
+    for (int bi = 0; bi < nbatch; bi += 2) {
+        load_stage(wb, cb, bi + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_stage(wa, ca);
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage(wa, ca, bi + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_stage(wb, cb);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();   // coefficient staging is dead: reuse LDS for the wave reduction
+
+    // Phase C: MFMA e, register v of a lane is token 4 kq + v, column jl * EPT + e
+    // of the tile.  The four waves' tiles are summed in wave order.
+    float* s_red = smem;   // [4][BT][CT]
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            s_red[(wave * BT + 4 * kq + v) * CT + jl * EPT + e] = acc[e][v];
+    __syncthreads();
+    float outv[OPT];
+#pragma unroll
+    for (int q = 0; q < OPT; ++q) {
+        const int o = q * kNT + tid;             // output index in the BT x CT tile
+        float sum = s_red[o];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) sum += s_red[w * BT * CT + o];
+        outv[q] = sum;
+    }
+#pragma unroll
+    for (int q = 0; q < OPT; ++q) {
+        const int o = q * kNT + tid;
+        const int64_t row = tok0 + o / CT, cg = (int64_t)tile * CT + (o % CT);
+        if (row < rows && cg < n_out) {
+            if (nsplit == 1) store_final(a, row * n_out + cg, outv[q]);
+            else store_agent(&a.partial[((int64_t)split * rows + row) * n_out + cg], outv[q]);
+        }
+    }
+
+    // Phase D: the last workgroup of this tile sums the partials in split
+    // order, with the loads of all its outputs for 8 splits in flight at once.
+    if (nsplit > 1) {
+        const int ci = tt * gridDim.x + tile;
+        if (last_split_arrived(&a.counters[ci], nsplit, &s_last)) {
+            const int64_t stride = rows * n_out;
+            int64_t base[OPT];
+            bool ok[OPT];
+            float sum[OPT];
+#pragma unroll
+            for (int q = 0; q < OPT; ++q) {
+                const int o = q * kNT + tid;
+                const int64_t row = tok0 + o / CT, cg = (int64_t)tile * CT + (o % CT);
+                ok[q] = row < rows && cg < n_out;
+                base[q] = ok[q] ? row * n_out + cg : 0;
+                sum[q] = 0.0f;
+            }
+            for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+                float v[8][OPT];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int q = 0; q < OPT; ++q)
+                        v[u][q] = (sp0 + u < nsplit && ok[q])
+                                      ? load_agent(a.partial + (int64_t)(sp0 + u) * stride + base[q]) : 0.0f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int q = 0; q < OPT; ++q)
+                        if (sp0 + u < nsplit) sum[q] += v[u][q];
+            }
+#pragma unroll
+            for (int q = 0; q < OPT; ++q)
+                if (ok[q]) store_final(a, base[q], sum[q]);
+            if (tid == 0) store_agent(&a.counters[ci], 0);
+        }
+    }
+}
+
 int pow2_tile(int64_t rows, int cap) {
     int bt = 1;
     while (bt < rows && bt < cap) bt *= 2;
@@ -492,9 +684,10 @@ GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16) {
     GemvPlan p{};
     p.lpr = kLPR;
     p.ept = w_is_bf16 ? 8 : 4;
-    p.ct = p.lpr * p.ept;
-    p.n_tiles = (int)ceil_div(n_out, p.ct);
     p.bt = pow2_tile(rows, 16);
+    // 16-token tiles run the MFMA kernel, whose workgroup covers 16 * EPT columns.
+    p.ct = p.bt == 16 ? 16 * p.ept : p.lpr * p.ept;
+    p.n_tiles = (int)ceil_div(n_out, p.ct);
     p.n_tok_tiles = (int)ceil_div(rows, p.bt);
     const int cand_max = 8192 / p.bt < 2048 ? 8192 / p.bt : 2048;   // <= 32 KB of coefficients
     const int64_t base = (int64_t)p.n_tiles * p.n_tok_tiles;
@@ -516,18 +709,27 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
     const int ept = w_is_bf16 ? 8 : 4;
     const int ct = kLPR * ept;
     const int tg = p.bt < 2 ? p.bt : 2;
+    dim3 grid(p.n_tiles, p.nsplit, p.n_tok_tiles);
+    if (p.bt == 16) {
+        const size_t padded = (size_t)p.cand + 3 * 64;
+        size_t lds = padded * 16 * 4 + padded * 4;
+        const size_t lds_red = (size_t)4 * 16 * 16 * ept * 4;
+        if (lds_red > lds) lds = lds_red;
+        if (w_is_bf16) gather_mfma_kernel<1><<<grid, dim3(kNT), lds, stream>>>(a, p.cand, p.nsplit);
+        else gather_mfma_kernel<0><<<grid, dim3(kNT), lds, stream>>>(a, p.cand, p.nsplit);
+        return hipGetLastError();
+    }
     const size_t padded = (size_t)p.cand + 3 * kNSlot * kMaxUnroll;
     size_t lds_a = padded * p.bt * 4 + padded * 4;
     size_t lds_c = (size_t)kNSlot * tg * ct * 4;
     size_t lds = lds_a > lds_c ? lds_a : lds_c;
-    dim3 grid(p.n_tiles, p.nsplit, p.n_tok_tiles);
 #define QS_GEMV_CASE(WB, BTV)                                                              \
     if (w_is_bf16 == WB && p.bt == BTV) {                                                  \
         gather_gemv_kernel<WB, BTV><<<grid, dim3(kNT), lds, stream>>>(a, p.cand, p.nsplit); \
         return hipGetLastError();                                                          \
     }
-    QS_GEMV_CASE(1, 1) QS_GEMV_CASE(1, 2) QS_GEMV_CASE(1, 4) QS_GEMV_CASE(1, 8) QS_GEMV_CASE(1, 16)
-    QS_GEMV_CASE(0, 1) QS_GEMV_CASE(0, 2) QS_GEMV_CASE(0, 4) QS_GEMV_CASE(0, 8) QS_GEMV_CASE(0, 16)
+    QS_GEMV_CASE(1, 1) QS_GEMV_CASE(1, 2) QS_GEMV_CASE(1, 4) QS_GEMV_CASE(1, 8)
+    QS_GEMV_CASE(0, 1) QS_GEMV_CASE(0, 2) QS_GEMV_CASE(0, 4) QS_GEMV_CASE(0, 8)
 #undef QS_GEMV_CASE
     return hipErrorInvalidValue;
 }

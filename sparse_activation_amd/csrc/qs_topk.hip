@@ -565,12 +565,12 @@ __device__ __forceinline__ void unpack_raw(const u32x4_t& w, uint32_t* raw) {
 // kr-th largest key, so no second barrier is needed.  Lane l owns bins
 // 255 - 4l - c (c = 0..3).  Returns the digit and the rank of the wanted key
 // inside its bin.
-template <int NW>
+template <int NS>
 __device__ __forceinline__ void find_digit(const uint32_t (*h)[256], uint32_t kr, int lane,
                                            uint32_t& digit, uint32_t& kr_out) {
     uint32_t c4[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
+    for (int w = 0; w < NS; ++w) {
         const uint4 v = *reinterpret_cast<const uint4*>(&h[w][252 - 4 * lane]);   // bins 252+3-4l .. 252-4l
         c4[0] += v.w; c4[1] += v.z; c4[2] += v.y; c4[3] += v.x;                // descending order
     }
@@ -590,15 +590,16 @@ __device__ __forceinline__ void find_digit(const uint32_t (*h)[256], uint32_t kr
     kr_out = (uint32_t)__builtin_amdgcn_readlane((int)kk, src);
 }
 
-template <int NQ, int KK, int XK>
-__global__ __launch_bounds__(256) void topk_vec_kernel(TopkArgs a) {
-    constexpr int NT = 256, NW = NT / kWave;
+template <int NT, int NQ, int KK, int XK>
+__global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
+    constexpr int NW = NT / kWave;
+    constexpr int NS = NW < 4 ? NW : 4;           // histogram copies (wave % NS)
     constexpr int V = VecOf<KK>::V, CS = V * NT, EPT = NQ * V;
     constexpr int KB = Elem<KK>::kKeyBits;
     constexpr uint32_t kInvalid = 0x80000000u;
     constexpr int kCap = 4096;
     constexpr int ESZ = elem_bytes<KK>();
-    __shared__ uint32_t s_hist[3][NW][256];     // rotating: count, scan, clear
+    __shared__ uint32_t s_hist[3][NS][256];     // rotating: count, scan, clear
     __shared__ uint32_t s_cand[kCap];
     __shared__ uint32_t s_tot[2][NQ][NW];
     __shared__ uint32_t s_cw[NW];
@@ -610,10 +611,7 @@ __global__ __launch_bounds__(256) void topk_vec_kernel(TopkArgs a) {
 
     if (r == 0 && a.zero_ptr != nullptr)
         for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
-#pragma unroll
-    for (int b = 0; b < 3; ++b)
-#pragma unroll
-        for (int w = 0; w < NW; ++w) s_hist[b][w][tid] = 0;
+    for (int i = tid; i < 3 * NS * 256; i += NT) (&s_hist[0][0][0])[i] = 0;
 
     // ---- load runs (past the row end the buffer reads zero)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -676,15 +674,14 @@ __global__ __launch_bounds__(256) void topk_vec_kernel(TopkArgs a) {
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             nzero += (uint32_t)__popcll(__ballot(key[i] == 0u));
-            if (key[i] != kInvalid && key[i] != 0u) atomicAdd(&s_hist[0][wave][key[i] >> shift], 1u);
+            if (key[i] != kInvalid && key[i] != 0u) atomicAdd(&s_hist[0][wave % NS][key[i] >> shift], 1u);
         }
         nzero = __builtin_amdgcn_readfirstlane(nzero);
-        if (lane == 0 && nzero != 0) atomicAdd(&s_hist[0][wave][0], nzero);
+        if (lane == 0 && nzero != 0) atomicAdd(&s_hist[0][wave % NS][0], nzero);
         __syncthreads();
         uint32_t dg;
-        find_digit<NW>(s_hist[0], kr, lane, dg, kr);
-#pragma unroll
-        for (int w = 0; w < NW; ++w) s_hist[2][w][tid] = 0;
+        find_digit<NS>(s_hist[0], kr, lane, dg, kr);
+        for (int i = tid; i < NS * 256; i += NT) (&s_hist[2][0][0])[i] = 0;
         lvl = 1;
         prefix = dg << shift;
         himask |= (0xFFu << shift) & ((1u << KB) - 1u);
@@ -711,7 +708,7 @@ __global__ __launch_bounds__(256) void topk_vec_kernel(TopkArgs a) {
                 __syncthreads();
             }
             // Each thread takes candidates tid, tid + NT, ... into registers once.
-            constexpr int CR = kCap / NT;
+            constexpr int CR = kCap / NT;                 // 16 (NT 256) or 4 (NT 1024)
             uint32_t cand[CR];
 #pragma unroll
             for (int i = 0; i < CR; ++i) {
@@ -729,18 +726,17 @@ __global__ __launch_bounds__(256) void topk_vec_kernel(TopkArgs a) {
                     for (int i = 0; i < CR; ++i) {
                         if ((uint32_t)(i * NT) >= nc) break;     // uniform
                         if ((cand[i] & himask) == prefix)
-                            atomicAdd(&hb[wave][(cand[i] >> nshift) & dmask], 1u);
+                            atomicAdd(&hb[wave % NS][(cand[i] >> nshift) & dmask], 1u);
                     }
                 } else {
 #pragma unroll
                     for (int i = 0; i < EPT; ++i)
                         if ((key[i] & himask) == prefix)
-                            atomicAdd(&hb[wave][(key[i] >> nshift) & dmask], 1u);
+                            atomicAdd(&hb[wave % NS][(key[i] >> nshift) & dmask], 1u);
                 }
                 __syncthreads();
-                find_digit<NW>(hb, kr, lane, dg, kr);
-#pragma unroll
-                for (int w = 0; w < NW; ++w) s_hist[(lvl + 2) % 3][w][tid] = 0;
+                find_digit<NS>(hb, kr, lane, dg, kr);
+                for (int i = tid; i < NS * 256; i += NT) (&s_hist[(lvl + 2) % 3][0][0])[i] = 0;
                 ++lvl;
                 prefix |= dg << nshift;
                 himask |= dmask << nshift;
@@ -879,27 +875,40 @@ __global__ __launch_bounds__(256) void topk_vec_kernel(TopkArgs a) {
     }
 }
 
+// Vectorised kernel with block size B, runs per thread chosen from the row length.
+template <int B, int KK, int XK>
+hipError_t launch_vec(int64_t rows, const TopkArgs& a, hipStream_t stream) {
+    constexpr int V = VecOf<KK>::V, CS = V * B;
+    constexpr int kMaxVecD = 16384;
+    const dim3 grid((unsigned)rows), block(B);
+    const int64_t nq = (a.d + CS - 1) / CS;
+    if (nq <= 1) topk_vec_kernel<B, 1, KK, XK><<<grid, block, 0, stream>>>(a);
+    else if (nq <= 2) topk_vec_kernel<B, 2, KK, XK><<<grid, block, 0, stream>>>(a);
+    else if constexpr (kMaxVecD / CS >= 4) {
+        if (nq <= 3) topk_vec_kernel<B, 3, KK, XK><<<grid, block, 0, stream>>>(a);
+        else if (nq <= 4) topk_vec_kernel<B, 4, KK, XK><<<grid, block, 0, stream>>>(a);
+        else if constexpr (kMaxVecD / CS >= 8) {
+            if (nq <= 8) topk_vec_kernel<B, 8, KK, XK><<<grid, block, 0, stream>>>(a);
+            else if constexpr (kMaxVecD / CS >= 16) {
+                if (nq <= 12) topk_vec_kernel<B, 12, KK, XK><<<grid, block, 0, stream>>>(a);
+                else topk_vec_kernel<B, 16, KK, XK><<<grid, block, 0, stream>>>(a);
+            }
+        }
+    }
+    return hipGetLastError();
+}
+
 template <int NT, int KK, int XK>
 hipError_t launch_kkx(int64_t rows, const TopkArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)rows), block(NT);
-    constexpr int R = 256;   // the register-resident kernels always run 4 waves
-    constexpr int V = VecOf<KK>::V, CS = V * R;
-    constexpr int kMaxVecD = 16384;               // 64 registers of entries per thread
-    if (a.d % V == 0 && a.d <= kMaxVecD) {
-        const int64_t nq = (a.d + CS - 1) / CS;
-        if (nq <= 1) topk_vec_kernel<1, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
-        else if (nq <= 2) topk_vec_kernel<2, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
-        else if constexpr (kMaxVecD / CS >= 4) {
-            if (nq <= 4) topk_vec_kernel<4, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
-            else if constexpr (kMaxVecD / CS >= 8) {
-                if (nq <= 8) topk_vec_kernel<8, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
-                else if constexpr (kMaxVecD / CS >= 16) {
-                    if (nq <= 12) topk_vec_kernel<12, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
-                    else topk_vec_kernel<16, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
-                }
-            }
-        }
-        return hipGetLastError();
+    constexpr int R = 256;   // the register-resident scalar kernel runs 4 waves
+    constexpr int V = VecOf<KK>::V;
+    if (a.d % V == 0 && a.d <= 16384) {
+        // Few rows (decode): 16 waves per row hide each other's latencies;
+        // many rows: 4 waves per row and many rows per CU.
+        if (rows <= 64 && a.d >= 1024 * V) return launch_vec<1024, KK, XK>(rows, a, stream);
+        if (rows <= 64 && a.d >= 512 * V) return launch_vec<512, KK, XK>(rows, a, stream);
+        return launch_vec<256, KK, XK>(rows, a, stream);
     }
     if (a.d <= 4 * R) {
         topk_reg_kernel<R, 4, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
