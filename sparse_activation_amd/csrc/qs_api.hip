@@ -67,7 +67,7 @@ LinearWs linear_ws(char* base, int64_t rows, int64_t d_in, int64_t n_out) {
     LinearWs w{};
     w.counters = (int32_t*)c.take(sizeof(int32_t) * (size_t)(pb.n_counters > pf.n_counters ? pb.n_counters : pf.n_counters));
     w.xs = (float*)c.take(sizeof(float) * (size_t)rows * d_in);
-    w.partial = (float*)c.take(sizeof(float) * max_sz(pb.partial_floats, pf.partial_floats));
+    w.partial = (float*)c.take(sizeof(float) * max_sz(pb.scratch_floats, pf.scratch_floats));
     w.xm = (uint16_t*)c.take(sizeof(uint16_t) * (size_t)rows * d_in);
     w.bytes = c.off;
     return w;
@@ -90,7 +90,7 @@ GatherWs gather_ws(char* base, int64_t rows, int64_t d_in, int64_t n_out) {
     c.base = base;
     GatherWs w{};
     w.counters = (int32_t*)c.take(sizeof(int32_t) * kGatherCounters);
-    w.partial = (float*)c.take(sizeof(float) * max_sz(pb.partial_floats, pf.partial_floats));
+    w.partial = (float*)c.take(sizeof(float) * max_sz(pb.scratch_floats, pf.scratch_floats));
     w.bytes = c.off;
     return w;
 }
@@ -136,11 +136,11 @@ FfnWs ffn_ws(char* base, int64_t rows, int64_t d, int64_t ffn, bool drelu) {
     if (!drelu) {
         qs::GemvPlan ub = qs::plan_gemv(rows, d, ffn, 1), uf = qs::plan_gemv(rows, d, ffn, 0);
         up_ctr = (size_t)(ub.n_counters > uf.n_counters ? ub.n_counters : uf.n_counters);
-        up_part = max_sz(ub.partial_floats, uf.partial_floats);
+        up_part = max_sz(ub.scratch_floats, uf.scratch_floats);
     }
     qs::GemvPlan db = qs::plan_gemv(rows, ffn, d, 1), df = qs::plan_gemv(rows, ffn, d, 0);
     size_t down_ctr = (size_t)(db.n_counters > df.n_counters ? db.n_counters : df.n_counters);
-    size_t down_part = max_sz(db.partial_floats, df.partial_floats);
+    size_t down_part = max_sz(db.scratch_floats, df.scratch_floats);
     w.n_ctr = (int)(up_ctr + down_ctr);
     w.ctr_up = (int32_t*)c.take(sizeof(int32_t) * (up_ctr + down_ctr));
     w.ctr_down = w.ctr_up ? w.ctr_up + up_ctr : nullptr;
@@ -275,6 +275,7 @@ qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_i
     g.xs = wsp.xs; g.rows = rows; g.d_in = d_in; g.n_out = n_out; g.w = w;
     g.partial = wsp.partial; g.counters = wsp.counters; g.y = y; g.y_bf16 = yt == QS_BF16;
     g.epilogue = qs::EPI_STORE;
+    g.xs_bf16 = xt == QS_BF16;
     e = qs::launch_gemv(plan, wb, g, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
@@ -411,6 +412,7 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
         g.xs = wsp.xs1; g.rows = rows; g.d_in = d; g.n_out = ffn; g.w = w_up;
         g.partial = wsp.partial; g.counters = wsp.ctr_up; g.y = hbuf; g.y_bf16 = 0;
         g.epilogue = qs::EPI_RELU2;
+        g.xs_bf16 = dt == QS_BF16;
         e = qs::launch_gemv(pu, wb, g, st);
         if (e != hipSuccess) return hip_fail(e, fn);
     } else {

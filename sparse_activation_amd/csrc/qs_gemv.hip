@@ -49,6 +49,14 @@ int target_wg() {
     return v;
 }
 
+// Integer tuning knob from the environment, clamped to [lo, hi].
+int env_int(const char* name, int dflt, int lo, int hi) {
+    const char* e = getenv(name);
+    int t = e ? atoi(e) : dflt;
+    if (t <= 0) t = dflt;
+    return t < lo ? lo : t > hi ? hi : t;
+}
+
 __device__ __forceinline__ uint32_t popc_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -493,6 +501,270 @@ __global__ __launch_bounds__(kNT) void gather_mfma_kernel(GemvArgs a, int cand, 
     }
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- bf16 MFMA gather
+// 16-token tiles with bf16 weights run on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16): tokens are the M side, a group of 32 consecutive
+// input rows one k-step, 16 columns the N side.  Each fp32 coefficient c is
+// split as hi = bf16(c), lo = bf16(c - hi): hi + lo keeps 16 significant bits,
+// the products with bf16 weights are exact in the fp32 accumulator, and lo is
+// dropped when the coefficients are bf16 values (bf16 activations).
+//
+// A fragment kernel rewrites X (.) M once, elementwise, into the MFMA A-operand
+// layout, plus one 32-bit mask per row group whose bit i says that row i of the
+// group is selected by at least one of the 16 tokens.  The gather kernel issues
+// the loads of unselected rows at an out-of-range buffer offset, so they move no
+// memory: the bytes read are those of the union of the tokens' selections.
+//
+// Per token tile tt (groups_total = ceil(d_in / 32)):
+//   frag[tt][g][hi|lo][64 lanes] u32x4: lane 16 q + t holds token t's
+//       coefficients of rows 32 g + 8 q .. 32 g + 8 q + 7
+//   mask[tt][g] u32
+constexpr int kBGroup = 32;
+constexpr int kBCols = 64;
+
+struct BFrag {
+    u32x4* frag;
+    uint32_t* mask;
+    int64_t groups;     // groups_total
+};
+
+__host__ __device__ inline size_t bfrag_bytes(int64_t d_in, int n_tok_tiles) {
+    const int64_t groups = (d_in + kBGroup - 1) / kBGroup;
+    const size_t masks = ((size_t)n_tok_tiles * groups * 4 + 255) / 256 * 256;
+    return masks + (size_t)n_tok_tiles * groups * 2 * 64 * 16;
+}
+
+__host__ inline BFrag bfrag_carve(void* base, int64_t d_in, int n_tok_tiles) {
+    const int64_t groups = (d_in + kBGroup - 1) / kBGroup;
+    BFrag f;
+    f.groups = groups;
+    f.mask = static_cast<uint32_t*>(base);
+    f.frag = reinterpret_cast<u32x4*>(static_cast<char*>(base) +
+                                      ((size_t)n_tok_tiles * groups * 4 + 255) / 256 * 256);
+    return f;
+}
+
+// One wave per row group: lane 16 q + t converts rows 32 g + 8 q .. + 7 of
+// token t.  Grid (ceil(groups / 4), token tiles), 256 threads.
+__global__ __launch_bounds__(kNT) void bfrag_kernel(const float* xs, int64_t rows, int64_t d_in,
+                                                   int use_lo, BFrag bf) {
+    constexpr int BT = 16;
+    const int tt = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (g >= bf.groups) return;
+    const int q = lane >> 4, t = lane & 15;
+    const int64_t tok0 = (int64_t)tt * BT;
+    const int64_t ntok = min((int64_t)BT, rows - tok0);
+    const int64_t j = g * kBGroup + 8 * q;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(xs + tok0 * d_in), (short)0, (int)(ntok * d_in * 4), 0x00020000);
+    const uint32_t o = t < ntok ? (uint32_t)((t * d_in + j) * 4) : kOOB;
+    const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(xr, o, 0, 0);
+    const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(xr, o + 16, 0, 0);
+    const uint32_t u[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t hw[4], lw[4], rowbits = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float c = j + e < d_in ? __uint_as_float(u[e]) : 0.0f;
+        const uint32_t hi = f32_to_bf16_rne(c);
+        const uint32_t lo = f32_to_bf16_rne(c - __uint_as_float(hi << 16));
+        if (e & 1) {
+            hw[e >> 1] |= hi << 16;
+            lw[e >> 1] |= lo << 16;
+        } else {
+            hw[e >> 1] = hi;
+            lw[e >> 1] = lo;
+        }
+        // Row 8 q + e of the group is selected by some token iff one of the 16
+        // lanes with this q sees a nonzero coefficient.
+        const uint64_t b = __ballot(c != 0.0f);
+        rowbits |= (uint32_t)((b >> (16 * 0)) & 0xFFFFu ? 1u : 0u) << (e);
+        rowbits |= (uint32_t)((b >> (16 * 1)) & 0xFFFFu ? 1u : 0u) << (8 + e);
+        rowbits |= (uint32_t)((b >> (16 * 2)) & 0xFFFFu ? 1u : 0u) << (16 + e);
+        rowbits |= (uint32_t)((b >> (16 * 3)) & 0xFFFFu ? 1u : 0u) << (24 + e);
+    }
+    const size_t base = ((size_t)tt * bf.groups + g) * 128;
+    bf.frag[base + lane] = (u32x4){hw[0], hw[1], hw[2], hw[3]};
+    if (use_lo) bf.frag[base + 64 + lane] = (u32x4){lw[0], lw[1], lw[2], lw[3]};
+    if (lane == 0) bf.mask[(size_t)tt * bf.groups + g] = rowbits;
+}
+
+// Streams rows split * cand .. + cand for a 64-column tile.  Wave w takes groups
+// w, w + 4, ... of the split; per stage a lane (r8 = lane / 8, c8 = lane % 8)
+// loads columns 8 c8 .. 8 c8 + 7 of rows 4 r8 .. 4 r8 + 3 of the group (whole
+// 128-byte row segments), which a per-wave LDS tile turns into the k-major B
+// operand.  The row mask of a group is fetched one stage ahead of its weights.
+__global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf, int cand, int nsplit,
+                                                          int use_lo) {
+    constexpr int BT = 16;
+    constexpr int OPT = BT * kBCols / kNT;    // outputs per thread in the reductions (4)
+    __shared__ __attribute__((aligned(16))) uint16_t s_tr[4 * kBGroup * kBCols];   // 16 KB
+    __shared__ int s_last;
+
+    const int tile = blockIdx.x, split = blockIdx.y, tt = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t rows = a.rows, n_out = a.n_out;
+    const int64_t tok0 = (int64_t)tt * BT;
+    const int64_t g0 = (int64_t)split * (cand / kBGroup);
+    const int64_t gl = min((int64_t)(cand / kBGroup), bf.groups - g0);   // groups of this split
+    const int nst = (int)((gl + 3) / 4);
+
+    const __amdgpu_buffer_rsrc_t mrr = __builtin_amdgcn_make_buffer_rsrc(
+        bf.mask + (size_t)tt * bf.groups + g0, (short)0, (int)(gl * 4), 0x00020000);
+    const __amdgpu_buffer_rsrc_t frr = __builtin_amdgcn_make_buffer_rsrc(
+        bf.frag + ((size_t)tt * bf.groups + g0) * 128, (short)0, (int)(gl * 128 * 16), 0x00020000);
+    const int r8 = lane >> 3, c8 = lane & 7;
+    const int kq = lane >> 4, n16 = lane & 15;
+    const int64_t col = (int64_t)tile * kBCols + 8 * c8;
+    const uint32_t colb = col < n_out ? (uint32_t)(col * 2) : kOOB;
+    const uint32_t rowbytes = (uint32_t)(n_out * 2);
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, a.d_in * n_out * 2);
+    // Byte offset of row 4 r8 of group 0 of the split.
+    const uint32_t rowb0 = (uint32_t)((g0 * kBGroup + 4 * r8) * rowbytes);
+    uint16_t* tr = s_tr + wave * kBGroup * kBCols;
+
+    auto load_mask = [&](int s) {
+        return __builtin_amdgcn_raw_buffer_load_b32(mrr, (uint32_t)((4 * s + wave) * 4), 0, 0);
+    };
+    auto load_w = [&](u32x4* w, uint32_t m, int s) {
+        const uint32_t rb = rowb0 + (uint32_t)((4 * s + wave) * kBGroup) * rowbytes + colb;
+        const uint32_t bits = m >> (4 * r8);
+        w[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, bits & 1u ? rb : kOOB, 0, 0);
+        w[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, bits & 2u ? rb + rowbytes : kOOB, 0, 0);
+        w[2] = __builtin_amdgcn_raw_buffer_load_b128(rs, bits & 4u ? rb + 2 * rowbytes : kOOB, 0, 0);
+        w[3] = __builtin_amdgcn_raw_buffer_load_b128(rs, bits & 8u ? rb + 3 * rowbytes : kOOB, 0, 0);
+    };
+    auto load_f = [&](u32x4* f, int s) {
+        const uint32_t fo = (uint32_t)(((4 * s + wave) * 128 + lane) * 16);
+        f[0] = __builtin_amdgcn_raw_buffer_load_b128(frr, fo, 0, 0);
+        f[1] = __builtin_amdgcn_raw_buffer_load_b128(frr, use_lo ? fo + 64 * 16 : kOOB, 0, 0);
+    };
+    f32x4_t acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    auto mfma_stage = [&](const u32x4* w, const u32x4* f, uint32_t m, int s) {
+        if (4 * s + wave >= gl || __builtin_amdgcn_readfirstlane(m) == 0) return;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = 4 * r8 + q;
+            *reinterpret_cast<u32x4*>(tr + row * kBCols + ((c8 ^ (2 * (row >> 3))) * 8)) = w[q];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int cidx = ((2 * t + (n16 >> 3)) ^ (2 * kq)) * 8 + (n16 & 7);
+            uint32_t bw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo16 = tr[(8 * kq + 2 * e) * kBCols + cidx];
+                const uint32_t hi16 = tr[(8 * kq + 2 * e + 1) * kBCols + cidx];
+                bw[e] = lo16 | (hi16 << 16);
+            }
+            const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, (u32x4){bw[0], bw[1], bw[2], bw[3]});
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f[0]), bv,
+                                                            acc[t], 0, 0, 0);
+            if (use_lo)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f[1]),
+                                                                bv, acc[t], 0, 0, 0);
+        }
+    };
+    // The prologue issues the loads in the loop's own order, so the wait
+    // counts at the loop head are the steady-state ones.
+    u32x4 wa[4], wb[4], fa[2], fb[2];
+    uint32_t ma = load_mask(0), mb = load_mask(1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(wa, ma, 0);
+    load_f(fa, 0);
+    uint32_t mc = load_mask(2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(wb, mb, 1);
+    load_f(fb, 1);
+    uint32_t md = load_mask(3);
+    for (int s = 0; s < nst; s += 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_stage(wa, fa, ma, s);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(wa, mc, s + 2);
+        load_f(fa, s + 2);
+        ma = mc;
+        mc = load_mask(s + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_stage(wb, fb, mb, s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(wb, md, s + 3);
+        load_f(fb, s + 3);
+        mb = md;
+        md = load_mask(s + 5);
+    }
+    __syncthreads();   // the transpose tiles are dead: reuse them for the wave reduction
+
+    // Phase C: register v of MFMA t is token 4 kq + v, column 16 t + n16.
+    float* s_red = reinterpret_cast<float*>(s_tr);   // [4][16][64]
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            s_red[(wave * BT + 4 * kq + v) * kBCols + 16 * t + n16] = acc[t][v];
+    __syncthreads();
+    float outv[OPT];
+#pragma unroll
+    for (int q = 0; q < OPT; ++q) {
+        const int o = q * kNT + tid;
+        float sum = s_red[o];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) sum += s_red[w * BT * kBCols + o];
+        outv[q] = sum;
+    }
+#pragma unroll
+    for (int q = 0; q < OPT; ++q) {
+        const int o = q * kNT + tid;
+        const int64_t row = tok0 + o / kBCols, cg = (int64_t)tile * kBCols + (o % kBCols);
+        if (row < rows && cg < n_out) {
+            if (nsplit == 1) store_final(a, row * n_out + cg, outv[q]);
+            else store_agent(&a.partial[((int64_t)split * rows + row) * n_out + cg], outv[q]);
+        }
+    }
+
+    // Phase D: the last workgroup of the tile sums the partials in split order.
+    if (nsplit > 1) {
+        const int ci = tt * gridDim.x + tile;
+        if (last_split_arrived(&a.counters[ci], nsplit, &s_last)) {
+            const int64_t stride = rows * n_out;
+            int64_t base[OPT];
+            bool ok[OPT];
+            float sum[OPT];
+#pragma unroll
+            for (int q = 0; q < OPT; ++q) {
+                const int o = q * kNT + tid;
+                const int64_t row = tok0 + o / kBCols, cg = (int64_t)tile * kBCols + (o % kBCols);
+                ok[q] = row < rows && cg < n_out;
+                base[q] = ok[q] ? row * n_out + cg : 0;
+                sum[q] = 0.0f;
+            }
+            for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+                float v[8][OPT];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int q = 0; q < OPT; ++q)
+                        v[u][q] = (sp0 + u < nsplit && ok[q])
+                                      ? load_agent(a.partial + (int64_t)(sp0 + u) * stride + base[q]) : 0.0f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int q = 0; q < OPT; ++q)
+                        if (sp0 + u < nsplit) sum[q] += v[u][q];
+            }
+#pragma unroll
+            for (int q = 0; q < OPT; ++q)
+                if (ok[q]) store_final(a, base[q], sum[q]);
+            if (tid == 0) store_agent(&a.counters[ci], 0);
+        }
+    }
+}
+
 int pow2_tile(int64_t rows, int cap) {
     int bt = 1;
     while (bt < rows && bt < cap) bt *= 2;
@@ -685,21 +957,36 @@ GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16) {
     p.lpr = kLPR;
     p.ept = w_is_bf16 ? 8 : 4;
     p.bt = pow2_tile(rows, 16);
-    // 16-token tiles run the MFMA kernel, whose workgroup covers 16 * EPT columns.
-    p.ct = p.bt == 16 ? 16 * p.ept : p.lpr * p.ept;
+    // 16-token tiles run an MFMA kernel: bf16 weights in 64-column tiles on the
+    // bf16 matrix cores, fp32 weights in 16 * EPT-column tiles on the fp32 ones.
+    const bool bmfma = p.bt == 16 && w_is_bf16;
+    p.ct = bmfma ? kBCols : p.bt == 16 ? 16 * p.ept : p.lpr * p.ept;
     p.n_tiles = (int)ceil_div(n_out, p.ct);
     p.n_tok_tiles = (int)ceil_div(rows, p.bt);
-    const int cand_max = 8192 / p.bt < 2048 ? 8192 / p.bt : 2048;   // <= 32 KB of coefficients
     const int64_t base = (int64_t)p.n_tiles * p.n_tok_tiles;
-    int64_t ns = ceil_div(target_wg(), base);
-    if (ns < 1) ns = 1;
-    int64_t cand = ceil_div(ceil_div(d_in, ns), 64) * 64;
-    if (cand > cand_max) cand = cand_max;
-    if (cand < 64) cand = 64;
+    int64_t cand;
+    if (bmfma) {
+        // As many splits as keep every workgroup resident at once (three per
+        // CU), in whole 4-group stages.
+        const int64_t cap = env_int("QS_BMFMA_RESIDENT_WG", 768, 1, 1 << 16);
+        int64_t ns = cap / base;
+        if (ns < 1) ns = 1;
+        cand = ceil_div(ceil_div(d_in, ns), 4 * kBGroup) * 4 * kBGroup;
+    } else {
+        // The FMA kernels stage <= 32 KB of coefficients in LDS.
+        const int cand_max = 8192 / p.bt < 2048 ? 8192 / p.bt : 2048;
+        int64_t ns = ceil_div(target_wg(), base);
+        if (ns < 1) ns = 1;
+        cand = ceil_div(ceil_div(d_in, ns), 64) * 64;
+        if (cand > cand_max) cand = cand_max;
+        if (cand < 64) cand = 64;
+    }
     p.cand = (int)cand;
     p.nsplit = (int)ceil_div(d_in, cand);
     if (p.nsplit < 1) p.nsplit = 1;
     p.partial_floats = p.nsplit > 1 ? (size_t)p.nsplit * rows * n_out : 0;
+    p.prep_bytes = bmfma ? bfrag_bytes(d_in, p.n_tok_tiles) : 0;
+    p.scratch_floats = (p.partial_floats * 4 + 255) / 256 * 64 + (p.prep_bytes + 3) / 4;
     p.n_counters = p.n_tiles * p.n_tok_tiles;
     return p;
 }
@@ -710,6 +997,15 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
     const int ct = kLPR * ept;
     const int tg = p.bt < 2 ? p.bt : 2;
     dim3 grid(p.n_tiles, p.nsplit, p.n_tok_tiles);
+    if (p.bt == 16 && w_is_bf16) {
+        const BFrag bf = bfrag_carve(reinterpret_cast<char*>(a.partial) + (p.partial_floats * 4 + 255) / 256 * 256,
+                                     a.d_in, p.n_tok_tiles);
+        const int use_lo = a.xs_bf16 ? 0 : 1;
+        bfrag_kernel<<<dim3((unsigned)ceil_div(bf.groups, 4), p.n_tok_tiles), dim3(kNT), 0, stream>>>(
+            a.xs, a.rows, a.d_in, use_lo, bf);
+        gather_bmfma_kernel<<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
+        return hipGetLastError();
+    }
     if (p.bt == 16) {
         const size_t padded = (size_t)p.cand + 3 * 64;
         size_t lds = padded * 16 * 4 + padded * 4;

@@ -61,6 +61,8 @@ struct GemvPlan {
     int cand;         // candidate input rows per split
     int nsplit;
     size_t partial_floats;  // nsplit * rows * n_out (0 if nsplit == 1)
+    size_t prep_bytes;      // compacted-row records of the bf16 MFMA kernel (0 otherwise)
+    size_t scratch_floats;  // workspace behind GemvArgs::partial: partials, then prep records
     int n_counters;         // n_tiles * n_tok_tiles
 };
 GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16);
@@ -69,11 +71,12 @@ struct GemvArgs {
     const float* xs;       // [rows, d_in] fp32, zero where not selected
     int64_t rows, d_in, n_out;
     const void* w;         // W^T [d_in, n_out], fp32 or bf16
-    float* partial;        // [nsplit, rows, n_out]
+    float* partial;        // [scratch_floats]: [nsplit, rows, n_out] partials, prep records
     int32_t* counters;     // [n_counters], zero on entry, left zero on exit
     void* y;               // [rows, n_out]
     int y_bf16;            // output dtype
     int epilogue;          // EPI_STORE or EPI_RELU2 (then y is fp32 h)
+    int xs_bf16;           // 1: every xs value is a bf16 number (from bf16 activations)
 };
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 
