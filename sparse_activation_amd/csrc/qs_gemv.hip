@@ -601,8 +601,8 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
                                                           int use_lo) {
     constexpr int BT = 16;
     constexpr int OPT = BT * kBCols / kNT;    // outputs per thread in the reductions (4)
-    __shared__ __attribute__((aligned(16))) uint16_t s_tr[4 * kBGroup * kBCols];   // 16 KB
-    __shared__ int s_last;
+    // 16 KB in all: the split-K arrival flag reuses the tile once it is dead.
+    __shared__ __attribute__((aligned(16))) uint16_t s_tr[4 * kBGroup * kBCols];
 
     const int tile = blockIdx.x, split = blockIdx.y, tt = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -672,14 +672,16 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
     };
     // The prologue issues the loads in the loop's own order, so the wait
     // counts at the loop head are the steady-state ones.
+    // The first two stages load every row without waiting for their masks
+    // (a skipped row only saves bandwidth; its coefficients are zero).
     u32x4 wa[4], wb[4], fa[2], fb[2];
     uint32_t ma = load_mask(0), mb = load_mask(1);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(wa, ma, 0);
+    load_w(wa, 0xFFFFFFFFu, 0);
     load_f(fa, 0);
     uint32_t mc = load_mask(2);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(wb, mb, 1);
+    load_w(wb, 0xFFFFFFFFu, 1);
     load_f(fb, 1);
     uint32_t md = load_mask(3);
     for (int s = 0; s < nst; s += 2) {
@@ -730,7 +732,7 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
     // Phase D: the last workgroup of the tile sums the partials in split order.
     if (nsplit > 1) {
         const int ci = tt * gridDim.x + tile;
-        if (last_split_arrived(&a.counters[ci], nsplit, &s_last)) {
+        if (last_split_arrived(&a.counters[ci], nsplit, reinterpret_cast<int*>(s_tr))) {
             const int64_t stride = rows * n_out;
             int64_t base[OPT];
             bool ok[OPT];

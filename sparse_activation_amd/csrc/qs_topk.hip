@@ -590,19 +590,80 @@ __device__ __forceinline__ void find_digit(const uint32_t (*h)[256], uint32_t kr
     kr_out = (uint32_t)__builtin_amdgcn_readlane((int)kk, src);
 }
 
+// Descending search of a histogram of 64 P bins (ascending bin index = digit)
+// held in LDS, done redundantly by every wavefront: lane l owns bins
+// 64 P - 1 - P l - c (c = 0 .. P - 1).  Returns the digit holding the kr-th
+// largest counted key, the rank of that key inside its bin and the bin count.
+template <int P>
+__device__ __forceinline__ void find_digit_p(const uint32_t* h, uint32_t kr, int lane,
+                                             uint32_t& digit, uint32_t& kr_out, uint32_t& cnt_out) {
+    static_assert(P % 4 == 0, "lanes own whole 16-byte groups of bins");
+    uint32_t c[P];
+#pragma unroll
+    for (int g = 0; g < P / 4; ++g) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&h[64 * P - P * (lane + 1) + P - 4 * (g + 1)]);
+        c[4 * g] = v.w; c[4 * g + 1] = v.z; c[4 * g + 2] = v.y; c[4 * g + 3] = v.x;
+    }
+    uint32_t lsum = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) lsum += c[i];
+    const uint32_t incl = wave_incl_scan_dpp(lsum);
+    const uint32_t excl = incl - lsum;
+    const uint64_t bm = __ballot(excl < kr && kr <= incl);
+    const int src = (int)__builtin_ctzll(bm);
+    uint32_t e = excl, dg = 0, kk = 0, cn = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        if (!found && e < kr && kr <= e + c[i]) {
+            found = true;
+            dg = (uint32_t)(64 * P - 1 - P * lane - i);
+            kk = kr - e;
+            cn = c[i];
+        }
+        e += c[i];
+    }
+    digit = (uint32_t)__builtin_amdgcn_readlane((int)dg, src);
+    kr_out = (uint32_t)__builtin_amdgcn_readlane((int)kk, src);
+    cnt_out = (uint32_t)__builtin_amdgcn_readlane((int)cn, src);
+}
+
+// Descending search over n <= 64 counts t[n - 1], ..., t[0] given in LDS:
+// lane c takes t[n - 1 - c], one wave scan finds the first (from the top) whose
+// running total reaches kr.  Returns its index and the total above it.
+__device__ __forceinline__ void find_top_lane(const uint32_t* t, int n, uint32_t kr, int lane,
+                                              int& idx, uint32_t& before) {
+    const uint32_t v = lane < n ? t[n - 1 - lane] : 0u;
+    const uint32_t incl = wave_incl_scan_dpp(v);
+    const uint64_t bm = __ballot(incl >= kr);
+    const int f = bm ? (int)__builtin_ctzll(bm) : n - 1;
+    idx = n - 1 - f;
+    before = (uint32_t)__builtin_amdgcn_readlane((int)(incl - v), f);
+}
+
 template <int NT, int NQ, int KK, int XK>
 __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
     constexpr int NW = NT / kWave;
-    constexpr int NS = NW < 4 ? NW : 4;           // histogram copies (wave % NS)
     constexpr int V = VecOf<KK>::V, CS = V * NT, EPT = NQ * V;
     constexpr int KB = Elem<KK>::kKeyBits;
     constexpr uint32_t kInvalid = 0x80000000u;
-    constexpr int kCap = 4096;
     constexpr int ESZ = elem_bytes<KK>();
-    __shared__ uint32_t s_hist[3][NS][256];     // rotating: count, scan, clear
+    // Digits: the first covers the top min(KB, 12) key bits (4096 bins, so
+    // that the few exponent values an activation spans spread over 16 bins
+    // each), the next ones 8 bits.  Every level has its own histogram,
+    // cleared once at the start.
+    constexpr int W1 = KB < 12 ? KB : 12;
+    constexpr int S1 = KB - W1;
+    constexpr int NB1 = 1 << W1;
+    constexpr int NB1P = NB1 < 256 ? 256 : NB1;
+    constexpr int kCap = 2048;    // boundary-bin keys finished by one wavefront
+    __shared__ __attribute__((aligned(16))) uint32_t s_h1[NB1P];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hl[3][256];
     __shared__ uint32_t s_cand[kCap];
+    __shared__ uint32_t s_chunk[16];
+    __shared__ uint32_t s_res[4];
+    __shared__ uint32_t s_nc;
     __shared__ uint32_t s_tot[2][NQ][NW];
-    __shared__ uint32_t s_cw[NW];
     __shared__ float s_max[NW];
 
     const int r = blockIdx.x;
@@ -611,7 +672,9 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
 
     if (r == 0 && a.zero_ptr != nullptr)
         for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
-    for (int i = tid; i < 3 * NS * 256; i += NT) (&s_hist[0][0][0])[i] = 0;
+    for (int i = tid; i < NB1P; i += NT) s_h1[i] = 0;
+    for (int i = tid; i < 3 * 256; i += NT) (&s_hl[0][0])[i] = 0;
+    if (tid == 0) s_nc = 0;
 
     // ---- load runs (past the row end the buffer reads zero)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -660,89 +723,104 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
     __syncthreads();   // histograms cleared
 
     // ---- select
-    // Level L counts into buffer L % 3 and clears buffer (L + 2) % 3, whose last
-    // reader (level L - 1) finished before level L's barrier and whose next
-    // writer (level L + 2) starts after level L + 1's barrier.
-    uint32_t prefix = 0, himask = kInvalid, kr = (uint32_t)k;
-    if (k > 0) {
-        int shift = KB > 8 ? KB - 8 : 0;
-        int lvl = 0;
-        // level 1 over every entry.  Zero keys (frequent: an FFN intermediate
-        // is often half zeros) are counted with a ballot instead of piling
-        // conflicting atomics onto bin 0.
+    // Count the entries that match the prefix into digit bins.  Zero keys
+    // (frequent: an FFN intermediate is often half zeros) are counted with a
+    // ballot instead of piling conflicting atomics onto bin 0.
+    auto count_level = [&](uint32_t* hist, uint32_t pre, uint32_t hm, int sh, uint32_t dm) {
         uint32_t nzero = 0;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
-            nzero += (uint32_t)__popcll(__ballot(key[i] == 0u));
-            if (key[i] != kInvalid && key[i] != 0u) atomicAdd(&s_hist[0][wave % NS][key[i] >> shift], 1u);
+            const bool m = key[i] != kInvalid && (key[i] & hm) == pre;
+            nzero += (uint32_t)__popcll(__ballot(m && key[i] == 0u));
+            if (m && key[i] != 0u) atomicAdd(&hist[(key[i] >> sh) & dm], 1u);
         }
         nzero = __builtin_amdgcn_readfirstlane(nzero);
-        if (lane == 0 && nzero != 0) atomicAdd(&s_hist[0][wave % NS][0], nzero);
+        if (lane == 0 && nzero != 0) atomicAdd(&hist[0], nzero);
+    };
+    uint32_t prefix = 0, himask = 0, kr = (uint32_t)k, eqtot = 0;
+    if (k > 0) {
+        uint32_t dg, cnt;
+        count_level(s_h1, 0u, 0u, S1, (uint32_t)(NB1 - 1));
         __syncthreads();
-        uint32_t dg;
-        find_digit<NS>(s_hist[0], kr, lane, dg, kr);
-        for (int i = tid; i < NS * 256; i += NT) (&s_hist[2][0][0])[i] = 0;
-        lvl = 1;
-        prefix = dg << shift;
-        himask |= (0xFFu << shift) & ((1u << KB) - 1u);
-        if (shift > 0) {
-            // compact the candidates
-            uint32_t cw = 0;
-#pragma unroll
-            for (int i = 0; i < EPT; ++i) cw += (uint32_t)__popcll(__ballot((key[i] & himask) == prefix));
-            cw = __builtin_amdgcn_readfirstlane(cw);
-            if (lane == 0) s_cw[wave] = cw;
+        // The digit searches below run in one wavefront while the others wait
+        // at the next barrier: a search done by all 16 wavefronts of a row
+        // costs four times over on each SIMD.
+        if constexpr (NB1 > 1024) {
+            for (int c = wave; c < NB1 / 256; c += NW) {
+                const uint4 v = *reinterpret_cast<const uint4*>(&s_h1[256 * c + 4 * lane]);
+                const uint32_t t = wave_incl_scan_dpp(v.x + v.y + v.z + v.w);
+                if (lane == kWave - 1) s_chunk[c] = t;
+            }
             __syncthreads();
-            uint32_t run = 0, nc = 0;
+            if (wave == 0) {
+                int cstar;
+                uint32_t before;
+                find_top_lane(s_chunk, NB1 / 256, kr, lane, cstar, before);
+                find_digit_p<4>(s_h1 + 256 * cstar, kr - before, lane, dg, kr, cnt);
+                dg += (uint32_t)(256 * cstar);
+            }
+        } else if (wave == 0) {
+            static_assert(NB1 <= 256, "first digits of 9 to 11 bits are not used");
+            find_digit_p<4>(s_h1, kr, lane, dg, kr, cnt);
+        }
+        if (wave == 0 && lane == 0) { s_res[0] = dg; s_res[1] = kr; s_res[2] = cnt; }
+        __syncthreads();
+        dg = s_res[0]; kr = s_res[1]; cnt = s_res[2];
+        prefix = dg << S1;
+        himask = (uint32_t)(NB1 - 1) << S1;
+        // Remaining digits are 8 bits wide, each level with its own 256-bin
+        // histogram s_hl[level], so no level clears a buffer.
+        if (S1 > 8 && cnt <= (uint32_t)kCap) {
+            // Several digits left over few keys: compact them (one LDS atomic
+            // per wavefront and entry slot) and let wavefront 0 finish alone.
 #pragma unroll
-            for (int w = 0; w < NW; ++w) { run += w < wave ? s_cw[w] : 0u; nc += s_cw[w]; }
-            const bool fits = nc <= (uint32_t)kCap;
-            if (fits) {
-#pragma unroll
-                for (int i = 0; i < EPT; ++i) {
-                    const bool m = (key[i] & himask) == prefix;
-                    const uint64_t bm = __ballot(m);
-                    if (m) s_cand[run + popc_below(bm)] = key[i];
-                    run += (uint32_t)__popcll(bm);
+            for (int i = 0; i < EPT; ++i) {
+                const bool m = key[i] != kInvalid && (key[i] & himask) == prefix;
+                const uint64_t bm = __ballot(m);
+                if (bm == 0) continue;   // uniform
+                uint32_t base = 0;
+                if (lane == 0) base = atomicAdd(&s_nc, (uint32_t)__popcll(bm));
+                base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+                if (m) s_cand[base + popc_below(bm)] = key[i];
+            }
+            __syncthreads();
+            if (wave == 0) {
+                const uint32_t ncand = cnt;
+                int shift = S1, l = 0;
+                while (shift > 0) {
+                    const int nshift = shift > 8 ? shift - 8 : 0;
+                    const uint32_t dmask = (1u << (shift - nshift)) - 1u;
+                    for (uint32_t c = (uint32_t)lane; c < ncand; c += kWave) {
+                        const uint32_t kc = s_cand[c];
+                        if ((kc & himask) == prefix) atomicAdd(&s_hl[l][(kc >> nshift) & dmask], 1u);
+                    }
+                    find_digit_p<4>(s_hl[l], kr, lane, dg, kr, cnt);
+                    prefix |= dg << nshift;
+                    himask |= dmask << nshift;
+                    shift = nshift;
+                    ++l;
                 }
-                __syncthreads();
+                if (lane == 0) { s_res[0] = prefix; s_res[1] = kr; s_res[2] = cnt; }
             }
-            // Each thread takes candidates tid, tid + NT, ... into registers once.
-            constexpr int CR = kCap / NT;                 // 16 (NT 256) or 4 (NT 1024)
-            uint32_t cand[CR];
-#pragma unroll
-            for (int i = 0; i < CR; ++i) {
-                const uint32_t c = (uint32_t)(tid + i * NT);
-                cand[i] = kInvalid;
-                if ((uint32_t)(i * NT) < nc && fits && c < nc) cand[i] = s_cand[c];
-            }
-            // remaining levels
+            __syncthreads();
+            prefix = s_res[0]; kr = s_res[1]; cnt = s_res[2];
+        } else {
+            // One digit left, or many keys (ties, zeros): all wavefronts count
+            // each digit and search its 256 bins.
+            int shift = S1, l = 0;
             while (shift > 0) {
                 const int nshift = shift > 8 ? shift - 8 : 0;
                 const uint32_t dmask = (1u << (shift - nshift)) - 1u;
-                uint32_t (*hb)[256] = s_hist[lvl % 3];
-                if (fits) {
-#pragma unroll
-                    for (int i = 0; i < CR; ++i) {
-                        if ((uint32_t)(i * NT) >= nc) break;     // uniform
-                        if ((cand[i] & himask) == prefix)
-                            atomicAdd(&hb[wave % NS][(cand[i] >> nshift) & dmask], 1u);
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < EPT; ++i)
-                        if ((key[i] & himask) == prefix)
-                            atomicAdd(&hb[wave % NS][(key[i] >> nshift) & dmask], 1u);
-                }
+                count_level(s_hl[l], prefix, himask, nshift, dmask);
                 __syncthreads();
-                find_digit<NS>(hb, kr, lane, dg, kr);
-                for (int i = tid; i < NS * 256; i += NT) (&s_hist[(lvl + 2) % 3][0][0])[i] = 0;
-                ++lvl;
+                find_digit_p<4>(s_hl[l], kr, lane, dg, kr, cnt);
                 prefix |= dg << nshift;
                 himask |= dmask << nshift;
                 shift = nshift;
+                ++l;
             }
         }
+        eqtot = cnt;   // the last bin holds exactly the keys equal to tau
     }
     const uint32_t tau = (k > 0) ? prefix : 0xFFFFFFFFu;
 
@@ -781,12 +859,25 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
             base += tot;
         }
     };
+    // The tie ranks are needed only when some keys equal to tau stay out (or
+    // the cutoff is asked for), the output slots only for the index list.
     uint32_t eqb[NQ], selc[NQ], selb[NQ];
-    block_scan(eqc, eqb, 0);
+    if (kr < eqtot || a.cutoff != nullptr) {
+        block_scan(eqc, eqb, 0);
+    } else {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
-        selc[q] = gtc[q] + (kr > eqb[q] ? min(eqc[q], kr - eqb[q]) : 0u);
-    block_scan(selc, selb, 1);
+        for (int q = 0; q < NQ; ++q) eqb[q] = 0;
+        kr = 0xFFFFFFFFu;   // every key equal to tau is selected
+    }
+    if (a.idx != nullptr) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            selc[q] = gtc[q] + (kr > eqb[q] ? min(eqc[q], kr - eqb[q]) : 0u);
+        block_scan(selc, selb, 1);
+    } else {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) selb[q] = 0;
+    }
 
     // Index list and cutoff (optional outputs): a separate pass behind one
     // uniform branch, so the common path carries no per-entry scatter.
@@ -878,22 +969,26 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
 // Vectorised kernel with block size B, runs per thread chosen from the row length.
 template <int B, int KK, int XK>
 hipError_t launch_vec(int64_t rows, const TopkArgs& a, hipStream_t stream) {
+    // At most 32 keys per thread (NQ * V <= 32): more would spill scalar
+    // registers in the unrolled per-entry loops.
     constexpr int V = VecOf<KK>::V, CS = V * B;
-    constexpr int kMaxVecD = 16384;
+    constexpr int kRowNQ = 16384 / CS > 0 ? 16384 / CS : 1;     // rows of at most 16384
+    constexpr int kMaxNQ = 32 / V < kRowNQ ? 32 / V : kRowNQ;
     const dim3 grid((unsigned)rows), block(B);
     const int64_t nq = (a.d + CS - 1) / CS;
     if (nq <= 1) topk_vec_kernel<B, 1, KK, XK><<<grid, block, 0, stream>>>(a);
     else if (nq <= 2) topk_vec_kernel<B, 2, KK, XK><<<grid, block, 0, stream>>>(a);
-    else if constexpr (kMaxVecD / CS >= 4) {
+    else if constexpr (kMaxNQ >= 4) {
         if (nq <= 3) topk_vec_kernel<B, 3, KK, XK><<<grid, block, 0, stream>>>(a);
         else if (nq <= 4) topk_vec_kernel<B, 4, KK, XK><<<grid, block, 0, stream>>>(a);
-        else if constexpr (kMaxVecD / CS >= 8) {
+        else if constexpr (kMaxNQ >= 8) {
             if (nq <= 8) topk_vec_kernel<B, 8, KK, XK><<<grid, block, 0, stream>>>(a);
-            else if constexpr (kMaxVecD / CS >= 16) {
-                if (nq <= 12) topk_vec_kernel<B, 12, KK, XK><<<grid, block, 0, stream>>>(a);
-                else topk_vec_kernel<B, 16, KK, XK><<<grid, block, 0, stream>>>(a);
-            }
+            else return hipErrorInvalidValue;
+        } else {
+            return hipErrorInvalidValue;
         }
+    } else {
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
@@ -905,10 +1000,12 @@ hipError_t launch_kkx(int64_t rows, const TopkArgs& a, hipStream_t stream) {
     constexpr int V = VecOf<KK>::V;
     if (a.d % V == 0 && a.d <= 16384) {
         // Few rows (decode): 16 waves per row hide each other's latencies;
-        // many rows: 4 waves per row and many rows per CU.
+        // many rows: 4 waves per row and many rows per CU, unless a row needs
+        // more than 32 keys per thread.
         if (rows <= 64 && a.d >= 1024 * V) return launch_vec<1024, KK, XK>(rows, a, stream);
         if (rows <= 64 && a.d >= 512 * V) return launch_vec<512, KK, XK>(rows, a, stream);
-        return launch_vec<256, KK, XK>(rows, a, stream);
+        if (a.d <= 256 * 32) return launch_vec<256, KK, XK>(rows, a, stream);
+        return launch_vec<512, KK, XK>(rows, a, stream);
     }
     if (a.d <= 4 * R) {
         topk_reg_kernel<R, 4, KK, XK><<<grid, dim3(R), 0, stream>>>(a);
