@@ -32,11 +32,16 @@ namespace qs {
 namespace {
 
 constexpr int kNT = 256;     // threads per workgroup
-constexpr int kLPR = 32;     // lanes per weight-row segment
+constexpr int kLPR = 32;     // lanes per weight-row segment (ternary kernel)
 constexpr int kRPI = 64 / kLPR;
 constexpr int kNSlot = 4 * kRPI;
 constexpr int kUnroll = 4;       // rows per pipeline stage per lane (ternary kernel)
 constexpr int kMaxUnroll = 8;    // the fp kernel uses 8 for small token tiles
+// The fp gather kernel reads 128-byte row segments: 8 lanes of 16 bytes per
+// row, 8 rows per wavefront load, 32 row slots per workgroup.
+constexpr int kFLPR = 8;
+constexpr int kFNSlot = 4 * (64 / kFLPR);
+constexpr int kFMaxCand = 2048;  // candidate rows per split (coefficients staged in LDS)
 
 // Workgroups the split-K plan aims for.  QS_GEMV_TARGET_WG overrides it (read
 // once per process; a tuning knob for measurements).
@@ -44,7 +49,7 @@ int target_wg() {
     static const int v = [] {
         const char* e = getenv("QS_GEMV_TARGET_WG");
         int t = e ? atoi(e) : 0;
-        return t > 0 ? t : 384;
+        return t > 0 ? t : 768;
     }();
     return v;
 }
@@ -133,13 +138,26 @@ __device__ __forceinline__ void store_final(const GemvArgs& a, int64_t i, float 
     }
 }
 
+// Inclusive prefix sum over a wavefront (DPP row shifts and broadcasts).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
 template <int WBF16, int BT>
 __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, int nsplit) {
     constexpr int EPT = WBF16 ? 8 : 4;
-    constexpr int CT = kLPR * EPT;
+    constexpr int CT = kFLPR * EPT;                      // 128-byte row segments
     constexpr int TG = BT < 2 ? BT : 2;
     constexpr int U = BT <= 4 ? kMaxUnroll : kUnroll;   // rows per stage per lane
-    constexpr int BATCH = kNSlot * U;                    // rows per pipeline stage
+    constexpr int BATCH = kFNSlot * U;                   // rows per pipeline stage
+    constexpr int MAXC = 8192 / BT < kFMaxCand ? 8192 / BT : kFMaxCand;   // as in the plan
+    constexpr int NCH = MAXC / kNT;                                      // candidate chunks
     extern __shared__ float smem[];
     float* s_coef = smem;                                  // [cand + 3 BATCH][BT]
     uint32_t* s_off = reinterpret_cast<uint32_t*>(smem + (size_t)(cand + 3 * BATCH) * BT);
@@ -156,42 +174,52 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
     const int64_t esize = WBF16 ? 2 : 4;
     const uint32_t rowbytes = (uint32_t)(n_out * esize);
 
-    // Phase A: selected candidate rows (union over the token tile), ascending;
-    // s_off holds their byte offsets in W^T and s_coef their coefficients.
-    // Coefficients come through a buffer view of this token tile's rows of xs,
-    // so the BT loads are issued together (rows past the batch read 0).
+    // Phase A: rows of [j0, j1) selected by any token of the tile.  All the
+    // coefficient loads are issued at once (candidate j0 + ch * 256 + tid is
+    // chunk ch of thread tid; rows past the range or the batch read 0), one
+    // block scan of the per-thread counts places them, in (thread, chunk)
+    // order: s_off holds their byte offsets in W^T, s_coef their coefficients.
     const int64_t ntok = min((int64_t)BT, rows - tok0);
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.xs + tok0 * d_in), (short)0, (int)(ntok * d_in * 4), 0x00020000);
-    int nact = 0;
-    for (int64_t c0 = j0; c0 < j1; c0 += kNT) {
-        const int64_t j = c0 + tid;
+    float c[NCH][BT];
+    uint32_t selbits = 0;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int64_t j = j0 + ch * kNT + tid;
         const bool jin = j < j1;
-        float c[BT];
 #pragma unroll
         for (int t = 0; t < BT; ++t)
-            c[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            c[ch][t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
                 xr, jin ? (uint32_t)((t * d_in + j) * 4) : kOOB, 0, 0));
+    }
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
         bool any = false;
 #pragma unroll
-        for (int t = 0; t < BT; ++t) any = any || (c[t] != 0.0f);
-        const uint64_t b = __ballot(any);
-        if (lane == 0) s_wcnt[wave] = (int)__popcll(b);
-        __syncthreads();
-        int before = nact, total = nact;
+        for (int t = 0; t < BT; ++t) any = any || (c[ch][t] != 0.0f);
+        selbits |= (any ? 1u : 0u) << ch;
+    }
+    const uint32_t mycnt = (uint32_t)__popc(selbits);
+    const uint32_t incl = wave_incl_scan_u32(mycnt);
+    if (lane == 63) s_wcnt[wave] = (int)incl;
+    __syncthreads();
+    int before = 0, nact = 0;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            if (w < wave) before += s_wcnt[w];
-            total += s_wcnt[w];
-        }
-        if (any) {
-            const int pos = before + (int)popc_below(b);
-            s_off[pos] = (uint32_t)j * rowbytes;
+    for (int w = 0; w < 4; ++w) {
+        const int cw = s_wcnt[w];
+        if (w < wave) before += cw;
+        nact += cw;
+    }
+    int pos = before + (int)(incl - mycnt);
 #pragma unroll
-            for (int t = 0; t < BT; ++t) s_coef[pos * BT + t] = c[t];
+    for (int ch = 0; ch < NCH; ++ch) {
+        if (selbits & (1u << ch)) {
+            s_off[pos] = (uint32_t)(j0 + ch * kNT + tid) * rowbytes;
+#pragma unroll
+            for (int t = 0; t < BT; ++t) s_coef[pos * BT + t] = c[ch][t];
+            ++pos;
         }
-        nact = total;
-        __syncthreads();
     }
     // Pad the list with rows that read as zero up to an even number of
     // pipeline stages plus the one stage that the last iteration prefetches.
@@ -205,8 +233,8 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
     __syncthreads();
 
     // Phase B: stream the selected W^T row segments, one stage ahead.
-    const int slot = wave * kRPI + lane / kLPR;
-    const int64_t col = (int64_t)tile * CT + (lane % kLPR) * EPT;
+    const int slot = wave * (64 / kFLPR) + lane / kFLPR;
+    const int64_t col = (int64_t)tile * CT + (lane % kFLPR) * EPT;
     const uint32_t colb = col < n_out ? (uint32_t)(col * esize) : kOOB;
     const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, a.d_in * (int64_t)rowbytes);
 
@@ -223,14 +251,14 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
 #pragma unroll
         for (int u = 0; u < U; ++u)
             dst[u] = __builtin_amdgcn_raw_buffer_load_b128(
-                rs, s_off[bi * BATCH + slot + u * kNSlot] + colb, 0, 0);
+                rs, s_off[bi * BATCH + slot + u * kFNSlot] + colb, 0, 0);
     };
     auto fma_stage = [&](const u32x4* src, int bi) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float w[EPT];
             unpack<WBF16>(src[u], w);
-            const int ai = bi * BATCH + slot + u * kNSlot;
+            const int ai = bi * BATCH + slot + u * kFNSlot;
 #pragma unroll
             for (int t = 0; t < BT; ++t) {
                 const float c = s_coef[ai * BT + t];
@@ -257,8 +285,8 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
     __syncthreads();   // s_coef / s_off are dead from here: reuse as the reduction buffer
 
     // Phase C: sum the row slots in slot order, token group by token group.
-    float* s_red = smem;   // [kNSlot][TG][CT]
-    const int cl = (lane % kLPR) * EPT;
+    float* s_red = smem;   // [kFNSlot][TG][CT]
+    const int cl = (lane % kFLPR) * EPT;
 #pragma unroll
     for (int t0 = 0; t0 < BT; t0 += TG) {
 #pragma unroll
@@ -269,7 +297,7 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
         for (int o = tid; o < TG * CT; o += kNT) {
             float s = 0.0f;
 #pragma unroll
-            for (int sl = 0; sl < kNSlot; ++sl) s += s_red[sl * TG * CT + o];
+            for (int sl = 0; sl < kFNSlot; ++sl) s += s_red[sl * TG * CT + o];
             const int64_t row = tok0 + t0 + o / CT;
             const int64_t cg = (int64_t)tile * CT + (o % CT);
             if (row < rows && cg < n_out) {
@@ -961,8 +989,11 @@ GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16) {
     p.bt = pow2_tile(rows, 16);
     // 16-token tiles run an MFMA kernel: bf16 weights in 64-column tiles on the
     // bf16 matrix cores, fp32 weights in 16 * EPT-column tiles on the fp32 ones.
+    // With bf16 weights, 8 tokens also take the bf16 MFMA kernel (as a half-empty
+    // 16-token tile): it beats eight fp32 FMAs per weight.
+    if (w_is_bf16 && p.bt == 8) p.bt = 16;
     const bool bmfma = p.bt == 16 && w_is_bf16;
-    p.ct = bmfma ? kBCols : p.bt == 16 ? 16 * p.ept : p.lpr * p.ept;
+    p.ct = bmfma ? kBCols : p.bt == 16 ? 16 * p.ept : kFLPR * p.ept;
     p.n_tiles = (int)ceil_div(n_out, p.ct);
     p.n_tok_tiles = (int)ceil_div(rows, p.bt);
     const int64_t base = (int64_t)p.n_tiles * p.n_tok_tiles;
@@ -976,7 +1007,7 @@ GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16) {
         cand = ceil_div(ceil_div(d_in, ns), 4 * kBGroup) * 4 * kBGroup;
     } else {
         // The FMA kernels stage <= 32 KB of coefficients in LDS.
-        const int cand_max = 8192 / p.bt < 2048 ? 8192 / p.bt : 2048;
+        const int cand_max = 8192 / p.bt < kFMaxCand ? 8192 / p.bt : kFMaxCand;
         int64_t ns = ceil_div(target_wg(), base);
         if (ns < 1) ns = 1;
         cand = ceil_div(ceil_div(d_in, ns), 64) * 64;
@@ -996,7 +1027,7 @@ GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16) {
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     const int ept = w_is_bf16 ? 8 : 4;
-    const int ct = kLPR * ept;
+    const int ct = kFLPR * ept;
     const int tg = p.bt < 2 ? p.bt : 2;
     dim3 grid(p.n_tiles, p.nsplit, p.n_tok_tiles);
     if (p.bt == 16 && w_is_bf16) {
@@ -1017,9 +1048,9 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
         else gather_mfma_kernel<0><<<grid, dim3(kNT), lds, stream>>>(a, p.cand, p.nsplit);
         return hipGetLastError();
     }
-    const size_t padded = (size_t)p.cand + 3 * kNSlot * kMaxUnroll;
+    const size_t padded = (size_t)p.cand + 3 * kFNSlot * kMaxUnroll;
     size_t lds_a = padded * p.bt * 4 + padded * 4;
-    size_t lds_c = (size_t)kNSlot * tg * ct * 4;
+    size_t lds_c = (size_t)kFNSlot * tg * ct * 4;
     size_t lds = lds_a > lds_c ? lds_a : lds_c;
 #define QS_GEMV_CASE(WB, BTV)                                                              \
     if (w_is_bf16 == WB && p.bt == BTV) {                                                  \
