@@ -190,6 +190,21 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     log(f"gather GEMV: {us_launch:.2f} us per launch (avg of up and down), {achieved:.0f} GB/s")
     traffic = committed_traffic("qs_gemv.hip", "gather_gemv_llama7b_relu2_b1_traffic.md")
 
+    # ceiling reference: a plain streaming read of the same bytes per launch,
+    # rotating over chunks of the weight copies (> 256 MB, so not from the MALL)
+    flat = [t.view(-1).view(torch.uint8) for t in wups + wdns]
+    nb = min(int(gemv_bytes / (2 * L)), min(f.numel() for f in flat)) // 16 * 16
+    chunks = [f[o:o + nb] for f in flat for o in range(0, f.numel() - nb + 1, nb)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def probe(i):
+        qs.qs_stream_read(chunks[i % len(chunks)], nb, sink)
+
+    ms_probe = time_graph(torch, stream, probe, L, 4)
+    probe_gbps = nb * L / (ms_probe * 1e-3) / 1e9
+    log(f"stream-read probe, {nb / 1e6:.1f} MB per launch over {len(chunks)} chunks: "
+        f"{probe_gbps:.0f} GB/s; gather GEMV at {achieved / probe_gbps:.1%} of it")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_c2(c, args.cpu_seconds)
@@ -205,7 +220,9 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "gather_gemv_kernel",
                      "algorithmic_bytes_per_launch": round(gemv_bytes / (2 * L)),
-                     "us_per_launch": round(us_launch, 3)},
+                     "us_per_launch": round(us_launch, 3),
+                     "stream_read_probe_gbps": round(probe_gbps, 1),
+                     "frac_of_stream_read_probe": round(achieved / probe_gbps, 4)},
         "cpu_baseline": cpu,
     }
 

@@ -247,6 +247,18 @@ qs_status qs_ternarize(const float* w_host, int64_t n_out, int64_t d_in, int8_t*
  */
 qs_status qs_pack_ternary(const int8_t* t_host, int64_t n_out, int64_t d_in, uint8_t* packed_host);
 
+/*
+ * qs_stream_read -- measurement reference, not part of the method: a plain
+ * streaming read of `bytes` bytes at `src` (device), with every byte loaded
+ * once and nothing written except, never in practice, *sink.  Its throughput
+ * on a buffer of the gather kernels' size is the practical HBM ceiling their
+ * roofline fraction is also quoted against.
+ *   src    device, 16-byte aligned; bytes % 16 == 0 (else QS_ERR_UNSUPPORTED).
+ *   sink   device u32, written only if the checksum of the data equals a
+ *          fixed constant.  Enqueued on `stream`, asynchronous.
+ */
+qs_status qs_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Text of the last error on the calling thread ("" if none); valid until the
  * next qs_* call on this thread. */
 const char* qs_last_error(void);

@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "load", "lib_path", "QS_OK", "QSError",
-    "qs_topk_mask", "qs_gather_linear", "gather_workspace", "qs_sparse_linear", "qs_sparse_linear_i8t", "qs_sparse_ffn",
+    "qs_topk_mask", "qs_gather_linear", "gather_workspace", "qs_stream_read", "qs_sparse_linear", "qs_sparse_linear_i8t", "qs_sparse_ffn",
     "qs_workspace_bytes", "qs_ternarize", "qs_pack_ternary", "qs_last_error", "qs_version",
     "F32", "BF16", "I8", "LAYOUT_WT", "LAYOUT_W", "ACT_RELU2", "ACT_DRELU",
     "OP_TOPK_MASK", "OP_SPARSE_LINEAR", "OP_SPARSE_LINEAR_I8T", "OP_SPARSE_FFN_RELU2",
@@ -46,6 +46,7 @@ _SIGS = {
     "qs_workspace_bytes": [_INT, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "qs_ternarize": [_P, _I64, _I64, _P, ctypes.POINTER(ctypes.c_float)],
     "qs_pack_ternary": [_P, _I64, _I64, _P],
+    "qs_stream_read": [_P, ctypes.c_size_t, _P, _P],
     "qs_last_error": [],
     "qs_version": [],
 }
@@ -186,6 +187,16 @@ def gather_workspace(rows: int, d_in: int, n_out: int, device=None):
     torch = _torch()
     need = qs_workspace_bytes(OP_GATHER_LINEAR, rows, d_in, n_out)
     return torch.zeros(max(need, 1), dtype=torch.uint8, device=device or "cuda")
+
+
+def qs_stream_read(buf, nbytes=None, sink=None):
+    """Streaming read of the first nbytes of a device tensor (bandwidth reference)."""
+    torch = _torch()
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check(load().qs_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf.device)))
+    return sink
 
 
 def qs_gather_linear(xs, wt, y=None, y_dtype=None, ws=None):

@@ -165,6 +165,188 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The same product for K % 128 == 0, pipelined.  Tile 256 x BN x 64 per
+// workgroup of NW wavefronts (NW / 2 x 2, each 256 / (NW / 2) x BN / 2).
+// Slices of 64 along k go global -> registers two slices ahead of the MFMAs
+// and registers -> LDS (one of two buffers) one slice ahead, one barrier per
+// slice.  The per-CU vector-memory path (64 bytes per clock) and the LDS
+// stores would stall a wavefront for most of a slice if issued as a block, so
+// each chunk's LDS store and the reload of its register are interleaved with
+// the MFMAs (three MFMAs, one store, one load).  A row of a slice is 8 chunks
+// of 16 bytes stored at chunk position c ^ ((row >> 1) & 7): with 64 four-byte
+// banks and 16 lanes served per pass, the 16 rows of a fragment read's pass
+// hit 16 distinct 16-byte bank groups.  (Direct global -> LDS loads would save
+// the register staging, but the compiler then waits for every load in flight
+// before each LDS read.)
+// ---------------------------------------------------------------------------
+template <int BN, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_nt_bf16_deep_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C,
+    int M, int N, int K, int c_bf16, int tiles_m, int tiles_n) {
+    constexpr int NTH = 64 * NW, WM = NW / 2;              // wavefronts: WM x 2
+    constexpr int BM = 256, TM = BM / WM / 32, TN = BN / 64;
+    constexpr int QA = BM * 8 / NTH, QB = BN * 8 / NTH;    // 16-byte chunks per thread per slice
+    static_assert(BN % 64 == 0, "tile shape");
+    __shared__ u32x4 sA0[BM * 8], sA1[BM * 8];
+    __shared__ u32x4 sB0[BN * 8], sB1[BN * 8];
+
+    const int ntiles = tiles_m * tiles_n;
+    int tile = blockIdx.x;
+    if (ntiles % 8 == 0) tile = (blockIdx.x % 8) * (ntiles / 8) + blockIdx.x / 8;
+    constexpr int GM = 8;
+    const int group = tile / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = min(GM, tiles_m - first_m);
+    const int tm = first_m + (tile % (GM * tiles_n)) % gm;
+    const int tn = (tile % (GM * tiles_n)) / gm;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // Chunk q of this thread: LDS slot q * NTH + tid (row = slot / 8), holding
+    // global chunk (slot % 8) ^ (row & 7) of that row.  Rows past M or N
+    // repeat the last row; their results are never stored.
+    int offa[QA], offb[QB];
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+        const int sl = q * NTH + tid, row = sl >> 3, c = (sl & 7) ^ ((row >> 1) & 7);
+        offa[q] = min(m0 + row, M - 1) * K + 8 * c;
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+        const int sl = q * NTH + tid, row = sl >> 3, c = (sl & 7) ^ ((row >> 1) & 7);
+        offb[q] = min(n0 + row, N - 1) * K + 8 * c;
+    }
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(A), (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(B), (short)0, 0x7FFFFFFF, 0x00020000);
+    const int nk = K / 64;   // even
+    // Slices past the end load at an out-of-range offset (zeros, no memory
+    // traffic): every load and store of the loop is unconditional, so the
+    // compiler's wait counts stay exact across iterations.
+    auto gload = [&](u32x4* ra, u32x4* rb, int kt) {
+        const int k0 = kt * 64;
+        const bool in = kt < nk;
+#pragma unroll
+        for (int q = 0; q < QA; ++q)
+            ra[q] = __builtin_amdgcn_raw_buffer_load_b128(ar, in ? (uint32_t)(offa[q] + k0) * 2u : 0x80000000u, 0, 0);
+#pragma unroll
+        for (int q = 0; q < QB; ++q)
+            rb[q] = __builtin_amdgcn_raw_buffer_load_b128(br, in ? (uint32_t)(offb[q] + k0) * 2u : 0x80000000u, 0, 0);
+    };
+    auto lstore = [&](u32x4* sa, u32x4* sb, const u32x4* ra, const u32x4* rb) {
+#pragma unroll
+        for (int q = 0; q < QA; ++q) sa[q * NTH + tid] = ra[q];
+#pragma unroll
+        for (int q = 0; q < QB; ++q) sb[q * NTH + tid] = rb[q];
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const int r32 = lane & 31, kg = lane >> 5;
+    auto frag = [&](const u32x4* sa, const u32x4* sb, int ks, bf16x8* af, bf16x8* bfr) {
+        const int c = 2 * ks + kg;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * (BM / WM) + i * 32 + r32;
+            af[i] = as_bf16x8(sa[row * 8 + (c ^ ((row >> 1) & 7))]);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int row = wn * (BN / 2) + j * 32 + r32;
+            bfr[j] = as_bf16x8(sb[row * 8 + (c ^ ((row >> 1) & 7))]);
+        }
+    };
+    // One slice: the MFMAs of slice kt (LDS buffer sa/sb), with the staging
+    // work spread between them: item q stores chunk q of slice kt + 1 (held in
+    // ra/rb) into the other buffer and reloads the register with chunk q of
+    // slice kt + 3.  sched_group_barrier lays the k-step out as: its fragment
+    // reads for the next k-step, then (3 MFMAs, 1 LDS store, 1 global load)
+    // groups, so the per-CU load and store traffic runs under the MFMAs
+    // instead of stalling the wavefront in a block of its own.
+    constexpr int NI = QA + QB;            // staging items per slice (14 for BN = 192)
+    constexpr int IPK = (NI + 3) / 4;      // items per k-step
+    auto item = [&](u32x4* wa, u32x4* wb, u32x4* ra, u32x4* rb, int q, int kt3) {
+        const int k0 = kt3 * 64;
+        const bool in = kt3 < nk;
+        if (q < QA) {
+            wa[q * NTH + tid] = ra[q];
+            ra[q] = __builtin_amdgcn_raw_buffer_load_b128(ar, in ? (uint32_t)(offa[q] + k0) * 2u : 0x80000000u, 0, 0);
+        } else {
+            const int qb = q - QA;
+            wb[qb * NTH + tid] = rb[qb];
+            rb[qb] = __builtin_amdgcn_raw_buffer_load_b128(br, in ? (uint32_t)(offb[qb] + k0) * 2u : 0x80000000u, 0, 0);
+        }
+    };
+    auto slice = [&](const u32x4* sa, const u32x4* sb, u32x4* wa, u32x4* wb, u32x4* ra, u32x4* rb, int kt3) {
+        bf16x8 af[2][TM], bfr[2][TN];
+        frag(sa, sb, 0, af[0], bfr[0]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks < 3) frag(sa, sb, ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+#pragma unroll
+            for (int m = 0; m < TM * TN; ++m) {
+                const int i = m / TN, j = m % TN;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
+                const int q = ks * IPK + m / 3;
+                if (m % 3 == 2 && m / 3 < IPK && q < NI) item(wa, wb, ra, rb, q, kt3);
+            }
+            if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);   // next fragments
+#pragma unroll
+            for (int g = 0; g < (TM * TN) / 3; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                  // 3 MFMAs
+                if (g < IPK && ks * IPK + g < NI) {
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);              // 1 LDS store
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);              // 1 global load
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    u32x4 ra0[QA], rb0[QB], ra1[QA], rb1[QB];
+    gload(ra0, rb0, 0);
+    gload(ra1, rb1, 1);
+    lstore(sA0, sB0, ra0, rb0);
+    gload(ra0, rb0, 2);
+    __syncthreads();
+    // Slice kt reads buffer kt % 2 and stages slice kt + 1 into the other one,
+    // whose last reader (slice kt - 1) finished before the previous barrier.
+    // The last pair stages a past-the-end slice into a buffer nobody reads.
+    for (int kt = 0; kt < nk; kt += 2) {
+        slice(sA0, sB0, sA1, sB1, ra1, rb1, kt + 3);
+        __syncthreads();
+        slice(sA1, sB1, sA0, sB0, ra0, rb0, kt + 4);
+        __syncthreads();
+    }
+
+    // acc[i][j][v]: row 8 (v / 4) + 4 (lane / 32) + v % 4, column lane % 32 of its 32x32 tile
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = n0 + wn * (BN / 2) + j * 32 + r32;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = m0 + wm * (BM / WM) + i * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
+                if (row < M && col < N) {
+                    const int64_t o = (int64_t)row * N + col;
+                    if (c_bf16) reinterpret_cast<uint16_t*>(C)[o] = f32_to_bf16_rne(acc[i][j][v]);
+                    else reinterpret_cast<float*>(C)[o] = acc[i][j][v];
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dReLU gate/up (Turbo Sparse summary, Eq. 2: ReLU after both the gate and the
 // up projection, so h = relu(g) * relu(u) is zero wherever g <= 0).
 //
@@ -313,6 +495,14 @@ hipError_t launch_gemm_cfg(const MfmaArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int BN, int NW>
+hipError_t launch_gemm_deep(const MfmaArgs& a, hipStream_t stream) {
+    const int tiles_m = (int)((a.m + 255) / 256), tiles_n = (int)((a.n + BN - 1) / BN);
+    gemm_nt_bf16_deep_kernel<BN, NW><<<dim3(tiles_m * tiles_n), dim3(64 * NW), 0, stream>>>(
+        a.x, a.w, a.y, (int)a.m, (int)a.n, (int)a.k, a.y_bf16, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_masked_gemm(const MfmaArgs& a, hipStream_t stream) {
@@ -321,7 +511,10 @@ hipError_t launch_masked_gemm(const MfmaArgs& a, hipStream_t stream) {
     const int64_t tm = (a.m + 255) / 256;
     const int64_t t256 = tm * ((a.n + 255) / 256), t192 = tm * ((a.n + 191) / 192);
     auto waste = [](int64_t t) { int64_t r = (t + 255) / 256 * 256; return (double)(r - t) / r; };
-    if (waste(t192) + 1e-9 < waste(t256)) return launch_gemm_cfg<256, 192, 2, 3>(a, stream);
+    const bool w192 = waste(t192) + 1e-9 < waste(t256);
+    if (a.k % 128 == 0 && (int64_t)a.m * a.k < (int64_t(1) << 30) && (int64_t)a.n * a.k < (int64_t(1) << 30))
+        return launch_gemm_deep<192, 8>(a, stream);
+    if (w192) return launch_gemm_cfg<256, 192, 2, 3>(a, stream);
     return launch_gemm_cfg<256, 256, 2, 4>(a, stream);
 }
 

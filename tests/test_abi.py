@@ -87,6 +87,15 @@ def test_gather_linear_validation():
                                 None) == 1
 
 
+def test_stream_read_validation():
+    lib = qs.load()
+    assert lib.qs_stream_read(None, 1024, FAKE, None) == 1
+    assert lib.qs_stream_read(FAKE, 1024, None, None) == 1
+    assert lib.qs_stream_read(FAKE, 1000, FAKE, None) == 2        # bytes % 16 != 0
+    assert lib.qs_stream_read(ctypes.c_void_p(0x1008), 1024, FAKE, None) == 2   # misaligned
+    assert lib.qs_stream_read(FAKE, 0, FAKE, None) == 0           # nothing to read
+
+
 def test_i8t_and_ffn_validation():
     lib = qs.load()
     need = qs.qs_workspace_bytes(qs.OP_SPARSE_LINEAR_I8T, 2, 256, 64)
