@@ -218,7 +218,8 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
         "union_rows_up": un1, "union_rows_down": un2,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "gather_gemv_kernel",
+                     "traffic": traffic if B == 1 else None,
+                     "kernel": "gather_gemv_kernel" if B < 8 else "bfrag_kernel + gather_bmfma_kernel",
                      "algorithmic_bytes_per_launch": round(gemv_bytes / (2 * L)),
                      "us_per_launch": round(us_launch, 3),
                      "stream_read_probe_gbps": round(probe_gbps, 1),
@@ -338,7 +339,7 @@ def run_c4(args, torch, np, qs, datagen, dev, stream):
                    "k": c["K"]},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "whole call (top-K + gemm_nt_bf16_kernel)"},
+                     "traffic": None, "kernel": "whole call (top-K + gemm_nt_bf16_deep_kernel)"},
         "cpu_baseline": None,
     }
 
