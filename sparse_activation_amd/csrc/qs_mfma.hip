@@ -458,6 +458,92 @@ __global__ __launch_bounds__(256) void drelu_gate_up_kernel(DreluArgs a) {
     }
 }
 
+// Single-token dReLU gate/up.  With one token the projections are plain
+// GEMVs, so a wavefront owns NPW neurons and reads each row as whole 1 KB
+// pieces (64 lanes x 16 bytes, 8 pieces for d = 4096): lane l holds x[512 i +
+// 8 l .. + 7] and the weights at the same k, all of a wavefront's gate rows are
+// in flight at once, and each dot product is reduced across the wavefront
+// with DPP in a fixed order.  The up rows are then loaded only for neurons
+// whose gate is positive (a wavefront-uniform decision).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float dot8(const u32x4& w, const u32x4& x, float acc) {
+    const uint32_t wu[4] = {w.x, w.y, w.z, w.w}, xu[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc = fmaf(__uint_as_float(wu[i] << 16), __uint_as_float(xu[i] << 16), acc);
+        acc = fmaf(__uint_as_float(wu[i] & 0xFFFF0000u), __uint_as_float(xu[i] & 0xFFFF0000u), acc);
+    }
+    return acc;
+}
+
+template <int NCH, int NPW>
+__global__ __launch_bounds__(256) void drelu_gate_up_b1_kernel(DreluArgs a) {
+    // NPW neurons per wavefront
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t d = a.d, ffn = a.ffn;
+    const int64_t nb = ((int64_t)blockIdx.x * 4 + wave) * NPW;
+    if (blockIdx.x == 0 && a.zero_ptr != nullptr)
+        for (int i = tid; i < a.n_zero; i += 256) a.zero_ptr[i] = 0;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.x), (short)0, (int)(d * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.wg), (short)0, (int)(ffn * d * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.wu), (short)0, (int)(ffn * d * 2), 0x00020000);
+    constexpr uint32_t kOff = 0x80000000u;
+    u32x4 xv[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int64_t k = (int64_t)i * 512 + 8 * lane;
+        xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, k < d ? (uint32_t)(k * 2) : kOff, 0, 0);
+    }
+    auto row_off = [&](int64_t n, int i) -> uint32_t {
+        const int64_t k = (int64_t)i * 512 + 8 * lane;
+        return (n < ffn && k < d) ? (uint32_t)((n * d + k) * 2) : kOff;
+    };
+    u32x4 wv[NPW][NCH];
+#pragma unroll
+    for (int j = 0; j < NPW; ++j)
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) wv[j][i] = __builtin_amdgcn_raw_buffer_load_b128(gr, row_off(nb + j, i), 0, 0);
+    float g[NPW];
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) s = dot8(wv[j][i], xv[i], s);
+        g[j] = wave_sum(s) + ((a.bg != nullptr && nb + j < ffn) ? a.bg[nb + j] : 0.0f);
+    }
+    // Up rows only where the gate is positive (g is wavefront-uniform).
+#pragma unroll
+    for (int j = 0; j < NPW; ++j)
+        if (g[j] > 0.0f)
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) wv[j][i] = __builtin_amdgcn_raw_buffer_load_b128(ur, row_off(nb + j, i), 0, 0);
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+        float hv = 0.0f;
+        if (g[j] > 0.0f) {
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) s = dot8(wv[j][i], xv[i], s);
+            const float uv = wave_sum(s) + ((a.bu != nullptr && nb + j < ffn) ? a.bu[nb + j] : 0.0f);
+            hv = uv > 0.0f ? __fmul_rn(g[j], uv) : 0.0f;
+        }
+        if (lane == 0 && nb + j < ffn) a.h[nb + j] = hv;
+    }
+}
+
 // Nonzero entries of each row of h, ascending (Turbo Sparse summary, per-layer
 // zero-activation figure: only the active neurons enter W_down).
 __global__ __launch_bounds__(256) void nonzero_lists_kernel(const float* __restrict__ h, int64_t n,
@@ -521,6 +607,14 @@ hipError_t launch_masked_gemm(const MfmaArgs& a, hipStream_t stream) {
 hipError_t launch_drelu_gate_up(const DreluArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     const unsigned blocks = (unsigned)((a.ffn + 15) / 16);
+    if (a.rows == 1 && a.d <= 8192) {   // two neurons per wavefront, eight per workgroup
+        const int nch = (int)((a.d + 511) / 512);
+        const unsigned b2 = (unsigned)((a.ffn + 7) / 8);
+        if (nch <= 4) drelu_gate_up_b1_kernel<4, 2><<<dim3(b2), dim3(256), 0, stream>>>(a);
+        else if (nch <= 8) drelu_gate_up_b1_kernel<8, 2><<<dim3(b2), dim3(256), 0, stream>>>(a);
+        else drelu_gate_up_b1_kernel<16, 2><<<dim3(b2), dim3(256), 0, stream>>>(a);
+        return hipGetLastError();
+    }
     drelu_gate_up_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
