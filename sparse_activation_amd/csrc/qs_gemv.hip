@@ -806,12 +806,18 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---------------------------------------------------------------- ternary x int8
 
 constexpr int kI8EPT = 32;                 // columns per lane (8 bytes of packed weights)
-constexpr int kI8CT = kLPR * kI8EPT;       // 1024 columns per tile
-constexpr int kI8TargetWG = 512;
+constexpr int kI8LPR = 8;                  // lanes per row segment (64 bytes = 256 columns)
+constexpr int kI8CT = kI8LPR * kI8EPT;     // 256 columns per tile
+constexpr int kI8NSlot = 4 * (64 / kI8LPR);   // 32 row slots per workgroup
+constexpr int kI8MaxCand = 4096;           // candidate rows per split (LDS staging)
+constexpr int kI8TargetWG = 128;           // the whole matrix is a few MB: few, fuller workgroups
+static_assert(kI8CT == kNT, "the slot reduction gives each thread one column");
 
 template <int BT>
 __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int nsplit) {
-    constexpr int BATCH = kNSlot * kUnroll;
+    constexpr int BATCH = kI8NSlot * kUnroll;
+    constexpr int NCH = kI8MaxCand / kNT;   // candidate chunks per thread
+    constexpr int OPT = BT * kI8CT / kNT;   // outputs per thread in the split sum
     extern __shared__ int ismem[];
     int* s_coef = ismem;                                                   // [cand+3 BATCH][BT]
     uint32_t* s_off = reinterpret_cast<uint32_t*>(ismem + (size_t)(cand + 3 * BATCH) * BT);
@@ -825,39 +831,50 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
     const int64_t j1 = min(d_in, j0 + (int64_t)cand);
     const int64_t tok0 = (int64_t)tt * BT;
 
+    // Rows of [j0, j1) with a nonzero q for some token of the tile: all loads
+    // issued at once, placed by one block scan in (thread, chunk) order.
     const uint32_t rowbytes = (uint32_t)(n_out / 4);
     const int64_t ntok = min((int64_t)BT, rows - tok0);
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t*>(a.qs + tok0 * d_in), (short)0, (int)(ntok * d_in), 0x00020000);
-    int nact = 0;
-    for (int64_t c0 = j0; c0 < j1; c0 += kNT) {
-        const int64_t j = c0 + tid;
+    int c[NCH][BT];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int64_t j = j0 + ch * kNT + tid;
         const bool jin = j < j1;
-        int c[BT];
 #pragma unroll
         for (int t = 0; t < BT; ++t)
-            c[t] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(
+            c[ch][t] = (int)(int8_t)__builtin_amdgcn_raw_buffer_load_b8(
                 qr, jin ? (uint32_t)(t * d_in + j) : kOOB, 0, 0);
+    }
+    uint32_t selbits = 0;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
         bool any = false;
 #pragma unroll
-        for (int t = 0; t < BT; ++t) any = any || (c[t] != 0);
-        const uint64_t b = __ballot(any);
-        if (lane == 0) s_wcnt[wave] = (int)__popcll(b);
-        __syncthreads();
-        int before = nact, total = nact;
+        for (int t = 0; t < BT; ++t) any = any || (c[ch][t] != 0);
+        selbits |= (any ? 1u : 0u) << ch;
+    }
+    const uint32_t mycnt = (uint32_t)__popc(selbits);
+    const uint32_t incl = wave_incl_scan_u32(mycnt);
+    if (lane == 63) s_wcnt[wave] = (int)incl;
+    __syncthreads();
+    int before = 0, nact = 0;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            if (w < wave) before += s_wcnt[w];
-            total += s_wcnt[w];
-        }
-        if (any) {
-            const int pos = before + (int)popc_below(b);
-            s_off[pos] = (uint32_t)j * rowbytes;
+    for (int w = 0; w < 4; ++w) {
+        const int cw = s_wcnt[w];
+        if (w < wave) before += cw;
+        nact += cw;
+    }
+    int pos = before + (int)(incl - mycnt);
 #pragma unroll
-            for (int t = 0; t < BT; ++t) s_coef[pos * BT + t] = c[t];
+    for (int ch = 0; ch < NCH; ++ch) {
+        if (selbits & (1u << ch)) {
+            s_off[pos] = (uint32_t)(j0 + ch * kNT + tid) * rowbytes;
+#pragma unroll
+            for (int t = 0; t < BT; ++t) s_coef[pos * BT + t] = c[ch][t];
+            ++pos;
         }
-        nact = total;
-        __syncthreads();
     }
     const int nbatch = (nact + BATCH - 1) / BATCH;
     const int npad = ((nbatch + 1) / 2 * 2 + 1) * BATCH;
@@ -868,8 +885,8 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
     }
     __syncthreads();
 
-    const int slot = wave * kRPI + lane / kLPR;
-    const int64_t col = (int64_t)tile * kI8CT + (lane % kLPR) * kI8EPT;
+    const int slot = wave * (64 / kI8LPR) + lane / kI8LPR;
+    const int64_t col = (int64_t)tile * kI8CT + (lane % kI8LPR) * kI8EPT;
     // Rows are only 4-byte aligned when n_out % 32 != 0: two dword loads; the
     // second is out of range (zero) for the last 16 columns of such a row.
     const uint32_t colb = col < n_out ? (uint32_t)(col / 4) : kOOB;
@@ -886,7 +903,7 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
     auto load_stage = [&](u32x2* dst, int bi) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t ro = s_off[bi * BATCH + slot + u * kNSlot];
+            const uint32_t ro = s_off[bi * BATCH + slot + u * kI8NSlot];
             dst[u].x = __builtin_amdgcn_raw_buffer_load_b32(rs, ro + colb, 0, 0);
             dst[u].y = __builtin_amdgcn_raw_buffer_load_b32(rs, ro + colb2, 0, 0);
         }
@@ -894,17 +911,17 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
     auto mac_stage = [&](const u32x2* src, int bi) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int ai = bi * BATCH + slot + u * kNSlot;
-            int c[BT];
+            const int ai = bi * BATCH + slot + u * kI8NSlot;
+            int cf[BT];
 #pragma unroll
-            for (int t = 0; t < BT; ++t) c[t] = s_coef[ai * BT + t];
+            for (int t = 0; t < BT; ++t) cf[t] = s_coef[ai * BT + t];
 #pragma unroll
             for (int e = 0; e < kI8EPT; ++e) {
                 const uint32_t word = e < 16 ? src[u].x : src[u].y;
                 // 2-bit two's complement field: 00 -> 0, 01 -> +1, 11 -> -1
                 const int tv = __builtin_amdgcn_sbfe((int)word, (2 * e) & 31, 2);
 #pragma unroll
-                for (int t = 0; t < BT; ++t) acc[t][e] += c[t] * tv;
+                for (int t = 0; t < BT; ++t) acc[t][e] += cf[t] * tv;
             }
         }
     };
@@ -926,54 +943,66 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
     __syncthreads();
 
     // Integer partial sums are exact, so only the epilogue needs an order.
-    int* s_red = ismem;   // [kNSlot][CT] per token
-    const int cl = (lane % kLPR) * kI8EPT;
+    int* s_red = ismem;   // [kI8NSlot][CT] per token
+    const int cl = (lane % kI8LPR) * kI8EPT;
+    auto finish = [&](int64_t row, int64_t cg, int sum) {
+        if (a.acc) a.acc[row * n_out + cg] = sum;
+        if (a.y) a.y[row * n_out + cg] = __fmul_rn((float)sum, __fdiv_rn(a.alpha, a.xscale[row]));
+    };
 #pragma unroll
     for (int t = 0; t < BT; ++t) {
 #pragma unroll
         for (int e = 0; e < kI8EPT; ++e) s_red[slot * kI8CT + cl + e] = acc[t][e];
         __syncthreads();
-        for (int o = tid; o < kI8CT; o += kNT) {
-            int s = 0;
+        {
+            const int o = tid;   // kI8CT == kNT: one column per thread
+            int sum = 0;
 #pragma unroll
-            for (int sl = 0; sl < kNSlot; ++sl) s += s_red[sl * kI8CT + o];
+            for (int sl = 0; sl < kI8NSlot; ++sl) sum += s_red[sl * kI8CT + o];
             const int64_t row = tok0 + t;
             const int64_t cg = (int64_t)tile * kI8CT + o;
             if (row < rows && cg < n_out) {
-                if (nsplit == 1) {
-                    if (a.acc) a.acc[row * n_out + cg] = s;
-                    if (a.y) a.y[row * n_out + cg] =
-                        __fmul_rn((float)s, __fdiv_rn(a.alpha, a.xscale[row]));
-                } else {
-                    store_agent(&a.partial[((int64_t)split * rows + row) * n_out + cg], s);
-                }
+                if (nsplit == 1) finish(row, cg, sum);
+                else store_agent(&a.partial[((int64_t)split * rows + row) * n_out + cg], sum);
             }
         }
         __syncthreads();
     }
 
+    // The last split of the tile sums the partials; the loads of all of a
+    // thread's outputs for 8 splits are in flight together.
     if (nsplit > 1) {
         const int ci = tt * gridDim.x + tile;
         if (last_split_arrived(&a.counters[ci], nsplit, &s_last)) {
-            for (int o = tid; o < BT * kI8CT; o += kNT) {
-                const int64_t row = tok0 + o / kI8CT;
-                const int64_t cg = (int64_t)tile * kI8CT + (o % kI8CT);
-                if (row < rows && cg < n_out) {
-                    const int32_t* pp = a.partial + row * n_out + cg;
-                    const int64_t stride = rows * n_out;
-                    int s = 0;
-                    for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
-                        int v[16];
+            const int64_t stride = rows * n_out;
+            int64_t base[OPT];
+            bool ok[OPT];
+            int sum[OPT];
 #pragma unroll
-                        for (int u = 0; u < 16; ++u)
-                            v[u] = sp0 + u < nsplit ? load_agent(pp + (int64_t)(sp0 + u) * stride) : 0;
+            for (int q = 0; q < OPT; ++q) {
+                const int o = q * kNT + tid;
+                const int64_t row = tok0 + o / kI8CT, cg = (int64_t)tile * kI8CT + (o % kI8CT);
+                ok[q] = row < rows && cg < n_out;
+                base[q] = ok[q] ? row * n_out + cg : 0;
+                sum[q] = 0;
+            }
+            for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+                int v[8][OPT];
 #pragma unroll
-                        for (int u = 0; u < 16; ++u) s += v[u];
-                    }
-                    if (a.acc) a.acc[row * n_out + cg] = s;
-                    if (a.y) a.y[row * n_out + cg] =
-                        __fmul_rn((float)s, __fdiv_rn(a.alpha, a.xscale[row]));
-                }
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int q = 0; q < OPT; ++q)
+                        v[u][q] = (sp0 + u < nsplit && ok[q])
+                                      ? load_agent(a.partial + (int64_t)(sp0 + u) * stride + base[q]) : 0;
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int q = 0; q < OPT; ++q) sum[q] += v[u][q];
+            }
+#pragma unroll
+            for (int q = 0; q < OPT; ++q) {
+                const int o = q * kNT + tid;
+                if (ok[q]) finish(tok0 + o / kI8CT, (int64_t)tile * kI8CT + (o % kI8CT), sum[q]);
             }
             if (tid == 0) store_agent(&a.counters[ci], 0);
         }
@@ -1069,7 +1098,7 @@ I8tPlan plan_i8t(int64_t rows, int64_t d_in, int64_t n_out) {
     p.n_tiles = (int)ceil_div(n_out, p.ct);
     p.bt = pow2_tile(rows, 2);   // 32 int32 accumulators per token per lane
     p.n_tok_tiles = (int)ceil_div(rows, p.bt);
-    const int cand_max = 4096 / p.bt;
+    const int cand_max = kI8MaxCand;
     const int64_t base = (int64_t)p.n_tiles * p.n_tok_tiles;
     int64_t ns = ceil_div(kI8TargetWG, base);
     if (ns < 1) ns = 1;
@@ -1086,9 +1115,9 @@ I8tPlan plan_i8t(int64_t rows, int64_t d_in, int64_t n_out) {
 
 hipError_t launch_i8t(const I8tPlan& p, const I8tArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
-    const size_t padded = (size_t)p.cand + 3 * kNSlot * kUnroll;
+    const size_t padded = (size_t)p.cand + 3 * kI8NSlot * kUnroll;
     size_t lds_a = padded * p.bt * 4 + padded * 4;
-    size_t lds_c = (size_t)kNSlot * kI8CT * 4;
+    size_t lds_c = (size_t)kI8NSlot * kI8CT * 4;
     size_t lds = lds_a > lds_c ? lds_a : lds_c;
     dim3 grid(p.n_tiles, p.nsplit, p.n_tok_tiles);
 #define QS_I8T_CASE(BTV)                                                                \
