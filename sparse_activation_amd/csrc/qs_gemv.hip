@@ -338,16 +338,17 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
 }
 
 // ---------------------------------------------------------------------------
-// MFMA variant for 16-token tiles.  With 16 tokens the gather is an
-// (16 x rows) . (rows x n_out) product, so the multiply-adds go to
-// v_mfma_f32_16x16x4_f32: A = the coefficients of 16 tokens for 4 selected
-// rows (one per lane), B = the 4 rows' weights.  A 16-byte load gives a lane
-// EPT consecutive columns of one row; the EPT values feed EPT MFMAs whose
-// output columns are permuted accordingly (MFMA e, lane column j -> column
-// j * EPT + e), so no LDS transpose is needed.  Each wavefront owns 16 * EPT
-// columns and walks every selected row of the workgroup's candidate range,
-// so the workgroup needs no cross-wave reduction; fp32 products and sums
-// keep the fp32 intermediate exact to fp32 rounding.
+// fp32-MFMA variant for 16-token tiles of fp32 weights (bf16 weights take the
+// bf16 MFMA kernel below).  With 16 tokens the gather is a (16 x rows) .
+// (rows x n_out) product, so the multiply-adds go to v_mfma_f32_16x16x4_f32:
+// A = the coefficients of 16 tokens for 4 selected rows (one per lane), B =
+// the 4 rows' weights.  A 16-byte load gives a lane EPT consecutive columns
+// of one row; the EPT values feed EPT MFMAs whose output columns are permuted
+// accordingly (MFMA e, lane column j -> column j * EPT + e), so no LDS
+// transpose is needed.  The four wavefronts take different 4-row groups of
+// the workgroup's selected rows for the same 16 * EPT columns and are summed
+// in LDS in wave order; fp32 products and sums keep the result exact to fp32
+// rounding.
 // ---------------------------------------------------------------------------
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
