@@ -108,6 +108,16 @@ def relu2(u):
     return r * r
 
 
+def relu2_glu(g, u):
+    """Gated squared ReLU: relu(gate)^2 (.) up (Q-Sparse news article, end of
+    the Top-K section: squared ReLU in the FFN, with (.) the Hadamard
+    product).  The gated reading of that sentence; h keeps the sign of up."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    r = np.maximum(g, 0.0)
+    return (r * r) * u
+
+
 def drelu(g, u):
     """dReLU: relu(gate) (.) relu(up) (Turbo Sparse summary, Eq. 2: ReLU is
     applied after both the gate and the up projection)."""
@@ -139,6 +149,25 @@ def ffn_relu2_down_from(h, k_mid, w_down):
     m2, idx2, tau2, cut2 = topk_select(magnitude(h), k_mid)
     y, t_y = sparse_linear(h, w_down, m2)
     return dict(mask2=m2, idx2=idx2, tau2=tau2, cutoff2=cut2, y=y, T_y=t_y)
+
+
+def ffn_relu2_glu(x, k_in, w_gate, w_up, k_mid, w_down):
+    """Gated squared-ReLU FFN with top-K on the input and on the intermediate.
+
+    Steps: mask1 = top-K(|x|, k_in) (the same sparse input feeds both
+    projections); g = (x (.) mask1) . W_gate^T; u = (x (.) mask1) . W_up^T;
+    h = relu(g)^2 (.) u; mask2 = top-K(|h|, k_mid); y = (h (.) mask2) .
+    W_down^T (Turbo Sparse summary, Eq. 3-4, for the top-k% by magnitude
+    before W_down).  Returns every stage.
+    """
+    m1, idx1, tau1, cut1 = topk_select(magnitude(x), k_in)
+    g, t_g = sparse_linear(x, w_gate, m1)
+    u, t_u = sparse_linear(x, w_up, m1)
+    h = relu2_glu(g, u)
+    m2, idx2, tau2, cut2 = topk_select(magnitude(h), k_mid)
+    y, t_y = sparse_linear(h, w_down, m2)
+    return dict(mask1=m1, idx1=idx1, tau1=tau1, cutoff1=cut1, g=g, T_g=t_g, u=u, T_u=t_u,
+                h=h, mask2=m2, idx2=idx2, tau2=tau2, cutoff2=cut2, y=y, T_y=t_y)
 
 
 def ffn_drelu(x, w_gate, b_gate, w_up, b_up, w_down):
