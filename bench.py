@@ -8,7 +8,8 @@ One step is one call of qs_sparse_ffn over one batch: top-K of x, gathered up
 projection with the squared-ReLU epilogue, top-K of the intermediate,
 gathered down projection.
 
-Other workloads (--workload): c1 (fp32 1024x1024 linear, 8 tokens), c3
+Other workloads (--workload): c1 (fp32 1024x1024 linear, 8 tokens), c2g (the
+same Llama-7B FFN with a gate: gated squared ReLU), c3
 (int8 x ternary 4096x4096 linear), c4 (fused-QKV prefill through the MFMA
 path, 2048 tokens), c5 (Mistral-7B dReLU FFN decode).
 
@@ -55,7 +56,7 @@ def parse_args():
     p.add_argument("--steps", type=int, default=480)
     p.add_argument("--warmup", type=int, default=48)
     p.add_argument("--batch", type=int, default=1)
-    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c2g", "c3", "c4", "c5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--roofline-launches", type=int, default=96)
@@ -344,6 +345,60 @@ def run_c4(args, torch, np, qs, datagen, dev, stream):
     }
 
 
+def run_c2g(args, torch, np, qs, datagen, dev, stream):
+    B = args.batch
+    log(f"workload c2g: gated relu2 FFN decode B={B}; generating weights")
+    c = datagen.c2g_relu2glu_ffn(B)
+    d, ffn = c["W_up"].shape[1], c["W_up"].shape[0]
+    k_in, k_mid = c["K_in"], c["K_mid"]
+    n_copies = 2                                   # 2 x 271 MB > 256 MB MALL
+    wg = [bf16_dev(torch, np, c["W_gate"].T, dev)]
+    wu = [bf16_dev(torch, np, c["W_up"].T, dev)]
+    wd = [bf16_dev(torch, np, c["W_down"].T, dev)]
+    for _ in range(n_copies - 1):
+        wg.append(wg[0].clone()); wu.append(wu[0].clone()); wd.append(wd[0].clone())
+    xs = [bf16_dev(torch, np, datagen.c2g_relu2glu_ffn(B, rotation=i, with_weights=False)["X"], dev)
+          for i in range(N_XROT)]
+    y = torch.empty((B, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(qs.qs_workspace_bytes(qs.OP_SPARSE_FFN_RELU2_GLU, B, d, ffn),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i):
+        j = i % n_copies
+        qs.qs_sparse_ffn(xs[i % N_XROT], qs.ACT_RELU2_GLU, k_in, k_mid, wu[j], wd[j],
+                         w_gate=wg[j], y=y, ws=ws)
+
+    ms_step = time_graph(torch, stream, step, args.steps, args.warmup) / args.steps
+    # measured unions: rows of W_gate^T and W_up^T selected by some token, rows of W_down^T
+    u1, u2 = [], []
+    for i in range(N_XROT):
+        _, _, _, _, x1 = qs.qs_topk_mask(xs[i], k_in, want_mask=False, want_idx=False,
+                                          want_desc=False, want_xs=True)
+        _, h, _, _ = qs.qs_sparse_ffn(xs[i], qs.ACT_RELU2_GLU, k_in, k_mid, wu[0], wd[0],
+                                      w_gate=wg[0], want_h=True)
+        _, _, _, _, x2 = qs.qs_topk_mask(h, k_mid, want_mask=False, want_idx=False,
+                                          want_desc=False, want_xs=True)
+        u1.append(int((x1 != 0).any(0).sum()))
+        u2.append(int((x2 != 0).any(0).sum()))
+    step_bytes = np.mean([2 * u1[i] * ffn * 2 + u2[i] * d * 2 + B * (d * 4 * 2 + ffn * 4 * 3)
+                          for i in range(N_XROT)])
+    achieved = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"c2g: {ms_step * 1e3:.2f} us/step, {B / (ms_step * 1e-3):.0f} tokens/s, {achieved:.0f} GB/s")
+    return {
+        "metric": "gated squared-ReLU sparse FFN tokens/s at Llama-7B decode, 1 GPU",
+        "unit": "tokens/s", "value": round(B / (ms_step * 1e-3), 1),
+        "ms_per_step": round(ms_step, 6), "dtype": "bf16",
+        "config": {"workload": "llama7b_relu2glu_ffn_decode", "batch": B, "d": d, "ffn": ffn,
+                   "k_in": k_in, "k_mid": k_mid, "weight_copies": n_copies,
+                   "x_rotations": N_XROT, "union_rows_in": u1, "union_rows_mid": u2},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "whole FFN step (gate, up, top-K of h, down)",
+                     "algorithmic_bytes_per_step": round(float(step_bytes))},
+        "cpu_baseline": None,
+    }
+
+
 def run_c3(args, torch, np, qs, datagen, dev, stream):
     B = args.batch
     log(f"workload c3: int8 x ternary linear B={B}")
@@ -416,7 +471,8 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     if args.copy_calibration:
         copy_calibration(torch, dev)
-    run = {"c1": run_c1, "c2": run_c2, "c3": run_c3, "c4": run_c4, "c5": run_c5}[args.workload]
+    run = {"c1": run_c1, "c2": run_c2, "c2g": run_c2g, "c3": run_c3, "c4": run_c4,
+           "c5": run_c5}[args.workload]
     out = run(args, torch, np, qs, datagen, dev, stream)
     line = {"metric": out.pop("metric"), "value": out.pop("value"), "unit": out.pop("unit"),
             "n_gpus": 1, "steps": out.pop("steps", args.steps), "warmup": args.warmup,

@@ -87,6 +87,19 @@ def c2_relu2_ffn(batch: int, rotation: int = 0, with_weights: bool = True,
     return out
 
 
+def c2g_relu2glu_ffn(batch: int, rotation: int = 0, with_weights: bool = True,
+                     d: int = 4096, ffn: int = 11008) -> dict:
+    """The same Llama-7B FFN with a gate (gated squared ReLU): C2's input and
+    W_up/W_down draws unchanged, W_gate drawn after them from the same stream."""
+    out = c2_relu2_ffn(batch, rotation, False, d, ffn)
+    if with_weights:
+        g = np.random.default_rng(202)
+        out["W_up"] = bf16_round(normal(g, (ffn, d), 0.02))
+        out["W_down"] = bf16_round(normal(g, (d, ffn), 0.02))
+        out["W_gate"] = bf16_round(normal(g, (ffn, d), 0.02))
+    return out
+
+
 def c3_i8t_linear(batch: int, rotation: int = 0, with_weights: bool = True,
                   d: int = 4096, n: int = 4096) -> dict:
     """BitNet-b1.58-style linear: fp32 X = t4, fp32 source W ~ N(0, 0.02), 38.75% kept."""

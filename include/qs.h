@@ -85,8 +85,9 @@ typedef enum qs_layout {
 } qs_layout;
 
 typedef enum qs_act {
-    QS_ACT_RELU2 = 0,   /* h = relu(u)^2                       [QS-TopK]  */
-    QS_ACT_DRELU = 1    /* h = relu(x W_gate^T + b_g) * relu(x W_up^T + b_u)   [TS-Eq2] */
+    QS_ACT_RELU2 = 0,     /* h = relu(u)^2                       [QS-TopK]  */
+    QS_ACT_DRELU = 1,     /* h = relu(x W_gate^T + b_g) * relu(x W_up^T + b_u)   [TS-Eq2] */
+    QS_ACT_RELU2_GLU = 2  /* h = relu(x W_gate^T)^2 * (x W_up^T)  [QS-TopK] */
 } qs_act;
 
 typedef enum qs_op {
@@ -95,7 +96,8 @@ typedef enum qs_op {
     QS_OP_SPARSE_LINEAR_I8T = 2,
     QS_OP_SPARSE_FFN_RELU2 = 3,
     QS_OP_SPARSE_FFN_DRELU = 4,
-    QS_OP_GATHER_LINEAR = 5
+    QS_OP_GATHER_LINEAR = 5,
+    QS_OP_SPARSE_FFN_RELU2_GLU = 6
 } qs_op;
 
 /*
@@ -196,6 +198,15 @@ qs_status qs_sparse_linear_i8t(const float* x, int64_t rows, int64_t d_in, int64
  *       y = (h (.) M2) . W_down^T.
  *       w_gate = NULL; w_up = W_up^T [d, ffn]; w_down_t = W_down^T [ffn, d];
  *       b_gate, b_up must be NULL.
+ *   act == QS_ACT_RELU2_GLU   [QS-TopK], [TS-Eq3-4]
+ *       The gated reading of the squared ReLU (the article's FFN sentence
+ *       names a Hadamard product): dt QS_F32 or QS_BF16 (weights in the same
+ *       dtype); xm = x (.) M1, M1 = top-k_in of |x|, feeds both projections;
+ *       g = xm . W_gate^T; u = xm . W_up^T; h = fl32(relu(g)^2) * u (fp32);
+ *       M2 = top-k_mid of |h| (h can be negative; k_mid < 0: M2 = all of h);
+ *       y = (h (.) M2) . W_down^T.
+ *       w_gate = W_gate^T [d, ffn]; w_up = W_up^T [d, ffn]; w_down_t =
+ *       W_down^T [ffn, d]; b_gate, b_up must be NULL.
  *   act == QS_ACT_DRELU   [TS-Eq2], [TS-Fig]
  *       dt QS_BF16 only;  xm = x (.) M1 (k_in == d: no selection);
  *       g = xm . W_gate^T + b_gate; u = xm . W_up^T + b_up;

@@ -16,9 +16,9 @@ __all__ = [
     "load", "lib_path", "QS_OK", "QSError",
     "qs_topk_mask", "qs_gather_linear", "gather_workspace", "qs_stream_read", "qs_sparse_linear", "qs_sparse_linear_i8t", "qs_sparse_ffn",
     "qs_workspace_bytes", "qs_ternarize", "qs_pack_ternary", "qs_last_error", "qs_version",
-    "F32", "BF16", "I8", "LAYOUT_WT", "LAYOUT_W", "ACT_RELU2", "ACT_DRELU",
+    "F32", "BF16", "I8", "LAYOUT_WT", "LAYOUT_W", "ACT_RELU2", "ACT_DRELU", "ACT_RELU2_GLU",
     "OP_TOPK_MASK", "OP_SPARSE_LINEAR", "OP_SPARSE_LINEAR_I8T", "OP_SPARSE_FFN_RELU2",
-    "OP_SPARSE_FFN_DRELU", "OP_GATHER_LINEAR",
+    "OP_SPARSE_FFN_DRELU", "OP_GATHER_LINEAR", "OP_SPARSE_FFN_RELU2_GLU",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,9 +26,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 QS_OK, QS_ERR_INVALID_ARG, QS_ERR_UNSUPPORTED, QS_ERR_WORKSPACE, QS_ERR_HIP = range(5)
 F32, BF16, I8 = 0, 1, 2
 LAYOUT_WT, LAYOUT_W = 0, 1
-ACT_RELU2, ACT_DRELU = 0, 1
+ACT_RELU2, ACT_DRELU, ACT_RELU2_GLU = 0, 1, 2
 (OP_TOPK_MASK, OP_SPARSE_LINEAR, OP_SPARSE_LINEAR_I8T, OP_SPARSE_FFN_RELU2,
- OP_SPARSE_FFN_DRELU, OP_GATHER_LINEAR) = range(6)
+ OP_SPARSE_FFN_DRELU, OP_GATHER_LINEAR, OP_SPARSE_FFN_RELU2_GLU) = range(7)
 
 # Every function the header declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -264,7 +264,7 @@ def qs_sparse_linear_i8t(x, k: int, wt_packed, alpha: float, n_out: int, acc=Non
 def qs_sparse_ffn(x, act: int, k_in: int, k_mid: int, w_up, w_down_t, w_gate=None,
                   b_gate=None, b_up=None, y=None, y_dtype=None, h=None, mid_idx=None,
                   mid_cnt=None, ws=None, want_h=False, want_mid=False):
-    """Sparse FFN (squared ReLU or dReLU); returns (y, h, mid_idx, mid_cnt)."""
+    """Sparse FFN (squared ReLU, dReLU or gated squared ReLU); returns (y, h, mid_idx, mid_cnt)."""
     torch = _torch()
     rows, d = x.shape
     ffn = w_down_t.shape[0]
@@ -277,7 +277,8 @@ def qs_sparse_ffn(x, act: int, k_in: int, k_mid: int, w_up, w_down_t, w_gate=Non
         mid_idx = torch.empty((rows, ffn), dtype=torch.int32, device=dev)
     if want_mid and mid_cnt is None:
         mid_cnt = torch.empty(rows, dtype=torch.int32, device=dev)
-    op = OP_SPARSE_FFN_RELU2 if act == ACT_RELU2 else OP_SPARSE_FFN_DRELU
+    op = {ACT_RELU2: OP_SPARSE_FFN_RELU2, ACT_DRELU: OP_SPARSE_FFN_DRELU,
+          ACT_RELU2_GLU: OP_SPARSE_FFN_RELU2_GLU}.get(act, OP_SPARSE_FFN_RELU2)
     ws, ws_bytes = _workspace(ws, op, rows, d, ffn, dev)
     _check(load().qs_sparse_ffn(_ptr(x), _dtype_code(x), rows, d, ffn, act, k_in, k_mid,
                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down_t), _ptr(b_gate),

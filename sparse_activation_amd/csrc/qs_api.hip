@@ -177,6 +177,7 @@ qs_status qs_workspace_bytes(qs_op op, int64_t rows, int64_t d, int64_t n, size_
     case QS_OP_SPARSE_LINEAR_I8T: *bytes = i8t_ws(nullptr, rows, d, n).bytes; break;
     case QS_OP_SPARSE_FFN_RELU2: *bytes = ffn_ws(nullptr, rows, d, n, false).bytes; break;
     case QS_OP_SPARSE_FFN_DRELU: *bytes = ffn_ws(nullptr, rows, d, n, true).bytes; break;
+    case QS_OP_SPARSE_FFN_RELU2_GLU: *bytes = ffn_ws(nullptr, rows, d, n, false).bytes; break;
     case QS_OP_GATHER_LINEAR: *bytes = gather_ws(nullptr, rows, d, n).bytes; break;
     default: return fail(QS_ERR_INVALID_ARG, "qs_workspace_bytes: unknown op %d", (int)op);
     }
@@ -366,7 +367,7 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     const char* fn = "qs_sparse_ffn";
     if (rows < 0 || d <= 0 || ffn <= 0 || d > (int64_t(1) << 24) || ffn > (int64_t(1) << 24))
         return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
-    if (act != QS_ACT_RELU2 && act != QS_ACT_DRELU)
+    if (act != QS_ACT_RELU2 && act != QS_ACT_DRELU && act != QS_ACT_RELU2_GLU)
         return fail(QS_ERR_INVALID_ARG, "%s: unknown activation", fn);
     if (k_in < 0 || k_in > d) return fail(QS_ERR_INVALID_ARG, "%s: need 0 <= k_in <= d", fn);
     if (k_mid > ffn) return fail(QS_ERR_INVALID_ARG, "%s: need k_mid <= ffn", fn);
@@ -385,6 +386,8 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     if (act == QS_ACT_DRELU && !w_gate) return fail(QS_ERR_INVALID_ARG, "%s: dReLU needs w_gate", fn);
     if (act == QS_ACT_RELU2 && (w_gate || b_gate || b_up))
         return fail(QS_ERR_INVALID_ARG, "%s: squared ReLU takes no gate weights or biases", fn);
+    if (act == QS_ACT_RELU2_GLU && (!w_gate || b_gate || b_up))
+        return fail(QS_ERR_INVALID_ARG, "%s: gated squared ReLU needs w_gate and takes no biases", fn);
     const void* ptrs[] = {x, w_gate, w_up, w_down_t, b_gate, b_up, y, h, mid_idx, mid_cnt, ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return fail(QS_ERR_UNSUPPORTED, "%s: pointer not 16-byte aligned", fn);
@@ -413,6 +416,18 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
         g.partial = wsp.partial; g.counters = wsp.ctr_up; g.y = hbuf; g.y_bf16 = 0;
         g.epilogue = qs::EPI_RELU2;
         g.xs_bf16 = dt == QS_BF16;
+        if (act == QS_ACT_RELU2_GLU) {
+            // Gate first, kept in fp32 in the buffer that later holds the
+            // selected intermediate; the up gather then forms h in its epilogue.
+            // Both gathers read the same selected rows; the split counters
+            // are left zero by each.
+            qs::GemvArgs gg = g;
+            gg.w = w_gate; gg.y = wsp.hs; gg.epilogue = qs::EPI_STORE;
+            e = qs::launch_gemv(pu, wb, gg, st);
+            if (e != hipSuccess) return hip_fail(e, fn);
+            g.epilogue = qs::EPI_RELU2_GLU;
+            g.gate = wsp.hs;
+        }
         e = qs::launch_gemv(pu, wb, g, st);
         if (e != hipSuccess) return hip_fail(e, fn);
     } else {

@@ -131,6 +131,9 @@ __device__ __forceinline__ void unpack(const u32x4& v, float* w) {
 __device__ __forceinline__ void store_final(const GemvArgs& a, int64_t i, float s) {
     if (a.epilogue == EPI_RELU2) {
         reinterpret_cast<float*>(a.y)[i] = s > 0.0f ? __fmul_rn(s, s) : 0.0f;
+    } else if (a.epilogue == EPI_RELU2_GLU) {
+        const float g = a.gate[i];
+        reinterpret_cast<float*>(a.y)[i] = g > 0.0f ? __fmul_rn(__fmul_rn(g, g), s) : 0.0f;
     } else if (a.y_bf16) {
         reinterpret_cast<uint16_t*>(a.y)[i] = f32_to_bf16_rne(s);
     } else {

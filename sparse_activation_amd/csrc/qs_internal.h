@@ -48,7 +48,7 @@ hipError_t launch_topk(int key_kind, int xs_kind, int64_t rows, const TopkArgs& 
 // ---------------------------------------------------------------- gather GEMV
 // The gather kernels address weights through 32-bit buffer offsets.
 constexpr int64_t kMaxGatherWeightBytes = int64_t(1) << 30;
-enum Epilogue : int { EPI_STORE = 0, EPI_RELU2 = 1 };
+enum Epilogue : int { EPI_STORE = 0, EPI_RELU2 = 1, EPI_RELU2_GLU = 2 };
 
 // Launch plan of the gather GEMV: deterministic function of the shape only.
 struct GemvPlan {
@@ -75,7 +75,8 @@ struct GemvArgs {
     int32_t* counters;     // [n_counters], zero on entry, left zero on exit
     void* y;               // [rows, n_out]
     int y_bf16;            // output dtype
-    int epilogue;          // EPI_STORE or EPI_RELU2 (then y is fp32 h)
+    int epilogue;          // EPI_STORE, EPI_RELU2 (y is fp32 h) or EPI_RELU2_GLU (y is fp32 h)
+    const float* gate;     // EPI_RELU2_GLU: fp32 gate projection [rows, n_out]
     int xs_bf16;           // 1: every xs value is a bf16 number (from bf16 activations)
 };
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);

@@ -116,6 +116,17 @@ def test_i8t_and_ffn_validation():
     assert lib.qs_sparse_ffn(FAKE, qs.BF16, 2, 256, 512, qs.ACT_RELU2, 100, 50, FAKE, FAKE,
                              FAKE, None, None, FAKE, qs.F32, None, None, None, FAKE, need,
                              None) == 1
+    # gated squared ReLU: needs the gate, takes no biases; same workspace as squared ReLU
+    assert qs.qs_workspace_bytes(qs.OP_SPARSE_FFN_RELU2_GLU, 2, 256, 512) == need
+    assert lib.qs_sparse_ffn(FAKE, qs.BF16, 2, 256, 512, qs.ACT_RELU2_GLU, 100, 50, None, FAKE,
+                             FAKE, None, None, FAKE, qs.F32, None, None, None, FAKE, need,
+                             None) == 1
+    assert lib.qs_sparse_ffn(FAKE, qs.BF16, 2, 256, 512, qs.ACT_RELU2_GLU, 100, 50, FAKE, FAKE,
+                             FAKE, FAKE, None, FAKE, qs.F32, None, None, None, FAKE, need,
+                             None) == 1
+    assert lib.qs_sparse_ffn(FAKE, qs.BF16, 2, 256, 512, 3, 100, 50, FAKE, FAKE,
+                             FAKE, None, None, FAKE, qs.F32, None, None, None, FAKE, need,
+                             None) == 1
 
 
 def test_workspace_sizes_depend_on_shape_only():

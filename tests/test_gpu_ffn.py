@@ -81,6 +81,63 @@ def test_relu2_bf16_output(gpu_lib):
                 ydt=torch.bfloat16)
 
 
+# ---------------------------------------------------------------- gated squared ReLU
+
+def _relu2_glu_case(gpu_lib, x, wg, wu, wd, k_in, k_mid, wtype="bf16"):
+    import torch
+    qs = gpu_lib
+    dt = torch.bfloat16 if wtype == "bf16" else torch.float32
+    tol = 4e-3 if wtype == "bf16" else 1e-5
+    f = wu.shape[0]
+    y, h, mid_idx, mid_cnt = qs.qs_sparse_ffn(
+        to_dev(x, dt), qs.ACT_RELU2_GLU, k_in, k_mid, to_dev(np.ascontiguousarray(wu.T), dt),
+        to_dev(np.ascontiguousarray(wd.T), dt), w_gate=to_dev(np.ascontiguousarray(wg.T), dt),
+        want_h=True, want_mid=True)
+    torch.cuda.synchronize()
+    y, h, mid_idx, mid_cnt = (a.cpu().numpy() for a in (y, h, mid_idx, mid_cnt))
+    ref = oracle.ffn_relu2_glu(x, k_in, wg, wu, k_mid if k_mid >= 0 else f, wd)
+    # h = relu(g)^2 u with g, u each within tol * T: relu is 1-Lipschitz, so
+    # |dh| <= (2 relu(g) dg + dg^2)(|u| + du) + relu(g)^2 du.
+    dg, du = tol * ref["T_g"], tol * ref["T_u"]
+    rg = np.maximum(ref["g"], 0.0)
+    bound = (2 * rg * dg + dg * dg) * (np.abs(ref["u"]) + du) + rg * rg * du
+    err = np.abs(h.astype(np.float64) - ref["h"])
+    assert np.all(err <= bound), f"h outside bound: worst {np.max(err - bound)}"
+    if k_mid >= 0:
+        down = oracle.ffn_relu2_down_from(h, k_mid, wd)
+        for r in range(x.shape[0]):
+            assert mid_cnt[r] == k_mid
+            assert np.array_equal(mid_idx[r, :k_mid], down["idx2"][r])
+    else:
+        down = oracle.ffn_drelu_down_from(h, wd)
+        for r in range(x.shape[0]):
+            assert mid_cnt[r] == down["nz_count"][r]
+            assert np.array_equal(mid_idx[r, :mid_cnt[r]], down["nz_idx"][r])
+    assert_within(y, down["y"], down["T_y"], tol, "relu2-glu y")
+
+
+@pytest.mark.parametrize("rows,d,f", [(1, 64, 96), (3, 256, 520), (17, 512, 264)])
+@pytest.mark.parametrize("wtype", ["f32", "bf16"])
+def test_relu2_glu_small(gpu_lib, rows, d, f, wtype):
+    rng = np.random.default_rng(rows + 2 * d + f)
+    x = datagen.student_t(rng, (rows, d))
+    wg = datagen.normal(rng, (f, d), 0.02)
+    wu = datagen.normal(rng, (f, d), 0.02)
+    wd = datagen.normal(rng, (d, f), 0.02)
+    if wtype == "bf16":
+        x, wg, wu, wd = (datagen.bf16_round(a) for a in (x, wg, wu, wd))
+    for k_in, k_mid in [(d, f), ((2 * d) // 5, (2 * f) // 5), (1, 3), (0, 0), (d // 2, -1)]:
+        note(f"relu2-glu {wtype} rows={rows} d={d} ffn={f} k_in={k_in} k_mid={k_mid}")
+        _relu2_glu_case(gpu_lib, x, wg, wu, wd, k_in, k_mid, wtype)
+
+
+@pytest.mark.parametrize("batch", [1, 8, 16])
+def test_relu2_glu_full_llama7b(gpu_lib, batch):
+    c = datagen.c2g_relu2glu_ffn(batch)
+    note(f"gated relu2 FFN, Llama-7B shape, B={batch}")
+    _relu2_glu_case(gpu_lib, c["X"], c["W_gate"], c["W_up"], c["W_down"], c["K_in"], c["K_mid"])
+
+
 # ---------------------------------------------------------------- dReLU
 
 def _drelu_case(gpu_lib, x, wg, bg, wu, bu, wd, k_in=None, k_mid=-1):
