@@ -290,3 +290,36 @@ def ste_backward(grad_y):
     sparsified tensor is copied unchanged to the dense input, including at
     masked positions (Q-Sparse news article, Top-K section, STE passage)."""
     return np.array(grad_y, copy=True)
+
+
+def sparse_linear_backward(x, w, mask, grad_y):
+    """Gradients of Y = (X (.) M) . W^T, given dL/dY, with the top-K
+    treated by the straight-through estimator.
+
+    Q-Sparse news article, "Sparsification with the Top-K function", the
+    back-propagation passage: the top-K has a zero gradient almost everywhere,
+    so Q-Sparse computes the gradient with respect to the sparsified tensor
+    and copies it unchanged to the tensor before sparsification.  Through the
+    linear map (plain chain rule):
+
+        dXs = dY . W           gradient w.r.t. X (.) M   ([R, N] . [N, D])
+        dX  = dXs              the STE copy: no mask, masked-out entries keep
+                               their gradient (ste_backward)
+        dW  = dY^T . (X (.) M) ([N, R] . [R, D]); column j is zero unless some
+                               row selected feature j
+
+    Returns float64 dx [R, D], dw [N, D] and the error scales
+    T_dx = |dY| . |W| and T_dw = |dY|^T . |X (.) M| (sums of the absolute
+    products, for tolerances).  Library matmuls serve as the product steps.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    gy = np.asarray(grad_y, dtype=np.float64)
+    m = np.asarray(mask).astype(bool)
+    xs = np.where(m, x, 0.0)
+    dxs = gy @ w
+    dx = ste_backward(dxs)
+    dw = gy.T @ xs
+    t_dx = np.abs(gy) @ np.abs(w)
+    t_dw = np.abs(gy).T @ np.abs(xs)
+    return dict(dx=dx, T_dx=t_dx, dw=dw, T_dw=t_dw)
