@@ -11,7 +11,8 @@ gathered down projection.
 Other workloads (--workload): c1 (fp32 1024x1024 linear, 8 tokens), c2g (the
 same Llama-7B FFN with a gate: gated squared ReLU), c3
 (int8 x ternary 4096x4096 linear), c4 (fused-QKV prefill through the MFMA
-path, 2048 tokens), c5 (Mistral-7B dReLU FFN decode).
+path, 2048 tokens), c4b (the same projection's training backward with the
+straight-through estimator: dX and dW), c5 (Mistral-7B dReLU FFN decode).
 
 Measurement:
   * inputs are resident in HBM before timing; weight copies rotate so that
@@ -56,7 +57,7 @@ def parse_args():
     p.add_argument("--steps", type=int, default=480)
     p.add_argument("--warmup", type=int, default=48)
     p.add_argument("--batch", type=int, default=1)
-    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c2g", "c3", "c4", "c5"])
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c2g", "c3", "c4", "c4b", "c5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--roofline-launches", type=int, default=96)
@@ -340,7 +341,48 @@ def run_c4(args, torch, np, qs, datagen, dev, stream):
                    "k": c["K"]},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "whole call (top-K + gemm_nt_bf16_deep_kernel)"},
+                     "traffic": None, "kernel": "whole call (top-K + gemm_bf16_deep_kernel)"},
+        "cpu_baseline": None,
+    }
+
+
+def run_c4b(args, torch, np, qs, datagen, dev, stream):
+    log("workload c4b: fused-QKV training backward (straight-through estimator)")
+    c = datagen.c4_prefill_qkv()
+    (m, kdim), n = c["X"].shape, c["W"].shape[0]
+    w = bf16_dev(torch, np, c["W"], dev)
+    xs = [bf16_dev(torch, np, datagen.c4_prefill_qkv(rotation=i, with_weights=False)["X"], dev)
+          for i in range(2)]
+    gys = [bf16_dev(torch, np, datagen.c4_backward_grad(m, n, rotation=i), dev) for i in range(2)]
+    dx = torch.empty((m, kdim), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((n, kdim), dtype=torch.float32, device=dev)
+    ws = torch.empty(qs.qs_workspace_bytes(qs.OP_SPARSE_LINEAR_BACKWARD, m, kdim, n),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i, want_dx=True, want_dw=True):
+        qs.qs_sparse_linear_backward(xs[i % 2], c["K"], w, gys[i % 2], layout=qs.LAYOUT_W,
+                                     want_dx=want_dx, want_dw=want_dw, dx=dx, dw=dw, ws=ws)
+
+    steps = max(4, min(args.steps, 40))
+    ms_step = time_graph(torch, stream, step, steps, 4) / steps
+    ms_dx = time_graph(torch, stream, lambda i: step(i, want_dw=False), steps, 2) / steps
+    ms_dw = time_graph(torch, stream, lambda i: step(i, want_dx=False), steps, 2) / steps
+    flops = 2.0 * m * n * kdim
+    tflops = 2 * flops / (ms_step * 1e-3) / 1e12
+    log(f"c4b: {ms_step * 1e3:.1f} us/step, {tflops:.0f} TFLOP/s (top-K + dW GEMM + dX GEMM); "
+        f"dX alone {ms_dx * 1e3:.1f} us = {flops / (ms_dx * 1e-3) / 1e12:.0f} TFLOP/s, "
+        f"dW with its top-K {ms_dw * 1e3:.1f} us = {flops / (ms_dw * 1e-3) / 1e12:.0f} TFLOP/s")
+    return {
+        "metric": "STE backward tokens/s (fused QKV 4096->12288: dX and dW), 1 GPU",
+        "unit": "tokens/s", "value": round(m / (ms_step * 1e-3), 1),
+        "ms_per_step": round(ms_step, 6), "dtype": "bf16", "steps": steps,
+        "config": {"workload": "qkv_backward_2048x4096x12288", "tokens": m, "d": kdim, "n": n,
+                   "k": c["K"], "dx": "bf16", "dw": "fp32"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "whole call (top-K + two gemm_bf16_deep_kernel launches)",
+                     "dx_us": round(ms_dx * 1e3, 2), "dw_us_with_topk": round(ms_dw * 1e3, 2)},
         "cpu_baseline": None,
     }
 
@@ -471,7 +513,7 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     if args.copy_calibration:
         copy_calibration(torch, dev)
-    run = {"c1": run_c1, "c2": run_c2, "c2g": run_c2g, "c3": run_c3, "c4": run_c4,
+    run = {"c1": run_c1, "c2": run_c2, "c2g": run_c2g, "c3": run_c3, "c4": run_c4, "c4b": run_c4b,
            "c5": run_c5}[args.workload]
     out = run(args, torch, np, qs, datagen, dev, stream)
     line = {"metric": out.pop("metric"), "value": out.pop("value"), "unit": out.pop("unit"),

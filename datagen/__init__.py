@@ -120,6 +120,13 @@ def c4_prefill_qkv(rotation: int = 0, with_weights: bool = True,
     return out
 
 
+def c4_backward_grad(tokens: int = 2048, n: int = 12288, rotation: int = 0) -> np.ndarray:
+    """Upstream gradient dL/dY for a training step of the fused QKV projection:
+    bf16 N(0, 1) of shape [tokens, n] (the loss scale is arbitrary; the
+    backward is linear in it)."""
+    return bf16_round(normal(np.random.default_rng(404 + 1000 * rotation), (tokens, n), 1.0))
+
+
 def c5_drelu_ffn(batch: int, rotation: int = 0, with_weights: bool = True,
                  d: int = 4096, ffn: int = 14336, bias: float = DRELU_BIAS) -> dict:
     """Mistral-7B-shaped dReLU FFN decode in bf16 with shifted gate/up biases."""

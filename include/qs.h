@@ -19,6 +19,10 @@
  *               intermediate by absolute value before W_down.
  *   [TS-Fig]    Turbo Sparse summary, per-layer zero-activation figure
  *               (about 90% of FFN neurons inactive).
+ *   [QS-STE]    Q-Sparse news article, the back-propagation passage of the
+ *               Top-K section: the gradient is computed with respect to the
+ *               sparsified tensor and passed unchanged to the tensor before
+ *               sparsification (straight-through estimator).
  *
  * Readings where the pages are silent (each is part of the contract):
  *   - top-K is per row (token); among equal |x| the lower index wins, so the
@@ -97,7 +101,8 @@ typedef enum qs_op {
     QS_OP_SPARSE_FFN_RELU2 = 3,
     QS_OP_SPARSE_FFN_DRELU = 4,
     QS_OP_GATHER_LINEAR = 5,
-    QS_OP_SPARSE_FFN_RELU2_GLU = 6
+    QS_OP_SPARSE_FFN_RELU2_GLU = 6,
+    QS_OP_SPARSE_LINEAR_BACKWARD = 7
 } qs_op;
 
 /*
@@ -231,6 +236,39 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
                         const float* b_gate, const float* b_up,
                         void* y, qs_dtype yt, float* h, int32_t* mid_idx, int32_t* mid_cnt,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qs_sparse_linear_backward -- gradients of Y = (X (.) M) . W^T for a given
+ * dL/dY, the top-K passed by the straight-through estimator  [QS-STE],
+ * [QS-TopK]:
+ *
+ *   dX = dY . W             not masked: the gradient reaching X (.) M is
+ *                           copied to X, entries outside the selection too;
+ *   dW = dY^T . (X (.) M)   M recomputed from x with the same k (the same
+ *                           selection as the forward); feature columns that
+ *                           no row selected get exact zeros.
+ *
+ *   x       device bf16 [rows, d_in]: the forward's input.
+ *   k       0 <= k <= d_in, the forward's K.
+ *   w       device bf16 weights in layout w_layout (QS_LAYOUT_WT: W^T
+ *           [d_in, n_out]; QS_LAYOUT_W: W [n_out, d_in]); may be NULL when
+ *           dx is NULL.
+ *   dy      device bf16 [rows, n_out].
+ *   dx      device [rows, d_in], dtype dxt (QS_F32 or QS_BF16), or NULL.
+ *   dw      device, the layout of w (W^T [d_in, n_out] or W [n_out, d_in]),
+ *           dtype dwt (QS_F32 or QS_BF16), or NULL; overwritten (rows == 0
+ *           writes zeros).
+ *   Arithmetic: bf16 products exact in fp32, fp32 accumulation on matrix
+ *   cores (v_mfma_f32_32x32x16_bf16), bf16 outputs rounded to nearest-even.
+ *   Workspace: qs_workspace_bytes(QS_OP_SPARSE_LINEAR_BACKWARD, rows, d_in,
+ *   n_out) (X (.) M in bf16); needed only when dw is given.
+ *   Limits: d_in % 8 == 0, n_out % 8 == 0, each operand < 2^30 elements.
+ */
+qs_status qs_sparse_linear_backward(const void* x, qs_dtype xt, int64_t rows, int64_t d_in,
+                                    int64_t k, const void* w, qs_dtype wt_t, qs_layout w_layout,
+                                    int64_t n_out, const void* dy, qs_dtype dyt, void* dx,
+                                    qs_dtype dxt, void* dw, qs_dtype dwt, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /*
  * qs_workspace_bytes -- device workspace needed by `op` at this shape.

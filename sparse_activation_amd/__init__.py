@@ -19,6 +19,7 @@ __all__ = [
     "F32", "BF16", "I8", "LAYOUT_WT", "LAYOUT_W", "ACT_RELU2", "ACT_DRELU", "ACT_RELU2_GLU",
     "OP_TOPK_MASK", "OP_SPARSE_LINEAR", "OP_SPARSE_LINEAR_I8T", "OP_SPARSE_FFN_RELU2",
     "OP_SPARSE_FFN_DRELU", "OP_GATHER_LINEAR", "OP_SPARSE_FFN_RELU2_GLU",
+    "OP_SPARSE_LINEAR_BACKWARD", "qs_sparse_linear_backward",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +29,8 @@ F32, BF16, I8 = 0, 1, 2
 LAYOUT_WT, LAYOUT_W = 0, 1
 ACT_RELU2, ACT_DRELU, ACT_RELU2_GLU = 0, 1, 2
 (OP_TOPK_MASK, OP_SPARSE_LINEAR, OP_SPARSE_LINEAR_I8T, OP_SPARSE_FFN_RELU2,
- OP_SPARSE_FFN_DRELU, OP_GATHER_LINEAR, OP_SPARSE_FFN_RELU2_GLU) = range(7)
+ OP_SPARSE_FFN_DRELU, OP_GATHER_LINEAR, OP_SPARSE_FFN_RELU2_GLU,
+ OP_SPARSE_LINEAR_BACKWARD) = range(8)
 
 # Every function the header declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -39,6 +41,8 @@ _SIGS = {
     "qs_gather_linear": [_P, _I64, _I64, _P, _INT, _I64, _P, _INT, _P, ctypes.c_size_t, _P],
     "qs_sparse_linear": [_P, _INT, _I64, _I64, _I64, _P, _INT, _INT, _I64, _P, _INT, _P,
                          ctypes.c_size_t, _P],
+    "qs_sparse_linear_backward": [_P, _INT, _I64, _I64, _I64, _P, _INT, _INT, _I64, _P, _INT,
+                                  _P, _INT, _P, _INT, _P, ctypes.c_size_t, _P],
     "qs_sparse_linear_i8t": [_P, _I64, _I64, _I64, _P, ctypes.c_float, _I64, _P, _P, _P, _P,
                              _P, _P, ctypes.c_size_t, _P],
     "qs_sparse_ffn": [_P, _INT, _I64, _I64, _I64, _INT, _I64, _I64, _P, _P, _P, _P, _P, _P,
@@ -237,6 +241,34 @@ def qs_sparse_linear(x, k: int, w, layout: int = LAYOUT_WT, y=None, y_dtype=None
                                    _dtype_code(w), layout, n_out, _ptr(y), _dtype_code(y),
                                    _ptr(ws), ws_bytes, _stream(dev)))
     return y
+
+
+def qs_sparse_linear_backward(x, k: int, w, dy, layout: int = LAYOUT_W, want_dx=True,
+                              want_dw=True, dx=None, dw=None, out_dtype=None, ws=None):
+    """Gradients of Y = (X (.) M) . W^T with the straight-through estimator:
+    dX = dY . W (not masked), dW = dY^T . (X (.) M) in the layout of `w`
+    (W^T [d_in, n_out] for LAYOUT_WT, W [n_out, d_in] for LAYOUT_W).
+    Returns (dx, dw); either is None when not asked for."""
+    torch = _torch()
+    rows, d_in = x.shape
+    n_out = w.shape[1] if layout == LAYOUT_WT else w.shape[0]
+    d_w = w.shape[0] if layout == LAYOUT_WT else w.shape[1]
+    if d_w != d_in or tuple(dy.shape) != (rows, n_out):
+        raise ValueError("shapes of x, w and dy do not match")
+    dev = _dev(x, w, dy, dx, dw, ws)
+    odt = out_dtype or torch.float32
+    if want_dx and dx is None:
+        dx = torch.empty((rows, d_in), dtype=odt, device=dev)
+    if want_dw and dw is None:
+        dw = torch.empty(tuple(w.shape), dtype=odt, device=dev)
+    dx = dx if want_dx else None
+    dw = dw if want_dw else None
+    ws, ws_bytes = _workspace(ws, OP_SPARSE_LINEAR_BACKWARD, rows, d_in, n_out, dev)
+    _check(load().qs_sparse_linear_backward(
+        _ptr(x), _dtype_code(x), rows, d_in, k, _ptr(w), _dtype_code(w), layout, n_out,
+        _ptr(dy), _dtype_code(dy), _ptr(dx), _dtype_code(dx) if dx is not None else F32,
+        _ptr(dw), _dtype_code(dw) if dw is not None else F32, _ptr(ws), ws_bytes, _stream(dev)))
+    return dx, dw
 
 
 def qs_sparse_linear_i8t(x, k: int, wt_packed, alpha: float, n_out: int, acc=None, y=None,

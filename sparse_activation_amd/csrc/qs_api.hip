@@ -179,6 +179,7 @@ qs_status qs_workspace_bytes(qs_op op, int64_t rows, int64_t d, int64_t n, size_
     case QS_OP_SPARSE_FFN_DRELU: *bytes = ffn_ws(nullptr, rows, d, n, true).bytes; break;
     case QS_OP_SPARSE_FFN_RELU2_GLU: *bytes = ffn_ws(nullptr, rows, d, n, false).bytes; break;
     case QS_OP_GATHER_LINEAR: *bytes = gather_ws(nullptr, rows, d, n).bytes; break;
+    case QS_OP_SPARSE_LINEAR_BACKWARD: *bytes = ((size_t)rows * (size_t)d * 2 + 255) & ~size_t(255); break;
     default: return fail(QS_ERR_INVALID_ARG, "qs_workspace_bytes: unknown op %d", (int)op);
     }
     return ok();
@@ -475,6 +476,79 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     g.epilogue = qs::EPI_STORE;
     e = qs::launch_gemv(pd, wb, g, st);
     if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+qs_status qs_sparse_linear_backward(const void* x, qs_dtype xt, int64_t rows, int64_t d_in,
+                                    int64_t k, const void* w, qs_dtype wt_t, qs_layout w_layout,
+                                    int64_t n_out, const void* dy, qs_dtype dyt, void* dx,
+                                    qs_dtype dxt, void* dw, qs_dtype dwt, void* ws,
+                                    size_t ws_bytes, void* stream) {
+    const char* fn = "qs_sparse_linear_backward";
+    if (rows < 0 || d_in <= 0 || n_out <= 0 || d_in > (int64_t(1) << 24))
+        return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
+    if (k < 0 || k > d_in) return fail(QS_ERR_INVALID_ARG, "%s: need 0 <= k <= d_in", fn);
+    if (w_layout != QS_LAYOUT_WT && w_layout != QS_LAYOUT_W)
+        return fail(QS_ERR_INVALID_ARG, "%s: unknown weight layout", fn);
+    if (xt != QS_BF16 || wt_t != QS_BF16 || dyt != QS_BF16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: x, w and dy must be QS_BF16", fn);
+    if ((dx && !valid_float_dtype(dxt)) || (dw && !valid_float_dtype(dwt)))
+        return fail(QS_ERR_UNSUPPORTED, "%s: dx and dw dtypes must be QS_F32 or QS_BF16", fn);
+    if (d_in % 8 != 0 || n_out % 8 != 0)
+        return fail(QS_ERR_UNSUPPORTED, "%s: d_in and n_out must be multiples of 8", fn);
+    const int64_t lim = int64_t(1) << 30;
+    if (rows * d_in >= lim || rows * n_out >= lim || d_in * n_out >= lim)
+        return fail(QS_ERR_UNSUPPORTED, "%s: every operand must hold fewer than 2^30 elements", fn);
+    if (dx == nullptr && dw == nullptr) return ok();
+    if ((rows > 0 && (!x || !dy)) || (dx && !w))
+        return fail(QS_ERR_INVALID_ARG, "%s: x, dy (and w for dx) must be non-NULL", fn);
+    const void* ptrs[] = {x, w, dy, dx, dw};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(QS_ERR_UNSUPPORTED, "%s: pointer not 16-byte aligned", fn);
+    const size_t need = ((size_t)rows * (size_t)d_in * 2 + 255) & ~size_t(255);
+    if (dw && rows > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws)))
+        return fail(QS_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (dw) {
+        // dW = dY^T . (X (.) M): the mask recomputed from x (same k, same
+        // selection as the forward), X (.) M written in bf16, then a GEMM
+        // contracting over the tokens, both operands k-major.  rows == 0
+        // gives a zero gradient (every load is out of range).
+        const uint16_t* xm = (const uint16_t*)dw;
+        if (rows > 0) {
+            qs::TopkArgs t{};
+            t.x = x; t.d = d_in; t.k = k; t.idx_stride = k;
+            t.xs = ws;
+            e = qs::launch_topk(qs::KEY_BF16, qs::XS_BF16, rows, t, st);
+            if (e != hipSuccess) return hip_fail(e, fn);
+            xm = (const uint16_t*)ws;
+        }
+        const uint16_t* gy = rows > 0 ? (const uint16_t*)dy : (const uint16_t*)dw;
+        qs::GemmArgs g{};
+        g.a_kmajor = 1; g.b_kmajor = 1; g.k = rows; g.c = dw; g.c_bf16 = dwt == QS_BF16;
+        if (w_layout == QS_LAYOUT_WT) {     // dW^T [d_in, n_out]
+            g.a = xm; g.lda = d_in; g.m = d_in;
+            g.b = gy; g.ldb = n_out; g.n = n_out;
+        } else {                            // dW [n_out, d_in]
+            g.a = gy; g.lda = n_out; g.m = n_out;
+            g.b = xm; g.ldb = d_in; g.n = d_in;
+        }
+        e = qs::launch_gemm_bf16(g, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
+    if (dx && rows > 0) {
+        // dX = dY . W, not masked (straight-through estimator).
+        qs::GemmArgs g{};
+        g.a = (const uint16_t*)dy; g.a_kmajor = 0; g.lda = n_out;
+        g.m = rows; g.n = d_in; g.k = n_out;
+        g.b = (const uint16_t*)w;
+        if (w_layout == QS_LAYOUT_WT) { g.b_kmajor = 0; g.ldb = n_out; }   // W^T [d_in, n_out]
+        else { g.b_kmajor = 1; g.ldb = d_in; }                            // W [n_out, d_in]
+        g.c = dx; g.c_bf16 = dxt == QS_BF16;
+        e = qs::launch_gemm_bf16(g, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+    }
     return ok();
 }
 

@@ -112,6 +112,20 @@ struct MfmaArgs {
 };
 hipError_t launch_masked_gemm(const MfmaArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- bf16 GEMM, either operand layout
+// C[M, N] = sum_k A(m, k) B(n, k), fp32 accumulation.  An operand is
+// k-contiguous ([M, K] with row pitch lda, K % 8 == 0) or k-major ([K, M]
+// with row pitch lda, M % 8 == 0).  Every operand must be < 2^30 elements.
+struct GemmArgs {
+    const uint16_t* a;
+    const uint16_t* b;
+    int a_kmajor, b_kmajor;  // (1, 0) is not supported
+    int64_t m, n, k, lda, ldb;
+    void* c;                 // [M, N] row-major, fp32 or bf16 (RNE)
+    int c_bf16;
+};
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream);
+
 // ---------------------------------------------------------------- dReLU gate/up
 struct DreluArgs {
     const uint16_t* x;       // bf16 [rows, d] (already masked if k_in < d)

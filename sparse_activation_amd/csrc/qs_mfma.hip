@@ -165,30 +165,62 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_nt_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// The same product for K % 128 == 0, pipelined.  Tile 256 x BN x 64 per
-// workgroup of NW wavefronts (NW / 2 x 2, each 256 / (NW / 2) x BN / 2).
-// Slices of 64 along k go global -> registers two slices ahead of the MFMAs
-// and registers -> LDS (one of two buffers) one slice ahead, one barrier per
-// slice.  The per-CU vector-memory path (64 bytes per clock) and the LDS
-// stores would stall a wavefront for most of a slice if issued as a block, so
-// each chunk's LDS store and the reload of its register are interleaved with
-// the MFMAs (three MFMAs, one store, one load).  A row of a slice is 8 chunks
-// of 16 bytes stored at chunk position c ^ ((row >> 1) & 7): with 64 four-byte
-// banks and 16 lanes served per pass, the 16 rows of a fragment read's pass
-// hit 16 distinct 16-byte bank groups.  (Direct global -> LDS loads would save
-// the register staging, but the compiler then waits for every load in flight
-// before each LDS read.)
+// The same product, pipelined, for either operand layout.  An operand is
+// k-contiguous (row m holds A(m, 0..K-1), the nn.Linear layout) or k-major
+// (row k holds A(0..M-1, k), e.g. activations [tokens, features] when the
+// contraction runs over tokens, as in the weight gradient).  Tile
+// 256 x BN x 64 per workgroup of NW wavefronts (NW / 2 x 2, each
+// 256 / (NW / 2) x BN / 2).  Slices of 64 along k go global -> registers two
+// slices ahead of the MFMAs and registers -> LDS (one of two buffers) one
+// slice ahead, one barrier per slice.  The per-CU vector-memory path (64 bytes
+// per clock) and the LDS stores would stall a wavefront for most of a slice if
+// issued as a block, so each chunk's LDS store and the reload of its register
+// are interleaved with the MFMAs (three MFMAs, one store, one load).
+//
+// LDS layouts.  k-contiguous: a row of a slice is 8 chunks of 16 bytes stored
+// at chunk position c ^ ((row >> 1) & 7): with 64 four-byte banks and 16 lanes
+// served per pass, the 16 rows of a fragment read's pass hit 16 distinct
+// 16-byte bank groups.  k-major: the slice is stored as it lies in memory,
+// 64 k-rows of BM (or BN) elements padded by 64 bytes, and fragments come from
+// gfx950's transposing LDS read (ds_read_b64_tr_b16: in each group of 16
+// lanes, lane 4e + q supplies the address of four consecutive elements of
+// k-row e, and lane j receives element j % 4 of lane 4e + j / 4's run for
+// e = 0..3, i.e. four consecutive k of column 4q + j % 4).  With the pad a
+// pass of 32 lanes (4 k-rows x 64 bytes) covers 64 distinct banks.
+// (Direct global -> LDS loads would save the register staging, but the
+// compiler then waits for every load in flight before each LDS read.)
 // ---------------------------------------------------------------------------
-template <int BN, int NW>
-__global__ __launch_bounds__(64 * NW) void gemm_nt_bf16_deep_kernel(
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const u32x4* base, int byte_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const char* p = reinterpret_cast<const char*>(base) + byte_off;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+#else
+    (void)base; (void)byte_off;
+    return u32x2{0u, 0u};
+#endif
+}
+
+template <int BN, int NW, bool AK, bool BK>
+__global__ __launch_bounds__(64 * NW) void gemm_bf16_deep_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* __restrict__ C,
-    int M, int N, int K, int c_bf16, int tiles_m, int tiles_n) {
+    int M, int N, int K, int lda, int ldb, int c_bf16, int tiles_m, int tiles_n) {
     constexpr int NTH = 64 * NW, WM = NW / 2;              // wavefronts: WM x 2
     constexpr int BM = 256, TM = BM / WM / 32, TN = BN / 64;
     constexpr int QA = BM * 8 / NTH, QB = BN * 8 / NTH;    // 16-byte chunks per thread per slice
-    static_assert(BN % 64 == 0, "tile shape");
-    __shared__ u32x4 sA0[BM * 8], sA1[BM * 8];
-    __shared__ u32x4 sB0[BN * 8], sB1[BN * 8];
+    static_assert(BN % 64 == 0 && (BM * 8) % NTH == 0 && (BN * 8) % NTH == 0, "tile shape");
+    // LDS pitch (16-byte chunks) of a k-row in the k-major layout: a 64-byte pad
+    // puts four consecutive k-rows 64 bytes apart modulo 256.
+    constexpr int APITCH = BM / 8 + 4, BPITCH = BN / 8 + 4;
+    static_assert((APITCH * 16) % 256 == 64 || (APITCH * 16) % 256 == 192, "A pitch");
+    static_assert((BPITCH * 16) % 256 == 64 || (BPITCH * 16) % 256 == 192, "B pitch");
+    constexpr int ASZ = AK ? 64 * APITCH : BM * 8;
+    constexpr int BSZ = BK ? 64 * BPITCH : BN * 8;
+    __shared__ u32x4 sA0[ASZ], sA1[ASZ];
+    __shared__ u32x4 sB0[BSZ], sB1[BSZ];
 
     const int ntiles = tiles_m * tiles_n;
     int tile = blockIdx.x;
@@ -204,43 +236,87 @@ __global__ __launch_bounds__(64 * NW) void gemm_nt_bf16_deep_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    // Chunk q of this thread: LDS slot q * NTH + tid (row = slot / 8), holding
-    // global chunk (slot % 8) ^ (row & 7) of that row.  Rows past M or N
-    // repeat the last row; their results are never stored.
+    // Chunk q of this thread (slot sl = q * NTH + tid).
+    //  k-contiguous: LDS slot sl (row sl / 8) holds global chunk
+    //    (sl % 8) ^ ((row >> 1) & 7) of that row; rows past M or N repeat the
+    //    last row (their results are never stored).  kq = 8 * chunk.
+    //  k-major: k-row sl / (BM / 8), chunk sl % (BM / 8) of 8 columns, stored
+    //    unswizzled at pitch APITCH; chunks past M or N repeat the last chunk
+    //    (M % 8 == 0).  kq = the k-row.
+    // A chunk of slice kt is loaded iff 64 kt + kq < K (K % 8 == 0 when the
+    // operand is k-contiguous); otherwise at an out-of-range offset, which
+    // reads zeros and moves no memory.
+    // kq and the LDS slot are recomputed from (q, tid) where used: with q a
+    // compile-time constant they fold to a per-thread base plus a constant
+    // (or a short multiply-shift), which costs fewer registers than arrays.
+    auto kqa = [&](int q) -> int {
+        const int sl = q * NTH + tid;
+        if constexpr (!AK) return 8 * ((sl & 7) ^ (((sl >> 3) >> 1) & 7));
+        else return sl / (BM / 8);
+    };
+    auto kqb = [&](int q) -> int {
+        const int sl = q * NTH + tid;
+        if constexpr (!BK) return 8 * ((sl & 7) ^ (((sl >> 3) >> 1) & 7));
+        else return sl / (BN / 8);
+    };
+    auto lsa = [&](int q) -> int {
+        const int sl = q * NTH + tid;
+        if constexpr (!AK) return sl;
+        else return (sl / (BM / 8)) * APITCH + sl % (BM / 8);
+    };
+    auto lsb = [&](int q) -> int {
+        const int sl = q * NTH + tid;
+        if constexpr (!BK) return sl;
+        else return (sl / (BN / 8)) * BPITCH + sl % (BN / 8);
+    };
     int offa[QA], offb[QB];
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
-        const int sl = q * NTH + tid, row = sl >> 3, c = (sl & 7) ^ ((row >> 1) & 7);
-        offa[q] = min(m0 + row, M - 1) * K + 8 * c;
+        const int sl = q * NTH + tid;
+        if constexpr (!AK) {
+            const int row = sl >> 3;
+            offa[q] = min(m0 + row, M - 1) * lda + kqa(q);
+        } else {
+            offa[q] = kqa(q) * lda + min(m0 + 8 * (sl % (BM / 8)), M - 8);
+        }
     }
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-        const int sl = q * NTH + tid, row = sl >> 3, c = (sl & 7) ^ ((row >> 1) & 7);
-        offb[q] = min(n0 + row, N - 1) * K + 8 * c;
+        const int sl = q * NTH + tid;
+        if constexpr (!BK) {
+            const int row = sl >> 3;
+            offb[q] = min(n0 + row, N - 1) * ldb + kqb(q);
+        } else {
+            offb[q] = kqb(q) * ldb + min(n0 + 8 * (sl % (BN / 8)), N - 8);
+        }
     }
+    const uint32_t ksa = AK ? 64u * (uint32_t)lda : 64u;   // elements per slice step
+    const uint32_t ksb = BK ? 64u * (uint32_t)ldb : 64u;
     const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(A), (short)0, 0x7FFFFFFF, 0x00020000);
     const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(B), (short)0, 0x7FFFFFFF, 0x00020000);
-    const int nk = K / 64;   // even
-    // Slices past the end load at an out-of-range offset (zeros, no memory
-    // traffic): every load and store of the loop is unconditional, so the
-    // compiler's wait counts stay exact across iterations.
+    const int nk = (K + 63) / 64;
+    // Every load and store of the loop is unconditional (slices past the end
+    // load at the out-of-range offset), so the compiler's wait counts stay
+    // exact across iterations.
+    auto aoff = [&](int q, int kt) -> uint32_t {
+        return 64 * kt + kqa(q) < K ? ((uint32_t)offa[q] + (uint32_t)kt * ksa) * 2u : 0x80000000u;
+    };
+    auto boff = [&](int q, int kt) -> uint32_t {
+        return 64 * kt + kqb(q) < K ? ((uint32_t)offb[q] + (uint32_t)kt * ksb) * 2u : 0x80000000u;
+    };
     auto gload = [&](u32x4* ra, u32x4* rb, int kt) {
-        const int k0 = kt * 64;
-        const bool in = kt < nk;
 #pragma unroll
-        for (int q = 0; q < QA; ++q)
-            ra[q] = __builtin_amdgcn_raw_buffer_load_b128(ar, in ? (uint32_t)(offa[q] + k0) * 2u : 0x80000000u, 0, 0);
+        for (int q = 0; q < QA; ++q) ra[q] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff(q, kt), 0, 0);
 #pragma unroll
-        for (int q = 0; q < QB; ++q)
-            rb[q] = __builtin_amdgcn_raw_buffer_load_b128(br, in ? (uint32_t)(offb[q] + k0) * 2u : 0x80000000u, 0, 0);
+        for (int q = 0; q < QB; ++q) rb[q] = __builtin_amdgcn_raw_buffer_load_b128(br, boff(q, kt), 0, 0);
     };
     auto lstore = [&](u32x4* sa, u32x4* sb, const u32x4* ra, const u32x4* rb) {
 #pragma unroll
-        for (int q = 0; q < QA; ++q) sa[q * NTH + tid] = ra[q];
+        for (int q = 0; q < QA; ++q) sa[lsa(q)] = ra[q];
 #pragma unroll
-        for (int q = 0; q < QB; ++q) sb[q * NTH + tid] = rb[q];
+        for (int q = 0; q < QB; ++q) sb[lsb(q)] = rb[q];
     };
 
     f32x16 acc[TM][TN];
@@ -252,17 +328,36 @@ __global__ __launch_bounds__(64 * NW) void gemm_nt_bf16_deep_kernel(
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int r32 = lane & 31, kg = lane >> 5;
+    // Transposing-read addresses (k-major operands): lane group G = lane / 16
+    // covers columns 16 (G % 2) .. +15 and k 8 (G / 2) .. +7 of a 32 x 16
+    // fragment; lane j of the group addresses k-row j / 4 (+4 for the second
+    // read) and columns 4 (j % 4) .. +3.
+    const int trk = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     auto frag = [&](const u32x4* sa, const u32x4* sb, int ks, bf16x8* af, bf16x8* bfr) {
-        const int c = 2 * ks + kg;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int row = wm * (BM / WM) + i * 32 + r32;
-            af[i] = as_bf16x8(sa[row * 8 + (c ^ ((row >> 1) & 7))]);
+            const int row = wm * (BM / WM) + i * 32;
+            if constexpr (!AK) {
+                const int r = row + r32, c = 2 * ks + kg;
+                af[i] = as_bf16x8(sa[r * 8 + (c ^ ((r >> 1) & 7))]);
+            } else {
+                const int off = ((16 * ks + trk) * APITCH * 16) + (row + trc) * 2;
+                const u32x2 lo = lds_read_tr16(sa, off), hi = lds_read_tr16(sa, off + 4 * APITCH * 16);
+                af[i] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int row = wn * (BN / 2) + j * 32 + r32;
-            bfr[j] = as_bf16x8(sb[row * 8 + (c ^ ((row >> 1) & 7))]);
+            const int row = wn * (BN / 2) + j * 32;
+            if constexpr (!BK) {
+                const int r = row + r32, c = 2 * ks + kg;
+                bfr[j] = as_bf16x8(sb[r * 8 + (c ^ ((r >> 1) & 7))]);
+            } else {
+                const int off = ((16 * ks + trk) * BPITCH * 16) + (row + trc) * 2;
+                const u32x2 lo = lds_read_tr16(sb, off), hi = lds_read_tr16(sb, off + 4 * BPITCH * 16);
+                bfr[j] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
         }
     };
     // One slice: the MFMAs of slice kt (LDS buffer sa/sb), with the staging
@@ -272,18 +367,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_nt_bf16_deep_kernel(
     // reads for the next k-step, then (3 MFMAs, 1 LDS store, 1 global load)
     // groups, so the per-CU load and store traffic runs under the MFMAs
     // instead of stalling the wavefront in a block of its own.
-    constexpr int NI = QA + QB;            // staging items per slice (14 for BN = 192)
+    constexpr int NI = QA + QB;            // staging items per slice
     constexpr int IPK = (NI + 3) / 4;      // items per k-step
+    constexpr int NFR = TM * (AK ? 2 : 1) + TN * (BK ? 2 : 1);   // LDS reads per k-step
+    constexpr int MPI = (TM * TN) / IPK;   // MFMAs before each staging item
+    static_assert(MPI >= 1 && 4 * IPK >= NI, "staging schedule");
     auto item = [&](u32x4* wa, u32x4* wb, u32x4* ra, u32x4* rb, int q, int kt3) {
-        const int k0 = kt3 * 64;
-        const bool in = kt3 < nk;
         if (q < QA) {
-            wa[q * NTH + tid] = ra[q];
-            ra[q] = __builtin_amdgcn_raw_buffer_load_b128(ar, in ? (uint32_t)(offa[q] + k0) * 2u : 0x80000000u, 0, 0);
+            wa[lsa(q)] = ra[q];
+            ra[q] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff(q, kt3), 0, 0);
         } else {
             const int qb = q - QA;
-            wb[qb * NTH + tid] = rb[qb];
-            rb[qb] = __builtin_amdgcn_raw_buffer_load_b128(br, in ? (uint32_t)(offb[qb] + k0) * 2u : 0x80000000u, 0, 0);
+            wb[lsb(qb)] = rb[qb];
+            rb[qb] = __builtin_amdgcn_raw_buffer_load_b128(br, boff(qb, kt3), 0, 0);
         }
     };
     auto slice = [&](const u32x4* sa, const u32x4* sb, u32x4* wa, u32x4* wb, u32x4* ra, u32x4* rb, int kt3) {
@@ -296,18 +392,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_nt_bf16_deep_kernel(
             for (int m = 0; m < TM * TN; ++m) {
                 const int i = m / TN, j = m % TN;
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0, 0, 0);
-                const int q = ks * IPK + m / 3;
-                if (m % 3 == 2 && m / 3 < IPK && q < NI) item(wa, wb, ra, rb, q, kt3);
+                const int q = ks * IPK + m / MPI;
+                if (m % MPI == MPI - 1 && m / MPI < IPK && q < NI) item(wa, wb, ra, rb, q, kt3);
             }
-            if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);   // next fragments
+            if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, NFR, 0);   // next fragments
 #pragma unroll
-            for (int g = 0; g < (TM * TN) / 3; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                  // 3 MFMAs
-                if (g < IPK && ks * IPK + g < NI) {
+            for (int g = 0; g < IPK; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, MPI, 0);                // MPI MFMAs
+                if (ks * IPK + g < NI) {
                     __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);              // 1 LDS store
                     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);              // 1 global load
                 }
             }
+            if constexpr (TM * TN > MPI * IPK)
+                __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - MPI * IPK, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -319,7 +417,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_nt_bf16_deep_kernel(
     __syncthreads();
     // Slice kt reads buffer kt % 2 and stages slice kt + 1 into the other one,
     // whose last reader (slice kt - 1) finished before the previous barrier.
-    // The last pair stages a past-the-end slice into a buffer nobody reads.
+    // An odd slice count runs one all-zero slice at the end; the last pair
+    // stages a past-the-end slice into a buffer nobody reads.
     for (int kt = 0; kt < nk; kt += 2) {
         slice(sA0, sB0, sA1, sB1, ra1, rb1, kt + 3);
         __syncthreads();
@@ -581,12 +680,30 @@ hipError_t launch_gemm_cfg(const MfmaArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int BN, int NW>
-hipError_t launch_gemm_deep(const MfmaArgs& a, hipStream_t stream) {
-    const int tiles_m = (int)((a.m + 255) / 256), tiles_n = (int)((a.n + BN - 1) / BN);
-    gemm_nt_bf16_deep_kernel<BN, NW><<<dim3(tiles_m * tiles_n), dim3(64 * NW), 0, stream>>>(
-        a.x, a.w, a.y, (int)a.m, (int)a.n, (int)a.k, a.y_bf16, tiles_m, tiles_n);
+template <int BN, int NW, bool AK, bool BK>
+hipError_t launch_gemm_deep(const uint16_t* A, const uint16_t* B, void* C, int64_t m, int64_t n,
+                            int64_t k, int64_t lda, int64_t ldb, int c_bf16, hipStream_t stream) {
+    const int tiles_m = (int)((m + 255) / 256), tiles_n = (int)((n + BN - 1) / BN);
+    gemm_bf16_deep_kernel<BN, NW, AK, BK><<<dim3(tiles_m * tiles_n), dim3(64 * NW), 0, stream>>>(
+        A, B, C, (int)m, (int)n, (int)k, (int)lda, (int)ldb, c_bf16, tiles_m, tiles_n);
     return hipGetLastError();
+}
+
+// Idle share of the last round of workgroups (one 256 x BN tile per CU).
+double tile_waste(int64_t m, int64_t n, int bn) {
+    const int64_t t = (m + 255) / 256 * ((n + bn - 1) / bn);
+    const int64_t r = (t + 255) / 256 * 256;
+    return (double)(r - t) / (double)r;
+}
+
+template <bool AK, bool BK>
+hipError_t launch_gemm_layout(const GemmArgs& g, hipStream_t stream) {
+    // (k-contiguous A, k-major B) at BN = 192 would need more than the 256
+    // registers a wavefront has at two wavefronts per SIMD: 128 only.
+    if ((!AK && BK) || tile_waste(g.m, g.n, 128) + 1e-9 < tile_waste(g.m, g.n, 192))
+        return launch_gemm_deep<128, 8, AK, BK>(g.a, g.b, g.c, g.m, g.n, g.k, g.lda, g.ldb, g.c_bf16, stream);
+    if constexpr (!AK && BK) return hipErrorInvalidValue;   // not reached
+    else return launch_gemm_deep<192, 8, AK, BK>(g.a, g.b, g.c, g.m, g.n, g.k, g.lda, g.ldb, g.c_bf16, stream);
 }
 
 }  // namespace
@@ -599,9 +716,17 @@ hipError_t launch_masked_gemm(const MfmaArgs& a, hipStream_t stream) {
     auto waste = [](int64_t t) { int64_t r = (t + 255) / 256 * 256; return (double)(r - t) / r; };
     const bool w192 = waste(t192) + 1e-9 < waste(t256);
     if (a.k % 128 == 0 && (int64_t)a.m * a.k < (int64_t(1) << 30) && (int64_t)a.n * a.k < (int64_t(1) << 30))
-        return launch_gemm_deep<192, 8>(a, stream);
+        return launch_gemm_deep<192, 8, false, false>(a.x, a.w, a.y, a.m, a.n, a.k, a.k, a.k, a.y_bf16, stream);
     if (w192) return launch_gemm_cfg<256, 192, 2, 3>(a, stream);
     return launch_gemm_cfg<256, 256, 2, 4>(a, stream);
+}
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream) {
+    if (g.m <= 0 || g.n <= 0) return hipSuccess;
+    if (!g.a_kmajor && !g.b_kmajor) return launch_gemm_layout<false, false>(g, stream);
+    if (!g.a_kmajor && g.b_kmajor) return launch_gemm_layout<false, true>(g, stream);
+    if (g.a_kmajor && g.b_kmajor) return launch_gemm_layout<true, true>(g, stream);
+    return hipErrorInvalidValue;   // k-major A with k-contiguous B: not instantiated
 }
 
 hipError_t launch_drelu_gate_up(const DreluArgs& a, hipStream_t stream) {

@@ -166,3 +166,31 @@ def test_pack_ternary_roundtrip_through_oracle_decoder():
     assert np.array_equal(oracle.unpack_ternary(packed, 64), t)
     with pytest.raises(qs.QSError):
         qs.qs_pack_ternary(np.full((4, 4), 2, dtype=np.int8))
+
+
+def test_backward_validation_and_workspace():
+    lib = qs.load()
+    need = qs.qs_workspace_bytes(qs.OP_SPARSE_LINEAR_BACKWARD, 4, 1024, 512)
+    assert need == 4 * 1024 * 2
+    assert qs.qs_workspace_bytes(qs.OP_SPARSE_LINEAR_BACKWARD, 3, 8, 16) == 256
+
+    def call(x=FAKE, xt=qs.BF16, rows=4, d=1024, k=100, w=FAKE, wt=qs.BF16, lay=qs.LAYOUT_W,
+             n=512, dy=FAKE, dyt=qs.BF16, dx=FAKE, dxt=qs.F32, dw=FAKE, dwt=qs.F32, ws=None,
+             wsb=0):
+        return lib.qs_sparse_linear_backward(x, xt, rows, d, k, w, wt, lay, n, dy, dyt, dx, dxt,
+                                             dw, dwt, ws, wsb, None)
+    assert call(k=1025) == 1                         # k > d_in
+    assert call(k=-1) == 1
+    assert call(lay=5) == 1                          # unknown layout
+    assert call(xt=qs.F32) == 2                      # bf16 only
+    assert call(dyt=qs.F32) == 2
+    assert call(dxt=qs.I8) == 2
+    assert call(d=1020) == 2                         # d_in % 8
+    assert call(n=500) == 2                          # n_out % 8
+    assert call(rows=1 << 20, d=1024) == 2           # operand of 2^30 elements
+    assert call(x=None) == 1
+    assert call(w=None) == 1                         # w needed for dx
+    assert call(dx=MISALIGNED) == 2
+    assert call() == 3                               # dw without workspace
+    assert call(ws=FAKE, wsb=need - 1) == 3
+    assert call(dx=None, dw=None) == 0               # nothing asked: no-op
