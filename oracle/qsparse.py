@@ -73,6 +73,37 @@ def topk_select(mag, k: int):
     return mask, idx, tau, cutoff
 
 
+def block_topk_select(mag, n_keep: int, block: int):
+    """Block Q-Sparse selection: top-``n_keep`` by magnitude inside every
+    contiguous block of ``block`` features of each row, ties to the lower
+    index (an N:M pattern, N = n_keep, M = block).
+
+    Q-Sparse abstract (the arXiv 2407.10969 listing page, authors' English
+    abstract) introduces Block Q-Sparse for batch training and inference; the
+    same page's machine-written Chinese summary (method details, key-design
+    item 3) says only that the activations are divided into blocks to use the
+    hardware better.  Neither gives the rule, so this is a reading:
+    the top-K of the Top-K section applied within each block of contiguous
+    features of a token, with K = n_keep per block, which is the N:M
+    structured pattern that sparse matrix cores accept (2:4 on the MI355X).
+
+    Step by step: for each block, sort its magnitudes by (magnitude
+    descending, index ascending) and keep the first n_keep.  Returns the u8
+    mask [R, D].  D must be a multiple of ``block``.
+    """
+    mag = np.asarray(mag, dtype=np.float64)
+    rows, d = mag.shape
+    if d % block != 0 or not 0 <= n_keep <= block:
+        raise ValueError("D must be a multiple of block and 0 <= n_keep <= block")
+    mask = np.zeros((rows, d), dtype=np.uint8)
+    j = np.arange(block)
+    for r in range(rows):
+        for b0 in range(0, d, block):
+            order = np.lexsort((j, -mag[r, b0:b0 + block]))
+            mask[r, b0 + order[:n_keep]] = 1
+    return mask
+
+
 # ---------------------------------------------------------------------------
 # Sparse-activation linear
 # ---------------------------------------------------------------------------
