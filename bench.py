@@ -12,7 +12,8 @@ Other workloads (--workload): c1 (fp32 1024x1024 linear, 8 tokens), c2g (the
 same Llama-7B FFN with a gate: gated squared ReLU), c3
 (int8 x ternary 4096x4096 linear), c4 (fused-QKV prefill through the MFMA
 path, 2048 tokens), c4b (the same projection's training backward with the
-straight-through estimator: dX and dW), c5 (Mistral-7B dReLU FFN decode).
+straight-through estimator: dX and dW), c4s (the same prefill under Block
+Q-Sparse 2:4 on the sparse matrix cores), c5 (Mistral-7B dReLU FFN decode).
 
 Measurement:
   * inputs are resident in HBM before timing; weight copies rotate so that
@@ -57,7 +58,7 @@ def parse_args():
     p.add_argument("--steps", type=int, default=480)
     p.add_argument("--warmup", type=int, default=48)
     p.add_argument("--batch", type=int, default=1)
-    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c2g", "c3", "c4", "c4b", "c5"])
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c2g", "c3", "c4", "c4b", "c4s", "c5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--roofline-launches", type=int, default=96)
@@ -346,6 +347,41 @@ def run_c4(args, torch, np, qs, datagen, dev, stream):
     }
 
 
+def run_c4s(args, torch, np, qs, datagen, dev, stream):
+    log("workload c4s: fused-QKV prefill under Block Q-Sparse (2:4) on sparse MFMA")
+    c = datagen.c4_prefill_qkv()
+    (m, kdim), n = c["X"].shape, c["W"].shape[0]
+    w = bf16_dev(torch, np, c["W"], dev)
+    xs = [bf16_dev(torch, np, datagen.c4_prefill_qkv(rotation=i, with_weights=False)["X"], dev)
+          for i in range(2)]
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(qs.qs_workspace_bytes(qs.OP_BLOCK_SPARSE_LINEAR, m, kdim, n),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i):
+        qs.qs_block_sparse_linear(xs[i % 2], w, y=y, ws=ws)
+
+    steps = max(4, min(args.steps, 40))
+    ms_step = time_graph(torch, stream, step, steps, 4) / steps
+    kept_flops = 2.0 * m * n * (kdim // 2)            # the MACs on kept entries
+    tflops = kept_flops / (ms_step * 1e-3) / 1e12
+    dense_eq = 2 * tflops
+    log(f"c4s: {ms_step * 1e3:.1f} us/step, {tflops:.0f} TFLOP/s on kept entries "
+        f"({dense_eq:.0f} dense-equivalent), pack + sparse GEMM")
+    return {
+        "metric": "Block Q-Sparse (2:4) prefill tokens/s (fused QKV 4096->12288), 1 GPU",
+        "unit": "tokens/s", "value": round(m / (ms_step * 1e-3), 1),
+        "ms_per_step": round(ms_step, 6), "dtype": "bf16", "steps": steps,
+        "config": {"workload": "qkv_prefill_block24_2048x4096x12288", "tokens": m, "d": kdim,
+                   "n": n, "pattern": "2:4"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "dense_equivalent_tflops": round(dense_eq, 1),
+                     "kernel": "whole call (nm24_pack_kernel + gemm_sp24_kernel)"},
+        "cpu_baseline": None,
+    }
+
+
 def run_c4b(args, torch, np, qs, datagen, dev, stream):
     log("workload c4b: fused-QKV training backward (straight-through estimator)")
     c = datagen.c4_prefill_qkv()
@@ -513,7 +549,7 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     if args.copy_calibration:
         copy_calibration(torch, dev)
-    run = {"c1": run_c1, "c2": run_c2, "c2g": run_c2g, "c3": run_c3, "c4": run_c4, "c4b": run_c4b,
+    run = {"c1": run_c1, "c2": run_c2, "c2g": run_c2g, "c3": run_c3, "c4": run_c4, "c4b": run_c4b, "c4s": run_c4s,
            "c5": run_c5}[args.workload]
     out = run(args, torch, np, qs, datagen, dev, stream)
     line = {"metric": out.pop("metric"), "value": out.pop("value"), "unit": out.pop("unit"),

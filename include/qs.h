@@ -23,6 +23,11 @@
  *               Top-K section: the gradient is computed with respect to the
  *               sparsified tensor and passed unchanged to the tensor before
  *               sparsification (straight-through estimator).
+ *   [QS-Block]  Q-Sparse abstract (arXiv 2407.10969 listing page, authors'
+ *               English abstract): Block Q-Sparse for batch training and
+ *               inference; the same page's Chinese summary (method details,
+ *               key-design item 3): activations split into blocks to use the
+ *               hardware better.  The rule itself is not on the pages.
  *
  * Readings where the pages are silent (each is part of the contract):
  *   - top-K is per row (token); among equal |x| the lower index wins, so the
@@ -102,7 +107,8 @@ typedef enum qs_op {
     QS_OP_SPARSE_FFN_DRELU = 4,
     QS_OP_GATHER_LINEAR = 5,
     QS_OP_SPARSE_FFN_RELU2_GLU = 6,
-    QS_OP_SPARSE_LINEAR_BACKWARD = 7
+    QS_OP_SPARSE_LINEAR_BACKWARD = 7,
+    QS_OP_BLOCK_SPARSE_LINEAR = 8
 } qs_op;
 
 /*
@@ -269,6 +275,30 @@ qs_status qs_sparse_linear_backward(const void* x, qs_dtype xt, int64_t rows, in
                                     int64_t n_out, const void* dy, qs_dtype dyt, void* dx,
                                     qs_dtype dxt, void* dw, qs_dtype dwt, void* ws,
                                     size_t ws_bytes, void* stream);
+
+/*
+ * qs_block_sparse_linear -- Block Q-Sparse linear Y = (X (.) M) . W^T with M
+ * the 2:4 block pattern  [QS-Block], [QS-TopK]
+ *
+ *   Reading (the pages give no rule): the top-K of [QS-TopK] taken inside
+ *   every contiguous block of 4 features of a token, K = 2 per block, ties to
+ *   the lower index (bf16 key = bits & 0x7FFF, as qs_topk_mask).  This is the
+ *   pattern the structured-sparse matrix cores take, so the product runs on
+ *   v_smfmac_f32_32x32x32_bf16 over the kept half of X.
+ *
+ *   x       device bf16 [rows, d_in].
+ *   w       device bf16 W [n_out, d_in] (nn.Linear layout).
+ *   y       device [rows, n_out], dtype yt (QS_F32 or QS_BF16, RNE).
+ *   mask    device u8 [rows, d_in] or NULL: 1 at the kept entries.
+ *   Arithmetic: bf16 products exact in fp32, fp32 accumulation.
+ *   Workspace: qs_workspace_bytes(QS_OP_BLOCK_SPARSE_LINEAR, rows, d_in,
+ *   n_out) (the packed operand: kept values and 2-bit positions).
+ *   Limits: d_in % 32 == 0, n_out % 8 == 0, x and w < 2^30 elements.
+ */
+qs_status qs_block_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_in,
+                                 const void* w, qs_dtype wt_t, int64_t n_out, void* y,
+                                 qs_dtype yt, uint8_t* mask, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /*
  * qs_workspace_bytes -- device workspace needed by `op` at this shape.

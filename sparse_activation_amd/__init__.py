@@ -19,7 +19,8 @@ __all__ = [
     "F32", "BF16", "I8", "LAYOUT_WT", "LAYOUT_W", "ACT_RELU2", "ACT_DRELU", "ACT_RELU2_GLU",
     "OP_TOPK_MASK", "OP_SPARSE_LINEAR", "OP_SPARSE_LINEAR_I8T", "OP_SPARSE_FFN_RELU2",
     "OP_SPARSE_FFN_DRELU", "OP_GATHER_LINEAR", "OP_SPARSE_FFN_RELU2_GLU",
-    "OP_SPARSE_LINEAR_BACKWARD", "qs_sparse_linear_backward",
+    "OP_SPARSE_LINEAR_BACKWARD", "qs_sparse_linear_backward", "OP_BLOCK_SPARSE_LINEAR",
+    "qs_block_sparse_linear",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,7 +31,7 @@ LAYOUT_WT, LAYOUT_W = 0, 1
 ACT_RELU2, ACT_DRELU, ACT_RELU2_GLU = 0, 1, 2
 (OP_TOPK_MASK, OP_SPARSE_LINEAR, OP_SPARSE_LINEAR_I8T, OP_SPARSE_FFN_RELU2,
  OP_SPARSE_FFN_DRELU, OP_GATHER_LINEAR, OP_SPARSE_FFN_RELU2_GLU,
- OP_SPARSE_LINEAR_BACKWARD) = range(8)
+ OP_SPARSE_LINEAR_BACKWARD, OP_BLOCK_SPARSE_LINEAR) = range(9)
 
 # Every function the header declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -43,6 +44,8 @@ _SIGS = {
                          ctypes.c_size_t, _P],
     "qs_sparse_linear_backward": [_P, _INT, _I64, _I64, _I64, _P, _INT, _INT, _I64, _P, _INT,
                                   _P, _INT, _P, _INT, _P, ctypes.c_size_t, _P],
+    "qs_block_sparse_linear": [_P, _INT, _I64, _I64, _P, _INT, _I64, _P, _INT, _P, _P,
+                               ctypes.c_size_t, _P],
     "qs_sparse_linear_i8t": [_P, _I64, _I64, _I64, _P, ctypes.c_float, _I64, _P, _P, _P, _P,
                              _P, _P, ctypes.c_size_t, _P],
     "qs_sparse_ffn": [_P, _INT, _I64, _I64, _I64, _INT, _I64, _I64, _P, _P, _P, _P, _P, _P,
@@ -269,6 +272,27 @@ def qs_sparse_linear_backward(x, k: int, w, dy, layout: int = LAYOUT_W, want_dx=
         _ptr(dy), _dtype_code(dy), _ptr(dx), _dtype_code(dx) if dx is not None else F32,
         _ptr(dw), _dtype_code(dw) if dw is not None else F32, _ptr(ws), ws_bytes, _stream(dev)))
     return dx, dw
+
+
+def qs_block_sparse_linear(x, w, y=None, y_dtype=None, want_mask=False, mask=None, ws=None):
+    """Block Q-Sparse linear: Y = (X (.) M) . W^T with M keeping the 2 largest
+    |x| of every contiguous block of 4 features (ties to the lower index).
+    `w` is W [n_out, d_in].  Returns (y, mask) (mask None unless asked for)."""
+    torch = _torch()
+    rows, d_in = x.shape
+    n_out = w.shape[0]
+    if w.shape[1] != d_in:
+        raise ValueError("weight shape does not match x")
+    dev = _dev(x, w, y, mask, ws)
+    if y is None:
+        y = torch.empty((rows, n_out), dtype=y_dtype or torch.float32, device=dev)
+    if want_mask and mask is None:
+        mask = torch.empty((rows, d_in), dtype=torch.uint8, device=dev)
+    ws, ws_bytes = _workspace(ws, OP_BLOCK_SPARSE_LINEAR, rows, d_in, n_out, dev)
+    _check(load().qs_block_sparse_linear(_ptr(x), _dtype_code(x), rows, d_in, _ptr(w),
+                                         _dtype_code(w), n_out, _ptr(y), _dtype_code(y),
+                                         _ptr(mask), _ptr(ws), ws_bytes, _stream(dev)))
+    return y, mask
 
 
 def qs_sparse_linear_i8t(x, k: int, wt_packed, alpha: float, n_out: int, acc=None, y=None,

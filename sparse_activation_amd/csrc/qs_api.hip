@@ -180,6 +180,7 @@ qs_status qs_workspace_bytes(qs_op op, int64_t rows, int64_t d, int64_t n, size_
     case QS_OP_SPARSE_FFN_RELU2_GLU: *bytes = ffn_ws(nullptr, rows, d, n, false).bytes; break;
     case QS_OP_GATHER_LINEAR: *bytes = gather_ws(nullptr, rows, d, n).bytes; break;
     case QS_OP_SPARSE_LINEAR_BACKWARD: *bytes = ((size_t)rows * (size_t)d * 2 + 255) & ~size_t(255); break;
+    case QS_OP_BLOCK_SPARSE_LINEAR: *bytes = qs::nm24_packed_bytes(rows, d); break;
     default: return fail(QS_ERR_INVALID_ARG, "qs_workspace_bytes: unknown op %d", (int)op);
     }
     return ok();
@@ -549,6 +550,36 @@ qs_status qs_sparse_linear_backward(const void* x, qs_dtype xt, int64_t rows, in
         e = qs::launch_gemm_bf16(g, st);
         if (e != hipSuccess) return hip_fail(e, fn);
     }
+    return ok();
+}
+
+qs_status qs_block_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_in,
+                                 const void* w, qs_dtype wt_t, int64_t n_out, void* y,
+                                 qs_dtype yt, uint8_t* mask, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    const char* fn = "qs_block_sparse_linear";
+    if (rows < 0 || d_in <= 0 || n_out <= 0) return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
+    if (xt != QS_BF16 || wt_t != QS_BF16)
+        return fail(QS_ERR_UNSUPPORTED, "%s: x and w must be QS_BF16", fn);
+    if (!valid_float_dtype(yt)) return fail(QS_ERR_UNSUPPORTED, "%s: y must be QS_F32 or QS_BF16", fn);
+    if (d_in % 32 != 0 || n_out % 8 != 0)
+        return fail(QS_ERR_UNSUPPORTED, "%s: need d_in %% 32 == 0 and n_out %% 8 == 0", fn);
+    const int64_t lim = int64_t(1) << 30;
+    if (rows * d_in >= lim || n_out * d_in >= lim || rows * n_out >= (int64_t(1) << 31))
+        return fail(QS_ERR_UNSUPPORTED, "%s: x and w must hold fewer than 2^30 elements", fn);
+    if (rows == 0) return ok();
+    if (!x || !w || !y) return fail(QS_ERR_INVALID_ARG, "%s: x, w and y must be non-NULL", fn);
+    const void* ptrs[] = {x, w, y, mask, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(QS_ERR_UNSUPPORTED, "%s: pointer not 16-byte aligned", fn);
+    const size_t need = qs::nm24_packed_bytes(rows, d_in);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(QS_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+    qs::BlockSparseArgs a{};
+    a.x = (const uint16_t*)x; a.rows = rows; a.d = d_in; a.n = n_out;
+    a.w = (const uint16_t*)w; a.y = y; a.y_bf16 = yt == QS_BF16; a.mask = mask; a.ws = ws;
+    hipError_t e = qs::launch_block_sparse_linear(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }
 

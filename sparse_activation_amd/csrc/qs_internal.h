@@ -126,6 +126,19 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream);
 
+// ---------------------------------------------------------------- Block Q-Sparse (2:4)
+struct BlockSparseArgs {
+    const uint16_t* x;       // bf16 [rows, d], d % 32 == 0
+    int64_t rows, d, n;
+    const uint16_t* w;       // bf16 W [n, d] (nn.Linear layout), n % 8 == 0
+    void* y;                 // [rows, n] fp32 or bf16
+    int y_bf16;
+    uint8_t* mask;           // [rows, d] or null
+    void* ws;                // nm24_packed_bytes(rows, d) bytes: the packed 2:4 operand
+};
+size_t nm24_packed_bytes(int64_t rows, int64_t d);
+hipError_t launch_block_sparse_linear(const BlockSparseArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- dReLU gate/up
 struct DreluArgs {
     const uint16_t* x;       // bf16 [rows, d] (already masked if k_in < d)

@@ -194,3 +194,25 @@ def test_backward_validation_and_workspace():
     assert call() == 3                               # dw without workspace
     assert call(ws=FAKE, wsb=need - 1) == 3
     assert call(dx=None, dw=None) == 0               # nothing asked: no-op
+
+
+def test_block_sparse_validation_and_workspace():
+    lib = qs.load()
+    need = qs.qs_workspace_bytes(qs.OP_BLOCK_SPARSE_LINEAR, 5, 96, 64)
+    # packed values: 2 slices x 5 rows x 64 B; positions: 2 slices x 3 chunks of 16 B
+    assert need == ((2 * 5 * 64 + 255) // 256) * 256 + ((2 * 3 * 16 + 255) // 256) * 256
+
+    def call(x=FAKE, xt=qs.BF16, rows=4, d=1024, w=FAKE, wt=qs.BF16, n=512, y=FAKE, yt=qs.F32,
+             mask=None, ws=FAKE, wsb=None):
+        wsb = qs.qs_workspace_bytes(qs.OP_BLOCK_SPARSE_LINEAR, rows, d, n) if wsb is None else wsb
+        return lib.qs_block_sparse_linear(x, xt, rows, d, w, wt, n, y, yt, mask, ws, wsb, None)
+    assert call(xt=qs.F32) == 2
+    assert call(wt=qs.F32) == 2
+    assert call(yt=qs.I8) == 2
+    assert call(d=1000) == 2                          # d_in % 32
+    assert call(n=500) == 2                           # n_out % 8
+    assert call(d=0, wsb=1 << 20) == 1
+    assert call(x=None) == 1
+    assert call(mask=MISALIGNED) == 2
+    assert call(wsb=16) == 3
+    assert call(rows=0) == 0
