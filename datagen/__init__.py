@@ -30,7 +30,7 @@ import numpy as np
 __all__ = [
     "bf16_round", "student_t", "normal", "k_from_fraction",
     "DRELU_BIAS", "c1_linear", "c2_relu2_ffn", "c3_i8t_linear",
-    "c4_prefill_qkv", "c5_drelu_ffn",
+    "c4_prefill_qkv", "c5_drelu_ffn", "c4_backward_grad", "MOE_BIAS", "c6_moe_drelu_ffn",
 ]
 
 # Shared gate/up bias of the dReLU workload: with g ~ N(0, s^2), s ~= 1.81
@@ -38,6 +38,9 @@ __all__ = [
 # about 90% of relu(g) * relu(u) is zero (Turbo Sparse, per-layer
 # zero-activation figure).
 DRELU_BIAS = -0.866
+# The same construction for the MoE experts' ~85% inactive neurons (Turbo
+# Sparse summary, per-expert figure): P(g + b > 0) ~= sqrt(0.15).
+MOE_BIAS = -0.518
 
 
 def bf16_round(a: np.ndarray) -> np.ndarray:
@@ -138,4 +141,29 @@ def c5_drelu_ffn(batch: int, rotation: int = 0, with_weights: bool = True,
         out["W_down"] = bf16_round(normal(g, (d, ffn), 0.02))
         out["b_gate"] = np.full(ffn, bias, dtype=np.float32)
         out["b_up"] = np.full(ffn, bias, dtype=np.float32)
+    return out
+
+
+def c6_moe_drelu_ffn(batch: int, rotation: int = 0, with_weights: bool = True, d: int = 4096,
+                     ffn: int = 14336, n_experts: int = 8, bias: float = MOE_BIAS) -> dict:
+    """Mixtral-47B-shaped dReLU MoE FFN decode in bf16: a router [E, d] and E
+    experts with W_gate, W_up [E, ffn, d] (neuron-major) and W_down^T [E, ffn, d]
+    (feature-major rows of the down projection), biases [E, ffn] = `bias`.
+    Expert e's matrices come from their own generator (seed 206 + e), drawn
+    in float32 to bound the host memory of the 8-expert layer."""
+    out = {"X": bf16_round(student_t(_x_rng(6, rotation), (batch, d)))}
+    if with_weights:
+        out["W_router"] = bf16_round(normal(np.random.default_rng(216), (n_experts, d), 0.02))
+        wg = np.empty((n_experts, ffn, d), dtype=np.float32)
+        wu = np.empty((n_experts, ffn, d), dtype=np.float32)
+        wd = np.empty((n_experts, ffn, d), dtype=np.float32)
+        for e in range(n_experts):
+            g = np.random.default_rng(206 + e)
+            for dst in (wg, wu, wd):
+                dst[e] = g.standard_normal((ffn, d), dtype=np.float32)
+                dst[e] *= np.float32(0.02)
+                dst[e] = bf16_round(dst[e])
+        out["W_gate"], out["W_up"], out["W_down_t"] = wg, wu, wd
+        out["b_gate"] = np.full((n_experts, ffn), bias, dtype=np.float32)
+        out["b_up"] = np.full((n_experts, ffn), bias, dtype=np.float32)
     return out

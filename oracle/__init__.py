@@ -33,4 +33,5 @@ from .qsparse import (  # noqa: F401
     magnitude, topk_select, block_topk_select, sparse_linear, relu2, relu2_glu, drelu, absmax_quant_i8,
     ternarize, unpack_ternary, i8t_linear, ffn_relu2, ffn_relu2_glu, ffn_drelu,
     ffn_relu2_down_from, ffn_drelu_down_from, ste_backward, sparse_linear_backward,
+    moe_route, moe_drelu_ffn,
 )

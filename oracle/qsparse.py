@@ -225,6 +225,83 @@ def ffn_drelu(x, w_gate, b_gate, w_up, b_up, w_down):
     return out
 
 
+def moe_route(x, w_router, top_k: int):
+    """Top-k expert routing of every token.
+
+    Turbo Sparse summary (per-layer zero-activation passage): the MoE model
+    activates 2 of its 8 experts per layer, and each expert FFN keeps only
+    ~15% of its neurons active after dReLU.  The routing rule is not on the
+    pages; the reading taken is the usual one for that model family:
+    logits = x . W_router^T, keep the top_k logits of each token (ties to the
+    lower expert index, the same rule as the activation top-K), and weight
+    the chosen experts by a softmax over the kept logits only.
+
+    Returns (logits f64 [R, E], experts i32 [R, top_k] ascending,
+    weights f64 [R, top_k] matching experts, T_logits scale).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    wr = np.asarray(w_router, dtype=np.float64)
+    logits = x @ wr.T
+    t_logits = np.abs(x) @ np.abs(wr).T
+    rows, e = logits.shape
+    if not 1 <= top_k <= e:
+        raise ValueError("need 1 <= top_k <= n_experts")
+    experts = np.zeros((rows, top_k), dtype=np.int32)
+    weights = np.zeros((rows, top_k))
+    for r in range(rows):
+        order = np.lexsort((np.arange(e), -logits[r]))
+        sel = np.sort(order[:top_k])
+        z = logits[r, sel] - logits[r, sel].max()
+        p = np.exp(z)
+        experts[r] = sel
+        weights[r] = p / p.sum()
+    return logits, experts, weights, t_logits
+
+
+def moe_drelu_ffn(x, w_router, top_k, w_gate, b_gate, w_up, b_up, w_down, experts=None,
+                  weights=None):
+    """Mixture-of-experts dReLU FFN: y = sum over the token's chosen experts e
+    of weight_e * FFN_e(x), FFN_e the dReLU FFN of expert e (ffn_drelu, whose
+    down projection gathers only the nonzero neurons).
+
+    Turbo Sparse summary: 2 of 8 experts per layer and ~85% of each expert's
+    neurons inactive, so ~3% of the layer's parameters are used per token.
+    Expert weights are stacked: w_gate, w_up [E, ffn, d], w_down [E, d, ffn]
+    (nn.Linear layout of the down projection, as ffn_drelu takes it), biases
+    [E, ffn] or None.  `experts`/`weights` override the routing (stage-wise
+    checks feed the routing a device produced).  Returns the routing, every
+    pair's hidden h [R, top_k, ffn] and down output, y and its scale T_y
+    (sum of weight * T_y over the pairs).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    logits, ex, wts, t_logits = moe_route(x, w_router, top_k)
+    if experts is not None:
+        ex = np.asarray(experts, dtype=np.int32)
+        wts = np.asarray(weights, dtype=np.float64)
+    rows = x.shape[0]
+    d = x.shape[1]
+    ffn = np.asarray(w_gate[0]).shape[0]
+    h = np.zeros((rows, top_k, ffn))
+    g = np.zeros((rows, top_k, ffn))
+    u = np.zeros((rows, top_k, ffn))
+    t_g = np.zeros((rows, top_k, ffn))
+    t_u = np.zeros((rows, top_k, ffn))
+    y_pair = np.zeros((rows, top_k, d))
+    t_pair = np.zeros((rows, top_k, d))
+    for r in range(rows):
+        for j in range(top_k):
+            e = int(ex[r, j])
+            out = ffn_drelu(x[r:r + 1], w_gate[e], None if b_gate is None else b_gate[e],
+                            w_up[e], None if b_up is None else b_up[e], w_down[e])
+            h[r, j], g[r, j], u[r, j] = out["h"][0], out["g"][0], out["u"][0]
+            t_g[r, j], t_u[r, j] = out["T_g"][0], out["T_u"][0]
+            y_pair[r, j], t_pair[r, j] = out["y"][0], out["T_y"][0]
+    y = np.einsum("rj,rjd->rd", wts, y_pair)
+    t_y = np.einsum("rj,rjd->rd", np.abs(wts), t_pair)
+    return dict(logits=logits, T_logits=t_logits, experts=ex, weights=wts, g=g, u=u,
+                T_g=t_g, T_u=t_u, h=h, y_pair=y_pair, T_pair=t_pair, y=y, T_y=t_y)
+
+
 def ffn_drelu_down_from(h, w_down):
     """Nonzero lists of h and the gathered down projection."""
     h = np.asarray(h, dtype=np.float64)
