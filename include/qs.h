@@ -18,7 +18,9 @@
  *   [TS-Eq3-4]  Turbo Sparse summary, Eq. 3-4: top-k% of the FFN
  *               intermediate by absolute value before W_down.
  *   [TS-Fig]    Turbo Sparse summary, per-layer zero-activation figure
- *               (about 90% of FFN neurons inactive).
+ *               (about 90% of FFN neurons inactive) and its passage on the
+ *               MoE model (2 of 8 experts per layer, ~85% of each expert's
+ *               neurons inactive, ~3% of the layer's parameters per token).
  *   [QS-STE]    Q-Sparse news article, the back-propagation passage of the
  *               Top-K section: the gradient is computed with respect to the
  *               sparsified tensor and passed unchanged to the tensor before
@@ -108,7 +110,8 @@ typedef enum qs_op {
     QS_OP_GATHER_LINEAR = 5,
     QS_OP_SPARSE_FFN_RELU2_GLU = 6,
     QS_OP_SPARSE_LINEAR_BACKWARD = 7,
-    QS_OP_BLOCK_SPARSE_LINEAR = 8
+    QS_OP_BLOCK_SPARSE_LINEAR = 8,
+    QS_OP_SPARSE_MOE_FFN = 9     /* rows = tokens * top_k (the (token, expert) pairs) */
 } qs_op;
 
 /*
@@ -299,6 +302,41 @@ qs_status qs_block_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64
                                  const void* w, qs_dtype wt_t, int64_t n_out, void* y,
                                  qs_dtype yt, uint8_t* mask, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/*
+ * qs_sparse_moe_ffn -- mixture-of-experts dReLU FFN for decode  [TS-Fig],
+ * [TS-Eq2]
+ *
+ *   Routing (a reading: the pages give no rule): logits = x . W_router^T
+ *   (fp32 sums), the top_k logits of each token (ties to the lower expert
+ *   index), weights = softmax over the kept logits.  Each chosen expert e
+ *   runs the dReLU FFN of qs_sparse_ffn (QS_ACT_DRELU, k_mid < 0): the gate
+ *   row of every neuron, the up row only where the gate is positive, the down
+ *   projection gathering only the rows of W_down^T where h != 0.  Then
+ *   y = sum over the chosen experts of weight_e * y_e (in ascending expert
+ *   order).
+ *
+ *   x          device bf16 [rows, d]; d % 8 == 0, d <= 8192.
+ *   w_router   device bf16 [n_experts, d]; 1 <= top_k <= n_experts <= 64.
+ *   w_gate     device bf16 [n_experts, ffn, d] (neuron-major per expert).
+ *   w_up       device bf16 [n_experts, ffn, d].
+ *   w_down_t   device bf16 [n_experts, ffn, d] (W_down^T of each expert).
+ *   b_gate, b_up  device fp32 [n_experts, ffn] or NULL.
+ *   y          device [rows, d], dtype yt (QS_F32 or QS_BF16).
+ *   router_logits  device fp32 [rows, n_experts] or NULL.
+ *   experts    device i32 [rows, top_k] or NULL: the chosen experts, ascending.
+ *   expert_weights device fp32 [rows, top_k] or NULL: their weights.
+ *   h          device fp32 [rows, top_k, ffn] or NULL: each pair's dReLU output.
+ *   Arithmetic: fp32 sums of exact bf16 products; fp32 h; ffn % 8 == 0; an
+ *   expert matrix < 1 GiB.
+ *   Workspace: qs_workspace_bytes(QS_OP_SPARSE_MOE_FFN, rows * top_k, d, ffn).
+ */
+qs_status qs_sparse_moe_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int64_t ffn,
+                            int64_t n_experts, int64_t top_k, const void* w_router,
+                            const void* w_gate, const void* w_up, const void* w_down_t,
+                            const float* b_gate, const float* b_up, void* y, qs_dtype yt,
+                            float* router_logits, int32_t* experts, float* expert_weights,
+                            float* h, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * qs_workspace_bytes -- device workspace needed by `op` at this shape.

@@ -20,7 +20,7 @@ __all__ = [
     "OP_TOPK_MASK", "OP_SPARSE_LINEAR", "OP_SPARSE_LINEAR_I8T", "OP_SPARSE_FFN_RELU2",
     "OP_SPARSE_FFN_DRELU", "OP_GATHER_LINEAR", "OP_SPARSE_FFN_RELU2_GLU",
     "OP_SPARSE_LINEAR_BACKWARD", "qs_sparse_linear_backward", "OP_BLOCK_SPARSE_LINEAR",
-    "qs_block_sparse_linear",
+    "qs_block_sparse_linear", "OP_SPARSE_MOE_FFN", "qs_sparse_moe_ffn",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +31,7 @@ LAYOUT_WT, LAYOUT_W = 0, 1
 ACT_RELU2, ACT_DRELU, ACT_RELU2_GLU = 0, 1, 2
 (OP_TOPK_MASK, OP_SPARSE_LINEAR, OP_SPARSE_LINEAR_I8T, OP_SPARSE_FFN_RELU2,
  OP_SPARSE_FFN_DRELU, OP_GATHER_LINEAR, OP_SPARSE_FFN_RELU2_GLU,
- OP_SPARSE_LINEAR_BACKWARD, OP_BLOCK_SPARSE_LINEAR) = range(9)
+ OP_SPARSE_LINEAR_BACKWARD, OP_BLOCK_SPARSE_LINEAR, OP_SPARSE_MOE_FFN) = range(10)
 
 # Every function the header declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -46,6 +46,8 @@ _SIGS = {
                                   _P, _INT, _P, _INT, _P, ctypes.c_size_t, _P],
     "qs_block_sparse_linear": [_P, _INT, _I64, _I64, _P, _INT, _I64, _P, _INT, _P, _P,
                                ctypes.c_size_t, _P],
+    "qs_sparse_moe_ffn": [_P, _INT, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
+                          _INT, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "qs_sparse_linear_i8t": [_P, _I64, _I64, _I64, _P, ctypes.c_float, _I64, _P, _P, _P, _P,
                              _P, _P, ctypes.c_size_t, _P],
     "qs_sparse_ffn": [_P, _INT, _I64, _I64, _I64, _INT, _I64, _I64, _P, _P, _P, _P, _P, _P,
@@ -293,6 +295,38 @@ def qs_block_sparse_linear(x, w, y=None, y_dtype=None, want_mask=False, mask=Non
                                          _dtype_code(w), n_out, _ptr(y), _dtype_code(y),
                                          _ptr(mask), _ptr(ws), ws_bytes, _stream(dev)))
     return y, mask
+
+
+def qs_sparse_moe_ffn(x, top_k: int, w_router, w_gate, w_up, w_down_t, b_gate=None, b_up=None,
+                      y=None, y_dtype=None, want_all=False, ws=None):
+    """Mixture-of-experts dReLU FFN (decode).  Weights are stacked per expert:
+    w_router [E, d], w_gate / w_up / w_down_t [E, ffn, d], biases [E, ffn].
+    Returns y, or with want_all (y, logits, experts, weights, h)."""
+    torch = _torch()
+    rows, d = x.shape
+    n_exp, ffn = w_gate.shape[0], w_gate.shape[1]
+    for t in (w_up, w_down_t):
+        if tuple(t.shape) != (n_exp, ffn, d):
+            raise ValueError("expert weights must all be [E, ffn, d]")
+    if tuple(w_router.shape) != (n_exp, d):
+        raise ValueError("w_router must be [E, d]")
+    dev = _dev(x, w_router, w_gate, w_up, w_down_t, b_gate, b_up, y, ws)
+    if y is None:
+        y = torch.empty((rows, d), dtype=y_dtype or torch.float32, device=dev)
+    logits = experts = weights = h = None
+    if want_all:
+        logits = torch.empty((rows, n_exp), dtype=torch.float32, device=dev)
+        experts = torch.empty((rows, top_k), dtype=torch.int32, device=dev)
+        weights = torch.empty((rows, top_k), dtype=torch.float32, device=dev)
+        h = torch.empty((rows, top_k, ffn), dtype=torch.float32, device=dev)
+    ws, ws_bytes = _workspace(ws, OP_SPARSE_MOE_FFN, rows * top_k, d, ffn, dev)
+    _check(load().qs_sparse_moe_ffn(
+        _ptr(x), _dtype_code(x), rows, d, ffn, n_exp, top_k, _ptr(w_router), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down_t), _ptr(b_gate), _ptr(b_up), _ptr(y), _dtype_code(y),
+        _ptr(logits), _ptr(experts), _ptr(weights), _ptr(h), _ptr(ws), ws_bytes, _stream(dev)))
+    if want_all:
+        return y, logits, experts, weights, h
+    return y
 
 
 def qs_sparse_linear_i8t(x, k: int, wt_packed, alpha: float, n_out: int, acc=None, y=None,

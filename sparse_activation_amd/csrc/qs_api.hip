@@ -155,6 +155,36 @@ FfnWs ffn_ws(char* base, int64_t rows, int64_t d, int64_t ffn, bool drelu) {
 
 bool valid_float_dtype(qs_dtype t) { return t == QS_F32 || t == QS_BF16; }
 
+// MoE FFN workspace for `pairs` = rows * top_k (token, expert) pairs.
+struct MoeWs {
+    int32_t* ctr;
+    int n_ctr;
+    int32_t* pair_token;
+    int32_t* pair_expert;
+    float* pair_weight;
+    float* h;
+    float* ypair;
+    float* partial;
+    size_t bytes;
+};
+
+MoeWs moe_ws(char* base, int64_t pairs, int64_t d, int64_t ffn) {
+    qs::GemvPlan p = qs::plan_gemv(pairs, ffn, d, 1, 1);
+    Carve c;
+    c.base = base;
+    MoeWs w{};
+    w.n_ctr = p.n_counters;
+    w.ctr = (int32_t*)c.take(sizeof(int32_t) * (size_t)p.n_counters);
+    w.pair_token = (int32_t*)c.take(sizeof(int32_t) * (size_t)pairs);
+    w.pair_expert = (int32_t*)c.take(sizeof(int32_t) * (size_t)pairs);
+    w.pair_weight = (float*)c.take(sizeof(float) * (size_t)pairs);
+    w.h = (float*)c.take(sizeof(float) * (size_t)pairs * ffn);
+    w.ypair = (float*)c.take(sizeof(float) * (size_t)pairs * d);
+    w.partial = (float*)c.take(sizeof(float) * p.scratch_floats);
+    w.bytes = c.off;
+    return w;
+}
+
 }  // namespace
 
 qs_status qs::set_error(qs_status st, const char* msg) {
@@ -181,6 +211,7 @@ qs_status qs_workspace_bytes(qs_op op, int64_t rows, int64_t d, int64_t n, size_
     case QS_OP_GATHER_LINEAR: *bytes = gather_ws(nullptr, rows, d, n).bytes; break;
     case QS_OP_SPARSE_LINEAR_BACKWARD: *bytes = ((size_t)rows * (size_t)d * 2 + 255) & ~size_t(255); break;
     case QS_OP_BLOCK_SPARSE_LINEAR: *bytes = qs::nm24_packed_bytes(rows, d); break;
+    case QS_OP_SPARSE_MOE_FFN: *bytes = moe_ws(nullptr, rows, d, n).bytes; break;
     default: return fail(QS_ERR_INVALID_ARG, "qs_workspace_bytes: unknown op %d", (int)op);
     }
     return ok();
@@ -579,6 +610,72 @@ qs_status qs_block_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64
     a.x = (const uint16_t*)x; a.rows = rows; a.d = d_in; a.n = n_out;
     a.w = (const uint16_t*)w; a.y = y; a.y_bf16 = yt == QS_BF16; a.mask = mask; a.ws = ws;
     hipError_t e = qs::launch_block_sparse_linear(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
+qs_status qs_sparse_moe_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int64_t ffn,
+                            int64_t n_experts, int64_t top_k, const void* w_router,
+                            const void* w_gate, const void* w_up, const void* w_down_t,
+                            const float* b_gate, const float* b_up, void* y, qs_dtype yt,
+                            float* router_logits, int32_t* experts, float* expert_weights,
+                            float* h, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "qs_sparse_moe_ffn";
+    if (rows < 0 || d <= 0 || ffn <= 0) return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
+    if (n_experts < 1 || top_k < 1 || top_k > n_experts)
+        return fail(QS_ERR_INVALID_ARG, "%s: need 1 <= top_k <= n_experts", fn);
+    if (n_experts > 64) return fail(QS_ERR_UNSUPPORTED, "%s: at most 64 experts", fn);
+    if (dt != QS_BF16) return fail(QS_ERR_UNSUPPORTED, "%s: x and the weights must be QS_BF16", fn);
+    if (!valid_float_dtype(yt)) return fail(QS_ERR_UNSUPPORTED, "%s: y must be QS_F32 or QS_BF16", fn);
+    if (d % 8 != 0 || ffn % 8 != 0 || d > 8192)
+        return fail(QS_ERR_UNSUPPORTED, "%s: need d %% 8 == 0, ffn %% 8 == 0 and d <= 8192", fn);
+    if (ffn * d * 2 >= qs::kMaxGatherWeightBytes)
+        return fail(QS_ERR_UNSUPPORTED, "%s: an expert matrix must be smaller than 1 GiB", fn);
+    if (rows * top_k > 0x7FFFFFFF) return fail(QS_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    if (rows == 0) return ok();
+    if (!x || !w_router || !w_gate || !w_up || !w_down_t || !y)
+        return fail(QS_ERR_INVALID_ARG, "%s: x, the weights and y must be non-NULL", fn);
+    const void* ptrs[] = {x, w_router, w_gate, w_up, w_down_t, b_gate, b_up, y, router_logits,
+                          experts, expert_weights, h, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(QS_ERR_UNSUPPORTED, "%s: pointer not 16-byte aligned", fn);
+    const int64_t pairs = rows * top_k;
+    MoeWs need = moe_ws(nullptr, pairs, d, ffn);
+    if (ws == nullptr || ws_bytes < need.bytes)
+        return fail(QS_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need.bytes);
+    MoeWs wsp = moe_ws((char*)ws, pairs, d, ffn);
+    hipStream_t st = (hipStream_t)stream;
+
+    // Router: (token, expert, weight) pairs.
+    qs::MoeRouteArgs r{};
+    r.x = (const uint16_t*)x; r.wr = (const uint16_t*)w_router; r.rows = rows; r.d = d;
+    r.n_experts = (int)n_experts; r.top_k = (int)top_k;
+    r.pair_token = wsp.pair_token; r.pair_expert = wsp.pair_expert; r.pair_weight = wsp.pair_weight;
+    r.logits = router_logits; r.out_experts = experts; r.out_weights = expert_weights;
+    hipError_t e = qs::launch_moe_route(r, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+
+    // Gate, then up only where the gate is positive, per pair (dReLU).
+    float* hbuf = h ? h : wsp.h;
+    qs::DreluArgs g{};
+    g.x = (const uint16_t*)x; g.rows = rows; g.d = d; g.ffn = ffn;
+    g.wg = (const uint16_t*)w_gate; g.wu = (const uint16_t*)w_up; g.bg = b_gate; g.bu = b_up;
+    g.h = hbuf; g.zero_ptr = wsp.ctr; g.n_zero = wsp.n_ctr;
+    g.pair_token = wsp.pair_token; g.pair_expert = wsp.pair_expert; g.pairs = pairs;
+    e = qs::launch_drelu_gate_up(g, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+
+    // Down: each pair gathers the rows of its expert's W_down^T where h != 0.
+    qs::GemvPlan pd = qs::plan_gemv(pairs, ffn, d, 1, 1);
+    qs::GemvArgs gd{};
+    gd.xs = hbuf; gd.rows = pairs; gd.d_in = ffn; gd.n_out = d; gd.w = w_down_t;
+    gd.partial = wsp.partial; gd.counters = wsp.ctr; gd.y = wsp.ypair; gd.y_bf16 = 0;
+    gd.epilogue = qs::EPI_STORE;
+    gd.row_expert = wsp.pair_expert; gd.expert_bytes = ffn * d * 2;
+    e = qs::launch_gemv(pd, 1, gd, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
+
+    e = qs::launch_moe_combine(wsp.ypair, wsp.pair_weight, rows, (int)top_k, d, y, yt == QS_BF16, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }

@@ -239,7 +239,10 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
     const int slot = wave * (64 / kFLPR) + lane / kFLPR;
     const int64_t col = (int64_t)tile * CT + (lane % kFLPR) * EPT;
     const uint32_t colb = col < n_out ? (uint32_t)(col * esize) : kOOB;
-    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, a.d_in * (int64_t)rowbytes);
+    const void* wbase = a.w;
+    if (BT == 1 && a.row_expert != nullptr)
+        wbase = reinterpret_cast<const char*>(a.w) + (int64_t)a.row_expert[tok0] * a.expert_bytes;
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(wbase, a.d_in * (int64_t)rowbytes);
 
     float acc[BT][EPT];
 #pragma unroll
@@ -1015,11 +1018,11 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
 
 }  // namespace
 
-GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16) {
+GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16, int max_bt) {
     GemvPlan p{};
     p.lpr = kLPR;
     p.ept = w_is_bf16 ? 8 : 4;
-    p.bt = pow2_tile(rows, 16);
+    p.bt = pow2_tile(rows, max_bt);
     // 16-token tiles run an MFMA kernel: bf16 weights in 64-column tiles on the
     // bf16 matrix cores, fp32 weights in 16 * EPT-column tiles on the fp32 ones.
     // With bf16 weights, 8 tokens also take the bf16 MFMA kernel (as a half-empty

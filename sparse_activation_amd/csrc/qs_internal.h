@@ -65,7 +65,9 @@ struct GemvPlan {
     size_t scratch_floats;  // workspace behind GemvArgs::partial: partials, then prep records
     int n_counters;         // n_tiles * n_tok_tiles
 };
-GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16);
+// max_bt caps the tokens per tile (1: every row its own tile, e.g. when rows
+// use different weight matrices, see GemvArgs::row_expert).
+GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16, int max_bt = 16);
 
 struct GemvArgs {
     const float* xs;       // [rows, d_in] fp32, zero where not selected
@@ -78,6 +80,8 @@ struct GemvArgs {
     int epilogue;          // EPI_STORE, EPI_RELU2 (y is fp32 h) or EPI_RELU2_GLU (y is fp32 h)
     const float* gate;     // EPI_RELU2_GLU: fp32 gate projection [rows, n_out]
     int xs_bf16;           // 1: every xs value is a bf16 number (from bf16 activations)
+    const int32_t* row_expert;  // null, or (one token per tile) row r reads the
+    int64_t expert_bytes;       //   matrix at w + row_expert[r] * expert_bytes
 };
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 
@@ -150,8 +154,32 @@ struct DreluArgs {
     float* h;                // [rows, ffn] fp32
     int32_t* zero_ptr;       // block 0 clears zero_ptr[0..n_zero) (split-K counters)
     int n_zero;
+    // Mixture of experts (null for a plain FFN; one-token kernel only): launch
+    // row r is the pair (token pair_token[r], expert pair_expert[r]); the
+    // expert's matrices start at wg / wu + expert * ffn * d, its biases at
+    // bg / bu + expert * ffn, and h row r is the pair's.
+    const int32_t* pair_token;
+    const int32_t* pair_expert;
+    int64_t pairs;
 };
 hipError_t launch_drelu_gate_up(const DreluArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- MoE routing and combine
+struct MoeRouteArgs {
+    const uint16_t* x;       // bf16 [rows, d]
+    const uint16_t* wr;      // bf16 router [n_experts, d]
+    int64_t rows, d;
+    int n_experts, top_k;    // n_experts <= 64
+    int32_t* pair_token;     // [rows * top_k]
+    int32_t* pair_expert;    // [rows * top_k], ascending within a token
+    float* pair_weight;      // [rows * top_k]
+    float* logits;           // [rows, n_experts] or null
+    int32_t* out_experts;    // [rows, top_k] or null: copy of pair_expert
+    float* out_weights;      // [rows, top_k] or null: copy of pair_weight
+};
+hipError_t launch_moe_route(const MoeRouteArgs& a, hipStream_t stream);
+hipError_t launch_moe_combine(const float* ypair, const float* pair_weight, int64_t rows,
+                              int top_k, int64_t d, void* y, int y_bf16, hipStream_t stream);
 
 // Nonzero compaction of h rows: idx[r, 0..cnt) ascending, cnt[r].
 hipError_t launch_nonzero_lists(const float* h, int64_t rows, int64_t n, int32_t* idx,

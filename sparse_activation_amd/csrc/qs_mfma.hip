@@ -591,14 +591,27 @@ __global__ __launch_bounds__(256) void drelu_gate_up_b1_kernel(DreluArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t d = a.d, ffn = a.ffn;
     const int64_t nb = ((int64_t)blockIdx.x * 4 + wave) * NPW;
-    if (blockIdx.x == 0 && a.zero_ptr != nullptr)
+    if (blockIdx.x == 0 && blockIdx.y == 0 && a.zero_ptr != nullptr)
         for (int i = tid; i < a.n_zero; i += 256) a.zero_ptr[i] = 0;
+    // Launch row blockIdx.y: the token itself, or a (token, expert) pair.
+    const int64_t pr = blockIdx.y;
+    int64_t tok = 0, ex = 0;
+    if (a.pair_expert != nullptr) {
+        tok = a.pair_token[pr];
+        ex = a.pair_expert[pr];
+    }
+    const uint16_t* xrow = a.x + tok * d;
+    const uint16_t* wgx = a.wg + ex * ffn * d;
+    const uint16_t* wux = a.wu + ex * ffn * d;
+    const float* bgx = a.bg != nullptr ? a.bg + ex * ffn : nullptr;
+    const float* bux = a.bu != nullptr ? a.bu + ex * ffn : nullptr;
+    float* hrow = a.h + pr * ffn;
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.x), (short)0, (int)(d * 2), 0x00020000);
+        const_cast<uint16_t*>(xrow), (short)0, (int)(d * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.wg), (short)0, (int)(ffn * d * 2), 0x00020000);
+        const_cast<uint16_t*>(wgx), (short)0, (int)(ffn * d * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.wu), (short)0, (int)(ffn * d * 2), 0x00020000);
+        const_cast<uint16_t*>(wux), (short)0, (int)(ffn * d * 2), 0x00020000);
     constexpr uint32_t kOff = 0x80000000u;
     u32x4 xv[NCH];
 #pragma unroll
@@ -621,7 +634,7 @@ __global__ __launch_bounds__(256) void drelu_gate_up_b1_kernel(DreluArgs a) {
         float s = 0.0f;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) s = dot8(wv[j][i], xv[i], s);
-        g[j] = wave_sum(s) + ((a.bg != nullptr && nb + j < ffn) ? a.bg[nb + j] : 0.0f);
+        g[j] = wave_sum(s) + ((bgx != nullptr && nb + j < ffn) ? bgx[nb + j] : 0.0f);
     }
     // Up rows only where the gate is positive (g is wavefront-uniform).
 #pragma unroll
@@ -636,10 +649,10 @@ __global__ __launch_bounds__(256) void drelu_gate_up_b1_kernel(DreluArgs a) {
             float s = 0.0f;
 #pragma unroll
             for (int i = 0; i < NCH; ++i) s = dot8(wv[j][i], xv[i], s);
-            const float uv = wave_sum(s) + ((a.bu != nullptr && nb + j < ffn) ? a.bu[nb + j] : 0.0f);
+            const float uv = wave_sum(s) + ((bux != nullptr && nb + j < ffn) ? bux[nb + j] : 0.0f);
             hv = uv > 0.0f ? __fmul_rn(g[j], uv) : 0.0f;
         }
-        if (lane == 0 && nb + j < ffn) a.h[nb + j] = hv;
+        if (lane == 0 && nb + j < ffn) hrow[nb + j] = hv;
     }
 }
 
@@ -732,12 +745,14 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream) {
 hipError_t launch_drelu_gate_up(const DreluArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     const unsigned blocks = (unsigned)((a.ffn + 15) / 16);
-    if (a.rows == 1 && a.d <= 8192) {   // two neurons per wavefront, eight per workgroup
+    const bool moe = a.pair_expert != nullptr;
+    if (moe && a.d > 8192) return hipErrorInvalidValue;
+    if ((a.rows == 1 || moe) && a.d <= 8192) {   // two neurons per wavefront, eight per workgroup
         const int nch = (int)((a.d + 511) / 512);
-        const unsigned b2 = (unsigned)((a.ffn + 7) / 8);
-        if (nch <= 4) drelu_gate_up_b1_kernel<4, 2><<<dim3(b2), dim3(256), 0, stream>>>(a);
-        else if (nch <= 8) drelu_gate_up_b1_kernel<8, 2><<<dim3(b2), dim3(256), 0, stream>>>(a);
-        else drelu_gate_up_b1_kernel<16, 2><<<dim3(b2), dim3(256), 0, stream>>>(a);
+        const dim3 g2((unsigned)((a.ffn + 7) / 8), moe ? (unsigned)a.pairs : 1u);
+        if (nch <= 4) drelu_gate_up_b1_kernel<4, 2><<<g2, dim3(256), 0, stream>>>(a);
+        else if (nch <= 8) drelu_gate_up_b1_kernel<8, 2><<<g2, dim3(256), 0, stream>>>(a);
+        else drelu_gate_up_b1_kernel<16, 2><<<g2, dim3(256), 0, stream>>>(a);
         return hipGetLastError();
     }
     drelu_gate_up_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(a);

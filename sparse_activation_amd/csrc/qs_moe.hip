@@ -1,0 +1,146 @@
+// Mixture-of-experts routing and combine for the dReLU MoE FFN.
+//
+// Turbo Sparse summary (blog.csdn.net), per-layer zero-activation passage:
+// the MoE model activates 2 of its 8 experts per layer and, with dReLU, only
+// ~15% of each expert's neurons, so ~3% of the layer's parameters are used
+// per token.  The routing rule is not on the pages; the reading taken is the
+// usual one for that model family: logits = x . W_router^T, the top_k logits
+// of each token (ties to the lower expert index), softmax over the kept
+// logits only.  The experts themselves run through the dReLU kernels with a
+// (token, expert) pair per launch row; this file holds the router and the
+// weighted sum of the pairs' outputs.
+#include "qs_internal.h"
+
+namespace qs {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Sum over the 64 lanes of a wavefront (fixed butterfly order).
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t b = __float_as_uint(f);
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return (uint16_t)(b >> 16);
+}
+
+// One workgroup (4 wavefronts) per token.  Wavefront w computes the logits of
+// experts w, w + 4, ...: each lane sums the products of its 8-feature runs
+// (features 512 i + 8 lane ..) in order, then the wavefront adds the lanes.
+// Wavefront 0 then selects and weights the experts.
+__global__ __launch_bounds__(256) void moe_route_kernel(MoeRouteArgs a) {
+    __shared__ float s_logit[64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t t = blockIdx.x, d = a.d;
+    const int E = a.n_experts, K = a.top_k;
+    const u32x4* xr = reinterpret_cast<const u32x4*>(a.x + t * d);
+    for (int e = wave; e < E; e += 4) {
+        const u32x4* wr = reinterpret_cast<const u32x4*>(a.wr + (int64_t)e * d);
+        float s = 0.0f;
+        for (int64_t k = 8 * lane; k < d; k += 512) {
+            const u32x4 xv = xr[k / 8], wv = wr[k / 8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                s = __fmaf_rn(bf16_lo(xv[q]), bf16_lo(wv[q]), s);
+                s = __fmaf_rn(bf16_hi(xv[q]), bf16_hi(wv[q]), s);
+            }
+        }
+        s = wave_sum64(s);
+        if (lane == 0) s_logit[e] = s;
+    }
+    __syncthreads();
+    if (tid != 0) return;
+    if (a.logits != nullptr)
+        for (int e = 0; e < E; ++e) a.logits[t * E + e] = s_logit[e];
+    // top_k largest logits, ties to the lower index; then ascending order.
+    uint64_t taken = 0;
+    int sel[64];
+    for (int j = 0; j < K; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+            if (taken >> e & 1) continue;
+            if (best < 0 || s_logit[e] > s_logit[best]) best = e;
+        }
+        taken |= uint64_t(1) << best;
+        sel[j] = best;
+    }
+    int n = 0;
+    for (int e = 0; e < E; ++e)
+        if (taken >> e & 1) sel[n++] = e;
+    float m = s_logit[sel[0]];
+    for (int j = 1; j < K; ++j) m = fmaxf(m, s_logit[sel[j]]);
+    float p[64], sum = 0.0f;
+    for (int j = 0; j < K; ++j) {
+        p[j] = expf(s_logit[sel[j]] - m);
+        sum += p[j];
+    }
+    for (int j = 0; j < K; ++j) {
+        const int64_t q = t * K + j;
+        const float wq = p[j] / sum;
+        a.pair_token[q] = (int32_t)t;
+        a.pair_expert[q] = sel[j];
+        a.pair_weight[q] = wq;
+        if (a.out_experts != nullptr) a.out_experts[q] = sel[j];
+        if (a.out_weights != nullptr) a.out_weights[q] = wq;
+    }
+}
+
+// y[t, c] = sum over j < top_k of weight[t, j] * ypair[t * top_k + j, c], in
+// j order; four columns per thread.
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ ypair,
+                                                          const float* __restrict__ w,
+                                                          int64_t rows, int top_k, int64_t d,
+                                                          void* __restrict__ y, int y_bf16) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per = d / 4;
+    if (i >= rows * per) return;
+    const int64_t t = i / per, c = (i % per) * 4;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < top_k; ++j) {
+        const float wj = w[t * top_k + j];
+        const float4 v = *reinterpret_cast<const float4*>(ypair + (t * top_k + j) * d + c);
+        acc[0] = __fmaf_rn(wj, v.x, acc[0]);
+        acc[1] = __fmaf_rn(wj, v.y, acc[1]);
+        acc[2] = __fmaf_rn(wj, v.z, acc[2]);
+        acc[3] = __fmaf_rn(wj, v.w, acc[3]);
+    }
+    if (y_bf16) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(y) + t * d + c;
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+        *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+    } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + t * d + c) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_moe_route(const MoeRouteArgs& a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    if (a.n_experts < 1 || a.n_experts > 64 || a.top_k < 1 || a.top_k > a.n_experts || a.d % 8 != 0)
+        return hipErrorInvalidValue;
+    moe_route_kernel<<<dim3((unsigned)a.rows), dim3(256), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_combine(const float* ypair, const float* pair_weight, int64_t rows,
+                              int top_k, int64_t d, void* y, int y_bf16, hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    if (d % 4 != 0) return hipErrorInvalidValue;
+    const int64_t n = rows * (d / 4);
+    moe_combine_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(
+        ypair, pair_weight, rows, top_k, d, y, y_bf16);
+    return hipGetLastError();
+}
+
+}  // namespace qs

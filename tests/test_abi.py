@@ -216,3 +216,24 @@ def test_block_sparse_validation_and_workspace():
     assert call(mask=MISALIGNED) == 2
     assert call(wsb=16) == 3
     assert call(rows=0) == 0
+
+
+def test_moe_validation_and_workspace():
+    lib = qs.load()
+    need = qs.qs_workspace_bytes(qs.OP_SPARSE_MOE_FFN, 2, 256, 512)
+    assert need > 2 * 512 * 4 + 2 * 256 * 4
+
+    def call(x=FAKE, dt=qs.BF16, rows=1, d=256, ffn=512, e=8, k=2, wr=FAKE, wg=FAKE, wu=FAKE,
+             wd=FAKE, y=FAKE, yt=qs.F32, ws=FAKE, wsb=None):
+        wsb = need if wsb is None else wsb
+        return lib.qs_sparse_moe_ffn(x, dt, rows, d, ffn, e, k, wr, wg, wu, wd, None, None, y, yt,
+                                     None, None, None, None, ws, wsb, None)
+    assert call(k=9) == 1                            # top_k > n_experts
+    assert call(k=0) == 1
+    assert call(e=65, k=2) == 2                      # at most 64 experts
+    assert call(dt=qs.F32) == 2
+    assert call(d=8200) == 2                         # d <= 8192
+    assert call(ffn=500) == 2                        # ffn % 8
+    assert call(wr=None) == 1
+    assert call(wsb=need - 1) == 3
+    assert call(rows=0) == 0
