@@ -13,7 +13,8 @@ same Llama-7B FFN with a gate: gated squared ReLU), c3
 (int8 x ternary 4096x4096 linear), c4 (fused-QKV prefill through the MFMA
 path, 2048 tokens), c4b (the same projection's training backward with the
 straight-through estimator: dX and dW), c4s (the same prefill under Block
-Q-Sparse 2:4 on the sparse matrix cores), c5 (Mistral-7B dReLU FFN decode).
+Q-Sparse 2:4 on the sparse matrix cores), c5 (Mistral-7B dReLU FFN decode),
+c6 (Mixtral-47B-shaped dReLU MoE FFN decode: 8 experts, top-2).
 
 Measurement:
   * inputs are resident in HBM before timing; weight copies rotate so that
@@ -58,7 +59,7 @@ def parse_args():
     p.add_argument("--steps", type=int, default=480)
     p.add_argument("--warmup", type=int, default=48)
     p.add_argument("--batch", type=int, default=1)
-    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c2g", "c3", "c4", "c4b", "c4s", "c5"])
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c2g", "c3", "c4", "c4b", "c4s", "c5", "c6"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--roofline-launches", type=int, default=96)
@@ -347,6 +348,76 @@ def run_c4(args, torch, np, qs, datagen, dev, stream):
     }
 
 
+def run_c6(args, torch, np, qs, datagen, dev, stream):
+    B = args.batch
+    log(f"workload c6: Mixtral-47B-shaped dReLU MoE FFN decode B={B}; generating weights")
+    c = datagen.c6_moe_drelu_ffn(B)
+    n_exp, ffn, d = c["W_gate"].shape
+    top_k = 2
+    bf = torch.bfloat16
+    wr = bf16_dev(torch, np, c["W_router"], dev)
+    mats = {}
+    for name in ("W_gate", "W_up", "W_down_t"):      # expert by expert: bounded host copies
+        t = torch.empty((n_exp, ffn, d), dtype=bf, device=dev)
+        for e in range(n_exp):
+            t[e] = torch.from_numpy(c[name][e]).to(dev).to(bf)
+        mats[name] = t
+        c[name] = None
+    bg = torch.from_numpy(c["b_gate"]).to(dev)
+    bu = torch.from_numpy(c["b_up"]).to(dev)
+    xs = [bf16_dev(torch, np, datagen.c6_moe_drelu_ffn(B, rotation=i, with_weights=False)["X"], dev)
+          for i in range(8)]
+    y = torch.empty((B, d), dtype=bf, device=dev)
+    ws = torch.empty(qs.qs_workspace_bytes(qs.OP_SPARSE_MOE_FFN, B * top_k, d, ffn),
+                     dtype=torch.uint8, device=dev)
+
+    # Algorithmic bytes of each input batch (bookkeeping outside the timed
+    # region): per expert the batch uses, its whole gate matrix, the up rows
+    # whose gate is positive for a token routed to it, the down rows where h is
+    # nonzero for such a token; plus the router, x and y.
+    step_bytes, up_frac, down_frac = [], [], []
+    for i in range(8):
+        _, _, ex, _, h = qs.qs_sparse_moe_ffn(xs[i], top_k, wr, mats["W_gate"], mats["W_up"],
+                                              mats["W_down_t"], bg, bu, want_all=True)
+        rows_read = 0
+        for e in sorted(set(ex.flatten().tolist())):
+            sel = ex == e                                  # [B, top_k]
+            toks = sel.any(dim=1).nonzero().flatten()
+            g = xs[i][toks].float() @ mats["W_gate"][e].float().t() + bg[e]
+            up = int((g > 0).any(dim=0).sum())
+            down = int((h[sel] != 0).any(dim=0).sum())
+            rows_read += ffn + up + down
+            up_frac.append(up / ffn)
+            down_frac.append(down / ffn)
+        step_bytes.append(rows_read * d * 2 + n_exp * d * 2 + 2 * B * d * 2)
+    torch.cuda.synchronize()
+
+    def step(i):
+        qs.qs_sparse_moe_ffn(xs[i % 8], top_k, wr, mats["W_gate"], mats["W_up"], mats["W_down_t"],
+                             bg, bu, y=y, ws=ws)
+
+    ms_step = time_graph(torch, stream, step, args.steps, args.warmup) / args.steps
+    alg = float(np.mean(step_bytes))
+    achieved = alg / (ms_step * 1e-3) / 1e9
+    log(f"c6: {ms_step * 1e3:.2f} us/step, {B / (ms_step * 1e-3):.0f} tokens/s, "
+        f"{achieved:.0f} GB/s on {alg / 1e6:.1f} MB; up rows {np.mean(up_frac):.3f}, "
+        f"down rows {np.mean(down_frac):.3f} of each used expert")
+    return {
+        "metric": "dReLU MoE FFN tokens/s at Mixtral-47B decode (8 experts, top-2), 1 GPU",
+        "unit": "tokens/s", "value": round(B / (ms_step * 1e-3), 1),
+        "ms_per_step": round(ms_step, 6), "dtype": "bf16",
+        "config": {"workload": "mixtral47b_drelu_moe_ffn_decode", "batch": B, "d": d, "ffn": ffn,
+                   "experts": n_exp, "top_k": top_k, "x_rotations": 8,
+                   "up_rows_frac": round(float(np.mean(up_frac)), 4),
+                   "down_rows_frac": round(float(np.mean(down_frac)), 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "whole MoE step (router, gate/up, down gather, combine)",
+                     "algorithmic_bytes_per_step": int(alg)},
+        "cpu_baseline": None,
+    }
+
+
 def run_c4s(args, torch, np, qs, datagen, dev, stream):
     log("workload c4s: fused-QKV prefill under Block Q-Sparse (2:4) on sparse MFMA")
     c = datagen.c4_prefill_qkv()
@@ -549,7 +620,7 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     if args.copy_calibration:
         copy_calibration(torch, dev)
-    run = {"c1": run_c1, "c2": run_c2, "c2g": run_c2g, "c3": run_c3, "c4": run_c4, "c4b": run_c4b, "c4s": run_c4s,
+    run = {"c1": run_c1, "c2": run_c2, "c2g": run_c2g, "c3": run_c3, "c4": run_c4, "c4b": run_c4b, "c4s": run_c4s, "c6": run_c6,
            "c5": run_c5}[args.workload]
     out = run(args, torch, np, qs, datagen, dev, stream)
     line = {"metric": out.pop("metric"), "value": out.pop("value"), "unit": out.pop("unit"),

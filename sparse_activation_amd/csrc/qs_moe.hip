@@ -32,63 +32,85 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(b >> 16);
 }
 
-// One workgroup (4 wavefronts) per token.  Wavefront w computes the logits of
-// experts w, w + 4, ...: each lane sums the products of its 8-feature runs
-// (features 512 i + 8 lane ..) in order, then the wavefront adds the lanes.
-// Wavefront 0 then selects and weights the experts.
-__global__ __launch_bounds__(256) void moe_route_kernel(MoeRouteArgs a) {
+// Order-preserving map of a float to an unsigned key (larger float, larger key).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+    const uint32_t b = __float_as_uint(f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// One workgroup of 8 wavefronts per token.  Wavefront w computes the logits
+// of experts w, w + 8, ...: each lane loads its NCH runs of 8 features
+// (features 512 i + 8 lane ..) of x and of the expert's router row at once,
+// sums the products in run order, then the wavefront adds the lanes in a
+// fixed butterfly.  Wavefront 0 then selects the experts with lane e holding
+// logit e: top_k rounds of a wavefront max over (logit, lower index first),
+// and the softmax over the chosen lanes.
+template <int NCH>
+__global__ __launch_bounds__(512) void moe_route_kernel(MoeRouteArgs a) {
     __shared__ float s_logit[64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t t = blockIdx.x, d = a.d;
     const int E = a.n_experts, K = a.top_k;
-    const u32x4* xr = reinterpret_cast<const u32x4*>(a.x + t * d);
-    for (int e = wave; e < E; e += 4) {
-        const u32x4* wr = reinterpret_cast<const u32x4*>(a.wr + (int64_t)e * d);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.x + t * d), (short)0, (int)(d * 2), 0x00020000);
+    u32x4 xv[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int64_t k = (int64_t)i * 512 + 8 * lane;
+        xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, k < d ? (uint32_t)(k * 2) : 0x80000000u, 0, 0);
+    }
+    for (int e = wave; e < E; e += 8) {
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(a.wr + (int64_t)e * d), (short)0, (int)(d * 2), 0x00020000);
+        u32x4 wv[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int64_t k = (int64_t)i * 512 + 8 * lane;
+            wv[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, k < d ? (uint32_t)(k * 2) : 0x80000000u, 0, 0);
+        }
         float s = 0.0f;
-        for (int64_t k = 8 * lane; k < d; k += 512) {
-            const u32x4 xv = xr[k / 8], wv = wr[k / 8];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                s = __fmaf_rn(bf16_lo(xv[q]), bf16_lo(wv[q]), s);
-                s = __fmaf_rn(bf16_hi(xv[q]), bf16_hi(wv[q]), s);
+                s = __fmaf_rn(bf16_lo(xv[i][q]), bf16_lo(wv[i][q]), s);
+                s = __fmaf_rn(bf16_hi(xv[i][q]), bf16_hi(wv[i][q]), s);
             }
-        }
         s = wave_sum64(s);
         if (lane == 0) s_logit[e] = s;
     }
     __syncthreads();
-    if (tid != 0) return;
-    if (a.logits != nullptr)
-        for (int e = 0; e < E; ++e) a.logits[t * E + e] = s_logit[e];
-    // top_k largest logits, ties to the lower index; then ascending order.
-    uint64_t taken = 0;
-    int sel[64];
+    if (wave != 0) return;
+    const bool valid = lane < E;
+    const float lg = valid ? s_logit[lane] : 0.0f;
+    if (valid && a.logits != nullptr) a.logits[t * E + lane] = lg;
+    // key: logit order in the high word, then the lower lane wins
+    const uint64_t key = valid ? ((uint64_t)f32_order_key(lg) << 32) | (uint32_t)(63 - lane) : 0;
+    bool chosen = false;
+    float mx = 0.0f;
     for (int j = 0; j < K; ++j) {
-        int best = -1;
-        for (int e = 0; e < E; ++e) {
-            if (taken >> e & 1) continue;
-            if (best < 0 || s_logit[e] > s_logit[best]) best = e;
+        uint64_t best = chosen ? 0 : key;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            const uint64_t o = ((uint64_t)(uint32_t)__shfl_xor((int)(best >> 32), m, 64) << 32) |
+                               (uint32_t)__shfl_xor((int)(best & 0xFFFFFFFFu), m, 64);
+            best = o > best ? o : best;
         }
-        taken |= uint64_t(1) << best;
-        sel[j] = best;
+        const int win = 63 - (int)(best & 0xFFFFFFFFu);
+        if (lane == win) chosen = true;
+        if (j == 0) mx = __shfl(lg, win, 64);
     }
-    int n = 0;
-    for (int e = 0; e < E; ++e)
-        if (taken >> e & 1) sel[n++] = e;
-    float m = s_logit[sel[0]];
-    for (int j = 1; j < K; ++j) m = fmaxf(m, s_logit[sel[j]]);
-    float p[64], sum = 0.0f;
-    for (int j = 0; j < K; ++j) {
-        p[j] = expf(s_logit[sel[j]] - m);
-        sum += p[j];
-    }
-    for (int j = 0; j < K; ++j) {
-        const int64_t q = t * K + j;
-        const float wq = p[j] / sum;
+    const float p = chosen ? expf(lg - mx) : 0.0f;
+    const float sum = wave_sum64(p);
+    const uint64_t sel = __ballot(chosen);
+    if (chosen) {
+        const int pos = __popcll(sel & ((uint64_t(1) << lane) - 1));
+        const int64_t q = t * K + pos;
+        const float wq = p / sum;
         a.pair_token[q] = (int32_t)t;
-        a.pair_expert[q] = sel[j];
+        a.pair_expert[q] = lane;
         a.pair_weight[q] = wq;
-        if (a.out_experts != nullptr) a.out_experts[q] = sel[j];
+        if (a.out_experts != nullptr) a.out_experts[q] = lane;
         if (a.out_weights != nullptr) a.out_weights[q] = wq;
     }
 }
@@ -129,7 +151,13 @@ hipError_t launch_moe_route(const MoeRouteArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     if (a.n_experts < 1 || a.n_experts > 64 || a.top_k < 1 || a.top_k > a.n_experts || a.d % 8 != 0)
         return hipErrorInvalidValue;
-    moe_route_kernel<<<dim3((unsigned)a.rows), dim3(256), 0, stream>>>(a);
+    if (a.d > 8192) return hipErrorInvalidValue;
+    const int nch = (int)((a.d + 511) / 512);
+    const dim3 grid((unsigned)a.rows), block(512);
+    if (nch <= 2) moe_route_kernel<2><<<grid, block, 0, stream>>>(a);
+    else if (nch <= 4) moe_route_kernel<4><<<grid, block, 0, stream>>>(a);
+    else if (nch <= 8) moe_route_kernel<8><<<grid, block, 0, stream>>>(a);
+    else moe_route_kernel<16><<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
 }
 
