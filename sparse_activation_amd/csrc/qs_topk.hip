@@ -19,6 +19,7 @@
 // news article, Top-K section: activations are quantised before top-K with
 // an epsilon-guarded denominator) and then selects on |q|.
 #include "qs_internal.h"
+#include "qs_select.h"
 
 namespace qs {
 namespace {
@@ -27,23 +28,10 @@ constexpr int kWave = 64;
 constexpr int kNSub = 4;               // LDS sub-histograms (spread atomic contention)
 constexpr int64_t kStageMaxD = 14336;  // raw words staged in LDS up to this row length
 
-__device__ __forceinline__ uint32_t popc_below(uint64_t m) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// Inclusive wavefront sum scan with DPP (in-register cross-lane moves:
-// row_shr 1, 2, 4, 8 inside each 16-lane row, then row_bcast 15 and 31 to
-// carry the row totals; out-of-row sources read zero).
-__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t x) {
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-    return x;
-}
+using sel::popc_below;
+using sel::wave_incl_scan_dpp;
+using sel::find_digit_p;
+using sel::find_top_lane;
 
 // Raw 32-bit word of element i, and its magnitude key.
 template <int KK> struct Elem;
@@ -590,79 +578,14 @@ __device__ __forceinline__ void find_digit(const uint32_t (*h)[256], uint32_t kr
     kr_out = (uint32_t)__builtin_amdgcn_readlane((int)kk, src);
 }
 
-// Descending search of a histogram of 64 P bins (ascending bin index = digit)
-// held in LDS, done redundantly by every wavefront: lane l owns bins
-// 64 P - 1 - P l - c (c = 0 .. P - 1).  Returns the digit holding the kr-th
-// largest counted key, the rank of that key inside its bin and the bin count.
-template <int P>
-__device__ __forceinline__ void find_digit_p(const uint32_t* h, uint32_t kr, int lane,
-                                             uint32_t& digit, uint32_t& kr_out, uint32_t& cnt_out) {
-    static_assert(P % 4 == 0, "lanes own whole 16-byte groups of bins");
-    uint32_t c[P];
-#pragma unroll
-    for (int g = 0; g < P / 4; ++g) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&h[64 * P - P * (lane + 1) + P - 4 * (g + 1)]);
-        c[4 * g] = v.w; c[4 * g + 1] = v.z; c[4 * g + 2] = v.y; c[4 * g + 3] = v.x;
-    }
-    uint32_t lsum = 0;
-#pragma unroll
-    for (int i = 0; i < P; ++i) lsum += c[i];
-    const uint32_t incl = wave_incl_scan_dpp(lsum);
-    const uint32_t excl = incl - lsum;
-    const uint64_t bm = __ballot(excl < kr && kr <= incl);
-    const int src = (int)__builtin_ctzll(bm);
-    uint32_t e = excl, dg = 0, kk = 0, cn = 0;
-    bool found = false;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-        if (!found && e < kr && kr <= e + c[i]) {
-            found = true;
-            dg = (uint32_t)(64 * P - 1 - P * lane - i);
-            kk = kr - e;
-            cn = c[i];
-        }
-        e += c[i];
-    }
-    digit = (uint32_t)__builtin_amdgcn_readlane((int)dg, src);
-    kr_out = (uint32_t)__builtin_amdgcn_readlane((int)kk, src);
-    cnt_out = (uint32_t)__builtin_amdgcn_readlane((int)cn, src);
-}
-
-// Descending search over n <= 64 counts t[n - 1], ..., t[0] given in LDS:
-// lane c takes t[n - 1 - c], one wave scan finds the first (from the top) whose
-// running total reaches kr.  Returns its index and the total above it.
-__device__ __forceinline__ void find_top_lane(const uint32_t* t, int n, uint32_t kr, int lane,
-                                              int& idx, uint32_t& before) {
-    const uint32_t v = lane < n ? t[n - 1 - lane] : 0u;
-    const uint32_t incl = wave_incl_scan_dpp(v);
-    const uint64_t bm = __ballot(incl >= kr);
-    const int f = bm ? (int)__builtin_ctzll(bm) : n - 1;
-    idx = n - 1 - f;
-    before = (uint32_t)__builtin_amdgcn_readlane((int)(incl - v), f);
-}
-
 template <int NT, int NQ, int KK, int XK>
 __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
     constexpr int NW = NT / kWave;
     constexpr int V = VecOf<KK>::V, CS = V * NT, EPT = NQ * V;
     constexpr int KB = Elem<KK>::kKeyBits;
-    constexpr uint32_t kInvalid = 0x80000000u;
+    constexpr uint32_t kInvalid = sel::kInvalid;
     constexpr int ESZ = elem_bytes<KK>();
-    // Digits: the first covers the top min(KB, 12) key bits (4096 bins, so
-    // that the few exponent values an activation spans spread over 16 bins
-    // each), the next ones 8 bits.  Every level has its own histogram,
-    // cleared once at the start.
-    constexpr int W1 = KB < 12 ? KB : 12;
-    constexpr int S1 = KB - W1;
-    constexpr int NB1 = 1 << W1;
-    constexpr int NB1P = NB1 < 256 ? 256 : NB1;
-    constexpr int kCap = 2048;    // boundary-bin keys finished by one wavefront
-    __shared__ __attribute__((aligned(16))) uint32_t s_h1[NB1P];
-    __shared__ __attribute__((aligned(16))) uint32_t s_hl[3][256];
-    __shared__ uint32_t s_cand[kCap];
-    __shared__ uint32_t s_chunk[16];
-    __shared__ uint32_t s_res[4];
-    __shared__ uint32_t s_nc;
+    __shared__ sel::SelectLds<KB> s_sel;
     __shared__ uint32_t s_tot[2][NQ][NW];
     __shared__ float s_max[NW];
 
@@ -672,9 +595,7 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
 
     if (r == 0 && a.zero_ptr != nullptr)
         for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
-    for (int i = tid; i < NB1P; i += NT) s_h1[i] = 0;
-    for (int i = tid; i < 3 * 256; i += NT) (&s_hl[0][0])[i] = 0;
-    if (tid == 0) s_nc = 0;
+    sel::select_clear<NT, KB>(s_sel, tid);
 
     // ---- load runs (past the row end the buffer reads zero)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -723,106 +644,8 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
     __syncthreads();   // histograms cleared
 
     // ---- select
-    // Count the entries that match the prefix into digit bins.  Zero keys
-    // (frequent: an FFN intermediate is often half zeros) are counted with a
-    // ballot instead of piling conflicting atomics onto bin 0.
-    auto count_level = [&](uint32_t* hist, uint32_t pre, uint32_t hm, int sh, uint32_t dm) {
-        uint32_t nzero = 0;
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const bool m = key[i] != kInvalid && (key[i] & hm) == pre;
-            nzero += (uint32_t)__popcll(__ballot(m && key[i] == 0u));
-            if (m && key[i] != 0u) atomicAdd(&hist[(key[i] >> sh) & dm], 1u);
-        }
-        nzero = __builtin_amdgcn_readfirstlane(nzero);
-        if (lane == 0 && nzero != 0) atomicAdd(&hist[0], nzero);
-    };
-    uint32_t prefix = 0, himask = 0, kr = (uint32_t)k, eqtot = 0;
-    if (k > 0) {
-        uint32_t dg, cnt;
-        count_level(s_h1, 0u, 0u, S1, (uint32_t)(NB1 - 1));
-        __syncthreads();
-        // The digit searches below run in one wavefront while the others wait
-        // at the next barrier: a search done by all 16 wavefronts of a row
-        // costs four times over on each SIMD.
-        if constexpr (NB1 > 1024) {
-            for (int c = wave; c < NB1 / 256; c += NW) {
-                const uint4 v = *reinterpret_cast<const uint4*>(&s_h1[256 * c + 4 * lane]);
-                const uint32_t t = wave_incl_scan_dpp(v.x + v.y + v.z + v.w);
-                if (lane == kWave - 1) s_chunk[c] = t;
-            }
-            __syncthreads();
-            if (wave == 0) {
-                int cstar;
-                uint32_t before;
-                find_top_lane(s_chunk, NB1 / 256, kr, lane, cstar, before);
-                find_digit_p<4>(s_h1 + 256 * cstar, kr - before, lane, dg, kr, cnt);
-                dg += (uint32_t)(256 * cstar);
-            }
-        } else if (wave == 0) {
-            static_assert(NB1 <= 256, "first digits of 9 to 11 bits are not used");
-            find_digit_p<4>(s_h1, kr, lane, dg, kr, cnt);
-        }
-        if (wave == 0 && lane == 0) { s_res[0] = dg; s_res[1] = kr; s_res[2] = cnt; }
-        __syncthreads();
-        dg = s_res[0]; kr = s_res[1]; cnt = s_res[2];
-        prefix = dg << S1;
-        himask = (uint32_t)(NB1 - 1) << S1;
-        // Remaining digits are 8 bits wide, each level with its own 256-bin
-        // histogram s_hl[level], so no level clears a buffer.
-        if (S1 > 8 && cnt <= (uint32_t)kCap) {
-            // Several digits left over few keys: compact them (one LDS atomic
-            // per wavefront and entry slot) and let wavefront 0 finish alone.
-#pragma unroll
-            for (int i = 0; i < EPT; ++i) {
-                const bool m = key[i] != kInvalid && (key[i] & himask) == prefix;
-                const uint64_t bm = __ballot(m);
-                if (bm == 0) continue;   // uniform
-                uint32_t base = 0;
-                if (lane == 0) base = atomicAdd(&s_nc, (uint32_t)__popcll(bm));
-                base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-                if (m) s_cand[base + popc_below(bm)] = key[i];
-            }
-            __syncthreads();
-            if (wave == 0) {
-                const uint32_t ncand = cnt;
-                int shift = S1, l = 0;
-                while (shift > 0) {
-                    const int nshift = shift > 8 ? shift - 8 : 0;
-                    const uint32_t dmask = (1u << (shift - nshift)) - 1u;
-                    for (uint32_t c = (uint32_t)lane; c < ncand; c += kWave) {
-                        const uint32_t kc = s_cand[c];
-                        if ((kc & himask) == prefix) atomicAdd(&s_hl[l][(kc >> nshift) & dmask], 1u);
-                    }
-                    find_digit_p<4>(s_hl[l], kr, lane, dg, kr, cnt);
-                    prefix |= dg << nshift;
-                    himask |= dmask << nshift;
-                    shift = nshift;
-                    ++l;
-                }
-                if (lane == 0) { s_res[0] = prefix; s_res[1] = kr; s_res[2] = cnt; }
-            }
-            __syncthreads();
-            prefix = s_res[0]; kr = s_res[1]; cnt = s_res[2];
-        } else {
-            // One digit left, or many keys (ties, zeros): all wavefronts count
-            // each digit and search its 256 bins.
-            int shift = S1, l = 0;
-            while (shift > 0) {
-                const int nshift = shift > 8 ? shift - 8 : 0;
-                const uint32_t dmask = (1u << (shift - nshift)) - 1u;
-                count_level(s_hl[l], prefix, himask, nshift, dmask);
-                __syncthreads();
-                find_digit_p<4>(s_hl[l], kr, lane, dg, kr, cnt);
-                prefix |= dg << nshift;
-                himask |= dmask << nshift;
-                shift = nshift;
-                ++l;
-            }
-        }
-        eqtot = cnt;   // the last bin holds exactly the keys equal to tau
-    }
-    const uint32_t tau = (k > 0) ? prefix : 0xFFFFFFFFu;
+    uint32_t tau = 0xFFFFFFFFu, kr = (uint32_t)k, eqtot = 0;
+    if (k > 0) sel::radix_select<NT, EPT, KB>(key, (uint32_t)k, s_sel, tid, tau, kr, eqtot);
 
     // ---- ordered output: two block scans over (run, thread) order.
     uint32_t eqc[NQ], gtc[NQ];
