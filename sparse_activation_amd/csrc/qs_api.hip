@@ -379,13 +379,21 @@ qs_status qs_sparse_linear_i8t(const float* x, int64_t rows, int64_t d_in, int64
     t.x = x; t.d = d_in; t.k = k; t.idx = idx; t.idx_stride = k;
     t.xs = wsp.qs; t.xq = xq; t.xscale = scale;
     t.zero_ptr = wsp.counters; t.n_zero = plan.n_counters;
+    // The matrix-core kernel's splits add into zeroed int32 sums: acc itself
+    // when asked for, else scratch; each row's selection workgroup zeroes it.
+    int32_t* acc_sum = nullptr;
+    if (plan.mfma && plan.nsplit > 1 && (acc || y)) {
+        acc_sum = acc ? acc : wsp.partial;
+        t.zero_rows = acc_sum;
+        t.zero_row_len = n_out;
+    }
     hipError_t e = qs::launch_topk(qs::KEY_Q8, qs::XS_I8, rows, t, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     if (!acc && !y) return ok();
     qs::I8tArgs g{};
     g.qs = wsp.qs; g.xscale = scale; g.rows = rows; g.d_in = d_in; g.n_out = n_out;
     g.wt = wt_packed; g.alpha = alpha; g.partial = wsp.partial; g.counters = wsp.counters;
-    g.acc = acc; g.y = y;
+    g.acc = acc; g.y = y; g.acc_sum = acc_sum;
     e = qs::launch_i8t(plan, g, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();

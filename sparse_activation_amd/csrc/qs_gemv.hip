@@ -1016,6 +1016,222 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Ternary x int8 on the int8 matrix cores, for token batches (16 and more):
+// the union of the batch's selections covers nearly every input feature, so
+// acc = Qs . T^T is a dense int8 contraction (Qs = the masked q, zeros where
+// not selected).  v_mfma_i32_32x32x32_i8 sums exactly in int32, so the
+// result is the same integer as any other order.
+// Workgroup: 64 tokens (two 32-row MFMA tiles) x 128 outputs (one 32-column
+// tile per wavefront) over a split of kT8Steps steps of 64 input features.
+// Every global load of the split is issued at the start (per thread and
+// step: 16 bytes of Qs and 8 packed bytes), so the steps only wait for data
+// already in flight.  Per step the workgroup stages A (64 tokens x 64
+// features, int8) and the decoded B tile ([k][n] int8, 64 x 128) in LDS; B
+// rows have a 144-byte pitch so that the eight rows a transposing read
+// touches land on distinct banks, and each wavefront takes its B operand with
+// ds_read_b64_tr_b8 (in each group of 16 lanes, lane 2e + h addresses k-row
+// e, columns 8h .. 8h + 7; lane j receives column j's eight k values).
+// ---------------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+constexpr int kT8CT = 128;     // output columns per workgroup
+constexpr int kT8MT = 64;      // tokens per workgroup
+constexpr int kT8KS = 128;     // features per step
+constexpr int kT8Steps = 8;    // steps per split
+constexpr int kT8Pitch = 144;  // LDS bytes per decoded k-row
+constexpr int kT8APitch = 144; // LDS bytes per staged token row (128 + 16: conflict-free 16-byte reads)
+constexpr int kSc1 = 16;       // buffer cache policy sc1 (agent-scope coherent)
+
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* base, int byte_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(base + byte_off));
+#else
+    (void)base; (void)byte_off;
+    return i32x2{0, 0};
+#endif
+}
+
+// One packed byte (4 ternary weights, 2-bit two's complement: 00 = 0,
+// 01 = +1, 11 = -1) -> 4 int8 in one word.  The even and the odd fields are
+// spread into their bytes by one multiply each (the shifted copies do not
+// overlap, so no carries), then bit 1 of each byte, set only for -1, fills
+// the byte's upper bits.
+__device__ __forceinline__ uint32_t decode_ternary4(uint32_t b) {
+    uint32_t y = (((b & 0x33u) * 0x1001u) & 0x00030003u) | (((b & 0xCCu) * 0x40040u) & 0x03000300u);
+    return y | ((y & 0x02020202u) * 0x7Fu);
+}
+
+__global__ __launch_bounds__(kNT) void i8t_mfma_kernel(I8tArgs a, int nsplit) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kT8KS * kT8Pitch];
+    __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kT8MT * kT8APitch];
+    __shared__ int s_last;
+    __shared__ float s_fac[kT8MT];    // fl32(alpha / s_r) of the tile's tokens
+    const int tile = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t rows = a.rows, d_in = a.d_in, n_out = a.n_out;
+    const int64_t m0 = (int64_t)mt * kT8MT, n0 = (int64_t)tile * kT8CT;
+    const int64_t k_begin = (int64_t)split * kT8Steps * kT8KS;
+    const int64_t k_end = min(d_in, k_begin + (int64_t)kT8Steps * kT8KS);
+    const int64_t pbytes = n_out / 4;                       // packed bytes per row
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(a.qs), (short)0, (int)(rows * d_in), 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.wt), (short)0, (int)(d_in * pbytes), 0x00020000);
+
+    // Thread t stages token row t / 4, features 32 (t % 4) .. +31 of a step,
+    // and packed k-row t / 2, bytes 16 (t % 2) .. +15 (64 columns) of the tile.
+    const int arow_l = tid >> 2, aq = tid & 3, prow = tid >> 1, pq = tid & 1;
+    const int64_t arow = m0 + arow_l;
+    const int64_t pbyte = n0 / 4 + 16 * pq;
+    uint32_t aoff[kT8Steps], poff[kT8Steps];
+#pragma unroll
+    for (int s = 0; s < kT8Steps; ++s) {
+        const int64_t ka = k_begin + (int64_t)s * kT8KS + 32 * aq;
+        const int64_t kp = k_begin + (int64_t)s * kT8KS + prow;
+        aoff[s] = (arow < rows && ka < k_end) ? (uint32_t)(arow * d_in + ka) : kOOB;
+        poff[s] = (kp < k_end && pbyte < pbytes) ? (uint32_t)(kp * pbytes + pbyte) : kOOB;
+    }
+    u32x4 ra[kT8Steps][2], rp[kT8Steps];
+#pragma unroll
+    for (int s = 0; s < kT8Steps; ++s) {
+        rp[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, poff[s], 0, 0);
+        ra[s][0] = __builtin_amdgcn_raw_buffer_load_b128(qr, aoff[s], 0, 0);
+        ra[s][1] = __builtin_amdgcn_raw_buffer_load_b128(qr, aoff[s] == kOOB ? kOOB : aoff[s] + 16u, 0, 0);
+    }
+    auto stage = [&](int buf, int s) {
+        u32x4* ad = reinterpret_cast<u32x4*>(&s_a[buf][arow_l * kT8APitch + 32 * aq]);
+        ad[0] = ra[s][0];
+        ad[1] = ra[s][1];
+        uint8_t* dst = &s_b[buf][prow * kT8Pitch + 64 * pq];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t v = rp[s][w];
+            *reinterpret_cast<uint4*>(dst + 16 * w) =
+                make_uint4(decode_ternary4(v & 0xFFu), decode_ternary4((v >> 8) & 0xFFu),
+                           decode_ternary4((v >> 16) & 0xFFu), decode_ternary4(v >> 24));
+        }
+    };
+    // Fragment reads (four 32-feature slices per step).  A: lane -> token row
+    // 32 i + lane % 32, features 32 sl + 16 (lane / 32) .. +15.  B: lane group
+    // g = lane / 16 covers columns 32 wave + 16 (g % 2) .. +15 and features
+    // 32 sl + 16 (g / 2) .. +15.
+    const int g = lane >> 4, li = lane & 15;
+    const int trow = 16 * (g >> 1) + (li >> 1);
+    const int tcol = 32 * wave + 16 * (g & 1) + 8 * (li & 1);
+
+    i32x16 acc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0;
+
+    stage(0, 0);
+    __syncthreads();
+    // All kT8Steps steps run (steps past the split's features read zeros), so
+    // the loop unrolls fully and the prefetched registers stay registers.
+#pragma unroll
+    for (int st = 0; st < kT8Steps; ++st) {
+        const int cb = st & 1;
+        i32x4 afr[2][4], bfr[4];
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            const int off = (32 * sl + trow) * kT8Pitch + tcol;
+            const i32x2 lo = lds_read_tr8(s_b[cb], off), hi = lds_read_tr8(s_b[cb], off + 8 * kT8Pitch);
+            bfr[sl] = i32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                afr[i][sl] = __builtin_bit_cast(i32x4, *reinterpret_cast<const u32x4*>(
+                    &s_a[cb][(32 * i + (lane & 31)) * kT8APitch + 32 * sl + 16 * (lane >> 5)]));
+        }
+        // The next step goes into the other buffers (last read before the
+        // previous barrier) while the MFMAs run.
+        if (st + 1 < kT8Steps) stage(cb ^ 1, st + 1);
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                acc[i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(afr[i][sl], bfr[sl], acc[i], 0, 0, 0);
+        __syncthreads();
+    }
+
+    // Outputs: acc[i][v] is token m0 + 32 i + 8 (v / 4) + 4 (lane / 32) + v % 4,
+    // column n0 + 32 wave + lane % 32.
+    const int64_t col = n0 + 32 * wave + (lane & 31);
+    // Dequantisation factors, one per token row of the tile (staged before
+    // any output is written, so no output waits on its own scale load).
+    auto stage_factors = [&]() {
+        if (a.y != nullptr && tid < kT8MT) {
+            const int64_t r = m0 + tid;
+            s_fac[tid] = r < rows ? __fdiv_rn(a.alpha, a.xscale[r]) : 0.0f;
+        }
+        __syncthreads();
+    };
+    auto finish = [&](int64_t row, int sum) {
+        if (a.acc) a.acc[row * n_out + col] = sum;
+        if (a.y) a.y[row * n_out + col] = __fmul_rn((float)sum, s_fac[row - m0]);
+    };
+    auto out_row = [&](int i, int v) -> int64_t {
+        return m0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    };
+    if (nsplit == 1) {
+        stage_factors();
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = out_row(i, v);
+                if (row < rows && col < n_out) finish(row, acc[i][v]);
+            }
+        return;
+    }
+    // Splits: add into the zeroed int32 sums (integer addition, so the result
+    // does not depend on the order the splits arrive in); the last split of
+    // the tile then dequantises (with factors staged before the handoff).
+    stage_factors();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t row = out_row(i, v);
+            if (row < rows && col < n_out)
+                __hip_atomic_fetch_add(&a.acc_sum[row * n_out + col], (int32_t)acc[i][v], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+    const int ci = mt * gridDim.x + tile;
+    if (last_split_arrived(&a.counters[ci], nsplit, &s_last)) {
+        if (a.y != nullptr) {
+            // Buffer loads with 32-bit offsets (entries past the batch or the
+            // outputs take the out-of-range offset and read 0), unconditional
+            // so that all of a thread's loads are in flight together; cache
+            // policy sc1: agent-coherent, as other workgroups added the sums.
+            const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+                a.acc_sum, (short)0, (int)(rows * n_out * 4), 0x00020000);
+            int sum[2][16];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t row = out_row(i, v);
+                    const bool ok = row < rows && col < n_out;
+                    sum[i][v] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+                        sr, ok ? (uint32_t)((row * n_out + col) * 4) : kOOB, 0, kSc1);
+                }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t row = out_row(i, v);
+                    if (row < rows && col < n_out)
+                        a.y[row * n_out + col] = __fmul_rn((float)sum[i][v], s_fac[row - m0]);
+                }
+        }
+        if (tid == 0) store_agent(&a.counters[ci], 0);
+    }
+}
+
 }  // namespace
 
 GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16, int max_bt) {
@@ -1101,6 +1317,22 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
 
 I8tPlan plan_i8t(int64_t rows, int64_t d_in, int64_t n_out) {
     I8tPlan p{};
+    // (The int32 sums are addressed with 32-bit buffer offsets below the
+    // out-of-range offset: at most 2^30 bytes.)
+    if (rows >= 16 && d_in % 16 == 0 && rows * n_out * 4 < (int64_t)kOOB) {
+        // Token batches: the int8 matrix-core kernel, 64 x 128 tiles, the
+        // features split into runs of 1024.
+        p.mfma = 1;
+        p.ct = kT8CT;
+        p.n_tiles = (int)ceil_div(n_out, kT8CT);
+        p.bt = kT8MT;
+        p.n_tok_tiles = (int)ceil_div(rows, kT8MT);
+        p.cand = kT8Steps * kT8KS;
+        p.nsplit = (int)ceil_div(d_in, p.cand);
+        p.partial_ints = p.nsplit > 1 ? (size_t)rows * n_out : 0;   // the int32 sums
+        p.n_counters = p.n_tiles * p.n_tok_tiles;
+        return p;
+    }
     p.ct = kI8CT;
     p.n_tiles = (int)ceil_div(n_out, p.ct);
     p.bt = pow2_tile(rows, 2);   // 32 int32 accumulators per token per lane
@@ -1122,6 +1354,11 @@ I8tPlan plan_i8t(int64_t rows, int64_t d_in, int64_t n_out) {
 
 hipError_t launch_i8t(const I8tPlan& p, const I8tArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
+    if (p.mfma) {
+        if (p.nsplit > 1 && a.acc_sum == nullptr) return hipErrorInvalidValue;
+        i8t_mfma_kernel<<<dim3(p.n_tiles, p.nsplit, p.n_tok_tiles), dim3(kNT), 0, stream>>>(a, p.nsplit);
+        return hipGetLastError();
+    }
     const size_t padded = (size_t)p.cand + 3 * kI8NSlot * kUnroll;
     size_t lds_a = padded * p.bt * 4 + padded * 4;
     size_t lds_c = (size_t)kI8NSlot * kI8CT * 4;

@@ -39,6 +39,8 @@ struct TopkArgs {
     float* xscale;        // KEY_Q8 only: [rows] or null
     int32_t* zero_ptr;    // block 0 clears zero_ptr[0..n_zero) (split-K counters)
     int n_zero;
+    int32_t* zero_rows;   // or null: the workgroup of row r clears
+    int64_t zero_row_len; //   zero_rows[r * zero_row_len ..) (zero_row_len % 4 == 0)
 };
 
 // One workgroup per row.  Returns a HIP error code (hipSuccess = 0).
@@ -87,6 +89,7 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
 
 // ---------------------------------------------------------------- ternary x int8 gather
 struct I8tPlan {
+    int mfma;        // 1: the int8 matrix-core kernel (token batches); cand = features per split
     int ct, n_tiles, bt, n_tok_tiles, cand, nsplit;
     size_t partial_ints;
     int n_counters;
@@ -103,6 +106,8 @@ struct I8tArgs {
     int32_t* counters;
     int32_t* acc;            // [rows, n_out] or null
     float* y;                // [rows, n_out] or null
+    int32_t* acc_sum;        // matrix-core kernel with splits: [rows, n_out], zero on
+                             //   entry; the splits add into it (acc itself, or scratch)
 };
 hipError_t launch_i8t(const I8tPlan& p, const I8tArgs& a, hipStream_t stream);
 

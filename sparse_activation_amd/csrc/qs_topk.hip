@@ -128,6 +128,9 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(TopkArgs a) {
 
     if (r == 0 && a.zero_ptr != nullptr)
         for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
+    if (a.zero_rows != nullptr)
+        for (int64_t i = tid; i < a.zero_row_len / 4; i += NT)
+            reinterpret_cast<uint4*>(a.zero_rows + (int64_t)r * a.zero_row_len)[i] = make_uint4(0u, 0u, 0u, 0u);
 
     // Quantisation scale (KEY_Q8): gamma = max|x| (exact), s = 127 / (gamma + eps).
     float scale = 0.0f;
@@ -310,6 +313,9 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
 
     if (r == 0 && a.zero_ptr != nullptr)
         for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
+    if (a.zero_rows != nullptr)
+        for (int64_t i = tid; i < a.zero_row_len / 4; i += NT)
+            reinterpret_cast<uint4*>(a.zero_rows + (int64_t)r * a.zero_row_len)[i] = make_uint4(0u, 0u, 0u, 0u);
 
     // Load the row: every load issued before any is used.
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -595,6 +601,9 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
 
     if (r == 0 && a.zero_ptr != nullptr)
         for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
+    if (a.zero_rows != nullptr)
+        for (int64_t i = tid; i < a.zero_row_len / 4; i += NT)
+            reinterpret_cast<uint4*>(a.zero_rows + (int64_t)r * a.zero_row_len)[i] = make_uint4(0u, 0u, 0u, 0u);
     sel::select_clear<NT, KB>(s_sel, tid);
 
     // ---- load runs (past the row end the buffer reads zero)

@@ -36,7 +36,11 @@ def _case(gpu_lib, x, w, k):
 
 
 @pytest.mark.parametrize("rows,d,n", [(1, 64, 16), (3, 300, 48), (5, 1000, 1040),
-                                      (9, 513, 2064), (33, 256, 64)])
+                                      (9, 513, 2064), (33, 256, 64),
+                                      # token batches: the int8 matrix-core kernel (ragged
+                                      # feature steps, column tiles and token tiles)
+                                      (16, 64, 16), (64, 1040, 400), (100, 512, 272),
+                                      (130, 2048, 128)])
 def test_i8t_random(gpu_lib, rows, d, n):
     rng = np.random.default_rng(rows + d + n)
     x = datagen.student_t(rng, (rows, d))
