@@ -136,7 +136,9 @@ FfnWs ffn_ws(char* base, int64_t rows, int64_t d, int64_t ffn, bool drelu) {
     if (!drelu) {
         qs::GemvPlan ub = qs::plan_gemv(rows, d, ffn, 1), uf = qs::plan_gemv(rows, d, ffn, 0);
         up_ctr = (size_t)(ub.n_counters > uf.n_counters ? ub.n_counters : uf.n_counters);
-        up_part = max_sz(ub.scratch_floats, uf.scratch_floats);
+        // The gated FFN's one-pass gather keeps the gate's split partials
+        // behind the up projection's.
+        up_part = max_sz(ub.scratch_floats, uf.scratch_floats) + max_sz(ub.partial_floats, uf.partial_floats);
     }
     qs::GemvPlan db = qs::plan_gemv(rows, ffn, d, 1), df = qs::plan_gemv(rows, ffn, d, 0);
     size_t down_ctr = (size_t)(db.n_counters > df.n_counters ? db.n_counters : df.n_counters);
@@ -457,7 +459,15 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
         g.partial = wsp.partial; g.counters = wsp.ctr_up; g.y = hbuf; g.y_bf16 = 0;
         g.epilogue = qs::EPI_RELU2;
         g.xs_bf16 = dt == QS_BF16;
-        if (act == QS_ACT_RELU2_GLU) {
+        if (act == QS_ACT_RELU2_GLU && qs::gemv_dual_supported(pu)) {
+            // Both projections in one gather: the gate's and the up rows of
+            // each selected feature are streamed together, and the last
+            // split forms h = relu(g)^2 * u.
+            g.w2 = w_gate;
+            g.partial2 = wsp.partial + (pu.partial_floats * 4 + 255) / 256 * 64;
+            e = qs::launch_gemv_dual(pu, wb, g, st);
+            if (e != hipSuccess) return hip_fail(e, fn);
+        } else if (act == QS_ACT_RELU2_GLU) {
             // Gate first, kept in fp32 in the buffer that later holds the
             // selected intermediate; the up gather then forms h in its epilogue.
             // Both gathers read the same selected rows; the split counters
@@ -468,9 +478,12 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
             if (e != hipSuccess) return hip_fail(e, fn);
             g.epilogue = qs::EPI_RELU2_GLU;
             g.gate = wsp.hs;
+            e = qs::launch_gemv(pu, wb, g, st);
+            if (e != hipSuccess) return hip_fail(e, fn);
+        } else {
+            e = qs::launch_gemv(pu, wb, g, st);
+            if (e != hipSuccess) return hip_fail(e, fn);
         }
-        e = qs::launch_gemv(pu, wb, g, st);
-        if (e != hipSuccess) return hip_fail(e, fn);
     } else {
         const uint16_t* xin = (const uint16_t*)x;
         bool zeroed = false;

@@ -141,6 +141,11 @@ __device__ __forceinline__ void store_final(const GemvArgs& a, int64_t i, float 
     }
 }
 
+// Gated squared ReLU of a (gate, up) pair of sums: relu(g)^2 * u.
+__device__ __forceinline__ float relu2_glu(float g, float u) {
+    return g > 0.0f ? __fmul_rn(__fmul_rn(g, g), u) : 0.0f;
+}
+
 // Inclusive prefix sum over a wavefront (DPP row shifts and broadcasts).
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
     x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
@@ -152,12 +157,15 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
     return x;
 }
 
-template <int WBF16, int BT>
+// DUAL: a second matrix (a.w2, the gate) is streamed at the same rows into a
+// second set of sums, and the output is relu2_glu(gate, up).
+template <int WBF16, int BT, bool DUAL = false>
 __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, int nsplit) {
     constexpr int EPT = WBF16 ? 8 : 4;
     constexpr int CT = kFLPR * EPT;                      // 128-byte row segments
     constexpr int TG = BT < 2 ? BT : 2;
-    constexpr int U = BT <= 4 ? kMaxUnroll : kUnroll;   // rows per stage per lane
+    // rows per stage per lane (the dual kernel keeps the same bytes in flight)
+    constexpr int U = (BT <= 4 && !DUAL) ? kMaxUnroll : kUnroll;
     constexpr int BATCH = kFNSlot * U;                   // rows per pipeline stage
     constexpr int MAXC = 8192 / BT < kFMaxCand ? 8192 / BT : kFMaxCand;   // as in the plan
     constexpr int NCH = MAXC / kNT;                                      // candidate chunks
@@ -243,33 +251,42 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
     if (BT == 1 && a.row_expert != nullptr)
         wbase = reinterpret_cast<const char*>(a.w) + (int64_t)a.row_expert[tok0] * a.expert_bytes;
     const __amdgpu_buffer_rsrc_t rs = weight_rsrc(wbase, a.d_in * (int64_t)rowbytes);
+    const __amdgpu_buffer_rsrc_t rs2 = weight_rsrc(DUAL ? a.w2 : wbase, a.d_in * (int64_t)rowbytes);
+    constexpr int NM = DUAL ? 2 : 1;   // matrices streamed: [0] = w, [1] = w2
 
-    float acc[BT][EPT];
+    float acc[NM][BT][EPT];
 #pragma unroll
-    for (int t = 0; t < BT; ++t)
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) acc[t][e] = 0.0f;
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) acc[m][t][e] = 0.0f;
 
     // Two register buffers in ping-pong (no copies, so the waits on one stage
-    // never cover the loads of the next): 2 * U rows in flight per lane.
-    u32x4 bufa[U], bufb[U];
-    auto load_stage = [&](u32x4* dst, int bi) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            dst[u] = __builtin_amdgcn_raw_buffer_load_b128(
-                rs, s_off[bi * BATCH + slot + u * kFNSlot] + colb, 0, 0);
-    };
-    auto fma_stage = [&](const u32x4* src, int bi) {
+    // never cover the loads of the next): 2 * U rows in flight per lane and matrix.
+    u32x4 bufa[NM][U], bufb[NM][U];
+    auto load_stage = [&](u32x4 (*dst)[U], int bi) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float w[EPT];
-            unpack<WBF16>(src[u], w);
+            const uint32_t off = s_off[bi * BATCH + slot + u * kFNSlot] + colb;
+            dst[0][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+            if constexpr (DUAL) dst[NM - 1][u] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off, 0, 0);
+        }
+    };
+    auto fma_stage = [&](const u32x4 (*src)[U], int bi) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
             const int ai = bi * BATCH + slot + u * kFNSlot;
 #pragma unroll
-            for (int t = 0; t < BT; ++t) {
-                const float c = s_coef[ai * BT + t];
+            for (int m = 0; m < NM; ++m) {
+                float w[EPT];
+                unpack<WBF16>(src[m][u], w);
 #pragma unroll
-                for (int e = 0; e < EPT; ++e) acc[t][e] = fmaf(c, w[e], acc[t][e]);
+                for (int t = 0; t < BT; ++t) {
+                    const float c = s_coef[ai * BT + t];
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e) acc[m][t][e] = fmaf(c, w[e], acc[m][t][e]);
+                }
             }
         }
     };
@@ -290,28 +307,43 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
     }
     __syncthreads();   // s_coef / s_off are dead from here: reuse as the reduction buffer
 
-    // Phase C: sum the row slots in slot order, token group by token group.
+    // Phase C: sum the row slots in slot order, token group by token group
+    // (and, for the dual kernel, the gate's sums first).
     float* s_red = smem;   // [kFNSlot][TG][CT]
     const int cl = (lane % kFLPR) * EPT;
+    constexpr int OPT = (TG * CT + kNT - 1) / kNT;   // outputs per thread and token group
 #pragma unroll
     for (int t0 = 0; t0 < BT; t0 += TG) {
+        float gsum[OPT];
 #pragma unroll
-        for (int g = 0; g < TG; ++g)
+        for (int m = NM - 1; m >= 0; --m) {
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) s_red[(slot * TG + g) * CT + cl + e] = acc[t0 + g][e];
-        __syncthreads();
-        for (int o = tid; o < TG * CT; o += kNT) {
-            float s = 0.0f;
+            for (int g = 0; g < TG; ++g)
 #pragma unroll
-            for (int sl = 0; sl < kFNSlot; ++sl) s += s_red[sl * TG * CT + o];
-            const int64_t row = tok0 + t0 + o / CT;
-            const int64_t cg = (int64_t)tile * CT + (o % CT);
-            if (row < rows && cg < n_out) {
-                if (nsplit == 1) store_final(a, row * n_out + cg, s);
-                else store_agent(&a.partial[((int64_t)split * rows + row) * n_out + cg], s);
+                for (int e = 0; e < EPT; ++e) s_red[(slot * TG + g) * CT + cl + e] = acc[m][t0 + g][e];
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < OPT; ++q) {
+                const int o = q * kNT + tid;
+                float s = 0.0f;
+                if (o < TG * CT) {
+#pragma unroll
+                    for (int sl = 0; sl < kFNSlot; ++sl) s += s_red[sl * TG * CT + o];
+                }
+                const int64_t row = o < TG * CT ? tok0 + t0 + o / CT : rows;   // rows: no store
+                const int64_t cg = (int64_t)tile * CT + (o % CT);
+                if (m == 1) {   // gate (dual kernel only)
+                    gsum[q] = s;
+                    if (nsplit > 1 && row < rows && cg < n_out)
+                        store_agent(&a.partial2[((int64_t)split * rows + row) * n_out + cg], s);
+                } else if (row < rows && cg < n_out) {
+                    if (nsplit > 1) store_agent(&a.partial[((int64_t)split * rows + row) * n_out + cg], s);
+                    else if (DUAL) reinterpret_cast<float*>(a.y)[row * n_out + cg] = relu2_glu(gsum[q], s);
+                    else store_final(a, row * n_out + cg, s);
+                }
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
 
     // Phase D: the last split of this tile sums the partials in split order.
@@ -323,19 +355,26 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
                 const int64_t cg = (int64_t)tile * CT + (o % CT);
                 if (row < rows && cg < n_out) {
                     // 16 independent loads in flight, summed in split order.
-                    const float* pp = a.partial + row * n_out + cg;
                     const int64_t stride = rows * n_out;
-                    float s = 0.0f;
-                    for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
-                        float v[16];
+                    auto split_sum = [&](const float* pp) {
+                        float s = 0.0f;
+                        for (int sp0 = 0; sp0 < nsplit; sp0 += 16) {
+                            float v[16];
 #pragma unroll
-                        for (int u = 0; u < 16; ++u)
-                            v[u] = sp0 + u < nsplit ? load_agent(pp + (int64_t)(sp0 + u) * stride) : 0.0f;
+                            for (int u = 0; u < 16; ++u)
+                                v[u] = sp0 + u < nsplit ? load_agent(pp + (int64_t)(sp0 + u) * stride) : 0.0f;
 #pragma unroll
-                        for (int u = 0; u < 16; ++u)
-                            if (sp0 + u < nsplit) s += v[u];
-                    }
-                    store_final(a, row * n_out + cg, s);
+                            for (int u = 0; u < 16; ++u)
+                                if (sp0 + u < nsplit) s += v[u];
+                        }
+                        return s;
+                    };
+                    const float s = split_sum(a.partial + row * n_out + cg);
+                    if constexpr (DUAL)
+                        reinterpret_cast<float*>(a.y)[row * n_out + cg] =
+                            relu2_glu(split_sum(a.partial2 + row * n_out + cg), s);
+                    else
+                        store_final(a, row * n_out + cg, s);
                 }
             }
             if (tid == 0) store_agent(&a.counters[ci], 0);
@@ -1023,11 +1062,11 @@ __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int 
 // not selected).  v_mfma_i32_32x32x32_i8 sums exactly in int32, so the
 // result is the same integer as any other order.
 // Workgroup: 64 tokens (two 32-row MFMA tiles) x 128 outputs (one 32-column
-// tile per wavefront) over a split of kT8Steps steps of 64 input features.
+// tile per wavefront) over a split of kT8Steps steps of 128 input features.
 // Every global load of the split is issued at the start (per thread and
-// step: 16 bytes of Qs and 8 packed bytes), so the steps only wait for data
-// already in flight.  Per step the workgroup stages A (64 tokens x 64
-// features, int8) and the decoded B tile ([k][n] int8, 64 x 128) in LDS; B
+// step: 32 bytes of Qs and 16 packed bytes), so the steps only wait for data
+// already in flight.  Per step the workgroup stages A (64 tokens x 128
+// features, int8) and the decoded B tile ([k][n] int8, 128 x 128) in LDS; B
 // rows have a 144-byte pitch so that the eight rows a transposing read
 // touches land on distinct banks, and each wavefront takes its B operand with
 // ds_read_b64_tr_b8 (in each group of 16 lanes, lane 2e + h addresses k-row
@@ -1313,6 +1352,32 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
     QS_GEMV_CASE(0, 1) QS_GEMV_CASE(0, 2) QS_GEMV_CASE(0, 4) QS_GEMV_CASE(0, 8)
 #undef QS_GEMV_CASE
     return hipErrorInvalidValue;
+}
+
+bool gemv_dual_supported(const GemvPlan& p) { return p.bt == 1 || p.bt == 2 || p.bt == 4; }
+
+hipError_t launch_gemv_dual(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    if (!gemv_dual_supported(p) || a.w2 == nullptr || (p.nsplit > 1 && a.partial2 == nullptr) ||
+        a.row_expert != nullptr)
+        return hipErrorNotSupported;
+    const int ept = w_is_bf16 ? 8 : 4;
+    const int ct = kFLPR * ept;
+    const int tg = p.bt < 2 ? p.bt : 2;
+    const dim3 grid(p.n_tiles, p.nsplit, p.n_tok_tiles);
+    const size_t padded = (size_t)p.cand + 3 * kFNSlot * kUnroll;
+    const size_t lds_a = padded * p.bt * 4 + padded * 4;
+    const size_t lds_c = (size_t)kFNSlot * tg * ct * 4;
+    const size_t lds = lds_a > lds_c ? lds_a : lds_c;
+#define QS_GEMV_DUAL_CASE(WB, BTV)                                                                \
+    if (w_is_bf16 == WB && p.bt == BTV) {                                                         \
+        gather_gemv_kernel<WB, BTV, true><<<grid, dim3(kNT), lds, stream>>>(a, p.cand, p.nsplit); \
+        return hipGetLastError();                                                                 \
+    }
+    QS_GEMV_DUAL_CASE(1, 1) QS_GEMV_DUAL_CASE(1, 2) QS_GEMV_DUAL_CASE(1, 4)
+    QS_GEMV_DUAL_CASE(0, 1) QS_GEMV_DUAL_CASE(0, 2) QS_GEMV_DUAL_CASE(0, 4)
+#undef QS_GEMV_DUAL_CASE
+    return hipErrorNotSupported;
 }
 
 I8tPlan plan_i8t(int64_t rows, int64_t d_in, int64_t n_out) {

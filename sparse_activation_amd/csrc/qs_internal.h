@@ -84,8 +84,18 @@ struct GemvArgs {
     int xs_bf16;           // 1: every xs value is a bf16 number (from bf16 activations)
     const int32_t* row_expert;  // null, or (one token per tile) row r reads the
     int64_t expert_bytes;       //   matrix at w + row_expert[r] * expert_bytes
+    // Gated pair (launch_gemv_dual): w2 = W_gate^T of the same shape as w, read
+    // at the same selected rows; y = relu(xs . w2)^2 * (xs . w), fp32.  Its
+    // split partials go to partial2 ([nsplit, rows, n_out]).
+    const void* w2;
+    float* partial2;
 };
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
+// Both projections of the gated squared ReLU in one gather (tiles of at most
+// four tokens); returns hipErrorNotSupported for plans that use the 16-token
+// MFMA kernels.
+bool gemv_dual_supported(const GemvPlan& p);
+hipError_t launch_gemv_dual(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- ternary x int8 gather
 struct I8tPlan {

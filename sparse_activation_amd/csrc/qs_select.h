@@ -179,7 +179,34 @@ __device__ __forceinline__ void radix_select(const uint32_t (&key)[EPT], uint32_
             if (m) s.cand[base + popc_below(bm)] = key[i];
         }
         __syncthreads();
-        if (wave == 0) {
+        if (wave == 0 && cnt <= (uint32_t)(2 * kWave)) {
+            // Few candidates (the usual case: a boundary bin of a 12-bit first
+            // digit holds tens of keys): two per lane in wave 0's registers.
+            // The remaining S1 bits are decided one at a time, most
+            // significant first; the live candidates are kept as two uniform
+            // ballot masks, so each bit costs one compare per register and a
+            // few scalar operations.
+            const uint32_t c0 = s.cand[lane < (int)cnt ? lane : 0];
+            const uint32_t c1 = s.cand[lane + kWave < (int)cnt ? lane + kWave : 0];
+            uint64_t live0 = __ballot(lane < (int)cnt);
+            uint64_t live1 = __ballot(lane + kWave < (int)cnt);
+#pragma unroll
+            for (int b = S1 - 1; b >= 0; --b) {
+                const uint64_t o0 = __ballot((c0 >> b) & 1u) & live0;
+                const uint64_t o1 = __ballot((c1 >> b) & 1u) & live1;
+                const uint32_t ones = (uint32_t)(__popcll(o0) + __popcll(o1));
+                if (kr <= ones) {   // uniform
+                    prefix |= 1u << b;
+                    live0 = o0;
+                    live1 = o1;
+                } else {
+                    kr -= ones;
+                    live0 &= ~o0;
+                    live1 &= ~o1;
+                }
+            }
+            if (lane == 0) { s.res[0] = prefix; s.res[1] = kr; s.res[2] = (uint32_t)(__popcll(live0) + __popcll(live1)); }
+        } else if (wave == 0) {
             const uint32_t ncand = cnt;
             int shift = S1, l = 0;
             while (shift > 0) {

@@ -116,7 +116,7 @@ def _relu2_glu_case(gpu_lib, x, wg, wu, wd, k_in, k_mid, wtype="bf16"):
     assert_within(y, down["y"], down["T_y"], tol, "relu2-glu y")
 
 
-@pytest.mark.parametrize("rows,d,f", [(1, 64, 96), (3, 256, 520), (17, 512, 264)])
+@pytest.mark.parametrize("rows,d,f", [(1, 64, 96), (2, 128, 200), (3, 256, 520), (17, 512, 264)])
 @pytest.mark.parametrize("wtype", ["f32", "bf16"])
 def test_relu2_glu_small(gpu_lib, rows, d, f, wtype):
     rng = np.random.default_rng(rows + 2 * d + f)
@@ -131,7 +131,7 @@ def test_relu2_glu_small(gpu_lib, rows, d, f, wtype):
         _relu2_glu_case(gpu_lib, x, wg, wu, wd, k_in, k_mid, wtype)
 
 
-@pytest.mark.parametrize("batch", [1, 8, 16])
+@pytest.mark.parametrize("batch", [1, 4, 8, 16])
 def test_relu2_glu_full_llama7b(gpu_lib, batch):
     c = datagen.c2g_relu2glu_ffn(batch)
     note(f"gated relu2 FFN, Llama-7B shape, B={batch}")

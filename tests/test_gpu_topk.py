@@ -84,3 +84,23 @@ def test_topk_full_configs(gpu_lib, cfg):
         x, k, kind = c["X"], c["K"], "bf16"
     note(f"topk full config {cfg} shape={x.shape} k={k}")
     _check(kind, x, k, _run(gpu_lib, kind, x, k))
+
+
+@pytest.mark.parametrize("nbin", [20, 64, 65, 128, 200, 256, 257, 600])
+def test_topk_boundary_bin_sizes(gpu_lib, nbin):
+    """fp32 rows whose threshold falls among nbin keys that share their top
+    12 bits (1 + i 2^-20 differ only in low mantissa bits), some of them
+    tied, so the select's last digits run over 1 to 4 register slots per lane
+    (nbin <= 256) or over its LDS histograms (more)."""
+    rng = np.random.default_rng(7000 + nbin)
+    d = 4096
+    big = 1200
+    x = np.full(d, 1e-3, dtype=np.float32)
+    x[:big] = 8.0 + rng.random(big).astype(np.float32)
+    i = rng.integers(0, 40, size=nbin)                    # values repeat: ties in the bin
+    x[big:big + nbin] = (1.0 + i * 2.0 ** -20).astype(np.float32)
+    x *= np.where(rng.random(d) < 0.5, -1.0, 1.0).astype(np.float32)
+    x = x[rng.permutation(d)][None, :].copy()
+    for k in sorted({big + 1, big + nbin // 3, big + nbin // 2, big + nbin - 1, big + nbin}):
+        note(f"topk boundary bin nbin={nbin} k={k}")
+        _check("f32", x, k, _run(gpu_lib, "f32", x, k))
