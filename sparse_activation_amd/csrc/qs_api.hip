@@ -164,11 +164,18 @@ struct MoeWs {
     int32_t* pair_token;
     int32_t* pair_expert;
     float* pair_weight;
+    int32_t* grp_count;
+    int32_t* grp_pairs;
+    int32_t* grp_tok;
     float* h;
     float* ypair;
     float* partial;
     size_t bytes;
 };
+
+// Batches with more pairs than this keep one launch row per pair (the
+// per-expert lists take 512 bytes per pair).
+constexpr int64_t kMoeGroupMaxPairs = 8192;
 
 MoeWs moe_ws(char* base, int64_t pairs, int64_t d, int64_t ffn) {
     qs::GemvPlan p = qs::plan_gemv(pairs, ffn, d, 1, 1);
@@ -180,6 +187,11 @@ MoeWs moe_ws(char* base, int64_t pairs, int64_t d, int64_t ffn) {
     w.pair_token = (int32_t*)c.take(sizeof(int32_t) * (size_t)pairs);
     w.pair_expert = (int32_t*)c.take(sizeof(int32_t) * (size_t)pairs);
     w.pair_weight = (float*)c.take(sizeof(float) * (size_t)pairs);
+    w.grp_count = (int32_t*)c.take(sizeof(int32_t) * 64);
+    if (pairs <= kMoeGroupMaxPairs) {
+        w.grp_pairs = (int32_t*)c.take(sizeof(int32_t) * 64 * (size_t)pairs);
+        w.grp_tok = (int32_t*)c.take(sizeof(int32_t) * 64 * (size_t)pairs);
+    }
     w.h = (float*)c.take(sizeof(float) * (size_t)pairs * ffn);
     w.ypair = (float*)c.take(sizeof(float) * (size_t)pairs * d);
     w.partial = (float*)c.take(sizeof(float) * p.scratch_floats);
@@ -683,7 +695,18 @@ qs_status qs_sparse_moe_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d,
     g.wg = (const uint16_t*)w_gate; g.wu = (const uint16_t*)w_up; g.bg = b_gate; g.bu = b_up;
     g.h = hbuf; g.zero_ptr = wsp.ctr; g.n_zero = wsp.n_ctr;
     g.pair_token = wsp.pair_token; g.pair_expert = wsp.pair_expert; g.pairs = pairs;
-    e = qs::launch_drelu_gate_up(g, st);
+    if (rows > 1 && pairs <= kMoeGroupMaxPairs && rows * d * 2 < (int64_t(1) << 31)) {
+        // Several tokens: group the pairs by expert so that each expert's gate
+        // rows are read once per chunk of its tokens, not once per pair.
+        e = qs::launch_moe_group(wsp.pair_expert, wsp.pair_token, pairs, (int)n_experts,
+                                 wsp.grp_count, wsp.grp_pairs, wsp.grp_tok, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        g.grp_count = wsp.grp_count; g.grp_pairs = wsp.grp_pairs; g.grp_tok = wsp.grp_tok;
+        g.n_experts = (int)n_experts;
+        e = qs::launch_drelu_grouped(g, st);
+    } else {
+        e = qs::launch_drelu_gate_up(g, st);
+    }
     if (e != hipSuccess) return hip_fail(e, fn);
 
     // Down: each pair gathers the rows of its expert's W_down^T where h != 0.

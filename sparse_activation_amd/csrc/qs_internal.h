@@ -176,8 +176,18 @@ struct DreluArgs {
     const int32_t* pair_token;
     const int32_t* pair_expert;
     int64_t pairs;
+    // Pairs grouped by expert (launch_drelu_grouped): expert e owns the
+    // grp_count[e] pair indices at grp_pairs[e * pairs ..], whose tokens are
+    // at grp_tok[e * pairs ..].
+    const int32_t* grp_count;
+    const int32_t* grp_pairs;
+    const int32_t* grp_tok;
+    int n_experts;
 };
 hipError_t launch_drelu_gate_up(const DreluArgs& a, hipStream_t stream);
+// MoE gate/up with the pairs of each expert processed together: every
+// expert's gate rows are read once per chunk of its tokens.
+hipError_t launch_drelu_grouped(const DreluArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- MoE routing and combine
 struct MoeRouteArgs {
@@ -193,6 +203,12 @@ struct MoeRouteArgs {
     float* out_weights;      // [rows, top_k] or null: copy of pair_weight
 };
 hipError_t launch_moe_route(const MoeRouteArgs& a, hipStream_t stream);
+// Lists the pairs of each expert: count[e] of them at list[e * pairs ..], their
+// tokens at tok[e * pairs ..] (the order inside an expert is not fixed, and
+// nothing computed from it depends on it).
+hipError_t launch_moe_group(const int32_t* pair_expert, const int32_t* pair_token, int64_t pairs,
+                            int n_experts, int32_t* count, int32_t* list, int32_t* tok,
+                            hipStream_t stream);
 hipError_t launch_moe_combine(const float* ypair, const float* pair_weight, int64_t rows,
                               int top_k, int64_t d, void* y, int y_bf16, hipStream_t stream);
 

@@ -656,6 +656,150 @@ __global__ __launch_bounds__(256) void drelu_gate_up_b1_kernel(DreluArgs a) {
     }
 }
 
+// Grouped MoE gate/up: workgroup (x, y) owns neurons 8x .. 8x + 7 of expert
+// y and runs them for every token routed to that expert, TC tokens at a time.
+// Per chunk the workgroup stages the TC token rows of x in LDS (rows past the
+// chunk are zero), then each wavefront loads its two gate rows (16-byte
+// slices per lane, as in the one-token kernel); the up rows are read only for
+// neurons whose gate is positive for some token of the chunk.  Each (neuron,
+// token) value is the same sum in the same order as in the one-token kernel,
+// so h does not depend on how the tokens are grouped.
+template <int NCH>
+__global__ __launch_bounds__(256) void drelu_grouped_kernel(DreluArgs a) {
+    constexpr int NPW = 2, TC = NCH <= 8 ? 4 : 2, RL = NCH * 512;   // RL: staged row length
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[TC][RL];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t d = a.d, ffn = a.ffn;
+    const int ex = blockIdx.y;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && a.zero_ptr != nullptr)
+        for (int i = tid; i < a.n_zero; i += 256) a.zero_ptr[i] = 0;
+    const int32_t* gq = a.grp_pairs + ex * a.pairs;
+    const int32_t* gt = a.grp_tok + ex * a.pairs;
+    const int cnt = a.grp_count[ex];
+    if (cnt == 0) return;   // uniform: no token chose this expert
+    const int64_t nb = ((int64_t)blockIdx.x * 4 + wave) * NPW;
+    const uint16_t* wgx = a.wg + ex * ffn * d;
+    const uint16_t* wux = a.wu + ex * ffn * d;
+    const float* bgx = a.bg != nullptr ? a.bg + ex * ffn : nullptr;
+    const float* bux = a.bu != nullptr ? a.bu + ex * ffn : nullptr;
+    constexpr uint32_t kOff = 0x80000000u;   // x and each expert matrix are below 2 GiB
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.x), (short)0, (int)(a.rows * d * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(wgx), (short)0, (int)(ffn * d * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ur = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(wux), (short)0, (int)(ffn * d * 2), 0x00020000);
+    auto row_off = [&](int64_t n, int i) -> uint32_t {
+        const int64_t k = (int64_t)i * 512 + 8 * lane;
+        return (n < ffn && k < d) ? (uint32_t)((n * d + k) * 2) : kOff;
+    };
+    auto xs = [&](int t, int i) {   // this lane's 8 features of run i of staged token t
+        return *reinterpret_cast<const u32x4*>(&s_x[t][i * 512 + 8 * lane]);
+    };
+    float bg[NPW], bu[NPW];
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+        bg[j] = (bgx != nullptr && nb + j < ffn) ? bgx[nb + j] : 0.0f;
+        bu[j] = (bux != nullptr && nb + j < ffn) ? bux[nb + j] : 0.0f;
+    }
+    constexpr int XPT = TC * RL / 8 / 256;   // 16-byte pieces of x staged per thread
+    for (int c0 = 0; c0 < cnt; c0 += TC) {
+        int32_t q[TC];
+        int64_t tokoff[TC];   // byte offset of each token's x row (uniform)
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+            const bool tv = c0 + t < cnt;
+            q[t] = tv ? gq[c0 + t] : -1;
+            tokoff[t] = tv ? (int64_t)gt[c0 + t] * d * 2 : -1;
+        }
+        u32x4 xp[XPT];
+#pragma unroll
+        for (int r = 0; r < XPT; ++r) {
+            const int ci = tid + 256 * r;
+            const int t = ci / (RL / 8);   // uniform per r: RL / 8 is a multiple of 256
+            const int64_t k = (int64_t)(ci % (RL / 8)) * 8;
+            xp[r] = __builtin_amdgcn_raw_buffer_load_b128(
+                xr, (tokoff[t] >= 0 && k < d) ? (uint32_t)(tokoff[t] + k * 2) : kOff, 0, 0);
+        }
+        __syncthreads();   // the previous chunk's reads of s_x are done
+#pragma unroll
+        for (int r = 0; r < XPT; ++r) {
+            const int ci = tid + 256 * r;
+            *reinterpret_cast<u32x4*>(&s_x[ci / (RL / 8)][(ci % (RL / 8)) * 8]) = xp[r];
+        }
+        // The gate rows are loaded after the (short, L2-resident) x staging,
+        // so that the staging registers are free again while they are in flight.
+        u32x4 wv[NPW][NCH];
+#pragma unroll
+        for (int j = 0; j < NPW; ++j)
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) wv[j][i] = __builtin_amdgcn_raw_buffer_load_b128(gr, row_off(nb + j, i), 0, 0);
+        __syncthreads();
+        // Token by token, so that only one token's slices are held (the
+        // scheduling barriers keep the LDS reads of the next token from
+        // being hoisted).  The empty asm statements mark the packed weights
+        // and slices as changed per token and neuron, so that their unpacked
+        // fp32 values (twice the registers) are not kept for reuse.
+        float g[NPW][TC];
+        bool need[NPW] = {};
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+#pragma unroll
+            for (int j = 0; j < NPW; ++j)
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) asm volatile("" : "+v"(wv[j][i]));
+            u32x4 xt[NCH];
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) xt[i] = xs(t, i);
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) {
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) asm volatile("" : "+v"(xt[i]));   // unpack per neuron
+                float s = 0.0f;
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) s = dot8(wv[j][i], xt[i], s);
+                g[j][t] = wave_sum(s) + bg[j];
+                need[j] = need[j] || (q[t] >= 0 && g[j][t] > 0.0f);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Up rows only where some token's gate is positive: the other lanes'
+        // offsets are out of range, so those loads move no data (and the
+        // gate rows are dead from here, whatever the branch).
+        u32x4 uw[NPW][NCH];
+#pragma unroll
+        for (int j = 0; j < NPW; ++j)
+#pragma unroll
+            for (int i = 0; i < NCH; ++i)
+                uw[j][i] = __builtin_amdgcn_raw_buffer_load_b128(ur, need[j] ? row_off(nb + j, i) : kOff, 0, 0);
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+#pragma unroll
+            for (int j = 0; j < NPW; ++j)
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) asm volatile("" : "+v"(uw[j][i]));
+            u32x4 xt[NCH];
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) xt[i] = xs(t, i);
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) {
+                float hv = 0.0f;
+                if (need[j] && q[t] >= 0 && g[j][t] > 0.0f) {
+#pragma unroll
+                    for (int i = 0; i < NCH; ++i) asm volatile("" : "+v"(xt[i]));
+                    float s = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < NCH; ++i) s = dot8(uw[j][i], xt[i], s);
+                    const float uv = wave_sum(s) + bu[j];
+                    hv = uv > 0.0f ? __fmul_rn(g[j][t], uv) : 0.0f;
+                }
+                if (lane == 0 && q[t] >= 0 && nb + j < ffn) a.h[(int64_t)q[t] * ffn + nb + j] = hv;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 // Nonzero entries of each row of h, ascending (Turbo Sparse summary, per-layer
 // zero-activation figure: only the active neurons enter W_down).
 __global__ __launch_bounds__(256) void nonzero_lists_kernel(const float* __restrict__ h, int64_t n,
@@ -756,6 +900,19 @@ hipError_t launch_drelu_gate_up(const DreluArgs& a, hipStream_t stream) {
         return hipGetLastError();
     }
     drelu_gate_up_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_drelu_grouped(const DreluArgs& a, hipStream_t stream) {
+    if (a.rows <= 0 || a.pairs <= 0) return hipSuccess;
+    if (a.d > 8192 || a.n_experts < 1 || a.n_experts > 64 || a.grp_count == nullptr ||
+        a.rows * a.d * 2 >= (int64_t(1) << 31) || a.ffn * a.d * 2 >= (int64_t(1) << 31))
+        return hipErrorInvalidValue;
+    const int nch = (int)((a.d + 511) / 512);
+    const dim3 grid((unsigned)((a.ffn + 7) / 8), (unsigned)a.n_experts);
+    if (nch <= 4) drelu_grouped_kernel<4><<<grid, dim3(256), 0, stream>>>(a);
+    else if (nch <= 8) drelu_grouped_kernel<8><<<grid, dim3(256), 0, stream>>>(a);
+    else drelu_grouped_kernel<16><<<grid, dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 

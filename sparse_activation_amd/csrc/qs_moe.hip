@@ -145,7 +145,40 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
     }
 }
 
+// One workgroup: expert e's pairs go to list[e * pairs + slot] with their
+// tokens in tok[e * pairs + slot], slots taken with LDS atomics, and the
+// counts to count[e].
+__global__ __launch_bounds__(256) void moe_group_kernel(const int32_t* __restrict__ pair_expert,
+                                                        const int32_t* __restrict__ pair_token,
+                                                        int64_t pairs, int n_experts,
+                                                        int32_t* __restrict__ count,
+                                                        int32_t* __restrict__ list,
+                                                        int32_t* __restrict__ tok) {
+    __shared__ uint32_t s_cnt[64];
+    const int tid = threadIdx.x;
+    if (tid < 64) s_cnt[tid] = 0;
+    __syncthreads();
+    for (int64_t q = tid; q < pairs; q += 256) {
+        const int e = pair_expert[q];
+        const int64_t slot = atomicAdd(&s_cnt[e], 1u);
+        list[e * pairs + slot] = (int32_t)q;
+        tok[e * pairs + slot] = pair_token[q];
+    }
+    __syncthreads();
+    if (tid < n_experts) count[tid] = (int32_t)s_cnt[tid];
+}
+
 }  // namespace
+
+hipError_t launch_moe_group(const int32_t* pair_expert, const int32_t* pair_token, int64_t pairs,
+                            int n_experts, int32_t* count, int32_t* list, int32_t* tok,
+                            hipStream_t stream) {
+    if (pairs <= 0) return hipSuccess;
+    if (n_experts < 1 || n_experts > 64) return hipErrorInvalidValue;
+    moe_group_kernel<<<dim3(1), dim3(256), 0, stream>>>(pair_expert, pair_token, pairs, n_experts,
+                                                        count, list, tok);
+    return hipGetLastError();
+}
 
 hipError_t launch_moe_route(const MoeRouteArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;

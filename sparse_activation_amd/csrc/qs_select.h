@@ -88,15 +88,20 @@ __device__ __forceinline__ void find_top_lane(const uint32_t* t, int n, uint32_t
 // the top min(KB, 12) key bits (4096 bins, so that the few exponent values an
 // activation spans spread over 16 bins each), the next ones 8 bits, every
 // level with its own histogram.
+// Keys of at most 20 bits (bf16, int8) have one 8-bit digit left at most, so
+// they need neither the candidate list nor more than one further histogram:
+// the smaller footprint lets more rows share a CU.
 template <int KB>
 struct SelectLds {
     static constexpr int W1 = KB < 12 ? KB : 12;
     static constexpr int S1 = KB - W1;
     static constexpr int NB1 = 1 << W1;
     static constexpr int NB1P = NB1 < 256 ? 256 : NB1;
+    static constexpr int NL = S1 > 8 ? 3 : 1;          // histograms after the first digit
+    static constexpr int NCAND = S1 > 8 ? kCap : 1;
     uint32_t h1[NB1P];
-    uint32_t hl[3][256];
-    uint32_t cand[kCap];
+    uint32_t hl[NL][256];
+    uint32_t cand[NCAND];
     uint32_t chunk[16];
     uint32_t res[4];
     uint32_t nc;
@@ -107,7 +112,7 @@ struct SelectLds {
 template <int NT, int KB>
 __device__ __forceinline__ void select_clear(SelectLds<KB>& s, int tid) {
     for (int i = tid; i < SelectLds<KB>::NB1P; i += NT) s.h1[i] = 0;
-    for (int i = tid; i < 3 * 256; i += NT) (&s.hl[0][0])[i] = 0;
+    for (int i = tid; i < SelectLds<KB>::NL * 256; i += NT) (&s.hl[0][0])[i] = 0;
     if (tid == 0) s.nc = 0;
 }
 
@@ -165,7 +170,10 @@ __device__ __forceinline__ void radix_select(const uint32_t (&key)[EPT], uint32_
     himask = (uint32_t)(NB1 - 1) << S1;
     // Remaining digits are 8 bits wide, each level with its own 256-bin
     // histogram hl[level], so no level clears a buffer.
-    if (S1 > 8 && cnt <= (uint32_t)kCap) {
+    bool compact = false;
+    if constexpr (S1 > 8) compact = cnt <= (uint32_t)kCap;
+    if (compact) {
+      if constexpr (S1 > 8) {
         // Several digits left over few keys: compact them (one LDS atomic per
         // wavefront and entry slot) and let wavefront 0 finish alone.
 #pragma unroll
@@ -226,6 +234,7 @@ __device__ __forceinline__ void radix_select(const uint32_t (&key)[EPT], uint32_
         }
         __syncthreads();
         prefix = s.res[0]; kr = s.res[1]; cnt = s.res[2];
+      }
     } else {
         // One digit left, or many keys (ties, zeros): all wavefronts count
         // each digit and search its 256 bins.

@@ -65,7 +65,7 @@ def _moe_case(qs, c, top_k, ydt=None):
 
 @pytest.mark.parametrize("rows,d,ffn,e,k", [(1, 256, 512, 8, 2), (3, 256, 520, 8, 2),
                                             (16, 512, 264, 8, 2), (5, 128, 136, 4, 1),
-                                            (4, 64, 48, 6, 3)])
+                                            (4, 64, 48, 6, 3), (12, 128, 136, 2, 1)])
 def test_moe_small(gpu_lib, rows, d, ffn, e, k):
     sigma = 0.02 * np.sqrt(2.0 * d)
     c = datagen.c6_moe_drelu_ffn(rows, d=d, ffn=ffn, n_experts=e, bias=-0.2864 * sigma)
