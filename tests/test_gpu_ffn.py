@@ -176,7 +176,8 @@ def _drelu_case(gpu_lib, x, wg, bg, wu, bu, wd, k_in=None, k_mid=-1):
     return float(np.mean(h == 0))
 
 
-@pytest.mark.parametrize("rows,d,f", [(1, 64, 48), (3, 256, 520), (16, 512, 264), (21, 200, 136)])
+@pytest.mark.parametrize("rows,d,f", [(1, 64, 48), (3, 256, 520), (4, 200, 136), (16, 512, 264),
+                                      (21, 200, 136)])
 def test_drelu_small(gpu_lib, rows, d, f):
     rng = np.random.default_rng(rows * 5 + d + f)
     x = datagen.bf16_round(datagen.student_t(rng, (rows, d)))
