@@ -187,9 +187,28 @@ __device__ __forceinline__ void radix_select(const uint32_t (&key)[EPT], uint32_
             if (m) s.cand[base + popc_below(bm)] = key[i];
         }
         __syncthreads();
-        if (wave == 0 && cnt <= (uint32_t)(2 * kWave)) {
-            // Few candidates (the usual case: a boundary bin of a 12-bit first
-            // digit holds tens of keys): two per lane in wave 0's registers.
+        if (wave == 0 && cnt <= (uint32_t)kWave) {
+            // At most one candidate per lane (the usual case: a boundary bin
+            // of a 12-bit first digit holds tens of keys): every lane counts
+            // the candidates above and equal to its own, broadcast one at a
+            // time; the kr-th largest is a candidate c with gt(c) < kr <=
+            // gt(c) + eq(c), and every lane holding that key finds the same.
+            const bool have = lane < (int)cnt;
+            const uint32_t c0 = s.cand[have ? lane : 0];
+            uint32_t gt = 0, eq = 0;
+            for (uint32_t j = 0; j < cnt; ++j) {   // uniform trip count
+                const uint32_t cj = (uint32_t)__builtin_amdgcn_readlane((int)c0, (int)j);
+                gt += cj > c0 ? 1u : 0u;
+                eq += cj == c0 ? 1u : 0u;
+            }
+            const uint64_t hit = __ballot(have && gt < kr && kr <= gt + eq);
+            const int src = (int)__builtin_ctzll(hit);
+            const uint32_t tv = (uint32_t)__builtin_amdgcn_readlane((int)c0, src);
+            const uint32_t gv = (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
+            const uint32_t ev = (uint32_t)__builtin_amdgcn_readlane((int)eq, src);
+            if (lane == 0) { s.res[0] = tv; s.res[1] = kr - gv; s.res[2] = ev; }
+        } else if (wave == 0 && cnt <= (uint32_t)(2 * kWave)) {
+            // Up to two candidates per lane in wave 0's registers.
             // The remaining S1 bits are decided one at a time, most
             // significant first; the live candidates are kept as two uniform
             // ballot masks, so each bit costs one compare per register and a
