@@ -859,6 +859,12 @@ constexpr int kI8CT = kI8LPR * kI8EPT;     // 256 columns per tile
 constexpr int kI8NSlot = 4 * (64 / kI8LPR);   // 32 row slots per workgroup
 constexpr int kI8MaxCand = 4096;           // candidate rows per split (LDS staging)
 constexpr int kI8TargetWG = 128;           // the whole matrix is a few MB: few, fuller workgroups
+// QS_I8T_TARGET_WG overrides the ternary gather's workgroup target (read once
+// per process; a tuning knob for measurements).
+int i8t_target_wg() {
+    static const int v = env_int("QS_I8T_TARGET_WG", kI8TargetWG, 1, 1 << 16);
+    return v;
+}
 static_assert(kI8CT == kNT, "the slot reduction gives each thread one column");
 
 template <int BT>
@@ -1406,7 +1412,7 @@ I8tPlan plan_i8t(int64_t rows, int64_t d_in, int64_t n_out) {
     p.n_tok_tiles = (int)ceil_div(rows, p.bt);
     const int cand_max = kI8MaxCand;
     const int64_t base = (int64_t)p.n_tiles * p.n_tok_tiles;
-    int64_t ns = ceil_div(kI8TargetWG, base);
+    int64_t ns = ceil_div(i8t_target_wg(), base);
     if (ns < 1) ns = 1;
     int64_t cand = ceil_div(ceil_div(d_in, ns), 64) * 64;
     if (cand > cand_max) cand = cand_max;
