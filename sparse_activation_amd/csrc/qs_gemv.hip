@@ -673,6 +673,10 @@ __global__ __launch_bounds__(kNT) void bfrag_kernel(const float* xs, int64_t row
 // loads columns 8 c8 .. 8 c8 + 7 of rows 4 r8 .. 4 r8 + 3 of the group (whole
 // 128-byte row segments), which a per-wave LDS tile turns into the k-major B
 // operand.  The row mask of a group is fetched one stage ahead of its weights.
+// FUSED: no packed records; each lane loads its 8 coefficients of a group two
+// stages ahead and forms its fragments and the group's row mask itself, as
+// bfrag_kernel does (the same values, so the same result).
+template <bool FUSED>
 __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf, int cand, int nsplit,
                                                           int use_lo) {
     constexpr int BT = 16;
@@ -718,6 +722,45 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
         f[0] = __builtin_amdgcn_raw_buffer_load_b128(frr, fo, 0, 0);
         f[1] = __builtin_amdgcn_raw_buffer_load_b128(frr, use_lo ? fo + 64 * 16 : kOOB, 0, 0);
     };
+    // FUSED: lane (kq, n16) holds coefficients 8 kq .. 8 kq + 7 of the group
+    // for token n16 (the A-operand layout of bfrag_kernel).
+    const int64_t d_in = a.d_in;
+    const int64_t ntok = min((int64_t)BT, rows - tok0);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.xs + tok0 * d_in), (short)0, (int)(ntok * d_in * 4), 0x00020000);
+    auto load_x = [&](u32x4* x, int s) {
+        const int64_t g = g0 + 4 * s + wave;
+        const int64_t j = g * kBGroup + 8 * kq;
+        const uint32_t o = (n16 < ntok && 4 * s + wave < gl) ? (uint32_t)((n16 * d_in + j) * 4) : kOOB;
+        x[0] = __builtin_amdgcn_raw_buffer_load_b128(xr, o, 0, 0);
+        x[1] = __builtin_amdgcn_raw_buffer_load_b128(xr, o == kOOB ? kOOB : o + 16, 0, 0);
+    };
+    auto convert = [&](const u32x4* x, u32x4* f, uint32_t& m, int s) {
+        const int64_t j = (g0 + 4 * s + wave) * kBGroup + 8 * kq;
+        const uint32_t u[8] = {x[0].x, x[0].y, x[0].z, x[0].w, x[1].x, x[1].y, x[1].z, x[1].w};
+        uint32_t hw[4], lw[4], rowbits = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float c = j + e < d_in ? __uint_as_float(u[e]) : 0.0f;
+            const uint32_t hi = f32_to_bf16_rne(c);
+            const uint32_t lo = f32_to_bf16_rne(c - __uint_as_float(hi << 16));
+            if (e & 1) {
+                hw[e >> 1] |= hi << 16;
+                lw[e >> 1] |= lo << 16;
+            } else {
+                hw[e >> 1] = hi;
+                lw[e >> 1] = lo;
+            }
+            const uint64_t b = __ballot(c != 0.0f);
+            rowbits |= (uint32_t)((b & 0xFFFFull) ? 1u : 0u) << e;
+            rowbits |= (uint32_t)(((b >> 16) & 0xFFFFull) ? 1u : 0u) << (8 + e);
+            rowbits |= (uint32_t)(((b >> 32) & 0xFFFFull) ? 1u : 0u) << (16 + e);
+            rowbits |= (uint32_t)(((b >> 48) & 0xFFFFull) ? 1u : 0u) << (24 + e);
+        }
+        f[0] = (u32x4){hw[0], hw[1], hw[2], hw[3]};
+        f[1] = (u32x4){lw[0], lw[1], lw[2], lw[3]};
+        m = rowbits;
+    };
     f32x4_t acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -751,6 +794,37 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
     // The first two stages load every row without waiting for their masks
     // (a skipped row only saves bandwidth; its coefficients are zero).
     u32x4 wa[4], wb[4], fa[2], fb[2];
+    if constexpr (FUSED) {
+        // The same schedule with the coefficients in place of the records:
+        // those of stage s + 2 are converted just before its weights are
+        // loaded (their mask decides which rows move).
+        u32x4 xa[2], xb[2], xc[2], xd[2];
+        uint32_t ma, mb, mc, md;
+        load_x(xa, 0);
+        load_x(xb, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(wa, 0xFFFFFFFFu, 0);
+        load_x(xc, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(wb, 0xFFFFFFFFu, 1);
+        load_x(xd, 3);
+        convert(xa, fa, ma, 0);
+        convert(xb, fb, mb, 1);
+        for (int s = 0; s < nst; s += 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_stage(wa, fa, ma, s);
+            __builtin_amdgcn_sched_barrier(0);
+            convert(xc, fa, ma, s + 2);
+            load_w(wa, ma, s + 2);
+            load_x(xc, s + 4);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_stage(wb, fb, mb, s + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            convert(xd, fb, mb, s + 3);
+            load_w(wb, mb, s + 3);
+            load_x(xd, s + 5);
+        }
+    } else {
     uint32_t ma = load_mask(0), mb = load_mask(1);
     __builtin_amdgcn_sched_barrier(0);
     load_w(wa, 0xFFFFFFFFu, 0);
@@ -775,6 +849,7 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
         load_f(fb, s + 3);
         mb = md;
         md = load_mask(s + 5);
+    }
     }
     __syncthreads();   // the transpose tiles are dead: reuse them for the wave reduction
 
@@ -1333,9 +1408,20 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
         const BFrag bf = bfrag_carve(reinterpret_cast<char*>(a.partial) + (p.partial_floats * 4 + 255) / 256 * 256,
                                      a.d_in, p.n_tok_tiles);
         const int use_lo = a.xs_bf16 ? 0 : 1;
+        // Forming the fragments inside the gather converts each group once
+        // per column tile instead of once, but saves the packing launch: it
+        // pays for a half-empty tile (8 tokens: 65.4 us per Llama-7B FFN step
+        // against 67.1), not for a full one (69.2 against 68.6).
+        // QS_BMFMA_FUSED=0/1 forces either (a tuning knob for measurements).
+        const char* fe = getenv("QS_BMFMA_FUSED");
+        const bool fused = fe ? fe[0] == '1' : a.rows <= 8;
+        if (fused) {
+            gather_bmfma_kernel<true><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
+            return hipGetLastError();
+        }
         bfrag_kernel<<<dim3((unsigned)ceil_div(bf.groups, 4), p.n_tok_tiles), dim3(kNT), 0, stream>>>(
             a.xs, a.rows, a.d_in, use_lo, bf);
-        gather_bmfma_kernel<<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
+        gather_bmfma_kernel<false><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
         return hipGetLastError();
     }
     if (p.bt == 16) {
