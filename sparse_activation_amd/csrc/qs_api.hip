@@ -490,6 +490,7 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
             if (e != hipSuccess) return hip_fail(e, fn);
             g.epilogue = qs::EPI_RELU2_GLU;
             g.gate = wsp.hs;
+            g.frag_ready = 1;   // the gate gather packed the same coefficients
             e = qs::launch_gemv(pu, wb, g, st);
             if (e != hipSuccess) return hip_fail(e, fn);
         } else {

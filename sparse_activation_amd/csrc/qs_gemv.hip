@@ -1419,8 +1419,9 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
             gather_bmfma_kernel<true><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
             return hipGetLastError();
         }
-        bfrag_kernel<<<dim3((unsigned)ceil_div(bf.groups, 4), p.n_tok_tiles), dim3(kNT), 0, stream>>>(
-            a.xs, a.rows, a.d_in, use_lo, bf);
+        if (!a.frag_ready)
+            bfrag_kernel<<<dim3((unsigned)ceil_div(bf.groups, 4), p.n_tok_tiles), dim3(kNT), 0, stream>>>(
+                a.xs, a.rows, a.d_in, use_lo, bf);
         gather_bmfma_kernel<false><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
         return hipGetLastError();
     }

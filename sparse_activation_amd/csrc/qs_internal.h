@@ -89,6 +89,10 @@ struct GemvArgs {
     // split partials go to partial2 ([nsplit, rows, n_out]).
     const void* w2;
     float* partial2;
+    // 16-token bf16 tiles: the packed coefficient records behind `partial`
+    // were written by a previous gather over the same xs (and plan), so the
+    // packing launch is skipped.
+    int frag_ready;
 };
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 // Both projections of the gated squared ReLU in one gather (tiles of at most
