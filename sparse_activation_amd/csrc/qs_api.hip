@@ -471,12 +471,12 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
         g.partial = wsp.partial; g.counters = wsp.ctr_up; g.y = hbuf; g.y_bf16 = 0;
         g.epilogue = qs::EPI_RELU2;
         g.xs_bf16 = dt == QS_BF16;
-        if (act == QS_ACT_RELU2_GLU && qs::gemv_dual_supported(pu)) {
+        if (act == QS_ACT_RELU2_GLU && qs::gemv_dual_supported(pu, wb)) {
             // Both projections in one gather: the gate's and the up rows of
             // each selected feature are streamed together, and the last
             // split forms h = relu(g)^2 * u.
             g.w2 = w_gate;
-            g.partial2 = wsp.partial + (pu.partial_floats * 4 + 255) / 256 * 64;
+            g.partial2 = wsp.partial + pu.scratch_floats;   // behind the partials and records
             e = qs::launch_gemv_dual(pu, wb, g, st);
             if (e != hipSuccess) return hip_fail(e, fn);
         } else if (act == QS_ACT_RELU2_GLU) {

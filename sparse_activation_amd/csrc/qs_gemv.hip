@@ -676,13 +676,16 @@ __global__ __launch_bounds__(kNT) void bfrag_kernel(const float* xs, int64_t row
 // FUSED: no packed records; each lane loads its 8 coefficients of a group two
 // stages ahead and forms its fragments and the group's row mask itself, as
 // bfrag_kernel does (the same values, so the same result).
-template <bool FUSED>
+// DUAL: a second matrix (a.w2, the gate) is streamed at the same rows with the
+// same A fragments into a second set of sums; y = relu2_glu(gate, up).
+template <bool FUSED, bool DUAL = false>
 __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf, int cand, int nsplit,
                                                           int use_lo) {
     constexpr int BT = 16;
     constexpr int OPT = BT * kBCols / kNT;    // outputs per thread in the reductions (4)
-    // 16 KB in all: the split-K arrival flag reuses the tile once it is dead.
-    __shared__ __attribute__((aligned(16))) uint16_t s_tr[4 * kBGroup * kBCols];
+    constexpr int NM = DUAL ? 2 : 1;
+    // 16 KB per matrix: the split-K arrival flag reuses the tiles once they are dead.
+    __shared__ __attribute__((aligned(16))) uint16_t s_tr[NM * 4 * kBGroup * kBCols];
 
     const int tile = blockIdx.x, split = blockIdx.y, tt = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -702,20 +705,27 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
     const uint32_t colb = col < n_out ? (uint32_t)(col * 2) : kOOB;
     const uint32_t rowbytes = (uint32_t)(n_out * 2);
     const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, a.d_in * n_out * 2);
+    const __amdgpu_buffer_rsrc_t rs2 = weight_rsrc(DUAL ? a.w2 : a.w, a.d_in * n_out * 2);
     // Byte offset of row 4 r8 of group 0 of the split.
     const uint32_t rowb0 = (uint32_t)((g0 * kBGroup + 4 * r8) * rowbytes);
     uint16_t* tr = s_tr + wave * kBGroup * kBCols;
+    uint16_t* tr2 = s_tr + (DUAL ? 4 * kBGroup * kBCols : 0) + wave * kBGroup * kBCols;
 
     auto load_mask = [&](int s) {
         return __builtin_amdgcn_raw_buffer_load_b32(mrr, (uint32_t)((4 * s + wave) * 4), 0, 0);
     };
+    // w[0 .. 3]: the four rows of matrix w; w[4 .. 7] (dual): the same rows of w2.
     auto load_w = [&](u32x4* w, uint32_t m, int s) {
         const uint32_t rb = rowb0 + (uint32_t)((4 * s + wave) * kBGroup) * rowbytes + colb;
         const uint32_t bits = m >> (4 * r8);
-        w[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, bits & 1u ? rb : kOOB, 0, 0);
-        w[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, bits & 2u ? rb + rowbytes : kOOB, 0, 0);
-        w[2] = __builtin_amdgcn_raw_buffer_load_b128(rs, bits & 4u ? rb + 2 * rowbytes : kOOB, 0, 0);
-        w[3] = __builtin_amdgcn_raw_buffer_load_b128(rs, bits & 8u ? rb + 3 * rowbytes : kOOB, 0, 0);
+        const uint32_t o[4] = {bits & 1u ? rb : kOOB, bits & 2u ? rb + rowbytes : kOOB,
+                               bits & 4u ? rb + 2 * rowbytes : kOOB, bits & 8u ? rb + 3 * rowbytes : kOOB};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, o[q], 0, 0);
+        if constexpr (DUAL) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[4 + q] = __builtin_amdgcn_raw_buffer_load_b128(rs2, o[q], 0, 0);
+        }
     };
     auto load_f = [&](u32x4* f, int s) {
         const uint32_t fo = (uint32_t)(((4 * s + wave) * 128 + lane) * 16);
@@ -761,15 +771,16 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
         f[1] = (u32x4){lw[0], lw[1], lw[2], lw[3]};
         m = rowbits;
     };
-    f32x4_t acc[4];
+    f32x4_t acc[NM][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    auto mfma_stage = [&](const u32x4* w, const u32x4* f, uint32_t m, int s) {
-        if (4 * s + wave >= gl || __builtin_amdgcn_readfirstlane(m) == 0) return;
+    for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[mi][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    auto mfma_one = [&](const u32x4* w, uint16_t* trp, f32x4_t* ac, const u32x4* f) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int row = 4 * r8 + q;
-            *reinterpret_cast<u32x4*>(tr + row * kBCols + ((c8 ^ (2 * (row >> 3))) * 8)) = w[q];
+            *reinterpret_cast<u32x4*>(trp + row * kBCols + ((c8 ^ (2 * (row >> 3))) * 8)) = w[q];
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -777,23 +788,28 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
             uint32_t bw[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t lo16 = tr[(8 * kq + 2 * e) * kBCols + cidx];
-                const uint32_t hi16 = tr[(8 * kq + 2 * e + 1) * kBCols + cidx];
+                const uint32_t lo16 = trp[(8 * kq + 2 * e) * kBCols + cidx];
+                const uint32_t hi16 = trp[(8 * kq + 2 * e + 1) * kBCols + cidx];
                 bw[e] = lo16 | (hi16 << 16);
             }
             const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, (u32x4){bw[0], bw[1], bw[2], bw[3]});
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f[0]), bv,
-                                                            acc[t], 0, 0, 0);
+            ac[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f[0]), bv,
+                                                           ac[t], 0, 0, 0);
             if (use_lo)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f[1]),
-                                                                bv, acc[t], 0, 0, 0);
+                ac[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f[1]),
+                                                               bv, ac[t], 0, 0, 0);
         }
+    };
+    auto mfma_stage = [&](const u32x4* w, const u32x4* f, uint32_t m, int s) {
+        if (4 * s + wave >= gl || __builtin_amdgcn_readfirstlane(m) == 0) return;
+        mfma_one(w, tr, acc[0], f);
+        if constexpr (DUAL) mfma_one(w + 4, tr2, acc[NM - 1], f);
     };
     // The prologue issues the loads in the loop's own order, so the wait
     // counts at the loop head are the steady-state ones.
     // The first two stages load every row without waiting for their masks
     // (a skipped row only saves bandwidth; its coefficients are zero).
-    u32x4 wa[4], wb[4], fa[2], fb[2];
+    u32x4 wa[4 * NM], wb[4 * NM], fa[2], fb[2];
     if constexpr (FUSED) {
         // The same schedule with the coefficients in place of the records:
         // those of stage s + 2 are converted just before its weights are
@@ -854,29 +870,44 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
     __syncthreads();   // the transpose tiles are dead: reuse them for the wave reduction
 
     // Phase C: register v of MFMA t is token 4 kq + v, column 16 t + n16.
-    float* s_red = reinterpret_cast<float*>(s_tr);   // [4][16][64]
+    float* s_red = reinterpret_cast<float*>(s_tr);   // [NM][4][16][64]
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            s_red[(wave * BT + 4 * kq + v) * kBCols + 16 * t + n16] = acc[t][v];
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                s_red[((mi * 4 + wave) * BT + 4 * kq + v) * kBCols + 16 * t + n16] = acc[mi][t][v];
     __syncthreads();
-    float outv[OPT];
+    float outv[NM][OPT];
 #pragma unroll
-    for (int q = 0; q < OPT; ++q) {
-        const int o = q * kNT + tid;
-        float sum = s_red[o];
+    for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-        for (int w = 1; w < 4; ++w) sum += s_red[w * BT * kBCols + o];
-        outv[q] = sum;
-    }
+        for (int q = 0; q < OPT; ++q) {
+            const int o = q * kNT + tid;
+            const float* sr = s_red + mi * 4 * BT * kBCols;
+            float sum = sr[o];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) sum += sr[w * BT * kBCols + o];
+            outv[mi][q] = sum;
+        }
 #pragma unroll
     for (int q = 0; q < OPT; ++q) {
         const int o = q * kNT + tid;
         const int64_t row = tok0 + o / kBCols, cg = (int64_t)tile * kBCols + (o % kBCols);
         if (row < rows && cg < n_out) {
-            if (nsplit == 1) store_final(a, row * n_out + cg, outv[q]);
-            else store_agent(&a.partial[((int64_t)split * rows + row) * n_out + cg], outv[q]);
+            const int64_t i = row * n_out + cg, pi = ((int64_t)split * rows + row) * n_out + cg;
+            if constexpr (DUAL) {
+                if (nsplit == 1) {
+                    reinterpret_cast<float*>(a.y)[i] = relu2_glu(outv[1][q], outv[0][q]);
+                } else {
+                    store_agent(&a.partial[pi], outv[0][q]);
+                    store_agent(&a.partial2[pi], outv[1][q]);
+                }
+            } else {
+                if (nsplit == 1) store_final(a, i, outv[0][q]);
+                else store_agent(&a.partial[pi], outv[0][q]);
+            }
         }
     }
 
@@ -896,23 +927,36 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
                 base[q] = ok[q] ? row * n_out + cg : 0;
                 sum[q] = 0.0f;
             }
-            for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
-                float v[8][OPT];
+            auto split_sums = [&](const float* part, float* sm) {
+                for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {
+                    float v[8][OPT];
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
+                    for (int u = 0; u < 8; ++u)
 #pragma unroll
-                    for (int q = 0; q < OPT; ++q)
-                        v[u][q] = (sp0 + u < nsplit && ok[q])
-                                      ? load_agent(a.partial + (int64_t)(sp0 + u) * stride + base[q]) : 0.0f;
+                        for (int q = 0; q < OPT; ++q)
+                            v[u][q] = (sp0 + u < nsplit && ok[q])
+                                          ? load_agent(part + (int64_t)(sp0 + u) * stride + base[q]) : 0.0f;
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
+                    for (int u = 0; u < 8; ++u)
 #pragma unroll
-                    for (int q = 0; q < OPT; ++q)
-                        if (sp0 + u < nsplit) sum[q] += v[u][q];
+                        for (int q = 0; q < OPT; ++q)
+                            if (sp0 + u < nsplit) sm[q] += v[u][q];
+                }
+            };
+            split_sums(a.partial, sum);
+            if constexpr (DUAL) {
+                float gs[OPT];
+#pragma unroll
+                for (int q = 0; q < OPT; ++q) gs[q] = 0.0f;
+                split_sums(a.partial2, gs);
+#pragma unroll
+                for (int q = 0; q < OPT; ++q)
+                    if (ok[q]) reinterpret_cast<float*>(a.y)[base[q]] = relu2_glu(gs[q], sum[q]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < OPT; ++q)
+                    if (ok[q]) store_final(a, base[q], sum[q]);
             }
-#pragma unroll
-            for (int q = 0; q < OPT; ++q)
-                if (ok[q]) store_final(a, base[q], sum[q]);
             if (tid == 0) store_agent(&a.counters[ci], 0);
         }
     }
@@ -1449,13 +1493,31 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
     return hipErrorInvalidValue;
 }
 
-bool gemv_dual_supported(const GemvPlan& p) { return p.bt == 1 || p.bt == 2 || p.bt == 4; }
+bool gemv_dual_supported(const GemvPlan& p, int w_is_bf16) {
+    return p.bt == 1 || p.bt == 2 || p.bt == 4 || (p.bt == 16 && w_is_bf16);
+}
 
 hipError_t launch_gemv_dual(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
-    if (!gemv_dual_supported(p) || a.w2 == nullptr || (p.nsplit > 1 && a.partial2 == nullptr) ||
+    if (!gemv_dual_supported(p, w_is_bf16) || a.w2 == nullptr || (p.nsplit > 1 && a.partial2 == nullptr) ||
         a.row_expert != nullptr)
         return hipErrorNotSupported;
+    if (p.bt == 16) {   // bf16 weights: the 16-token MFMA gather with both matrices
+        const dim3 grid(p.n_tiles, p.nsplit, p.n_tok_tiles);
+        const BFrag bf = bfrag_carve(reinterpret_cast<char*>(a.partial) + (p.partial_floats * 4 + 255) / 256 * 256,
+                                     a.d_in, p.n_tok_tiles);
+        const int use_lo = a.xs_bf16 ? 0 : 1;
+        const char* fe = getenv("QS_BMFMA_FUSED");
+        const bool fused = fe ? fe[0] == '1' : a.rows <= 8;
+        if (fused) {
+            gather_bmfma_kernel<true, true><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
+            return hipGetLastError();
+        }
+        bfrag_kernel<<<dim3((unsigned)ceil_div(bf.groups, 4), p.n_tok_tiles), dim3(kNT), 0, stream>>>(
+            a.xs, a.rows, a.d_in, use_lo, bf);
+        gather_bmfma_kernel<false, true><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
+        return hipGetLastError();
+    }
     const int ept = w_is_bf16 ? 8 : 4;
     const int ct = kFLPR * ept;
     const int tg = p.bt < 2 ? p.bt : 2;

@@ -96,9 +96,9 @@ struct GemvArgs {
 };
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 // Both projections of the gated squared ReLU in one gather (tiles of at most
-// four tokens); returns hipErrorNotSupported for plans that use the 16-token
-// MFMA kernels.
-bool gemv_dual_supported(const GemvPlan& p);
+// four tokens, or 16-token tiles of bf16 weights); returns hipErrorNotSupported
+// for other plans.  partial2 must not overlap the scratch behind partial.
+bool gemv_dual_supported(const GemvPlan& p, int w_is_bf16);
 hipError_t launch_gemv_dual(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- ternary x int8 gather
