@@ -450,13 +450,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_deep_kernel(
 // up projection, so h = relu(g) * relu(u) is zero wherever g <= 0).
 //
 // One workgroup owns 16 neurons; its four wavefronts split the model
-// dimension (k-steps of 32 dealt round-robin) and each computes a 16 tokens x
-// 16 neurons partial product with v_mfma_f32_16x16x32_bf16 (A = tokens, rows
-// past the batch are zero and load nothing; B = 16 rows of W).  The partials
-// are summed in LDS in wave order, the bias is added, and the up projection
-// is then computed only for neurons with g > 0 for some token of the tile:
-// lanes of inactive neurons issue no loads, so the rows of W_up of inactive
-// neurons are never read.
+// dimension (a contiguous quarter of the k-steps each) and each computes a
+// 16 tokens x 16 neurons partial product with v_mfma_f32_16x16x32_bf16 (A =
+// tokens, rows past the batch are zero and load nothing; B = 16 rows of W).
+// The partials are summed in LDS in wave order, the bias is added, and the up
+// projection is then computed only for neurons with g > 0 for some token of
+// the tile: lanes of inactive neurons issue no loads, so the rows of W_up of
+// inactive neurons are never read.
 // ---------------------------------------------------------------------------
 
 constexpr int kDreluUnroll = 8;
@@ -478,13 +478,18 @@ __device__ __forceinline__ void drelu_partial(const uint16_t* __restrict__ x, in
         const_cast<uint16_t*>(w_tile), (short)0, (int)(n_tile * d * 2), 0x00020000);
     const uint32_t xrow = (uint32_t)(r16 * d * 2);   // this lane's token row / neuron row
     const int nsteps = (int)((d + 31) / 32);
-    for (int s0 = wave; s0 < nsteps; s0 += 4 * kDreluUnroll) {
+    // Wave w takes a contiguous quarter of the k-steps, kDreluUnroll at a time,
+    // so its back-to-back loads read long runs of each row (512 bytes per
+    // neuron per group) rather than 64-byte pieces shared out among waves.
+    const int per = (nsteps + 3) / 4;
+    const int s_end = min(nsteps, (wave + 1) * per);
+    for (int s0 = wave * per; s0 < s_end; s0 += kDreluUnroll) {
         u32x4 av[kDreluUnroll], bv[kDreluUnroll];
 #pragma unroll
         for (int u = 0; u < kDreluUnroll; ++u) {
-            const int s = s0 + 4 * u;
+            const int s = s0 + u;
             const int64_t k = (int64_t)s * 32 + kg * 8;
-            const bool in = s < nsteps && k < d;
+            const bool in = s < s_end && k < d;
             av[u] = __builtin_amdgcn_raw_buffer_load_b128(xrs, in ? xrow + (uint32_t)(k * 2) : kOff, 0, 0);
             bv[u] = __builtin_amdgcn_raw_buffer_load_b128(
                 wrs, in && load_w ? xrow + (uint32_t)(k * 2) : kOff, 0, 0);
