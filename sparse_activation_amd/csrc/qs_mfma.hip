@@ -459,50 +459,80 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_deep_kernel(
 // inactive neurons are never read.
 // ---------------------------------------------------------------------------
 
-constexpr int kDreluUnroll = 8;
+// Each wave takes a contiguous quarter of d in stages of 128 features: per
+// stage it loads 256 contiguous bytes of each of the 16 neuron rows (four
+// lanes per row, 64 bytes each), writes them to its LDS tile (rows 272
+// bytes apart, so both the 16-byte writes and the fragment reads below are
+// free of bank conflicts) and reads the MFMA B operand from there; the x
+// fragments (16 tokens, L2-resident) come straight from memory.  Two
+// register stages keep the next stage's loads in flight.  LDS instructions
+// of one wave complete in order, so a stage's tile writes follow the
+// previous stage's reads.
+constexpr int kDreluStageK = 128;                 // features per stage
+constexpr int kDreluPitch = kDreluStageK + 8;     // tile row pitch in bf16 (272 bytes)
 
 // w_tile = the workgroup's first neuron row, n_tile = neurons of the tile that
-// exist (both uniform); lanes with load_w == false read zeros.
+// exist (both uniform); only rows whose bit is set in wmask are read.
 __device__ __forceinline__ void drelu_partial(const uint16_t* __restrict__ x, int64_t rows,
                                               int64_t tok0, int64_t d,
                                               const uint16_t* __restrict__ w_tile, int64_t n_tile,
-                                              bool load_w, int wave, int lane, f32x4& acc) {
-    // Buffer views: loads never branch, and rows past the batch, lanes of
-    // inactive neurons and k past the row end read zero.
-    const int r16 = lane & 15, kg = lane >> 4;
+                                              uint32_t wmask, int wave, int lane, f32x4& acc,
+                                              uint16_t* __restrict__ tile) {
+    // Buffer views: loads never branch, and rows past the batch, inactive
+    // neurons and k past the row end read zero.
+    const int r16 = lane & 15, kg = lane >> 4;          // MFMA lanes: row / k group
+    const int wr = lane >> 2, wsg = lane & 3;            // loading lanes: row / 64-byte segment
     constexpr uint32_t kOff = 0x40000000u;   // out of range for both views
     const int64_t ntok = min((int64_t)16, rows - tok0);
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(x + tok0 * d), (short)0, (int)(ntok * d * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(w_tile), (short)0, (int)(n_tile * d * 2), 0x00020000);
-    const uint32_t xrow = (uint32_t)(r16 * d * 2);   // this lane's token row / neuron row
-    const int nsteps = (int)((d + 31) / 32);
-    // Wave w takes a contiguous quarter of the k-steps, kDreluUnroll at a time,
-    // so its back-to-back loads read long runs of each row (512 bytes per
-    // neuron per group) rather than 64-byte pieces shared out among waves.
-    const int per = (nsteps + 3) / 4;
-    const int s_end = min(nsteps, (wave + 1) * per);
-    for (int s0 = wave * per; s0 < s_end; s0 += kDreluUnroll) {
-        u32x4 av[kDreluUnroll], bv[kDreluUnroll];
+    const bool wload = ((wmask >> wr) & 1u) != 0u;
+    const int nst = (int)((d + kDreluStageK - 1) / kDreluStageK);
+    const int per = (nst + 3) / 4;
+    const int st0 = wave * per, st1 = min(nst, st0 + per);
+    auto load = [&](u32x4* wv, u32x4* xv, int st) {
+        const int64_t k0 = (int64_t)st * kDreluStageK;
+        const bool in = st < st1;
 #pragma unroll
-        for (int u = 0; u < kDreluUnroll; ++u) {
-            const int s = s0 + u;
-            const int64_t k = (int64_t)s * 32 + kg * 8;
-            const bool in = s < s_end && k < d;
-            av[u] = __builtin_amdgcn_raw_buffer_load_b128(xrs, in ? xrow + (uint32_t)(k * 2) : kOff, 0, 0);
-            bv[u] = __builtin_amdgcn_raw_buffer_load_b128(
-                wrs, in && load_w ? xrow + (uint32_t)(k * 2) : kOff, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            const int64_t kw = k0 + 32 * wsg + 8 * i;
+            wv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                wrs, in && wload && kw < d ? (uint32_t)((wr * d + kw) * 2) : kOff, 0, 0);
+            const int64_t kx = k0 + 32 * i + 8 * kg;
+            xv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                xrs, in && kx < d ? (uint32_t)((r16 * d + kx) * 2) : kOff, 0, 0);
         }
+    };
+    auto compute = [&](const u32x4* wv, const u32x4* xv) {
 #pragma unroll
-        for (int u = 0; u < kDreluUnroll; ++u)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[u]), as_bf16x8(bv[u]), acc,
-                                                          0, 0, 0);
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x4*>(tile + wr * kDreluPitch + 32 * wsg + 8 * i) = wv[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 bv = *reinterpret_cast<const u32x4*>(tile + r16 * kDreluPitch + 32 * i + 8 * kg);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[i]), as_bf16x8(bv), acc, 0, 0, 0);
+        }
+    };
+    u32x4 wa[4], xa[4], wb[4], xb[4];
+    load(wa, xa, st0);
+    for (int st = st0; st < st1; st += 2) {
+        load(wb, xb, st + 1);   // past the quarter: out of range, no data moved
+        __builtin_amdgcn_sched_barrier(0);
+        compute(wa, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 1 >= st1) break;   // uniform
+        load(wa, xa, st + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(wb, xb);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 __global__ __launch_bounds__(256) void drelu_gate_up_kernel(DreluArgs a) {
     __shared__ f32x4 s_part[4][64];
+    __shared__ __attribute__((aligned(16))) uint16_t s_tile[4][16 * kDreluPitch];
     __shared__ uint32_t s_act;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, kg = lane >> 4;
@@ -518,7 +548,8 @@ __global__ __launch_bounds__(256) void drelu_gate_up_kernel(DreluArgs a) {
         // gate partials
         const int64_t n_tile = min((int64_t)16, ffn - n0);
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        drelu_partial(a.x, rows, tok0, d, a.wg + n0 * d, n_tile, n_ok, wave, lane, acc);
+        drelu_partial(a.x, rows, tok0, d, a.wg + n0 * d, n_tile, 0xFFFFu, wave, lane, acc,
+                      s_tile[wave]);
         s_part[wave][lane] = acc;
         __syncthreads();
         f32x4 g = s_part[0][lane];
@@ -538,8 +569,7 @@ __global__ __launch_bounds__(256) void drelu_gate_up_kernel(DreluArgs a) {
 
         f32x4 u = {0.0f, 0.0f, 0.0f, 0.0f};
         if (act != 0u) {   // uniform: every wave computes the same ballot
-            const bool mine = ((act >> r16) & 1u) != 0u;
-            drelu_partial(a.x, rows, tok0, d, a.wu + n0 * d, n_tile, mine, wave, lane, u);
+            drelu_partial(a.x, rows, tok0, d, a.wu + n0 * d, n_tile, act, wave, lane, u, s_tile[wave]);
             s_part[wave][lane] = u;
             __syncthreads();
             u = s_part[0][lane];
