@@ -464,8 +464,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_bf16_deep_kernel(
 // lanes per row, 64 bytes each), writes them to its LDS tile (rows 272
 // bytes apart, so both the 16-byte writes and the fragment reads below are
 // free of bank conflicts) and reads the MFMA B operand from there; the x
-// fragments (16 tokens, L2-resident) come straight from memory.  Two
-// register stages keep the next stage's loads in flight.  LDS instructions
+// fragments (16 tokens, L2-resident) come straight from memory.  Three
+// register stages keep the next two stages' loads in flight.  LDS instructions
 // of one wave complete in order, so a stage's tile writes follow the
 // previous stage's reads.
 constexpr int kDreluStageK = 128;                 // features per stage
@@ -515,17 +515,23 @@ __device__ __forceinline__ void drelu_partial(const uint16_t* __restrict__ x, in
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xv[i]), as_bf16x8(bv), acc, 0, 0, 0);
         }
     };
-    u32x4 wa[4], xa[4], wb[4], xb[4];
+    u32x4 wa[4], xa[4], wb[4], xb[4], wc[4], xc[4];
     load(wa, xa, st0);
-    for (int st = st0; st < st1; st += 2) {
-        load(wb, xb, st + 1);   // past the quarter: out of range, no data moved
+    load(wb, xb, st0 + 1);   // past the quarter: out of range, no data moved
+    for (int st = st0; st < st1; st += 3) {
+        load(wc, xc, st + 2);
         __builtin_amdgcn_sched_barrier(0);
         compute(wa, xa);
         __builtin_amdgcn_sched_barrier(0);
         if (st + 1 >= st1) break;   // uniform
-        load(wa, xa, st + 2);
+        load(wa, xa, st + 3);
         __builtin_amdgcn_sched_barrier(0);
         compute(wb, xb);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 2 >= st1) break;
+        load(wb, xb, st + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(wc, xc);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
