@@ -23,7 +23,8 @@ Measurement:
   * the K timed steps are captured in one HIP graph (no host launch gaps)
     and timed with HIP events on the stream the library launches on;
   * roofline (c2): the gather GEMV, the dominant kernel, is timed alone
-    through qs_gather_linear, launch by launch in a graph, on the same
+    through qs_gather_linear_acc (the accumulate form that the FFN step
+    runs with fp32 outputs), launch by launch in a graph, on the same
     inputs; achieved = algorithmic bytes (selected weight rows of the
     batch's union, each read once, plus activations and outputs) / time;
   * traffic: HBM bytes per launch from committed rocprofv3 PMC summaries
@@ -63,6 +64,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--roofline-launches", type=int, default=96)
+    p.add_argument("--deterministic", action="store_true",
+                   help="fixed-order split-K sums (qs_set_deterministic(1)) instead of float atomics")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 256 MiB device copy (for PMC byte calibration)")
     return p.parse_args()
@@ -176,16 +179,18 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     step_bytes = sum(bytes_up(i % N_XROT) + bytes_dn(i % N_XROT)
                      for i in range(args.steps)) / args.steps
 
-    # roofline leg: the gather GEMV alone, launch by launch
+    # roofline leg: the gather GEMV alone, launch by launch, in the form the
+    # step runs (the accumulate form, unless fixed-order sums were asked for)
     L = args.roofline_launches
-    yup = torch.empty((B, ffn), dtype=torch.float32, device=dev)
-    ydn = torch.empty((B, d), dtype=torch.float32, device=dev)
+    yup = torch.zeros((B, ffn), dtype=torch.float32, device=dev)
+    ydn = torch.zeros((B, d), dtype=torch.float32, device=dev)
     ws_up = qs.gather_workspace(B, d, ffn, dev)
     ws_dn = qs.gather_workspace(B, ffn, d, dev)
+    gather = qs.qs_gather_linear if args.deterministic else qs.qs_gather_linear_acc
 
     def gemv_pair(i):
-        qs.qs_gather_linear(u1[i % N_XROT], wups[i % n_copies], y=yup, ws=ws_up)
-        qs.qs_gather_linear(u2[i % N_XROT], wdns[i % n_copies], y=ydn, ws=ws_dn)
+        gather(u1[i % N_XROT], wups[i % n_copies], y=yup, ws=ws_up)
+        gather(u2[i % N_XROT], wdns[i % n_copies], y=ydn, ws=ws_dn)
 
     ms_gemv = time_graph(torch, stream, gemv_pair, L, 4)
     gemv_bytes = sum(bytes_up(i % N_XROT) + bytes_dn(i % N_XROT) for i in range(L))
@@ -616,6 +621,7 @@ def main():
     import sparse_activation_amd as qs
 
     qs.load()
+    qs.qs_set_deterministic(args.deterministic)
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
     if args.copy_calibration:
@@ -629,6 +635,8 @@ def main():
             "vs_baseline": None, "dtype": out.pop("dtype"),
             "data": "synthetic (seeded Student-t(4) activations, N(0,0.02) weights)"}
     line.update(out)
+    if isinstance(line.get("config"), dict):
+        line["config"]["split_k_sums"] = "fixed_order" if args.deterministic else "atomic"
     print(json.dumps(line), flush=True)
 
 

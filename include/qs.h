@@ -58,8 +58,15 @@
  *     nonzero qs_status; qs_last_error() then describes it.  No C++
  *     exception crosses the ABI.  rows == 0 is a valid no-op.
  *   - Device pointers must be 16-byte aligned.
- *   - Results are bitwise deterministic for fixed inputs, shapes and stream
- *     (no floating-point atomics; every reduction has a fixed order).
+ *   - Split-K sums: by default a gather whose output is fp32 lets each of
+ *     its workgroups add its partial tile into the (zeroed) output with
+ *     float atomics, so the fp32 rounding of a sum depends on the order in
+ *     which the splits arrive (results stay within the stated error bounds
+ *     but may differ in the last bits between runs).  qs_set_deterministic(1)
+ *     switches every entry point to fixed-order sums (the last workgroup of
+ *     each tile adds the partials in split order): results are then bitwise
+ *     deterministic for fixed inputs and shapes.  Integer results are exact
+ *     either way.
  *   - A workspace (`ws`, `ws_bytes`) is device memory of at least the size
  *     qs_workspace_bytes() reports for the same op and shape; its contents
  *     are scratch and need no initialisation (qs_gather_linear excepted, see
@@ -173,6 +180,34 @@ qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_i
 qs_status qs_gather_linear(const float* xs, int64_t rows, int64_t d_in, const void* wt,
                            qs_dtype wt_t, int64_t n_out, void* y, qs_dtype yt,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qs_gather_linear_acc -- Y += Xs . W^T into an fp32 Y, reading the same rows
+ * of W^T as qs_gather_linear  [QS-TopK], [QS-Adv].  This is the gather that
+ * qs_sparse_linear and qs_sparse_ffn run when their output is fp32 and
+ * fixed-order sums are not asked for: every workgroup adds its partial tile
+ * into y with float atomics (no handoff between the K-splits), so the
+ * rounding of each sum depends on the arrival order of the splits, whatever
+ * qs_set_deterministic says.
+ *
+ *   xs, wt, wt_t, rows, d_in, n_out: as qs_gather_linear.
+ *   y     device fp32 [rows, n_out], read and written.
+ *   Workspace: as qs_gather_linear (its counters are not touched).
+ *   Limits: as qs_gather_linear; fp32 weights need rows <= 8
+ *   (QS_ERR_UNSUPPORTED otherwise).
+ */
+qs_status qs_gather_linear_acc(const float* xs, int64_t rows, int64_t d_in, const void* wt,
+                               qs_dtype wt_t, int64_t n_out, float* y, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/*
+ * qs_set_deterministic -- process-wide choice of the split-K summation (see
+ * the conventions above): on != 0 gives fixed-order, bitwise reproducible
+ * sums in every entry point; 0 (the default) lets fp32 outputs be summed with
+ * float atomics.  Takes effect for calls made after it returns; returns the
+ * previous setting.  Not a device call: it cannot fail.
+ */
+int qs_set_deterministic(int on);
 
 /*
  * qs_sparse_linear_i8t -- quantised Q-Sparse linear  [QS-TopK]

@@ -21,6 +21,7 @@ __all__ = [
     "OP_SPARSE_FFN_DRELU", "OP_GATHER_LINEAR", "OP_SPARSE_FFN_RELU2_GLU",
     "OP_SPARSE_LINEAR_BACKWARD", "qs_sparse_linear_backward", "OP_BLOCK_SPARSE_LINEAR",
     "qs_block_sparse_linear", "OP_SPARSE_MOE_FFN", "qs_sparse_moe_ffn",
+    "qs_gather_linear_acc", "qs_set_deterministic",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +41,8 @@ _INT = ctypes.c_int
 _SIGS = {
     "qs_topk_mask": [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P],
     "qs_gather_linear": [_P, _I64, _I64, _P, _INT, _I64, _P, _INT, _P, ctypes.c_size_t, _P],
+    "qs_gather_linear_acc": [_P, _I64, _I64, _P, _INT, _I64, _P, _P, ctypes.c_size_t, _P],
+    "qs_set_deterministic": [_INT],
     "qs_sparse_linear": [_P, _INT, _I64, _I64, _I64, _P, _INT, _INT, _I64, _P, _INT, _P,
                          ctypes.c_size_t, _P],
     "qs_sparse_linear_backward": [_P, _INT, _I64, _I64, _I64, _P, _INT, _INT, _I64, _P, _INT,
@@ -228,6 +231,35 @@ def qs_gather_linear(xs, wt, y=None, y_dtype=None, ws=None):
     _check(load().qs_gather_linear(_ptr(xs), rows, d_in, _ptr(wt), _dtype_code(wt), n_out,
                                    _ptr(y), _dtype_code(y), _ptr(ws), ws_bytes, _stream(dev)))
     return y
+
+
+def qs_gather_linear_acc(xs, wt, y, ws=None):
+    """Y += Xs . W^T into the fp32 tensor `y` (float atomics across K-splits).
+
+    `ws` as for qs_gather_linear."""
+    torch = _torch()
+    rows, d_in = xs.shape
+    if xs.dtype != torch.float32 or y.dtype != torch.float32:
+        raise TypeError("xs and y must be float32")
+    if wt.shape[0] != d_in:
+        raise ValueError("wt must be [d_in, n_out]")
+    n_out = wt.shape[1]
+    if tuple(y.shape) != (rows, n_out):
+        raise ValueError("y must be [rows, n_out]")
+    dev = _dev(xs, wt, y, ws)
+    if ws is None:
+        ws = gather_workspace(rows, d_in, n_out, dev)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(load().qs_gather_linear_acc(_ptr(xs), rows, d_in, _ptr(wt), _dtype_code(wt), n_out,
+                                       _ptr(y), _ptr(ws), ws_bytes, _stream(dev)))
+    return y
+
+
+def qs_set_deterministic(on: bool) -> bool:
+    """Process-wide: fixed-order split-K sums (bitwise reproducible) if on.
+
+    Returns the previous setting."""
+    return bool(load().qs_set_deterministic(1 if on else 0))
 
 
 def qs_sparse_linear(x, k: int, w, layout: int = LAYOUT_WT, y=None, y_dtype=None, ws=None):

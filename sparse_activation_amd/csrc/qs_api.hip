@@ -1,6 +1,7 @@
 // C ABI of libqs.so: argument validation, workspace layout and dispatch to
 // the HIP kernels.  Every check runs before anything is enqueued, so a call
 // that fails leaves the outputs untouched.
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -12,6 +13,10 @@
 namespace {
 
 thread_local std::string g_err;
+
+// Process-wide: 1 = every split-K sum in a fixed order (bitwise reproducible).
+std::atomic<int> g_deterministic{0};
+bool deterministic() { return g_deterministic.load(std::memory_order_relaxed) != 0; }
 
 qs_status fail(qs_status st, const char* fmt, ...) {
     char buf[512];
@@ -124,6 +129,7 @@ struct FfnWs {
     uint16_t* xm;          // drelu: X (.) M1 (bf16)
     float* h;
     float* hs;
+    float* gacc;           // relu2 kinds: the gate sums of the gated FFN's accumulate form
     float* partial;
     size_t bytes;
 };
@@ -150,6 +156,7 @@ FfnWs ffn_ws(char* base, int64_t rows, int64_t d, int64_t ffn, bool drelu) {
     else w.xm = (uint16_t*)c.take(sizeof(uint16_t) * (size_t)rows * d);
     w.h = (float*)c.take(sizeof(float) * (size_t)rows * ffn);
     w.hs = (float*)c.take(sizeof(float) * (size_t)rows * ffn);
+    if (!drelu) w.gacc = (float*)c.take(sizeof(float) * (size_t)rows * ffn);
     w.partial = (float*)c.take(sizeof(float) * max_sz(up_part, down_part));
     w.bytes = c.off;
     return w;
@@ -313,26 +320,32 @@ qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_i
     }
     const int wb = wt_t == QS_BF16;
     qs::GemvPlan plan = qs::plan_gemv(rows, d_in, n_out, wb);
+    // fp32 y: the selection launch clears y and the gather's workgroups add
+    // into it (no split handoff), unless fixed-order sums are asked for.
+    const bool acc = !deterministic() && yt == QS_F32 && qs::gemv_accumulate_supported(plan, wb);
     qs::TopkArgs t{};
     t.x = x; t.d = d_in; t.k = k; t.idx_stride = k;
     t.xs = wsp.xs;
     t.zero_ptr = wsp.counters; t.n_zero = plan.n_counters;
+    if (acc) { t.zero_rows = (int32_t*)y; t.zero_row_len = n_out; }
     e = qs::launch_topk(kk, qs::XS_F32, rows, t, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     qs::GemvArgs g{};
     g.xs = wsp.xs; g.rows = rows; g.d_in = d_in; g.n_out = n_out; g.w = w;
     g.partial = wsp.partial; g.counters = wsp.counters; g.y = y; g.y_bf16 = yt == QS_BF16;
     g.epilogue = qs::EPI_STORE;
+    g.accumulate = acc ? 1 : 0;
     g.xs_bf16 = xt == QS_BF16;
     e = qs::launch_gemv(plan, wb, g, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
 }
 
-qs_status qs_gather_linear(const float* xs, int64_t rows, int64_t d_in, const void* wt,
-                           qs_dtype wt_t, int64_t n_out, void* y, qs_dtype yt,
-                           void* ws, size_t ws_bytes, void* stream) {
-    const char* fn = "qs_gather_linear";
+namespace {
+
+qs_status gather_linear(const char* fn, bool accumulate, const float* xs, int64_t rows,
+                        int64_t d_in, const void* wt, qs_dtype wt_t, int64_t n_out, void* y,
+                        qs_dtype yt, void* ws, size_t ws_bytes, void* stream) {
     if (rows < 0 || d_in <= 0 || n_out <= 0 || d_in > (int64_t(1) << 24))
         return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
     if (!valid_float_dtype(wt_t) || !valid_float_dtype(yt))
@@ -356,13 +369,36 @@ qs_status qs_gather_linear(const float* xs, int64_t rows, int64_t d_in, const vo
     qs::GemvPlan plan = qs::plan_gemv(rows, d_in, n_out, wb);
     if (plan.n_counters > kGatherCounters)
         return fail(QS_ERR_UNSUPPORTED, "%s: too many output tiles (n_out or rows too large)", fn);
+    if (accumulate && !qs::gemv_accumulate_supported(plan, wb))
+        return fail(QS_ERR_UNSUPPORTED, "%s: fp32 weights need at most 8 rows", fn);
     qs::GemvArgs g{};
     g.xs = xs; g.rows = rows; g.d_in = d_in; g.n_out = n_out; g.w = wt;
     g.partial = wsp.partial; g.counters = wsp.counters; g.y = y; g.y_bf16 = yt == QS_BF16;
     g.epilogue = qs::EPI_STORE;
+    g.accumulate = accumulate ? 1 : 0;
     hipError_t e = qs::launch_gemv(plan, wb, g, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
+}
+
+}  // namespace
+
+qs_status qs_gather_linear(const float* xs, int64_t rows, int64_t d_in, const void* wt,
+                           qs_dtype wt_t, int64_t n_out, void* y, qs_dtype yt,
+                           void* ws, size_t ws_bytes, void* stream) {
+    return gather_linear("qs_gather_linear", false, xs, rows, d_in, wt, wt_t, n_out, y, yt, ws,
+                         ws_bytes, stream);
+}
+
+qs_status qs_gather_linear_acc(const float* xs, int64_t rows, int64_t d_in, const void* wt,
+                               qs_dtype wt_t, int64_t n_out, float* y, void* ws,
+                               size_t ws_bytes, void* stream) {
+    return gather_linear("qs_gather_linear_acc", true, xs, rows, d_in, wt, wt_t, n_out, y, QS_F32,
+                         ws, ws_bytes, stream);
+}
+
+int qs_set_deterministic(int on) {
+    return g_deterministic.exchange(on ? 1 : 0, std::memory_order_relaxed);
 }
 
 qs_status qs_sparse_linear_i8t(const float* x, int64_t rows, int64_t d_in, int64_t k,
@@ -456,27 +492,47 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     const int kk = wb ? qs::KEY_BF16 : qs::KEY_F32;
     float* hbuf = h ? h : wsp.h;
     hipError_t e;
+    // Accumulate forms (unless fixed-order sums are asked for): the gathers'
+    // workgroups add their partial tiles into zeroed fp32 buffers instead of
+    // handing them to a last workgroup.  Up projection: the input selection
+    // clears the sums, and the selection of h maps them to h (so only with
+    // k_mid >= 0).  Down projection: the selection of h clears y.
+    qs::GemvPlan pd = qs::plan_gemv(rows, ffn, d, wb);
+    const bool acc_down = !deterministic() && k_mid >= 0 && yt == QS_F32 &&
+                          qs::gemv_accumulate_supported(pd, wb);
+    bool acc_up = false, dual = false;
 
     // Stage 1: the intermediate h.
     if (!drelu) {
         qs::GemvPlan pu = qs::plan_gemv(rows, d, ffn, wb);
+        dual = act == QS_ACT_RELU2_GLU && qs::gemv_dual_supported(pu, wb);
+        acc_up = !deterministic() && k_mid >= 0 && qs::topk_xform_supported(ffn) &&
+                 qs::gemv_accumulate_supported(pu, wb) && (act == QS_ACT_RELU2 || dual);
         qs::TopkArgs t{};
         t.x = x; t.d = d; t.k = k_in; t.idx_stride = k_in;
         t.xs = wsp.xs1;
         t.zero_ptr = wsp.ctr_up; t.n_zero = wsp.n_ctr;
+        if (acc_up) {
+            t.zero_rows = (int32_t*)hbuf;
+            t.zero_rows2 = dual ? (int32_t*)wsp.gacc : nullptr;
+            t.zero_row_len = ffn;
+        }
         e = qs::launch_topk(kk, qs::XS_F32, rows, t, st);
         if (e != hipSuccess) return hip_fail(e, fn);
         qs::GemvArgs g{};
         g.xs = wsp.xs1; g.rows = rows; g.d_in = d; g.n_out = ffn; g.w = w_up;
         g.partial = wsp.partial; g.counters = wsp.ctr_up; g.y = hbuf; g.y_bf16 = 0;
-        g.epilogue = qs::EPI_RELU2;
+        g.epilogue = acc_up ? qs::EPI_STORE : qs::EPI_RELU2;
+        g.accumulate = acc_up ? 1 : 0;
         g.xs_bf16 = dt == QS_BF16;
-        if (act == QS_ACT_RELU2_GLU && qs::gemv_dual_supported(pu, wb)) {
+        if (dual) {
             // Both projections in one gather: the gate's and the up rows of
             // each selected feature are streamed together, and the last
-            // split forms h = relu(g)^2 * u.
+            // split (or, in the accumulate form, the selection of h) forms
+            // h = relu(g)^2 * u.
             g.w2 = w_gate;
-            g.partial2 = wsp.partial + pu.scratch_floats;   // behind the partials and records
+            if (acc_up) g.y2 = wsp.gacc;
+            else g.partial2 = wsp.partial + pu.scratch_floats;   // behind the partials and records
             e = qs::launch_gemv_dual(pu, wb, g, st);
             if (e != hipSuccess) return hip_fail(e, fn);
         } else if (act == QS_ACT_RELU2_GLU) {
@@ -526,6 +582,14 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
         t.x = hbuf; t.d = ffn; t.k = k_mid;
         t.idx = mid_idx; t.idx_stride = ffn; t.count = mid_cnt;
         t.xs = wsp.hs;
+        if (acc_up) {
+            // hbuf holds the raw up sums (and gacc the gate's): map them to h
+            // here, and write h back where the caller asked for it.
+            t.xform = dual ? qs::XF_RELU2_GLU : qs::XF_RELU2;
+            t.x2 = wsp.gacc;
+            t.h_out = h;
+        }
+        if (acc_down) { t.zero_rows = (int32_t*)y; t.zero_row_len = d; }
         e = qs::launch_topk(qs::KEY_F32, qs::XS_F32, rows, t, st);
         if (e != hipSuccess) return hip_fail(e, fn);
         hsel = wsp.hs;
@@ -535,11 +599,11 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     }
 
     // Stage 3: gathered down projection.
-    qs::GemvPlan pd = qs::plan_gemv(rows, ffn, d, wb);
     qs::GemvArgs g{};
     g.xs = hsel; g.rows = rows; g.d_in = ffn; g.n_out = d; g.w = w_down_t;
     g.partial = wsp.partial; g.counters = wsp.ctr_down; g.y = y; g.y_bf16 = yt == QS_BF16;
     g.epilogue = qs::EPI_STORE;
+    g.accumulate = acc_down ? 1 : 0;
     e = qs::launch_gemv(pd, wb, g, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();

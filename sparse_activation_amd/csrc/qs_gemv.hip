@@ -336,10 +336,13 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
                 const int64_t cg = (int64_t)tile * CT + (o % CT);
                 if (m == 1) {   // gate (dual kernel only)
                     gsum[q] = s;
-                    if (nsplit > 1 && row < rows && cg < n_out)
-                        store_agent(&a.partial2[((int64_t)split * rows + row) * n_out + cg], s);
+                    if (row < rows && cg < n_out) {
+                        if (a.accumulate) unsafeAtomicAdd(&a.y2[row * n_out + cg], s);
+                        else if (nsplit > 1) store_agent(&a.partial2[((int64_t)split * rows + row) * n_out + cg], s);
+                    }
                 } else if (row < rows && cg < n_out) {
-                    if (nsplit > 1) store_agent(&a.partial[((int64_t)split * rows + row) * n_out + cg], s);
+                    if (a.accumulate) unsafeAtomicAdd(&reinterpret_cast<float*>(a.y)[row * n_out + cg], s);
+                    else if (nsplit > 1) store_agent(&a.partial[((int64_t)split * rows + row) * n_out + cg], s);
                     else if (DUAL) reinterpret_cast<float*>(a.y)[row * n_out + cg] = relu2_glu(gsum[q], s);
                     else store_final(a, row * n_out + cg, s);
                 }
@@ -348,8 +351,9 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
         }
     }
 
-    // Phase D: the last split of this tile sums the partials in split order.
-    if (nsplit > 1) {
+    // Phase D: the last split of this tile sums the partials in split order
+    // (in the accumulate form the atomics above already formed y).
+    if (nsplit > 1 && !a.accumulate) {
         const int ci = tt * gridDim.x + tile;
         if (last_split_arrived(&a.counters[ci], nsplit, &s_last)) {
             for (int o = tid; o < BT * CT; o += kNT) {
@@ -897,7 +901,10 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
         const int64_t row = tok0 + o / kBCols, cg = (int64_t)tile * kBCols + (o % kBCols);
         if (row < rows && cg < n_out) {
             const int64_t i = row * n_out + cg, pi = ((int64_t)split * rows + row) * n_out + cg;
-            if constexpr (DUAL) {
+            if (a.accumulate) {
+                unsafeAtomicAdd(&reinterpret_cast<float*>(a.y)[i], outv[0][q]);
+                if constexpr (DUAL) unsafeAtomicAdd(&a.y2[i], outv[NM - 1][q]);
+            } else if constexpr (DUAL) {
                 if (nsplit == 1) {
                     reinterpret_cast<float*>(a.y)[i] = relu2_glu(outv[1][q], outv[0][q]);
                 } else {
@@ -912,7 +919,7 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
     }
 
     // Phase D: the last workgroup of the tile sums the partials in split order.
-    if (nsplit > 1) {
+    if (nsplit > 1 && !a.accumulate) {
         const int ci = tt * gridDim.x + tile;
         if (last_split_arrived(&a.counters[ci], nsplit, reinterpret_cast<int*>(s_tr))) {
             const int64_t stride = rows * n_out;
@@ -1442,8 +1449,14 @@ GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16, int
     return p;
 }
 
+bool gemv_accumulate_supported(const GemvPlan& p, int w_is_bf16) {
+    return !(p.bt == 16 && !w_is_bf16);
+}
+
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
+    if (a.accumulate && (a.y_bf16 || a.epilogue != EPI_STORE || !gemv_accumulate_supported(p, w_is_bf16)))
+        return hipErrorInvalidValue;
     const int ept = w_is_bf16 ? 8 : 4;
     const int ct = kFLPR * ept;
     const int tg = p.bt < 2 ? p.bt : 2;
@@ -1499,8 +1512,8 @@ bool gemv_dual_supported(const GemvPlan& p, int w_is_bf16) {
 
 hipError_t launch_gemv_dual(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
-    if (!gemv_dual_supported(p, w_is_bf16) || a.w2 == nullptr || (p.nsplit > 1 && a.partial2 == nullptr) ||
-        a.row_expert != nullptr)
+    if (!gemv_dual_supported(p, w_is_bf16) || a.w2 == nullptr || a.row_expert != nullptr ||
+        (a.accumulate ? a.y2 == nullptr : p.nsplit > 1 && a.partial2 == nullptr))
         return hipErrorNotSupported;
     if (p.bt == 16) {   // bf16 weights: the 16-token MFMA gather with both matrices
         const dim3 grid(p.n_tiles, p.nsplit, p.n_tok_tiles);

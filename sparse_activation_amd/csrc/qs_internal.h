@@ -41,7 +41,18 @@ struct TopkArgs {
     int n_zero;
     int32_t* zero_rows;   // or null: the workgroup of row r clears
     int64_t zero_row_len; //   zero_rows[r * zero_row_len ..) (zero_row_len % 4 == 0)
+    int32_t* zero_rows2;  // or null: cleared the same way (same row length)
+    // KEY_F32 only: the row is first mapped elementwise (XF_RELU2: relu(x)^2;
+    // XF_RELU2_GLU: relu(x2)^2 * x, x2 of the shape of x), and the mapped
+    // values are selected, written to xs and, if h_out is set, to h_out
+    // (which may be x itself).  Only rows that the vector kernel takes
+    // (topk_xform_supported).
+    int xform;
+    const float* x2;
+    float* h_out;
 };
+enum Xform : int { XF_NONE = 0, XF_RELU2 = 1, XF_RELU2_GLU = 2 };
+bool topk_xform_supported(int64_t d);
 
 // One workgroup per row.  Returns a HIP error code (hipSuccess = 0).
 hipError_t launch_topk(int key_kind, int xs_kind, int64_t rows, const TopkArgs& a,
@@ -93,6 +104,12 @@ struct GemvArgs {
     // were written by a previous gather over the same xs (and plan), so the
     // packing launch is skipped.
     int frag_ready;
+    // 1: y is fp32 and already holds the values to add to; every workgroup
+    // adds its partial tile into y (and the dual gather its gate tile into
+    // y2) with float atomics, so there is no split handoff and no epilogue
+    // (epilogue must be EPI_STORE).  The sum order depends on timing.
+    int accumulate;
+    float* y2;
 };
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 // Both projections of the gated squared ReLU in one gather (tiles of at most
@@ -100,6 +117,8 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
 // for other plans.  partial2 must not overlap the scratch behind partial.
 bool gemv_dual_supported(const GemvPlan& p, int w_is_bf16);
 hipError_t launch_gemv_dual(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
+// Plans whose kernel has the accumulate form (all but fp32 16-token tiles).
+bool gemv_accumulate_supported(const GemvPlan& p, int w_is_bf16);
 
 // ---------------------------------------------------------------- ternary x int8 gather
 struct I8tPlan {

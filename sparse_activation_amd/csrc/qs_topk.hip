@@ -25,6 +25,21 @@ namespace qs {
 namespace {
 
 constexpr int kWave = 64;
+
+// Side jobs of the selection launch, done before anything else: workgroup 0
+// clears the split-K counters of the gather that follows, and the workgroup
+// of row r clears row r of the buffers that the next kernel adds into.
+template <int NT>
+__device__ __forceinline__ void clear_side_buffers(const TopkArgs& a, int r, int tid) {
+    if (r == 0 && a.zero_ptr != nullptr)
+        for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
+    int32_t* const zr[2] = {a.zero_rows, a.zero_rows2};
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+        if (zr[b] != nullptr)
+            for (int64_t i = tid; i < a.zero_row_len / 4; i += NT)
+                reinterpret_cast<uint4*>(zr[b] + (int64_t)r * a.zero_row_len)[i] = make_uint4(0u, 0u, 0u, 0u);
+}
 constexpr int kNSub = 4;               // LDS sub-histograms (spread atomic contention)
 constexpr int64_t kStageMaxD = 14336;  // raw words staged in LDS up to this row length
 
@@ -126,11 +141,7 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(TopkArgs a) {
     const int64_t k = a.k;
     const int64_t row0 = (int64_t)r * d;
 
-    if (r == 0 && a.zero_ptr != nullptr)
-        for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
-    if (a.zero_rows != nullptr)
-        for (int64_t i = tid; i < a.zero_row_len / 4; i += NT)
-            reinterpret_cast<uint4*>(a.zero_rows + (int64_t)r * a.zero_row_len)[i] = make_uint4(0u, 0u, 0u, 0u);
+    clear_side_buffers<NT>(a, r, tid);
 
     // Quantisation scale (KEY_Q8): gamma = max|x| (exact), s = 127 / (gamma + eps).
     float scale = 0.0f;
@@ -311,11 +322,7 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
     const int64_t row0 = (int64_t)r * d;
     const int nch = (int)((d + NT - 1) / NT);     // chunks holding entries (<= EPT)
 
-    if (r == 0 && a.zero_ptr != nullptr)
-        for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
-    if (a.zero_rows != nullptr)
-        for (int64_t i = tid; i < a.zero_row_len / 4; i += NT)
-            reinterpret_cast<uint4*>(a.zero_rows + (int64_t)r * a.zero_row_len)[i] = make_uint4(0u, 0u, 0u, 0u);
+    clear_side_buffers<NT>(a, r, tid);
 
     // Load the row: every load issued before any is used.
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -599,11 +606,7 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int64_t d = a.d, k = a.k, row0 = (int64_t)r * d;
 
-    if (r == 0 && a.zero_ptr != nullptr)
-        for (int i = tid; i < a.n_zero; i += NT) a.zero_ptr[i] = 0;
-    if (a.zero_rows != nullptr)
-        for (int64_t i = tid; i < a.zero_row_len / 4; i += NT)
-            reinterpret_cast<uint4*>(a.zero_rows + (int64_t)r * a.zero_row_len)[i] = make_uint4(0u, 0u, 0u, 0u);
+    clear_side_buffers<NT>(a, r, tid);
     sel::select_clear<NT, KB>(s_sel, tid);
 
     // ---- load runs (past the row end the buffer reads zero)
@@ -618,6 +621,44 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
         unpack_raw<KK>(w, raw + q * V);
     }
     auto run_valid = [&](int q) { return (int64_t)q * CS + V * tid < d; };   // d % V == 0
+
+    // Elementwise map of the row before the selection (the FFN intermediate
+    // from raw projection sums): h = relu(u)^2, or relu(g)^2 * u with the
+    // gate sums g in x2, in the same fp32 operations as the gather epilogue.
+    if constexpr (KK == KEY_F32) {
+        if (a.xform != XF_NONE) {
+            uint32_t graw[EPT];
+            if (a.xform == XF_RELU2_GLU) {
+                const __amdgpu_buffer_rsrc_t rs2 = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<float*>(a.x2 + row0), (short)0, (int)(d * 4), 0x00020000);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(
+                        rs2, (uint32_t)((q * CS + V * tid) * 4), 0, 0);
+                    unpack_raw<KK>(w, graw + q * V);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) {
+                const float u = __uint_as_float(raw[i]);
+                float hv;
+                if (a.xform == XF_RELU2) {
+                    hv = u > 0.0f ? __fmul_rn(u, u) : 0.0f;
+                } else {
+                    const float g = __uint_as_float(graw[i]);
+                    hv = g > 0.0f ? __fmul_rn(__fmul_rn(g, g), u) : 0.0f;
+                }
+                raw[i] = __float_as_uint(hv);
+            }
+            if (a.h_out != nullptr) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    if (run_valid(q))
+                        *reinterpret_cast<uint4*>(a.h_out + row0 + q * CS + V * tid) =
+                            make_uint4(raw[q * V], raw[q * V + 1], raw[q * V + 2], raw[q * V + 3]);
+            }
+        }
+    }
 
     if constexpr (KK == KEY_Q8) {
         float m = 0.0f;
@@ -892,9 +933,19 @@ __global__ void zero_i32_kernel(int32_t* p, int64_t n) {
 
 }  // namespace
 
+bool topk_xform_supported(int64_t d) { return d % 4 == 0 && d <= 16384; }
+
 hipError_t launch_topk(int key_kind, int xs_kind, int64_t rows, const TopkArgs& a,
                        hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
+    // The elementwise map lives in the vector kernel, which takes exactly
+    // these rows (fp32 keys, d % 4 == 0, d <= 16384).
+    if (a.xform != XF_NONE &&
+        (key_kind != KEY_F32 || !topk_xform_supported(a.d) || a.xform > XF_RELU2_GLU ||
+         (a.xform == XF_RELU2_GLU && a.x2 == nullptr)))
+        return hipErrorInvalidValue;
+    if ((a.zero_rows != nullptr || a.zero_rows2 != nullptr) && a.zero_row_len % 4 != 0)
+        return hipErrorInvalidValue;
     // Few rows (decode): one big workgroup per row; many rows: smaller ones.
     if (rows <= 64) return launch_nt<1024>(key_kind, xs_kind, rows, a, stream);
     return launch_nt<256>(key_kind, xs_kind, rows, a, stream);

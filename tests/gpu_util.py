@@ -50,3 +50,18 @@ def assert_within(y, y_ref, t, tol, what=""):
     with np.errstate(invalid="ignore", divide="ignore"):
         rel = np.where(t > 0, err / t, 0.0)
     return float(rel.max()) if rel.size else 0.0
+
+
+class reduction_mode:
+    """Context manager: fixed-order (deterministic=True) or atomic split-K sums."""
+
+    def __init__(self, qs, deterministic: bool):
+        self.qs, self.det, self.prev = qs, deterministic, None
+
+    def __enter__(self):
+        self.prev = self.qs.qs_set_deterministic(self.det)
+        return self
+
+    def __exit__(self, *exc):
+        self.qs.qs_set_deterministic(self.prev)
+        return False

@@ -15,7 +15,7 @@ import pytest
 
 import datagen
 import oracle
-from gpu_util import assert_within, note, to_dev
+from gpu_util import assert_within, note, reduction_mode, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -53,16 +53,20 @@ def _relu2_case(gpu_lib, x, w_up, w_down, k_in, k_mid, wtype="bf16", ydt=None):
 
 @pytest.mark.parametrize("rows,d,f", [(1, 64, 96), (3, 256, 520), (17, 512, 264)])
 @pytest.mark.parametrize("wtype", ["f32", "bf16"])
-def test_relu2_small(gpu_lib, rows, d, f, wtype):
+@pytest.mark.parametrize("det", [False, True])
+def test_relu2_small(gpu_lib, rows, d, f, wtype, det):
+    """det: fixed-order split-K sums; else the accumulate forms (the
+    selections clear the sums, the selection of h applies relu^2)."""
     rng = np.random.default_rng(rows + d + f)
     x = datagen.student_t(rng, (rows, d))
     w_up = datagen.normal(rng, (f, d), 0.02)
     w_down = datagen.normal(rng, (d, f), 0.02)
     if wtype == "bf16":
         x, w_up, w_down = (datagen.bf16_round(a) for a in (x, w_up, w_down))
-    for k_in, k_mid in [(d, f), ((2 * d) // 5, (2 * f) // 5), (1, 3), (0, 0), (d // 2, -1)]:
-        note(f"relu2 {wtype} rows={rows} d={d} ffn={f} k_in={k_in} k_mid={k_mid}")
-        _relu2_case(gpu_lib, x, w_up, w_down, k_in, k_mid, wtype)
+    with reduction_mode(gpu_lib, det):
+        for k_in, k_mid in [(d, f), ((2 * d) // 5, (2 * f) // 5), (1, 3), (0, 0), (d // 2, -1)]:
+            note(f"relu2 {wtype} det={det} rows={rows} d={d} ffn={f} k_in={k_in} k_mid={k_mid}")
+            _relu2_case(gpu_lib, x, w_up, w_down, k_in, k_mid, wtype)
 
 
 @pytest.mark.parametrize("batch", [1, 2, 4, 8, 16])
@@ -118,7 +122,8 @@ def _relu2_glu_case(gpu_lib, x, wg, wu, wd, k_in, k_mid, wtype="bf16"):
 
 @pytest.mark.parametrize("rows,d,f", [(1, 64, 96), (2, 128, 200), (3, 256, 520), (17, 512, 264)])
 @pytest.mark.parametrize("wtype", ["f32", "bf16"])
-def test_relu2_glu_small(gpu_lib, rows, d, f, wtype):
+@pytest.mark.parametrize("det", [False, True])
+def test_relu2_glu_small(gpu_lib, rows, d, f, wtype, det):
     rng = np.random.default_rng(rows + 2 * d + f)
     x = datagen.student_t(rng, (rows, d))
     wg = datagen.normal(rng, (f, d), 0.02)
@@ -126,9 +131,10 @@ def test_relu2_glu_small(gpu_lib, rows, d, f, wtype):
     wd = datagen.normal(rng, (d, f), 0.02)
     if wtype == "bf16":
         x, wg, wu, wd = (datagen.bf16_round(a) for a in (x, wg, wu, wd))
-    for k_in, k_mid in [(d, f), ((2 * d) // 5, (2 * f) // 5), (1, 3), (0, 0), (d // 2, -1)]:
-        note(f"relu2-glu {wtype} rows={rows} d={d} ffn={f} k_in={k_in} k_mid={k_mid}")
-        _relu2_glu_case(gpu_lib, x, wg, wu, wd, k_in, k_mid, wtype)
+    with reduction_mode(gpu_lib, det):
+        for k_in, k_mid in [(d, f), ((2 * d) // 5, (2 * f) // 5), (1, 3), (0, 0), (d // 2, -1)]:
+            note(f"relu2-glu {wtype} det={det} rows={rows} d={d} ffn={f} k_in={k_in} k_mid={k_mid}")
+            _relu2_glu_case(gpu_lib, x, wg, wu, wd, k_in, k_mid, wtype)
 
 
 @pytest.mark.parametrize("batch", [1, 4, 8, 16])

@@ -11,7 +11,7 @@ import pytest
 
 import datagen
 import oracle
-from gpu_util import assert_within, note, to_dev
+from gpu_util import assert_within, note, reduction_mode, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -78,14 +78,61 @@ def test_linear_bf16_output_and_dense_k(gpu_lib):
 
 
 def test_linear_deterministic(gpu_lib):
+    """With fixed-order sums two runs agree bit for bit; the default (atomic)
+    sums stay within the same tolerance of the oracle in every run."""
     import torch
     rng = np.random.default_rng(47)
     x = datagen.bf16_round(datagen.student_t(rng, (5, 4096)))
     w = datagen.bf16_round(datagen.normal(rng, (4096, 4096), 0.02))
     note("linear run-twice determinism")
-    y1 = _run(gpu_lib, x, 1638, w, torch.bfloat16, torch.bfloat16, torch.float32)
-    y2 = _run(gpu_lib, x, 1638, w, torch.bfloat16, torch.bfloat16, torch.float32)
+    with reduction_mode(gpu_lib, True):
+        y1 = _run(gpu_lib, x, 1638, w, torch.bfloat16, torch.bfloat16, torch.float32)
+        y2 = _run(gpu_lib, x, 1638, w, torch.bfloat16, torch.bfloat16, torch.float32)
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    y_ref, t = _ref(x, 1638, w)
+    assert_within(y1, y_ref, t, 4e-3, "fixed order")
+    note("linear atomic split-K sums")
+    with reduction_mode(gpu_lib, False):
+        for _ in range(2):
+            y3 = _run(gpu_lib, x, 1638, w, torch.bfloat16, torch.bfloat16, torch.float32)
+            assert_within(y3, y_ref, t, 4e-3, "atomic sums")
+
+
+@pytest.mark.parametrize("wtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,d,n", [(1, 4096, 1024), (3, 1000, 520), (8, 2048, 264),
+                                      (16, 4096, 1024)])
+def test_gather_linear_acc(gpu_lib, wtype, rows, d, n):
+    """qs_gather_linear_acc adds Xs . W^T to what y holds (every kernel form:
+    1-8 token tiles, and 16-token bf16 MFMA tiles); fp32 weights in 16-token
+    tiles are refused."""
+    import torch
+    qs = gpu_lib
+    rng = np.random.default_rng(rows * 7 + d + n)
+    x = datagen.student_t(rng, (rows, d))
+    w = datagen.normal(rng, (n, d), 0.02)
+    y0 = datagen.normal(rng, (rows, n), 1.0).astype(np.float32)
+    dt = torch.float32 if wtype == "f32" else torch.bfloat16
+    tol = 1e-5 if wtype == "f32" else 4e-3
+    if wtype == "bf16":
+        x, w = datagen.bf16_round(x), datagen.bf16_round(w)
+    k = (2 * d) // 5
+    m_ref, _, _, _ = oracle.topk_select(oracle.magnitude(x), k)
+    xs = np.where(m_ref == 1, x, 0.0).astype(np.float32)
+    wt = to_dev(np.ascontiguousarray(w.T), dt)
+    y = to_dev(y0)
+    note(f"gather_linear_acc {wtype} rows={rows} d={d} n={n}")
+    if wtype == "f32" and rows > 8:
+        with pytest.raises(qs.QSError):
+            qs.qs_gather_linear_acc(to_dev(xs), wt, y)
+        return
+    qs.qs_gather_linear_acc(to_dev(xs), wt, y)
+    torch.cuda.synchronize()
+    y_ref, t = oracle.sparse_linear(x, w, m_ref)
+    got = y.cpu().numpy().astype(np.float64) - y0
+    # Each of the (at most 64) split additions into y0 rounds once in fp32 on a
+    # value of magnitude <= |y0| + T.
+    slack = 64 * 2.0 ** -24 * (np.abs(y0.astype(np.float64)) + t)
+    assert np.all(np.abs(got - y_ref) <= tol * t + slack), "y - y0 outside tol*T"
 
 
 def test_linear_full_c1(gpu_lib):
