@@ -498,7 +498,9 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     // clears the sums, and the selection of h maps them to h (so only with
     // k_mid >= 0).  Down projection: the selection of h clears y.
     qs::GemvPlan pd = qs::plan_gemv(rows, ffn, d, wb);
-    const bool acc_down = !deterministic() && k_mid >= 0 && yt == QS_F32 &&
+    // (y is cleared by the selection of h, or without one by the dReLU
+    // gate/up launch.)
+    const bool acc_down = !deterministic() && (k_mid >= 0 || drelu) && yt == QS_F32 &&
                           qs::gemv_accumulate_supported(pd, wb);
     bool acc_up = false, dual = false;
 
@@ -571,6 +573,7 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
         g.wg = (const uint16_t*)w_gate; g.wu = (const uint16_t*)w_up;
         g.bg = b_gate; g.bu = b_up; g.h = hbuf;
         g.zero_ptr = zeroed ? nullptr : wsp.ctr_up; g.n_zero = zeroed ? 0 : wsp.n_ctr;
+        if (acc_down && k_mid < 0) { g.zero_out = (float*)y; g.n_zero_out = rows * d; }
         e = qs::launch_drelu_gate_up(g, st);
         if (e != hipSuccess) return hip_fail(e, fn);
     }
@@ -754,11 +757,19 @@ qs_status qs_sparse_moe_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d,
     if (e != hipSuccess) return hip_fail(e, fn);
 
     // Gate, then up only where the gate is positive, per pair (dReLU).
+    // Accumulate form of the down gather (unless fixed-order sums are asked
+    // for): each pair's workgroups add weight * partial into its token's row
+    // of an fp32 sum that this launch clears: y itself (no combine launch),
+    // or for a bf16 y the pair buffer, which one pass then rounds into y.
+    qs::GemvPlan pd = qs::plan_gemv(pairs, ffn, d, 1, 1);
+    const bool acc = !deterministic() && qs::gemv_accumulate_supported(pd, 1);
+    float* yacc = yt == QS_F32 ? (float*)y : wsp.ypair;   // ypair holds pairs >= rows rows
     float* hbuf = h ? h : wsp.h;
     qs::DreluArgs g{};
     g.x = (const uint16_t*)x; g.rows = rows; g.d = d; g.ffn = ffn;
     g.wg = (const uint16_t*)w_gate; g.wu = (const uint16_t*)w_up; g.bg = b_gate; g.bu = b_up;
     g.h = hbuf; g.zero_ptr = wsp.ctr; g.n_zero = wsp.n_ctr;
+    if (acc) { g.zero_out = yacc; g.n_zero_out = rows * d; }
     g.pair_token = wsp.pair_token; g.pair_expert = wsp.pair_expert; g.pairs = pairs;
     if (rows > 1 && pairs <= kMoeGroupMaxPairs && rows * d * 2 < (int64_t(1) << 31)) {
         // Several tokens: group the pairs by expert so that each expert's gate
@@ -775,14 +786,23 @@ qs_status qs_sparse_moe_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d,
     if (e != hipSuccess) return hip_fail(e, fn);
 
     // Down: each pair gathers the rows of its expert's W_down^T where h != 0.
-    qs::GemvPlan pd = qs::plan_gemv(pairs, ffn, d, 1, 1);
     qs::GemvArgs gd{};
     gd.xs = hbuf; gd.rows = pairs; gd.d_in = ffn; gd.n_out = d; gd.w = w_down_t;
     gd.partial = wsp.partial; gd.counters = wsp.ctr; gd.y = wsp.ypair; gd.y_bf16 = 0;
     gd.epilogue = qs::EPI_STORE;
     gd.row_expert = wsp.pair_expert; gd.expert_bytes = ffn * d * 2;
+    if (acc) {
+        gd.y = yacc; gd.accumulate = 1;
+        gd.row_scale = wsp.pair_weight; gd.row_out = wsp.pair_token;
+    }
     e = qs::launch_gemv(pd, 1, gd, st);
     if (e != hipSuccess) return hip_fail(e, fn);
+    if (acc) {
+        if (yt == QS_F32) return ok();
+        e = qs::launch_moe_combine(yacc, nullptr, rows, 1, d, y, 1, st);   // weights already applied
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return ok();
+    }
 
     e = qs::launch_moe_combine(wsp.ypair, wsp.pair_weight, rows, (int)top_k, d, y, yt == QS_BF16, st);
     if (e != hipSuccess) return hip_fail(e, fn);

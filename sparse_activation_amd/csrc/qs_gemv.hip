@@ -341,7 +341,15 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
                         else if (nsplit > 1) store_agent(&a.partial2[((int64_t)split * rows + row) * n_out + cg], s);
                     }
                 } else if (row < rows && cg < n_out) {
-                    if (a.accumulate) unsafeAtomicAdd(&reinterpret_cast<float*>(a.y)[row * n_out + cg], s);
+                    if (a.accumulate) {
+                        int64_t orow = row;
+                        float v = s;
+                        if (BT == 1 && a.row_out != nullptr) {
+                            orow = a.row_out[row];
+                            v = __fmul_rn(a.row_scale[row], s);
+                        }
+                        unsafeAtomicAdd(&reinterpret_cast<float*>(a.y)[orow * n_out + cg], v);
+                    }
                     else if (nsplit > 1) store_agent(&a.partial[((int64_t)split * rows + row) * n_out + cg], s);
                     else if (DUAL) reinterpret_cast<float*>(a.y)[row * n_out + cg] = relu2_glu(gsum[q], s);
                     else store_final(a, row * n_out + cg, s);
@@ -1456,6 +1464,8 @@ bool gemv_accumulate_supported(const GemvPlan& p, int w_is_bf16) {
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     if (a.accumulate && (a.y_bf16 || a.epilogue != EPI_STORE || !gemv_accumulate_supported(p, w_is_bf16)))
+        return hipErrorInvalidValue;
+    if (a.row_out != nullptr && (!a.accumulate || p.bt != 1 || a.row_scale == nullptr))
         return hipErrorInvalidValue;
     const int ept = w_is_bf16 ? 8 : 4;
     const int ct = kFLPR * ept;

@@ -110,6 +110,11 @@ struct GemvArgs {
     // (epilogue must be EPI_STORE).  The sum order depends on timing.
     int accumulate;
     float* y2;
+    // Accumulate form with one-token tiles only (or null): row r's sums are
+    // scaled by row_scale[r] and added into output row row_out[r] (the MoE
+    // pairs' routing weights and tokens).
+    const float* row_scale;
+    const int32_t* row_out;
 };
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 // Both projections of the gated squared ReLU in one gather (tiles of at most
@@ -192,6 +197,8 @@ struct DreluArgs {
     float* h;                // [rows, ffn] fp32
     int32_t* zero_ptr;       // block 0 clears zero_ptr[0..n_zero) (split-K counters)
     int n_zero;
+    float* zero_out;         // or null: the launch's workgroups clear zero_out[0..n_zero_out)
+    int64_t n_zero_out;      //   (n_zero_out % 4 == 0): the output the down gather adds into
     // Mixture of experts (null for a plain FFN; one-token kernel only): launch
     // row r is the pair (token pair_token[r], expert pair_expert[r]); the
     // expert's matrices start at wg / wu + expert * ffn * d, its biases at
@@ -232,6 +239,8 @@ hipError_t launch_moe_route(const MoeRouteArgs& a, hipStream_t stream);
 hipError_t launch_moe_group(const int32_t* pair_expert, const int32_t* pair_token, int64_t pairs,
                             int n_experts, int32_t* count, int32_t* list, int32_t* tok,
                             hipStream_t stream);
+// y[t] = sum over j < top_k of pair_weight[t * top_k + j] * ypair[t * top_k + j]
+// (pair_weight null: weight 1, so top_k == 1 just rounds ypair into y).
 hipError_t launch_moe_combine(const float* ypair, const float* pair_weight, int64_t rows,
                               int top_k, int64_t d, void* y, int y_bf16, hipStream_t stream);
 

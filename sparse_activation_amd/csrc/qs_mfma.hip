@@ -536,6 +536,23 @@ __device__ __forceinline__ void drelu_partial(const uint16_t* __restrict__ x, in
     }
 }
 
+// Side jobs of a gate/up launch, done first (also by workgroups that then
+// find no work): workgroup 0 clears the split-K counters of the down gather,
+// and all workgroups together clear the output that the down gather adds into.
+// (The fields come by value: a reference to the kernel's argument struct
+// costs the kernels registers.)
+__device__ __forceinline__ void drelu_side_clear(int32_t* zero_ptr, int n_zero, float* zero_out,
+                                                 int64_t n_zero_out, int tid) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && zero_ptr != nullptr)
+        for (int i = tid; i < n_zero; i += 256) zero_ptr[i] = 0;
+    if (zero_out != nullptr) {   // (n_zero_out < 2^31, checked by the launchers)
+        const int n4 = (int)(n_zero_out / 4), step = (int)(gridDim.x * gridDim.y) * 256;
+        uint4* z = reinterpret_cast<uint4*>(zero_out);
+        for (int i = (int)(blockIdx.y * gridDim.x + blockIdx.x) * 256 + tid; i < n4; i += step)
+            z[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
 __global__ __launch_bounds__(256) void drelu_gate_up_kernel(DreluArgs a) {
     __shared__ f32x4 s_part[4][64];
     __shared__ __attribute__((aligned(16))) uint16_t s_tile[4][16 * kDreluPitch];
@@ -547,8 +564,7 @@ __global__ __launch_bounds__(256) void drelu_gate_up_kernel(DreluArgs a) {
     const int64_t n = n0 + r16;                 // this lane's neuron (B column / D column)
     const bool n_ok = n < ffn;
 
-    if (blockIdx.x == 0 && a.zero_ptr != nullptr)
-        for (int i = tid; i < a.n_zero; i += 256) a.zero_ptr[i] = 0;
+    drelu_side_clear(a.zero_ptr, a.n_zero, a.zero_out, a.n_zero_out, tid);
 
     for (int64_t tok0 = 0; tok0 < rows; tok0 += 16) {
         // gate partials
@@ -632,8 +648,7 @@ __global__ __launch_bounds__(256) void drelu_gate_up_b1_kernel(DreluArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t d = a.d, ffn = a.ffn;
     const int64_t nb = ((int64_t)blockIdx.x * 4 + wave) * NPW;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && a.zero_ptr != nullptr)
-        for (int i = tid; i < a.n_zero; i += 256) a.zero_ptr[i] = 0;
+    drelu_side_clear(a.zero_ptr, a.n_zero, a.zero_out, a.n_zero_out, tid);
     // Launch row blockIdx.y: the token itself, or a (token, expert) pair.
     const int64_t pr = blockIdx.y;
     int64_t tok = 0, ex = 0;
@@ -714,8 +729,7 @@ __global__ __launch_bounds__(256) void drelu_grouped_kernel(DreluArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t d = a.d, ffn = a.ffn;
     const int ex = blockIdx.y;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && a.zero_ptr != nullptr)
-        for (int i = tid; i < a.n_zero; i += 256) a.zero_ptr[i] = 0;
+    drelu_side_clear(a.zero_ptr, a.n_zero, a.zero_out, a.n_zero_out, tid);
     // Without expert lists (a dense FFN): one matrix, row t of x is h row t.
     const bool ident = a.grp_count == nullptr;
     const int32_t* gq = ident ? nullptr : a.grp_pairs + ex * a.pairs;
@@ -933,6 +947,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t stream) {
 
 hipError_t launch_drelu_gate_up(const DreluArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
+    if (a.zero_out != nullptr && (a.n_zero_out % 4 != 0 || a.n_zero_out >= (int64_t(1) << 31)))
+        return hipErrorInvalidValue;
     const unsigned blocks = (unsigned)((a.ffn + 15) / 16);
     const bool moe = a.pair_expert != nullptr;
     if (moe && a.d > 8192) return hipErrorInvalidValue;
@@ -960,6 +976,8 @@ hipError_t launch_drelu_gate_up(const DreluArgs& a, hipStream_t stream) {
 
 hipError_t launch_drelu_grouped(const DreluArgs& a, hipStream_t stream) {
     if (a.rows <= 0 || (a.grp_count != nullptr && a.pairs <= 0)) return hipSuccess;
+    if (a.zero_out != nullptr && (a.n_zero_out % 4 != 0 || a.n_zero_out >= (int64_t(1) << 31)))
+        return hipErrorInvalidValue;
     if (a.d > 8192 || a.n_experts < 1 || a.n_experts > 64 ||
         a.rows * a.d * 2 >= (int64_t(1) << 31) || a.ffn * a.d * 2 >= (int64_t(1) << 31))
         return hipErrorInvalidValue;

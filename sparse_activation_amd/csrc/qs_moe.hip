@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
     const int64_t t = i / per, c = (i % per) * 4;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int j = 0; j < top_k; ++j) {
-        const float wj = w[t * top_k + j];
+        const float wj = w != nullptr ? w[t * top_k + j] : 1.0f;
         const float4 v = *reinterpret_cast<const float4*>(ypair + (t * top_k + j) * d + c);
         acc[0] = __fmaf_rn(wj, v.x, acc[0]);
         acc[1] = __fmaf_rn(wj, v.y, acc[1]);

@@ -184,7 +184,8 @@ def _drelu_case(gpu_lib, x, wg, bg, wu, bu, wd, k_in=None, k_mid=-1):
 
 @pytest.mark.parametrize("rows,d,f", [(1, 64, 48), (3, 256, 520), (4, 200, 136), (16, 512, 264),
                                       (21, 200, 136)])
-def test_drelu_small(gpu_lib, rows, d, f):
+@pytest.mark.parametrize("det", [False, True])
+def test_drelu_small(gpu_lib, rows, d, f, det):
     rng = np.random.default_rng(rows * 5 + d + f)
     x = datagen.bf16_round(datagen.student_t(rng, (rows, d)))
     wg = datagen.bf16_round(datagen.normal(rng, (f, d), 0.02))
@@ -192,10 +193,11 @@ def test_drelu_small(gpu_lib, rows, d, f):
     wd = datagen.bf16_round(datagen.normal(rng, (d, f), 0.02))
     bg = rng.normal(-0.2, 0.1, size=f).astype(np.float32)
     bu = rng.normal(-0.2, 0.1, size=f).astype(np.float32)
-    note(f"drelu rows={rows} d={d} ffn={f} (biases)")
-    _drelu_case(gpu_lib, x, wg, bg, wu, bu, wd)
-    note(f"drelu rows={rows} d={d} ffn={f} (no biases, top-K on x and on h)")
-    _drelu_case(gpu_lib, x, wg, None, wu, None, wd, k_in=d // 2, k_mid=f // 3)
+    with reduction_mode(gpu_lib, det):
+        note(f"drelu det={det} rows={rows} d={d} ffn={f} (biases)")
+        _drelu_case(gpu_lib, x, wg, bg, wu, bu, wd)
+        note(f"drelu det={det} rows={rows} d={d} ffn={f} (no biases, top-K on x and on h)")
+        _drelu_case(gpu_lib, x, wg, None, wu, None, wd, k_in=d // 2, k_mid=f // 3)
 
 
 @pytest.mark.parametrize("batch", [1, 4, 16])

@@ -16,7 +16,7 @@ import pytest
 
 import datagen
 import oracle
-from gpu_util import note, to_dev
+from gpu_util import note, reduction_mode, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -66,19 +66,25 @@ def _moe_case(qs, c, top_k, ydt=None):
 @pytest.mark.parametrize("rows,d,ffn,e,k", [(1, 256, 512, 8, 2), (3, 256, 520, 8, 2),
                                             (16, 512, 264, 8, 2), (5, 128, 136, 4, 1),
                                             (4, 64, 48, 6, 3), (12, 128, 136, 2, 1)])
-def test_moe_small(gpu_lib, rows, d, ffn, e, k):
+@pytest.mark.parametrize("det", [False, True])
+def test_moe_small(gpu_lib, rows, d, ffn, e, k, det):
+    """det: fixed-order sums and the combine launch; else each pair's down
+    gather adds weight * partial straight into its token's row of y."""
     sigma = 0.02 * np.sqrt(2.0 * d)
     c = datagen.c6_moe_drelu_ffn(rows, d=d, ffn=ffn, n_experts=e, bias=-0.2864 * sigma)
-    note(f"moe rows={rows} d={d} ffn={ffn} E={e} k={k}")
-    zf = _moe_case(gpu_lib, c, k)
+    note(f"moe det={det} rows={rows} d={d} ffn={ffn} E={e} k={k}")
+    with reduction_mode(gpu_lib, det):
+        zf = _moe_case(gpu_lib, c, k)
     assert 0.6 < zf < 0.98
 
 
-def test_moe_bf16_output(gpu_lib):
+@pytest.mark.parametrize("det", [False, True])
+def test_moe_bf16_output(gpu_lib, det):
     import torch
     c = datagen.c6_moe_drelu_ffn(2, d=256, ffn=512, bias=-0.13)
-    note("moe bf16 y")
-    _moe_case(gpu_lib, c, 2, ydt=torch.bfloat16)
+    note(f"moe bf16 y det={det}")
+    with reduction_mode(gpu_lib, det):
+        _moe_case(gpu_lib, c, 2, ydt=torch.bfloat16)
 
 
 def test_moe_full_mixtral(gpu_lib):
