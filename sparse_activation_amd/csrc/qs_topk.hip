@@ -606,7 +606,6 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int64_t d = a.d, k = a.k, row0 = (int64_t)r * d;
 
-    clear_side_buffers<NT>(a, r, tid);
     sel::select_clear<NT, KB>(s_sel, tid);
 
     // ---- load runs (past the row end the buffer reads zero)
@@ -621,6 +620,8 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
         unpack_raw<KK>(w, raw + q * V);
     }
     auto run_valid = [&](int q) { return (int64_t)q * CS + V * tid < d; };   // d % V == 0
+    // The side stores go out behind the row's loads, which start the critical chain.
+    clear_side_buffers<NT>(a, r, tid);
 
     // Elementwise map of the row before the selection (the FFN intermediate
     // from raw projection sums): h = relu(u)^2, or relu(g)^2 * u with the
