@@ -39,6 +39,22 @@ qs_status hip_fail(hipError_t e, const char* where) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Whether the selection launch over rows of length d can write the 16-token
+// MFMA gather's packed records (its vector kernel, whole 8-entry chunks).
+bool records_ok(int64_t d) { return d % 8 == 0 && d <= 16384; }
+
+// Points a selection launch at the packed records of the gather planned by p
+// (when that gather would pack them itself) and marks the gather to read
+// them.  frag_lo: the values are not all bf16 numbers.
+void route_records(qs::TopkArgs& t, qs::GemvArgs& g, const qs::GemvPlan& p, int wb, int64_t rows,
+                   int64_t d_in, float* partial, int frag_lo) {
+    if (!qs::gemv_packs_records(p, wb, rows) || !records_ok(d_in)) return;
+    t.frag = qs::gemv_records(p, partial, d_in, &t.frag_groups);
+    t.frag_lo = frag_lo;
+    t.xs = nullptr;   // the gather reads the records only
+    g.frag_ready = 2;
+}
+
 // Bump allocator over the caller's workspace (256-byte aligned regions).
 struct Carve {
     size_t off = 0;
@@ -328,14 +344,15 @@ qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_i
     t.xs = wsp.xs;
     t.zero_ptr = wsp.counters; t.n_zero = plan.n_counters;
     if (acc) { t.zero_rows = (int32_t*)y; t.zero_row_len = n_out; }
-    e = qs::launch_topk(kk, qs::XS_F32, rows, t, st);
-    if (e != hipSuccess) return hip_fail(e, fn);
     qs::GemvArgs g{};
     g.xs = wsp.xs; g.rows = rows; g.d_in = d_in; g.n_out = n_out; g.w = w;
     g.partial = wsp.partial; g.counters = wsp.counters; g.y = y; g.y_bf16 = yt == QS_BF16;
     g.epilogue = qs::EPI_STORE;
     g.accumulate = acc ? 1 : 0;
     g.xs_bf16 = xt == QS_BF16;
+    route_records(t, g, plan, wb, rows, d_in, wsp.partial, xt != QS_BF16);
+    e = qs::launch_topk(kk, qs::XS_F32, rows, t, st);
+    if (e != hipSuccess) return hip_fail(e, fn);
     e = qs::launch_gemv(plan, wb, g, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
@@ -519,14 +536,19 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
             t.zero_rows2 = dual ? (int32_t*)wsp.gacc : nullptr;
             t.zero_row_len = ffn;
         }
-        e = qs::launch_topk(kk, qs::XS_F32, rows, t, st);
-        if (e != hipSuccess) return hip_fail(e, fn);
         qs::GemvArgs g{};
         g.xs = wsp.xs1; g.rows = rows; g.d_in = d; g.n_out = ffn; g.w = w_up;
         g.partial = wsp.partial; g.counters = wsp.ctr_up; g.y = hbuf; g.y_bf16 = 0;
         g.epilogue = acc_up ? qs::EPI_STORE : qs::EPI_RELU2;
         g.accumulate = acc_up ? 1 : 0;
         g.xs_bf16 = dt == QS_BF16;
+        // (The non-dual gated form runs two gathers over the same xs.)
+        // (Not for the gated forms: the dual gather measured slower reading
+        // records at its register budget, and the non-dual one runs two
+        // gathers over the same xs.)
+        if (act == QS_ACT_RELU2) route_records(t, g, pu, wb, rows, d, wsp.partial, dt != QS_BF16);
+        e = qs::launch_topk(kk, qs::XS_F32, rows, t, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
         if (dual) {
             // Both projections in one gather: the gate's and the up rows of
             // each selected feature are streamed together, and the last
@@ -579,6 +601,11 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     }
 
     // Stage 2: select the intermediate entries that enter W_down.
+    qs::GemvArgs g{};   // the down gather (stage 3)
+    g.rows = rows; g.d_in = ffn; g.n_out = d; g.w = w_down_t;
+    g.partial = wsp.partial; g.counters = wsp.ctr_down; g.y = y; g.y_bf16 = yt == QS_BF16;
+    g.epilogue = qs::EPI_STORE;
+    g.accumulate = acc_down ? 1 : 0;
     const float* hsel = hbuf;
     if (k_mid >= 0) {
         qs::TopkArgs t{};
@@ -593,6 +620,7 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
             t.h_out = h;
         }
         if (acc_down) { t.zero_rows = (int32_t*)y; t.zero_row_len = d; }
+        route_records(t, g, pd, wb, rows, ffn, wsp.partial, 1);
         e = qs::launch_topk(qs::KEY_F32, qs::XS_F32, rows, t, st);
         if (e != hipSuccess) return hip_fail(e, fn);
         hsel = wsp.hs;
@@ -602,11 +630,7 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     }
 
     // Stage 3: gathered down projection.
-    qs::GemvArgs g{};
-    g.xs = hsel; g.rows = rows; g.d_in = ffn; g.n_out = d; g.w = w_down_t;
-    g.partial = wsp.partial; g.counters = wsp.ctr_down; g.y = y; g.y_bf16 = yt == QS_BF16;
-    g.epilogue = qs::EPI_STORE;
-    g.accumulate = acc_down ? 1 : 0;
+    g.xs = hsel;
     e = qs::launch_gemv(pd, wb, g, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();

@@ -685,12 +685,17 @@ __global__ __launch_bounds__(kNT) void bfrag_kernel(const float* xs, int64_t row
 // loads columns 8 c8 .. 8 c8 + 7 of rows 4 r8 .. 4 r8 + 3 of the group (whole
 // 128-byte row segments), which a per-wave LDS tile turns into the k-major B
 // operand.  The row mask of a group is fetched one stage ahead of its weights.
-// FUSED: no packed records; each lane loads its 8 coefficients of a group two
-// stages ahead and forms its fragments and the group's row mask itself, as
-// bfrag_kernel does (the same values, so the same result).
+// MODE 0: packed records and row masks from bfrag_kernel.
+// MODE 1 (fused): no packed records; each lane loads its 8 coefficients of a
+// group two stages ahead and forms its fragments and the group's row mask
+// itself, as bfrag_kernel does (the same values, so the same result).
+// MODE 2: packed records written by the selection kernel, no masks: each lane
+// loads its records two stages ahead and the group's row mask is formed by
+// ballot over their nonzero entries.  (A value whose hi and lo parts are both
+// zero multiplies to zero either way, so the skipped rows change nothing.)
 // DUAL: a second matrix (a.w2, the gate) is streamed at the same rows with the
 // same A fragments into a second set of sums; y = relu2_glu(gate, up).
-template <bool FUSED, bool DUAL = false>
+template <int MODE, bool DUAL = false>
 __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf, int cand, int nsplit,
                                                           int use_lo) {
     constexpr int BT = 16;
@@ -753,11 +758,37 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
     auto load_x = [&](u32x4* x, int s) {
         const int64_t g = g0 + 4 * s + wave;
         const int64_t j = g * kBGroup + 8 * kq;
+        if constexpr (MODE == 2) {
+            // Records of tokens past the batch and of chunks past d_in were
+            // never written: they load as zero.
+            const uint32_t fo = (n16 < ntok && j < d_in) ? (uint32_t)(((4 * s + wave) * 128 + lane) * 16) : kOOB;
+            x[0] = __builtin_amdgcn_raw_buffer_load_b128(frr, fo, 0, 0);
+            x[1] = __builtin_amdgcn_raw_buffer_load_b128(frr, use_lo && fo != kOOB ? fo + 64 * 16 : kOOB, 0, 0);
+            return;
+        }
         const uint32_t o = (n16 < ntok && 4 * s + wave < gl) ? (uint32_t)((n16 * d_in + j) * 4) : kOOB;
         x[0] = __builtin_amdgcn_raw_buffer_load_b128(xr, o, 0, 0);
         x[1] = __builtin_amdgcn_raw_buffer_load_b128(xr, o == kOOB ? kOOB : o + 16, 0, 0);
     };
     auto convert = [&](const u32x4* x, u32x4* f, uint32_t& m, int s) {
+        if constexpr (MODE == 2) {
+            const uint32_t hw[4] = {x[0].x, x[0].y, x[0].z, x[0].w};
+            const uint32_t lw[4] = {x[1].x, x[1].y, x[1].z, x[1].w};
+            uint32_t rowbits = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t nz = ((hw[e >> 1] | lw[e >> 1]) >> (16 * (e & 1))) & 0xFFFFu;
+                const uint64_t b = __ballot(nz != 0u);
+                rowbits |= (uint32_t)((b & 0xFFFFull) ? 1u : 0u) << e;
+                rowbits |= (uint32_t)(((b >> 16) & 0xFFFFull) ? 1u : 0u) << (8 + e);
+                rowbits |= (uint32_t)(((b >> 32) & 0xFFFFull) ? 1u : 0u) << (16 + e);
+                rowbits |= (uint32_t)(((b >> 48) & 0xFFFFull) ? 1u : 0u) << (24 + e);
+            }
+            f[0] = x[0];
+            f[1] = x[1];
+            m = rowbits;
+            return;
+        }
         const int64_t j = (g0 + 4 * s + wave) * kBGroup + 8 * kq;
         const uint32_t u[8] = {x[0].x, x[0].y, x[0].z, x[0].w, x[1].x, x[1].y, x[1].z, x[1].w};
         uint32_t hw[4], lw[4], rowbits = 0;
@@ -822,8 +853,9 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
     // The first two stages load every row without waiting for their masks
     // (a skipped row only saves bandwidth; its coefficients are zero).
     u32x4 wa[4 * NM], wb[4 * NM], fa[2], fb[2];
-    if constexpr (FUSED) {
-        // The same schedule with the coefficients in place of the records:
+    if constexpr (MODE != 0) {
+        // The same schedule with the coefficients (or the unmasked records)
+        // in place of the records:
         // those of stage s + 2 are converted just before its weights are
         // loaded (their mask decides which rows move).
         u32x4 xa[2], xb[2], xc[2], xd[2];
@@ -1457,6 +1489,30 @@ GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16, int
     return p;
 }
 
+// Forming the fragments inside the gather converts each group once per column
+// tile instead of once, but saves the packing launch: it pays for a half-empty
+// tile (8 tokens: 65.4 us per Llama-7B FFN step against 67.1), not for a full
+// one (69.2 against 68.6).  QS_BMFMA_FUSED=0/1 forces either (a tuning knob
+// for measurements).
+bool bmfma_fused(int64_t rows) {
+    static const int v = [] {
+        const char* fe = getenv("QS_BMFMA_FUSED");
+        return fe ? (fe[0] == '1' ? 1 : 0) : -1;
+    }();
+    return v >= 0 ? v == 1 : rows <= 8;
+}
+
+bool gemv_packs_records(const GemvPlan& p, int w_is_bf16, int64_t rows) {
+    return p.bt == 16 && w_is_bf16 && !bmfma_fused(rows);
+}
+
+void* gemv_records(const GemvPlan& p, float* partial, int64_t d_in, int64_t* groups) {
+    const BFrag bf = bfrag_carve(reinterpret_cast<char*>(partial) + (p.partial_floats * 4 + 255) / 256 * 256,
+                                 d_in, p.n_tok_tiles);
+    *groups = bf.groups;
+    return bf.frag;
+}
+
 bool gemv_accumulate_supported(const GemvPlan& p, int w_is_bf16) {
     return !(p.bt == 16 && !w_is_bf16);
 }
@@ -1475,21 +1531,18 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
         const BFrag bf = bfrag_carve(reinterpret_cast<char*>(a.partial) + (p.partial_floats * 4 + 255) / 256 * 256,
                                      a.d_in, p.n_tok_tiles);
         const int use_lo = a.xs_bf16 ? 0 : 1;
-        // Forming the fragments inside the gather converts each group once
-        // per column tile instead of once, but saves the packing launch: it
-        // pays for a half-empty tile (8 tokens: 65.4 us per Llama-7B FFN step
-        // against 67.1), not for a full one (69.2 against 68.6).
-        // QS_BMFMA_FUSED=0/1 forces either (a tuning knob for measurements).
-        const char* fe = getenv("QS_BMFMA_FUSED");
-        const bool fused = fe ? fe[0] == '1' : a.rows <= 8;
-        if (fused) {
-            gather_bmfma_kernel<true><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
+        if (a.frag_ready == 2) {   // records from the selection launch
+            gather_bmfma_kernel<2><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
+            return hipGetLastError();
+        }
+        if (bmfma_fused(a.rows)) {
+            gather_bmfma_kernel<1><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
             return hipGetLastError();
         }
         if (!a.frag_ready)
             bfrag_kernel<<<dim3((unsigned)ceil_div(bf.groups, 4), p.n_tok_tiles), dim3(kNT), 0, stream>>>(
                 a.xs, a.rows, a.d_in, use_lo, bf);
-        gather_bmfma_kernel<false><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
+        gather_bmfma_kernel<0><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
         return hipGetLastError();
     }
     if (p.bt == 16) {
@@ -1530,15 +1583,14 @@ hipError_t launch_gemv_dual(const GemvPlan& p, int w_is_bf16, const GemvArgs& a,
         const BFrag bf = bfrag_carve(reinterpret_cast<char*>(a.partial) + (p.partial_floats * 4 + 255) / 256 * 256,
                                      a.d_in, p.n_tok_tiles);
         const int use_lo = a.xs_bf16 ? 0 : 1;
-        const char* fe = getenv("QS_BMFMA_FUSED");
-        const bool fused = fe ? fe[0] == '1' : a.rows <= 8;
-        if (fused) {
-            gather_bmfma_kernel<true, true><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
+        if (a.frag_ready == 2) return hipErrorNotSupported;   // records come with masks here
+        if (bmfma_fused(a.rows)) {
+            gather_bmfma_kernel<1, true><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
             return hipGetLastError();
         }
         bfrag_kernel<<<dim3((unsigned)ceil_div(bf.groups, 4), p.n_tok_tiles), dim3(kNT), 0, stream>>>(
             a.xs, a.rows, a.d_in, use_lo, bf);
-        gather_bmfma_kernel<false, true><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
+        gather_bmfma_kernel<0, true><<<grid, dim3(kNT), 0, stream>>>(a, bf, p.cand, p.nsplit, use_lo);
         return hipGetLastError();
     }
     const int ept = w_is_bf16 ? 8 : 4;

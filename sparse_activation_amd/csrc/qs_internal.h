@@ -50,6 +50,14 @@ struct TopkArgs {
     int xform;
     const float* x2;
     float* h_out;
+    // XS_F32 kinds of the vector kernel only (or null): the selected values
+    // are also written as the packed A-operand records of the 16-token MFMA
+    // gather (bf16 hi parts, and with frag_lo the bf16 lo parts of the
+    // remainder; the layout of bfrag_kernel, without its row masks): row r is
+    // token r % 16 of token tile r / 16, frag_groups = ceil(d / 32).
+    void* frag;
+    int64_t frag_groups;
+    int frag_lo;
 };
 enum Xform : int { XF_NONE = 0, XF_RELU2 = 1, XF_RELU2_GLU = 2 };
 bool topk_xform_supported(int64_t d);
@@ -100,9 +108,10 @@ struct GemvArgs {
     // split partials go to partial2 ([nsplit, rows, n_out]).
     const void* w2;
     float* partial2;
-    // 16-token bf16 tiles: the packed coefficient records behind `partial`
-    // were written by a previous gather over the same xs (and plan), so the
-    // packing launch is skipped.
+    // 16-token bf16 tiles: 1 = the packed coefficient records and row masks
+    // behind `partial` were written by a previous gather over the same xs
+    // (and plan), so the packing launch is skipped; 2 = the records (no
+    // masks) were written by the selection launch (xs is not read).
     int frag_ready;
     // 1: y is fp32 and already holds the values to add to; every workgroup
     // adds its partial tile into y (and the dual gather its gate tile into
@@ -124,6 +133,12 @@ bool gemv_dual_supported(const GemvPlan& p, int w_is_bf16);
 hipError_t launch_gemv_dual(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 // Plans whose kernel has the accumulate form (all but fp32 16-token tiles).
 bool gemv_accumulate_supported(const GemvPlan& p, int w_is_bf16);
+// Plans whose launch packs the coefficients into MFMA records first (bf16
+// weights in full 16-token tiles).  A selection launch can write those
+// records instead (TopkArgs::frag at gemv_records(), frag_ready = 2 here;
+// launch_gemv only, not the dual gather).
+bool gemv_packs_records(const GemvPlan& p, int w_is_bf16, int64_t rows);
+void* gemv_records(const GemvPlan& p, float* partial, int64_t d_in, int64_t* groups);
 
 // ---------------------------------------------------------------- ternary x int8 gather
 struct I8tPlan {

@@ -540,6 +540,14 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
 // at once, one barrier each), after which every thread writes its runs with
 // vector stores.
 // ---------------------------------------------------------------------------
+// bf16 round-to-nearest-even of an fp32 value (finite inputs), as the
+// 16-token MFMA gather's packing splits a coefficient into hi + lo.
+__device__ __forceinline__ uint32_t frag_bf16_rne(float f) {
+    uint32_t b = __float_as_uint(f);
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return b >> 16;
+}
+
 template <int KK> struct VecOf;
 template <> struct VecOf<KEY_F32> { static constexpr int V = 4; };
 template <> struct VecOf<KEY_Q8> { static constexpr int V = 4; };
@@ -819,6 +827,31 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
                 for (int e = 0; e < V; e += 4)
                     *reinterpret_cast<uint4*>(xp + e) = make_uint4(xsv[e], xsv[e + 1], xsv[e + 2], xsv[e + 3]);
             }
+            if (a.frag != nullptr) {
+                // Entries j0 .. j0 + V - 1 lie in one 8-entry chunk (V = 4 or
+                // 8, j0 % V == 0): chunk (j0 % 32) / 8 of row group j0 / 32,
+                // the record slot of token r % 16.
+                uint32_t hi[V / 2], lo[V / 2];
+#pragma unroll
+                for (int e = 0; e < V; e += 2) {
+                    const float c0 = __uint_as_float(xsv[e]), c1 = __uint_as_float(xsv[e + 1]);
+                    const uint32_t h0 = frag_bf16_rne(c0), h1 = frag_bf16_rne(c1);
+                    hi[e / 2] = h0 | (h1 << 16);
+                    lo[e / 2] = frag_bf16_rne(c0 - __uint_as_float(h0 << 16)) |
+                                (frag_bf16_rne(c1 - __uint_as_float(h1 << 16)) << 16);
+                }
+                const int64_t slot = ((int64_t)(r / 16) * a.frag_groups + j0 / 32) * 128 +
+                                     16 * ((j0 % 32) / 8) + r % 16;
+                char* base = reinterpret_cast<char*>(a.frag) + slot * 16 + (j0 % 8) * 2;
+                if constexpr (V == 8) {
+                    *reinterpret_cast<uint4*>(base) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+                    if (a.frag_lo)
+                        *reinterpret_cast<uint4*>(base + 64 * 16) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+                } else {
+                    *reinterpret_cast<uint2*>(base) = make_uint2(hi[0], hi[1]);
+                    if (a.frag_lo) *reinterpret_cast<uint2*>(base + 64 * 16) = make_uint2(lo[0], lo[1]);
+                }
+            }
         } else if constexpr (XK == XS_BF16) {
             if (a.xs != nullptr) {
                 uint16_t* xp = reinterpret_cast<uint16_t*>(a.xs) + row0 + j0;   // V == 8
@@ -946,6 +979,12 @@ hipError_t launch_topk(int key_kind, int xs_kind, int64_t rows, const TopkArgs& 
          (a.xform == XF_RELU2_GLU && a.x2 == nullptr)))
         return hipErrorInvalidValue;
     if ((a.zero_rows != nullptr || a.zero_rows2 != nullptr) && a.zero_row_len % 4 != 0)
+        return hipErrorInvalidValue;
+    // Packed records: fp32 values of the vector kernel (d % 8 == 0 keeps every
+    // run inside one 8-entry chunk).
+    if (a.frag != nullptr &&
+        (xs_kind != XS_F32 || (key_kind != KEY_F32 && key_kind != KEY_BF16) || a.d % 8 != 0 ||
+         a.d > 16384 || a.frag_groups != (a.d + 31) / 32))
         return hipErrorInvalidValue;
     // Few rows (decode): one big workgroup per row; many rows: smaller ones.
     if (rows <= 64) return launch_nt<1024>(key_kind, xs_kind, rows, a, stream);
