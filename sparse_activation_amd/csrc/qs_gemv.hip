@@ -13,14 +13,18 @@
 //     it loads the sparsified activations xs of its token tile for that
 //     range, and one wavefront ballot per 64 candidates compacts the rows
 //     that some token selects into an LDS list (ascending);
-//   * each half-wavefront streams one selected W^T row segment per step
-//     with 16-byte loads (512 contiguous bytes per row per instruction),
-//     four rows in flight per lane, and accumulates into fp32 registers;
-//   * the eight row slots of the workgroup are summed in LDS in a fixed
-//     order, the split's partial tile goes to the workspace, and the last
+//   * eight lanes stream one selected W^T row segment of 128 bytes with
+//     16-byte loads (eight rows per wavefront instruction), several rows in
+//     flight per lane in two ping-pong register stages, and accumulate into
+//     fp32 registers;
+//   * the row slots of the workgroup are summed in LDS in a fixed order;
+//     then either (accumulate form, fp32 outputs) the partial tile is added
+//     into y, which an earlier launch cleared, with float atomics, so the
+//     rounding depends on the order in which the splits arrive; or (fixed
+//     order) the split's partial tile goes to the workspace and the last
 //     workgroup of each column tile (device-scope counter) sums the splits
-//     in split order, applies the epilogue and stores y.  No floating-point
-//     atomics: the result is bitwise reproducible.
+//     in split order, applies the epilogue and stores y: bitwise
+//     reproducible.
 //
 // The ternary x int8 variant does the same with 2-bit packed weights and
 // exact int32 accumulation.
