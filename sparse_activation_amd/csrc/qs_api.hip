@@ -48,7 +48,7 @@ bool records_ok(int64_t d) { return d % 8 == 0 && d <= 16384; }
 // them.  frag_lo: the values are not all bf16 numbers.
 void route_records(qs::TopkArgs& t, qs::GemvArgs& g, const qs::GemvPlan& p, int wb, int64_t rows,
                    int64_t d_in, float* partial, int frag_lo) {
-    if (!qs::gemv_packs_records(p, wb, rows) || !records_ok(d_in)) return;
+    if (!qs::gemv_takes_records(p, wb, rows) || !records_ok(d_in)) return;
     t.frag = qs::gemv_records(p, partial, d_in, &t.frag_groups);
     t.frag_lo = frag_lo;
     t.xs = nullptr;   // the gather reads the records only

@@ -133,11 +133,11 @@ bool gemv_dual_supported(const GemvPlan& p, int w_is_bf16);
 hipError_t launch_gemv_dual(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 // Plans whose kernel has the accumulate form (all but fp32 16-token tiles).
 bool gemv_accumulate_supported(const GemvPlan& p, int w_is_bf16);
-// Plans whose launch packs the coefficients into MFMA records first (bf16
-// weights in full 16-token tiles).  A selection launch can write those
-// records instead (TopkArgs::frag at gemv_records(), frag_ready = 2 here;
-// launch_gemv only, not the dual gather).
-bool gemv_packs_records(const GemvPlan& p, int w_is_bf16, int64_t rows);
+// Plans (bf16 weights in 16-token tiles of at least 8 tokens) whose gather
+// reads the coefficients best as packed MFMA records written by the selection
+// launch (TopkArgs::frag at gemv_records(), frag_ready = 2 here; launch_gemv
+// only, not the dual gather).
+bool gemv_takes_records(const GemvPlan& p, int w_is_bf16, int64_t rows);
 void* gemv_records(const GemvPlan& p, float* partial, int64_t d_in, int64_t* groups);
 
 // ---------------------------------------------------------------- ternary x int8 gather
