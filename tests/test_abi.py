@@ -87,6 +87,32 @@ def test_gather_linear_validation():
                                 None) == 1
 
 
+def test_gather_linear_acc_validation():
+    """Y += Xs . W^T takes qs_gather_linear's workspace and checks; fp32 weights
+    in 16-token tiles have no accumulate form."""
+    lib = qs.load()
+    need = qs.qs_workspace_bytes(qs.OP_GATHER_LINEAR, 2, 512, 256)
+    assert lib.qs_gather_linear_acc(FAKE, 2, 512, FAKE, qs.BF16, 252, FAKE, FAKE, need, None) == 2
+    assert lib.qs_gather_linear_acc(FAKE, 2, 512, FAKE, qs.BF16, 256, FAKE, FAKE, need - 1,
+                                    None) == 3
+    assert lib.qs_gather_linear_acc(None, 2, 512, FAKE, qs.BF16, 256, FAKE, FAKE, need, None) == 1
+    need16 = qs.qs_workspace_bytes(qs.OP_GATHER_LINEAR, 16, 512, 256)
+    assert lib.qs_gather_linear_acc(FAKE, 16, 512, FAKE, qs.F32, 256, FAKE, FAKE, need16,
+                                    None) == 2
+    assert "8 rows" in qs.qs_last_error()
+
+
+def test_set_deterministic_returns_previous_setting():
+    lib = qs.load()
+    prev = lib.qs_set_deterministic(1)
+    try:
+        assert lib.qs_set_deterministic(0) == 1
+        assert lib.qs_set_deterministic(7) == 0      # any nonzero value means on
+        assert qs.qs_set_deterministic(False) is True
+    finally:
+        lib.qs_set_deterministic(prev)
+
+
 def test_stream_read_validation():
     lib = qs.load()
     assert lib.qs_stream_read(None, 1024, FAKE, None) == 1
