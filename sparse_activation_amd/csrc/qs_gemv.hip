@@ -1451,7 +1451,8 @@ __global__ __launch_bounds__(kNT) void i8t_mfma_kernel(I8tArgs a, int nsplit) {
 
 }  // namespace
 
-GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16, int max_bt) {
+GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16, int max_bt,
+                   int64_t target) {
     GemvPlan p{};
     p.lpr = kLPR;
     p.ept = w_is_bf16 ? 8 : 4;
@@ -1477,7 +1478,7 @@ GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16, int
     } else {
         // The FMA kernels stage <= 32 KB of coefficients in LDS.
         const int cand_max = 8192 / p.bt < kFMaxCand ? 8192 / p.bt : kFMaxCand;
-        int64_t ns = ceil_div(target_wg(), base);
+        int64_t ns = ceil_div(target > 0 ? target : target_wg(), base);
         if (ns < 1) ns = 1;
         cand = ceil_div(ceil_div(d_in, ns), 64) * 64;
         if (cand > cand_max) cand = cand_max;

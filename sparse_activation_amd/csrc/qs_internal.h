@@ -88,7 +88,10 @@ struct GemvPlan {
 };
 // max_bt caps the tokens per tile (1: every row its own tile, e.g. when rows
 // use different weight matrices, see GemvArgs::row_expert).
-GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16, int max_bt = 16);
+// target_wg > 0: the workgroup count the split-K plan aims for (else the
+// default; the plan is still a function of its arguments only).
+GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16, int max_bt = 16,
+                   int64_t target_wg = 0);
 
 struct GemvArgs {
     const float* xs;       // [rows, d_in] fp32, zero where not selected
