@@ -37,6 +37,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -52,6 +53,10 @@ METRIC = "sparse-linear tokens/s and HBM GB/s (% of roofline) at 7B FFN decode, 
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 N_XROT = 8
+C2_COPIES = 16    # relu2 FFN: 16 x 180 MB
+C2G_COPIES = 8    # gated relu2 FFN: 8 x 271 MB (108 MB read per step at one token)
+C5_COPIES = 6     # dReLU FFN: 6 x 352 MB (the whole gate, 117 MB, is read every step)
+C6_COPIES = 3     # MoE: 3 x 2.8 GB (two experts' 361 MB per step)
 
 
 def parse_args():
@@ -64,6 +69,10 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--roofline-launches", type=int, default=96)
+    p.add_argument("--weight-copies", type=int, default=0,
+                   help="weight copies to rotate over (0: the workload's default)")
+    p.add_argument("--replays", type=int, default=50,
+                   help="extra replays of the timed graph for the median per step")
     p.add_argument("--deterministic", action="store_true",
                    help="fixed-order split-K sums (qs_set_deterministic(1)) instead of float atomics")
     p.add_argument("--copy-calibration", action="store_true",
@@ -75,8 +84,12 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def time_graph(torch, stream, fn, steps, warmup):
-    """Warm up eagerly, capture `steps` calls of fn(i) in a graph, time one replay."""
+def time_graph(torch, stream, fn, steps, warmup, replays=0):
+    """Warm up eagerly, capture `steps` calls of fn(i) in one HIP graph, time
+    one replay bracketed by device synchronisations (the timed region of the
+    JSON line).  With replays > 0 the same graph is then replayed that many
+    more times, each replay between two events on the stream, and the
+    per-replay times (ms) are returned as well."""
     with torch.cuda.stream(stream):
         for i in range(warmup):
             fn(i)
@@ -94,7 +107,31 @@ def time_graph(torch, stream, fn, steps, warmup):
         graph.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-    return e0.elapsed_time(e1)
+        ms = e0.elapsed_time(e1)
+        if replays <= 0:
+            return ms
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+        ev[0].record(stream)
+        for r in range(replays):
+            graph.replay()
+            ev[r + 1].record(stream)
+        torch.cuda.synchronize()
+    return ms, [ev[r].elapsed_time(ev[r + 1]) for r in range(replays)]
+
+
+def replay_stats(per_replay_ms, steps):
+    """Median / min / max time per step over graph replays of `steps` steps."""
+    import statistics
+    per = [m * 1e3 / steps for m in per_replay_ms]
+    return {"replays": len(per), "steps_per_replay": steps,
+            "median_us_per_step": round(statistics.median(per), 3),
+            "min_us_per_step": round(min(per), 3), "max_us_per_step": round(max(per), 3)}
+
+
+def time_steps(args, torch, stream, fn, steps, warmup):
+    """(ms per step of the timed region, replay statistics) for `steps` steps."""
+    ms, per = time_graph(torch, stream, fn, steps, warmup, replays=args.replays)
+    return ms / steps, replay_stats(per, steps)
 
 
 def committed_traffic(kernel_src: str, name: str):
@@ -124,6 +161,16 @@ def copy_calibration(torch, dev):
     log("copy calibration: 3 x 256 MiB device copies")
 
 
+def probe_library():
+    """qsprobe_stream_read from _lib/libqs_probe.so (a measurement probe built
+    beside libqs.so, not part of its ABI)."""
+    path = os.path.join(ROOT, "sparse_activation_amd", "_lib", "libqs_probe.so")
+    fn = ctypes.CDLL(path).qsprobe_stream_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    return fn
+
+
 def bf16_dev(torch, np, a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
 
@@ -136,7 +183,11 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     c = datagen.c2_relu2_ffn(B)
     d, ffn = c["W_up"].shape[1], c["W_up"].shape[0]
     k_in, k_mid = c["K_in"], c["K_mid"]
-    n_copies = 3                                   # 3 x 180 MB > 256 MB MALL
+    # Weight copies rotate so that the other steps' traffic between two visits
+    # to one copy is several times the 256 MB Infinity Cache (MALL): a step
+    # reads only the selected rows (72 MB at one token), so 16 copies put
+    # 15 x 72 MB = 1.08 GB between visits.
+    n_copies = args.weight_copies or C2_COPIES
     wup0 = bf16_dev(torch, np, c["W_up"].T, dev)
     wdn0 = bf16_dev(torch, np, c["W_down"].T, dev)
     wups = [wup0] + [wup0.clone() for _ in range(n_copies - 1)]
@@ -151,8 +202,7 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
         qs.qs_sparse_ffn(xs[i % N_XROT], qs.ACT_RELU2, k_in, k_mid, wups[i % n_copies],
                          wdns[i % n_copies], y=y, ws=ws)
 
-    ms_total = time_graph(torch, stream, step, args.steps, args.warmup)
-    ms_step = ms_total / args.steps
+    ms_step, timing = time_steps(args, torch, stream, step, args.steps, args.warmup)
     log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step, {B / (ms_step * 1e-3):.0f} tokens/s")
 
     # union sizes of the rotated batches (for the algorithmic bytes)
@@ -192,7 +242,10 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
         gather(u1[i % N_XROT], wups[i % n_copies], y=yup, ws=ws_up)
         gather(u2[i % N_XROT], wdns[i % n_copies], y=ydn, ws=ws_dn)
 
-    ms_gemv = time_graph(torch, stream, gemv_pair, L, 4)
+    # (median over graph replays of L launch pairs; each replay's time / 2L is
+    # the average launch duration that the kernel trace reports)
+    _, per = time_graph(torch, stream, gemv_pair, L, 4, replays=args.replays)
+    ms_gemv = sorted(per)[len(per) // 2]
     gemv_bytes = sum(bytes_up(i % N_XROT) + bytes_dn(i % N_XROT) for i in range(L))
     us_launch = ms_gemv * 1e3 / (2 * L)
     achieved = gemv_bytes / (ms_gemv * 1e-3) / 1e9
@@ -205,11 +258,17 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     nb = min(int(gemv_bytes / (2 * L)), min(f.numel() for f in flat)) // 16 * 16
     chunks = [f[o:o + nb] for f in flat for o in range(0, f.numel() - nb + 1, nb)]
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream_read = probe_library()
 
     def probe(i):
-        qs.qs_stream_read(chunks[i % len(chunks)], nb, sink)
+        rc = stream_read(ctypes.c_void_p(chunks[i % len(chunks)].data_ptr()), nb,
+                         ctypes.c_void_p(sink.data_ptr()),
+                         ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"stream-read probe failed ({rc})")
 
-    ms_probe = time_graph(torch, stream, probe, L, 4)
+    _, per = time_graph(torch, stream, probe, L, 4, replays=max(5, args.replays // 5))
+    ms_probe = sorted(per)[len(per) // 2]
     probe_gbps = nb * L / (ms_probe * 1e-3) / 1e9
     log(f"stream-read probe, {nb / 1e6:.1f} MB per launch over {len(chunks)} chunks: "
         f"{probe_gbps:.0f} GB/s; gather GEMV at {achieved / probe_gbps:.1%} of it")
@@ -233,37 +292,66 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
                      "us_per_launch": round(us_launch, 3),
                      "stream_read_probe_gbps": round(probe_gbps, 1),
                      "frac_of_stream_read_probe": round(achieved / probe_gbps, 4)},
-        "cpu_baseline": cpu,
+        "timing": timing, "cpu_baseline": cpu,
     }
 
 
-def _cores():
+def host_info():
+    """Threads the oracle may use on this host (the CPU affinity set, capped by
+    OMP_NUM_THREADS where the environment sets one), the CPU model and the
+    BLAS library NumPy was built with."""
+    import numpy as np
+    threads = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        threads = min(threads, int(omp))
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        dep = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{dep.get('name', '?')} {dep.get('version', '')}".strip()
     except Exception:
-        return 1
+        pass
+    return threads, model, blas
 
 
 def cpu_baseline_c2(c, seconds):
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import datagen
     import oracle
-    cores = _cores()
+    threads, model, blas = host_info()
     w_up = c["W_up"].astype(np.float64)
     w_dn = c["W_down"].astype(np.float64)
-    n, t0 = 0, time.perf_counter()
-    while n < 64:
-        x = datagen.c2_relu2_ffn(1, rotation=n % N_XROT, with_weights=False)["X"]
-        oracle.ffn_relu2(x, c["K_in"], w_up, c["K_mid"], w_dn)
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    log(f"cpu oracle: {n} tokens in {dt:.1f} s")
-    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} single-token steps of the same workload (B=1), float64 NumPy oracle"}
+    with threadpool_limits(limits=threads):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] or [1])
+        times, n, t0 = [], 0, time.perf_counter()
+        while n < 64:
+            x = datagen.c2_relu2_ffn(1, rotation=n % N_XROT, with_weights=False)["X"]
+            t1 = time.perf_counter()
+            oracle.ffn_relu2(x, c["K_in"], w_up, c["K_mid"], w_dn)
+            times.append(time.perf_counter() - t1)
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    dt = sum(times)
+    med = sorted(times)[len(times) // 2]
+    log(f"cpu oracle: {n} tokens in {dt:.1f} s ({used} BLAS threads, {model}, {blas})")
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "median_ms_per_token": round(med * 1e3, 2), "cpu_model": model, "blas": blas,
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{n} single-token steps of the same workload (B=1), float64 NumPy "
+                      f"oracle (select, matmuls, epilogues; input generation not timed)"}
 
 
 # ---------------------------------------------------------------- other workloads
@@ -273,7 +361,7 @@ def run_c5(args, torch, np, qs, datagen, dev, stream):
     log(f"workload c5: dReLU FFN decode B={B}; generating weights")
     c = datagen.c5_drelu_ffn(B)
     ffn, d = c["W_gate"].shape
-    n_copies = 2                                   # 2 x 352 MB > 256 MB MALL
+    n_copies = args.weight_copies or C5_COPIES                           # 5 x >= 166 MB between visits
     wg = [bf16_dev(torch, np, c["W_gate"], dev)]
     wu = [bf16_dev(torch, np, c["W_up"], dev)]
     wd = [bf16_dev(torch, np, c["W_down"].T, dev)]
@@ -292,7 +380,7 @@ def run_c5(args, torch, np, qs, datagen, dev, stream):
         qs.qs_sparse_ffn(xs[i % N_XROT], qs.ACT_DRELU, d, -1, wu[j], wd[j], w_gate=wg[j],
                          b_gate=bg, b_up=bu, y=y, ws=ws)
 
-    ms_step = time_graph(torch, stream, step, args.steps, args.warmup) / args.steps
+    ms_step, timing = time_steps(args, torch, stream, step, args.steps, args.warmup)
     # measured unions: gate read in full, up rows with g > 0 for some token, down rows with h != 0
     hs = [qs.qs_sparse_ffn(xs[i], qs.ACT_DRELU, d, -1, wu[0], wd[0], w_gate=wg[0], b_gate=bg,
                            b_up=bu, want_h=True)[1] for i in range(N_XROT)]
@@ -317,7 +405,7 @@ def run_c5(args, torch, np, qs, datagen, dev, stream):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "whole FFN step (gate/up + down)",
                      "algorithmic_bytes_per_step": round(float(step_bytes))},
-        "cpu_baseline": None,
+        "timing": timing, "cpu_baseline": None,
     }
 
 
@@ -336,7 +424,7 @@ def run_c4(args, torch, np, qs, datagen, dev, stream):
         qs.qs_sparse_linear(xs[i % 2], c["K"], w, layout=qs.LAYOUT_W, y=y, ws=ws)
 
     steps = max(4, min(args.steps, 40))
-    ms_step = time_graph(torch, stream, step, steps, 4) / steps
+    ms_step, timing = time_steps(args, torch, stream, step, steps, 4)
     flops = 2.0 * m * n * kdim
     tflops = flops / (ms_step * 1e-3) / 1e12
     log(f"c4: {ms_step * 1e3:.1f} us/step, {tflops:.0f} TFLOP/s (top-K + GEMM)")
@@ -349,7 +437,7 @@ def run_c4(args, torch, np, qs, datagen, dev, stream):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "kernel": "whole call (top-K + gemm_bf16_deep_kernel)"},
-        "cpu_baseline": None,
+        "timing": timing, "cpu_baseline": None,
     }
 
 
@@ -397,11 +485,18 @@ def run_c6(args, torch, np, qs, datagen, dev, stream):
         step_bytes.append(rows_read * d * 2 + n_exp * d * 2 + 2 * B * d * 2)
     torch.cuda.synchronize()
 
-    def step(i):
-        qs.qs_sparse_moe_ffn(xs[i % 8], top_k, wr, mats["W_gate"], mats["W_up"], mats["W_down_t"],
-                             bg, bu, y=y, ws=ws)
+    # Copies of the expert weights rotate as well, so that an expert two
+    # consecutive batches both route to is not re-read from the MALL.
+    n_copies = args.weight_copies or C6_COPIES
+    copies = [(mats["W_gate"], mats["W_up"], mats["W_down_t"])]
+    for _ in range(n_copies - 1):
+        copies.append(tuple(t.clone() for t in copies[0]))
 
-    ms_step = time_graph(torch, stream, step, args.steps, args.warmup) / args.steps
+    def step(i):
+        g, u, dn = copies[i % n_copies]
+        qs.qs_sparse_moe_ffn(xs[i % 8], top_k, wr, g, u, dn, bg, bu, y=y, ws=ws)
+
+    ms_step, timing = time_steps(args, torch, stream, step, args.steps, args.warmup)
     alg = float(np.mean(step_bytes))
     achieved = alg / (ms_step * 1e-3) / 1e9
     log(f"c6: {ms_step * 1e3:.2f} us/step, {B / (ms_step * 1e-3):.0f} tokens/s, "
@@ -413,13 +508,14 @@ def run_c6(args, torch, np, qs, datagen, dev, stream):
         "ms_per_step": round(ms_step, 6), "dtype": "bf16",
         "config": {"workload": "mixtral47b_drelu_moe_ffn_decode", "batch": B, "d": d, "ffn": ffn,
                    "experts": n_exp, "top_k": top_k, "x_rotations": 8,
+                   "weight_copies": n_copies,
                    "up_rows_frac": round(float(np.mean(up_frac)), 4),
                    "down_rows_frac": round(float(np.mean(down_frac)), 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "whole MoE step (router, gate/up, down gather, combine)",
                      "algorithmic_bytes_per_step": int(alg)},
-        "cpu_baseline": None,
+        "timing": timing, "cpu_baseline": None,
     }
 
 
@@ -438,7 +534,7 @@ def run_c4s(args, torch, np, qs, datagen, dev, stream):
         qs.qs_block_sparse_linear(xs[i % 2], w, y=y, ws=ws)
 
     steps = max(4, min(args.steps, 40))
-    ms_step = time_graph(torch, stream, step, steps, 4) / steps
+    ms_step, timing = time_steps(args, torch, stream, step, steps, 4)
     kept_flops = 2.0 * m * n * (kdim // 2)            # the MACs on kept entries
     tflops = kept_flops / (ms_step * 1e-3) / 1e12
     dense_eq = 2 * tflops
@@ -454,7 +550,7 @@ def run_c4s(args, torch, np, qs, datagen, dev, stream):
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "dense_equivalent_tflops": round(dense_eq, 1),
                      "kernel": "whole call (nm24_pack_kernel + gemm_sp24_kernel)"},
-        "cpu_baseline": None,
+        "timing": timing, "cpu_baseline": None,
     }
 
 
@@ -476,7 +572,7 @@ def run_c4b(args, torch, np, qs, datagen, dev, stream):
                                      want_dx=want_dx, want_dw=want_dw, dx=dx, dw=dw, ws=ws)
 
     steps = max(4, min(args.steps, 40))
-    ms_step = time_graph(torch, stream, step, steps, 4) / steps
+    ms_step, timing = time_steps(args, torch, stream, step, steps, 4)
     ms_dx = time_graph(torch, stream, lambda i: step(i, want_dw=False), steps, 2) / steps
     ms_dw = time_graph(torch, stream, lambda i: step(i, want_dx=False), steps, 2) / steps
     flops = 2.0 * m * n * kdim
@@ -495,7 +591,7 @@ def run_c4b(args, torch, np, qs, datagen, dev, stream):
                      "traffic": None,
                      "kernel": "whole call (top-K + two gemm_bf16_deep_kernel launches)",
                      "dx_us": round(ms_dx * 1e3, 2), "dw_us_with_topk": round(ms_dw * 1e3, 2)},
-        "cpu_baseline": None,
+        "timing": timing, "cpu_baseline": None,
     }
 
 
@@ -505,7 +601,7 @@ def run_c2g(args, torch, np, qs, datagen, dev, stream):
     c = datagen.c2g_relu2glu_ffn(B)
     d, ffn = c["W_up"].shape[1], c["W_up"].shape[0]
     k_in, k_mid = c["K_in"], c["K_mid"]
-    n_copies = 2                                   # 2 x 271 MB > 256 MB MALL
+    n_copies = args.weight_copies or C2G_COPIES                          # 7 x >= 108 MB between visits
     wg = [bf16_dev(torch, np, c["W_gate"].T, dev)]
     wu = [bf16_dev(torch, np, c["W_up"].T, dev)]
     wd = [bf16_dev(torch, np, c["W_down"].T, dev)]
@@ -522,7 +618,7 @@ def run_c2g(args, torch, np, qs, datagen, dev, stream):
         qs.qs_sparse_ffn(xs[i % N_XROT], qs.ACT_RELU2_GLU, k_in, k_mid, wu[j], wd[j],
                          w_gate=wg[j], y=y, ws=ws)
 
-    ms_step = time_graph(torch, stream, step, args.steps, args.warmup) / args.steps
+    ms_step, timing = time_steps(args, torch, stream, step, args.steps, args.warmup)
     # measured unions: rows of W_gate^T and W_up^T selected by some token, rows of W_down^T
     u1, u2 = [], []
     for i in range(N_XROT):
@@ -549,7 +645,7 @@ def run_c2g(args, torch, np, qs, datagen, dev, stream):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "whole FFN step (gate, up, top-K of h, down)",
                      "algorithmic_bytes_per_step": round(float(step_bytes))},
-        "cpu_baseline": None,
+        "timing": timing, "cpu_baseline": None,
     }
 
 
@@ -572,13 +668,13 @@ def run_c3(args, torch, np, qs, datagen, dev, stream):
         qs.qs_sparse_linear_i8t(xs[i % N_XROT], c["K"], copies[i % 128], alpha, n, acc=acc, y=y,
                                 ws=ws, want_all=False)
 
-    ms_step = time_graph(torch, stream, step, args.steps, args.warmup) / args.steps
+    ms_step, timing = time_steps(args, torch, stream, step, args.steps, args.warmup)
     log(f"c3: {ms_step * 1e3:.2f} us/step")
     return {
         "metric": "int8 x ternary sparse linear tokens/s (4096x4096), 1 GPU", "unit": "tokens/s",
         "value": round(B / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 6), "dtype": "int8",
         "config": {"workload": "bitnet_i8t_linear_4096", "batch": B, "k": c["K"]},
-        "roofline": None, "cpu_baseline": None,
+        "roofline": None, "timing": timing, "cpu_baseline": None,
     }
 
 
@@ -596,13 +692,13 @@ def run_c1(args, torch, np, qs, datagen, dev, stream):
     def step(i):
         qs.qs_sparse_linear(xs[i % N_XROT], c["K"], copies[i % 128], y=y, ws=ws)
 
-    ms_step = time_graph(torch, stream, step, args.steps, args.warmup) / args.steps
+    ms_step, timing = time_steps(args, torch, stream, step, args.steps, args.warmup)
     log(f"c1: {ms_step * 1e3:.2f} us/step")
     return {
         "metric": "fp32 sparse linear tokens/s (1024x1024, 8 tokens), 1 GPU", "unit": "tokens/s",
         "value": round(8 / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 6), "dtype": "f32",
         "config": {"workload": "fp32_linear_1024", "batch": 8, "k": c["K"]},
-        "roofline": None, "cpu_baseline": None,
+        "roofline": None, "timing": timing, "cpu_baseline": None,
     }
 
 

@@ -47,10 +47,14 @@
  *     fp32 between the up and the down projection.
  *
  * Conventions for every entry point:
- *   - Device pointers are caller-owned (allocate them however you like,
- *     e.g. through torch).  The library allocates no device memory, keeps no
- *     pointer after the call returns, and may access the buffers until the
- *     stream reaches the end of the enqueued work.
+ *   - Device pointers are caller-owned.  They must point to ordinary
+ *     (coarse-grained) device memory of the GPU that runs the stream, as
+ *     hipMalloc or torch's CUDA allocator give: outputs and workspaces are
+ *     updated with device-scope float and integer atomics, which host-pinned,
+ *     managed and fine-grained memory do not support.  The library allocates
+ *     no device memory, keeps no pointer after the call returns, and may
+ *     access the buffers until the stream reaches the end of the enqueued
+ *     work.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *     asynchronous and never synchronise the host.
  *   - Arguments are validated before anything is enqueued; on any error the
@@ -155,7 +159,12 @@ qs_status qs_topk_mask(const void* x, qs_dtype xt, int64_t rows, int64_t d, int6
  *                         token batches; needs xt == wt_t == QS_BF16.
  *   y       device [rows, n_out], dtype yt (QS_F32 or QS_BF16, bf16 rounded
  *           to nearest-even from the fp32 sum).
- *   Arithmetic: products of the exact input values, fp32 accumulation.
+ *   Arithmetic: fp32 accumulation of the products of the input values.
+ *   The products are exact except in one case: with bf16 weights, fp32 x and
+ *   tiles of 8 to 16 tokens, the gather runs on the bf16 matrix cores and
+ *   carries each selected fp32 activation as the sum of two bf16 numbers
+ *   (hi = bf16(x), lo = bf16(x - hi)), a relative error of at most 2^-18 per
+ *   activation, inside the fp32 bound 1e-5 * sum |x w|.
  *   Alignment: n_out % 8 == 0 (bf16 weights) or n_out % 4 == 0 (fp32), and
  *   d_in % 8 == 0 for QS_LAYOUT_W.
  */
@@ -398,18 +407,6 @@ qs_status qs_ternarize(const float* w_host, int64_t n_out, int64_t d_in, int8_t*
  * [d_in, n_out/4]).  n_out % 4 == 0.  Host-only.
  */
 qs_status qs_pack_ternary(const int8_t* t_host, int64_t n_out, int64_t d_in, uint8_t* packed_host);
-
-/*
- * qs_stream_read -- measurement reference, not part of the method: a plain
- * streaming read of `bytes` bytes at `src` (device), with every byte loaded
- * once and nothing written except, never in practice, *sink.  Its throughput
- * on a buffer of the gather kernels' size is the practical HBM ceiling their
- * roofline fraction is also quoted against.
- *   src    device, 16-byte aligned; bytes % 16 == 0 (else QS_ERR_UNSUPPORTED).
- *   sink   device u32, written only if the checksum of the data equals a
- *          fixed constant.  Enqueued on `stream`, asynchronous.
- */
-qs_status qs_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 /* Text of the last error on the calling thread ("" if none); valid until the
  * next qs_* call on this thread. */

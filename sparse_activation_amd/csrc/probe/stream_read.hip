@@ -1,12 +1,19 @@
-// Bandwidth reference: a plain streaming read of a device buffer.  The gather
+// Bandwidth reference for measurements (libqs_probe.so, not part of libqs.so
+// or its ABI): a plain streaming read of a device buffer.  The gather
 // kernels' HBM throughput is reported against the published peak and against
 // what this read reaches on the same number of bytes, the practical ceiling of
 // a kernel that size.
+//
+//   int qsprobe_stream_read(const void* src, size_t bytes, uint32_t* sink,
+//                           void* stream)
+//     src    device, 16-byte aligned; bytes % 16 == 0.
+//     sink   device u32, written only if the checksum of the data equals a
+//            fixed constant (never in practice).
+//     Returns 0, 1 (bad argument) or 2 (HIP launch error).  Asynchronous on
+//     `stream` (a hipStream_t).
 #include <hip/hip_runtime.h>
 
-#include <cstdio>
-
-#include "qs_error.h"
+#include <cstdint>
 
 namespace qs {
 namespace {
@@ -43,19 +50,11 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* p, size_t
 }  // namespace
 }  // namespace qs
 
-extern "C" qs_status qs_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
-    if (src == nullptr || sink == nullptr)
-        return qs::set_error(QS_ERR_INVALID_ARG, "qs_stream_read: null pointer");
-    if (bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15u) != 0)
-        return qs::set_error(QS_ERR_UNSUPPORTED, "qs_stream_read: src and bytes must be 16-byte aligned");
-    if (bytes == 0) return qs::set_error(QS_OK, "");
+extern "C" int qsprobe_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    if (src == nullptr || sink == nullptr) return 1;
+    if (bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15u) != 0) return 1;
+    if (bytes == 0) return 0;
     qs::stream_read_kernel<<<dim3(qs::kProbeWG), dim3(256), 0, (hipStream_t)stream>>>(
         static_cast<const qs::u32x4*>(src), bytes / 16, sink);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) {
-        char msg[256];
-        snprintf(msg, sizeof msg, "qs_stream_read: %s", hipGetErrorString(e));
-        return qs::set_error(QS_ERR_HIP, msg);
-    }
-    return qs::set_error(QS_OK, "");
+    return hipGetLastError() == hipSuccess ? 0 : 2;
 }

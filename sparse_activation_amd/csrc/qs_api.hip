@@ -147,8 +147,18 @@ struct FfnWs {
     float* hs;
     float* gacc;           // relu2 kinds: the gate sums of the gated FFN's accumulate form
     float* partial;
+    size_t partial_cap;    // floats carved for `partial`
+    size_t up_ctr_cap, down_ctr_cap;
     size_t bytes;
 };
+
+// Plan of the FFN's down gather.  Without a selection on h the dReLU
+// intermediate is ~90% zero, so a candidate range holds few active rows:
+// fewer, longer splits (Mistral-7B dReLU FFN at one token: 35.0 us per step
+// aiming at 320 workgroups against 35.6 at the default 640).
+qs::GemvPlan ffn_down_plan(int64_t rows, int64_t d, int64_t ffn, int wb, bool drelu, int64_t k_mid) {
+    return qs::plan_gemv(rows, ffn, d, wb, 16, drelu && k_mid < 0 ? 320 : 0);
+}
 
 FfnWs ffn_ws(char* base, int64_t rows, int64_t d, int64_t ffn, bool drelu) {
     Carve c;
@@ -162,9 +172,15 @@ FfnWs ffn_ws(char* base, int64_t rows, int64_t d, int64_t ffn, bool drelu) {
         // behind the up projection's.
         up_part = max_sz(ub.scratch_floats, uf.scratch_floats) + max_sz(ub.partial_floats, uf.partial_floats);
     }
-    qs::GemvPlan db = qs::plan_gemv(rows, ffn, d, 1), df = qs::plan_gemv(rows, ffn, d, 0);
-    size_t down_ctr = (size_t)(db.n_counters > df.n_counters ? db.n_counters : df.n_counters);
-    size_t down_part = max_sz(db.scratch_floats, df.scratch_floats);
+    // The down gather's plan as qs_sparse_ffn makes it (ffn_down_plan), for
+    // both weight dtypes and both selection forms of dReLU.
+    size_t down_ctr = 0, down_part = 0;
+    for (int wb = 0; wb < 2; ++wb)
+        for (int sel = 0; sel < 2; ++sel) {
+            const qs::GemvPlan p = ffn_down_plan(rows, d, ffn, wb, drelu, sel == 0 ? -1 : 0);
+            down_ctr = max_sz(down_ctr, (size_t)p.n_counters);
+            down_part = max_sz(down_part, p.scratch_floats);
+        }
     w.n_ctr = (int)(up_ctr + down_ctr);
     w.ctr_up = (int32_t*)c.take(sizeof(int32_t) * (up_ctr + down_ctr));
     w.ctr_down = w.ctr_up ? w.ctr_up + up_ctr : nullptr;
@@ -174,6 +190,9 @@ FfnWs ffn_ws(char* base, int64_t rows, int64_t d, int64_t ffn, bool drelu) {
     w.hs = (float*)c.take(sizeof(float) * (size_t)rows * ffn);
     if (!drelu) w.gacc = (float*)c.take(sizeof(float) * (size_t)rows * ffn);
     w.partial = (float*)c.take(sizeof(float) * max_sz(up_part, down_part));
+    w.partial_cap = max_sz(up_part, down_part);
+    w.up_ctr_cap = up_ctr;
+    w.down_ctr_cap = down_ctr;
     w.bytes = c.off;
     return w;
 }
@@ -514,11 +533,17 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     // handing them to a last workgroup.  Up projection: the input selection
     // clears the sums, and the selection of h maps them to h (so only with
     // k_mid >= 0).  Down projection: the selection of h clears y.
-    // Without a selection on h the dReLU intermediate is ~90% zero, so a
-    // candidate range holds few active rows: fewer, longer splits (Mistral-7B
-    // dReLU FFN at one token: 35.0 us per step aiming at 320 workgroups
-    // against 35.6 at the default 640).
-    qs::GemvPlan pd = qs::plan_gemv(rows, ffn, d, wb, 16, drelu && k_mid < 0 ? 320 : 0);
+    const qs::GemvPlan pd = ffn_down_plan(rows, d, ffn, wb, drelu, k_mid);
+    // The carved regions hold every plan this call launches (by construction;
+    // checked on the host before anything is enqueued).
+    if (pd.scratch_floats > wsp.partial_cap || (size_t)pd.n_counters > wsp.down_ctr_cap)
+        return fail(QS_ERR_WORKSPACE, "%s: internal: down-gather plan exceeds its workspace", fn);
+    if (!drelu) {
+        const qs::GemvPlan pu = qs::plan_gemv(rows, d, ffn, wb);
+        if (pu.scratch_floats + pu.partial_floats > wsp.partial_cap ||
+            (size_t)pu.n_counters > wsp.up_ctr_cap)
+            return fail(QS_ERR_WORKSPACE, "%s: internal: up-gather plan exceeds its workspace", fn);
+    }
     // (y is cleared by the selection of h, or without one by the dReLU
     // gate/up launch.)
     const bool acc_down = !deterministic() && (k_mid >= 0 || drelu) && yt == QS_F32 &&

@@ -28,8 +28,6 @@
 //
 // The ternary x int8 variant does the same with 2-bit packed weights and
 // exact int32 accumulation.
-#include <cstdlib>
-
 #include "qs_internal.h"
 
 namespace qs {
@@ -49,24 +47,8 @@ constexpr int kFMaxCand = 2048;  // candidate rows per split (coefficients stage
 
 // Workgroups the split-K plan aims for: 2.5 per CU, measured best on the
 // Llama-7B FFN decode gathers (12.2 us per launch against 12.6 at 768 and
-// 13.0 at 512).  QS_GEMV_TARGET_WG overrides it (read once per process; a
-// tuning knob for measurements).
-int target_wg() {
-    static const int v = [] {
-        const char* e = getenv("QS_GEMV_TARGET_WG");
-        int t = e ? atoi(e) : 0;
-        return t > 0 ? t : 640;
-    }();
-    return v;
-}
-
-// Integer tuning knob from the environment, clamped to [lo, hi].
-int env_int(const char* name, int dflt, int lo, int hi) {
-    const char* e = getenv(name);
-    int t = e ? atoi(e) : dflt;
-    if (t <= 0) t = dflt;
-    return t < lo ? lo : t > hi ? hi : t;
-}
+// 13.0 at 512).
+constexpr int kGemvTargetWG = 640;
 
 __device__ __forceinline__ uint32_t popc_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
@@ -75,10 +57,12 @@ __device__ __forceinline__ uint32_t popc_below(uint64_t m) {
 
 // Split-K handoff between workgroups that may sit on different XCDs (each
 // with its own L2): partials are written and read with relaxed agent-scope
-// atomics, which the compiler emits as sc1 stores/loads that bypass the
-// non-coherent L2 state, so no L2 writeback/invalidate fence is needed.
-// s_waitcnt vmcnt(0) (0x0F70) makes this wave's stores complete before the
-// workgroup barrier and the counter increment.
+// atomics (sc1 stores and loads, coherent at agent scope without a cache
+// flush), and the counter increment is an acquire-release RMW at agent
+// scope, so by the memory model every partial a workgroup stored before its
+// increment is visible to the workgroup whose increment comes last.  Each
+// wave first waits for its own stores (s_waitcnt vmcnt(0), 0x0F70), and the
+// workgroup barrier orders them before thread 0's release.
 template <typename T>
 __device__ __forceinline__ void store_agent(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -94,7 +78,7 @@ __device__ __forceinline__ bool last_split_arrived(int32_t* counter, int nsplit,
     wait_stores();
     __syncthreads();
     if (threadIdx.x == 0)
-        *s_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED,
+        *s_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL,
                                          __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
     __syncthreads();
     return *s_flag != 0;
@@ -1029,12 +1013,6 @@ constexpr int kI8CT = kI8LPR * kI8EPT;     // 256 columns per tile
 constexpr int kI8NSlot = 4 * (64 / kI8LPR);   // 32 row slots per workgroup
 constexpr int kI8MaxCand = 4096;           // candidate rows per split (LDS staging)
 constexpr int kI8TargetWG = 128;           // the whole matrix is a few MB: few, fuller workgroups
-// QS_I8T_TARGET_WG overrides the ternary gather's workgroup target (read once
-// per process; a tuning knob for measurements).
-int i8t_target_wg() {
-    static const int v = env_int("QS_I8T_TARGET_WG", kI8TargetWG, 1, 1 << 16);
-    return v;
-}
 static_assert(kI8CT == kNT, "the slot reduction gives each thread one column");
 
 template <int BT>
@@ -1471,14 +1449,14 @@ GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16, int
     if (bmfma) {
         // As many splits as keep every workgroup resident at once (three per
         // CU), in whole 4-group stages.
-        const int64_t cap = env_int("QS_BMFMA_RESIDENT_WG", 768, 1, 1 << 16);
+        const int64_t cap = 768;
         int64_t ns = cap / base;
         if (ns < 1) ns = 1;
         cand = ceil_div(ceil_div(d_in, ns), 4 * kBGroup) * 4 * kBGroup;
     } else {
         // The FMA kernels stage <= 32 KB of coefficients in LDS.
         const int cand_max = 8192 / p.bt < kFMaxCand ? 8192 / p.bt : kFMaxCand;
-        int64_t ns = ceil_div(target > 0 ? target : target_wg(), base);
+        int64_t ns = ceil_div(target > 0 ? target : kGemvTargetWG, base);
         if (ns < 1) ns = 1;
         cand = ceil_div(ceil_div(d_in, ns), 64) * 64;
         if (cand > cand_max) cand = cand_max;
@@ -1497,15 +1475,8 @@ GemvPlan plan_gemv(int64_t rows, int64_t d_in, int64_t n_out, int w_is_bf16, int
 // Forming the fragments inside the gather converts each group once per column
 // tile instead of once, but saves the packing launch: it pays for a half-empty
 // tile (8 tokens: 65.4 us per Llama-7B FFN step against 67.1), not for a full
-// one (69.2 against 68.6).  QS_BMFMA_FUSED=0/1 forces either (a tuning knob
-// for measurements).
-bool bmfma_fused(int64_t rows) {
-    static const int v = [] {
-        const char* fe = getenv("QS_BMFMA_FUSED");
-        return fe ? (fe[0] == '1' ? 1 : 0) : -1;
-    }();
-    return v >= 0 ? v == 1 : rows <= 8;
-}
+// one (69.2 against 68.6).
+bool bmfma_fused(int64_t rows) { return rows <= 8; }
 
 // Records written by the selection launch beat both the packing launch and
 // the fused conversion from 8 tokens on (Llama-7B FFN step at 8 tokens: 61.0
@@ -1644,7 +1615,7 @@ I8tPlan plan_i8t(int64_t rows, int64_t d_in, int64_t n_out) {
     p.n_tok_tiles = (int)ceil_div(rows, p.bt);
     const int cand_max = kI8MaxCand;
     const int64_t base = (int64_t)p.n_tiles * p.n_tok_tiles;
-    int64_t ns = ceil_div(i8t_target_wg(), base);
+    int64_t ns = ceil_div(kI8TargetWG, base);
     if (ns < 1) ns = 1;
     int64_t cand = ceil_div(ceil_div(d_in, ns), 64) * 64;
     if (cand > cand_max) cand = cand_max;

@@ -113,13 +113,20 @@ def test_set_deterministic_returns_previous_setting():
         lib.qs_set_deterministic(prev)
 
 
-def test_stream_read_validation():
+def test_probe_library_is_separate():
+    """The streaming-read probe the bench quotes bandwidth against lives in
+    its own library: libqs.so does not export it."""
     lib = qs.load()
-    assert lib.qs_stream_read(None, 1024, FAKE, None) == 1
-    assert lib.qs_stream_read(FAKE, 1024, None, None) == 1
-    assert lib.qs_stream_read(FAKE, 1000, FAKE, None) == 2        # bytes % 16 != 0
-    assert lib.qs_stream_read(ctypes.c_void_p(0x1008), 1024, FAKE, None) == 2   # misaligned
-    assert lib.qs_stream_read(FAKE, 0, FAKE, None) == 0           # nothing to read
+    assert not hasattr(lib, "qs_stream_read")
+    probe = ctypes.CDLL(os.path.join(os.path.dirname(qs.lib_path()), "libqs_probe.so"))
+    fn = probe.qsprobe_stream_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    assert fn(None, 1024, FAKE, None) == 1
+    assert fn(FAKE, 1024, None, None) == 1
+    assert fn(FAKE, 1000, FAKE, None) == 1                       # bytes % 16 != 0
+    assert fn(ctypes.c_void_p(0x1008), 1024, FAKE, None) == 1    # misaligned
+    assert fn(FAKE, 0, FAKE, None) == 0                          # nothing to read
 
 
 def test_i8t_and_ffn_validation():

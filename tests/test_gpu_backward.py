@@ -128,9 +128,10 @@ def test_backward_deterministic(gpu_lib):
 @pytest.mark.parametrize("layout", ["W", "WT"])
 def test_backward_full_c4_sampled(gpu_lib, layout):
     """The fused-QKV shape as a training step: X [2048, 4096], W [12288, 4096],
-    K = 2867, dY [2048, 12288].  The oracle checks 24 sampled rows of dX (all
-    4096 entries each) and 24 sampled output neurons of dW (all 4096 input
-    features each), at the launch shapes the bench times."""
+    K = 2867, dY [2048, 12288].  The oracle checks sampled rows of dX (all
+    4096 entries each) and sampled output neurons of dW (all 4096 input
+    features each), covering every tile of both GEMMs, at the launch shapes
+    the bench times."""
     import torch
     qs = gpu_lib
     lay = qs.LAYOUT_W if layout == "W" else qs.LAYOUT_WT
@@ -140,9 +141,15 @@ def test_backward_full_c4_sampled(gpu_lib, layout):
     note(f"backward full C4 layout={layout}")
     dx, dw = _run(qs, x, k, w, gy, lay, torch.float32)
     rng = np.random.default_rng(73)
-    rows = np.sort(rng.choice(x.shape[0], 24, replace=False))
-    outs = np.sort(rng.choice(w.shape[0], 24, replace=False))
-    rows[0], rows[-1], outs[0], outs[-1] = 0, x.shape[0] - 1, 0, w.shape[0] - 1
+    # One sampled token in every 256-token block (the dX GEMM's M tiles) and
+    # one output neuron in every 128-neuron block, which meets every M tile of
+    # the W-layout dW GEMM (256 neurons) and every N tile (128 or 192
+    # neurons) of the W^T-layout one; every checked row or neuron is checked
+    # over all 4096 features, i.e. across every tile of the other dimension.
+    rows = np.array([b + rng.integers(0, 256) for b in range(0, x.shape[0], 256)])
+    outs = np.array([b + rng.integers(0, 128) for b in range(0, w.shape[0], 128)])
+    rows = np.unique(np.concatenate([rows, [0, x.shape[0] - 1]]))
+    outs = np.unique(np.concatenate([outs, [0, w.shape[0] - 1]]))
     mask, _, _, _ = oracle.topk_select(oracle.magnitude(x), k)
     r_dx = oracle.sparse_linear_backward(x[rows], w, mask[rows], gy[rows])
     assert_within(dx[rows], r_dx["dx"], r_dx["T_dx"], 4e-3, "C4 dx")

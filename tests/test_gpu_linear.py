@@ -225,3 +225,23 @@ def test_linear_mfma_full_c4_sampled(gpu_lib):
     y_ref, t = _ref(x[rows], k, w)
     assert_within(y[rows], y_ref, t, 4e-3, "C4 fp32 out")
     assert_within(yb[rows], y_ref, t, 4e-3, "C4 bf16 out")
+
+
+@pytest.mark.parametrize("rows", [5, 8, 16, 23])
+@pytest.mark.parametrize("det", [False, True])
+def test_linear_fp32_x_bf16_w(gpu_lib, rows, det):
+    """fp32 activations with bf16 weights: tiles of 8-16 tokens run the bf16
+    matrix-core gather, which carries each fp32 coefficient as a two-term
+    bf16 split (relative error at most 2^-18); with fp32 accumulation the
+    result stays within the fp32 bound 1e-5 * T."""
+    import torch
+    rng = np.random.default_rng(500 + rows)
+    d, n = 1536, 1032
+    x = datagen.student_t(rng, (rows, d))
+    w = datagen.bf16_round(datagen.normal(rng, (n, d), 0.02))
+    with reduction_mode(gpu_lib, det):
+        for k in (d // 3, d):
+            note(f"linear fp32 x / bf16 w rows={rows} k={k} det={det}")
+            y = _run(gpu_lib, x, k, w, torch.float32, torch.bfloat16, torch.float32)
+            y_ref, t = _ref(x, k, w)
+            assert_within(y, y_ref, t, 1e-5, f"fp32 x, bf16 w, rows={rows}")
