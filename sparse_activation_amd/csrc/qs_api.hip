@@ -138,6 +138,7 @@ I8tWs i8t_ws(char* base, int64_t rows, int64_t d_in, int64_t n_out) {
 }
 
 struct FfnWs {
+    uint32_t* desc;        // relu2 kinds: top-k descriptor of h: tau [rows], then cutoff [rows]
     int32_t* ctr_up;
     int32_t* ctr_down;
     int n_ctr;             // ctr_up and ctr_down are contiguous: n_ctr ints in total
@@ -183,6 +184,7 @@ FfnWs ffn_ws(char* base, int64_t rows, int64_t d, int64_t ffn, bool drelu) {
         }
     w.n_ctr = (int)(up_ctr + down_ctr);
     w.ctr_up = (int32_t*)c.take(sizeof(int32_t) * (up_ctr + down_ctr));
+    w.desc = drelu ? nullptr : (uint32_t*)c.take(sizeof(uint32_t) * 2 * (size_t)rows);
     w.ctr_down = w.ctr_up ? w.ctr_up + up_ctr : nullptr;
     if (!drelu) w.xs1 = (float*)c.take(sizeof(float) * (size_t)rows * d);
     else w.xm = (uint16_t*)c.take(sizeof(uint16_t) * (size_t)rows * d);
@@ -528,6 +530,55 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     const int kk = wb ? qs::KEY_BF16 : qs::KEY_F32;
     float* hbuf = h ? h : wsp.h;
     hipError_t e;
+
+    // Small batches of the squared-ReLU kinds with bf16 weights.  The input
+    // selection writes X (.) M; the up launch computes whole column tiles of
+    // u over all selected rows (fixed-order sums, no K split, no atomics) and
+    // writes h; the selection of h writes only its descriptor (tau, cutoff)
+    // (and the index list if asked for); the down gather applies it to h and
+    // gathers only the selected rows of W_down^T.
+    if (!drelu && wb && qs::up_cols_supported(rows, d, ffn)) {
+        const qs::GemvPlan pdn = qs::plan_gemv(rows, ffn, d, wb);
+        if (pdn.bt <= 8 && pdn.scratch_floats <= wsp.partial_cap &&
+            (size_t)pdn.n_counters <= wsp.down_ctr_cap) {
+            const bool acc = !deterministic() && yt == QS_F32 && qs::gemv_accumulate_supported(pdn, wb);
+            qs::TopkArgs t{};
+            t.x = x; t.d = d; t.k = k_in; t.idx_stride = k_in;
+            t.xs = wsp.xs1;
+            t.zero_ptr = wsp.ctr_down; t.n_zero = pdn.n_counters;
+            if (acc) { t.zero_rows = (int32_t*)y; t.zero_row_len = d; }
+            e = qs::launch_topk(kk, qs::XS_F32, rows, t, st);
+            if (e != hipSuccess) return hip_fail(e, fn);
+            qs::UpColsArgs u{};
+            u.xs = wsp.xs1; u.rows = rows; u.d = d; u.ffn = ffn;
+            u.w = (const uint16_t*)w_up;
+            u.w2 = act == QS_ACT_RELU2_GLU ? (const uint16_t*)w_gate : nullptr;
+            u.h = hbuf;
+            e = qs::launch_up_cols(u, st);
+            if (e != hipSuccess) return hip_fail(e, fn);
+            if (k_mid >= 0) {
+                qs::TopkArgs tm{};
+                tm.x = hbuf; tm.d = ffn; tm.k = k_mid;
+                tm.tau = wsp.desc; tm.cutoff = (int32_t*)wsp.desc + rows; tm.cutoff_any = 1;
+                tm.idx = mid_idx; tm.idx_stride = ffn; tm.count = mid_cnt;
+                e = qs::launch_topk(qs::KEY_F32, qs::XS_NONE, rows, tm, st);
+                if (e != hipSuccess) return hip_fail(e, fn);
+            } else if (mid_idx || mid_cnt) {
+                e = qs::launch_nonzero_lists(hbuf, rows, ffn, mid_idx, mid_cnt, st);
+                if (e != hipSuccess) return hip_fail(e, fn);
+            }
+            qs::GemvArgs g{};
+            g.xs = hbuf; g.rows = rows; g.d_in = ffn; g.n_out = d; g.w = w_down_t;
+            g.partial = wsp.partial; g.counters = wsp.ctr_down; g.y = y; g.y_bf16 = yt == QS_BF16;
+            g.epilogue = qs::EPI_STORE;
+            g.accumulate = acc ? 1 : 0;
+            g.sel_desc = k_mid >= 0 ? wsp.desc : nullptr;   // k_mid < 0: every nonzero entry
+            e = qs::launch_gemv(pdn, wb, g, st);
+            if (e != hipSuccess) return hip_fail(e, fn);
+            return ok();
+        }
+    }
+
     // Accumulate forms (unless fixed-order sums are asked for): the gathers'
     // workgroups add their partial tiles into zeroed fp32 buffers instead of
     // handing them to a last workgroup.  Up projection: the input selection

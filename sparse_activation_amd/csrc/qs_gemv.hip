@@ -29,6 +29,7 @@
 // The ternary x int8 variant does the same with 2-bit packed weights and
 // exact int32 accumulation.
 #include "qs_internal.h"
+#include "qs_rowsel.h"
 
 namespace qs {
 namespace {
@@ -149,6 +150,10 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
 
 // DUAL: a second matrix (a.w2, the gate) is streamed at the same rows into a
 // second set of sums, and the output is relu2_glu(gate, up).
+// With a.sel_desc, xs is not yet sparsified: each token's coefficients are
+// kept only where the top-k descriptor (tau, cutoff) of its row selects them
+// (Turbo Sparse summary, Eq. 3-4: the top-k% of the intermediate by |h|
+// before W_down), so no selection launch and no sparsified copy are needed.
 template <int WBF16, int BT, bool DUAL = false>
 __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, int nsplit) {
     constexpr int EPT = WBF16 ? 8 : 4;
@@ -193,6 +198,19 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
         for (int t = 0; t < BT; ++t)
             c[ch][t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
                 xr, jin ? (uint32_t)((t * d_in + j) * 4) : kOOB, 0, 0));
+    }
+    if (a.sel_desc != nullptr) {   // uniform
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+            if (t >= ntok) break;   // uniform
+            const uint32_t tau = a.sel_desc[tok0 + t], cut = a.sel_desc[rows + tok0 + t];
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) {
+                const uint32_t j = (uint32_t)(j0 + ch * kNT + tid);
+                if (!rowsel::selected(__float_as_uint(c[ch][t]) & 0x7FFFFFFFu, j, tau, cut))
+                    c[ch][t] = 0.0f;
+            }
+        }
     }
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
@@ -380,6 +398,204 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
                 }
             }
             if (tid == 0) store_agent(&a.counters[ci], 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Up projection of a small-batch squared-ReLU FFN without a K split (Q-Sparse
+// news article, section "Sparsification with the Top-K function": X (.) M
+// replaces X in the product, so only the rows of W_up^T that some token
+// selects are read).
+//
+//   * each workgroup (512 threads) owns a tile of 64 output columns over ALL
+//     rows that some token of its tile selects: it compacts the nonzero
+//     entries of the sparsified x (written by the selection launch) into an
+//     ascending row list, then eight lanes stream one 128-byte row segment
+//     with 16-byte loads (eight rows per wavefront load), U rows per lane and
+//     stage in two ping-pong register stages, fp32 FMA;
+//   * the 64 row slots are summed with one DPP rotation and then in LDS, in a
+//     fixed order, so u is complete (no split partials, no atomics, bitwise
+//     reproducible) and the activation is applied here: h = relu(u)^2, or
+//     with the gate (DUAL) h = relu(g)^2 * u;
+// ---------------------------------------------------------------------------
+constexpr int kUcNT = 512;                   // threads per workgroup
+constexpr int kUcLPR = 8;                    // lanes per 128-byte row segment
+constexpr int kUcSlots = kUcNT / kUcLPR;     // 64 row slots per workgroup
+constexpr int kUcCols = kUcLPR * 8;          // 64 bf16 columns per tile
+
+// Rows per lane and pipeline stage: one token streams 16 (a Llama-7B
+// selection in two stages), more tokens or the gated pair 8.
+template <int BT, bool DUAL>
+constexpr int uc_unroll() { return BT == 1 && !DUAL ? 16 : 8; }
+
+// Entries of the padded row list for rows of length d (the stage loop reads
+// one stage past an even number of stages).
+constexpr int64_t uc_list_cap(int64_t d, int u) {
+    const int64_t batch = (int64_t)kUcSlots * u;
+    const int64_t nb = (d + batch - 1) / batch;
+    return ((nb + 1) / 2 * 2 + 1) * batch;
+}
+
+template <int BT, int E, bool DUAL>
+__global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
+    constexpr int U = uc_unroll<BT, DUAL>();
+    constexpr int BATCH = kUcSlots * U;
+    constexpr int NM = DUAL ? 2 : 1;
+    constexpr int NW = kUcNT / 64;
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    __shared__ uint32_t s_wsum[16];
+
+    const int tile = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t d = a.d, ffn = a.ffn;
+    const int64_t tok0 = (int64_t)blockIdx.y * BT;
+    const int64_t ntok = min((int64_t)BT, a.rows - tok0);
+
+    // Phase 1: this thread's run of E entries of each token's sparsified x.
+    float xv[BT][E];
+    uint32_t selm[BT];
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(a.xs + (tok0 + t) * d), (short)0,
+            t < ntok ? (int)(d * 4) : 0, 0x00020000);
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                xr, (uint32_t)((tid * E + 4 * q) * 4), 0, 0);
+            xv[t][4 * q] = __uint_as_float(v.x); xv[t][4 * q + 1] = __uint_as_float(v.y);
+            xv[t][4 * q + 2] = __uint_as_float(v.z); xv[t][4 * q + 3] = __uint_as_float(v.w);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+        selm[t] = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) selm[t] |= (xv[t][e] != 0.0f ? 1u : 0u) << e;
+    }
+
+    // Phase 2: the union of the selections as an ascending row list with each
+    // token's coefficient (0 where the token does not select the row).
+    const int64_t cap = uc_list_cap(d, U);
+    uint32_t* s_off = reinterpret_cast<uint32_t*>(smem);
+    float* s_coef = smem + cap;
+    uint32_t um = 0;
+#pragma unroll
+    for (int t = 0; t < BT; ++t) um |= selm[t];
+    uint32_t nsel;
+    uint32_t pos = rowsel::block_excl_scan<kUcNT>((uint32_t)__popc(um), s_wsum, tid, nsel);
+    const uint32_t rowbytes = (uint32_t)(ffn * 2);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (um & (1u << e)) {
+            s_off[pos] = (uint32_t)(tid * E + e) * rowbytes;
+#pragma unroll
+            for (int t = 0; t < BT; ++t) s_coef[pos * BT + t] = xv[t][e];
+            ++pos;
+        }
+    }
+    const int nbatch = (int)((nsel + BATCH - 1) / BATCH);
+    const int npad = ((nbatch + 1) / 2 * 2 + 1) * BATCH;
+    for (int i = (int)nsel + tid; i < npad; i += kUcNT) {
+        s_off[i] = kOOB;
+#pragma unroll
+        for (int t = 0; t < BT; ++t) s_coef[i * BT + t] = 0.0f;
+    }
+    __syncthreads();
+
+    // Phase 3: stream the 128-byte segments of the selected rows.
+    const int slot = tid / kUcLPR;
+    const int64_t col = (int64_t)tile * kUcCols + (lane % kUcLPR) * 8;
+    const uint32_t colb = col < ffn ? (uint32_t)(col * 2) : kOOB;
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, d * (int64_t)rowbytes);
+    const __amdgpu_buffer_rsrc_t rs2 = weight_rsrc(DUAL ? a.w2 : a.w, d * (int64_t)rowbytes);
+    float acc[NM][BT][8];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[m][t][e] = 0.0f;
+    u32x4 bufa[NM][U], bufb[NM][U];
+    auto load_stage = [&](u32x4 (*dst)[U], int bi) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t off = s_off[bi * BATCH + u * kUcSlots + slot] + colb;
+            dst[0][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+            if constexpr (DUAL) dst[1][u] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off, 0, 0);
+        }
+    };
+    auto fma_stage = [&](const u32x4 (*src)[U], int bi) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int ai = bi * BATCH + u * kUcSlots + slot;
+            float cf[BT];
+#pragma unroll
+            for (int t = 0; t < BT; ++t) cf[t] = s_coef[ai * BT + t];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                float w[8];
+                unpack<1>(src[m][u], w);
+#pragma unroll
+                for (int t = 0; t < BT; ++t)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[m][t][e] = fmaf(cf[t], w[e], acc[m][t][e]);
+            }
+        }
+    };
+    load_stage(bufa, 0);
+    for (int bi = 0; bi < nbatch; bi += 2) {
+        load_stage(bufb, bi + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        fma_stage(bufa, bi);
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage(bufa, bi + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        fma_stage(bufb, bi + 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Phase 4: sum the 64 row slots in a fixed order.  Inside each 16-lane
+    // row the two slots of a column group are summed by one DPP rotation
+    // (row_ror 8); lanes 0..7 of each row then hold the row's sums, and the
+    // 32 rows of the workgroup are summed in LDS in row order (over the dead
+    // row list).
+    __syncthreads();
+    float* s_red = smem;   // [32][NM][BT][kUcCols]
+    const int rrow = wave * 4 + (lane >> 4);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float v = acc[m][t][e];
+                v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+                if ((lane & 15) < kUcLPR)
+                    s_red[((rrow * NM + m) * BT + t) * kUcCols + (lane & 15) * 8 + e] = v;
+            }
+    __syncthreads();
+    static_assert(BT * kUcCols <= kUcNT, "one output per thread");
+    if (tid < BT * kUcCols) {   // wavefront t holds token t's 64 columns
+        const int t = tid / kUcCols, c = tid % kUcCols;
+        float sum[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            float v = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4 * NW; ++r) v += s_red[((r * NM + m) * BT + t) * kUcCols + c];
+            sum[m] = v;
+        }
+        const int64_t cg = (int64_t)tile * kUcCols + c;
+        const bool valid = t < ntok && cg < ffn;
+        float hv = 0.0f;
+        if constexpr (DUAL) hv = relu2_glu(sum[1], sum[0]);
+        else hv = sum[0] > 0.0f ? __fmul_rn(sum[0], sum[0]) : 0.0f;
+        if (valid) {
+            const int64_t i = (tok0 + t) * ffn + cg;
+            a.h[i] = hv;
+            if (a.h2 != nullptr) a.h2[i] = hv;
         }
     }
 }
@@ -1498,6 +1714,8 @@ bool gemv_accumulate_supported(const GemvPlan& p, int w_is_bf16) {
 
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
+    // The descriptor form exists in the FMA kernel (tiles of at most eight tokens).
+    if (a.sel_desc != nullptr && p.bt > 8) return hipErrorInvalidValue;
     if (a.accumulate && (a.y_bf16 || a.epilogue != EPI_STORE || !gemv_accumulate_supported(p, w_is_bf16)))
         return hipErrorInvalidValue;
     if (a.row_out != nullptr && (!a.accumulate || p.bt != 1 || a.row_scale == nullptr))
@@ -1545,6 +1763,35 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
     QS_GEMV_CASE(1, 1) QS_GEMV_CASE(1, 2) QS_GEMV_CASE(1, 4) QS_GEMV_CASE(1, 8)
     QS_GEMV_CASE(0, 1) QS_GEMV_CASE(0, 2) QS_GEMV_CASE(0, 4) QS_GEMV_CASE(0, 8)
 #undef QS_GEMV_CASE
+    return hipErrorInvalidValue;
+}
+
+bool up_cols_supported(int64_t rows, int64_t d, int64_t ffn) {
+    return rows >= 1 && rows <= 4 && d % 4 == 0 && d <= kUpColsMaxD && ffn % 8 == 0 &&
+           ffn <= kUpColsMaxFfn;
+}
+
+hipError_t launch_up_cols(const UpColsArgs& a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    if (!up_cols_supported(a.rows, a.d, a.ffn)) return hipErrorInvalidValue;
+    const int bt = a.rows == 1 ? 1 : a.rows == 2 ? 2 : 4;
+    const int e = a.d <= 4 * kUcNT ? 4 : a.d <= 8 * kUcNT ? 8 : a.d <= 12 * kUcNT ? 12 : 16;
+    const dim3 grid((unsigned)ceil_div(a.ffn, kUcCols), (unsigned)ceil_div(a.rows, bt));
+    const bool dual = a.w2 != nullptr;
+    const int u = bt == 1 && !dual ? 16 : 8;
+    size_t lds = (size_t)uc_list_cap(a.d, u) * (4 + 4 * bt);
+    const size_t lds_red = (size_t)32 * (dual ? 2 : 1) * bt * kUcCols * 4;
+    if (lds < lds_red) lds = lds_red;
+#define QS_UC_CASE(BTV, EV, DU)                                                          \
+    if (bt == BTV && e == EV && dual == DU) {                                            \
+        up_cols_kernel<BTV, EV, DU><<<grid, dim3(kUcNT), lds, stream>>>(a);              \
+        return hipGetLastError();                                                        \
+    }
+#define QS_UC_E(BTV, DU) QS_UC_CASE(BTV, 4, DU) QS_UC_CASE(BTV, 8, DU) QS_UC_CASE(BTV, 12, DU) QS_UC_CASE(BTV, 16, DU)
+    QS_UC_E(1, false) QS_UC_E(2, false) QS_UC_E(4, false)
+    QS_UC_E(1, true) QS_UC_E(2, true) QS_UC_E(4, true)
+#undef QS_UC_E
+#undef QS_UC_CASE
     return hipErrorInvalidValue;
 }
 

@@ -58,6 +58,10 @@ struct TopkArgs {
     void* frag;
     int64_t frag_groups;
     int frag_lo;
+    // 1: any cutoff that gives the same selection will do (a descriptor for
+    // a later launch, not an output): when every key equal to tau is
+    // selected, cutoff = 0x7FFFFFFF and the tie ranking is skipped.
+    int cutoff_any;
 };
 enum Xform : int { XF_NONE = 0, XF_RELU2 = 1, XF_RELU2_GLU = 2 };
 bool topk_xform_supported(int64_t d);
@@ -127,6 +131,12 @@ struct GemvArgs {
     // pairs' routing weights and tokens).
     const float* row_scale;
     const int32_t* row_out;
+    // Or null: xs is not sparsified yet; row r's selected entries are those
+    // with key > tau_r, or key == tau_r and index < cutoff_r (key = the
+    // magnitude bits), with tau = sel_desc[0 .. rows) and cutoff =
+    // sel_desc[rows .. 2 rows) (the top-k descriptor of launch_topk), and
+    // only they are gathered.
+    const uint32_t* sel_desc;
 };
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 // Both projections of the gated squared ReLU in one gather (tiles of at most
@@ -142,6 +152,23 @@ bool gemv_accumulate_supported(const GemvPlan& p, int w_is_bf16);
 // only, not the dual gather).
 bool gemv_takes_records(const GemvPlan& p, int w_is_bf16, int64_t rows);
 void* gemv_records(const GemvPlan& p, float* partial, int64_t d_in, int64_t* groups);
+
+// ---------------------------------------------------------------- small-batch FFN up projection
+// u = xs . W_up^T (and with w2 the gate's g) over every row that some token
+// of the tile selects, no K split (whole 64-column tiles per workgroup), then
+// h = relu(u)^2 (relu(g)^2 * u).
+struct UpColsArgs {
+    const float* xs;         // fp32 [rows, d]: the sparsified x (0 off the selection)
+    int64_t rows, d, ffn;
+    const uint16_t* w;       // bf16 W_up^T [d, ffn]
+    const uint16_t* w2;      // bf16 W_gate^T [d, ffn] (gated form) or null
+    float* h;                // fp32 [rows, ffn]
+    float* h2;               // or null: a second copy of h
+};
+constexpr int64_t kUpColsMaxD = 16 * 512;
+constexpr int64_t kUpColsMaxFfn = 32 * 512;
+bool up_cols_supported(int64_t rows, int64_t d, int64_t ffn);
+hipError_t launch_up_cols(const UpColsArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- ternary x int8 gather
 struct I8tPlan {

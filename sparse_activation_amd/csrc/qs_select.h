@@ -132,14 +132,14 @@ __device__ __forceinline__ void radix_select(const uint32_t (&key)[EPT], uint32_
     constexpr int NW = NT / kWave, S1 = L::S1, NB1 = L::NB1;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
     auto count_level = [&](uint32_t* hist, uint32_t pre, uint32_t hm, int sh, uint32_t dm) {
-        uint32_t nzero = 0;
+        uint32_t nzero = 0;   // this thread's zero keys, summed over the wavefront below
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             const bool m = key[i] != kInvalid && (key[i] & hm) == pre;
-            nzero += (uint32_t)__popcll(__ballot(m && key[i] == 0u));
+            nzero += (m && key[i] == 0u) ? 1u : 0u;
             if (m && key[i] != 0u) atomicAdd(&hist[(key[i] >> sh) & dm], 1u);
         }
-        nzero = __builtin_amdgcn_readfirstlane(nzero);
+        nzero = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan_dpp(nzero), kWave - 1);
         if (lane == 0 && nzero != 0) atomicAdd(&hist[0], nzero);
     };
     uint32_t prefix = 0, himask = 0, kr = k, dg = 0, cnt = 0;
@@ -175,16 +175,21 @@ __device__ __forceinline__ void radix_select(const uint32_t (&key)[EPT], uint32_
     if (compact) {
       if constexpr (S1 > 8) {
         // Several digits left over few keys: compact them (one LDS atomic per
-        // wavefront and entry slot) and let wavefront 0 finish alone.
+        // wavefront, a wavefront prefix sum placing each thread's run; the
+        // order of the candidates does not matter) and let wavefront 0
+        // finish alone.
+        uint32_t mc = 0;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i)
+            mc += (key[i] != kInvalid && (key[i] & himask) == prefix) ? 1u : 0u;
+        const uint32_t incl = wave_incl_scan_dpp(mc);
+        const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+        uint32_t base = 0;
+        if (lane == 0 && wtot != 0) base = atomicAdd(&s.nc, wtot);
+        uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane((int)base) + incl - mc;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
-            const bool m = key[i] != kInvalid && (key[i] & himask) == prefix;
-            const uint64_t bm = __ballot(m);
-            if (bm == 0) continue;   // uniform
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&s.nc, (uint32_t)__popcll(bm));
-            base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-            if (m) s.cand[base + popc_below(bm)] = key[i];
+            if (key[i] != kInvalid && (key[i] & himask) == prefix) s.cand[pos++] = key[i];
         }
         __syncthreads();
         if (wave == 0 && cnt <= (uint32_t)kWave) {

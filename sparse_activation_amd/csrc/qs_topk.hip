@@ -744,7 +744,8 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
     // The tie ranks are needed only when some keys equal to tau stay out (or
     // the cutoff is asked for), the output slots only for the index list.
     uint32_t eqb[NQ], selc[NQ], selb[NQ];
-    if (kr < eqtot || a.cutoff != nullptr) {
+    const bool all_ties = k > 0 && kr >= eqtot;   // uniform
+    if (kr < eqtot || (a.cutoff != nullptr && !(a.cutoff_any && all_ties))) {
         block_scan(eqc, eqb, 0);
     } else {
 #pragma unroll
@@ -763,7 +764,8 @@ __global__ __launch_bounds__(NT) void topk_vec_kernel(TopkArgs a) {
 
     // Index list and cutoff (optional outputs): a separate pass behind one
     // uniform branch, so the common path carries no per-entry scatter.
-    if (a.idx != nullptr || a.cutoff != nullptr) {
+    if (a.cutoff_any && all_ties && a.cutoff != nullptr && tid == 0) a.cutoff[r] = 0x7FFFFFFF;
+    if (a.idx != nullptr || (a.cutoff != nullptr && !(a.cutoff_any && all_ties))) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             if (!run_valid(q)) continue;
