@@ -291,6 +291,31 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qs_sparse_ffn_static -- qs_sparse_ffn without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.
+ *
+ *   Arguments, arithmetic, outputs and errors as qs_sparse_ffn.  The
+ *   workspace is a file-scope device array of QS_STATIC_SCRATCH_BYTES (32
+ *   MiB) in the library, one per GPU, held from the first call on that GPU
+ *   until the process ends; the call itself allocates nothing.  A shape
+ *   whose qs_sparse_ffn workspace (qs_workspace_bytes) exceeds that size is
+ *   rejected with QS_ERR_UNSUPPORTED before anything is enqueued (every
+ *   Llama-7B / Mistral-7B shaped FFN of up to 16 tokens fits).
+ *   The stream must belong to the current device.  The array keeps the last
+ *   call's contents and needs no clearing (every call clears what it uses).
+ *   Calls that may overlap on one GPU (other streams, other host threads)
+ *   race on the shared array: serialise them.
+ */
+#define QS_STATIC_SCRATCH_BYTES (32u << 20)
+qs_status qs_sparse_ffn_static(const void* x, qs_dtype dt, int64_t rows, int64_t d, int64_t ffn,
+                               qs_act act, int64_t k_in, int64_t k_mid,
+                               const void* w_gate, const void* w_up, const void* w_down_t,
+                               const float* b_gate, const float* b_up,
+                               void* y, qs_dtype yt, float* h, int32_t* mid_idx,
+                               int32_t* mid_cnt, void* stream);
+
+/*
  * qs_sparse_linear_backward -- gradients of Y = (X (.) M) . W^T for a given
  * dL/dY, the top-K passed by the straight-through estimator  [QS-STE],
  * [QS-TopK]:

@@ -22,12 +22,14 @@ __all__ = [
     "OP_SPARSE_FFN_DRELU", "OP_GATHER_LINEAR", "OP_SPARSE_FFN_RELU2_GLU",
     "OP_SPARSE_LINEAR_BACKWARD", "qs_sparse_linear_backward", "OP_BLOCK_SPARSE_LINEAR",
     "qs_block_sparse_linear", "OP_SPARSE_MOE_FFN", "qs_sparse_moe_ffn",
-    "qs_gather_linear_acc", "qs_set_deterministic",
+    "qs_gather_linear_acc", "qs_set_deterministic", "qs_sparse_ffn_static",
+    "STATIC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
 QS_OK, QS_ERR_INVALID_ARG, QS_ERR_UNSUPPORTED, QS_ERR_WORKSPACE, QS_ERR_HIP = range(5)
+STATIC_SCRATCH_BYTES = 32 << 20   # QS_STATIC_SCRATCH_BYTES
 F32, BF16, I8 = 0, 1, 2
 LAYOUT_WT, LAYOUT_W = 0, 1
 ACT_RELU2, ACT_DRELU, ACT_RELU2_GLU = 0, 1, 2
@@ -56,6 +58,8 @@ _SIGS = {
                              _P, _P, ctypes.c_size_t, _P],
     "qs_sparse_ffn": [_P, _INT, _I64, _I64, _I64, _INT, _I64, _I64, _P, _P, _P, _P, _P, _P,
                       _INT, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "qs_sparse_ffn_static": [_P, _INT, _I64, _I64, _I64, _INT, _I64, _I64, _P, _P, _P, _P, _P,
+                             _P, _INT, _P, _P, _P, _P],
     "qs_workspace_bytes": [_INT, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
     "qs_ternarize": [_P, _I64, _I64, _P, ctypes.POINTER(ctypes.c_float)],
     "qs_pack_ternary": [_P, _I64, _I64, _P],
@@ -396,6 +400,30 @@ def qs_sparse_ffn(x, act: int, k_in: int, k_mid: int, w_up, w_down_t, w_gate=Non
                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down_t), _ptr(b_gate),
                                 _ptr(b_up), _ptr(y), _dtype_code(y), _ptr(h), _ptr(mid_idx),
                                 _ptr(mid_cnt), _ptr(ws), ws_bytes, _stream(dev)))
+    return y, h, mid_idx, mid_cnt
+
+
+def qs_sparse_ffn_static(x, act: int, k_in: int, k_mid: int, w_up, w_down_t, w_gate=None,
+                         b_gate=None, b_up=None, y=None, y_dtype=None, h=None, mid_idx=None,
+                         mid_cnt=None, want_h=False, want_mid=False):
+    """qs_sparse_ffn on the library's per-GPU scratch array (no workspace is
+    allocated); returns (y, h, mid_idx, mid_cnt)."""
+    torch = _torch()
+    rows, d = x.shape
+    ffn = w_down_t.shape[0]
+    dev = _dev(x, w_up, w_down_t, w_gate, b_gate, b_up, y, h, mid_idx, mid_cnt)
+    if y is None:
+        y = torch.empty((rows, d), dtype=y_dtype or torch.float32, device=dev)
+    if want_h and h is None:
+        h = torch.empty((rows, ffn), dtype=torch.float32, device=dev)
+    if want_mid and mid_idx is None:
+        mid_idx = torch.empty((rows, ffn), dtype=torch.int32, device=dev)
+    if want_mid and mid_cnt is None:
+        mid_cnt = torch.empty(rows, dtype=torch.int32, device=dev)
+    _check(load().qs_sparse_ffn_static(_ptr(x), _dtype_code(x), rows, d, ffn, act, k_in, k_mid,
+                                       _ptr(w_gate), _ptr(w_up), _ptr(w_down_t), _ptr(b_gate),
+                                       _ptr(b_up), _ptr(y), _dtype_code(y), _ptr(h),
+                                       _ptr(mid_idx), _ptr(mid_cnt), _stream(dev)))
     return y, h, mid_idx, mid_cnt
 
 

@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/qs.h"
@@ -714,6 +715,72 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     e = qs::launch_gemv(pd, wb, g, st);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------------------- allocation-free FFN
+// Scratch of qs_sparse_ffn_static: one array per GPU, held until the process
+// ends.  Host code never passes the array's name to a kernel or a copy (on
+// the host it is a stand-in, not a device address): each device's address is
+// looked up once with hipGetSymbolAddress, with that device current, and the
+// kernels receive it as their workspace.
+static __device__ __align__(256) unsigned char scratch[QS_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device
+
+// The current device's address of the scratch array (looked up on the first
+// call on that device).
+qs_status static_scratch(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(QS_ERR_UNSUPPORTED, "%s: device index %d is beyond %d", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, fn);
+        if (p == nullptr) return fail(QS_ERR_HIP, "%s: no device address for the scratch array", fn);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qs_status qs_sparse_ffn_static(const void* x, qs_dtype dt, int64_t rows, int64_t d, int64_t ffn,
+                               qs_act act, int64_t k_in, int64_t k_mid,
+                               const void* w_gate, const void* w_up, const void* w_down_t,
+                               const float* b_gate, const float* b_up,
+                               void* y, qs_dtype yt, float* h, int32_t* mid_idx,
+                               int32_t* mid_cnt, void* stream) {
+    const char* fn = "qs_sparse_ffn_static";
+    // qs_sparse_ffn's own validation first: without a workspace it enqueues
+    // nothing and, for valid arguments, stops at the workspace check.
+    const qs_status v = qs_sparse_ffn(x, dt, rows, d, ffn, act, k_in, k_mid, w_gate, w_up, w_down_t,
+                                      b_gate, b_up, y, yt, h, mid_idx, mid_cnt, nullptr, 0, stream);
+    if (v != QS_ERR_WORKSPACE) return v;   // QS_OK (rows == 0) or an argument error
+    const size_t need = ffn_ws(nullptr, rows, d, ffn, act == QS_ACT_DRELU).bytes;
+    if (need > (size_t)QS_STATIC_SCRATCH_BYTES)
+        return fail(QS_ERR_UNSUPPORTED,
+                    "%s: this shape needs %zu bytes of scratch, more than the %zu the library "
+                    "holds per GPU (use qs_sparse_ffn with a workspace)",
+                    fn, need, (size_t)QS_STATIC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    const qs_status st = static_scratch(fn, &ws);
+    if (st != QS_OK) return st;
+    return qs_sparse_ffn(x, dt, rows, d, ffn, act, k_in, k_mid, w_gate, w_up, w_down_t, b_gate,
+                         b_up, y, yt, h, mid_idx, mid_cnt, ws, (size_t)QS_STATIC_SCRATCH_BYTES,
+                         stream);
 }
 
 qs_status qs_sparse_linear_backward(const void* x, qs_dtype xt, int64_t rows, int64_t d_in,

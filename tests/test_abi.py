@@ -270,3 +270,21 @@ def test_moe_validation_and_workspace():
     assert call(wr=None) == 1
     assert call(wsb=need - 1) == 3
     assert call(rows=0) == 0
+
+
+def test_static_ffn_validation():
+    """The allocation-free FFN rejects a shape whose workspace exceeds its
+    per-GPU scratch before any HIP call, and rows == 0 is a no-op."""
+    lib = qs.load()
+    need = qs.qs_workspace_bytes(qs.OP_SPARSE_FFN_RELU2, 64, 4096, 11008)
+    assert need > qs.STATIC_SCRATCH_BYTES
+    assert qs.qs_workspace_bytes(qs.OP_SPARSE_FFN_RELU2, 16, 4096, 14336) <= qs.STATIC_SCRATCH_BYTES
+    st = lib.qs_sparse_ffn_static(FAKE, qs.BF16, 64, 4096, 11008, qs.ACT_RELU2, 1638, 4403,
+                                  None, FAKE, FAKE, None, None, FAKE, qs.F32, None, None, None,
+                                  None)
+    assert st == qs.QS_ERR_UNSUPPORTED and "scratch" in qs.qs_last_error()
+    assert lib.qs_sparse_ffn_static(None, qs.BF16, 0, 4096, 11008, qs.ACT_RELU2, 1, 1, None,
+                                    None, None, None, None, None, qs.F32, None, None, None,
+                                    None) == qs.QS_OK
+    assert lib.qs_sparse_ffn_static(FAKE, qs.BF16, 2, 4096, 11008, 9, 1, 1, None, FAKE, FAKE,
+                                    None, None, FAKE, qs.F32, None, None, None, None) == 1
