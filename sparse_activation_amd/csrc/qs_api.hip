@@ -463,6 +463,17 @@ qs_status qs_sparse_linear_i8t(const float* x, int64_t rows, int64_t d_in, int64
     I8tWs wsp = i8t_ws((char*)ws, rows, d_in, n_out);
     qs::I8tPlan plan = qs::plan_i8t(rows, d_in, n_out);
     hipStream_t st = (hipStream_t)stream;
+    if (qs::i8t_fused_supported(rows, d_in, n_out)) {
+        // 1-4 tokens: quantisation, selection and the exact integer sums in
+        // one launch (the workspace is not used).
+        qs::I8fArgs f{};
+        f.x = x; f.rows = rows; f.d_in = d_in; f.n_out = n_out; f.k = k;
+        f.wt = wt_packed; f.alpha = alpha; f.acc = acc; f.y = y; f.xq = xq; f.xscale = xscale;
+        f.idx = idx;
+        const hipError_t e = qs::launch_i8t_fused(f, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return ok();
+    }
     float* scale = xscale ? xscale : wsp.scale;
     qs::TopkArgs t{};
     t.x = x; t.d = d_in; t.k = k; t.idx = idx; t.idx_stride = k;

@@ -1231,6 +1231,224 @@ constexpr int kI8MaxCand = 4096;           // candidate rows per split (LDS stag
 constexpr int kI8TargetWG = 128;           // the whole matrix is a few MB: few, fuller workgroups
 static_assert(kI8CT == kNT, "the slot reduction gives each thread one column");
 
+// ---------------------------------------------------------------------------
+// The quantised linear for 1-4 tokens in one launch (Q-Sparse news article,
+// section "Sparsification with the Top-K function": activations quantised to
+// 8 bits before the top-K; ternary weights alpha * t).  Every workgroup
+//   * loads the fp32 x rows of its tokens (thread t holds entries
+//     [t E, t E + E)), forms gamma = max |x| by a block reduction and q =
+//     clamp(rint(x * s)), s = 127 / (gamma + 1e-5), every step IEEE binary32
+//     round-to-nearest-even;
+//   * finds the top-k of |q| itself: every wavefront reads the 128-bin LDS
+//     histogram of the 7-bit keys from the top and finds the key tau of the
+//     k-th largest and how many keys equal to it are taken; each thread then
+//     ranks its own ties by a block prefix count (index order = thread order),
+//     so no cutoff has to be broadcast;
+//   * each thread sums q_j t_j over its own selected features for the
+//     workgroup's CT output columns in exact int32 (CT / 4 packed bytes per
+//     row; the loads of unselected features use an out-of-range offset and
+//     move no data), then the threads' sums are added in LDS: integer sums,
+//     the same in any order, so there is no K split, handoff or atomic;
+//   * writes acc and y = fl32(fl32(acc) * fl32(alpha / s)); workgroup 0 also
+//     writes q, s and the index list when they are asked for.
+// ---------------------------------------------------------------------------
+template <int BT>
+constexpr int i8f_cols() { return 16; }
+
+template <int BT, int E>
+__global__ __launch_bounds__(kNT) void i8t_fused_kernel(I8fArgs a) {
+    constexpr int CT = i8f_cols<BT>();
+    constexpr int NW = kNT / 64;
+    extern __shared__ __attribute__((aligned(16))) int32_t ism[];
+    __shared__ uint32_t s_wsum[16];
+    __shared__ uint32_t s_tie[BT][NW];
+    __shared__ float s_fmax[BT][NW];
+    __shared__ uint32_t s_hist[BT][128];
+
+    const int tile = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t d = a.d_in, n_out = a.n_out;
+    const int ntok = (int)a.rows;
+    const int nvalid = (int)d - tid * E;         // entries of this thread's run
+
+    // Phase 1: x, gamma, q and the histogram of |q|.
+    float xv[BT][E];
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(a.x + (int64_t)t * d), (short)0, t < ntok ? (int)(d * 4) : 0, 0x00020000);
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)((tid * E + 4 * q) * 4), 0, 0);
+            xv[t][4 * q] = __uint_as_float(v.x); xv[t][4 * q + 1] = __uint_as_float(v.y);
+            xv[t][4 * q + 2] = __uint_as_float(v.z); xv[t][4 * q + 3] = __uint_as_float(v.w);
+        }
+    }
+    for (int i = tid; i < BT * 128; i += kNT) (&s_hist[0][0])[i] = 0;
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(xv[t][e]));
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if (lane == 0) s_fmax[t][wave] = m;
+    }
+    __syncthreads();
+    float scale[BT];
+    int32_t qv[BT][E];
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+        float g = s_fmax[t][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) g = fmaxf(g, s_fmax[t][w]);
+        scale[t] = __fdiv_rn(127.0f, __fadd_rn(g, 1e-5f));
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float r = rintf(__fmul_rn(xv[t][e], scale[t]));
+            r = fminf(fmaxf(r, -128.0f), 127.0f);
+            qv[t][e] = (int32_t)r;
+            if (t < ntok && e < nvalid) atomicAdd(&s_hist[t][qv[t][e] < 0 ? -qv[t][e] : qv[t][e]], 1u);
+        }
+    }
+    __syncthreads();
+
+    // Phase 2: selection masks over this thread's run, per token.
+    const uint32_t kk = (uint32_t)a.k;
+    uint32_t selm[BT];
+#pragma unroll
+    for (int t = 0; t < BT; ++t) {
+        selm[t] = 0;
+        if (t >= ntok || kk == 0) continue;   // uniform
+        // tau: lane l holds bins 127 - 2l and 126 - 2l; the running total from
+        // the top reaches k in exactly one lane.
+        const uint32_t c0 = s_hist[t][127 - 2 * lane], c1 = s_hist[t][126 - 2 * lane];
+        const uint32_t incl = sel::wave_incl_scan_dpp(c0 + c1);
+        const uint32_t excl = incl - c0 - c1;
+        const uint64_t hit = __ballot(excl < kk && kk <= incl);
+        const int src = (int)__builtin_ctzll(hit);
+        const uint32_t ex = (uint32_t)__builtin_amdgcn_readlane((int)excl, src);
+        const uint32_t h0 = (uint32_t)__builtin_amdgcn_readlane((int)c0, src);
+        const uint32_t h1 = (uint32_t)__builtin_amdgcn_readlane((int)c1, src);
+        const bool upper = kk <= ex + h0;
+        const uint32_t tau = upper ? 127u - 2u * (uint32_t)src : 126u - 2u * (uint32_t)src;
+        const uint32_t need = upper ? kk - ex : kk - ex - h0;   // keys equal to tau taken
+        const uint32_t eqn = upper ? h0 : h1;                   // keys equal to tau in all
+        uint32_t before = 0;   // keys equal to tau before this thread's run
+        if (need < eqn) {      // uniform: rank the ties in index order
+            uint32_t eq = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) eq += (e < nvalid && (uint32_t)abs(qv[t][e]) == tau) ? 1u : 0u;
+            const uint32_t wi = sel::wave_incl_scan_dpp(eq);
+            if (lane == 63) s_tie[t][wave] = wi;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < NW; ++w) before += w < wave ? s_tie[t][w] : 0u;
+            before += wi - eq;
+        } else {
+            before = 0;
+        }
+        uint32_t r = before;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t kv = (uint32_t)abs(qv[t][e]);
+            const bool tie = e < nvalid && kv == tau;
+            const bool on = e < nvalid && (kv > tau || (tie && r < need));
+            r += tie ? 1u : 0u;
+            selm[t] |= (on ? 1u : 0u) << e;
+        }
+    }
+
+    // Workgroup 0: the optional outputs q, s and the index list.
+    if (tile == 0) {
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+            if (t >= ntok) break;   // uniform
+            if (a.xq != nullptr) {
+#pragma unroll
+                for (int q = 0; q < E / 4; ++q) {
+                    if (4 * q >= nvalid) break;
+                    uint32_t pk = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pk |= ((uint32_t)qv[t][4 * q + i] & 0xFFu) << (8 * i);
+                    *reinterpret_cast<uint32_t*>(a.xq + (int64_t)t * d + tid * E + 4 * q) = pk;
+                }
+            }
+            if (a.xscale != nullptr && tid == 0) a.xscale[t] = scale[t];
+            if (a.idx != nullptr) {
+                uint32_t tot;
+                uint32_t pos = rowsel::block_excl_scan<kNT>((uint32_t)__popc(selm[t]), s_wsum, tid, tot);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if (selm[t] & (1u << e)) a.idx[(int64_t)t * a.k + pos++] = tid * E + e;
+            }
+        }
+    }
+
+    // Phase 3: this thread's selected rows (CT / 4 = 4 packed bytes each).
+    const uint32_t rowbytes = (uint32_t)(n_out / 4);
+    const uint32_t colb = (uint32_t)(tile * (CT / 4));
+    const __amdgpu_buffer_rsrc_t wr = weight_rsrc(a.wt, d * (int64_t)rowbytes);
+    uint32_t um = 0;
+#pragma unroll
+    for (int t = 0; t < BT; ++t) um |= selm[t];
+    uint32_t wseg[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        wseg[e] = __builtin_amdgcn_raw_buffer_load_b32(
+            wr, (um >> e) & 1u ? (uint32_t)(tid * E + e) * rowbytes + colb : kOOB, 0, 0);
+    int32_t acc[BT][CT];
+#pragma unroll
+    for (int t = 0; t < BT; ++t)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) acc[t][c] = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        int32_t qq[BT];
+#pragma unroll
+        for (int t = 0; t < BT; ++t) qq[t] = (selm[t] >> e) & 1u ? qv[t][e] : 0;
+#pragma unroll
+        for (int f = 0; f < 16; ++f) {
+            const int32_t tv = __builtin_amdgcn_sbfe(wseg[e], 2 * f, 2);   // 00 0, 01 +1, 11 -1
+#pragma unroll
+            for (int t = 0; t < BT; ++t) acc[t][f] += qq[t] * tv;
+        }
+    }
+
+    // Phase 4: exact sums over the threads, [BT * CT][kNT + 1] in LDS: PARTS
+    // threads add SPAN entries of one value each, then one thread per value
+    // adds the PARTS sums (integer sums: the same in any order).
+    constexpr int NV = BT * CT;
+    int32_t* s_red = ism;
+#pragma unroll
+    for (int t = 0; t < BT; ++t)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) s_red[(t * CT + c) * (kNT + 1) + tid] = acc[t][c];
+    __syncthreads();
+    constexpr int PARTS = kNT / NV;
+    constexpr int SPAN = kNT / PARTS;
+    int32_t part = 0;
+    {
+        const int v = tid % NV, p = tid / NV;
+#pragma unroll 8
+        for (int i = 0; i < SPAN; ++i) part += s_red[v * (kNT + 1) + p * SPAN + i];
+    }
+    __syncthreads();
+    s_red[tid] = part;   // [PARTS][NV]
+    __syncthreads();
+    if (tid < NV) {
+        int32_t sum = 0;
+#pragma unroll
+        for (int p = 0; p < PARTS; ++p) sum += s_red[p * NV + tid];
+        const int t = tid / CT, c = tid % CT;
+        const int64_t col = (int64_t)tile * CT + c;
+        if (t < ntok && col < n_out) {
+            if (a.acc != nullptr) a.acc[(int64_t)t * n_out + col] = sum;
+            if (a.y != nullptr)
+                a.y[(int64_t)t * n_out + col] = __fmul_rn((float)sum, __fdiv_rn(a.alpha, scale[t]));
+        }
+    }
+}
+
 template <int BT>
 __global__ __launch_bounds__(kNT) void i8t_gemv_kernel(I8tArgs a, int cand, int nsplit) {
     constexpr int BATCH = kI8NSlot * kUnroll;
@@ -1873,6 +2091,31 @@ I8tPlan plan_i8t(int64_t rows, int64_t d_in, int64_t n_out) {
     p.partial_ints = p.nsplit > 1 ? (size_t)p.nsplit * rows * n_out : 0;
     p.n_counters = p.n_tiles * p.n_tok_tiles;
     return p;
+}
+
+bool i8t_fused_supported(int64_t rows, int64_t d_in, int64_t n_out) {
+    return rows >= 1 && rows <= 4 && d_in % 4 == 0 && d_in <= 16 * kNT && n_out % 16 == 0;
+}
+
+hipError_t launch_i8t_fused(const I8fArgs& a, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    if (!i8t_fused_supported(a.rows, a.d_in, a.n_out) || a.k < 0 || a.k > a.d_in)
+        return hipErrorInvalidValue;
+    const int bt = a.rows == 1 ? 1 : a.rows == 2 ? 2 : 4;
+    const int ct = bt == 4 ? i8f_cols<4>() : i8f_cols<1>();
+    const int e = a.d_in <= 4 * kNT ? 4 : a.d_in <= 8 * kNT ? 8 : 16;
+    const dim3 grid((unsigned)ceil_div(a.n_out, ct));
+    const size_t lds = (size_t)bt * ct * (kNT + 1) * 4;
+#define QS_I8F_CASE(BTV, EV)                                                       \
+    if (bt == BTV && e == EV) {                                                    \
+        i8t_fused_kernel<BTV, EV><<<grid, dim3(kNT), lds, stream>>>(a);            \
+        return hipGetLastError();                                                  \
+    }
+    QS_I8F_CASE(1, 4) QS_I8F_CASE(1, 8) QS_I8F_CASE(1, 16)
+    QS_I8F_CASE(2, 4) QS_I8F_CASE(2, 8) QS_I8F_CASE(2, 16)
+    QS_I8F_CASE(4, 4) QS_I8F_CASE(4, 8) QS_I8F_CASE(4, 16)
+#undef QS_I8F_CASE
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_i8t(const I8tPlan& p, const I8tArgs& a, hipStream_t stream) {

@@ -194,6 +194,23 @@ struct I8tArgs {
 };
 hipError_t launch_i8t(const I8tPlan& p, const I8tArgs& a, hipStream_t stream);
 
+// The whole quantised linear for 1-4 tokens in one launch: every workgroup
+// quantises x, selects the top-k of |q| and sums its output columns over the
+// selected rows in exact int32 (no workspace).
+struct I8fArgs {
+    const float* x;          // fp32 [rows, d_in]
+    int64_t rows, d_in, n_out, k;
+    const uint8_t* wt;       // [d_in, n_out/4] packed
+    float alpha;
+    int32_t* acc;            // [rows, n_out] or null
+    float* y;                // [rows, n_out] or null
+    int8_t* xq;              // [rows, d_in] or null
+    float* xscale;           // [rows] or null
+    int32_t* idx;            // [rows, k] or null
+};
+bool i8t_fused_supported(int64_t rows, int64_t d_in, int64_t n_out);
+hipError_t launch_i8t_fused(const I8fArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- masked MFMA GEMM
 struct MfmaArgs {
     const uint16_t* x;       // bf16 [M, K]: X (.) M

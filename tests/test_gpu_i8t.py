@@ -36,6 +36,9 @@ def _case(gpu_lib, x, w, k):
 
 
 @pytest.mark.parametrize("rows,d,n", [(1, 64, 16), (3, 300, 48), (5, 1000, 1040),
+                                      # 1-4 tokens: the one-launch kernel (ragged column
+                                      # tiles, runs past the row end, d % 4 != 0 elsewhere)
+                                      (2, 64, 16), (4, 4096, 48), (3, 1000, 1040), (1, 301, 32),
                                       (9, 513, 2064), (33, 256, 64),
                                       # token batches: the int8 matrix-core kernel (ragged
                                       # feature steps, column tiles and token tiles)
@@ -67,3 +70,25 @@ def test_i8t_full_c3(gpu_lib, batch):
     c = datagen.c3_i8t_linear(batch)
     note(f"i8t full config C3 B={batch}")
     _case(gpu_lib, c["X"], c["W"], c["K"])
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4])
+def test_i8t_bench_call(gpu_lib, batch):
+    """The call the benchmark times: acc and y only (no q, s or index list)."""
+    import torch
+    qs = gpu_lib
+    c = datagen.c3_i8t_linear(batch)
+    n, d = c["W"].shape
+    t_lib, alpha = qs.qs_ternarize(c["W"])
+    packed = to_dev(qs.qs_pack_ternary(t_lib))
+    acc = torch.empty((batch, n), dtype=torch.int32, device="cuda")
+    y = torch.empty((batch, n), dtype=torch.float32, device="cuda")
+    note(f"i8t bench call C3 B={batch}")
+    qs.qs_sparse_linear_i8t(to_dev(c["X"]), c["K"], packed, alpha, n, acc=acc, y=y, want_all=False)
+    torch.cuda.synchronize()
+    q_ref, s_ref, _ = oracle.absmax_quant_i8(c["X"])
+    t_ref, a_ref = oracle.ternarize(c["W"])
+    m_ref, _, _, _ = oracle.topk_select(oracle.magnitude(q_ref), c["K"])
+    acc_ref, y_ref = oracle.i8t_linear(q_ref, s_ref, t_ref, a_ref, m_ref)
+    assert np.array_equal(acc.cpu().numpy(), acc_ref)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
