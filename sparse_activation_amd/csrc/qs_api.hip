@@ -543,26 +543,37 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     float* hbuf = h ? h : wsp.h;
     hipError_t e;
 
-    // Small batches of the squared-ReLU kinds with bf16 weights.  The input
-    // selection writes X (.) M; the up launch computes whole column tiles of
-    // u over all selected rows (fixed-order sums, no K split, no atomics) and
-    // writes h; the selection of h writes only its descriptor (tau, cutoff)
-    // (and the index list if asked for); the down gather applies it to h and
-    // gathers only the selected rows of W_down^T.
+    // Small batches of the squared-ReLU kinds with bf16 weights.  The up
+    // launch (for one token selecting the top-k_in of x in every workgroup,
+    // else after a selection launch) computes whole column tiles of u over
+    // all selected rows (fixed-order sums, no K split, no atomics), writing
+    // h; the selection of h writes only its descriptor (tau, cutoff) (and the
+    // index list if asked for); the down gather applies it to h and gathers
+    // only the selected rows of W_down^T.
     if (!drelu && wb && qs::up_cols_supported(rows, d, ffn)) {
         const qs::GemvPlan pdn = qs::plan_gemv(rows, ffn, d, wb);
         if (pdn.bt <= 8 && pdn.scratch_floats <= wsp.partial_cap &&
             (size_t)pdn.n_counters <= wsp.down_ctr_cap) {
             const bool acc = !deterministic() && yt == QS_F32 && qs::gemv_accumulate_supported(pdn, wb);
-            qs::TopkArgs t{};
-            t.x = x; t.d = d; t.k = k_in; t.idx_stride = k_in;
-            t.xs = wsp.xs1;
-            t.zero_ptr = wsp.ctr_down; t.n_zero = pdn.n_counters;
-            if (acc) { t.zero_rows = (int32_t*)y; t.zero_row_len = d; }
-            e = qs::launch_topk(kk, qs::XS_F32, rows, t, st);
-            if (e != hipSuccess) return hip_fail(e, fn);
             qs::UpColsArgs u{};
-            u.xs = wsp.xs1; u.rows = rows; u.d = d; u.ffn = ffn;
+            u.x = (const uint16_t*)x; u.rows = rows; u.d = d; u.ffn = ffn; u.k = k_in;
+            if (rows == 1) {
+                // One token: the up launch selects it itself and clears what
+                // the down gather needs cleared.
+                if (acc) { u.zero = (float*)y; u.n_zero = rows * d; }
+                else { u.zero_i = wsp.ctr_down; u.n_zero_i = pdn.n_counters; }
+            } else {
+                // Several tokens: one selection launch (a workgroup per token)
+                // beats selecting every token in every up workgroup.
+                qs::TopkArgs t{};
+                t.x = x; t.d = d; t.k = k_in; t.idx_stride = k_in;
+                t.xs = wsp.xs1;
+                t.zero_ptr = wsp.ctr_down; t.n_zero = pdn.n_counters;
+                if (acc) { t.zero_rows = (int32_t*)y; t.zero_row_len = d; }
+                e = qs::launch_topk(kk, qs::XS_F32, rows, t, st);
+                if (e != hipSuccess) return hip_fail(e, fn);
+                u.xs = wsp.xs1;
+            }
             u.w = (const uint16_t*)w_up;
             u.w2 = act == QS_ACT_RELU2_GLU ? (const uint16_t*)w_gate : nullptr;
             u.h = hbuf;

@@ -408,10 +408,12 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
 // replaces X in the product, so only the rows of W_up^T that some token
 // selects are read).
 //
-//   * each workgroup (512 threads) owns a tile of 64 output columns over ALL
-//     rows that some token of its tile selects: it compacts the nonzero
-//     entries of the sparsified x (written by the selection launch) into an
-//     ascending row list, then eight lanes stream one 128-byte row segment
+//   * each workgroup (512 threads) finds the top-k of each token's bf16 x
+//     itself (two LDS histogram levels over the 15-bit magnitude keys, see
+//     rowsel::select15_masks), so no selection launch precedes it;
+//   * it owns a tile of 64 output columns over ALL rows that some token of
+//     its tile selects: the selected entries become an ascending row list
+//     with their coefficients, then eight lanes stream one 128-byte row segment
 //     with 16-byte loads (eight rows per wavefront load), U rows per lane and
 //     stage in two ping-pong register stages, fp32 FMA;
 //   * the 64 row slots are summed with one DPP rotation and then in LDS, in a
@@ -452,27 +454,75 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
     const int64_t tok0 = (int64_t)blockIdx.y * BT;
     const int64_t ntok = min((int64_t)BT, a.rows - tok0);
 
-    // Phase 1: this thread's run of E entries of each token's sparsified x.
-    float xv[BT][E];
-    uint32_t selm[BT];
-#pragma unroll
-    for (int t = 0; t < BT; ++t) {
-        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(a.xs + (tok0 + t) * d), (short)0,
-            t < ntok ? (int)(d * 4) : 0, 0x00020000);
-#pragma unroll
-        for (int q = 0; q < E / 4; ++q) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-                xr, (uint32_t)((tid * E + 4 * q) * 4), 0, 0);
-            xv[t][4 * q] = __uint_as_float(v.x); xv[t][4 * q + 1] = __uint_as_float(v.y);
-            xv[t][4 * q + 2] = __uint_as_float(v.z); xv[t][4 * q + 3] = __uint_as_float(v.w);
-        }
+    // Side jobs for the down projection that follows: clear a slice of the
+    // buffer it adds into (workgroups in turn), and its split counters.
+    if (a.zero != nullptr && blockIdx.y == 0) {
+        const int64_t per = (a.n_zero / 4 + gridDim.x - 1) / gridDim.x;
+        for (int64_t i = tile * per + tid; i < min((tile + 1) * per, a.n_zero / 4); i += kUcNT)
+            reinterpret_cast<uint4*>(a.zero)[i] = make_uint4(0u, 0u, 0u, 0u);
     }
+    if (a.zero_i != nullptr && tile == 0 && blockIdx.y == 0)
+        for (int i = tid; i < a.n_zero_i; i += kUcNT) a.zero_i[i] = 0;
+
+    // Phase 1: this thread's run of E entries of each token's activations
+    // and the token's selection as a bit mask over the run: either from the
+    // sparsified x of a selection launch (a.xs), or (a.x) the top-k of each
+    // token's bf16 x found inside this workgroup (Q-Sparse news article,
+    // Top-K section: the K entries of largest |x|, ties to the lower index),
+    // so that no selection launch precedes this one.
+    uint32_t selm[BT];
+    float xv[BT][E];
+    const int nvalid = (int)d - tid * E;
+    if (a.xs != nullptr) {   // uniform
 #pragma unroll
-    for (int t = 0; t < BT; ++t) {
-        selm[t] = 0;
+        for (int t = 0; t < BT; ++t) {
+            const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(a.xs + (tok0 + t) * d), (short)0,
+                t < ntok ? (int)(d * 4) : 0, 0x00020000);
 #pragma unroll
-        for (int e = 0; e < E; ++e) selm[t] |= (xv[t][e] != 0.0f ? 1u : 0u) << e;
+            for (int q = 0; q < E / 4; ++q) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                    xr, (uint32_t)((tid * E + 4 * q) * 4), 0, 0);
+                xv[t][4 * q] = __uint_as_float(v.x); xv[t][4 * q + 1] = __uint_as_float(v.y);
+                xv[t][4 * q + 2] = __uint_as_float(v.z); xv[t][4 * q + 3] = __uint_as_float(v.w);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+            selm[t] = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) selm[t] |= (xv[t][e] != 0.0f ? 1u : 0u) << e;
+        }
+    } else {
+        auto& L = *reinterpret_cast<rowsel::Sel15Lds<BT, NW>*>(smem);
+        uint32_t xr16[BT][E / 2];   // bf16 pairs
+#pragma unroll
+        for (int t = 0; t < BT; ++t) {
+            const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(a.x + (tok0 + t) * d), (short)0,
+                t < ntok ? (int)(d * 2) : 0, 0x00020000);
+#pragma unroll
+            for (int q = 0; q < E / 8; ++q) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                    xr, (uint32_t)((tid * E + 8 * q) * 2), 0, 0);
+                xr16[t][4 * q] = v.x; xr16[t][4 * q + 1] = v.y; xr16[t][4 * q + 2] = v.z; xr16[t][4 * q + 3] = v.w;
+            }
+        }
+        for (int i = tid; i < (int)(sizeof(L) / 4); i += kUcNT) reinterpret_cast<uint32_t*>(&L)[i] = 0;
+        uint32_t key[BT][E];
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                key[t][e] = e < nvalid ? (xr16[t][e / 2] >> (16 * (e % 2))) & 0x7FFFu : sel::kInvalid;
+        __syncthreads();
+        rowsel::select15_masks<kUcNT, BT, E>(key, (int)ntok, a.k, L, tid, selm);
+        __syncthreads();   // the selection scratch becomes the row list
+#pragma unroll
+        for (int t = 0; t < BT; ++t)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                xv[t][e] = (selm[t] >> e) & 1u ? __uint_as_float((xr16[t][e / 2] >> (16 * (e % 2))) << 16) : 0.0f;
     }
 
     // Phase 2: the union of the selections as an ascending row list with each
@@ -491,7 +541,7 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
         if (um & (1u << e)) {
             s_off[pos] = (uint32_t)(tid * E + e) * rowbytes;
 #pragma unroll
-            for (int t = 0; t < BT; ++t) s_coef[pos * BT + t] = xv[t][e];
+            for (int t = 0; t < BT; ++t) s_coef[pos * BT + t] = xv[t][e];   // 0 off the token's selection
             ++pos;
         }
     }
@@ -1985,7 +2035,7 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
 }
 
 bool up_cols_supported(int64_t rows, int64_t d, int64_t ffn) {
-    return rows >= 1 && rows <= 4 && d % 4 == 0 && d <= kUpColsMaxD && ffn % 8 == 0 &&
+    return rows >= 1 && rows <= 4 && d % 8 == 0 && d <= kUpColsMaxD && ffn % 8 == 0 &&
            ffn <= kUpColsMaxFfn;
 }
 
@@ -1993,19 +2043,22 @@ hipError_t launch_up_cols(const UpColsArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     if (!up_cols_supported(a.rows, a.d, a.ffn)) return hipErrorInvalidValue;
     const int bt = a.rows == 1 ? 1 : a.rows == 2 ? 2 : 4;
-    const int e = a.d <= 4 * kUcNT ? 4 : a.d <= 8 * kUcNT ? 8 : a.d <= 12 * kUcNT ? 12 : 16;
+    if (a.zero != nullptr && a.n_zero % 4 != 0) return hipErrorInvalidValue;
+    const int e = a.d <= 8 * kUcNT ? 8 : 16;
     const dim3 grid((unsigned)ceil_div(a.ffn, kUcCols), (unsigned)ceil_div(a.rows, bt));
     const bool dual = a.w2 != nullptr;
     const int u = bt == 1 && !dual ? 16 : 8;
     size_t lds = (size_t)uc_list_cap(a.d, u) * (4 + 4 * bt);
     const size_t lds_red = (size_t)32 * (dual ? 2 : 1) * bt * kUcCols * 4;
+    const size_t lds_sel = (size_t)bt * (4 * 256 + 128 + kUcNT / 64) * 4;
     if (lds < lds_red) lds = lds_red;
+    if (lds < lds_sel) lds = lds_sel;
 #define QS_UC_CASE(BTV, EV, DU)                                                          \
     if (bt == BTV && e == EV && dual == DU) {                                            \
         up_cols_kernel<BTV, EV, DU><<<grid, dim3(kUcNT), lds, stream>>>(a);              \
         return hipGetLastError();                                                        \
     }
-#define QS_UC_E(BTV, DU) QS_UC_CASE(BTV, 4, DU) QS_UC_CASE(BTV, 8, DU) QS_UC_CASE(BTV, 12, DU) QS_UC_CASE(BTV, 16, DU)
+#define QS_UC_E(BTV, DU) QS_UC_CASE(BTV, 8, DU) QS_UC_CASE(BTV, 16, DU)
     QS_UC_E(1, false) QS_UC_E(2, false) QS_UC_E(4, false)
     QS_UC_E(1, true) QS_UC_E(2, true) QS_UC_E(4, true)
 #undef QS_UC_E

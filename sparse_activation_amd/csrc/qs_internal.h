@@ -154,12 +154,18 @@ bool gemv_takes_records(const GemvPlan& p, int w_is_bf16, int64_t rows);
 void* gemv_records(const GemvPlan& p, float* partial, int64_t d_in, int64_t* groups);
 
 // ---------------------------------------------------------------- small-batch FFN up projection
-// u = xs . W_up^T (and with w2 the gate's g) over every row that some token
-// of the tile selects, no K split (whole 64-column tiles per workgroup), then
-// h = relu(u)^2 (relu(g)^2 * u).
+// The top-k of each bf16 x row (selected inside every workgroup), then u =
+// (x (.) M) . W_up^T (and with w2 the gate's g) over every row that some
+// token of the tile selects, no K split (whole 64-column tiles per
+// workgroup), then h = relu(u)^2 (relu(g)^2 * u).
 struct UpColsArgs {
-    const float* xs;         // fp32 [rows, d]: the sparsified x (0 off the selection)
-    int64_t rows, d, ffn;
+    const float* xs;         // fp32 [rows, d] sparsified x (0 off the selection), or null:
+    const uint16_t* x;       //   bf16 [rows, d], of which every workgroup selects
+    int64_t rows, d, ffn, k; //   the top-k of each row itself
+    float* zero;             // or null: cleared by the launch (n_zero % 4 == 0)
+    int64_t n_zero;
+    int32_t* zero_i;         // or null: int32 counters cleared by workgroup 0
+    int n_zero_i;
     const uint16_t* w;       // bf16 W_up^T [d, ffn]
     const uint16_t* w2;      // bf16 W_gate^T [d, ffn] (gated form) or null
     float* h;                // fp32 [rows, ffn]
