@@ -579,7 +579,11 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
             u.h = hbuf;
             e = qs::launch_up_cols(u, st);
             if (e != hipSuccess) return hip_fail(e, fn);
-            if (k_mid >= 0) {
+            if (k_mid >= 0 && !mid_idx && !mid_cnt && qs::desc31_supported(ffn)) {
+                // Only the descriptor: the lean selection.
+                e = qs::launch_desc31(hbuf, rows, ffn, k_mid, wsp.desc, st);
+                if (e != hipSuccess) return hip_fail(e, fn);
+            } else if (k_mid >= 0) {
                 qs::TopkArgs tm{};
                 tm.x = hbuf; tm.d = ffn; tm.k = k_mid;
                 tm.tau = wsp.desc; tm.cutoff = (int32_t*)wsp.desc + rows; tm.cutoff_any = 1;

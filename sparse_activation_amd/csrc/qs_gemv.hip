@@ -199,17 +199,19 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
             c[ch][t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
                 xr, jin ? (uint32_t)((t * d_in + j) * 4) : kOOB, 0, 0));
     }
+    auto apply_desc = [&](int t, uint32_t tau, uint32_t cut) {
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+            const uint32_t j = (uint32_t)(j0 + ch * kNT + tid);
+            if (!rowsel::selected(__float_as_uint(c[ch][t]) & 0x7FFFFFFFu, j, tau, cut))
+                c[ch][t] = 0.0f;
+        }
+    };
     if (a.sel_desc != nullptr) {   // uniform
 #pragma unroll
         for (int t = 0; t < BT; ++t) {
             if (t >= ntok) break;   // uniform
-            const uint32_t tau = a.sel_desc[tok0 + t], cut = a.sel_desc[rows + tok0 + t];
-#pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-                const uint32_t j = (uint32_t)(j0 + ch * kNT + tid);
-                if (!rowsel::selected(__float_as_uint(c[ch][t]) & 0x7FFFFFFFu, j, tau, cut))
-                    c[ch][t] = 0.0f;
-            }
+            apply_desc(t, a.sel_desc[tok0 + t], a.sel_desc[rows + tok0 + t]);
         }
     }
 #pragma unroll
@@ -2050,7 +2052,7 @@ hipError_t launch_up_cols(const UpColsArgs& a, hipStream_t stream) {
     const int u = bt == 1 && !dual ? 16 : 8;
     size_t lds = (size_t)uc_list_cap(a.d, u) * (4 + 4 * bt);
     const size_t lds_red = (size_t)32 * (dual ? 2 : 1) * bt * kUcCols * 4;
-    const size_t lds_sel = (size_t)bt * (4 * 256 + 128 + kUcNT / 64) * 4;
+    const size_t lds_sel = sizeof(rowsel::Sel15Lds<4, kUcNT / 64>) / 4 * bt;
     if (lds < lds_red) lds = lds_red;
     if (lds < lds_sel) lds = lds_sel;
 #define QS_UC_CASE(BTV, EV, DU)                                                          \

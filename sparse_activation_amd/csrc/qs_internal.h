@@ -313,6 +313,14 @@ hipError_t launch_moe_combine(const float* ypair, const float* pair_weight, int6
                               int top_k, int64_t d, void* y, int y_bf16, hipStream_t stream);
 
 // Nonzero compaction of h rows: idx[r, 0..cnt) ascending, cnt[r].
+// Top-k descriptor of each row of fp32 x [rows, d] by |x| (one workgroup per
+// row, rowsel::select_desc31): tau -> desc[r], cutoff -> desc[rows + r].
+// d % 4 == 0, d <= kDescMaxD.
+constexpr int64_t kDescMaxD = 4 * 4096;
+inline bool desc31_supported(int64_t d) { return d > 0 && d % 4 == 0 && d <= kDescMaxD; }
+hipError_t launch_desc31(const float* x, int64_t rows, int64_t d, int64_t k, uint32_t* desc,
+                         hipStream_t stream);
+
 hipError_t launch_nonzero_lists(const float* h, int64_t rows, int64_t n, int32_t* idx,
                                 int32_t* cnt, hipStream_t stream);
 

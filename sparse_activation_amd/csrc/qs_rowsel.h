@@ -47,10 +47,14 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
 //            of them in index order lets each thread take its own.
 // Three or four barriers, no broadcast of the result.  L must be zeroed, and
 // a barrier passed, before the call.
+constexpr int kH1Pitch = 256 + 16;
+
 template <int BT, int NW>
 struct Sel15Lds {
-    uint32_t h1[BT][4][256];   // four copies (by lane % 4): the few exponent bins of
-                               // an activation would serialise one copy's atomics
+    uint32_t h1[BT][4][kH1Pitch];   // four copies (by lane % 4): the few exponent bins
+                                    // of an activation would serialise one copy's
+                                    // atomics; the pitch puts a bin's copies on
+                                    // different banks
     uint32_t h2[BT][128];
     uint32_t tie[BT][NW];
 };
@@ -153,6 +157,242 @@ __device__ __forceinline__ void select15_masks(const uint32_t (&key)[BT][E], int
             selm[t] |= (on ? 1u : 0u) << e;
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Descriptor (tau, cutoff) of the top-k of one row of 31-bit keys (fp32
+// magnitudes) held by a workgroup, for kernels that select a row that a
+// previous launch wrote (the FFN intermediate h; Turbo Sparse summary, Eq. 3-4:
+// the top-k% of h by |h| before W_down).  Every wavefront scans each
+// histogram itself, so no wavefront waits for another's search:
+//   level 1: bits 30..20 of the nonzero keys (2048 bins: an exponent and three
+//            mantissa bits, so an activation's few exponents spread out); zero
+//            keys are not counted, so a row that is half zeros adds no
+//            conflicting atomics on one bin;
+//   level 2: bits 19..10 of the keys in level 1's boundary bin, which the same
+//            pass also copies, with their indices, into a short list;
+//   finish:  the few listed keys that share level 2's boundary bin are ranked
+//            against each other inside each wavefront (key descending, then
+//            index ascending): the k-th is tau and its index + 1 the cutoff;
+//   else:    (a long list, many equal keys) level 3 on bits 9..0, and where
+//            some keys equal to tau stay out, a block prefix count of them in
+//            index order.
+// A boundary bin that is taken whole ends the search early: tau is then one
+// below the bin's smallest key and the cutoff 0.  Two barriers in the usual
+// case, besides the one after the caller clears the histograms.
+// ---------------------------------------------------------------------------
+constexpr int kS31Cap = 256;   // listed keys of level 1's boundary bin
+
+template <int NQ, int NW>
+struct Sel31Lds {
+    uint32_t h1[2048];
+    uint32_t h2[1024];
+    uint32_t h3[1024];
+    uint32_t nc;               // listed keys
+    uint32_t cut;              // the tie search's result
+    uint32_t pad[2];
+    uint32_t ckey[kS31Cap], cidx[kS31Cap];
+    uint32_t wkey[NW][64], widx[NW][64];   // each wavefront's finishing candidates
+    uint32_t tie[NQ][NW];
+};
+
+// Clear what select_desc31 expects zeroed (h1 .. nc); a barrier must follow.
+template <int NT, int NQ>
+__device__ __forceinline__ void sel31_clear(Sel31Lds<NQ, NT / 64>& L, int tid) {
+    constexpr int N4 = (2048 + 1024 + 1024 + 4) / 4;
+    uint4* p = reinterpret_cast<uint4*>(&L.h1[0]);
+    for (int i = tid; i < N4; i += NT) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Descending search of a histogram of 256 NC bins.  False (uniform) when
+// fewer than kr keys are counted; else the bin that holds the kr-th largest
+// counted key, the rank of that key inside its bin (1-based) and the bin's
+// count.  Every read is a 16-byte load with the lanes on consecutive 16-byte
+// blocks (a lane owning a long run of bins would put all lanes of a load on
+// the same banks): the chunk totals first, then the chunk that holds the
+// key, where lane l owns bins 255 - 4 l - i (i = 0 .. 3).
+template <int NC>
+__device__ __forceinline__ bool desc_bin(const uint32_t* h, uint32_t kr, int lane, uint32_t& digit,
+                                         uint32_t& rank, uint32_t& cnt, uint32_t& total) {
+    uint32_t t[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&h[256 * c + 4 * lane]);
+        t[c] = (uint32_t)__builtin_amdgcn_readlane((int)sel::wave_incl_scan_dpp(v.x + v.y + v.z + v.w), 63);
+    }
+    total = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) total += t[c];
+    if (kr > total) return false;
+    int cs = 0;
+    uint32_t above = 0;
+#pragma unroll
+    for (int c = NC - 1; c >= 0; --c) {   // uniform
+        if (kr <= above + t[c]) { cs = c; break; }
+        above += t[c];
+    }
+    const uint32_t kc = kr - above;
+    const uint4 v = *reinterpret_cast<const uint4*>(&h[256 * cs + 252 - 4 * lane]);
+    const uint32_t c4[4] = {v.w, v.z, v.y, v.x};   // descending bins
+    const uint32_t lsum = c4[0] + c4[1] + c4[2] + c4[3];
+    const uint32_t incl = sel::wave_incl_scan_dpp(lsum);
+    const uint32_t excl = incl - lsum;
+    const int src = (int)__builtin_ctzll(__ballot(excl < kc && kc <= incl));
+    uint32_t e = excl, dg = 0, rk = 0, cn = 0;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (!found && e < kc && kc <= e + c4[i]) {
+            found = true;
+            dg = (uint32_t)(256 * cs + 255 - 4 * lane - i);
+            rk = kc - e;
+            cn = c4[i];
+        }
+        e += c4[i];
+    }
+    digit = (uint32_t)__builtin_amdgcn_readlane((int)dg, src);
+    rank = (uint32_t)__builtin_amdgcn_readlane((int)rk, src);
+    cnt = (uint32_t)__builtin_amdgcn_readlane((int)cn, src);
+    return true;
+}
+
+// Thread t holds key[4 q + e] = the key of entry q * 4 NT + 4 t + e, and 0
+// past the row end of n entries (zero keys are never counted, and as ties
+// they come after every entry of the row).  L cleared by sel31_clear, then a
+// barrier.
+// Returns, uniform over the workgroup: entry j is among the top k iff key_j >
+// tau, or key_j == tau and j < cutoff.
+template <int NT, int NQ>
+__device__ __forceinline__ void select_desc31(const uint32_t (&key)[4 * NQ], int64_t n, int64_t k,
+                                              Sel31Lds<NQ, NT / 64>& L, int tid, uint32_t& tau_out,
+                                              uint32_t& cut_out) {
+    constexpr int NW = NT / 64, KPT = 4 * NQ;
+    constexpr uint32_t kAll = 0x7FFFFFFFu;
+    const int lane = tid & 63, wave = tid / 64;
+    if (k <= 0) { tau_out = kAll; cut_out = 0; return; }   // nothing (keys are < 2^31 - 1 or NaN)
+    if (k >= n) { tau_out = 0; cut_out = kAll; return; }   // everything
+
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+        if (key[i] != 0u) atomicAdd(&L.h1[key[i] >> 20], 1u);
+    __syncthreads();
+
+    uint32_t tau = 0, need = 0, eqn = 0;
+    uint32_t b1, r1, c1, tot;
+    if (!desc_bin<8>(L.h1, (uint32_t)k, lane, b1, r1, c1, tot)) {
+        // Fewer than k nonzero keys: all of them, and the first zeros.
+        tau = 0; need = (uint32_t)k - tot; eqn = (uint32_t)n - tot;
+    } else if (r1 == c1) {
+        // The boundary bin is taken whole: every key >= its lowest (a key
+        // counted in bin 0 is nonzero).
+        tau_out = b1 == 0 ? 0u : (b1 << 20) - 1u; cut_out = 0; return;
+    } else {
+        // Level 2, and the list of level 1's boundary keys (each listed with
+        // one LDS atomic: they are few).  A zero key matches no boundary bin:
+        // key >= lo1 (lo1 = 1 only for bin 0) excludes it, a test the
+        // compiler cannot merge with level 1's, whose lane masks would
+        // otherwise stay alive, one per key, across the search.
+        const bool list = c1 <= (uint32_t)kS31Cap;   // uniform
+        const uint32_t lo1 = b1 == 0 ? 1u : 0u;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            if ((key[i] >> 20) == b1 && key[i] >= lo1) {
+                atomicAdd(&L.h2[(key[i] >> 10) & 1023u], 1u);
+                if (list) {
+                    const uint32_t pos = atomicAdd(&L.nc, 1u);
+                    L.ckey[pos] = key[i];
+                    L.cidx[pos] = (uint32_t)((i / 4) * 4 * NT + 4 * tid + (i % 4));
+                }
+            }
+        }
+        __syncthreads();
+        uint32_t b2, r2, c2;
+        desc_bin<4>(L.h2, r1, lane, b2, r2, c2, tot);   // r1 <= c1 = the level's total
+        const uint32_t pre2 = (b1 << 10) | b2;            // the top 21 key bits
+        if (r2 == c2) {
+            const uint32_t lo = pre2 << 10;
+            tau_out = lo == 0 ? 0u : lo - 1u; cut_out = 0; return;
+        }
+        if (list && c2 <= 64u) {
+            // The c2 keys of the boundary bin, gathered from the list into
+            // this wavefront's slots (lane i takes the i-th), then ranked.
+            uint32_t base = 0;
+            for (uint32_t ch = 0; ch < c1; ch += 64) {   // uniform
+                const uint32_t e = ch + (uint32_t)lane;
+                const uint32_t kv = e < c1 ? L.ckey[e] : sel::kInvalid;
+                const bool m = e < c1 && (kv >> 10) == pre2;
+                const uint64_t bm = __ballot(m);
+                if (m) {
+                    const uint32_t slot = base + sel::popc_below(bm);
+                    L.wkey[wave][slot] = kv;
+                    L.widx[wave][slot] = L.cidx[e];
+                }
+                base += (uint32_t)__popcll(bm);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const bool have = lane < (int)c2;
+            const uint32_t ck = have ? L.wkey[wave][lane] : 0u;
+            const uint32_t cj = have ? L.widx[wave][lane] : 0u;
+            uint32_t rank = 0;
+            for (uint32_t m = 0; m < c2; ++m) {   // uniform trip count
+                const uint32_t km = (uint32_t)__builtin_amdgcn_readlane((int)ck, (int)m);
+                const uint32_t jm = (uint32_t)__builtin_amdgcn_readlane((int)cj, (int)m);
+                rank += (km > ck || (km == ck && jm < cj)) ? 1u : 0u;
+            }
+            const int src = (int)__builtin_ctzll(__ballot(have && rank == r2 - 1u));
+            tau_out = (uint32_t)__builtin_amdgcn_readlane((int)ck, src);
+            cut_out = (uint32_t)__builtin_amdgcn_readlane((int)cj, src) + 1u;
+            return;
+        }
+        // Level 3: the low ten bits.
+        const uint32_t lo2 = pre2 == 0 ? 1u : 0u;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+            if ((key[i] >> 10) == pre2 && key[i] >= lo2) atomicAdd(&L.h3[key[i] & 1023u], 1u);
+        __syncthreads();
+        uint32_t b3;
+        desc_bin<4>(L.h3, r2, lane, b3, need, eqn, tot);
+        tau = (pre2 << 10) | b3;
+        if (need == eqn) { tau_out = tau; cut_out = kAll; return; }
+    }
+
+    // Some keys equal to tau stay out: the need-th of them in index order
+    // (runs in (q, thread, e) order) ends the selection.  The ties are kept
+    // as bits, 4 per run, so the keys are tested once.
+    uint32_t tb[NQ], incl[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        tb[q] = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tb[q] |= (key[4 * q + e] == tau ? 1u : 0u) << e;
+        incl[q] = sel::wave_incl_scan_dpp((uint32_t)__popc(tb[q]));
+        if (lane == 63) L.tie[q][wave] = incl[q];
+    }
+    __syncthreads();
+    uint32_t base = 0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        uint32_t before = 0, qt = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const uint32_t t = L.tie[q][w];
+            before += w < wave ? t : 0u;
+            qt += t;
+        }
+        const uint32_t c = (uint32_t)__popc(tb[q]);
+        const uint32_t r = base + before + incl[q] - c;   // ties before this run
+        if (r < need && need <= r + c) {
+            uint32_t bits = tb[q];
+            for (uint32_t s2 = r + 1; s2 < need; ++s2) bits &= bits - 1u;   // drop the lower ties
+            L.cut = (uint32_t)(q * 4 * NT + 4 * tid + __builtin_ctz(bits)) + 1u;
+        }
+        base += qt;
+    }
+    __syncthreads();
+    tau_out = tau;
+    cut_out = L.cut;
 }
 
 __device__ __forceinline__ bool selected(uint32_t key, uint32_t j, uint32_t tau, uint32_t cutoff) {

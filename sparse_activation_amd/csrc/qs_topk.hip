@@ -20,6 +20,7 @@
 // an epsilon-guarded denominator) and then selects on |q|.
 #include "qs_internal.h"
 #include "qs_select.h"
+#include "qs_rowsel.h"
 
 namespace qs {
 namespace {
@@ -970,6 +971,50 @@ __global__ void zero_i32_kernel(int32_t* p, int64_t n) {
 }  // namespace
 
 bool topk_xform_supported(int64_t d) { return d % 4 == 0 && d <= 16384; }
+
+// ---------------------------------------------------------------------------
+// Top-k descriptor of a row of fp32 values by magnitude (the FFN
+// intermediate; Turbo Sparse summary, Eq. 3-4: the top-k% of h by |h| before
+// W_down), when neither the index list nor the sparsified row is wanted: the
+// next launch applies (tau, cutoff) itself.  One workgroup of 1024 threads per
+// row, NQ runs of 4 entries per thread; rowsel::select_desc31 does the rest.
+// ---------------------------------------------------------------------------
+constexpr int kDescNT = 1024;
+
+template <int NQ>
+__global__ __launch_bounds__(kDescNT) void desc31_kernel(const float* x, int64_t rows, int64_t d,
+                                                         int64_t k, uint32_t* desc) {
+    __shared__ rowsel::Sel31Lds<NQ, kDescNT / 64> L;
+    const int r = blockIdx.x, tid = threadIdx.x;
+    rowsel::sel31_clear<kDescNT, NQ>(L, tid);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(x + (int64_t)r * d), (short)0, (int)(d * 4), 0x00020000);
+    uint32_t key[4 * NQ];   // past the row end (d % 4 == 0) the loads read 0
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, (uint32_t)((q * 4 * kDescNT + 4 * tid) * 4), 0, 0);
+        key[4 * q] = v.x & 0x7FFFFFFFu; key[4 * q + 1] = v.y & 0x7FFFFFFFu;
+        key[4 * q + 2] = v.z & 0x7FFFFFFFu; key[4 * q + 3] = v.w & 0x7FFFFFFFu;
+    }
+    __syncthreads();
+    uint32_t tau, cut;
+    rowsel::select_desc31<kDescNT, NQ>(key, d, k, L, tid, tau, cut);
+    if (tid == 0) { desc[r] = tau; desc[rows + r] = cut; }
+}
+
+hipError_t launch_desc31(const float* x, int64_t rows, int64_t d, int64_t k, uint32_t* desc,
+                         hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    if (!desc31_supported(d)) return hipErrorInvalidValue;
+    const int nq = (int)((d + 4 * kDescNT - 1) / (4 * kDescNT));
+    const dim3 grid((unsigned)rows), block(kDescNT);
+    if (nq <= 1) desc31_kernel<1><<<grid, block, 0, stream>>>(x, rows, d, k, desc);
+    else if (nq <= 2) desc31_kernel<2><<<grid, block, 0, stream>>>(x, rows, d, k, desc);
+    else if (nq <= 3) desc31_kernel<3><<<grid, block, 0, stream>>>(x, rows, d, k, desc);
+    else desc31_kernel<4><<<grid, block, 0, stream>>>(x, rows, d, k, desc);
+    return hipGetLastError();
+}
 
 hipError_t launch_topk(int key_kind, int xs_kind, int64_t rows, const TopkArgs& a,
                        hipStream_t stream) {
