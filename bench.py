@@ -4,9 +4,10 @@
 Default workload (the headline line): the Llama-7B-shaped squared-ReLU sparse
 FFN at decode (d = 4096, ffn = 11008, bf16 weights, top-K 40% of the input
 features, then top-K 40% of relu(u)^2 before the down projection), batch 1.
-One step is one call of qs_sparse_ffn over one batch: top-K of x, gathered up
-projection with the squared-ReLU epilogue, top-K of the intermediate,
-gathered down projection.
+One step is one call of qs_sparse_ffn over one batch: the top-K of x and the
+up projection over the selected rows of W_up^T with the squared-ReLU
+epilogue (one launch at one token), the top-K descriptor of the
+intermediate, and the down projection over the rows of W_down^T it selects.
 
 Other workloads (--workload): c1 (fp32 1024x1024 linear, 8 tokens), c2g (the
 same Llama-7B FFN with a gate: gated squared ReLU), c3
@@ -22,11 +23,14 @@ Measurement:
     large, and eight activation batches rotate so the selections change;
   * the K timed steps are captured in one HIP graph (no host launch gaps)
     and timed with HIP events on the stream the library launches on;
-  * roofline (c2): the gather GEMV, the dominant kernel, is timed alone
-    through qs_gather_linear_acc (the accumulate form that the FFN step
-    runs with fp32 outputs), launch by launch in a graph, on the same
-    inputs; achieved = algorithmic bytes (selected weight rows of the
-    batch's union, each read once, plus activations and outputs) / time;
+  * roofline (c2): the step's dominant kernel is timed alone, launch by
+    launch in a graph, on the same inputs: at one token the up projection's
+    column kernel (through qs_sparse_linear, which runs that kernel alone
+    for one bf16 token), at more tokens the down gather (through
+    qs_gather_linear_acc, the accumulate form the step runs with fp32
+    outputs); the other kernel is reported beside it; achieved =
+    algorithmic bytes (selected weight rows of the batch's union, each read
+    once, plus activations and outputs) / time;
   * traffic: HBM bytes per launch from committed rocprofv3 PMC summaries
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), used
     only while the kernel source is unchanged since they were taken;
@@ -229,33 +233,59 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     step_bytes = sum(bytes_up(i % N_XROT) + bytes_dn(i % N_XROT)
                      for i in range(args.steps)) / args.steps
 
-    # roofline leg: the gather GEMV alone, launch by launch, in the form the
-    # step runs (the accumulate form, unless fixed-order sums were asked for)
+    # roofline leg, launch by launch, each kernel in the form the step runs
+    # it.  One token: the step's longest kernel is the up projection's column
+    # kernel (selection of x inside every workgroup, whole 64-column tiles of
+    # u), which qs_sparse_linear runs alone for one bf16 token (the same
+    # kernel, grid and bytes; only the epilogue stores u instead of
+    # relu(u)^2).  More tokens: the down gather (the step's gather over the
+    # rows its descriptor selects; here from the sparsified h, the same rows
+    # in the same order), in the accumulate form unless fixed-order sums
+    # were asked for.
     L = args.roofline_launches
-    yup = torch.zeros((B, ffn), dtype=torch.float32, device=dev)
     ydn = torch.zeros((B, d), dtype=torch.float32, device=dev)
-    ws_up = qs.gather_workspace(B, d, ffn, dev)
     ws_dn = qs.gather_workspace(B, ffn, d, dev)
     gather = qs.qs_gather_linear if args.deterministic else qs.qs_gather_linear_acc
 
-    def gemv_pair(i):
-        gather(u1[i % N_XROT], wups[i % n_copies], y=yup, ws=ws_up)
+    def down_launch(i):
         gather(u2[i % N_XROT], wdns[i % n_copies], y=ydn, ws=ws_dn)
 
-    # (median over graph replays of L launch pairs; each replay's time / 2L is
-    # the average launch duration that the kernel trace reports)
-    _, per = time_graph(torch, stream, gemv_pair, L, 4, replays=args.replays)
-    ms_gemv = sorted(per)[len(per) // 2]
-    gemv_bytes = sum(bytes_up(i % N_XROT) + bytes_dn(i % N_XROT) for i in range(L))
-    us_launch = ms_gemv * 1e3 / (2 * L)
-    achieved = gemv_bytes / (ms_gemv * 1e-3) / 1e9
-    log(f"gather GEMV: {us_launch:.2f} us per launch (avg of up and down), {achieved:.0f} GB/s")
-    traffic = committed_traffic("qs_gemv.hip", "gather_gemv_llama7b_relu2_b1_traffic.md")
+    # (median over graph replays of L launches; each replay's time / L is the
+    # average launch duration that the kernel trace reports)
+    _, per = time_graph(torch, stream, down_launch, L, 4, replays=args.replays)
+    us_dn = sorted(per)[len(per) // 2] * 1e3 / L
+    dn_bytes = sum(bytes_dn(i % N_XROT) for i in range(L)) / L
+    ach_dn = dn_bytes / (us_dn * 1e-6) / 1e9
+    log(f"down gather: {us_dn:.2f} us per launch, {ach_dn:.0f} GB/s")
+    kernels = {"gather_gemv_kernel (down)": {"us_per_launch": round(us_dn, 3),
+                                             "algorithmic_bytes_per_launch": round(dn_bytes),
+                                             "achieved_gbps": round(ach_dn, 1)}}
+    if B == 1:
+        yup = torch.empty((B, ffn), dtype=torch.float32, device=dev)
+        ws_lin = torch.empty(qs.qs_workspace_bytes(qs.OP_SPARSE_LINEAR, B, d, ffn),
+                             dtype=torch.uint8, device=dev)
 
+        def up_launch(i):
+            qs.qs_sparse_linear(xs[i % N_XROT], k_in, wups[i % n_copies], y=yup, ws=ws_lin)
+
+        _, per = time_graph(torch, stream, up_launch, L, 4, replays=args.replays)
+        us_up = sorted(per)[len(per) // 2] * 1e3 / L
+        up_bytes = sum(bytes_up(i % N_XROT) for i in range(L)) / L
+        ach_up = up_bytes / (us_up * 1e-6) / 1e9
+        log(f"up column kernel: {us_up:.2f} us per launch, {ach_up:.0f} GB/s")
+        kernels["up_cols_kernel (up)"] = {"us_per_launch": round(us_up, 3),
+                                          "algorithmic_bytes_per_launch": round(up_bytes),
+                                          "achieved_gbps": round(ach_up, 1)}
+        dom, us_launch, bytes_launch, achieved = "up_cols_kernel", us_up, up_bytes, ach_up
+        traffic = committed_traffic("qs_gemv.hip", "up_cols_llama7b_relu2_b1_traffic.md")
+    else:
+        dom = "gather_gemv_kernel" if B < 8 else "bfrag_kernel + gather_bmfma_kernel"
+        us_launch, bytes_launch, achieved = us_dn, dn_bytes, ach_dn
+        traffic = None
     # ceiling reference: a plain streaming read of the same bytes per launch,
     # rotating over chunks of the weight copies (> 256 MB, so not from the MALL)
     flat = [t.view(-1).view(torch.uint8) for t in wups + wdns]
-    nb = min(int(gemv_bytes / (2 * L)), min(f.numel() for f in flat)) // 16 * 16
+    nb = min(int(bytes_launch), min(f.numel() for f in flat)) // 16 * 16
     chunks = [f[o:o + nb] for f in flat for o in range(0, f.numel() - nb + 1, nb)]
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     stream_read = probe_library()
@@ -271,7 +301,7 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     ms_probe = sorted(per)[len(per) // 2]
     probe_gbps = nb * L / (ms_probe * 1e-3) / 1e9
     log(f"stream-read probe, {nb / 1e6:.1f} MB per launch over {len(chunks)} chunks: "
-        f"{probe_gbps:.0f} GB/s; gather GEMV at {achieved / probe_gbps:.1%} of it")
+        f"{probe_gbps:.0f} GB/s; {dom} at {achieved / probe_gbps:.1%} of it")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -286,12 +316,12 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
         "union_rows_up": un1, "union_rows_down": un2,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic if B == 1 else None,
-                     "kernel": "gather_gemv_kernel" if B < 8 else "bfrag_kernel + gather_bmfma_kernel",
-                     "algorithmic_bytes_per_launch": round(gemv_bytes / (2 * L)),
+                     "traffic": traffic, "kernel": dom,
+                     "algorithmic_bytes_per_launch": round(bytes_launch),
                      "us_per_launch": round(us_launch, 3),
                      "stream_read_probe_gbps": round(probe_gbps, 1),
-                     "frac_of_stream_read_probe": round(achieved / probe_gbps, 4)},
+                     "frac_of_stream_read_probe": round(achieved / probe_gbps, 4),
+                     "kernels": kernels},
         "timing": timing, "cpu_baseline": cpu,
     }
 
@@ -336,7 +366,7 @@ def cpu_baseline_c2(c, seconds):
         used = max([i.get("num_threads", 1) for i in threadpool_info()
                     if i.get("user_api") == "blas"] or [1])
         times, n, t0 = [], 0, time.perf_counter()
-        while n < 64:
+        while n < 4096:   # bounded by --cpu-seconds of oracle time
             x = datagen.c2_relu2_ffn(1, rotation=n % N_XROT, with_weights=False)["X"]
             t1 = time.perf_counter()
             oracle.ffn_relu2(x, c["K_in"], w_up, c["K_mid"], w_dn)

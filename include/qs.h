@@ -154,7 +154,10 @@ qs_status qs_topk_mask(const void* x, qs_dtype xt, int64_t rows, int64_t d, int6
  *   w       device weights, dtype wt_t (QS_F32 or QS_BF16), layout w_layout:
  *           QS_LAYOUT_WT  W^T [d_in, n_out]: the gather path, which reads only
  *                         the rows of W^T selected by some token of the batch
- *                         (any rows; meant for decode batches);
+ *                         (any rows; meant for decode batches).  One bf16
+ *                         token with bf16 weights, d_in <= 8192 and n_out <=
+ *                         16384 (both multiples of 8) takes one launch with
+ *                         fixed-order sums, whatever qs_set_deterministic says;
  *           QS_LAYOUT_W   W [n_out, d_in]: the masked dense MFMA path for large
  *                         token batches; needs xt == wt_t == QS_BF16.
  *   y       device [rows, n_out], dtype yt (QS_F32 or QS_BF16, bf16 rounded

@@ -357,6 +357,19 @@ qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_i
         return ok();
     }
     const int wb = wt_t == QS_BF16;
+    if (rows == 1 && xt == QS_BF16 && wb && qs::up_cols_supported(rows, d_in, n_out)) {
+        // One bf16 token: a single launch whose workgroups each select the
+        // top-k of x and compute whole 64-column tiles of y over the
+        // selected rows (fixed-order sums, no K split).
+        qs::UpColsArgs u{};
+        u.x = (const uint16_t*)x; u.rows = rows; u.d = d_in; u.ffn = n_out; u.k = k;
+        u.w = (const uint16_t*)w; u.linear = 1;
+        if (yt == QS_BF16) u.hb = (uint16_t*)y;
+        else u.h = (float*)y;
+        e = qs::launch_up_cols(u, st);
+        if (e != hipSuccess) return hip_fail(e, fn);
+        return ok();
+    }
     qs::GemvPlan plan = qs::plan_gemv(rows, d_in, n_out, wb);
     // fp32 y: the selection launch clears y and the gather's workgroups add
     // into it (no split handoff), unless fixed-order sums are asked for.

@@ -643,10 +643,11 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
         const bool valid = t < ntok && cg < ffn;
         float hv = 0.0f;
         if constexpr (DUAL) hv = relu2_glu(sum[1], sum[0]);
-        else hv = sum[0] > 0.0f ? __fmul_rn(sum[0], sum[0]) : 0.0f;
+        else hv = a.linear ? sum[0] : sum[0] > 0.0f ? __fmul_rn(sum[0], sum[0]) : 0.0f;
         if (valid) {
             const int64_t i = (tok0 + t) * ffn + cg;
-            a.h[i] = hv;
+            if (a.hb != nullptr) a.hb[i] = f32_to_bf16_rne(hv);
+            else a.h[i] = hv;
             if (a.h2 != nullptr) a.h2[i] = hv;
         }
     }
@@ -2043,7 +2044,9 @@ bool up_cols_supported(int64_t rows, int64_t d, int64_t ffn) {
 
 hipError_t launch_up_cols(const UpColsArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
-    if (!up_cols_supported(a.rows, a.d, a.ffn)) return hipErrorInvalidValue;
+    if (!up_cols_supported(a.rows, a.d, a.ffn) || (a.h == nullptr) == (a.hb == nullptr) ||
+        (a.linear && a.w2 != nullptr))
+        return hipErrorInvalidValue;
     const int bt = a.rows == 1 ? 1 : a.rows == 2 ? 2 : 4;
     if (a.zero != nullptr && a.n_zero % 4 != 0) return hipErrorInvalidValue;
     const int e = a.d <= 8 * kUcNT ? 8 : 16;

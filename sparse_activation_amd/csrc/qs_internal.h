@@ -168,8 +168,10 @@ struct UpColsArgs {
     int n_zero_i;
     const uint16_t* w;       // bf16 W_up^T [d, ffn]
     const uint16_t* w2;      // bf16 W_gate^T [d, ffn] (gated form) or null
-    float* h;                // fp32 [rows, ffn]
+    float* h;                // fp32 [rows, ffn], or null with hb:
+    uint16_t* hb;            //   bf16 [rows, ffn] (nearest-even from the fp32 value)
     float* h2;               // or null: a second copy of h
+    int linear;              // 1: h = u, the plain sparse linear (w2 null)
 };
 constexpr int64_t kUpColsMaxD = 16 * 512;
 constexpr int64_t kUpColsMaxFfn = 32 * 512;

@@ -51,6 +51,28 @@ def test_linear_random(gpu_lib, wtype, rows, d, n):
         assert_within(y, y_ref, t, tol, f"linear {wtype} k={k}")
 
 
+@pytest.mark.parametrize("d,n", [(8, 8), (1000, 1040), (8192, 520), (256, 16384), (4096, 11008)])
+def test_linear_one_bf16_token(gpu_lib, d, n):
+    """One bf16 token, bf16 W^T: the single-launch column kernel (selection
+    inside every workgroup, fixed-order sums), fp32 and bf16 y; two calls in
+    the default (atomic) reduction mode agree bitwise."""
+    import torch
+    rng = np.random.default_rng(d + 3 * n)
+    x = datagen.bf16_round(datagen.student_t(rng, (1, d)))
+    w = datagen.bf16_round(datagen.normal(rng, (n, d), 0.02))
+    for k in sorted({0, 1, 7, (2 * d) // 5, d - 1, d}):
+        note(f"linear one bf16 token d={d} n={n} k={k}")
+        y = _run(gpu_lib, x, k, w, torch.bfloat16, torch.bfloat16, torch.float32)
+        y2 = _run(gpu_lib, x, k, w, torch.bfloat16, torch.bfloat16, torch.float32)
+        assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+        y_ref, t = _ref(x, k, w)
+        assert_within(y, y_ref, t, 4e-3, f"one token k={k}")
+        yb = _run(gpu_lib, x, k, w, torch.bfloat16, torch.bfloat16, torch.bfloat16)
+        # bf16 output: the fp32 result rounded to nearest-even
+        exp = torch.from_numpy(y).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(yb, exp), "bf16 y is not the rounded fp32 y"
+
+
 @pytest.mark.parametrize("wtype", ["f32", "bf16"])
 def test_linear_integer_valued_is_exact(gpu_lib, wtype):
     import torch
