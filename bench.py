@@ -6,8 +6,9 @@ FFN at decode (d = 4096, ffn = 11008, bf16 weights, top-K 40% of the input
 features, then top-K 40% of relu(u)^2 before the down projection), batch 1.
 One step is one call of qs_sparse_ffn over one batch: the top-K of x and the
 up projection over the selected rows of W_up^T with the squared-ReLU
-epilogue (one launch at one token), the top-K descriptor of the
-intermediate, and the down projection over the rows of W_down^T it selects.
+epilogue, then the top-K of the intermediate and the down projection over
+the rows of W_down^T it selects (at one token two launches, each selecting
+inside its workgroups).
 
 Other workloads (--workload): c1 (fp32 1024x1024 linear, 8 tokens), c2g (the
 same Llama-7B FFN with a gate: gated squared ReLU), c3
@@ -23,14 +24,15 @@ Measurement:
     large, and eight activation batches rotate so the selections change;
   * the K timed steps are captured in one HIP graph (no host launch gaps)
     and timed with HIP events on the stream the library launches on;
-  * roofline (c2): the step's dominant kernel is timed alone, launch by
-    launch in a graph, on the same inputs: at one token the up projection's
-    column kernel (through qs_sparse_linear, which runs that kernel alone
-    for one bf16 token), at more tokens the down gather (through
-    qs_gather_linear_acc, the accumulate form the step runs with fp32
-    outputs); the other kernel is reported beside it; achieved =
-    algorithmic bytes (selected weight rows of the batch's union, each read
-    once, plus activations and outputs) / time;
+  * roofline (c2): the step's weight-streaming kernels are timed alone,
+    launch by launch in a graph, on the same inputs, through entry points
+    that run exactly those kernels: at one token the up projection's column
+    kernel (qs_sparse_linear for one bf16 token) and the down gather that
+    selects h itself (qs_topk_gather_linear_acc), at more tokens the down
+    gather (qs_gather_linear_acc, the accumulate form the step runs with
+    fp32 outputs); the roofline is the longer (dominant) one, both are
+    reported; achieved = algorithmic bytes (selected weight rows of the
+    batch's union, each read once, plus activations and outputs) / time;
   * traffic: HBM bytes per launch from committed rocprofv3 PMC summaries
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), used
     only while the kernel source is unchanged since they were taken;
@@ -210,7 +212,7 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step, {B / (ms_step * 1e-3):.0f} tokens/s")
 
     # union sizes of the rotated batches (for the algorithmic bytes)
-    u1, u2 = [], []
+    u1, u2, hs = [], [], []
     for i in range(N_XROT):
         _, _, _, _, x1 = qs.qs_topk_mask(xs[i], k_in, want_mask=False, want_idx=False,
                                           want_desc=False, want_xs=True)
@@ -220,6 +222,7 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
                                           want_desc=False, want_xs=True)
         u1.append(x1)
         u2.append(x2)
+        hs.append(h)
     torch.cuda.synchronize()
     un1 = [int((a != 0).any(0).sum()) for a in u1]
     un2 = [int((a != 0).any(0).sum()) for a in u2]
@@ -233,33 +236,46 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     step_bytes = sum(bytes_up(i % N_XROT) + bytes_dn(i % N_XROT)
                      for i in range(args.steps)) / args.steps
 
-    # roofline leg, launch by launch, each kernel in the form the step runs
-    # it.  One token: the step's longest kernel is the up projection's column
-    # kernel (selection of x inside every workgroup, whole 64-column tiles of
-    # u), which qs_sparse_linear runs alone for one bf16 token (the same
-    # kernel, grid and bytes; only the epilogue stores u instead of
-    # relu(u)^2).  More tokens: the down gather (the step's gather over the
-    # rows its descriptor selects; here from the sparsified h, the same rows
-    # in the same order), in the accumulate form unless fixed-order sums
-    # were asked for.
+    # roofline leg, launch by launch, each of the step's two weight-streaming
+    # kernels in the form the step runs it, through an entry point that runs
+    # that kernel alone (the same kernel, grid and bytes):
+    #   * one token: the up projection's column kernel (qs_sparse_linear for
+    #     one bf16 token; only the epilogue stores u instead of relu(u)^2),
+    #     and the down gather that selects h itself
+    #     (qs_topk_gather_linear_acc on the step's h);
+    #   * more tokens: the down gather over the rows the descriptor selects
+    #     (qs_gather_linear_acc on the sparsified h: the same rows in the same
+    #     order), in the accumulate form unless fixed-order sums were asked for.
+    # The roofline is the longer of the two (the dominant kernel); both are
+    # reported.  Each figure is the median over graph replays of L launches,
+    # divided by L: the average launch duration the kernel trace reports.
     L = args.roofline_launches
     ydn = torch.zeros((B, d), dtype=torch.float32, device=dev)
-    ws_dn = qs.gather_workspace(B, ffn, d, dev)
-    gather = qs.qs_gather_linear if args.deterministic else qs.qs_gather_linear_acc
+    kernels = {}
 
-    def down_launch(i):
-        gather(u2[i % N_XROT], wdns[i % n_copies], y=ydn, ws=ws_dn)
+    def timed(name, fn, nbytes):
+        _, per = time_graph(torch, stream, fn, L, 4, replays=args.replays)
+        us = sorted(per)[len(per) // 2] * 1e3 / L
+        gbps = nbytes / (us * 1e-6) / 1e9
+        log(f"{name}: {us:.2f} us per launch, {gbps:.0f} GB/s")
+        kernels[name] = {"us_per_launch": round(us, 3), "algorithmic_bytes_per_launch": round(nbytes),
+                         "achieved_gbps": round(gbps, 1)}
+        return us, gbps
 
-    # (median over graph replays of L launches; each replay's time / L is the
-    # average launch duration that the kernel trace reports)
-    _, per = time_graph(torch, stream, down_launch, L, 4, replays=args.replays)
-    us_dn = sorted(per)[len(per) // 2] * 1e3 / L
     dn_bytes = sum(bytes_dn(i % N_XROT) for i in range(L)) / L
-    ach_dn = dn_bytes / (us_dn * 1e-6) / 1e9
-    log(f"down gather: {us_dn:.2f} us per launch, {ach_dn:.0f} GB/s")
-    kernels = {"gather_gemv_kernel (down)": {"us_per_launch": round(us_dn, 3),
-                                             "algorithmic_bytes_per_launch": round(dn_bytes),
-                                             "achieved_gbps": round(ach_dn, 1)}}
+    up_bytes = sum(bytes_up(i % N_XROT) for i in range(L)) / L
+    if B == 1 and not args.deterministic:
+        def down_launch(i):
+            qs.qs_topk_gather_linear_acc(hs[i % N_XROT], k_mid, wdns[i % n_copies], ydn)
+        dn_name = "gather_sel_kernel (down, selection of h inside)"
+    else:
+        ws_dn = qs.gather_workspace(B, ffn, d, dev)
+        gather = qs.qs_gather_linear if args.deterministic else qs.qs_gather_linear_acc
+
+        def down_launch(i):
+            gather(u2[i % N_XROT], wdns[i % n_copies], y=ydn, ws=ws_dn)
+        dn_name = "gather_gemv_kernel (down)"
+    cands = [(dn_name,) + timed(dn_name, down_launch, dn_bytes) + (dn_bytes,)]
     if B == 1:
         yup = torch.empty((B, ffn), dtype=torch.float32, device=dev)
         ws_lin = torch.empty(qs.qs_workspace_bytes(qs.OP_SPARSE_LINEAR, B, d, ffn),
@@ -268,20 +284,16 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
         def up_launch(i):
             qs.qs_sparse_linear(xs[i % N_XROT], k_in, wups[i % n_copies], y=yup, ws=ws_lin)
 
-        _, per = time_graph(torch, stream, up_launch, L, 4, replays=args.replays)
-        us_up = sorted(per)[len(per) // 2] * 1e3 / L
-        up_bytes = sum(bytes_up(i % N_XROT) for i in range(L)) / L
-        ach_up = up_bytes / (us_up * 1e-6) / 1e9
-        log(f"up column kernel: {us_up:.2f} us per launch, {ach_up:.0f} GB/s")
-        kernels["up_cols_kernel (up)"] = {"us_per_launch": round(us_up, 3),
-                                          "algorithmic_bytes_per_launch": round(up_bytes),
-                                          "achieved_gbps": round(ach_up, 1)}
-        dom, us_launch, bytes_launch, achieved = "up_cols_kernel", us_up, up_bytes, ach_up
+        up_name = "up_cols_kernel (up, selection of x inside)"
+        cands.append((up_name,) + timed(up_name, up_launch, up_bytes) + (up_bytes,))
+    dom, us_launch, achieved, bytes_launch = max(cands, key=lambda c: c[1])
+    traffic = None
+    if dom.startswith("up_cols"):
         traffic = committed_traffic("qs_gemv.hip", "up_cols_llama7b_relu2_b1_traffic.md")
-    else:
-        dom = "gather_gemv_kernel" if B < 8 else "bfrag_kernel + gather_bmfma_kernel"
-        us_launch, bytes_launch, achieved = us_dn, dn_bytes, ach_dn
-        traffic = None
+    elif dom.startswith("gather_sel"):
+        traffic = committed_traffic("qs_gemv.hip", "gather_sel_llama7b_relu2_b1_traffic.md")
+    dom = dom.split(" ")[0]
+
     # ceiling reference: a plain streaming read of the same bytes per launch,
     # rotating over chunks of the weight copies (> 256 MB, so not from the MALL)
     flat = [t.view(-1).view(torch.uint8) for t in wups + wdns]
@@ -650,7 +662,7 @@ def run_c2g(args, torch, np, qs, datagen, dev, stream):
 
     ms_step, timing = time_steps(args, torch, stream, step, args.steps, args.warmup)
     # measured unions: rows of W_gate^T and W_up^T selected by some token, rows of W_down^T
-    u1, u2 = [], []
+    u1, u2, hs = [], [], []
     for i in range(N_XROT):
         _, _, _, _, x1 = qs.qs_topk_mask(xs[i], k_in, want_mask=False, want_idx=False,
                                           want_desc=False, want_xs=True)

@@ -213,6 +213,31 @@ qs_status qs_gather_linear_acc(const float* xs, int64_t rows, int64_t d_in, cons
                                size_t ws_bytes, void* stream);
 
 /*
+ * qs_topk_gather_linear_acc -- Y += (X (.) M) . W^T into an fp32 Y, with M the
+ * per-row top-K mask of X by |x| (ties to the lower index)  [QS-TopK],
+ * [TS-Eq3-4]: the selection and the gather in one launch, with no selection
+ * output and no sparsified copy of X.  This is the down projection that
+ * qs_sparse_ffn runs for one token when neither h nor its index list is
+ * asked for.  Every workgroup (one per CU: a 64-column tile and a split of
+ * the rows of W^T) finds the top-K descriptor of its row of X itself, keeps
+ * the selected nonzero entries of its split and streams their rows of W^T;
+ * the workgroups add their sums into y with float atomics, so the rounding
+ * of each sum depends on their arrival order.  Meant for one or a few
+ * tokens: each row of X gathers its own rows of W^T.
+ *
+ *   x       device fp32 [rows, d_in] (not sparsified).
+ *   k       0 <= k <= d_in.
+ *   wt      device bf16 W^T [d_in, n_out].
+ *   y       device fp32 [rows, n_out], read and written.
+ *   Arithmetic: fp32 products and sums (the fp32 tolerance).
+ *   Limits: d_in % 4 == 0, d_in <= 16384, n_out % 8 == 0, rows <= 65535,
+ *   W^T smaller than 1 GiB; QS_ERR_UNSUPPORTED otherwise.  No workspace.
+ */
+qs_status qs_topk_gather_linear_acc(const float* x, int64_t rows, int64_t d_in, int64_t k,
+                                    const void* wt, qs_dtype wt_t, int64_t n_out, float* y,
+                                    void* stream);
+
+/*
  * qs_set_deterministic -- process-wide choice of the split-K summation (see
  * the conventions above): on != 0 gives fixed-order, bitwise reproducible
  * sums in every entry point; 0 (the default) lets fp32 outputs be summed with

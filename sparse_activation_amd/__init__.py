@@ -22,7 +22,8 @@ __all__ = [
     "OP_SPARSE_FFN_DRELU", "OP_GATHER_LINEAR", "OP_SPARSE_FFN_RELU2_GLU",
     "OP_SPARSE_LINEAR_BACKWARD", "qs_sparse_linear_backward", "OP_BLOCK_SPARSE_LINEAR",
     "qs_block_sparse_linear", "OP_SPARSE_MOE_FFN", "qs_sparse_moe_ffn",
-    "qs_gather_linear_acc", "qs_set_deterministic", "qs_sparse_ffn_static",
+    "qs_gather_linear_acc", "qs_topk_gather_linear_acc", "qs_set_deterministic",
+    "qs_sparse_ffn_static",
     "STATIC_SCRATCH_BYTES",
 ]
 
@@ -45,6 +46,7 @@ _SIGS = {
     "qs_topk_mask": [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P],
     "qs_gather_linear": [_P, _I64, _I64, _P, _INT, _I64, _P, _INT, _P, ctypes.c_size_t, _P],
     "qs_gather_linear_acc": [_P, _I64, _I64, _P, _INT, _I64, _P, _P, ctypes.c_size_t, _P],
+    "qs_topk_gather_linear_acc": [_P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P],
     "qs_set_deterministic": [_INT],
     "qs_sparse_linear": [_P, _INT, _I64, _I64, _I64, _P, _INT, _INT, _I64, _P, _INT, _P,
                          ctypes.c_size_t, _P],
@@ -246,6 +248,25 @@ def qs_gather_linear_acc(xs, wt, y, ws=None):
     ws_bytes = ws.numel() * ws.element_size()
     _check(load().qs_gather_linear_acc(_ptr(xs), rows, d_in, _ptr(wt), _dtype_code(wt), n_out,
                                        _ptr(y), _ptr(ws), ws_bytes, _stream(dev)))
+    return y
+
+
+def qs_topk_gather_linear_acc(x, k: int, wt, y):
+    """Y += (X (.) M) . W^T into the fp32 tensor `y`, M the per-row top-k mask
+    of the fp32 `x` by magnitude, selection and gather in one launch (bf16
+    W^T [d_in, n_out]; float atomics across the workgroups)."""
+    torch = _torch()
+    rows, d_in = x.shape
+    if x.dtype != torch.float32 or y.dtype != torch.float32:
+        raise TypeError("x and y must be float32")
+    if wt.shape[0] != d_in:
+        raise ValueError("wt must be [d_in, n_out]")
+    n_out = wt.shape[1]
+    if tuple(y.shape) != (rows, n_out):
+        raise ValueError("y must be [rows, n_out]")
+    dev = _dev(x, wt, y)
+    _check(load().qs_topk_gather_linear_acc(_ptr(x), rows, d_in, k, _ptr(wt), _dtype_code(wt),
+                                            n_out, _ptr(y), _stream(dev)))
     return y
 
 

@@ -449,6 +449,32 @@ qs_status qs_gather_linear_acc(const float* xs, int64_t rows, int64_t d_in, cons
                          ws, ws_bytes, stream);
 }
 
+qs_status qs_topk_gather_linear_acc(const float* x, int64_t rows, int64_t d_in, int64_t k,
+                                    const void* wt, qs_dtype wt_t, int64_t n_out, float* y,
+                                    void* stream) {
+    const char* fn = "qs_topk_gather_linear_acc";
+    if (rows < 0 || d_in <= 0 || n_out <= 0) return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
+    if (k < 0 || k > d_in) return fail(QS_ERR_INVALID_ARG, "%s: need 0 <= k <= d_in", fn);
+    if (wt_t != QS_BF16) return fail(QS_ERR_UNSUPPORTED, "%s: W^T must be bf16", fn);
+    if (rows > 65535 || !qs::gather_sel_supported(rows == 0 ? 1 : rows, d_in, n_out))
+        return fail(QS_ERR_UNSUPPORTED,
+                    "%s: needs d_in %% 4 == 0, d_in <= 16384, n_out %% 8 == 0, rows <= 65535", fn);
+    if (d_in * n_out * 2 >= qs::kMaxGatherWeightBytes)
+        return fail(QS_ERR_UNSUPPORTED, "%s: W^T must be smaller than 1 GiB", fn);
+    if (rows == 0) return ok();
+    if (!x || !wt || !y) return fail(QS_ERR_INVALID_ARG, "%s: x, wt and y must be non-NULL", fn);
+    if (!aligned16(x) || !aligned16(wt) || !aligned16(y))
+        return fail(QS_ERR_UNSUPPORTED, "%s: pointer not 16-byte aligned", fn);
+    qs::GemvArgs g{};
+    g.xs = x; g.rows = rows; g.d_in = d_in; g.n_out = n_out; g.w = wt; g.y = y;
+    g.epilogue = qs::EPI_STORE;
+    g.accumulate = 1;
+    g.sel_k = k;
+    hipError_t e = qs::launch_gather_sel(g, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+}
+
 int qs_set_deterministic(int on) {
     return g_deterministic.exchange(on ? 1 : 0, std::memory_order_relaxed);
 }
@@ -590,8 +616,28 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
             u.w = (const uint16_t*)w_up;
             u.w2 = act == QS_ACT_RELU2_GLU ? (const uint16_t*)w_gate : nullptr;
             u.h = hbuf;
+            // One token without the index list or count of h: the down
+            // gather's workgroups select h themselves (one launch less).
+            int fs_tiles = 0, fs_split = 0, fs_cand = 0;
+            if (rows == 1) qs::gather_sel_plan(ffn, d, &fs_tiles, &fs_split, &fs_cand);
+            const bool fused_sel = rows == 1 && k_mid >= 0 && !mid_idx && !mid_cnt &&
+                                   qs::gather_sel_supported(rows, ffn, d) &&
+                                   (size_t)fs_split * d <= wsp.partial_cap &&
+                                   (size_t)fs_tiles <= wsp.down_ctr_cap;
+            if (fused_sel && !acc && u.n_zero_i < fs_tiles) u.n_zero_i = fs_tiles;
             e = qs::launch_up_cols(u, st);
             if (e != hipSuccess) return hip_fail(e, fn);
+            if (fused_sel) {
+                qs::GemvArgs g{};
+                g.xs = hbuf; g.rows = rows; g.d_in = ffn; g.n_out = d; g.w = w_down_t;
+                g.partial = wsp.partial; g.counters = wsp.ctr_down; g.y = y; g.y_bf16 = yt == QS_BF16;
+                g.epilogue = qs::EPI_STORE;
+                g.accumulate = acc ? 1 : 0;
+                g.sel_k = k_mid;
+                e = qs::launch_gather_sel(g, st);
+                if (e != hipSuccess) return hip_fail(e, fn);
+                return ok();
+            }
             if (k_mid >= 0 && !mid_idx && !mid_cnt && qs::desc31_supported(ffn)) {
                 // Only the descriptor: the lean selection.
                 e = qs::launch_desc31(hbuf, rows, ffn, k_mid, wsp.desc, st);

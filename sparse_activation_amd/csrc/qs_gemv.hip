@@ -405,6 +405,187 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
 }
 
 // ---------------------------------------------------------------------------
+// Down projection of a one-token FFN with the selection of h inside the
+// gather (Turbo Sparse summary, Eq. 3-4: the top-k% of h by |h| before
+// W_down).  One workgroup of 1024 threads per CU (a 64-column tile of y and a
+// split of the candidate rows): each finds the top-k descriptor of the whole
+// row of h itself (rowsel::select_desc31, as the descriptor launch does),
+// keeps the entries of its split that the descriptor selects, and streams
+// their rows of W_down^T: eight lanes per 128-byte row segment, 128 row slots,
+// 8 rows per slot and stage in two ping-pong register stages.  The 128 slots
+// are summed in a fixed order (one DPP rotation, then 64 rows in LDS).
+// ---------------------------------------------------------------------------
+constexpr int kFsNT = 1024;
+constexpr int kFsSlots = kFsNT / kFLPR;     // 128 row slots
+constexpr int kFsU = 8;                     // rows per slot and stage
+constexpr int kFsBatch = kFsSlots * kFsU;   // 1024 rows per stage
+constexpr int kFsMaxCand = 4 * kFsNT;       // candidates per split
+constexpr int kFsCols = kFLPR * 8;          // 64 bf16 columns per tile
+
+template <int NQ>
+__global__ __launch_bounds__(kFsNT) void gather_sel_kernel(GemvArgs a, int cand, int nsplit) {
+    constexpr int NCH = kFsMaxCand / kFsNT;
+    constexpr int NW = kFsNT / 64;
+    // All LDS is dynamic, from offset 0 (a selection scratch placed behind
+    // static variables ran its search more than twice as slowly): the
+    // selection scratch, then (after its last read) the row list, then the
+    // reduction rows; the scan totals and the split flag sit after the list.
+    extern __shared__ __attribute__((aligned(256))) float smem[];
+    float* s_coef = smem;                                                         // [cand + 3 batch]
+    uint32_t* s_off = reinterpret_cast<uint32_t*>(smem + cand + 3 * kFsBatch);   // [cand + 3 batch]
+    constexpr int kSelWords = (int)(sizeof(rowsel::Sel31Lds<NQ, NW>) / 4);
+    const int tail = 2 * (cand + 3 * kFsBatch) > kSelWords ? 2 * (cand + 3 * kFsBatch) : kSelWords;
+    uint32_t* s_wsum = reinterpret_cast<uint32_t*>(smem + tail);                  // [NW]
+    int* s_last = reinterpret_cast<int*>(s_wsum + NW);
+
+    const int tile = blockIdx.x, split = blockIdx.y;
+    const int64_t row = blockIdx.z;   // (split partials: one row)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t d_in = a.d_in, n_out = a.n_out;
+    const int64_t j0 = (int64_t)split * cand;
+    const int64_t j1 = min(d_in, j0 + (int64_t)cand);
+    const uint32_t rowbytes = (uint32_t)(n_out * 2);
+
+    // The split's candidate coefficients (entry j0 + ch * 1024 + tid is chunk
+    // ch of thread tid) and the whole row's keys, 4 entries per run.
+    const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.xs + row * d_in), (short)0, (int)(d_in * 4), 0x00020000);
+    float c[NCH];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int64_t j = j0 + ch * kFsNT + tid;
+        c[ch] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            hr, j < j1 ? (uint32_t)(j * 4) : kOOB, 0, 0));
+    }
+    auto& L = *reinterpret_cast<rowsel::Sel31Lds<NQ, NW>*>(smem);
+    rowsel::sel31_clear<kFsNT, NQ>(L, tid);
+    uint32_t key[4 * NQ];   // past the row end (d_in % 4 == 0) the loads read 0
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+            hr, (uint32_t)((q * 4 * kFsNT + 4 * tid) * 4), 0, 0);
+        key[4 * q] = v.x & 0x7FFFFFFFu; key[4 * q + 1] = v.y & 0x7FFFFFFFu;
+        key[4 * q + 2] = v.z & 0x7FFFFFFFu; key[4 * q + 3] = v.w & 0x7FFFFFFFu;
+    }
+    // (an empty asm per key: the compiler would otherwise keep the loaded
+    // words as well, to recompute each key where it is used)
+#pragma unroll
+    for (int i = 0; i < 4 * NQ; ++i) asm volatile("" : "+v"(key[i]));
+    __syncthreads();
+    uint32_t tau, cut;
+    rowsel::select_desc31<kFsNT, NQ>(key, d_in, a.sel_k, L, tid, tau, cut);
+
+    // The selected nonzero candidates as a list (one block scan; the list
+    // overwrites the selection scratch after its barrier).
+    uint32_t selbits = 0;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        const uint32_t j = (uint32_t)(j0 + ch * kFsNT + tid);
+        if (!rowsel::selected(__float_as_uint(c[ch]) & 0x7FFFFFFFu, j, tau, cut)) c[ch] = 0.0f;
+        selbits |= (c[ch] != 0.0f ? 1u : 0u) << ch;
+    }
+    const uint32_t mycnt = (uint32_t)__popc(selbits);
+    const uint32_t incl = sel::wave_incl_scan_dpp(mycnt);
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, nact = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t cw = s_wsum[w];
+        before += w < wave ? cw : 0u;
+        nact += cw;
+    }
+    uint32_t pos = before + incl - mycnt;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        if ((selbits >> ch) & 1u) {
+            s_off[pos] = (uint32_t)(j0 + ch * kFsNT + tid) * rowbytes;
+            s_coef[pos] = c[ch];
+            ++pos;
+        }
+    }
+    const int nbatch = (int)((nact + kFsBatch - 1) / kFsBatch);
+    const int npad = ((nbatch + 1) / 2 * 2 + 1) * kFsBatch;
+    for (int i = (int)nact + tid; i < npad; i += kFsNT) { s_off[i] = kOOB; s_coef[i] = 0.0f; }
+    __syncthreads();
+
+    // Stream the selected rows' 128-byte segments, one stage ahead.
+    const int slot = tid / kFLPR;
+    const int64_t col = (int64_t)tile * kFsCols + (lane % kFLPR) * 8;
+    const uint32_t colb = col < n_out ? (uint32_t)(col * 2) : kOOB;
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, d_in * (int64_t)rowbytes);
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    u32x4 bufa[kFsU], bufb[kFsU];
+    auto load_stage = [&](u32x4* dst, int bi) {
+#pragma unroll
+        for (int u = 0; u < kFsU; ++u)
+            dst[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                rs, s_off[bi * kFsBatch + u * kFsSlots + slot] + colb, 0, 0);
+    };
+    auto fma_stage = [&](const u32x4* src, int bi) {
+#pragma unroll
+        for (int u = 0; u < kFsU; ++u) {
+            const float cf = s_coef[bi * kFsBatch + u * kFsSlots + slot];
+            float w[8];
+            unpack<1>(src[u], w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(cf, w[e], acc[e]);
+        }
+    };
+    load_stage(bufa, 0);
+    for (int bi = 0; bi < nbatch; bi += 2) {
+        load_stage(bufb, bi + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        fma_stage(bufa, bi);
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage(bufa, bi + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        fma_stage(bufb, bi + 1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Fixed-order sum of the 128 slots: slots 2r and 2r + 1 of a 16-lane row
+    // by one DPP rotation, then the 64 rows in LDS in row order.
+    __syncthreads();   // the list is dead: the reduction buffer overwrites it
+    float* s_red = smem;   // [64][kFsCols]
+    const int rrow = wave * 4 + (lane >> 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float v = acc[e];
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+        if ((lane & 15) < kFLPR) s_red[rrow * kFsCols + (lane & 15) * 8 + e] = v;
+    }
+    __syncthreads();
+    if (tid < kFsCols) {
+        float s = 0.0f;
+#pragma unroll 8
+        for (int r = 0; r < 4 * NW; ++r) s += s_red[r * kFsCols + tid];
+        const int64_t cg = (int64_t)tile * kFsCols + tid;
+        if (cg < n_out) {
+            if (a.accumulate) unsafeAtomicAdd(&reinterpret_cast<float*>(a.y)[row * n_out + cg], s);
+            else if (nsplit > 1) store_agent(&a.partial[(int64_t)split * n_out + cg], s);
+            else store_final(a, cg, s);
+        }
+    }
+    // The last split of this tile sums the partials in split order.
+    if (nsplit > 1 && !a.accumulate) {
+        if (last_split_arrived(&a.counters[tile], nsplit, s_last)) {
+            if (tid < kFsCols) {
+                const int64_t cg = (int64_t)tile * kFsCols + tid;
+                if (cg < n_out) {
+                    float s = 0.0f;
+                    for (int sp = 0; sp < nsplit; ++sp) s += load_agent(&a.partial[(int64_t)sp * n_out + cg]);
+                    store_final(a, cg, s);
+                }
+            }
+            if (tid == 0) store_agent(&a.counters[tile], 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Up projection of a small-batch squared-ReLU FFN without a K split (Q-Sparse
 // news article, section "Sparsification with the Top-K function": X (.) M
 // replaces X in the product, so only the rows of W_up^T that some token
@@ -429,7 +610,8 @@ constexpr int kUcSlots = kUcNT / kUcLPR;     // 64 row slots per workgroup
 constexpr int kUcCols = kUcLPR * 8;          // 64 bf16 columns per tile
 
 // Rows per lane and pipeline stage: one token streams 16 (a Llama-7B
-// selection in two stages), more tokens or the gated pair 8.
+// selection in two stages), more tokens or the gated pair 8.  (1024 threads
+// with 8 rows each streamed as fast but selected more slowly.)
 template <int BT, bool DUAL>
 constexpr int uc_unroll() { return BT == 1 && !DUAL ? 16 : 8; }
 
@@ -441,14 +623,28 @@ constexpr int64_t uc_list_cap(int64_t d, int u) {
     return ((nb + 1) / 2 * 2 + 1) * batch;
 }
 
+// Words of LDS before the scan totals: the largest of the row list, the
+// selection scratch and the reduction rows.
+template <int BT, bool DUAL>
+__host__ __device__ constexpr int64_t uc_lds_tail(int64_t d) {
+    const int64_t list = uc_list_cap(d, uc_unroll<BT, DUAL>()) * (1 + BT);
+    const int64_t selw = (int64_t)sizeof(rowsel::Sel15Lds<BT, kUcNT / 64>) / 4;
+    const int64_t red = (int64_t)(kUcNT / 16) * (DUAL ? 2 : 1) * BT * kUcCols;
+    const int64_t m = list > selw ? list : selw;
+    return m > red ? m : red;
+}
+
 template <int BT, int E, bool DUAL>
 __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
     constexpr int U = uc_unroll<BT, DUAL>();
     constexpr int BATCH = kUcSlots * U;
     constexpr int NM = DUAL ? 2 : 1;
     constexpr int NW = kUcNT / 64;
-    extern __shared__ __attribute__((aligned(16))) float smem[];
-    __shared__ uint32_t s_wsum[16];
+    // All LDS is dynamic, from offset 0 (tables behind static variables ran
+    // markedly slower): the selection scratch or the row list, later the
+    // reduction rows; the scan totals sit behind the largest of them.
+    extern __shared__ __attribute__((aligned(256))) float smem[];
+    uint32_t* s_wsum = reinterpret_cast<uint32_t*>(smem + uc_lds_tail<BT, DUAL>(a.d));   // [16]
 
     const int tile = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -2037,6 +2233,46 @@ hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipS
     return hipErrorInvalidValue;
 }
 
+bool gather_sel_supported(int64_t rows, int64_t d_in, int64_t n_out) {
+    return rows >= 1 && rows <= 65535 && desc31_supported(d_in) && n_out % 8 == 0 && n_out > 0;
+}
+
+void gather_sel_plan(int64_t d_in, int64_t n_out, int* n_tiles, int* nsplit, int* cand) {
+    const int64_t nt = ceil_div(n_out, kFsCols);
+    int64_t ns = ceil_div(256, nt);   // one workgroup per CU
+    const int64_t ns_min = ceil_div(d_in, kFsMaxCand);
+    if (ns < ns_min) ns = ns_min;
+    int64_t cd = ceil_div(ceil_div(d_in, ns), 64) * 64;
+    if (cd > kFsMaxCand) cd = kFsMaxCand;
+    *n_tiles = (int)nt;
+    *cand = (int)cd;
+    *nsplit = (int)ceil_div(d_in, cd);
+}
+
+hipError_t launch_gather_sel(const GemvArgs& a, hipStream_t stream) {
+    if (!gather_sel_supported(a.rows, a.d_in, a.n_out) || a.sel_desc != nullptr ||
+        a.epilogue != EPI_STORE || (a.accumulate && a.y_bf16) || (!a.accumulate && a.rows != 1))
+        return hipErrorInvalidValue;
+    int nt, ns, cand;
+    gather_sel_plan(a.d_in, a.n_out, &nt, &ns, &cand);
+    const int nq = (int)ceil_div(a.d_in, 4 * kFsNT);
+    // (the list covers the reduction rows; the scan totals and the flag sit
+    // behind the larger of the list and the selection scratch, as in the kernel)
+    static_assert((size_t)64 * kFsCols * 4 <= (size_t)2 * 3 * kFsBatch * 4, "reduction rows fit");
+    const dim3 grid((unsigned)nt, (unsigned)ns, (unsigned)a.rows), block(kFsNT);
+#define QS_FS_CASE(NQV)                                                                   \
+    if (nq <= NQV) {                                                                      \
+        const size_t sel = sizeof(rowsel::Sel31Lds<NQV, kFsNT / 64>) / 4;                 \
+        size_t tail = (size_t)2 * (cand + 3 * kFsBatch);                                  \
+        if (tail < sel) tail = sel;                                                       \
+        gather_sel_kernel<NQV><<<grid, block, (tail + kFsNT / 64 + 1) * 4, stream>>>(a, cand, ns); \
+        return hipGetLastError();                                                         \
+    }
+    QS_FS_CASE(1) QS_FS_CASE(2) QS_FS_CASE(3) QS_FS_CASE(4)
+#undef QS_FS_CASE
+    return hipErrorInvalidValue;
+}
+
 bool up_cols_supported(int64_t rows, int64_t d, int64_t ffn) {
     return rows >= 1 && rows <= 4 && d % 8 == 0 && d <= kUpColsMaxD && ffn % 8 == 0 &&
            ffn <= kUpColsMaxFfn;
@@ -2052,14 +2288,9 @@ hipError_t launch_up_cols(const UpColsArgs& a, hipStream_t stream) {
     const int e = a.d <= 8 * kUcNT ? 8 : 16;
     const dim3 grid((unsigned)ceil_div(a.ffn, kUcCols), (unsigned)ceil_div(a.rows, bt));
     const bool dual = a.w2 != nullptr;
-    const int u = bt == 1 && !dual ? 16 : 8;
-    size_t lds = (size_t)uc_list_cap(a.d, u) * (4 + 4 * bt);
-    const size_t lds_red = (size_t)32 * (dual ? 2 : 1) * bt * kUcCols * 4;
-    const size_t lds_sel = sizeof(rowsel::Sel15Lds<4, kUcNT / 64>) / 4 * bt;
-    if (lds < lds_red) lds = lds_red;
-    if (lds < lds_sel) lds = lds_sel;
 #define QS_UC_CASE(BTV, EV, DU)                                                          \
     if (bt == BTV && e == EV && dual == DU) {                                            \
+        const size_t lds = (size_t)(uc_lds_tail<BTV, DU>(a.d) + 16) * 4;                 \
         up_cols_kernel<BTV, EV, DU><<<grid, dim3(kUcNT), lds, stream>>>(a);              \
         return hipGetLastError();                                                        \
     }

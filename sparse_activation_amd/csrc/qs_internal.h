@@ -137,6 +137,7 @@ struct GemvArgs {
     // sel_desc[rows .. 2 rows) (the top-k descriptor of launch_topk), and
     // only they are gathered.
     const uint32_t* sel_desc;
+    int64_t sel_k;         // launch_gather_sel: the top-k of h that the workgroups find
 };
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 // Both projections of the gated squared ReLU in one gather (tiles of at most
@@ -315,6 +316,16 @@ hipError_t launch_moe_combine(const float* ypair, const float* pair_weight, int6
                               int top_k, int64_t d, void* y, int y_bf16, hipStream_t stream);
 
 // Nonzero compaction of h rows: idx[r, 0..cnt) ascending, cnt[r].
+// Gather that selects the top-a.sel_k of each row of a.xs (fp32, not
+// sparsified) by magnitude itself: one launch instead of a descriptor launch
+// and the gather (the one-token FFN's down projection).  bf16 W^T; the
+// accumulate form adds into fp32 y (any rows, one grid layer each), else
+// (one row) split partials with the last split finishing (a.partial: nsplit *
+// n_out floats, a.counters: n_tiles counters, zero on entry and exit).
+bool gather_sel_supported(int64_t rows, int64_t d_in, int64_t n_out);
+void gather_sel_plan(int64_t d_in, int64_t n_out, int* n_tiles, int* nsplit, int* cand);
+hipError_t launch_gather_sel(const GemvArgs& a, hipStream_t stream);
+
 // Top-k descriptor of each row of fp32 x [rows, d] by |x| (one workgroup per
 // row, rowsel::select_desc31): tau -> desc[r], cutoff -> desc[rows + r].
 // d % 4 == 0, d <= kDescMaxD.

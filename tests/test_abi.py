@@ -102,6 +102,23 @@ def test_gather_linear_acc_validation():
     assert "8 rows" in qs.qs_last_error()
 
 
+def test_topk_gather_linear_acc_validation():
+    """Selection-in-gather accumulate: bf16 W^T only, d_in % 4 == 0 and <= 16384,
+    n_out % 8 == 0, 0 <= k <= d_in, no workspace; rows == 0 is a no-op."""
+    lib = qs.load()
+    f = lib.qs_topk_gather_linear_acc
+    assert f(FAKE, 1, 11008, 4403, FAKE, qs.F32, 4096, FAKE, None) == 2     # fp32 W^T
+    assert f(FAKE, 1, 11006, 4403, FAKE, qs.BF16, 4096, FAKE, None) == 2    # d_in % 4
+    assert f(FAKE, 1, 16388, 4403, FAKE, qs.BF16, 4096, FAKE, None) == 2    # d_in too large
+    assert f(FAKE, 1, 11008, 4403, FAKE, qs.BF16, 4092, FAKE, None) == 2    # n_out % 8
+    assert f(FAKE, 1, 11008, 11009, FAKE, qs.BF16, 4096, FAKE, None) == 1   # k > d_in
+    assert f(FAKE, 1, 11008, -1, FAKE, qs.BF16, 4096, FAKE, None) == 1
+    assert f(None, 1, 11008, 4403, FAKE, qs.BF16, 4096, FAKE, None) == 1
+    assert f(MISALIGNED, 1, 11008, 4403, FAKE, qs.BF16, 4096, FAKE, None) == 2
+    assert f(FAKE, 65536, 11008, 4403, FAKE, qs.BF16, 4096, FAKE, None) == 2
+    assert f(None, 0, 11008, 4403, None, qs.BF16, 4096, None, None) == 0
+
+
 def test_set_deterministic_returns_previous_setting():
     lib = qs.load()
     prev = lib.qs_set_deterministic(1)

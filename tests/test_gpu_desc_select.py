@@ -5,15 +5,18 @@ descriptor (tau, cutoff), which the down gather applies to h.
 Q-Sparse's top-k on the intermediate: Turbo Sparse summary, Eq. 3-4 (the
 top-k% of h by |h| before W_down); ties go to the lower index.
 
-Each case runs the bare call twice against the call with every optional
-output on, whose selection of h comes from the selection launch that the FFN
-tests check against the oracle index by index:
+With one token the down gather's workgroups find the descriptor themselves
+(no descriptor launch).  Each case runs the bare call in both reduction
+modes beside the call with every optional output on, whose index list of h
+comes from the selection launch and is checked against the oracle's
+selection of the same h index by index, and:
 
-* fixed-order sums: y of the bare call is bitwise equal to y of the full
-  call (the same rows gathered in the same order give the same bits; a
-  different selection would not);
-* both forms: y is within the bf16 tolerance of the oracle's down projection
-  of the call's own h (h has no atomics, so it is the same in both calls).
+* y of the bare call is within the fp32 summation bound (1e-5 * T_y) of the
+  oracle's down projection of the call's own h (h has no atomics, so it is
+  the same in every call) over the oracle's selection: one intermediate
+  entry selected wrongly moves y by about T_y / k_mid, far more;
+* with several tokens (the same gather kernel in both calls), fixed-order
+  sums: y of the bare call is bitwise equal to y of the full call.
 
 The inputs steer the selection into each branch of its search:
 plain rows, rows whose boundary falls among many equal values (the long-list
@@ -31,6 +34,7 @@ from gpu_util import assert_within, note, reduction_mode, to_dev
 pytestmark = pytest.mark.gpu
 
 TOL_BF16 = 4e-3
+SUM_EPS = 1e-5    # the fp32 tolerance: bound of the gathers' fp32 summation
 
 
 def _weights(kind, rng, d, f):
@@ -77,13 +81,13 @@ def _check(qs, x, k_in, k_mid, wu, wd, what):
              f"ffn={wu.shape[0]} k_mid={k_mid}")
         with reduction_mode(qs, det):
             y_bare, y_full, h, idx = _run(qs, x, k_in, k_mid, wu, wd)
-        if det:
+        if det and x.shape[0] > 1:
             assert np.array_equal(y_bare.view(np.uint32), y_full.view(np.uint32)), \
                 f"{what}: bare call (descriptor only) differs from the full call"
         down = oracle.ffn_relu2_down_from(h, k_mid, wd)
         for r in range(x.shape[0]):
             assert np.array_equal(idx[r, :k_mid], down["idx2"][r]), f"{what}: index list row {r}"
-        assert_within(y_bare, down["y"], down["T_y"], TOL_BF16, f"{what} y")
+        assert_within(y_bare, down["y"], down["T_y"], SUM_EPS, f"{what} y")
         hvals = h
     return hvals
 
