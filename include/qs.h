@@ -98,18 +98,26 @@ typedef enum qs_status {
 typedef enum qs_dtype {
     QS_F32 = 0,
     QS_BF16 = 1,
-    QS_I8 = 2
+    QS_I8 = 2,
+    /* (not values: they make every int a valid value of the type, so that an
+       out-of-range argument is rejected as QS_ERR_UNSUPPORTED, not undefined) */
+    QS_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+    QS_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
 } qs_dtype;
 
 typedef enum qs_layout {
     QS_LAYOUT_WT = 0,   /* feature-major W^T [d_in, n_out], row j = weights of input feature j */
-    QS_LAYOUT_W = 1     /* neuron-major W [n_out, d_in] (nn.Linear layout) */
+    QS_LAYOUT_W = 1,    /* neuron-major W [n_out, d_in] (nn.Linear layout) */
+    QS_LAYOUT_RANGE_MIN_ = -0x7FFFFFFF - 1,   /* (range only, as for qs_dtype) */
+    QS_LAYOUT_RANGE_MAX_ = 0x7FFFFFFF
 } qs_layout;
 
 typedef enum qs_act {
     QS_ACT_RELU2 = 0,     /* h = relu(u)^2                       [QS-TopK]  */
     QS_ACT_DRELU = 1,     /* h = relu(x W_gate^T + b_g) * relu(x W_up^T + b_u)   [TS-Eq2] */
-    QS_ACT_RELU2_GLU = 2  /* h = relu(x W_gate^T)^2 * (x W_up^T)  [QS-TopK] */
+    QS_ACT_RELU2_GLU = 2, /* h = relu(x W_gate^T)^2 * (x W_up^T)  [QS-TopK] */
+    QS_ACT_RANGE_MIN_ = -0x7FFFFFFF - 1,      /* (range only, as for qs_dtype) */
+    QS_ACT_RANGE_MAX_ = 0x7FFFFFFF
 } qs_act;
 
 typedef enum qs_op {
@@ -122,7 +130,9 @@ typedef enum qs_op {
     QS_OP_SPARSE_FFN_RELU2_GLU = 6,
     QS_OP_SPARSE_LINEAR_BACKWARD = 7,
     QS_OP_BLOCK_SPARSE_LINEAR = 8,
-    QS_OP_SPARSE_MOE_FFN = 9     /* rows = tokens * top_k (the (token, expert) pairs) */
+    QS_OP_SPARSE_MOE_FFN = 9,    /* rows = tokens * top_k (the (token, expert) pairs) */
+    QS_OP_RANGE_MIN_ = -0x7FFFFFFF - 1,       /* (range only, as for qs_dtype) */
+    QS_OP_RANGE_MAX_ = 0x7FFFFFFF
 } qs_op;
 
 /*

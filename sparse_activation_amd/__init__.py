@@ -82,12 +82,13 @@ def lib_path() -> str:
     return os.path.join(_HERE, "_lib", "libqs.so")
 
 
-def load():
-    """Load libqs.so (built in-tree by sparse_activation_amd.build)."""
+def load(path: str | None = None):
+    """Load libqs.so (built in-tree by sparse_activation_amd.build), or the
+    library at `path` in its place (for example the host-sanitized build)."""
     global _lib
-    if _lib is not None:
+    if _lib is not None and path is None:
         return _lib
-    path = lib_path()
+    path = path or lib_path()
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m sparse_activation_amd.build`")
     lib = ctypes.CDLL(path)
