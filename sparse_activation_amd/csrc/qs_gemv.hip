@@ -57,13 +57,20 @@ __device__ __forceinline__ uint32_t popc_below(uint64_t m) {
 }
 
 // Split-K handoff between workgroups that may sit on different XCDs (each
-// with its own L2): partials are written and read with relaxed agent-scope
-// atomics (sc1 stores and loads, coherent at agent scope without a cache
-// flush), and the counter increment is an acquire-release RMW at agent
-// scope, so by the memory model every partial a workgroup stored before its
-// increment is visible to the workgroup whose increment comes last.  Each
-// wave first waits for its own stores (s_waitcnt vmcnt(0), 0x0F70), and the
-// workgroup barrier orders them before thread 0's release.
+// with its own L2).  Every value that crosses workgroups is itself an
+// agent-scope atomic access: the partials are written and read with relaxed
+// agent-scope atomic stores and loads (sc1: they bypass the XCD's
+// non-coherent L2, so each is coherent across the device on its own), and the
+// counter is a relaxed agent-scope RMW.  What orders a workgroup's partial
+// stores before its counter increment is the hardware wait for their
+// completion: each wave waits for its own stores (s_waitcnt vmcnt(0), 0x0F70;
+// an sc1 store completes at the device's coherence point), and the workgroup
+// barrier orders all waves before thread 0's increment.  An acquire-release
+// RMW would express the same order in the language's memory model, but at
+// agent scope it writes back and invalidates the whole L2 of the XCD
+// (buffer_wbl2 / buffer_inv) in every workgroup: a 16-token FFN step in the
+// fixed-order mode measured 111 us with it; the protocol relies on this
+// gfx950 behaviour of sc1 accesses instead.
 template <typename T>
 __device__ __forceinline__ void store_agent(T* p, T v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -79,7 +86,7 @@ __device__ __forceinline__ bool last_split_arrived(int32_t* counter, int nsplit,
     wait_stores();
     __syncthreads();
     if (threadIdx.x == 0)
-        *s_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL,
+        *s_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
     __syncthreads();
     return *s_flag != 0;
