@@ -479,8 +479,28 @@ __global__ __launch_bounds__(kFsNT) void gather_sel_kernel(GemvArgs a, int cand,
 #pragma unroll
     for (int i = 0; i < 4 * NQ; ++i) asm volatile("" : "+v"(key[i]));
     __syncthreads();
+    // Once level 1 of the search is known, the candidates whose keys lie in a
+    // higher level-1 bin are selected for sure: each thread touches the
+    // 128-byte line of its tile's segment of such a row (one 4-byte load), so
+    // those lines come from HBM into the caches while the search finishes.
+    // The search's barriers order LDS only, so these loads stay in flight.
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, d_in * (int64_t)rowbytes);
+    const uint32_t tileb = (uint32_t)tile * kFsCols * 2;
+    uint32_t pf = 0;
+    auto prefetch = [&](uint32_t b1) {
+        // one load per thread (its first such row): more loads per wave
+        // would stall the search behind their issue
+        uint32_t off = kOOB;
+#pragma unroll
+        for (int ch = NCH - 1; ch >= 0; --ch) {
+            const int64_t j = j0 + ch * kFsNT + tid;
+            const uint32_t kc = __float_as_uint(c[ch]) & 0x7FFFFFFFu;
+            if (j < j1 && (kc >> 20) > b1) off = (uint32_t)j * rowbytes + tileb;
+        }
+        pf = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+    };
     uint32_t tau, cut;
-    rowsel::select_desc31<kFsNT, NQ>(key, d_in, a.sel_k, L, tid, tau, cut);
+    rowsel::select_desc31<kFsNT, NQ>(key, d_in, a.sel_k, L, tid, tau, cut, prefetch);
 
     // The selected nonzero candidates as a list (one block scan; the list
     // overwrites the selection scratch after its barrier).
@@ -494,7 +514,7 @@ __global__ __launch_bounds__(kFsNT) void gather_sel_kernel(GemvArgs a, int cand,
     const uint32_t mycnt = (uint32_t)__popc(selbits);
     const uint32_t incl = sel::wave_incl_scan_dpp(mycnt);
     if (lane == 63) s_wsum[wave] = incl;
-    __syncthreads();
+    rowsel::lds_barrier();
     uint32_t before = 0, nact = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -514,13 +534,12 @@ __global__ __launch_bounds__(kFsNT) void gather_sel_kernel(GemvArgs a, int cand,
     const int nbatch = (int)((nact + kFsBatch - 1) / kFsBatch);
     const int npad = ((nbatch + 1) / 2 * 2 + 1) * kFsBatch;
     for (int i = (int)nact + tid; i < npad; i += kFsNT) { s_off[i] = kOOB; s_coef[i] = 0.0f; }
-    __syncthreads();
+    rowsel::lds_barrier();
 
     // Stream the selected rows' 128-byte segments, one stage ahead.
     const int slot = tid / kFLPR;
     const int64_t col = (int64_t)tile * kFsCols + (lane % kFLPR) * 8;
     const uint32_t colb = col < n_out ? (uint32_t)(col * 2) : kOOB;
-    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, d_in * (int64_t)rowbytes);
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
@@ -553,6 +572,9 @@ __global__ __launch_bounds__(kFsNT) void gather_sel_kernel(GemvArgs a, int cand,
         __builtin_amdgcn_sched_barrier(0);
     }
 
+    // (the touched lines' values are not needed: an empty asm consumes them)
+    asm volatile("" : : "v"(pf));
+
     // Fixed-order sum of the 128 slots: slots 2r and 2r + 1 of a 16-lane row
     // by one DPP rotation, then the 64 rows in LDS in row order.
     __syncthreads();   // the list is dead: the reduction buffer overwrites it
@@ -565,12 +587,20 @@ __global__ __launch_bounds__(kFsNT) void gather_sel_kernel(GemvArgs a, int cand,
         if ((lane & 15) < kFLPR) s_red[rrow * kFsCols + (lane & 15) * 8 + e] = v;
     }
     __syncthreads();
-    if (tid < kFsCols) {
+    {
+        // 16 lanes per column (one 16-lane row): lane `part` sums rows 4 part
+        // .. 4 part + 3, then an inclusive DPP scan across the row (row_shr 1,
+        // 2, 4, 8) leaves the column's total, in a fixed order, in lane 15.
+        const int col = tid >> 4, part = tid & 15;
         float s = 0.0f;
-#pragma unroll 8
-        for (int r = 0; r < 4 * NW; ++r) s += s_red[r * kFsCols + tid];
-        const int64_t cg = (int64_t)tile * kFsCols + tid;
-        if (cg < n_out) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s += s_red[(4 * part + i) * kFsCols + col];
+        s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x111, 0xF, 0xF, true));
+        s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x112, 0xF, 0xF, true));
+        s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x114, 0xF, 0xF, true));
+        s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x118, 0xF, 0xF, true));
+        const int64_t cg = (int64_t)tile * kFsCols + col;
+        if (part == 15 && cg < n_out) {
             if (a.accumulate) unsafeAtomicAdd(&reinterpret_cast<float*>(a.y)[row * n_out + cg], s);
             else if (nsplit > 1) store_agent(&a.partial[(int64_t)split * n_out + cg], s);
             else store_final(a, cg, s);

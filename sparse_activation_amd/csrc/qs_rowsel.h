@@ -11,6 +11,19 @@
 namespace qs {
 namespace rowsel {
 
+// A workgroup barrier that orders LDS accesses only: global loads in flight
+// stay in flight (__syncthreads() waits for them to land first).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// No-op hook of select_desc31.
+struct NoLevel1Hook {
+    __device__ __forceinline__ void operator()(uint32_t) const {}
+};
+
 // Exclusive prefix over the threads of a workgroup (in thread order) of one
 // count per thread; `tot` receives the total.  Two barriers.
 template <int NT>
@@ -179,7 +192,10 @@ __device__ __forceinline__ void select15_masks(const uint32_t (&key)[BT][E], int
 //            index order.
 // A boundary bin that is taken whole ends the search early: tau is then one
 // below the bin's smallest key and the cutoff 0.  Two barriers in the usual
-// case, besides the one after the caller clears the histograms.
+// case, besides the one after the caller clears the histograms; they order
+// LDS only, so global loads the caller has in flight stay in flight.  The
+// hook is called (uniformly) with level 1's boundary bin: every key whose
+// bits 30..20 exceed it is selected, whatever the later levels find.
 // ---------------------------------------------------------------------------
 constexpr int kS31Cap = 256;   // listed keys of level 1's boundary bin
 
@@ -262,10 +278,10 @@ __device__ __forceinline__ bool desc_bin(const uint32_t* h, uint32_t kr, int lan
 // barrier.
 // Returns, uniform over the workgroup: entry j is among the top k iff key_j >
 // tau, or key_j == tau and j < cutoff.
-template <int NT, int NQ>
+template <int NT, int NQ, typename Hook = NoLevel1Hook>
 __device__ __forceinline__ void select_desc31(const uint32_t (&key)[4 * NQ], int64_t n, int64_t k,
                                               Sel31Lds<NQ, NT / 64>& L, int tid, uint32_t& tau_out,
-                                              uint32_t& cut_out) {
+                                              uint32_t& cut_out, Hook level1 = Hook()) {
     constexpr int NW = NT / 64, KPT = 4 * NQ;
     constexpr uint32_t kAll = 0x7FFFFFFFu;
     const int lane = tid & 63, wave = tid / 64;
@@ -275,11 +291,13 @@ __device__ __forceinline__ void select_desc31(const uint32_t (&key)[4 * NQ], int
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
         if (key[i] != 0u) atomicAdd(&L.h1[key[i] >> 20], 1u);
-    __syncthreads();
+    lds_barrier();
 
     uint32_t tau = 0, need = 0, eqn = 0;
     uint32_t b1, r1, c1, tot;
-    if (!desc_bin<8>(L.h1, (uint32_t)k, lane, b1, r1, c1, tot)) {
+    const bool found1 = desc_bin<8>(L.h1, (uint32_t)k, lane, b1, r1, c1, tot);
+    if (found1) level1(b1);   // keys of level-1 bins above b1 are selected for sure
+    if (!found1) {
         // Fewer than k nonzero keys: all of them, and the first zeros.
         tau = 0; need = (uint32_t)k - tot; eqn = (uint32_t)n - tot;
     } else if (r1 == c1) {
@@ -305,7 +323,7 @@ __device__ __forceinline__ void select_desc31(const uint32_t (&key)[4 * NQ], int
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         uint32_t b2, r2, c2;
         desc_bin<4>(L.h2, r1, lane, b2, r2, c2, tot);   // r1 <= c1 = the level's total
         const uint32_t pre2 = (b1 << 10) | b2;            // the top 21 key bits
@@ -351,7 +369,7 @@ __device__ __forceinline__ void select_desc31(const uint32_t (&key)[4 * NQ], int
 #pragma unroll
         for (int i = 0; i < KPT; ++i)
             if ((key[i] >> 10) == pre2 && key[i] >= lo2) atomicAdd(&L.h3[key[i] & 1023u], 1u);
-        __syncthreads();
+        lds_barrier();
         uint32_t b3;
         desc_bin<4>(L.h3, r2, lane, b3, need, eqn, tot);
         tau = (pre2 << 10) | b3;
@@ -370,7 +388,7 @@ __device__ __forceinline__ void select_desc31(const uint32_t (&key)[4 * NQ], int
         incl[q] = sel::wave_incl_scan_dpp((uint32_t)__popc(tb[q]));
         if (lane == 63) L.tie[q][wave] = incl[q];
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t base = 0;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
@@ -390,7 +408,7 @@ __device__ __forceinline__ void select_desc31(const uint32_t (&key)[4 * NQ], int
         }
         base += qt;
     }
-    __syncthreads();
+    lds_barrier();
     tau_out = tau;
     cut_out = L.cut;
 }
