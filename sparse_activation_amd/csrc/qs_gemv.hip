@@ -645,6 +645,7 @@ constexpr int kUcNT = 512;                   // threads per workgroup
 constexpr int kUcLPR = 8;                    // lanes per 128-byte row segment
 constexpr int kUcSlots = kUcNT / kUcLPR;     // 64 row slots per workgroup
 constexpr int kUcCols = kUcLPR * 8;          // 64 bf16 columns per tile
+constexpr int kUcPf = 1;                     // lines warmed per thread during the selection (more stall it)
 
 // Rows per lane and pipeline stage: one token streams 16 (a Llama-7B
 // selection in two stages), more tokens or the gated pair 8.  (1024 threads
@@ -708,6 +709,14 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
     uint32_t selm[BT];
     float xv[BT][E];
     const int nvalid = (int)d - tid * E;
+    const uint32_t rowbytes = (uint32_t)(ffn * 2);
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, d * (int64_t)rowbytes);
+    const __amdgpu_buffer_rsrc_t rs2 = weight_rsrc(DUAL ? a.w2 : a.w, d * (int64_t)rowbytes);
+    uint32_t pf[NM][kUcPf];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int g = 0; g < kUcPf; ++g) pf[m][g] = 0;
     if (a.xs != nullptr) {   // uniform
 #pragma unroll
         for (int t = 0; t < BT; ++t) {
@@ -751,8 +760,29 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
             for (int e = 0; e < E; ++e)
                 key[t][e] = e < nvalid ? (xr16[t][e / 2] >> (16 * (e % 2))) & 0x7FFFu : sel::kInvalid;
         __syncthreads();
-        rowsel::select15_masks<kUcNT, BT, E>(key, (int)ntok, a.k, L, tid, selm);
-        __syncthreads();   // the selection scratch becomes the row list
+        // Once level 1 of the search is known, the entries whose keys lie in
+        // a higher level-1 bin are selected for sure: each thread touches the
+        // 128-byte line of this tile's segment of up to kUcPf such rows (one
+        // 4-byte load each, the first such entry of each group of E / kUcPf),
+        // so those lines come from HBM into the caches while the search
+        // finishes.  The barriers up to the stream order LDS only, so these
+        // loads stay in flight.
+        const uint32_t tileb = (uint32_t)tile * kUcCols * 2;
+        auto prefetch = [&](int t, uint32_t b1) {
+            if (t != 0) return;
+#pragma unroll
+            for (int g = 0; g < kUcPf; ++g) {
+                uint32_t off = kOOB;
+#pragma unroll
+                for (int e = (g + 1) * (E / kUcPf) - 1; e >= g * (E / kUcPf); --e)
+                    if (key[0][e] != sel::kInvalid && (key[0][e] >> 7) > b1)
+                        off = (uint32_t)(tid * E + e) * rowbytes + tileb;
+                pf[0][g] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+                if constexpr (DUAL) pf[1][g] = __builtin_amdgcn_raw_buffer_load_b32(rs2, off, 0, 0);
+            }
+        };
+        rowsel::select15_masks<kUcNT, BT, E>(key, (int)ntok, a.k, L, tid, selm, prefetch);
+        rowsel::lds_barrier();   // the selection scratch becomes the row list
 #pragma unroll
         for (int t = 0; t < BT; ++t)
 #pragma unroll
@@ -769,8 +799,7 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
 #pragma unroll
     for (int t = 0; t < BT; ++t) um |= selm[t];
     uint32_t nsel;
-    uint32_t pos = rowsel::block_excl_scan<kUcNT>((uint32_t)__popc(um), s_wsum, tid, nsel);
-    const uint32_t rowbytes = (uint32_t)(ffn * 2);
+    uint32_t pos = rowsel::block_excl_scan<kUcNT, true>((uint32_t)__popc(um), s_wsum, tid, nsel);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         if (um & (1u << e)) {
@@ -787,14 +816,12 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
 #pragma unroll
         for (int t = 0; t < BT; ++t) s_coef[i * BT + t] = 0.0f;
     }
-    __syncthreads();
+    rowsel::lds_barrier();
 
     // Phase 3: stream the 128-byte segments of the selected rows.
     const int slot = tid / kUcLPR;
     const int64_t col = (int64_t)tile * kUcCols + (lane % kUcLPR) * 8;
     const uint32_t colb = col < ffn ? (uint32_t)(col * 2) : kOOB;
-    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, d * (int64_t)rowbytes);
-    const __amdgpu_buffer_rsrc_t rs2 = weight_rsrc(DUAL ? a.w2 : a.w, d * (int64_t)rowbytes);
     float acc[NM][BT][8];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -840,6 +867,11 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
         fma_stage(bufb, bi + 1);
         __builtin_amdgcn_sched_barrier(0);
     }
+    // (the touched lines' values are not needed: an empty asm consumes them)
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int g = 0; g < kUcPf; ++g) asm volatile("" : : "v"(pf[m][g]));
 
     // Phase 4: sum the 64 row slots in a fixed order.  Inside each 16-lane
     // row the two slots of a column group are summed by one DPP rotation

@@ -19,21 +19,23 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// No-op hook of select_desc31.
+// No-op level-1 hook of select_desc31 and select15_masks.
 struct NoLevel1Hook {
-    __device__ __forceinline__ void operator()(uint32_t) const {}
+    template <typename... A>
+    __device__ __forceinline__ void operator()(A...) const {}
 };
 
 // Exclusive prefix over the threads of a workgroup (in thread order) of one
-// count per thread; `tot` receives the total.  Two barriers.
-template <int NT>
+// count per thread; `tot` receives the total.  Two barriers (with LDS_ONLY,
+// barriers that order LDS only: the caller's global loads stay in flight).
+template <int NT, bool LDS_ONLY = false>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, int tid,
                                                     uint32_t& tot) {
     constexpr int NW = NT / sel::kWave;
     const int lane = tid & (sel::kWave - 1), wave = tid / sel::kWave;
     const uint32_t inc = sel::wave_incl_scan_dpp(v);
     if (lane == sel::kWave - 1) wsum[wave] = inc;
-    __syncthreads();
+    if constexpr (LDS_ONLY) lds_barrier(); else __syncthreads();
     uint32_t before = 0, t = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -41,7 +43,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
         before += w < wave ? c : 0u;
         t += c;
     }
-    __syncthreads();   // wsum may be reused after this
+    if constexpr (LDS_ONLY) lds_barrier(); else __syncthreads();   // wsum may be reused after this
     tot = t;
     return before + inc - v;
 }
@@ -58,7 +60,10 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
 //            taken and how many there are;
 //   ties:    only when some keys equal to tau stay out, a block prefix count
 //            of them in index order lets each thread take its own.
-// Three or four barriers, no broadcast of the result.  L must be zeroed, and
+// Three or four barriers, no broadcast of the result; they order LDS only, so
+// global loads the caller has in flight stay in flight.  The hook is called
+// (uniformly) with each row's level-1 boundary bin: every key whose 8 high
+// bits exceed it is selected, whatever level 2 finds.  L must be zeroed, and
 // a barrier passed, before the call.
 constexpr int kH1Pitch = 256 + 16;
 
@@ -72,10 +77,10 @@ struct Sel15Lds {
     uint32_t tie[BT][NW];
 };
 
-template <int NT, int BT, int E>
+template <int NT, int BT, int E, typename Hook = NoLevel1Hook>
 __device__ __forceinline__ void select15_masks(const uint32_t (&key)[BT][E], int ntok, int64_t k,
                                                Sel15Lds<BT, NT / 64>& L, int tid,
-                                               uint32_t (&selm)[BT]) {
+                                               uint32_t (&selm)[BT], Hook level1 = Hook()) {
     constexpr int NW = NT / 64;
     const int lane = tid & 63, wave = tid / 64;
     const uint32_t kk = (uint32_t)k;
@@ -86,7 +91,7 @@ __device__ __forceinline__ void select15_masks(const uint32_t (&key)[BT][E], int
         for (int e = 0; e < E; ++e)
             if (key[t][e] != sel::kInvalid) atomicAdd(&L.h1[t][lane & 3][key[t][e] >> 7], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t b1[BT], r1[BT];
 #pragma unroll
     for (int t = 0; t < BT; ++t) {
@@ -111,12 +116,13 @@ __device__ __forceinline__ void select15_masks(const uint32_t (&key)[BT][E], int
         const int src = (int)__builtin_ctzll(hit);
         b1[t] = (uint32_t)__builtin_amdgcn_readlane((int)bin, src);
         r1[t] = (uint32_t)__builtin_amdgcn_readlane((int)rank, src);
+        level1(t, b1[t]);   // keys of level-1 bins above b1 are selected for sure
 #pragma unroll
         for (int e2 = 0; e2 < E; ++e2)
             if (key[t][e2] != sel::kInvalid && (key[t][e2] >> 7) == b1[t])
                 atomicAdd(&L.h2[t][key[t][e2] & 127u], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t tau[BT], need[BT];
     bool ties = false;
 #pragma unroll
@@ -147,7 +153,7 @@ __device__ __forceinline__ void select15_masks(const uint32_t (&key)[BT][E], int
             r1[t] = wi - cnt;         // this thread's ties before it inside the wavefront
         }
     }
-    if (ties) __syncthreads();   // uniform
+    if (ties) lds_barrier();   // uniform
 #pragma unroll
     for (int t = 0; t < BT; ++t) {
         selm[t] = 0;
