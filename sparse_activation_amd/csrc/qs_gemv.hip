@@ -1570,18 +1570,46 @@ static_assert(kI8CT == kNT, "the slot reduction gives each thread one column");
 //   * writes acc and y = fl32(fl32(acc) * fl32(alpha / s)); workgroup 0 also
 //     writes q, s and the index list when they are asked for.
 // ---------------------------------------------------------------------------
-template <int BT>
-constexpr int i8f_cols() { return 16; }
+// Output columns per workgroup: 16, 4 packed bytes of each selected row
+// (32 or 64 columns, with fewer cache-line requests for the same bytes, ran
+// slower: the unpacking and sums per thread grow and fewer CUs take part).
+constexpr int kI8Ct = 16;
+// The |q| histogram in copies by lane (the few small |q| bins of an
+// activation would serialise one copy's atomics), pitched so that a bin's
+// copies sit on different LDS banks.
+constexpr int kI8HistCopies = 4;
+constexpr int kI8HistPitch = 128 + 16;
+
+// One step of the wavefront butterfly below, on lane bit B, with NV >> (5 -
+// B) values still held per lane (or one), then the next lower bit.
+template <int NV, int B>
+__device__ __forceinline__ void i8_butterfly(int32_t (&cur)[NV], int lane) {
+    if constexpr (B >= 0) {
+        constexpr int n = (NV >> (5 - B)) > 1 ? (NV >> (5 - B)) : 1;
+        if constexpr (n > 1) {
+            const bool up = (lane >> B) & 1;
+#pragma unroll
+            for (int i = 0; i < n / 2; ++i) {
+                const int32_t send = up ? cur[i] : cur[i + n / 2];
+                const int32_t keep = up ? cur[i + n / 2] : cur[i];
+                cur[i] = keep + __shfl_xor(send, 1 << B);
+            }
+        } else {
+            cur[0] += __shfl_xor(cur[0], 1 << B);
+        }
+        i8_butterfly<NV, B - 1>(cur, lane);
+    }
+}
 
 template <int BT, int E>
 __global__ __launch_bounds__(kNT) void i8t_fused_kernel(I8fArgs a) {
-    constexpr int CT = i8f_cols<BT>();
+    constexpr int CT = kI8Ct;
     constexpr int NW = kNT / 64;
-    extern __shared__ __attribute__((aligned(16))) int32_t ism[];
+    __shared__ int32_t s_part[NW][BT * CT];
     __shared__ uint32_t s_wsum[16];
     __shared__ uint32_t s_tie[BT][NW];
     __shared__ float s_fmax[BT][NW];
-    __shared__ uint32_t s_hist[BT][128];
+    __shared__ uint32_t s_hist[BT][kI8HistCopies][kI8HistPitch];
 
     const int tile = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1602,7 +1630,7 @@ __global__ __launch_bounds__(kNT) void i8t_fused_kernel(I8fArgs a) {
             xv[t][4 * q + 2] = __uint_as_float(v.z); xv[t][4 * q + 3] = __uint_as_float(v.w);
         }
     }
-    for (int i = tid; i < BT * 128; i += kNT) (&s_hist[0][0])[i] = 0;
+    for (int i = tid; i < BT * kI8HistCopies * kI8HistPitch; i += kNT) (&s_hist[0][0][0])[i] = 0;
 #pragma unroll
     for (int t = 0; t < BT; ++t) {
         float m = 0.0f;
@@ -1625,7 +1653,8 @@ __global__ __launch_bounds__(kNT) void i8t_fused_kernel(I8fArgs a) {
             float r = rintf(__fmul_rn(xv[t][e], scale[t]));
             r = fminf(fmaxf(r, -128.0f), 127.0f);
             qv[t][e] = (int32_t)r;
-            if (t < ntok && e < nvalid) atomicAdd(&s_hist[t][qv[t][e] < 0 ? -qv[t][e] : qv[t][e]], 1u);
+            if (t < ntok && e < nvalid)
+                atomicAdd(&s_hist[t][lane % kI8HistCopies][qv[t][e] < 0 ? -qv[t][e] : qv[t][e]], 1u);
         }
     }
     __syncthreads();
@@ -1637,9 +1666,14 @@ __global__ __launch_bounds__(kNT) void i8t_fused_kernel(I8fArgs a) {
     for (int t = 0; t < BT; ++t) {
         selm[t] = 0;
         if (t >= ntok || kk == 0) continue;   // uniform
-        // tau: lane l holds bins 127 - 2l and 126 - 2l; the running total from
-        // the top reaches k in exactly one lane.
-        const uint32_t c0 = s_hist[t][127 - 2 * lane], c1 = s_hist[t][126 - 2 * lane];
+        // tau: lane l holds bins 127 - 2l and 126 - 2l (summed over the
+        // copies); the running total from the top reaches k in exactly one lane.
+        uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+        for (int cp = 0; cp < kI8HistCopies; ++cp) {
+            c0 += s_hist[t][cp][127 - 2 * lane];
+            c1 += s_hist[t][cp][126 - 2 * lane];
+        }
         const uint32_t incl = sel::wave_incl_scan_dpp(c0 + c1);
         const uint32_t excl = incl - c0 - c1;
         const uint64_t hit = __ballot(excl < kk && kk <= incl);
@@ -1658,12 +1692,10 @@ __global__ __launch_bounds__(kNT) void i8t_fused_kernel(I8fArgs a) {
             for (int e = 0; e < E; ++e) eq += (e < nvalid && (uint32_t)abs(qv[t][e]) == tau) ? 1u : 0u;
             const uint32_t wi = sel::wave_incl_scan_dpp(eq);
             if (lane == 63) s_tie[t][wave] = wi;
-            __syncthreads();
+            rowsel::lds_barrier();
 #pragma unroll
             for (int w = 0; w < NW; ++w) before += w < wave ? s_tie[t][w] : 0u;
             before += wi - eq;
-        } else {
-            before = 0;
         }
         uint32_t r = before;
 #pragma unroll
@@ -1732,31 +1764,29 @@ __global__ __launch_bounds__(kNT) void i8t_fused_kernel(I8fArgs a) {
         }
     }
 
-    // Phase 4: exact sums over the threads, [BT * CT][kNT + 1] in LDS: PARTS
-    // threads add SPAN entries of one value each, then one thread per value
-    // adds the PARTS sums (integer sums: the same in any order).
+    // Phase 4: exact sums over the threads.  Inside each wavefront a
+    // butterfly over the lane bits, high bit first: while a lane holds more
+    // than one value it keeps half of them (the upper half where the lane
+    // bit is set) and adds its partner's copy of that half, so after
+    // log2(NV) steps lane l holds value l >> (6 - log2 NV), summed over the
+    // lanes that differ in those bits; the remaining steps add the rest.  The
+    // wavefronts' totals are then added in LDS (integer sums: the same in any
+    // order).
     constexpr int NV = BT * CT;
-    int32_t* s_red = ism;
+    static_assert(NV == 16 || NV == 32 || NV == 64, "one value per lane group");
+    int32_t cur[NV];
 #pragma unroll
     for (int t = 0; t < BT; ++t)
 #pragma unroll
-        for (int c = 0; c < CT; ++c) s_red[(t * CT + c) * (kNT + 1) + tid] = acc[t][c];
-    __syncthreads();
-    constexpr int PARTS = kNT / NV;
-    constexpr int SPAN = kNT / PARTS;
-    int32_t part = 0;
-    {
-        const int v = tid % NV, p = tid / NV;
-#pragma unroll 8
-        for (int i = 0; i < SPAN; ++i) part += s_red[v * (kNT + 1) + p * SPAN + i];
-    }
-    __syncthreads();
-    s_red[tid] = part;   // [PARTS][NV]
+        for (int c = 0; c < CT; ++c) cur[t * CT + c] = acc[t][c];
+    i8_butterfly<NV, 5>(cur, lane);
+    constexpr int LG = NV == 16 ? 4 : NV == 32 ? 5 : 6;
+    if ((lane & ((1 << (6 - LG)) - 1)) == 0) s_part[wave][lane >> (6 - LG)] = cur[0];
     __syncthreads();
     if (tid < NV) {
         int32_t sum = 0;
 #pragma unroll
-        for (int p = 0; p < PARTS; ++p) sum += s_red[p * NV + tid];
+        for (int w = 0; w < NW; ++w) sum += s_part[w][tid];
         const int t = tid / CT, c = tid % CT;
         const int64_t col = (int64_t)tile * CT + c;
         if (t < ntok && col < n_out) {
@@ -2355,6 +2385,9 @@ hipError_t launch_up_cols(const UpColsArgs& a, hipStream_t stream) {
     const int bt = a.rows == 1 ? 1 : a.rows == 2 ? 2 : 4;
     if (a.zero != nullptr && a.n_zero % 4 != 0) return hipErrorInvalidValue;
     const int e = a.d <= 8 * kUcNT ? 8 : 16;
+    // One 64-column tile (128 bytes of each row) per workgroup.  (Spreading
+    // the columns evenly over 256 workgroups, 40 or 48 each, was slower: the
+    // row segments then straddle 128-byte lines that two workgroups fetch.)
     const dim3 grid((unsigned)ceil_div(a.ffn, kUcCols), (unsigned)ceil_div(a.rows, bt));
     const bool dual = a.w2 != nullptr;
 #define QS_UC_CASE(BTV, EV, DU)                                                          \
@@ -2460,13 +2493,11 @@ hipError_t launch_i8t_fused(const I8fArgs& a, hipStream_t stream) {
     if (!i8t_fused_supported(a.rows, a.d_in, a.n_out) || a.k < 0 || a.k > a.d_in)
         return hipErrorInvalidValue;
     const int bt = a.rows == 1 ? 1 : a.rows == 2 ? 2 : 4;
-    const int ct = bt == 4 ? i8f_cols<4>() : i8f_cols<1>();
     const int e = a.d_in <= 4 * kNT ? 4 : a.d_in <= 8 * kNT ? 8 : 16;
-    const dim3 grid((unsigned)ceil_div(a.n_out, ct));
-    const size_t lds = (size_t)bt * ct * (kNT + 1) * 4;
+    const dim3 grid((unsigned)ceil_div(a.n_out, kI8Ct));
 #define QS_I8F_CASE(BTV, EV)                                                       \
     if (bt == BTV && e == EV) {                                                    \
-        i8t_fused_kernel<BTV, EV><<<grid, dim3(kNT), lds, stream>>>(a);            \
+        i8t_fused_kernel<BTV, EV><<<grid, dim3(kNT), 0, stream>>>(a);              \
         return hipGetLastError();                                                  \
     }
     QS_I8F_CASE(1, 4) QS_I8F_CASE(1, 8) QS_I8F_CASE(1, 16)
