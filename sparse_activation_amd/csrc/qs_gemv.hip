@@ -1574,6 +1574,9 @@ static_assert(kI8CT == kNT, "the slot reduction gives each thread one column");
 // (32 or 64 columns, with fewer cache-line requests for the same bytes, ran
 // slower: the unpacking and sums per thread grow and fewer CUs take part).
 constexpr int kI8Ct = 16;
+// Threads per workgroup: 1024 for one token, 512 for 2-4 (the chains of
+// dependent steps are per thread; 256 threads ran 5% and 9% slower).
+constexpr int i8f_threads(int bt) { return bt == 1 ? 1024 : 512; }
 // The |q| histogram in copies by lane (the few small |q| bins of an
 // activation would serialise one copy's atomics), pitched so that a bin's
 // copies sit on different LDS banks.
@@ -1602,9 +1605,10 @@ __device__ __forceinline__ void i8_butterfly(int32_t (&cur)[NV], int lane) {
 }
 
 template <int BT, int E>
-__global__ __launch_bounds__(kNT) void i8t_fused_kernel(I8fArgs a) {
+__global__ __launch_bounds__(i8f_threads(BT)) void i8t_fused_kernel(I8fArgs a) {
+    constexpr int NT = i8f_threads(BT);
     constexpr int CT = kI8Ct;
-    constexpr int NW = kNT / 64;
+    constexpr int NW = NT / 64;
     __shared__ int32_t s_part[NW][BT * CT];
     __shared__ uint32_t s_wsum[16];
     __shared__ uint32_t s_tie[BT][NW];
@@ -1630,7 +1634,7 @@ __global__ __launch_bounds__(kNT) void i8t_fused_kernel(I8fArgs a) {
             xv[t][4 * q + 2] = __uint_as_float(v.z); xv[t][4 * q + 3] = __uint_as_float(v.w);
         }
     }
-    for (int i = tid; i < BT * kI8HistCopies * kI8HistPitch; i += kNT) (&s_hist[0][0][0])[i] = 0;
+    for (int i = tid; i < BT * kI8HistCopies * kI8HistPitch; i += NT) (&s_hist[0][0][0])[i] = 0;
 #pragma unroll
     for (int t = 0; t < BT; ++t) {
         float m = 0.0f;
@@ -1726,7 +1730,7 @@ __global__ __launch_bounds__(kNT) void i8t_fused_kernel(I8fArgs a) {
             if (a.xscale != nullptr && tid == 0) a.xscale[t] = scale[t];
             if (a.idx != nullptr) {
                 uint32_t tot;
-                uint32_t pos = rowsel::block_excl_scan<kNT>((uint32_t)__popc(selm[t]), s_wsum, tid, tot);
+                uint32_t pos = rowsel::block_excl_scan<NT>((uint32_t)__popc(selm[t]), s_wsum, tid, tot);
 #pragma unroll
                 for (int e = 0; e < E; ++e)
                     if (selm[t] & (1u << e)) a.idx[(int64_t)t * a.k + pos++] = tid * E + e;
@@ -2485,7 +2489,8 @@ I8tPlan plan_i8t(int64_t rows, int64_t d_in, int64_t n_out) {
 }
 
 bool i8t_fused_supported(int64_t rows, int64_t d_in, int64_t n_out) {
-    return rows >= 1 && rows <= 4 && d_in % 4 == 0 && d_in <= 16 * kNT && n_out % 16 == 0;
+    return rows >= 1 && rows <= 4 && d_in % 4 == 0 && d_in <= 16 * i8f_threads(rows == 1 ? 1 : 2) &&
+           n_out % 16 == 0;
 }
 
 hipError_t launch_i8t_fused(const I8fArgs& a, hipStream_t stream) {
@@ -2493,11 +2498,12 @@ hipError_t launch_i8t_fused(const I8fArgs& a, hipStream_t stream) {
     if (!i8t_fused_supported(a.rows, a.d_in, a.n_out) || a.k < 0 || a.k > a.d_in)
         return hipErrorInvalidValue;
     const int bt = a.rows == 1 ? 1 : a.rows == 2 ? 2 : 4;
-    const int e = a.d_in <= 4 * kNT ? 4 : a.d_in <= 8 * kNT ? 8 : 16;
+    const int nt = i8f_threads(bt);
+    const int e = a.d_in <= 4 * nt ? 4 : a.d_in <= 8 * nt ? 8 : 16;
     const dim3 grid((unsigned)ceil_div(a.n_out, kI8Ct));
 #define QS_I8F_CASE(BTV, EV)                                                       \
     if (bt == BTV && e == EV) {                                                    \
-        i8t_fused_kernel<BTV, EV><<<grid, dim3(kNT), 0, stream>>>(a);              \
+        i8t_fused_kernel<BTV, EV><<<grid, dim3(i8f_threads(BTV)), 0, stream>>>(a); \
         return hipGetLastError();                                                  \
     }
     QS_I8F_CASE(1, 4) QS_I8F_CASE(1, 8) QS_I8F_CASE(1, 16)
