@@ -417,33 +417,46 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
 // W_down).  One workgroup of 1024 threads per CU (a 64-column tile of y and a
 // split of the candidate rows): each finds the top-k descriptor of the whole
 // row of h itself (rowsel::select_desc31, as the descriptor launch does),
-// keeps the entries of its split that the descriptor selects, and streams
-// their rows of W_down^T: eight lanes per 128-byte row segment, 128 row slots,
-// 8 rows per slot and stage in two ping-pong register stages.  The 128 slots
-// are summed in a fixed order (one DPP rotation, then 64 rows in LDS).
+// and every wavefront lists the entries of its own share of the split that
+// the descriptor selects (ballots into its own LDS segment: no workgroup
+// barrier between the search and the stream) and streams their rows of
+// W_down^T: eight lanes per 128-byte row segment (eight rows per wavefront
+// load), up to 8 loads per lane and stage in two ping-pong register stages,
+// no loads past the list's end.  The 128 row slots are summed in a fixed
+// order (one DPP rotation, then 64 rows in LDS).
 // ---------------------------------------------------------------------------
 constexpr int kFsNT = 1024;
-constexpr int kFsSlots = kFsNT / kFLPR;     // 128 row slots
-constexpr int kFsU = 8;                     // rows per slot and stage
-constexpr int kFsBatch = kFsSlots * kFsU;   // 1024 rows per stage
+constexpr int kFsU = 8;                     // loads per lane and stage
 constexpr int kFsMaxCand = 4 * kFsNT;       // candidates per split
 constexpr int kFsCols = kFLPR * 8;          // 64 bf16 columns per tile
+
+// Words of the selection scratch (whole 256-byte blocks) and of the kernel's
+// LDS: the scratch (which the 64 x 64 reduction rows reuse), each
+// wavefront's list of row offsets and coefficients, the split flag.
+template <int NQ>
+__host__ __device__ constexpr int fs_sel_words() {
+    return (int)((sizeof(rowsel::Sel31Lds<NQ, kFsNT / 64>) / 4 + 63) / 64 * 64);
+}
+template <int NQ>
+__host__ __device__ constexpr int fs_lds_words() {
+    return fs_sel_words<NQ>() + 2 * (kFsNT / 64) * (kFsMaxCand / kFsNT) * 64 + 1;
+}
+static_assert(64 * kFsCols <= fs_sel_words<1>(), "reduction rows fit in the selection scratch");
 
 template <int NQ>
 __global__ __launch_bounds__(kFsNT) void gather_sel_kernel(GemvArgs a, int cand, int nsplit) {
     constexpr int NCH = kFsMaxCand / kFsNT;
     constexpr int NW = kFsNT / 64;
+    constexpr int kWCap = NCH * 64;   // a wavefront's candidates
     // All LDS is dynamic, from offset 0 (a selection scratch placed behind
     // static variables ran its search more than twice as slowly): the
-    // selection scratch, then (after its last read) the row list, then the
-    // reduction rows; the scan totals and the split flag sit after the list.
+    // selection scratch (later the reduction rows), then each wavefront's row
+    // list, then the split flag.
     extern __shared__ __attribute__((aligned(256))) float smem[];
-    float* s_coef = smem;                                                         // [cand + 3 batch]
-    uint32_t* s_off = reinterpret_cast<uint32_t*>(smem + cand + 3 * kFsBatch);   // [cand + 3 batch]
-    constexpr int kSelWords = (int)(sizeof(rowsel::Sel31Lds<NQ, NW>) / 4);
-    const int tail = 2 * (cand + 3 * kFsBatch) > kSelWords ? 2 * (cand + 3 * kFsBatch) : kSelWords;
-    uint32_t* s_wsum = reinterpret_cast<uint32_t*>(smem + tail);                  // [NW]
-    int* s_last = reinterpret_cast<int*>(s_wsum + NW);
+    constexpr int kSelWords = fs_sel_words<NQ>();
+    uint32_t* s_woff = reinterpret_cast<uint32_t*>(smem + kSelWords);             // [NW][kWCap]
+    float* s_wcoef = smem + kSelWords + NW * kWCap;                               // [NW][kWCap]
+    int* s_last = reinterpret_cast<int*>(smem + kSelWords + 2 * NW * kWCap);
 
     const int tile = blockIdx.x, split = blockIdx.y;
     const int64_t row = blockIdx.z;   // (split partials: one row)
@@ -502,74 +515,76 @@ __global__ __launch_bounds__(kFsNT) void gather_sel_kernel(GemvArgs a, int cand,
     uint32_t tau, cut;
     rowsel::select_desc31<kFsNT, NQ>(key, d_in, a.sel_k, L, tid, tau, cut, prefetch);
 
-    // The selected nonzero candidates as a list (one block scan; the list
-    // overwrites the selection scratch after its barrier).
-    uint32_t selbits = 0;
+    // This wavefront's selected nonzero candidates (entries j0 + ch * 1024 +
+    // 64 wave + lane) as a list in its own LDS segment, in (ch, lane) order.
+    uint32_t* w_off = s_woff + wave * kWCap;
+    float* w_coef = s_wcoef + wave * kWCap;
+    uint32_t n = 0;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-        const uint32_t j = (uint32_t)(j0 + ch * kFsNT + tid);
-        if (!rowsel::selected(__float_as_uint(c[ch]) & 0x7FFFFFFFu, j, tau, cut)) c[ch] = 0.0f;
-        selbits |= (c[ch] != 0.0f ? 1u : 0u) << ch;
-    }
-    const uint32_t mycnt = (uint32_t)__popc(selbits);
-    const uint32_t incl = sel::wave_incl_scan_dpp(mycnt);
-    if (lane == 63) s_wsum[wave] = incl;
-    rowsel::lds_barrier();
-    uint32_t before = 0, nact = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint32_t cw = s_wsum[w];
-        before += w < wave ? cw : 0u;
-        nact += cw;
-    }
-    uint32_t pos = before + incl - mycnt;
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-        if ((selbits >> ch) & 1u) {
-            s_off[pos] = (uint32_t)(j0 + ch * kFsNT + tid) * rowbytes;
-            s_coef[pos] = c[ch];
-            ++pos;
+        const int64_t j = j0 + ch * kFsNT + tid;
+        const bool on = j < j1 && c[ch] != 0.0f &&
+                        rowsel::selected(__float_as_uint(c[ch]) & 0x7FFFFFFFu, (uint32_t)j, tau, cut);
+        const uint64_t m = __ballot(on);
+        if (on) {
+            const uint32_t p = n + sel::popc_below(m);
+            w_off[p] = (uint32_t)j * rowbytes;
+            w_coef[p] = c[ch];
         }
+        n += (uint32_t)__popcll(m);
     }
-    const int nbatch = (int)((nact + kFsBatch - 1) / kFsBatch);
-    const int npad = ((nbatch + 1) / 2 * 2 + 1) * kFsBatch;
-    for (int i = (int)nact + tid; i < npad; i += kFsNT) { s_off[i] = kOOB; s_coef[i] = 0.0f; }
-    rowsel::lds_barrier();
+    n = __builtin_amdgcn_readfirstlane(n);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // Stream the selected rows' 128-byte segments, one stage ahead.
-    const int slot = tid / kFLPR;
+    // Stream the listed rows' 128-byte segments, one stage ahead: wavefront
+    // load li covers list entries 8 li .. 8 li + 7 (lane / 8 picks the row).
+    const int rsub = lane / kFLPR;
     const int64_t col = (int64_t)tile * kFsCols + (lane % kFLPR) * 8;
     const uint32_t colb = col < n_out ? (uint32_t)(col * 2) : kOOB;
+    const int nld = (int)((n + kFLPR - 1) / kFLPR);
+    const int nst = (nld + kFsU - 1) / kFsU;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
     u32x4 bufa[kFsU], bufb[kFsU];
-    auto load_stage = [&](u32x4* dst, int bi) {
-#pragma unroll
-        for (int u = 0; u < kFsU; ++u)
-            dst[u] = __builtin_amdgcn_raw_buffer_load_b128(
-                rs, s_off[bi * kFsBatch + u * kFsSlots + slot] + colb, 0, 0);
-    };
-    auto fma_stage = [&](const u32x4* src, int bi) {
+    auto load_stage = [&](u32x4* dst, int st) {
 #pragma unroll
         for (int u = 0; u < kFsU; ++u) {
-            const float cf = s_coef[bi * kFsBatch + u * kFsSlots + slot];
-            float w[8];
-            unpack<1>(src[u], w);
+            const int li = st * kFsU + u;
+            if (li < nld) {   // uniform
+                const int r = li * kFLPR + rsub;
+                dst[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, (r < (int)n ? w_off[r] : kOOB) + colb, 0, 0);
+            }
+        }
+    };
+    auto fma_stage = [&](const u32x4* src, int st) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = fmaf(cf, w[e], acc[e]);
+        for (int u = 0; u < kFsU; ++u) {
+            const int li = st * kFsU + u;
+            if (li < nld) {   // uniform
+                const int r = li * kFLPR + rsub;
+                const float cf = r < (int)n ? w_coef[r] : 0.0f;
+                float w[8];
+                unpack<1>(src[u], w);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(cf, w[e], acc[e]);
+            }
         }
     };
     load_stage(bufa, 0);
-    for (int bi = 0; bi < nbatch; bi += 2) {
-        load_stage(bufb, bi + 1);
+    load_stage(bufb, 1);
+    for (int st = 0; st < nst; st += 2) {   // uniform
         __builtin_amdgcn_sched_barrier(0);
-        fma_stage(bufa, bi);
+        fma_stage(bufa, st);
         __builtin_amdgcn_sched_barrier(0);
-        load_stage(bufa, bi + 2);
+        if (st + 2 < nst) load_stage(bufa, st + 2);
         __builtin_amdgcn_sched_barrier(0);
-        fma_stage(bufb, bi + 1);
+        if (st + 1 < nst) fma_stage(bufb, st + 1);
         __builtin_amdgcn_sched_barrier(0);
+        if (st + 3 < nst) load_stage(bufb, st + 3);
     }
 
     // (the touched lines' values are not needed: an empty asm consumes them)
@@ -632,10 +647,12 @@ __global__ __launch_bounds__(kFsNT) void gather_sel_kernel(GemvArgs a, int cand,
 //     itself (two LDS histogram levels over the 15-bit magnitude keys, see
 //     rowsel::select15_masks), so no selection launch precedes it;
 //   * it owns a tile of 64 output columns over ALL rows that some token of
-//     its tile selects: the selected entries become an ascending row list
-//     with their coefficients, then eight lanes stream one 128-byte row segment
-//     with 16-byte loads (eight rows per wavefront load), U rows per lane and
-//     stage in two ping-pong register stages, fp32 FMA;
+//     its tile selects: every wavefront lists the selected entries of its own
+//     run of the row (a wavefront scan into its own LDS segment, no
+//     workgroup barrier) with their coefficients, then eight lanes stream one
+//     128-byte row segment with 16-byte loads (eight rows per wavefront load),
+//     up to U loads per lane and stage in two ping-pong register stages, none
+//     past the list's end, fp32 FMA;
 //   * the 64 row slots are summed with one DPP rotation and then in LDS, in a
 //     fixed order, so u is complete (no split partials, no atomics, bitwise
 //     reproducible) and the activation is applied here: h = relu(u)^2, or
@@ -653,36 +670,29 @@ constexpr int kUcPf = 1;                     // lines warmed per thread during t
 template <int BT, bool DUAL>
 constexpr int uc_unroll() { return BT == 1 && !DUAL ? 16 : 8; }
 
-// Entries of the padded row list for rows of length d (the stage loop reads
-// one stage past an even number of stages).
-constexpr int64_t uc_list_cap(int64_t d, int u) {
-    const int64_t batch = (int64_t)kUcSlots * u;
-    const int64_t nb = (d + batch - 1) / batch;
-    return ((nb + 1) / 2 * 2 + 1) * batch;
+// LDS words: the selection scratch (whole 256-byte blocks), then each
+// wavefront's row list (64 E entries: a row offset and BT coefficients
+// each); the reduction rows reuse the front once the stream is done.
+template <int BT>
+__host__ __device__ constexpr int64_t uc_sel_words() {
+    return ((int64_t)sizeof(rowsel::Sel15Lds<BT, kUcNT / 64>) / 4 + 63) / 64 * 64;
 }
-
-// Words of LDS before the scan totals: the largest of the row list, the
-// selection scratch and the reduction rows.
-template <int BT, bool DUAL>
-__host__ __device__ constexpr int64_t uc_lds_tail(int64_t d) {
-    const int64_t list = uc_list_cap(d, uc_unroll<BT, DUAL>()) * (1 + BT);
-    const int64_t selw = (int64_t)sizeof(rowsel::Sel15Lds<BT, kUcNT / 64>) / 4;
+template <int BT, int E, bool DUAL>
+__host__ __device__ constexpr int64_t uc_lds_words() {
+    const int64_t lists = uc_sel_words<BT>() + (int64_t)(kUcNT / 64) * 64 * E * (1 + BT);
     const int64_t red = (int64_t)(kUcNT / 16) * (DUAL ? 2 : 1) * BT * kUcCols;
-    const int64_t m = list > selw ? list : selw;
-    return m > red ? m : red;
+    return lists > red ? lists : red;
 }
 
 template <int BT, int E, bool DUAL>
 __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
     constexpr int U = uc_unroll<BT, DUAL>();
-    constexpr int BATCH = kUcSlots * U;
     constexpr int NM = DUAL ? 2 : 1;
     constexpr int NW = kUcNT / 64;
     // All LDS is dynamic, from offset 0 (tables behind static variables ran
     // markedly slower): the selection scratch or the row list, later the
     // reduction rows; the scan totals sit behind the largest of them.
     extern __shared__ __attribute__((aligned(256))) float smem[];
-    uint32_t* s_wsum = reinterpret_cast<uint32_t*>(smem + uc_lds_tail<BT, DUAL>(a.d));   // [16]
 
     const int tile = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -782,7 +792,6 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
             }
         };
         rowsel::select15_masks<kUcNT, BT, E>(key, (int)ntok, a.k, L, tid, selm, prefetch);
-        rowsel::lds_barrier();   // the selection scratch becomes the row list
 #pragma unroll
         for (int t = 0; t < BT; ++t)
 #pragma unroll
@@ -790,38 +799,41 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
                 xv[t][e] = (selm[t] >> e) & 1u ? __uint_as_float((xr16[t][e / 2] >> (16 * (e % 2))) << 16) : 0.0f;
     }
 
-    // Phase 2: the union of the selections as an ascending row list with each
-    // token's coefficient (0 where the token does not select the row).
-    const int64_t cap = uc_list_cap(d, U);
-    uint32_t* s_off = reinterpret_cast<uint32_t*>(smem);
-    float* s_coef = smem + cap;
+    // Phase 2: the union of the selections over this wavefront's run of the
+    // row (entries 64 E wave .. 64 E wave + 64 E - 1) as an ascending row list
+    // in its own LDS segment, with each token's coefficient (0 where the
+    // token does not select the row).
+    constexpr int kWCap = 64 * E;
+    uint32_t* w_off = reinterpret_cast<uint32_t*>(smem + uc_sel_words<BT>()) + wave * kWCap;
+    float* w_coef = smem + uc_sel_words<BT>() + NW * kWCap + wave * kWCap * BT;
     uint32_t um = 0;
 #pragma unroll
     for (int t = 0; t < BT; ++t) um |= selm[t];
-    uint32_t nsel;
-    uint32_t pos = rowsel::block_excl_scan<kUcNT, true>((uint32_t)__popc(um), s_wsum, tid, nsel);
+    const uint32_t ucnt = (uint32_t)__popc(um);
+    const uint32_t uincl = sel::wave_incl_scan_dpp(ucnt);
+    const int n = __builtin_amdgcn_readlane((int)uincl, 63);
+    uint32_t pos = uincl - ucnt;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         if (um & (1u << e)) {
-            s_off[pos] = (uint32_t)(tid * E + e) * rowbytes;
+            w_off[pos] = (uint32_t)(tid * E + e) * rowbytes;
 #pragma unroll
-            for (int t = 0; t < BT; ++t) s_coef[pos * BT + t] = xv[t][e];   // 0 off the token's selection
+            for (int t = 0; t < BT; ++t) w_coef[pos * BT + t] = xv[t][e];
             ++pos;
         }
     }
-    const int nbatch = (int)((nsel + BATCH - 1) / BATCH);
-    const int npad = ((nbatch + 1) / 2 * 2 + 1) * BATCH;
-    for (int i = (int)nsel + tid; i < npad; i += kUcNT) {
-        s_off[i] = kOOB;
-#pragma unroll
-        for (int t = 0; t < BT; ++t) s_coef[i * BT + t] = 0.0f;
-    }
-    rowsel::lds_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // Phase 3: stream the 128-byte segments of the selected rows.
-    const int slot = tid / kUcLPR;
+    // Phase 3: stream the 128-byte segments of the listed rows, one stage
+    // ahead: wavefront load li covers list entries 8 li .. 8 li + 7 (lane / 8
+    // picks the row).
+    const int rsub = lane / kUcLPR;
     const int64_t col = (int64_t)tile * kUcCols + (lane % kUcLPR) * 8;
     const uint32_t colb = col < ffn ? (uint32_t)(col * 2) : kOOB;
+    const int nld = (n + kUcLPR - 1) / kUcLPR;
+    const int nst = (nld + U - 1) / U;
     float acc[NM][BT][8];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -830,42 +842,50 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[m][t][e] = 0.0f;
     u32x4 bufa[NM][U], bufb[NM][U];
-    auto load_stage = [&](u32x4 (*dst)[U], int bi) {
+    auto load_stage = [&](u32x4 (*dst)[U], int st) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t off = s_off[bi * BATCH + u * kUcSlots + slot] + colb;
-            dst[0][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-            if constexpr (DUAL) dst[1][u] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off, 0, 0);
+            const int li = st * U + u;
+            if (li < nld) {   // uniform
+                const int r = li * kUcLPR + rsub;
+                const uint32_t off = (r < n ? w_off[r] : kOOB) + colb;
+                dst[0][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+                if constexpr (DUAL) dst[1][u] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off, 0, 0);
+            }
         }
     };
-    auto fma_stage = [&](const u32x4 (*src)[U], int bi) {
+    auto fma_stage = [&](const u32x4 (*src)[U], int st) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int ai = bi * BATCH + u * kUcSlots + slot;
-            float cf[BT];
+            const int li = st * U + u;
+            if (li < nld) {   // uniform
+                const int r = li * kUcLPR + rsub;
+                float cf[BT];
 #pragma unroll
-            for (int t = 0; t < BT; ++t) cf[t] = s_coef[ai * BT + t];
+                for (int t = 0; t < BT; ++t) cf[t] = r < n ? w_coef[r * BT + t] : 0.0f;
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                float w[8];
-                unpack<1>(src[m][u], w);
+                for (int m = 0; m < NM; ++m) {
+                    float w[8];
+                    unpack<1>(src[m][u], w);
 #pragma unroll
-                for (int t = 0; t < BT; ++t)
+                    for (int t = 0; t < BT; ++t)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[m][t][e] = fmaf(cf[t], w[e], acc[m][t][e]);
+                        for (int e = 0; e < 8; ++e) acc[m][t][e] = fmaf(cf[t], w[e], acc[m][t][e]);
+                }
             }
         }
     };
     load_stage(bufa, 0);
-    for (int bi = 0; bi < nbatch; bi += 2) {
-        load_stage(bufb, bi + 1);
+    load_stage(bufb, 1);
+    for (int st = 0; st < nst; st += 2) {   // uniform
         __builtin_amdgcn_sched_barrier(0);
-        fma_stage(bufa, bi);
+        fma_stage(bufa, st);
         __builtin_amdgcn_sched_barrier(0);
-        load_stage(bufa, bi + 2);
+        if (st + 2 < nst) load_stage(bufa, st + 2);
         __builtin_amdgcn_sched_barrier(0);
-        fma_stage(bufb, bi + 1);
+        if (st + 1 < nst) fma_stage(bufb, st + 1);
         __builtin_amdgcn_sched_barrier(0);
+        if (st + 3 < nst) load_stage(bufb, st + 3);
     }
     // (the touched lines' values are not needed: an empty asm consumes them)
 #pragma unroll
@@ -2359,16 +2379,10 @@ hipError_t launch_gather_sel(const GemvArgs& a, hipStream_t stream) {
     int nt, ns, cand;
     gather_sel_plan(a.d_in, a.n_out, &nt, &ns, &cand);
     const int nq = (int)ceil_div(a.d_in, 4 * kFsNT);
-    // (the list covers the reduction rows; the scan totals and the flag sit
-    // behind the larger of the list and the selection scratch, as in the kernel)
-    static_assert((size_t)64 * kFsCols * 4 <= (size_t)2 * 3 * kFsBatch * 4, "reduction rows fit");
     const dim3 grid((unsigned)nt, (unsigned)ns, (unsigned)a.rows), block(kFsNT);
 #define QS_FS_CASE(NQV)                                                                   \
     if (nq <= NQV) {                                                                      \
-        const size_t sel = sizeof(rowsel::Sel31Lds<NQV, kFsNT / 64>) / 4;                 \
-        size_t tail = (size_t)2 * (cand + 3 * kFsBatch);                                  \
-        if (tail < sel) tail = sel;                                                       \
-        gather_sel_kernel<NQV><<<grid, block, (tail + kFsNT / 64 + 1) * 4, stream>>>(a, cand, ns); \
+        gather_sel_kernel<NQV><<<grid, block, (size_t)fs_lds_words<NQV>() * 4, stream>>>(a, cand, ns); \
         return hipGetLastError();                                                         \
     }
     QS_FS_CASE(1) QS_FS_CASE(2) QS_FS_CASE(3) QS_FS_CASE(4)
@@ -2377,8 +2391,16 @@ hipError_t launch_gather_sel(const GemvArgs& a, hipStream_t stream) {
 }
 
 bool up_cols_supported(int64_t rows, int64_t d, int64_t ffn) {
-    return rows >= 1 && rows <= 4 && d % 8 == 0 && d <= kUpColsMaxD && ffn % 8 == 0 &&
-           ffn <= kUpColsMaxFfn;
+    if (!(rows >= 1 && rows <= 4 && d % 8 == 0 && d <= kUpColsMaxD && ffn % 8 == 0 &&
+          ffn <= kUpColsMaxFfn))
+        return false;
+    // The wavefronts' row lists must fit in the 160 KiB of LDS (for a tile
+    // of four tokens: d <= 4096).
+    const bool e8 = d <= 8 * kUcNT;
+    const int64_t words = rows == 1 ? (e8 ? uc_lds_words<1, 8, true>() : uc_lds_words<1, 16, true>())
+                          : rows == 2 ? (e8 ? uc_lds_words<2, 8, true>() : uc_lds_words<2, 16, true>())
+                                      : (e8 ? uc_lds_words<4, 8, true>() : uc_lds_words<4, 16, true>());
+    return words * 4 <= 160 * 1024;
 }
 
 hipError_t launch_up_cols(const UpColsArgs& a, hipStream_t stream) {
@@ -2396,7 +2418,7 @@ hipError_t launch_up_cols(const UpColsArgs& a, hipStream_t stream) {
     const bool dual = a.w2 != nullptr;
 #define QS_UC_CASE(BTV, EV, DU)                                                          \
     if (bt == BTV && e == EV && dual == DU) {                                            \
-        const size_t lds = (size_t)(uc_lds_tail<BTV, DU>(a.d) + 16) * 4;                 \
+        const size_t lds = (size_t)uc_lds_words<BTV, EV, DU>() * 4;                      \
         up_cols_kernel<BTV, EV, DU><<<grid, dim3(kUcNT), lds, stream>>>(a);              \
         return hipGetLastError();                                                        \
     }
