@@ -670,9 +670,29 @@ constexpr int kUcPf = 1;                     // lines warmed per thread during t
 template <int BT, bool DUAL>
 constexpr int uc_unroll() { return BT == 1 && !DUAL ? 16 : 8; }
 
-// LDS words: the selection scratch (whole 256-byte blocks), then each
-// wavefront's row list (64 E entries: a row offset and BT coefficients
-// each); the reduction rows reuse the front once the stream is done.
+// Entries of the padded workgroup-wide row list for rows of length d (the
+// stage loop reads one stage past an even number of stages).
+constexpr int64_t uc_list_cap(int64_t d, int u) {
+    const int64_t batch = (int64_t)kUcSlots * u;
+    const int64_t nb = (d + batch - 1) / batch;
+    return ((nb + 1) / 2 * 2 + 1) * batch;
+}
+
+// Words of LDS of the workgroup-wide list form before its scan totals: the
+// largest of the row list, the selection scratch and the reduction rows.
+template <int BT, bool DUAL>
+__host__ __device__ constexpr int64_t uc_lds_tail(int64_t d) {
+    const int64_t list = uc_list_cap(d, uc_unroll<BT, DUAL>()) * (1 + BT);
+    const int64_t selw = (int64_t)sizeof(rowsel::Sel15Lds<BT, kUcNT / 64>) / 4;
+    const int64_t red = (int64_t)(kUcNT / 16) * (DUAL ? 2 : 1) * BT * kUcCols;
+    const int64_t m = list > selw ? list : selw;
+    return m > red ? m : red;
+}
+
+// LDS words of the per-wavefront list form: the selection scratch (whole
+// 256-byte blocks), then each wavefront's row list (64 E entries: a row
+// offset and BT coefficients each); the reduction rows reuse the front once
+// the stream is done.
 template <int BT>
 __host__ __device__ constexpr int64_t uc_sel_words() {
     return ((int64_t)sizeof(rowsel::Sel15Lds<BT, kUcNT / 64>) / 4 + 63) / 64 * 64;
@@ -688,6 +708,11 @@ template <int BT, int E, bool DUAL>
 __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
     constexpr int U = uc_unroll<BT, DUAL>();
     constexpr int NM = DUAL ? 2 : 1;
+    // One token of the plain squared-ReLU form (or the linear): every
+    // wavefront lists and streams its own rows.  Several tokens or the
+    // gated pair: one workgroup-wide row list, streamed by all 64 row slots
+    // in whole stages (measured faster for their longer lists).
+    constexpr bool kWaveLists = BT == 1 && !DUAL;
     constexpr int NW = kUcNT / 64;
     // All LDS is dynamic, from offset 0 (tables behind static variables ran
     // markedly slower): the selection scratch or the row list, later the
@@ -792,6 +817,7 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
             }
         };
         rowsel::select15_masks<kUcNT, BT, E>(key, (int)ntok, a.k, L, tid, selm, prefetch);
+        if constexpr (!kWaveLists) rowsel::lds_barrier();   // the selection scratch becomes the row list
 #pragma unroll
         for (int t = 0; t < BT; ++t)
 #pragma unroll
@@ -799,41 +825,6 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
                 xv[t][e] = (selm[t] >> e) & 1u ? __uint_as_float((xr16[t][e / 2] >> (16 * (e % 2))) << 16) : 0.0f;
     }
 
-    // Phase 2: the union of the selections over this wavefront's run of the
-    // row (entries 64 E wave .. 64 E wave + 64 E - 1) as an ascending row list
-    // in its own LDS segment, with each token's coefficient (0 where the
-    // token does not select the row).
-    constexpr int kWCap = 64 * E;
-    uint32_t* w_off = reinterpret_cast<uint32_t*>(smem + uc_sel_words<BT>()) + wave * kWCap;
-    float* w_coef = smem + uc_sel_words<BT>() + NW * kWCap + wave * kWCap * BT;
-    uint32_t um = 0;
-#pragma unroll
-    for (int t = 0; t < BT; ++t) um |= selm[t];
-    const uint32_t ucnt = (uint32_t)__popc(um);
-    const uint32_t uincl = sel::wave_incl_scan_dpp(ucnt);
-    const int n = __builtin_amdgcn_readlane((int)uincl, 63);
-    uint32_t pos = uincl - ucnt;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        if (um & (1u << e)) {
-            w_off[pos] = (uint32_t)(tid * E + e) * rowbytes;
-#pragma unroll
-            for (int t = 0; t < BT; ++t) w_coef[pos * BT + t] = xv[t][e];
-            ++pos;
-        }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // Phase 3: stream the 128-byte segments of the listed rows, one stage
-    // ahead: wavefront load li covers list entries 8 li .. 8 li + 7 (lane / 8
-    // picks the row).
-    const int rsub = lane / kUcLPR;
-    const int64_t col = (int64_t)tile * kUcCols + (lane % kUcLPR) * 8;
-    const uint32_t colb = col < ffn ? (uint32_t)(col * 2) : kOOB;
-    const int nld = (n + kUcLPR - 1) / kUcLPR;
-    const int nst = (nld + U - 1) / U;
     float acc[NM][BT][8];
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -841,52 +832,163 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
         for (int t = 0; t < BT; ++t)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[m][t][e] = 0.0f;
-    u32x4 bufa[NM][U], bufb[NM][U];
-    auto load_stage = [&](u32x4 (*dst)[U], int st) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int li = st * U + u;
-            if (li < nld) {   // uniform
-                const int r = li * kUcLPR + rsub;
-                const uint32_t off = (r < n ? w_off[r] : kOOB) + colb;
+    if constexpr (kWaveLists) {
+        // Phase 2: the union of the selections over this wavefront's run of the
+        // row (entries 64 E wave .. 64 E wave + 64 E - 1) as an ascending row list
+        // in its own LDS segment, with each token's coefficient (0 where the
+        // token does not select the row).
+        constexpr int kWCap = 64 * E;
+        uint32_t* w_off = reinterpret_cast<uint32_t*>(smem + uc_sel_words<BT>()) + wave * kWCap;
+        float* w_coef = smem + uc_sel_words<BT>() + NW * kWCap + wave * kWCap * BT;
+        uint32_t um = 0;
+    #pragma unroll
+        for (int t = 0; t < BT; ++t) um |= selm[t];
+        const uint32_t ucnt = (uint32_t)__popc(um);
+        const uint32_t uincl = sel::wave_incl_scan_dpp(ucnt);
+        const int n = __builtin_amdgcn_readlane((int)uincl, 63);
+        uint32_t pos = uincl - ucnt;
+    #pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (um & (1u << e)) {
+                w_off[pos] = (uint32_t)(tid * E + e) * rowbytes;
+    #pragma unroll
+                for (int t = 0; t < BT; ++t) w_coef[pos * BT + t] = xv[t][e];
+                ++pos;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // Phase 3: stream the 128-byte segments of the listed rows, one stage
+        // ahead: wavefront load li covers list entries 8 li .. 8 li + 7 (lane / 8
+        // picks the row).
+        const int rsub = lane / kUcLPR;
+        const int64_t col = (int64_t)tile * kUcCols + (lane % kUcLPR) * 8;
+        const uint32_t colb = col < ffn ? (uint32_t)(col * 2) : kOOB;
+        const int nld = (n + kUcLPR - 1) / kUcLPR;
+        const int nst = (nld + U - 1) / U;
+        u32x4 bufa[NM][U], bufb[NM][U];
+        auto load_stage = [&](u32x4 (*dst)[U], int st) {
+    #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int li = st * U + u;
+                if (li < nld) {   // uniform
+                    const int r = li * kUcLPR + rsub;
+                    const uint32_t off = (r < n ? w_off[r] : kOOB) + colb;
+                    dst[0][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+                    if constexpr (DUAL) dst[1][u] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off, 0, 0);
+                }
+            }
+        };
+        auto fma_stage = [&](const u32x4 (*src)[U], int st) {
+    #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int li = st * U + u;
+                if (li < nld) {   // uniform
+                    const int r = li * kUcLPR + rsub;
+                    float cf[BT];
+    #pragma unroll
+                    for (int t = 0; t < BT; ++t) cf[t] = r < n ? w_coef[r * BT + t] : 0.0f;
+    #pragma unroll
+                    for (int m = 0; m < NM; ++m) {
+                        float w[8];
+                        unpack<1>(src[m][u], w);
+    #pragma unroll
+                        for (int t = 0; t < BT; ++t)
+    #pragma unroll
+                            for (int e = 0; e < 8; ++e) acc[m][t][e] = fmaf(cf[t], w[e], acc[m][t][e]);
+                    }
+                }
+            }
+        };
+        load_stage(bufa, 0);
+        load_stage(bufb, 1);
+        for (int st = 0; st < nst; st += 2) {   // uniform
+            __builtin_amdgcn_sched_barrier(0);
+            fma_stage(bufa, st);
+            __builtin_amdgcn_sched_barrier(0);
+            if (st + 2 < nst) load_stage(bufa, st + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            if (st + 1 < nst) fma_stage(bufb, st + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (st + 3 < nst) load_stage(bufb, st + 3);
+        }
+    } else {
+        // Phase 2: the union of the selections as an ascending row list with each
+        // token's coefficient (0 where the token does not select the row).
+        constexpr int BATCH = kUcSlots * U;
+        uint32_t* s_wsum = reinterpret_cast<uint32_t*>(smem + uc_lds_tail<BT, DUAL>(a.d));   // [16]
+        const int64_t cap = uc_list_cap(d, U);
+        uint32_t* s_off = reinterpret_cast<uint32_t*>(smem);
+        float* s_coef = smem + cap;
+        uint32_t um = 0;
+    #pragma unroll
+        for (int t = 0; t < BT; ++t) um |= selm[t];
+        uint32_t nsel;
+        uint32_t pos = rowsel::block_excl_scan<kUcNT, true>((uint32_t)__popc(um), s_wsum, tid, nsel);
+    #pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (um & (1u << e)) {
+                s_off[pos] = (uint32_t)(tid * E + e) * rowbytes;
+    #pragma unroll
+                for (int t = 0; t < BT; ++t) s_coef[pos * BT + t] = xv[t][e];   // 0 off the token's selection
+                ++pos;
+            }
+        }
+        const int nbatch = (int)((nsel + BATCH - 1) / BATCH);
+        const int npad = ((nbatch + 1) / 2 * 2 + 1) * BATCH;
+        for (int i = (int)nsel + tid; i < npad; i += kUcNT) {
+            s_off[i] = kOOB;
+    #pragma unroll
+            for (int t = 0; t < BT; ++t) s_coef[i * BT + t] = 0.0f;
+        }
+        rowsel::lds_barrier();
+
+        // Phase 3: stream the 128-byte segments of the selected rows.
+        const int slot = tid / kUcLPR;
+        const int64_t col = (int64_t)tile * kUcCols + (lane % kUcLPR) * 8;
+        const uint32_t colb = col < ffn ? (uint32_t)(col * 2) : kOOB;
+        u32x4 bufa[NM][U], bufb[NM][U];
+        auto load_stage = [&](u32x4 (*dst)[U], int bi) {
+    #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t off = s_off[bi * BATCH + u * kUcSlots + slot] + colb;
                 dst[0][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
                 if constexpr (DUAL) dst[1][u] = __builtin_amdgcn_raw_buffer_load_b128(rs2, off, 0, 0);
             }
-        }
-    };
-    auto fma_stage = [&](const u32x4 (*src)[U], int st) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int li = st * U + u;
-            if (li < nld) {   // uniform
-                const int r = li * kUcLPR + rsub;
+        };
+        auto fma_stage = [&](const u32x4 (*src)[U], int bi) {
+    #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int ai = bi * BATCH + u * kUcSlots + slot;
                 float cf[BT];
-#pragma unroll
-                for (int t = 0; t < BT; ++t) cf[t] = r < n ? w_coef[r * BT + t] : 0.0f;
-#pragma unroll
+    #pragma unroll
+                for (int t = 0; t < BT; ++t) cf[t] = s_coef[ai * BT + t];
+    #pragma unroll
                 for (int m = 0; m < NM; ++m) {
                     float w[8];
                     unpack<1>(src[m][u], w);
-#pragma unroll
+    #pragma unroll
                     for (int t = 0; t < BT; ++t)
-#pragma unroll
+    #pragma unroll
                         for (int e = 0; e < 8; ++e) acc[m][t][e] = fmaf(cf[t], w[e], acc[m][t][e]);
                 }
             }
+        };
+        load_stage(bufa, 0);
+        for (int bi = 0; bi < nbatch; bi += 2) {
+            load_stage(bufb, bi + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            fma_stage(bufa, bi);
+            __builtin_amdgcn_sched_barrier(0);
+            load_stage(bufa, bi + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            fma_stage(bufb, bi + 1);
+            __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    load_stage(bufa, 0);
-    load_stage(bufb, 1);
-    for (int st = 0; st < nst; st += 2) {   // uniform
-        __builtin_amdgcn_sched_barrier(0);
-        fma_stage(bufa, st);
-        __builtin_amdgcn_sched_barrier(0);
-        if (st + 2 < nst) load_stage(bufa, st + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        if (st + 1 < nst) fma_stage(bufb, st + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (st + 3 < nst) load_stage(bufb, st + 3);
     }
+
     // (the touched lines' values are not needed: an empty asm consumes them)
 #pragma unroll
     for (int m = 0; m < NM; ++m)
@@ -2394,12 +2496,17 @@ bool up_cols_supported(int64_t rows, int64_t d, int64_t ffn) {
     if (!(rows >= 1 && rows <= 4 && d % 8 == 0 && d <= kUpColsMaxD && ffn % 8 == 0 &&
           ffn <= kUpColsMaxFfn))
         return false;
-    // The wavefronts' row lists must fit in the 160 KiB of LDS (for a tile
-    // of four tokens: d <= 4096).
+    // The row lists must fit in the 160 KiB of LDS (for a tile of four
+    // tokens: d <= 4096).
     const bool e8 = d <= 8 * kUcNT;
-    const int64_t words = rows == 1 ? (e8 ? uc_lds_words<1, 8, true>() : uc_lds_words<1, 16, true>())
-                          : rows == 2 ? (e8 ? uc_lds_words<2, 8, true>() : uc_lds_words<2, 16, true>())
-                                      : (e8 ? uc_lds_words<4, 8, true>() : uc_lds_words<4, 16, true>());
+    int64_t words = 0;
+    if (rows == 1) {
+        const int64_t w1 = e8 ? uc_lds_words<1, 8, false>() : uc_lds_words<1, 16, false>();
+        const int64_t w2 = uc_lds_tail<1, true>(d) + 16;
+        words = w1 > w2 ? w1 : w2;
+    } else {
+        words = rows == 2 ? uc_lds_tail<2, true>(d) + 16 : uc_lds_tail<4, true>(d) + 16;
+    }
     return words * 4 <= 160 * 1024;
 }
 
@@ -2418,7 +2525,8 @@ hipError_t launch_up_cols(const UpColsArgs& a, hipStream_t stream) {
     const bool dual = a.w2 != nullptr;
 #define QS_UC_CASE(BTV, EV, DU)                                                          \
     if (bt == BTV && e == EV && dual == DU) {                                            \
-        const size_t lds = (size_t)uc_lds_words<BTV, EV, DU>() * 4;                      \
+        const size_t lds = (size_t)(BTV == 1 && !DU ? uc_lds_words<BTV, EV, DU>()       \
+                                                    : uc_lds_tail<BTV, DU>(a.d) + 16) * 4; \
         up_cols_kernel<BTV, EV, DU><<<grid, dim3(kUcNT), lds, stream>>>(a);              \
         return hipGetLastError();                                                        \
     }
