@@ -8,7 +8,10 @@ One step is one call of qs_sparse_ffn over one batch: the top-K of x and the
 up projection over the selected rows of W_up^T with the squared-ReLU
 epilogue, then the top-K of the intermediate and the down projection over
 the rows of W_down^T it selects (at one token two launches, each selecting
-inside its workgroups).
+inside its workgroups).  At one token the weight rows are padded by 64 bf16
+(--row-pad; config.weight_row_pitch): with the natural 1 KiB-multiple pitch
+the row segments of some column tiles share a subset of the memory channels
+and those tiles finish last; the kernels read the same bytes either way.
 
 Other workloads (--workload): c1 (fp32 1024x1024 linear, 8 tokens), c2g (the
 same Llama-7B FFN with a gate: gated squared ReLU), c3
@@ -75,6 +78,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--roofline-launches", type=int, default=96)
+    p.add_argument("--row-pad", type=int, default=64,
+                   help="c2, one token: bf16 columns of padding per weight row (0: natural rows)")
     p.add_argument("--weight-copies", type=int, default=0,
                    help="weight copies to rotate over (0: the workload's default)")
     p.add_argument("--replays", type=int, default=50,
@@ -194,10 +199,24 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     # reads only the selected rows (72 MB at one token), so 16 copies put
     # 15 x 72 MB = 1.08 GB between visits.
     n_copies = args.weight_copies or C2_COPIES
+    # One token: the rows of W_up^T and W_down^T are padded by --row-pad bf16
+    # (64: an odd multiple of 128 bytes), so that no column tile's row
+    # segments sit at one offset modulo 1 KiB on a subset of the memory
+    # channels; the kernels read the same bytes.  More tokens: natural rows.
+    pad = args.row_pad if B == 1 else 0
     wup0 = bf16_dev(torch, np, c["W_up"].T, dev)
     wdn0 = bf16_dev(torch, np, c["W_down"].T, dev)
-    wups = [wup0] + [wup0.clone() for _ in range(n_copies - 1)]
-    wdns = [wdn0] + [wdn0.clone() for _ in range(n_copies - 1)]
+
+    def padded_copy(src):
+        base = torch.zeros((src.shape[0], src.shape[1] + pad), dtype=src.dtype, device=dev)
+        base[:, :src.shape[1]] = src
+        return base
+
+    up_bases = [padded_copy(wup0) for _ in range(n_copies)]
+    dn_bases = [padded_copy(wdn0) for _ in range(n_copies)]
+    del wup0, wdn0
+    wups = [b[:, :ffn] for b in up_bases]
+    wdns = [b[:, :d] for b in dn_bases]
     xs = [bf16_dev(torch, np, datagen.c2_relu2_ffn(B, rotation=i, with_weights=False)["X"], dev)
           for i in range(N_XROT)]
     y = torch.empty((B, d), dtype=torch.float32, device=dev)
@@ -296,7 +315,7 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
 
     # ceiling reference: a plain streaming read of the same bytes per launch,
     # rotating over chunks of the weight copies (> 256 MB, so not from the MALL)
-    flat = [t.view(-1).view(torch.uint8) for t in wups + wdns]
+    flat = [t.view(-1).view(torch.uint8) for t in up_bases + dn_bases]
     nb = min(int(bytes_launch), min(f.numel() for f in flat)) // 16 * 16
     chunks = [f[o:o + nb] for f in flat for o in range(0, f.numel() - nb + 1, nb)]
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -323,6 +342,7 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
         "ms_per_step": round(ms_step, 6), "dtype": "bf16",
         "config": {"workload": "llama7b_relu2_ffn_decode", "batch": B, "d": d, "ffn": ffn,
                    "k_in": k_in, "k_mid": k_mid, "weights": "bf16",
+                   "weight_row_pad": pad, "weight_row_pitch": {"w_up_t": ffn + pad, "w_down_t": d + pad},
                    "weight_copies": n_copies, "x_rotations": N_XROT},
         "hbm_gbps_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "union_rows_up": un1, "union_rows_down": un2,

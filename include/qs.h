@@ -186,6 +186,29 @@ qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_i
                            void* y, qs_dtype yt, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * qs_sparse_linear_pitched -- qs_sparse_linear with the row pitch of the
+ * weights given  [QS-TopK], [QS-Adv].
+ *
+ *   ldw     elements from one row of w to the next: the natural pitch (n_out
+ *           for QS_LAYOUT_WT, d_in for QS_LAYOUT_W) gives qs_sparse_linear.
+ *           Any other pitch needs QS_LAYOUT_WT, ldw >= n_out and a multiple of
+ *           8, and the single-launch path (one bf16 token, bf16 W^T, d_in <=
+ *           8192, n_out <= 16384); QS_ERR_INVALID_ARG or QS_ERR_UNSUPPORTED
+ *           otherwise, before anything is enqueued.  The padding columns are
+ *           never read.
+ *   Why: every workgroup of the gather reads one 128-byte column segment of
+ *   each selected row; with a pitch that is a multiple of 1 KiB those
+ *   segments sit at the same address offsets in every row and some tiles'
+ *   lines pile onto a subset of the memory channels, so their workgroups
+ *   finish last.  Rows padded by 64 bf16 (an odd multiple of 128 bytes)
+ *   spread every tile over all channels.
+ */
+qs_status qs_sparse_linear_pitched(const void* x, qs_dtype xt, int64_t rows, int64_t d_in,
+                                   int64_t k, const void* w, int64_t ldw, qs_dtype wt_t,
+                                   qs_layout w_layout, int64_t n_out, void* y, qs_dtype yt,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
  * qs_gather_linear -- Y = Xs . W^T for an already sparsified Xs (for example
  * the xs output of qs_topk_mask), reading only the rows of W^T whose input
  * feature is nonzero for some row of Xs  [QS-TopK], [QS-Adv].
@@ -237,15 +260,18 @@ qs_status qs_gather_linear_acc(const float* xs, int64_t rows, int64_t d_in, cons
  *
  *   x       device fp32 [rows, d_in] (not sparsified).
  *   k       0 <= k <= d_in.
- *   wt      device bf16 W^T [d_in, n_out].
+ *   wt      device bf16 W^T [d_in, n_out], rows ldw elements apart.
+ *   ldw     n_out, or a larger multiple of 8 (padded rows: see
+ *           qs_sparse_linear_pitched); QS_ERR_INVALID_ARG otherwise.
  *   y       device fp32 [rows, n_out], read and written.
  *   Arithmetic: fp32 products and sums (the fp32 tolerance).
  *   Limits: d_in % 4 == 0, d_in <= 16384, n_out % 8 == 0, rows <= 65535,
- *   W^T smaller than 1 GiB; QS_ERR_UNSUPPORTED otherwise.  No workspace.
+ *   W^T (d_in x ldw) smaller than 1 GiB; QS_ERR_UNSUPPORTED otherwise.  No
+ *   workspace.
  */
 qs_status qs_topk_gather_linear_acc(const float* x, int64_t rows, int64_t d_in, int64_t k,
-                                    const void* wt, qs_dtype wt_t, int64_t n_out, float* y,
-                                    void* stream);
+                                    const void* wt, qs_dtype wt_t, int64_t n_out, int64_t ldw,
+                                    float* y, void* stream);
 
 /*
  * qs_set_deterministic -- process-wide choice of the split-K summation (see
@@ -327,6 +353,30 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
                         const float* b_gate, const float* b_up,
                         void* y, qs_dtype yt, float* h, int32_t* mid_idx, int32_t* mid_cnt,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qs_sparse_ffn_pitched -- qs_sparse_ffn with the row pitches of W_up^T (and
+ * W_gate^T) and W_down^T given  [QS-TopK], [TS-Eq3-4].
+ *
+ *   ld_up    elements from one row of w_up (and of w_gate) to the next, at
+ *            least the row length (ffn for W_up^T, d for dReLU's W_up), a
+ *            multiple of 8.
+ *   ld_down  elements from one row of W_down^T to the next, >= d, a multiple
+ *            of 8.
+ *   The natural pitches give qs_sparse_ffn.  Other pitches need the
+ *   one-token path of the squared-ReLU kinds (QS_ACT_RELU2 or
+ *   QS_ACT_RELU2_GLU, rows == 1, bf16 x and weights, k_mid >= 0, mid_idx
+ *   and mid_cnt NULL, shapes of the single-launch up projection); otherwise
+ *   QS_ERR_UNSUPPORTED before anything is enqueued.  Padding columns are never
+ *   read.  Rows padded by 64 bf16 keep each column tile's lines off a single
+ *   subset of the memory channels (see qs_sparse_linear_pitched).
+ */
+qs_status qs_sparse_ffn_pitched(const void* x, qs_dtype dt, int64_t rows, int64_t d, int64_t ffn,
+                                qs_act act, int64_t k_in, int64_t k_mid, const void* w_gate,
+                                const void* w_up, int64_t ld_up, const void* w_down_t,
+                                int64_t ld_down, const float* b_gate, const float* b_up,
+                                void* y, qs_dtype yt, float* h, int32_t* mid_idx,
+                                int32_t* mid_cnt, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * qs_sparse_ffn_static -- qs_sparse_ffn without a workspace argument, for

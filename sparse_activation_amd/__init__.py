@@ -23,7 +23,7 @@ __all__ = [
     "OP_SPARSE_LINEAR_BACKWARD", "qs_sparse_linear_backward", "OP_BLOCK_SPARSE_LINEAR",
     "qs_block_sparse_linear", "OP_SPARSE_MOE_FFN", "qs_sparse_moe_ffn",
     "qs_gather_linear_acc", "qs_topk_gather_linear_acc", "qs_set_deterministic",
-    "qs_sparse_ffn_static",
+    "qs_sparse_ffn_static", "qs_sparse_linear_pitched", "qs_sparse_ffn_pitched",
     "STATIC_SCRATCH_BYTES",
 ]
 
@@ -46,10 +46,12 @@ _SIGS = {
     "qs_topk_mask": [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P],
     "qs_gather_linear": [_P, _I64, _I64, _P, _INT, _I64, _P, _INT, _P, ctypes.c_size_t, _P],
     "qs_gather_linear_acc": [_P, _I64, _I64, _P, _INT, _I64, _P, _P, ctypes.c_size_t, _P],
-    "qs_topk_gather_linear_acc": [_P, _I64, _I64, _I64, _P, _INT, _I64, _P, _P],
+    "qs_topk_gather_linear_acc": [_P, _I64, _I64, _I64, _P, _INT, _I64, _I64, _P, _P],
     "qs_set_deterministic": [_INT],
     "qs_sparse_linear": [_P, _INT, _I64, _I64, _I64, _P, _INT, _INT, _I64, _P, _INT, _P,
                          ctypes.c_size_t, _P],
+    "qs_sparse_linear_pitched": [_P, _INT, _I64, _I64, _I64, _P, _I64, _INT, _INT, _I64, _P,
+                                 _INT, _P, ctypes.c_size_t, _P],
     "qs_sparse_linear_backward": [_P, _INT, _I64, _I64, _I64, _P, _INT, _INT, _I64, _P, _INT,
                                   _P, _INT, _P, _INT, _P, ctypes.c_size_t, _P],
     "qs_block_sparse_linear": [_P, _INT, _I64, _I64, _P, _INT, _I64, _P, _INT, _P, _P,
@@ -60,6 +62,8 @@ _SIGS = {
                              _P, _P, ctypes.c_size_t, _P],
     "qs_sparse_ffn": [_P, _INT, _I64, _I64, _I64, _INT, _I64, _I64, _P, _P, _P, _P, _P, _P,
                       _INT, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "qs_sparse_ffn_pitched": [_P, _INT, _I64, _I64, _I64, _INT, _I64, _I64, _P, _P, _I64, _P,
+                              _I64, _P, _P, _P, _INT, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "qs_sparse_ffn_static": [_P, _INT, _I64, _I64, _I64, _INT, _I64, _I64, _P, _P, _P, _P, _P,
                              _P, _INT, _P, _P, _P, _P],
     "qs_workspace_bytes": [_INT, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
@@ -136,14 +140,20 @@ def _torch_dtype(code: int):
     return {F32: torch.float32, BF16: torch.bfloat16, I8: torch.int8}[code]
 
 
-def _dev(*ts):
+def _dev(*ts, strided=()):
+    """The common device of the tensors; each must be contiguous, except those
+    also listed in `strided` (weights whose row pitch the caller passes on),
+    which need contiguous rows."""
     dev = None
     for t in ts:
         if t is None:
             continue
         if not t.is_cuda:
             raise ValueError("all tensors must be on the GPU")
-        if not t.is_contiguous():
+        if any(t is s for s in strided):
+            if t.dim() != 2 or t.stride(1) != 1 or t.stride(0) < t.shape[1]:
+                raise ValueError("weights must be 2-D with contiguous rows")
+        elif not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
         if dev is None:
             dev = t.device
@@ -154,6 +164,14 @@ def _dev(*ts):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _row_pitch(t, name: str) -> int:
+    """Elements from one row of the 2-D tensor `t` to the next; its rows must
+    be contiguous (a column slice of a wider tensor gives a padded pitch)."""
+    if t.dim() != 2 or t.stride(1) != 1 or t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    return int(t.stride(0))
 
 
 def _stream(dev):
@@ -265,9 +283,10 @@ def qs_topk_gather_linear_acc(x, k: int, wt, y):
     n_out = wt.shape[1]
     if tuple(y.shape) != (rows, n_out):
         raise ValueError("y must be [rows, n_out]")
-    dev = _dev(x, wt, y)
+    dev = _dev(x, wt, y, strided=(wt,))
+    ldw = _row_pitch(wt, "wt")
     _check(load().qs_topk_gather_linear_acc(_ptr(x), rows, d_in, k, _ptr(wt), _dtype_code(wt),
-                                            n_out, _ptr(y), _stream(dev)))
+                                            n_out, ldw, _ptr(y), _stream(dev)))
     return y
 
 
@@ -286,14 +305,28 @@ def qs_sparse_linear(x, k: int, w, layout: int = LAYOUT_WT, y=None, y_dtype=None
     d_w = w.shape[0] if layout == LAYOUT_WT else w.shape[1]
     if d_w != d_in:
         raise ValueError("weight shape does not match x")
-    dev = _dev(x, w, y, ws)
+    dev = _dev(x, w, y, ws, strided=(w,) if layout == LAYOUT_WT else ())
+    ldw = _row_pitch(w, "w")
+    natural = n_out if layout == LAYOUT_WT else d_in
     if y is None:
         y = torch.empty((rows, n_out), dtype=y_dtype or torch.float32, device=dev)
     ws, ws_bytes = _workspace(ws, OP_SPARSE_LINEAR, rows, d_in, n_out, dev)
-    _check(load().qs_sparse_linear(_ptr(x), _dtype_code(x), rows, d_in, k, _ptr(w),
-                                   _dtype_code(w), layout, n_out, _ptr(y), _dtype_code(y),
-                                   _ptr(ws), ws_bytes, _stream(dev)))
+    if ldw == natural:
+        _check(load().qs_sparse_linear(_ptr(x), _dtype_code(x), rows, d_in, k, _ptr(w),
+                                       _dtype_code(w), layout, n_out, _ptr(y), _dtype_code(y),
+                                       _ptr(ws), ws_bytes, _stream(dev)))
+    else:
+        _check(load().qs_sparse_linear_pitched(_ptr(x), _dtype_code(x), rows, d_in, k, _ptr(w),
+                                               ldw, _dtype_code(w), layout, n_out, _ptr(y),
+                                               _dtype_code(y), _ptr(ws), ws_bytes, _stream(dev)))
     return y
+
+
+def qs_sparse_linear_pitched(x, k: int, w, layout: int = LAYOUT_WT, y=None, y_dtype=None,
+                             ws=None):
+    """qs_sparse_linear; the row pitch of `w` is taken from its strides (a
+    column slice of a wider tensor is a padded W^T)."""
+    return qs_sparse_linear(x, k, w, layout, y=y, y_dtype=y_dtype, ws=ws)
 
 
 def qs_sparse_linear_backward(x, k: int, w, dy, layout: int = LAYOUT_W, want_dx=True,
@@ -406,7 +439,8 @@ def qs_sparse_ffn(x, act: int, k_in: int, k_mid: int, w_up, w_down_t, w_gate=Non
     torch = _torch()
     rows, d = x.shape
     ffn = w_down_t.shape[0]
-    dev = _dev(x, w_up, w_down_t, w_gate, b_gate, b_up, y, h, mid_idx, mid_cnt, ws)
+    dev = _dev(x, w_up, w_down_t, w_gate, b_gate, b_up, y, h, mid_idx, mid_cnt, ws,
+               strided=(w_up, w_down_t, w_gate))
     if y is None:
         y = torch.empty((rows, d), dtype=y_dtype or torch.float32, device=dev)
     if want_h and h is None:
@@ -418,11 +452,26 @@ def qs_sparse_ffn(x, act: int, k_in: int, k_mid: int, w_up, w_down_t, w_gate=Non
     op = {ACT_RELU2: OP_SPARSE_FFN_RELU2, ACT_DRELU: OP_SPARSE_FFN_DRELU,
           ACT_RELU2_GLU: OP_SPARSE_FFN_RELU2_GLU}.get(act, OP_SPARSE_FFN_RELU2)
     ws, ws_bytes = _workspace(ws, op, rows, d, ffn, dev)
-    _check(load().qs_sparse_ffn(_ptr(x), _dtype_code(x), rows, d, ffn, act, k_in, k_mid,
-                                _ptr(w_gate), _ptr(w_up), _ptr(w_down_t), _ptr(b_gate),
-                                _ptr(b_up), _ptr(y), _dtype_code(y), _ptr(h), _ptr(mid_idx),
-                                _ptr(mid_cnt), _ptr(ws), ws_bytes, _stream(dev)))
+    ld_up, ld_down = _row_pitch(w_up, "w_up"), _row_pitch(w_down_t, "w_down_t")
+    if w_gate is not None and _row_pitch(w_gate, "w_gate") != ld_up:
+        raise ValueError("w_gate and w_up must have the same row pitch")
+    if (ld_up, ld_down) == (d if act == ACT_DRELU else ffn, d):
+        _check(load().qs_sparse_ffn(_ptr(x), _dtype_code(x), rows, d, ffn, act, k_in, k_mid,
+                                    _ptr(w_gate), _ptr(w_up), _ptr(w_down_t), _ptr(b_gate),
+                                    _ptr(b_up), _ptr(y), _dtype_code(y), _ptr(h), _ptr(mid_idx),
+                                    _ptr(mid_cnt), _ptr(ws), ws_bytes, _stream(dev)))
+    else:
+        _check(load().qs_sparse_ffn_pitched(
+            _ptr(x), _dtype_code(x), rows, d, ffn, act, k_in, k_mid, _ptr(w_gate), _ptr(w_up),
+            ld_up, _ptr(w_down_t), ld_down, _ptr(b_gate), _ptr(b_up), _ptr(y), _dtype_code(y),
+            _ptr(h), _ptr(mid_idx), _ptr(mid_cnt), _ptr(ws), ws_bytes, _stream(dev)))
     return y, h, mid_idx, mid_cnt
+
+
+def qs_sparse_ffn_pitched(x, act: int, k_in: int, k_mid: int, w_up, w_down_t, **kw):
+    """qs_sparse_ffn; the row pitches of the weights are taken from their
+    strides (column slices of wider tensors are padded rows)."""
+    return qs_sparse_ffn(x, act, k_in, k_mid, w_up, w_down_t, **kw)
 
 
 def qs_sparse_ffn_static(x, act: int, k_in: int, k_mid: int, w_up, w_down_t, w_gate=None,
@@ -442,6 +491,10 @@ def qs_sparse_ffn_static(x, act: int, k_in: int, k_mid: int, w_up, w_down_t, w_g
         mid_idx = torch.empty((rows, ffn), dtype=torch.int32, device=dev)
     if want_mid and mid_cnt is None:
         mid_cnt = torch.empty(rows, dtype=torch.int32, device=dev)
+    up_len = d if act == ACT_DRELU else ffn
+    if (_row_pitch(w_up, "w_up"), _row_pitch(w_down_t, "w_down_t")) != (up_len, d) or (
+            w_gate is not None and _row_pitch(w_gate, "w_gate") != up_len):
+        raise ValueError("qs_sparse_ffn_static takes unpadded weights")
     _check(load().qs_sparse_ffn_static(_ptr(x), _dtype_code(x), rows, d, ffn, act, k_in, k_mid,
                                        _ptr(w_gate), _ptr(w_up), _ptr(w_down_t), _ptr(b_gate),
                                        _ptr(b_up), _ptr(y), _dtype_code(y), _ptr(h),

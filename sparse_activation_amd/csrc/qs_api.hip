@@ -310,6 +310,14 @@ qs_status qs_topk_mask(const void* x, qs_dtype xt, int64_t rows, int64_t d, int6
 qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_in, int64_t k,
                            const void* w, qs_dtype wt_t, qs_layout w_layout, int64_t n_out,
                            void* y, qs_dtype yt, void* ws, size_t ws_bytes, void* stream) {
+    return qs_sparse_linear_pitched(x, xt, rows, d_in, k, w, w_layout == QS_LAYOUT_W ? d_in : n_out,
+                                    wt_t, w_layout, n_out, y, yt, ws, ws_bytes, stream);
+}
+
+qs_status qs_sparse_linear_pitched(const void* x, qs_dtype xt, int64_t rows, int64_t d_in,
+                                   int64_t k, const void* w, int64_t ldw, qs_dtype wt_t,
+                                   qs_layout w_layout, int64_t n_out, void* y, qs_dtype yt,
+                                   void* ws, size_t ws_bytes, void* stream) {
     const char* fn = "qs_sparse_linear";
     if (rows < 0 || d_in <= 0 || n_out <= 0 || d_in > (int64_t(1) << 24))
         return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
@@ -319,6 +327,19 @@ qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_i
     if (w_layout != QS_LAYOUT_WT && w_layout != QS_LAYOUT_W)
         return fail(QS_ERR_INVALID_ARG, "%s: unknown weight layout", fn);
     if (rows > 0x7FFFFFFF) return fail(QS_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    // The row pitch of the weights: the natural one, or (W^T, one bf16 token
+    // with bf16 weights: the single-launch path) at least n_out, a multiple of 8.
+    const bool pitched = ldw != (w_layout == QS_LAYOUT_W ? d_in : n_out);
+    if (pitched) {
+        if (w_layout != QS_LAYOUT_WT || ldw < n_out || ldw % 8 != 0)
+            return fail(QS_ERR_INVALID_ARG, "%s: need ldw >= n_out, a multiple of 8, with QS_LAYOUT_WT", fn);
+        if (!(rows <= 1 && xt == QS_BF16 && wt_t == QS_BF16 && qs::up_cols_supported(1, d_in, n_out)))
+            return fail(QS_ERR_UNSUPPORTED,
+                        "%s: a row pitch other than n_out needs one bf16 token, bf16 W^T, "
+                        "d_in <= 8192 and n_out <= 16384", fn);
+        if (d_in * ldw * 2 >= qs::kMaxGatherWeightBytes)
+            return fail(QS_ERR_UNSUPPORTED, "%s: W^T must be smaller than 1 GiB", fn);
+    }
     if (w_layout == QS_LAYOUT_W) {
         if (xt != QS_BF16 || wt_t != QS_BF16)
             return fail(QS_ERR_UNSUPPORTED, "%s: QS_LAYOUT_W (MFMA path) needs bf16 x and w", fn);
@@ -363,7 +384,7 @@ qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_i
         // selected rows (fixed-order sums, no K split).
         qs::UpColsArgs u{};
         u.x = (const uint16_t*)x; u.rows = rows; u.d = d_in; u.ffn = n_out; u.k = k;
-        u.w = (const uint16_t*)w; u.linear = 1;
+        u.w = (const uint16_t*)w; u.linear = 1; u.w_ld = ldw;
         if (yt == QS_BF16) u.hb = (uint16_t*)y;
         else u.h = (float*)y;
         e = qs::launch_up_cols(u, st);
@@ -450,8 +471,8 @@ qs_status qs_gather_linear_acc(const float* xs, int64_t rows, int64_t d_in, cons
 }
 
 qs_status qs_topk_gather_linear_acc(const float* x, int64_t rows, int64_t d_in, int64_t k,
-                                    const void* wt, qs_dtype wt_t, int64_t n_out, float* y,
-                                    void* stream) {
+                                    const void* wt, qs_dtype wt_t, int64_t n_out, int64_t ldw,
+                                    float* y, void* stream) {
     const char* fn = "qs_topk_gather_linear_acc";
     if (rows < 0 || d_in <= 0 || n_out <= 0) return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
     if (k < 0 || k > d_in) return fail(QS_ERR_INVALID_ARG, "%s: need 0 <= k <= d_in", fn);
@@ -459,7 +480,9 @@ qs_status qs_topk_gather_linear_acc(const float* x, int64_t rows, int64_t d_in, 
     if (rows > 65535 || !qs::gather_sel_supported(rows == 0 ? 1 : rows, d_in, n_out))
         return fail(QS_ERR_UNSUPPORTED,
                     "%s: needs d_in %% 4 == 0, d_in <= 16384, n_out %% 8 == 0, rows <= 65535", fn);
-    if (d_in * n_out * 2 >= qs::kMaxGatherWeightBytes)
+    if (ldw < n_out || ldw % 8 != 0)
+        return fail(QS_ERR_INVALID_ARG, "%s: need ldw >= n_out, a multiple of 8", fn);
+    if (d_in * ldw * 2 >= qs::kMaxGatherWeightBytes)
         return fail(QS_ERR_UNSUPPORTED, "%s: W^T must be smaller than 1 GiB", fn);
     if (rows == 0) return ok();
     if (!x || !wt || !y) return fail(QS_ERR_INVALID_ARG, "%s: x, wt and y must be non-NULL", fn);
@@ -470,6 +493,7 @@ qs_status qs_topk_gather_linear_acc(const float* x, int64_t rows, int64_t d_in, 
     g.epilogue = qs::EPI_STORE;
     g.accumulate = 1;
     g.sel_k = k;
+    g.w_ld = ldw;
     hipError_t e = qs::launch_gather_sel(g, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, fn);
     return ok();
@@ -544,6 +568,18 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
                         const float* b_gate, const float* b_up,
                         void* y, qs_dtype yt, float* h, int32_t* mid_idx, int32_t* mid_cnt,
                         void* ws, size_t ws_bytes, void* stream) {
+    // (natural pitches: W_up^T / W_gate^T rows of ffn, dReLU's W_up / W_gate rows of d)
+    return qs_sparse_ffn_pitched(x, dt, rows, d, ffn, act, k_in, k_mid, w_gate, w_up,
+                                 act == QS_ACT_DRELU ? d : ffn, w_down_t, d, b_gate, b_up, y, yt,
+                                 h, mid_idx, mid_cnt, ws, ws_bytes, stream);
+}
+
+qs_status qs_sparse_ffn_pitched(const void* x, qs_dtype dt, int64_t rows, int64_t d, int64_t ffn,
+                                qs_act act, int64_t k_in, int64_t k_mid, const void* w_gate,
+                                const void* w_up, int64_t ld_up, const void* w_down_t,
+                                int64_t ld_down, const float* b_gate, const float* b_up,
+                                void* y, qs_dtype yt, float* h, int32_t* mid_idx,
+                                int32_t* mid_cnt, void* ws, size_t ws_bytes, void* stream) {
     const char* fn = "qs_sparse_ffn";
     if (rows < 0 || d <= 0 || ffn <= 0 || d > (int64_t(1) << 24) || ffn > (int64_t(1) << 24))
         return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
@@ -557,7 +593,16 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
         return fail(QS_ERR_UNSUPPORTED, "%s: dReLU path needs bf16 x and weights", fn);
     if (d % 8 != 0 || ffn % 8 != 0)
         return fail(QS_ERR_UNSUPPORTED, "%s: d and ffn must be multiples of 8", fn);
-    if (d * ffn * (dt == QS_BF16 ? 2 : 4) >= qs::kMaxGatherWeightBytes)
+    // Natural pitches: rows of W_up^T (and W_gate^T) hold ffn entries, rows
+    // of dReLU's W_up (and W_gate) d entries, rows of W_down^T d entries.
+    const int64_t up_len = act == QS_ACT_DRELU ? d : ffn;
+    const int64_t up_rows = act == QS_ACT_DRELU ? ffn : d;
+    if (ld_up < up_len || ld_down < d || ld_up % 8 != 0 || ld_down % 8 != 0)
+        return fail(QS_ERR_INVALID_ARG,
+                    "%s: need row pitches of at least the row lengths, multiples of 8", fn);
+    const bool pitched = ld_up != up_len || ld_down != d;
+    if (up_rows * ld_up * (dt == QS_BF16 ? 2 : 4) >= qs::kMaxGatherWeightBytes ||
+        ffn * ld_down * (dt == QS_BF16 ? 2 : 4) >= qs::kMaxGatherWeightBytes)
         return fail(QS_ERR_UNSUPPORTED, "%s: each weight matrix must be smaller than 1 GiB", fn);
     if (rows > 0x7FFFFFFF) return fail(QS_ERR_UNSUPPORTED, "%s: too many rows", fn);
     if (rows == 0) return ok();
@@ -581,6 +626,25 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
     const int kk = wb ? qs::KEY_BF16 : qs::KEY_F32;
     float* hbuf = h ? h : wsp.h;
     hipError_t e;
+    if (pitched) {
+        // Row pitches are honoured by the one-token path of the squared-ReLU
+        // kinds (two launches, each selecting inside); decided before
+        // anything is enqueued, with the conditions under which it is taken.
+        bool one_token = !drelu && wb && rows == 1 && k_mid >= 0 && !mid_idx && !mid_cnt &&
+                         qs::up_cols_supported(1, d, ffn) && qs::gather_sel_supported(1, ffn, d);
+        if (one_token) {
+            const qs::GemvPlan pdn = qs::plan_gemv(rows, ffn, d, wb);
+            int fs_tiles = 0, fs_split = 0, fs_cand = 0;
+            qs::gather_sel_plan(ffn, d, &fs_tiles, &fs_split, &fs_cand);
+            one_token = pdn.bt <= 8 && pdn.scratch_floats <= wsp.partial_cap &&
+                        (size_t)pdn.n_counters <= wsp.down_ctr_cap &&
+                        (size_t)fs_split * d <= wsp.partial_cap && (size_t)fs_tiles <= wsp.down_ctr_cap;
+        }
+        if (!one_token)
+            return fail(QS_ERR_UNSUPPORTED,
+                        "%s: row pitches other than (ffn, d) need one token of a squared-ReLU kind "
+                        "with bf16 weights, k_mid >= 0 and no mid_idx / mid_cnt", fn);
+    }
 
     // Small batches of the squared-ReLU kinds with bf16 weights.  The up
     // launch (for one token selecting the top-k_in of x in every workgroup,
@@ -596,6 +660,7 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
             const bool acc = !deterministic() && yt == QS_F32 && qs::gemv_accumulate_supported(pdn, wb);
             qs::UpColsArgs u{};
             u.x = (const uint16_t*)x; u.rows = rows; u.d = d; u.ffn = ffn; u.k = k_in;
+            u.w_ld = ld_up;   // (the natural ffn unless the one-token path was checked above)
             if (rows == 1) {
                 // One token: the up launch selects it itself and clears what
                 // the down gather needs cleared.
@@ -634,6 +699,7 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
                 g.epilogue = qs::EPI_STORE;
                 g.accumulate = acc ? 1 : 0;
                 g.sel_k = k_mid;
+                g.w_ld = ld_down;
                 e = qs::launch_gather_sel(g, st);
                 if (e != hipSuccess) return hip_fail(e, fn);
                 return ok();

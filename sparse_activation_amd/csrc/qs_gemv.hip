@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kFsNT) void gather_sel_kernel(GemvArgs a, int cand,
     const int64_t d_in = a.d_in, n_out = a.n_out;
     const int64_t j0 = (int64_t)split * cand;
     const int64_t j1 = min(d_in, j0 + (int64_t)cand);
-    const uint32_t rowbytes = (uint32_t)(n_out * 2);
+    const uint32_t rowbytes = (uint32_t)((a.w_ld > 0 ? a.w_ld : n_out) * 2);   // row pitch
 
     // The split's candidate coefficients (entry j0 + ch * 1024 + tid is chunk
     // ch of thread tid) and the whole row's keys, 4 entries per run.
@@ -744,7 +744,7 @@ __global__ __launch_bounds__(kUcNT) void up_cols_kernel(UpColsArgs a) {
     uint32_t selm[BT];
     float xv[BT][E];
     const int nvalid = (int)d - tid * E;
-    const uint32_t rowbytes = (uint32_t)(ffn * 2);
+    const uint32_t rowbytes = (uint32_t)((a.w_ld > 0 ? a.w_ld : ffn) * 2);   // row pitch
     const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, d * (int64_t)rowbytes);
     const __amdgpu_buffer_rsrc_t rs2 = weight_rsrc(DUAL ? a.w2 : a.w, d * (int64_t)rowbytes);
     uint32_t pf[NM][kUcPf];
@@ -2476,7 +2476,8 @@ void gather_sel_plan(int64_t d_in, int64_t n_out, int* n_tiles, int* nsplit, int
 
 hipError_t launch_gather_sel(const GemvArgs& a, hipStream_t stream) {
     if (!gather_sel_supported(a.rows, a.d_in, a.n_out) || a.sel_desc != nullptr ||
-        a.epilogue != EPI_STORE || (a.accumulate && a.y_bf16) || (!a.accumulate && a.rows != 1))
+        a.epilogue != EPI_STORE || (a.accumulate && a.y_bf16) || (!a.accumulate && a.rows != 1) ||
+        (a.w_ld != 0 && (a.w_ld < a.n_out || a.w_ld % 8 != 0)))
         return hipErrorInvalidValue;
     int nt, ns, cand;
     gather_sel_plan(a.d_in, a.n_out, &nt, &ns, &cand);
@@ -2513,7 +2514,7 @@ bool up_cols_supported(int64_t rows, int64_t d, int64_t ffn) {
 hipError_t launch_up_cols(const UpColsArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     if (!up_cols_supported(a.rows, a.d, a.ffn) || (a.h == nullptr) == (a.hb == nullptr) ||
-        (a.linear && a.w2 != nullptr))
+        (a.linear && a.w2 != nullptr) || (a.w_ld != 0 && (a.w_ld < a.ffn || a.w_ld % 8 != 0)))
         return hipErrorInvalidValue;
     const int bt = a.rows == 1 ? 1 : a.rows == 2 ? 2 : 4;
     if (a.zero != nullptr && a.n_zero % 4 != 0) return hipErrorInvalidValue;

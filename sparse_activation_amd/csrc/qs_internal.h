@@ -138,6 +138,7 @@ struct GemvArgs {
     // only they are gathered.
     const uint32_t* sel_desc;
     int64_t sel_k;         // launch_gather_sel: the top-k of h that the workgroups find
+    int64_t w_ld;          // launch_gather_sel: elements from one row of w to the next (0: n_out)
 };
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 // Both projections of the gated squared ReLU in one gather (tiles of at most
@@ -173,6 +174,7 @@ struct UpColsArgs {
     uint16_t* hb;            //   bf16 [rows, ffn] (nearest-even from the fp32 value)
     float* h2;               // or null: a second copy of h
     int linear;              // 1: h = u, the plain sparse linear (w2 null)
+    int64_t w_ld;            // elements from one row of w (and w2) to the next (0: ffn)
 };
 constexpr int64_t kUpColsMaxD = 16 * 512;
 constexpr int64_t kUpColsMaxFfn = 32 * 512;

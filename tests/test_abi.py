@@ -104,19 +104,57 @@ def test_gather_linear_acc_validation():
 
 def test_topk_gather_linear_acc_validation():
     """Selection-in-gather accumulate: bf16 W^T only, d_in % 4 == 0 and <= 16384,
-    n_out % 8 == 0, 0 <= k <= d_in, no workspace; rows == 0 is a no-op."""
+    n_out % 8 == 0, 0 <= k <= d_in, a row pitch ldw >= n_out that is a multiple
+    of 8, no workspace; rows == 0 is a no-op."""
     lib = qs.load()
     f = lib.qs_topk_gather_linear_acc
-    assert f(FAKE, 1, 11008, 4403, FAKE, qs.F32, 4096, FAKE, None) == 2     # fp32 W^T
-    assert f(FAKE, 1, 11006, 4403, FAKE, qs.BF16, 4096, FAKE, None) == 2    # d_in % 4
-    assert f(FAKE, 1, 16388, 4403, FAKE, qs.BF16, 4096, FAKE, None) == 2    # d_in too large
-    assert f(FAKE, 1, 11008, 4403, FAKE, qs.BF16, 4092, FAKE, None) == 2    # n_out % 8
-    assert f(FAKE, 1, 11008, 11009, FAKE, qs.BF16, 4096, FAKE, None) == 1   # k > d_in
-    assert f(FAKE, 1, 11008, -1, FAKE, qs.BF16, 4096, FAKE, None) == 1
-    assert f(None, 1, 11008, 4403, FAKE, qs.BF16, 4096, FAKE, None) == 1
-    assert f(MISALIGNED, 1, 11008, 4403, FAKE, qs.BF16, 4096, FAKE, None) == 2
-    assert f(FAKE, 65536, 11008, 4403, FAKE, qs.BF16, 4096, FAKE, None) == 2
-    assert f(None, 0, 11008, 4403, None, qs.BF16, 4096, None, None) == 0
+    assert f(FAKE, 1, 11008, 4403, FAKE, qs.F32, 4096, 4096, FAKE, None) == 2     # fp32 W^T
+    assert f(FAKE, 1, 11006, 4403, FAKE, qs.BF16, 4096, 4096, FAKE, None) == 2    # d_in % 4
+    assert f(FAKE, 1, 16388, 4403, FAKE, qs.BF16, 4096, 4096, FAKE, None) == 2    # d_in too large
+    assert f(FAKE, 1, 11008, 4403, FAKE, qs.BF16, 4092, 4092, FAKE, None) == 2    # n_out % 8
+    assert f(FAKE, 1, 11008, 11009, FAKE, qs.BF16, 4096, 4096, FAKE, None) == 1   # k > d_in
+    assert f(FAKE, 1, 11008, -1, FAKE, qs.BF16, 4096, 4096, FAKE, None) == 1
+    assert f(None, 1, 11008, 4403, FAKE, qs.BF16, 4096, 4096, FAKE, None) == 1
+    assert f(MISALIGNED, 1, 11008, 4403, FAKE, qs.BF16, 4096, 4096, FAKE, None) == 2
+    assert f(FAKE, 65536, 11008, 4403, FAKE, qs.BF16, 4096, 4096, FAKE, None) == 2
+    assert f(FAKE, 1, 11008, 4403, FAKE, qs.BF16, 4096, 4092, FAKE, None) == 1  # ldw < n_out
+    assert f(FAKE, 1, 11008, 4403, FAKE, qs.BF16, 4096, 4100, FAKE, None) == 1  # ldw % 8
+    assert f(FAKE, 1, 11008, 4403, FAKE, qs.BF16, 4096, 1 << 17, FAKE, None) == 2  # > 1 GiB
+    assert f(None, 0, 11008, 4403, None, qs.BF16, 4096, 4096, None, None) == 0
+
+
+def test_pitched_entry_points_validation():
+    """Row pitches: ld >= the natural width, a multiple of 8; a pitch other
+    than the natural one only on the one-token paths that read it (the
+    single-launch linear, the one-token squared-ReLU FFNs), rejected before
+    anything is enqueued everywhere else."""
+    lib = qs.load()
+    big = ctypes.c_size_t(1 << 40)
+    ffn_p = lib.qs_sparse_ffn_pitched
+
+    def ffn(rows, act, ld_up, ld_down, gate=None, k_mid=4403, mid=None, dt=qs.BF16):
+        return ffn_p(FAKE, dt, rows, 4096, 11008, act, 1638, k_mid, gate, FAKE, ld_up, FAKE,
+                     ld_down, None, None, FAKE, qs.F32, None, mid, None, FAKE, big, None)
+    assert ffn(1, qs.ACT_RELU2, 11000, 4160) == 1            # ld_up < ffn
+    assert ffn(1, qs.ACT_RELU2, 11072, 4100) == 1            # ld_down % 8
+    assert ffn(2, qs.ACT_RELU2, 11072, 4160) == 2            # two tokens
+    assert ffn(1, qs.ACT_DRELU, 11072, 4160, gate=FAKE) == 2  # dReLU
+    assert ffn(1, qs.ACT_RELU2, 11072, 4160, k_mid=-1) == 2  # no top-k of h
+    assert ffn(1, qs.ACT_RELU2, 11072, 4160, mid=FAKE) == 2  # index list asked for
+    assert ffn(1, qs.ACT_RELU2, 11072, 4160, dt=qs.F32) == 2  # fp32 weights
+    assert ffn(1, qs.ACT_RELU2, 1 << 17, 4160) == 2          # padded W_up^T >= 1 GiB
+    assert "row pitch" in qs.qs_last_error() or "1 GiB" in qs.qs_last_error()
+    lin = lib.qs_sparse_linear_pitched
+
+    def linear(rows, ldw, layout=qs.LAYOUT_WT, xt=qs.BF16, wt=qs.BF16):
+        return lin(FAKE, xt, rows, 4096, 1638, FAKE, ldw, wt, layout, 11008, FAKE, qs.F32, FAKE,
+                   big, None)
+    assert linear(1, 11000) == 1                              # ldw < n_out
+    assert linear(1, 11076) == 1                              # ldw % 8
+    assert linear(1, 5000, layout=qs.LAYOUT_W) == 1           # pitched dense layout
+    assert linear(2, 11072) == 2                              # two tokens
+    assert linear(1, 11072, xt=qs.F32) == 2                   # fp32 x
+    assert "row pitch" in qs.qs_last_error()
 
 
 def test_set_deterministic_returns_previous_setting():
