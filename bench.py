@@ -79,7 +79,7 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--roofline-launches", type=int, default=96)
     p.add_argument("--row-pad", type=int, default=64,
-                   help="c2, one token: bf16 columns of padding per weight row (0: natural rows)")
+                   help="c2 and c2g, one token: bf16 columns of padding per weight row (0: natural rows)")
     p.add_argument("--weight-copies", type=int, default=0,
                    help="weight copies to rotate over (0: the workload's default)")
     p.add_argument("--replays", type=int, default=50,
@@ -664,11 +664,18 @@ def run_c2g(args, torch, np, qs, datagen, dev, stream):
     d, ffn = c["W_up"].shape[1], c["W_up"].shape[0]
     k_in, k_mid = c["K_in"], c["K_mid"]
     n_copies = args.weight_copies or C2G_COPIES                          # 7 x >= 108 MB between visits
-    wg = [bf16_dev(torch, np, c["W_gate"].T, dev)]
-    wu = [bf16_dev(torch, np, c["W_up"].T, dev)]
-    wd = [bf16_dev(torch, np, c["W_down"].T, dev)]
-    for _ in range(n_copies - 1):
-        wg.append(wg[0].clone()); wu.append(wu[0].clone()); wd.append(wd[0].clone())
+    pad = args.row_pad if B == 1 else 0   # padded rows at one token, as in c2
+
+    def copies(a):
+        src = bf16_dev(torch, np, a, dev)
+        out = []
+        for _ in range(n_copies):
+            base = torch.zeros((src.shape[0], src.shape[1] + pad), dtype=src.dtype, device=dev)
+            base[:, :src.shape[1]] = src
+            out.append(base[:, :src.shape[1]])
+        return out
+
+    wg, wu, wd = copies(c["W_gate"].T), copies(c["W_up"].T), copies(c["W_down"].T)
     xs = [bf16_dev(torch, np, datagen.c2g_relu2glu_ffn(B, rotation=i, with_weights=False)["X"], dev)
           for i in range(N_XROT)]
     y = torch.empty((B, d), dtype=torch.float32, device=dev)
@@ -701,7 +708,7 @@ def run_c2g(args, torch, np, qs, datagen, dev, stream):
         "unit": "tokens/s", "value": round(B / (ms_step * 1e-3), 1),
         "ms_per_step": round(ms_step, 6), "dtype": "bf16",
         "config": {"workload": "llama7b_relu2glu_ffn_decode", "batch": B, "d": d, "ffn": ffn,
-                   "k_in": k_in, "k_mid": k_mid, "weight_copies": n_copies,
+                   "k_in": k_in, "k_mid": k_mid, "weight_row_pad": pad, "weight_copies": n_copies,
                    "x_rotations": N_XROT, "union_rows_in": u1, "union_rows_mid": u2},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
