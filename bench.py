@@ -203,7 +203,9 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     # (64: an odd multiple of 128 bytes), so that no column tile's row
     # segments sit at one offset modulo 1 KiB on a subset of the memory
     # channels; the kernels read the same bytes.  More tokens: natural rows.
-    pad = args.row_pad if B == 1 else 0
+    # (--deterministic keeps natural rows: its roofline leg times the plain
+    # gather, which reads natural rows only)
+    pad = args.row_pad if B == 1 and not args.deterministic else 0
     wup0 = bf16_dev(torch, np, c["W_up"].T, dev)
     wdn0 = bf16_dev(torch, np, c["W_down"].T, dev)
 
