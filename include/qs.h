@@ -191,9 +191,9 @@ qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_i
  *
  *   ldw     elements from one row of w to the next: the natural pitch (n_out
  *           for QS_LAYOUT_WT, d_in for QS_LAYOUT_W) gives qs_sparse_linear.
- *           Any other pitch needs QS_LAYOUT_WT, ldw >= n_out and a multiple of
- *           8, and the single-launch path (one bf16 token, bf16 W^T, d_in <=
- *           8192, n_out <= 16384); QS_ERR_INVALID_ARG or QS_ERR_UNSUPPORTED
+ *           Any other pitch needs QS_LAYOUT_WT (every batch size: the gather
+ *           paths), ldw >= n_out and a multiple of 8, and W^T (d_in x ldw)
+ *           smaller than 1 GiB; QS_ERR_INVALID_ARG or QS_ERR_UNSUPPORTED
  *           otherwise, before anything is enqueued.  The padding columns are
  *           never read.
  *   Why: every workgroup of the gather reads one 128-byte column segment of
@@ -360,14 +360,12 @@ qs_status qs_sparse_ffn(const void* x, qs_dtype dt, int64_t rows, int64_t d, int
  *
  *   ld_up    elements from one row of w_up (and of w_gate) to the next, at
  *            least the row length (ffn for W_up^T, d for dReLU's W_up), a
- *            multiple of 8.
+ *            multiple of 8.  dReLU needs the natural pitch d (its gate/up
+ *            kernels read whole rows); QS_ERR_UNSUPPORTED otherwise.
  *   ld_down  elements from one row of W_down^T to the next, >= d, a multiple
- *            of 8.
- *   The natural pitches give qs_sparse_ffn.  Other pitches need the
- *   one-token path of the squared-ReLU kinds (QS_ACT_RELU2 or
- *   QS_ACT_RELU2_GLU, rows == 1, bf16 x and weights, k_mid >= 0, mid_idx
- *   and mid_cnt NULL, shapes of the single-launch up projection); otherwise
- *   QS_ERR_UNSUPPORTED before anything is enqueued.  Padding columns are never
+ *            of 8 (every kind).
+ *   The natural pitches give qs_sparse_ffn; the others work at every batch
+ *   size, each padded matrix smaller than 1 GiB.  Padding columns are never
  *   read.  Rows padded by 64 bf16 keep each column tile's lines off a single
  *   subset of the memory channels (see qs_sparse_linear_pitched).
  */

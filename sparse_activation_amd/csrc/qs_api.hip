@@ -330,14 +330,10 @@ qs_status qs_sparse_linear_pitched(const void* x, qs_dtype xt, int64_t rows, int
     // The row pitch of the weights: the natural one, or (W^T, one bf16 token
     // with bf16 weights: the single-launch path) at least n_out, a multiple of 8.
     const bool pitched = ldw != (w_layout == QS_LAYOUT_W ? d_in : n_out);
-    if (pitched) {
+    if (pitched) {   // (the gather path reads any pitch; the dense MFMA path natural rows)
         if (w_layout != QS_LAYOUT_WT || ldw < n_out || ldw % 8 != 0)
             return fail(QS_ERR_INVALID_ARG, "%s: need ldw >= n_out, a multiple of 8, with QS_LAYOUT_WT", fn);
-        if (!(rows <= 1 && xt == QS_BF16 && wt_t == QS_BF16 && qs::up_cols_supported(1, d_in, n_out)))
-            return fail(QS_ERR_UNSUPPORTED,
-                        "%s: a row pitch other than n_out needs one bf16 token, bf16 W^T, "
-                        "d_in <= 8192 and n_out <= 16384", fn);
-        if (d_in * ldw * 2 >= qs::kMaxGatherWeightBytes)
+        if (d_in * ldw * (wt_t == QS_BF16 ? 2 : 4) >= qs::kMaxGatherWeightBytes)
             return fail(QS_ERR_UNSUPPORTED, "%s: W^T must be smaller than 1 GiB", fn);
     }
     if (w_layout == QS_LAYOUT_W) {
@@ -401,7 +397,7 @@ qs_status qs_sparse_linear_pitched(const void* x, qs_dtype xt, int64_t rows, int
     t.zero_ptr = wsp.counters; t.n_zero = plan.n_counters;
     if (acc) { t.zero_rows = (int32_t*)y; t.zero_row_len = n_out; }
     qs::GemvArgs g{};
-    g.xs = wsp.xs; g.rows = rows; g.d_in = d_in; g.n_out = n_out; g.w = w;
+    g.xs = wsp.xs; g.rows = rows; g.d_in = d_in; g.n_out = n_out; g.w = w; g.w_ld = ldw;
     g.partial = wsp.partial; g.counters = wsp.counters; g.y = y; g.y_bf16 = yt == QS_BF16;
     g.epilogue = qs::EPI_STORE;
     g.accumulate = acc ? 1 : 0;
@@ -600,7 +596,6 @@ qs_status qs_sparse_ffn_pitched(const void* x, qs_dtype dt, int64_t rows, int64_
     if (ld_up < up_len || ld_down < d || ld_up % 8 != 0 || ld_down % 8 != 0)
         return fail(QS_ERR_INVALID_ARG,
                     "%s: need row pitches of at least the row lengths, multiples of 8", fn);
-    const bool pitched = ld_up != up_len || ld_down != d;
     if (up_rows * ld_up * (dt == QS_BF16 ? 2 : 4) >= qs::kMaxGatherWeightBytes ||
         ffn * ld_down * (dt == QS_BF16 ? 2 : 4) >= qs::kMaxGatherWeightBytes)
         return fail(QS_ERR_UNSUPPORTED, "%s: each weight matrix must be smaller than 1 GiB", fn);
@@ -626,25 +621,8 @@ qs_status qs_sparse_ffn_pitched(const void* x, qs_dtype dt, int64_t rows, int64_
     const int kk = wb ? qs::KEY_BF16 : qs::KEY_F32;
     float* hbuf = h ? h : wsp.h;
     hipError_t e;
-    if (pitched) {
-        // Row pitches are honoured by the one-token path of the squared-ReLU
-        // kinds (two launches, each selecting inside); decided before
-        // anything is enqueued, with the conditions under which it is taken.
-        bool one_token = !drelu && wb && rows == 1 && k_mid >= 0 && !mid_idx && !mid_cnt &&
-                         qs::up_cols_supported(1, d, ffn) && qs::gather_sel_supported(1, ffn, d);
-        if (one_token) {
-            const qs::GemvPlan pdn = qs::plan_gemv(rows, ffn, d, wb);
-            int fs_tiles = 0, fs_split = 0, fs_cand = 0;
-            qs::gather_sel_plan(ffn, d, &fs_tiles, &fs_split, &fs_cand);
-            one_token = pdn.bt <= 8 && pdn.scratch_floats <= wsp.partial_cap &&
-                        (size_t)pdn.n_counters <= wsp.down_ctr_cap &&
-                        (size_t)fs_split * d <= wsp.partial_cap && (size_t)fs_tiles <= wsp.down_ctr_cap;
-        }
-        if (!one_token)
-            return fail(QS_ERR_UNSUPPORTED,
-                        "%s: row pitches other than (ffn, d) need one token of a squared-ReLU kind "
-                        "with bf16 weights, k_mid >= 0 and no mid_idx / mid_cnt", fn);
-    }
+    if (drelu && ld_up != up_len)   // (the dReLU gate/up kernels read whole natural rows)
+        return fail(QS_ERR_UNSUPPORTED, "%s: dReLU takes W_gate and W_up with natural rows", fn);
 
     // Small batches of the squared-ReLU kinds with bf16 weights.  The up
     // launch (for one token selecting the top-k_in of x in every workgroup,
@@ -660,7 +638,7 @@ qs_status qs_sparse_ffn_pitched(const void* x, qs_dtype dt, int64_t rows, int64_
             const bool acc = !deterministic() && yt == QS_F32 && qs::gemv_accumulate_supported(pdn, wb);
             qs::UpColsArgs u{};
             u.x = (const uint16_t*)x; u.rows = rows; u.d = d; u.ffn = ffn; u.k = k_in;
-            u.w_ld = ld_up;   // (the natural ffn unless the one-token path was checked above)
+            u.w_ld = ld_up;
             if (rows == 1) {
                 // One token: the up launch selects it itself and clears what
                 // the down gather needs cleared.
@@ -720,7 +698,7 @@ qs_status qs_sparse_ffn_pitched(const void* x, qs_dtype dt, int64_t rows, int64_
                 if (e != hipSuccess) return hip_fail(e, fn);
             }
             qs::GemvArgs g{};
-            g.xs = hbuf; g.rows = rows; g.d_in = ffn; g.n_out = d; g.w = w_down_t;
+            g.xs = hbuf; g.rows = rows; g.d_in = ffn; g.n_out = d; g.w = w_down_t; g.w_ld = ld_down;
             g.partial = wsp.partial; g.counters = wsp.ctr_down; g.y = y; g.y_bf16 = yt == QS_BF16;
             g.epilogue = qs::EPI_STORE;
             g.accumulate = acc ? 1 : 0;
@@ -769,7 +747,7 @@ qs_status qs_sparse_ffn_pitched(const void* x, qs_dtype dt, int64_t rows, int64_
             t.zero_row_len = ffn;
         }
         qs::GemvArgs g{};
-        g.xs = wsp.xs1; g.rows = rows; g.d_in = d; g.n_out = ffn; g.w = w_up;
+        g.xs = wsp.xs1; g.rows = rows; g.d_in = d; g.n_out = ffn; g.w = w_up; g.w_ld = ld_up;
         g.partial = wsp.partial; g.counters = wsp.ctr_up; g.y = hbuf; g.y_bf16 = 0;
         g.epilogue = acc_up ? qs::EPI_STORE : qs::EPI_RELU2;
         g.accumulate = acc_up ? 1 : 0;
@@ -834,7 +812,7 @@ qs_status qs_sparse_ffn_pitched(const void* x, qs_dtype dt, int64_t rows, int64_
 
     // Stage 2: select the intermediate entries that enter W_down.
     qs::GemvArgs g{};   // the down gather (stage 3)
-    g.rows = rows; g.d_in = ffn; g.n_out = d; g.w = w_down_t;
+    g.rows = rows; g.d_in = ffn; g.n_out = d; g.w = w_down_t; g.w_ld = ld_down;
     g.partial = wsp.partial; g.counters = wsp.ctr_down; g.y = y; g.y_bf16 = yt == QS_BF16;
     g.epilogue = qs::EPI_STORE;
     g.accumulate = acc_down ? 1 : 0;

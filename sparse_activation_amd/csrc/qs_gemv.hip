@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kNT) void gather_gemv_kernel(GemvArgs a, int cand, 
     const int64_t tok0 = (int64_t)tt * BT;
 
     const int64_t esize = WBF16 ? 2 : 4;
-    const uint32_t rowbytes = (uint32_t)(n_out * esize);
+    const uint32_t rowbytes = (uint32_t)((a.w_ld > 0 ? a.w_ld : n_out) * esize);   // row pitch
 
     // Phase A: rows of [j0, j1) selected by any token of the tile.  All the
     // coefficient loads are issued at once (candidate j0 + ch * 256 + tid is
@@ -1076,7 +1076,7 @@ __global__ __launch_bounds__(kNT) void gather_mfma_kernel(GemvArgs a, int cand, 
     const int64_t j1 = min(d_in, j0 + (int64_t)cand);
     const int64_t tok0 = (int64_t)tt * BT;
     const int64_t esize = WBF16 ? 2 : 4;
-    const uint32_t rowbytes = (uint32_t)(n_out * esize);
+    const uint32_t rowbytes = (uint32_t)((a.w_ld > 0 ? a.w_ld : n_out) * esize);   // row pitch
 
     // Phase A: union of the selected rows of this candidate range (as in the
     // fp32-FMA kernel), with the 16 tokens' coefficients.
@@ -1364,9 +1364,9 @@ __global__ __launch_bounds__(kNT) void gather_bmfma_kernel(GemvArgs a, BFrag bf,
     const int kq = lane >> 4, n16 = lane & 15;
     const int64_t col = (int64_t)tile * kBCols + 8 * c8;
     const uint32_t colb = col < n_out ? (uint32_t)(col * 2) : kOOB;
-    const uint32_t rowbytes = (uint32_t)(n_out * 2);
-    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, a.d_in * n_out * 2);
-    const __amdgpu_buffer_rsrc_t rs2 = weight_rsrc(DUAL ? a.w2 : a.w, a.d_in * n_out * 2);
+    const uint32_t rowbytes = (uint32_t)((a.w_ld > 0 ? a.w_ld : n_out) * 2);   // row pitch
+    const __amdgpu_buffer_rsrc_t rs = weight_rsrc(a.w, a.d_in * (int64_t)rowbytes);
+    const __amdgpu_buffer_rsrc_t rs2 = weight_rsrc(DUAL ? a.w2 : a.w, a.d_in * (int64_t)rowbytes);
     // Byte offset of row 4 r8 of group 0 of the split.
     const uint32_t rowb0 = (uint32_t)((g0 * kBGroup + 4 * r8) * rowbytes);
     uint16_t* tr = s_tr + wave * kBGroup * kBCols;
@@ -2404,8 +2404,14 @@ bool gemv_accumulate_supported(const GemvPlan& p, int w_is_bf16) {
     return !(p.bt == 16 && !w_is_bf16);
 }
 
+// A row pitch is 0 (n_out) or at least n_out, in whole 16-byte units.
+static bool gemv_pitch_ok(const GemvArgs& a, int w_is_bf16) {
+    return a.w_ld == 0 || (a.w_ld >= a.n_out && a.w_ld % (w_is_bf16 ? 8 : 4) == 0);
+}
+
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
+    if (!gemv_pitch_ok(a, w_is_bf16)) return hipErrorInvalidValue;
     // The descriptor form exists in the FMA kernel (tiles of at most eight tokens).
     if (a.sel_desc != nullptr && p.bt > 8) return hipErrorInvalidValue;
     if (a.accumulate && (a.y_bf16 || a.epilogue != EPI_STORE || !gemv_accumulate_supported(p, w_is_bf16)))
@@ -2545,6 +2551,7 @@ bool gemv_dual_supported(const GemvPlan& p, int w_is_bf16) {
 
 hipError_t launch_gemv_dual(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
+    if (!gemv_pitch_ok(a, w_is_bf16)) return hipErrorInvalidValue;
     if (!gemv_dual_supported(p, w_is_bf16) || a.w2 == nullptr || a.row_expert != nullptr ||
         (a.accumulate ? a.y2 == nullptr : p.nsplit > 1 && a.partial2 == nullptr))
         return hipErrorNotSupported;

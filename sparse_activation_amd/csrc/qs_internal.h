@@ -138,7 +138,7 @@ struct GemvArgs {
     // only they are gathered.
     const uint32_t* sel_desc;
     int64_t sel_k;         // launch_gather_sel: the top-k of h that the workgroups find
-    int64_t w_ld;          // launch_gather_sel: elements from one row of w to the next (0: n_out)
+    int64_t w_ld;          // elements from one row of w (and w2) to the next (0: n_out)
 };
 hipError_t launch_gemv(const GemvPlan& p, int w_is_bf16, const GemvArgs& a, hipStream_t stream);
 // Both projections of the gated squared ReLU in one gather (tiles of at most

@@ -124,37 +124,32 @@ def test_topk_gather_linear_acc_validation():
 
 
 def test_pitched_entry_points_validation():
-    """Row pitches: ld >= the natural width, a multiple of 8; a pitch other
-    than the natural one only on the one-token paths that read it (the
-    single-launch linear, the one-token squared-ReLU FFNs), rejected before
-    anything is enqueued everywhere else."""
+    """Row pitches: at least the row length, a multiple of 8, the padded matrix
+    under 1 GiB; dReLU's W_gate / W_up and the dense layout take natural rows
+    only.  Every call below fails validation (nothing is enqueued)."""
     lib = qs.load()
     big = ctypes.c_size_t(1 << 40)
     ffn_p = lib.qs_sparse_ffn_pitched
 
-    def ffn(rows, act, ld_up, ld_down, gate=None, k_mid=4403, mid=None, dt=qs.BF16):
-        return ffn_p(FAKE, dt, rows, 4096, 11008, act, 1638, k_mid, gate, FAKE, ld_up, FAKE,
-                     ld_down, None, None, FAKE, qs.F32, None, mid, None, FAKE, big, None)
-    assert ffn(1, qs.ACT_RELU2, 11000, 4160) == 1            # ld_up < ffn
-    assert ffn(1, qs.ACT_RELU2, 11072, 4100) == 1            # ld_down % 8
-    assert ffn(2, qs.ACT_RELU2, 11072, 4160) == 2            # two tokens
-    assert ffn(1, qs.ACT_DRELU, 11072, 4160, gate=FAKE) == 2  # dReLU
-    assert ffn(1, qs.ACT_RELU2, 11072, 4160, k_mid=-1) == 2  # no top-k of h
-    assert ffn(1, qs.ACT_RELU2, 11072, 4160, mid=FAKE) == 2  # index list asked for
-    assert ffn(1, qs.ACT_RELU2, 11072, 4160, dt=qs.F32) == 2  # fp32 weights
-    assert ffn(1, qs.ACT_RELU2, 1 << 17, 4160) == 2          # padded W_up^T >= 1 GiB
-    assert "row pitch" in qs.qs_last_error() or "1 GiB" in qs.qs_last_error()
+    def ffn(act, ld_up, ld_down, gate=None):
+        return ffn_p(FAKE, qs.BF16, 2, 4096, 11008, act, 1638, 4403, gate, FAKE, ld_up, FAKE,
+                     ld_down, None, None, FAKE, qs.F32, None, None, None, FAKE, big, None)
+    assert ffn(qs.ACT_RELU2, 11000, 4160) == 1                # ld_up < ffn
+    assert ffn(qs.ACT_RELU2, 11072, 4100) == 1                # ld_down % 8
+    assert ffn(qs.ACT_RELU2, 11072, 4088) == 1                # ld_down < d
+    assert ffn(qs.ACT_DRELU, 4160, 4160, gate=FAKE) == 2      # dReLU W_up padded
+    assert "natural rows" in qs.qs_last_error()
+    assert ffn(qs.ACT_RELU2, 1 << 17, 4160) == 2              # padded W_up^T >= 1 GiB
+    assert "1 GiB" in qs.qs_last_error()
     lin = lib.qs_sparse_linear_pitched
 
-    def linear(rows, ldw, layout=qs.LAYOUT_WT, xt=qs.BF16, wt=qs.BF16):
-        return lin(FAKE, xt, rows, 4096, 1638, FAKE, ldw, wt, layout, 11008, FAKE, qs.F32, FAKE,
-                   big, None)
-    assert linear(1, 11000) == 1                              # ldw < n_out
-    assert linear(1, 11076) == 1                              # ldw % 8
-    assert linear(1, 5000, layout=qs.LAYOUT_W) == 1           # pitched dense layout
-    assert linear(2, 11072) == 2                              # two tokens
-    assert linear(1, 11072, xt=qs.F32) == 2                   # fp32 x
-    assert "row pitch" in qs.qs_last_error()
+    def linear(ldw, layout=qs.LAYOUT_WT):
+        return lin(FAKE, qs.BF16, 2, 4096, 1638, FAKE, ldw, qs.BF16, layout, 11008, FAKE, qs.F32,
+                   FAKE, big, None)
+    assert linear(11000) == 1                                 # ldw < n_out
+    assert linear(11076) == 1                                 # ldw % 8
+    assert linear(5000, layout=qs.LAYOUT_W) == 1              # pitched dense layout
+    assert linear(1 << 17) == 2                               # W^T >= 1 GiB
 
 
 def test_set_deterministic_returns_previous_setting():

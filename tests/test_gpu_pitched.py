@@ -1,7 +1,7 @@
 """GPU parity of padded weight rows (a row pitch wider than the row): the
-one-token squared-ReLU FFNs, the single-launch linear for one bf16 token and
-the selection-in-gather read the rows of W^T ldw elements apart and never
-touch the padding.
+squared-ReLU FFNs at 1-16 tokens, the dReLU FFN's down gather, the sparse
+linear and the selection-in-gather read the rows of W^T ldw elements apart
+and never touch the padding.
 
 Every padding column holds NaN, so a read of it would show in y.  The padded
 call reads the same numbers in the same order as the unpadded call (only the
@@ -141,18 +141,89 @@ def test_pitched_topk_gather(gpu_lib, pad):
         assert_within(y.cpu().numpy(), y_ref, t, SUM_EPS, "pitched topk-gather vs oracle")
 
 
-def test_pitched_rejected_off_the_one_token_path(gpu_lib):
-    """Two tokens with padded rows: QS_ERR_UNSUPPORTED, nothing enqueued (y untouched)."""
+@pytest.mark.parametrize("rows", [2, 4, 8, 16])
+@pytest.mark.parametrize("glu", [False, True])
+def test_pitched_ffn_batches(gpu_lib, rows, glu):
+    """2-16 tokens (the selection launch, the column kernel or the gathers,
+    the 16-token matrix-core gather): fixed-order y bitwise equal to the
+    unpadded call's, NaN padding never read."""
     import torch
     qs = gpu_lib
     bf = torch.bfloat16
-    c = _small(3)
-    x2 = np.concatenate([c["X"], c["X"]])
-    y = torch.full((2, 520), 7.0, dtype=torch.float32, device="cuda")
+    for d, f in ((4096, 11008), (520, 1368)):
+        c = (datagen.c2g_relu2glu_ffn if glu else datagen.c2_relu2_ffn)(rows, d=d, ffn=f)
+        act = qs.ACT_RELU2_GLU if glu else qs.ACT_RELU2
+        wu_t, wd_t = np.ascontiguousarray(c["W_up"].T), np.ascontiguousarray(c["W_down"].T)
+        wg_t = np.ascontiguousarray(c["W_gate"].T) if glu else None
+        xd = to_dev(c["X"], bf)
+        note(f"pitched FFN rows={rows} glu={glu} {d}x{f}")
+        with reduction_mode(qs, True):
+            y0, _, _, _ = qs.qs_sparse_ffn(xd, act, c["K_in"], c["K_mid"], to_dev(wu_t, bf),
+                                           to_dev(wd_t, bf),
+                                           w_gate=to_dev(wg_t, bf) if glu else None)
+            y1, _, _, _ = qs.qs_sparse_ffn(xd, act, c["K_in"], c["K_mid"], _padded(wu_t, 64, bf),
+                                           _padded(wd_t, 64, bf),
+                                           w_gate=_padded(wg_t, 64, bf) if glu else None)
+            torch.cuda.synchronize()
+        y0, y1 = y0.cpu().numpy(), y1.cpu().numpy()
+        assert np.all(np.isfinite(y1))
+        assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32)), f"rows={rows} {d}x{f}"
+
+
+@pytest.mark.parametrize("rows", [1, 4, 16])
+def test_pitched_drelu_down(gpu_lib, rows):
+    """dReLU with W_down^T rows padded (W_gate and W_up natural): fixed-order y
+    bitwise equal to the unpadded call's."""
+    import torch
+    qs = gpu_lib
+    bf = torch.bfloat16
+    c = datagen.c5_drelu_ffn(rows, d=1024, ffn=3584)
+    wd_t = np.ascontiguousarray(c["W_down"].T)
+    xd = to_dev(c["X"], bf)
+    kw = dict(w_gate=to_dev(c["W_gate"], bf), b_gate=to_dev(c["b_gate"]), b_up=to_dev(c["b_up"]))
+    note(f"pitched dReLU rows={rows}")
+    with reduction_mode(qs, True):
+        y0, _, _, _ = qs.qs_sparse_ffn(xd, qs.ACT_DRELU, 1024, -1, to_dev(c["W_up"], bf),
+                                       to_dev(wd_t, bf), **kw)
+        y1, _, _, _ = qs.qs_sparse_ffn(xd, qs.ACT_DRELU, 1024, -1, to_dev(c["W_up"], bf),
+                                       _padded(wd_t, 64, bf), **kw)
+        torch.cuda.synchronize()
+    y0, y1 = y0.cpu().numpy(), y1.cpu().numpy()
+    assert np.all(np.isfinite(y1))
+    assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows", [3, 8, 16])
+def test_pitched_linear_batches(gpu_lib, rows):
+    """qs_sparse_linear on padded W^T rows through the selection launch and
+    the gathers: fixed-order y bitwise equal to the unpadded call's."""
+    import torch
+    qs = gpu_lib
+    bf = torch.bfloat16
+    rng = np.random.default_rng(40 + rows)
+    x = datagen.bf16_round(datagen.student_t(rng, (rows, 1536)))
+    wt = np.ascontiguousarray(datagen.bf16_round(datagen.normal(rng, (1032, 1536), 0.02)).T)
+    xd = to_dev(x, bf)
+    note(f"pitched linear rows={rows}")
+    with reduction_mode(qs, True):
+        y0 = qs.qs_sparse_linear(xd, 614, to_dev(wt, bf))
+        y1 = qs.qs_sparse_linear(xd, 614, _padded(wt, 64, bf))
+        torch.cuda.synchronize()
+    assert np.array_equal(y0.cpu().numpy().view(np.uint32), y1.cpu().numpy().view(np.uint32))
+
+
+def test_pitched_drelu_up_rejected(gpu_lib):
+    """dReLU with padded W_up rows: QS_ERR_UNSUPPORTED, nothing enqueued (y untouched)."""
+    import torch
+    qs = gpu_lib
+    bf = torch.bfloat16
+    c = datagen.c5_drelu_ffn(2, d=1024, ffn=3584)
+    y = torch.full((2, 1024), 7.0, dtype=torch.float32, device="cuda")
     with pytest.raises(qs.QSError) as e:
-        qs.qs_sparse_ffn(to_dev(x2, bf), qs.ACT_RELU2, c["K_in"], c["K_mid"],
-                         _padded(np.ascontiguousarray(c["W_up"].T), 8, bf),
-                         _padded(np.ascontiguousarray(c["W_down"].T), 8, bf), y=y)
+        qs.qs_sparse_ffn(to_dev(c["X"], bf), qs.ACT_DRELU, 1024, -1, _padded(c["W_up"], 8, bf),
+                         to_dev(np.ascontiguousarray(c["W_down"].T), bf),
+                         w_gate=_padded(c["W_gate"], 8, bf), b_gate=to_dev(c["b_gate"]),
+                         b_up=to_dev(c["b_up"]), y=y)
     assert e.value.status == qs.QS_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert bool((y == 7.0).all())
