@@ -8,10 +8,10 @@ One step is one call of qs_sparse_ffn over one batch: the top-K of x and the
 up projection over the selected rows of W_up^T with the squared-ReLU
 epilogue, then the top-K of the intermediate and the down projection over
 the rows of W_down^T it selects (at one token two launches, each selecting
-inside its workgroups).  At one token the weight rows are padded by 64 bf16
-(--row-pad; config.weight_row_pitch): with the natural 1 KiB-multiple pitch
-the row segments of some column tiles share a subset of the memory channels
-and those tiles finish last; the kernels read the same bytes either way.
+inside its workgroups).  The weight rows are padded by 64 bf16 (--row-pad;
+config.weight_row_pitch): with the natural 1 KiB-multiple pitch the row
+segments of some column tiles share a subset of the memory channels and
+those tiles finish last; the kernels read the same bytes either way.
 
 Other workloads (--workload): c1 (fp32 1024x1024 linear, 8 tokens), c2g (the
 same Llama-7B FFN with a gate: gated squared ReLU), c3
@@ -79,7 +79,8 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--roofline-launches", type=int, default=96)
     p.add_argument("--row-pad", type=int, default=64,
-                   help="c2 and c2g, one token: bf16 columns of padding per weight row (0: natural rows)")
+                   help="bf16 columns of padding per W^T row: c2, c2g (all gathered matrices), c5 "
+                        "(W_down^T); 0: natural rows")
     p.add_argument("--weight-copies", type=int, default=0,
                    help="weight copies to rotate over (0: the workload's default)")
     p.add_argument("--replays", type=int, default=50,
@@ -199,13 +200,11 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     # reads only the selected rows (72 MB at one token), so 16 copies put
     # 15 x 72 MB = 1.08 GB between visits.
     n_copies = args.weight_copies or C2_COPIES
-    # One token: the rows of W_up^T and W_down^T are padded by --row-pad bf16
-    # (64: an odd multiple of 128 bytes), so that no column tile's row
-    # segments sit at one offset modulo 1 KiB on a subset of the memory
-    # channels; the kernels read the same bytes.  More tokens: natural rows.
-    # (--deterministic keeps natural rows: its roofline leg times the plain
-    # gather, which reads natural rows only)
-    pad = args.row_pad if B == 1 and not args.deterministic else 0
+    # The rows of W_up^T and W_down^T are padded by --row-pad bf16 (64: an odd
+    # multiple of 128 bytes), so that no column tile's row segments sit at one
+    # offset modulo 1 KiB on a subset of the memory channels; the kernels read
+    # the same bytes.
+    pad = args.row_pad
     wup0 = bf16_dev(torch, np, c["W_up"].T, dev)
     wdn0 = bf16_dev(torch, np, c["W_down"].T, dev)
 
@@ -428,9 +427,18 @@ def run_c5(args, torch, np, qs, datagen, dev, stream):
     n_copies = args.weight_copies or C5_COPIES                           # 5 x >= 166 MB between visits
     wg = [bf16_dev(torch, np, c["W_gate"], dev)]
     wu = [bf16_dev(torch, np, c["W_up"], dev)]
-    wd = [bf16_dev(torch, np, c["W_down"].T, dev)]
     for _ in range(n_copies - 1):
-        wg.append(wg[0].clone()); wu.append(wu[0].clone()); wd.append(wd[0].clone())
+        wg.append(wg[0].clone()); wu.append(wu[0].clone())
+    # W_down^T rows padded by --row-pad bf16 (the down gather's column tiles,
+    # as in c2); W_gate and W_up are read in whole rows and keep theirs.
+    pad = args.row_pad
+    wd0 = bf16_dev(torch, np, c["W_down"].T, dev)
+    wd = []
+    for _ in range(n_copies):
+        base = torch.zeros((ffn, d + pad), dtype=wd0.dtype, device=dev)
+        base[:, :d] = wd0
+        wd.append(base[:, :d])
+    del wd0
     bg = torch.from_numpy(c["b_gate"]).to(dev)
     bu = torch.from_numpy(c["b_up"]).to(dev)
     xs = [bf16_dev(torch, np, datagen.c5_drelu_ffn(B, rotation=i, with_weights=False)["X"], dev)
@@ -462,6 +470,7 @@ def run_c5(args, torch, np, qs, datagen, dev, stream):
         "metric": "dReLU sparse FFN tokens/s at Mistral-7B decode, 1 GPU", "unit": "tokens/s",
         "value": round(B / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 6), "dtype": "bf16",
         "config": {"workload": "mistral7b_drelu_ffn_decode", "batch": B, "d": d, "ffn": ffn,
+                   "w_down_t_row_pad": pad,
                    "weight_copies": n_copies, "x_rotations": N_XROT,
                    "zero_fraction_h": round(zero_frac, 4), "up_rows_read": g_pos,
                    "down_rows_read": nz},
@@ -666,7 +675,7 @@ def run_c2g(args, torch, np, qs, datagen, dev, stream):
     d, ffn = c["W_up"].shape[1], c["W_up"].shape[0]
     k_in, k_mid = c["K_in"], c["K_mid"]
     n_copies = args.weight_copies or C2G_COPIES                          # 7 x >= 108 MB between visits
-    pad = args.row_pad if B == 1 else 0   # padded rows at one token, as in c2
+    pad = args.row_pad   # padded rows, as in c2
 
     def copies(a):
         src = bf16_dev(torch, np, a, dev)

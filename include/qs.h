@@ -214,7 +214,10 @@ qs_status qs_sparse_linear_pitched(const void* x, qs_dtype xt, int64_t rows, int
  * feature is nonzero for some row of Xs  [QS-TopK], [QS-Adv].
  *
  *   xs      device fp32 [rows, d_in].
- *   wt      device W^T [d_in, n_out], dtype wt_t (QS_F32 or QS_BF16).
+ *   wt      device W^T [d_in, n_out], dtype wt_t (QS_F32 or QS_BF16), rows ldw
+ *           elements apart.
+ *   ldw     n_out, or a larger multiple of 8 (padded rows: see
+ *           qs_sparse_linear_pitched); QS_ERR_INVALID_ARG otherwise.
  *   y       device [rows, n_out], dtype yt (QS_F32 or QS_BF16).
  *   Arithmetic and alignment as qs_sparse_linear with QS_LAYOUT_WT.
  *   Workspace: sized by qs_workspace_bytes(QS_OP_GATHER_LINEAR, ...); unlike
@@ -223,7 +226,7 @@ qs_status qs_sparse_linear_pitched(const void* x, qs_dtype xt, int64_t rows, int
  *   that the call is a single kernel launch.
  */
 qs_status qs_gather_linear(const float* xs, int64_t rows, int64_t d_in, const void* wt,
-                           qs_dtype wt_t, int64_t n_out, void* y, qs_dtype yt,
+                           qs_dtype wt_t, int64_t n_out, int64_t ldw, void* y, qs_dtype yt,
                            void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -235,14 +238,14 @@ qs_status qs_gather_linear(const float* xs, int64_t rows, int64_t d_in, const vo
  * rounding of each sum depends on the arrival order of the splits, whatever
  * qs_set_deterministic says.
  *
- *   xs, wt, wt_t, rows, d_in, n_out: as qs_gather_linear.
+ *   xs, wt, wt_t, rows, d_in, n_out, ldw: as qs_gather_linear.
  *   y     device fp32 [rows, n_out], read and written.
  *   Workspace: as qs_gather_linear (its counters are not touched).
  *   Limits: as qs_gather_linear; fp32 weights need rows <= 8
  *   (QS_ERR_UNSUPPORTED otherwise).
  */
 qs_status qs_gather_linear_acc(const float* xs, int64_t rows, int64_t d_in, const void* wt,
-                               qs_dtype wt_t, int64_t n_out, float* y, void* ws,
+                               qs_dtype wt_t, int64_t n_out, int64_t ldw, float* y, void* ws,
                                size_t ws_bytes, void* stream);
 
 /*

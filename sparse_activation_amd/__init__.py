@@ -44,8 +44,8 @@ _I64 = ctypes.c_int64
 _INT = ctypes.c_int
 _SIGS = {
     "qs_topk_mask": [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P],
-    "qs_gather_linear": [_P, _I64, _I64, _P, _INT, _I64, _P, _INT, _P, ctypes.c_size_t, _P],
-    "qs_gather_linear_acc": [_P, _I64, _I64, _P, _INT, _I64, _P, _P, ctypes.c_size_t, _P],
+    "qs_gather_linear": [_P, _I64, _I64, _P, _INT, _I64, _I64, _P, _INT, _P, ctypes.c_size_t, _P],
+    "qs_gather_linear_acc": [_P, _I64, _I64, _P, _INT, _I64, _I64, _P, _P, ctypes.c_size_t, _P],
     "qs_topk_gather_linear_acc": [_P, _I64, _I64, _I64, _P, _INT, _I64, _I64, _P, _P],
     "qs_set_deterministic": [_INT],
     "qs_sparse_linear": [_P, _INT, _I64, _I64, _I64, _P, _INT, _INT, _I64, _P, _INT, _P,
@@ -237,14 +237,15 @@ def qs_gather_linear(xs, wt, y=None, y_dtype=None, ws=None):
     if wt.shape[0] != d_in:
         raise ValueError("wt must be [d_in, n_out]")
     n_out = wt.shape[1]
-    dev = _dev(xs, wt, y, ws)
+    dev = _dev(xs, wt, y, ws, strided=(wt,))
     if y is None:
         y = torch.empty((rows, n_out), dtype=y_dtype or torch.float32, device=dev)
     if ws is None:
         ws = gather_workspace(rows, d_in, n_out, dev)
     ws_bytes = ws.numel() * ws.element_size()
     _check(load().qs_gather_linear(_ptr(xs), rows, d_in, _ptr(wt), _dtype_code(wt), n_out,
-                                   _ptr(y), _dtype_code(y), _ptr(ws), ws_bytes, _stream(dev)))
+                                   _row_pitch(wt, "wt"), _ptr(y), _dtype_code(y), _ptr(ws),
+                                   ws_bytes, _stream(dev)))
     return y
 
 
@@ -261,12 +262,13 @@ def qs_gather_linear_acc(xs, wt, y, ws=None):
     n_out = wt.shape[1]
     if tuple(y.shape) != (rows, n_out):
         raise ValueError("y must be [rows, n_out]")
-    dev = _dev(xs, wt, y, ws)
+    dev = _dev(xs, wt, y, ws, strided=(wt,))
     if ws is None:
         ws = gather_workspace(rows, d_in, n_out, dev)
     ws_bytes = ws.numel() * ws.element_size()
     _check(load().qs_gather_linear_acc(_ptr(xs), rows, d_in, _ptr(wt), _dtype_code(wt), n_out,
-                                       _ptr(y), _ptr(ws), ws_bytes, _stream(dev)))
+                                       _row_pitch(wt, "wt"), _ptr(y), _ptr(ws), ws_bytes,
+                                       _stream(dev)))
     return y
 
 

@@ -413,8 +413,8 @@ qs_status qs_sparse_linear_pitched(const void* x, qs_dtype xt, int64_t rows, int
 namespace {
 
 qs_status gather_linear(const char* fn, bool accumulate, const float* xs, int64_t rows,
-                        int64_t d_in, const void* wt, qs_dtype wt_t, int64_t n_out, void* y,
-                        qs_dtype yt, void* ws, size_t ws_bytes, void* stream) {
+                        int64_t d_in, const void* wt, qs_dtype wt_t, int64_t n_out, int64_t ldw,
+                        void* y, qs_dtype yt, void* ws, size_t ws_bytes, void* stream) {
     if (rows < 0 || d_in <= 0 || n_out <= 0 || d_in > (int64_t(1) << 24))
         return fail(QS_ERR_INVALID_ARG, "%s: bad shape", fn);
     if (!valid_float_dtype(wt_t) || !valid_float_dtype(yt))
@@ -422,7 +422,9 @@ qs_status gather_linear(const char* fn, bool accumulate, const float* xs, int64_
     if (n_out % (wt_t == QS_BF16 ? 8 : 4) != 0)
         return fail(QS_ERR_UNSUPPORTED, "%s: n_out must be a multiple of %d", fn,
                     wt_t == QS_BF16 ? 8 : 4);
-    if (d_in * n_out * (wt_t == QS_BF16 ? 2 : 4) >= qs::kMaxGatherWeightBytes)
+    if (ldw < n_out || ldw % 8 != 0)
+        return fail(QS_ERR_INVALID_ARG, "%s: need ldw >= n_out, a multiple of 8", fn);
+    if (d_in * ldw * (wt_t == QS_BF16 ? 2 : 4) >= qs::kMaxGatherWeightBytes)
         return fail(QS_ERR_UNSUPPORTED, "%s: W^T must be smaller than 1 GiB", fn);
     if (rows > 0x7FFFFFFF) return fail(QS_ERR_UNSUPPORTED, "%s: too many rows", fn);
     if (rows == 0) return ok();
@@ -441,7 +443,7 @@ qs_status gather_linear(const char* fn, bool accumulate, const float* xs, int64_
     if (accumulate && !qs::gemv_accumulate_supported(plan, wb))
         return fail(QS_ERR_UNSUPPORTED, "%s: fp32 weights need at most 8 rows", fn);
     qs::GemvArgs g{};
-    g.xs = xs; g.rows = rows; g.d_in = d_in; g.n_out = n_out; g.w = wt;
+    g.xs = xs; g.rows = rows; g.d_in = d_in; g.n_out = n_out; g.w = wt; g.w_ld = ldw;
     g.partial = wsp.partial; g.counters = wsp.counters; g.y = y; g.y_bf16 = yt == QS_BF16;
     g.epilogue = qs::EPI_STORE;
     g.accumulate = accumulate ? 1 : 0;
@@ -453,17 +455,17 @@ qs_status gather_linear(const char* fn, bool accumulate, const float* xs, int64_
 }  // namespace
 
 qs_status qs_gather_linear(const float* xs, int64_t rows, int64_t d_in, const void* wt,
-                           qs_dtype wt_t, int64_t n_out, void* y, qs_dtype yt,
+                           qs_dtype wt_t, int64_t n_out, int64_t ldw, void* y, qs_dtype yt,
                            void* ws, size_t ws_bytes, void* stream) {
-    return gather_linear("qs_gather_linear", false, xs, rows, d_in, wt, wt_t, n_out, y, yt, ws,
-                         ws_bytes, stream);
+    return gather_linear("qs_gather_linear", false, xs, rows, d_in, wt, wt_t, n_out, ldw, y, yt,
+                         ws, ws_bytes, stream);
 }
 
 qs_status qs_gather_linear_acc(const float* xs, int64_t rows, int64_t d_in, const void* wt,
-                               qs_dtype wt_t, int64_t n_out, float* y, void* ws,
+                               qs_dtype wt_t, int64_t n_out, int64_t ldw, float* y, void* ws,
                                size_t ws_bytes, void* stream) {
-    return gather_linear("qs_gather_linear_acc", true, xs, rows, d_in, wt, wt_t, n_out, y, QS_F32,
-                         ws, ws_bytes, stream);
+    return gather_linear("qs_gather_linear_acc", true, xs, rows, d_in, wt, wt_t, n_out, ldw, y,
+                         QS_F32, ws, ws_bytes, stream);
 }
 
 qs_status qs_topk_gather_linear_acc(const float* x, int64_t rows, int64_t d_in, int64_t k,

@@ -79,12 +79,16 @@ def test_gather_linear_validation():
     lib = qs.load()
     need = qs.qs_workspace_bytes(qs.OP_GATHER_LINEAR, 2, 512, 256)
     assert need >= 16384
-    assert lib.qs_gather_linear(FAKE, 2, 512, FAKE, qs.BF16, 252, FAKE, qs.F32, FAKE, need,
+    assert lib.qs_gather_linear(FAKE, 2, 512, FAKE, qs.BF16, 252, 252, FAKE, qs.F32, FAKE, need,
                                 None) == 2
-    assert lib.qs_gather_linear(FAKE, 2, 512, FAKE, qs.BF16, 256, FAKE, qs.F32, FAKE, need - 1,
+    assert lib.qs_gather_linear(FAKE, 2, 512, FAKE, qs.BF16, 256, 256, FAKE, qs.F32, FAKE, need - 1,
                                 None) == 3
-    assert lib.qs_gather_linear(None, 2, 512, FAKE, qs.BF16, 256, FAKE, qs.F32, FAKE, need,
+    assert lib.qs_gather_linear(None, 2, 512, FAKE, qs.BF16, 256, 256, FAKE, qs.F32, FAKE, need,
                                 None) == 1
+    assert lib.qs_gather_linear(FAKE, 2, 512, FAKE, qs.BF16, 256, 252, FAKE, qs.F32, FAKE, need,
+                                None) == 1   # ldw < n_out
+    assert lib.qs_gather_linear(FAKE, 2, 512, FAKE, qs.BF16, 256, 260, FAKE, qs.F32, FAKE, need,
+                                None) == 1   # ldw % 8
 
 
 def test_gather_linear_acc_validation():
@@ -92,12 +96,12 @@ def test_gather_linear_acc_validation():
     in 16-token tiles have no accumulate form."""
     lib = qs.load()
     need = qs.qs_workspace_bytes(qs.OP_GATHER_LINEAR, 2, 512, 256)
-    assert lib.qs_gather_linear_acc(FAKE, 2, 512, FAKE, qs.BF16, 252, FAKE, FAKE, need, None) == 2
-    assert lib.qs_gather_linear_acc(FAKE, 2, 512, FAKE, qs.BF16, 256, FAKE, FAKE, need - 1,
+    assert lib.qs_gather_linear_acc(FAKE, 2, 512, FAKE, qs.BF16, 252, 252, FAKE, FAKE, need, None) == 2
+    assert lib.qs_gather_linear_acc(FAKE, 2, 512, FAKE, qs.BF16, 256, 256, FAKE, FAKE, need - 1,
                                     None) == 3
-    assert lib.qs_gather_linear_acc(None, 2, 512, FAKE, qs.BF16, 256, FAKE, FAKE, need, None) == 1
+    assert lib.qs_gather_linear_acc(None, 2, 512, FAKE, qs.BF16, 256, 256, FAKE, FAKE, need, None) == 1
     need16 = qs.qs_workspace_bytes(qs.OP_GATHER_LINEAR, 16, 512, 256)
-    assert lib.qs_gather_linear_acc(FAKE, 16, 512, FAKE, qs.F32, 256, FAKE, FAKE, need16,
+    assert lib.qs_gather_linear_acc(FAKE, 16, 512, FAKE, qs.F32, 256, 256, FAKE, FAKE, need16,
                                     None) == 2
     assert "8 rows" in qs.qs_last_error()
 
