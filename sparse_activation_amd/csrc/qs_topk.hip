@@ -1023,6 +1023,61 @@ hipError_t launch_desc31(const float* x, int64_t rows, int64_t d, int64_t k, uin
     return hipGetLastError();
 }
 
+namespace {
+
+// Many rows of bf16 x whose only output is X (.) M in bf16 (the operand of the
+// dense MFMA paths): one workgroup of 256 threads per row, E entries per
+// thread.  The top-k of the 15-bit magnitude keys comes from two LDS
+// histogram levels (8 high bits, then the 7 low bits of the boundary bin;
+// ties to the lower index, Q-Sparse news article, section "Sparsification
+// with the Top-K function"), without the candidate lists and digit loops of
+// the general kernel; then each thread writes its run of X (.) M.
+constexpr int kS15NT = 256;
+
+template <int E>
+__global__ __launch_bounds__(kS15NT) void select15_xs_kernel(TopkArgs a) {
+    __shared__ rowsel::Sel15Lds<1, kS15NT / 64> L;
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int d = (int)a.d;
+    const int nvalid = d - tid * E;
+    if (a.zero_ptr != nullptr && row == 0)
+        for (int i = tid; i < a.n_zero; i += kS15NT) a.zero_ptr[i] = 0;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(reinterpret_cast<const void*>(reinterpret_cast<const uint16_t*>(a.x) + row * d)),
+        (short)0, d * 2, 0x00020000);
+    uint32_t xr16[E / 2];   // bf16 pairs (entry 2i in the low half)
+#pragma unroll
+    for (int q = 0; q < E / 8; ++q) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)((tid * E + 8 * q) * 2), 0, 0);
+        xr16[4 * q] = v.x; xr16[4 * q + 1] = v.y; xr16[4 * q + 2] = v.z; xr16[4 * q + 3] = v.w;
+    }
+    for (int i = tid; i < (int)(sizeof(L) / 4); i += kS15NT) reinterpret_cast<uint32_t*>(&L)[i] = 0;
+    uint32_t key[1][E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        key[0][e] = e < nvalid ? (xr16[e / 2] >> (16 * (e % 2))) & 0x7FFFu : sel::kInvalid;
+    __syncthreads();
+    uint32_t selm[1];
+    rowsel::select15_masks<kS15NT, 1, E>(key, 1, a.k, L, tid, selm);
+    uint16_t* xs = reinterpret_cast<uint16_t*>(a.xs) + row * d;
+#pragma unroll
+    for (int q = 0; q < E / 8; ++q) {
+        if (tid * E + 8 * q >= d) break;   // (d % 8 == 0: whole runs)
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 8 * q + 2 * i;
+            const uint32_t lo = (selm[0] >> e) & 1u ? 0x0000FFFFu : 0u;
+            const uint32_t hi = (selm[0] >> (e + 1)) & 1u ? 0xFFFF0000u : 0u;
+            w[i] = xr16[4 * q + i] & (lo | hi);
+        }
+        *reinterpret_cast<uint4*>(xs + tid * E + 8 * q) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+}  // namespace
+
 hipError_t launch_topk(int key_kind, int xs_kind, int64_t rows, const TopkArgs& a,
                        hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
@@ -1040,6 +1095,18 @@ hipError_t launch_topk(int key_kind, int xs_kind, int64_t rows, const TopkArgs& 
         (xs_kind != XS_F32 || (key_kind != KEY_F32 && key_kind != KEY_BF16) || a.d % 8 != 0 ||
          a.d > 16384 || a.frag_groups != (a.d + 31) / 32))
         return hipErrorInvalidValue;
+    // Many rows of bf16 keys whose only output is X (.) M in bf16: the lean
+    // two-level selection (measured against the general kernel on the
+    // 2048 x 4096 prefill rows).
+    if (key_kind == KEY_BF16 && xs_kind == XS_BF16 && rows > 64 && rows <= 0x7FFFFFFF &&
+        a.d % 8 == 0 && a.d <= 16 * kS15NT && a.xs != nullptr && a.mask == nullptr &&
+        a.idx == nullptr && a.count == nullptr && a.tau == nullptr && a.cutoff == nullptr &&
+        a.zero_rows == nullptr && a.zero_rows2 == nullptr && a.xform == XF_NONE &&
+        a.frag == nullptr) {
+        if (a.d <= 8 * kS15NT) select15_xs_kernel<8><<<dim3((unsigned)rows), dim3(kS15NT), 0, stream>>>(a);
+        else select15_xs_kernel<16><<<dim3((unsigned)rows), dim3(kS15NT), 0, stream>>>(a);
+        return hipGetLastError();
+    }
     // Few rows (decode): one big workgroup per row; many rows: smaller ones.
     if (rows <= 64) return launch_nt<1024>(key_kind, xs_kind, rows, a, stream);
     return launch_nt<256>(key_kind, xs_kind, rows, a, stream);

@@ -218,16 +218,21 @@ def test_linear_mfma_random(gpu_lib, rows, d, n):
         assert_within(y, y_ref, t, 4e-3, f"mfma k={k}")
 
 
-def test_linear_mfma_integer_valued_is_exact(gpu_lib):
+@pytest.mark.parametrize("rows,d,n,k", [(300, 512, 400, 300), (100, 4096, 264, 2867),
+                                        (97, 2056, 136, 1)])
+def test_linear_mfma_integer_valued_is_exact(gpu_lib, rows, d, n, k):
+    """Integer-valued x (|x| <= 8: most of the selection is decided by the
+    index rule among equal magnitudes) and w: y is exact, so it is equal to
+    the oracle's only if the selection (run for many rows by the two-level
+    bf16 selection kernel) is the oracle's."""
     import torch
     qs = gpu_lib
-    rng = np.random.default_rng(61)
-    rows, d, n = 300, 512, 400
+    rng = np.random.default_rng(61 + d)
     x = rng.integers(-8, 9, size=(rows, d)).astype(np.float32)
     w = rng.integers(-2, 3, size=(n, d)).astype(np.float32)
-    note("linear MFMA integer-valued")
-    y = _run(gpu_lib, x, 300, w, torch.bfloat16, torch.bfloat16, torch.float32, layout=qs.LAYOUT_W)
-    y_ref, _ = _ref(x, 300, w)
+    note(f"linear MFMA integer-valued rows={rows} d={d} k={k}")
+    y = _run(gpu_lib, x, k, w, torch.bfloat16, torch.bfloat16, torch.float32, layout=qs.LAYOUT_W)
+    y_ref, _ = _ref(x, k, w)
     assert np.array_equal(y, y_ref)
 
 
