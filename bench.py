@@ -9,9 +9,9 @@ up projection over the selected rows of W_up^T with the squared-ReLU
 epilogue, then the top-K of the intermediate and the down projection over
 the rows of W_down^T it selects (at one token two launches, each selecting
 inside its workgroups).  The weight rows are padded by 64 bf16 (--row-pad;
-config.weight_row_pitch): with the natural 1 KiB-multiple pitch the row
-segments of some column tiles share a subset of the memory channels and
-those tiles finish last; the kernels read the same bytes either way.
+config.weight_row_pitch): with the natural pitches (multiples of 512 bytes)
+the row segments of some column tiles share a subset of the memory channels
+and those tiles finish last; the kernels read the same bytes either way.
 
 Other workloads (--workload): c1 (fp32 1024x1024 linear, 8 tokens), c2g (the
 same Llama-7B FFN with a gate: gated squared ReLU), c3

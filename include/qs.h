@@ -197,10 +197,10 @@ qs_status qs_sparse_linear(const void* x, qs_dtype xt, int64_t rows, int64_t d_i
  *           otherwise, before anything is enqueued.  The padding columns are
  *           never read.
  *   Why: every workgroup of the gather reads one 128-byte column segment of
- *   each selected row; with a pitch that is a multiple of 1 KiB those
- *   segments sit at the same address offsets in every row and some tiles'
- *   lines pile onto a subset of the memory channels, so their workgroups
- *   finish last.  Rows padded by 64 bf16 (an odd multiple of 128 bytes)
+ *   each selected row; with a pitch that is a multiple of 512 bytes (the
+ *   natural ones of 7B shapes: 8192 and 22016 bytes) those segments sit at
+ *   one or two offsets modulo 1 KiB in every row and some tiles' lines pile
+ *   onto a subset of the memory channels, so their workgroups finish last.  Rows padded by 64 bf16 (an odd multiple of 128 bytes)
  *   spread every tile over all channels.
  */
 qs_status qs_sparse_linear_pitched(const void* x, qs_dtype xt, int64_t rows, int64_t d_in,
