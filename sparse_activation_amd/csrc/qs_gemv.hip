@@ -501,15 +501,15 @@ __global__ __launch_bounds__(kFsNT) void gather_sel_kernel(GemvArgs a, int cand,
     const uint32_t tileb = (uint32_t)tile * kFsCols * 2;
     uint32_t pf = 0;
     auto prefetch = [&](uint32_t b1) {
-        // one load per thread (its first such row): more loads per wave
-        // would stall the search behind their issue
-        uint32_t off = kOOB;
-#pragma unroll
-        for (int ch = NCH - 1; ch >= 0; --ch) {
-            const int64_t j = j0 + ch * kFsNT + tid;
-            const uint32_t kc = __float_as_uint(c[ch]) & 0x7FFFFFFFu;
-            if (j < j1 && (kc >> 20) > b1) off = (uint32_t)j * rowbytes + tileb;
-        }
+        // one load per thread, for a row of the split's first 1024 entries
+        // only (about a third of the selected rows): HBM delivers that much
+        // before the stream starts; touching more rows (one per thread
+        // wherever it lies) had the stream read lines whose touch was still
+        // in flight a second time.  More loads per wave would stall the
+        // search behind their issue.
+        const int64_t j = j0 + tid;
+        const uint32_t kc = __float_as_uint(c[0]) & 0x7FFFFFFFu;
+        const uint32_t off = j < j1 && (kc >> 20) > b1 ? (uint32_t)j * rowbytes + tileb : kOOB;
         pf = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
     };
     uint32_t tau, cut;
