@@ -146,15 +146,32 @@ def time_steps(args, torch, stream, fn, steps, warmup):
     return ms / steps, replay_stats(per, steps)
 
 
-def committed_traffic(kernel_src: str, name: str):
-    """Traffic per launch from profiles/<name>, if its source hash matches."""
+# The sources a one-token FFN kernel is compiled from: the kernel file and the
+# headers it includes, in this order.
+GEMV_SOURCES = ("qs_gemv.hip", "qs_rowsel.h", "qs_select.h", "qs_internal.h")
+
+
+def sources_sha256(srcs=GEMV_SOURCES):
+    """sha256 over the bytes of `srcs` (under csrc/), concatenated in order;
+    None if one is missing."""
+    h = hashlib.sha256()
+    for f in srcs:
+        path = os.path.join(ROOT, "sparse_activation_amd", "csrc", f)
+        if not os.path.exists(path):
+            return None
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
+def committed_traffic(name: str, srcs=GEMV_SOURCES):
+    """Traffic per launch from profiles/<name>, if the hash of the sources it
+    was counted on matches the current sources (else the kernel changed since)."""
     path = os.path.join(ROOT, "profiles", name)
-    src = os.path.join(ROOT, "sparse_activation_amd", "csrc", kernel_src)
-    if not (os.path.exists(path) and os.path.exists(src)):
+    sha = sources_sha256(srcs)
+    if sha is None or not os.path.exists(path):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     text = open(path).read()
-    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_sha = re.search(r"sources_sha256:\s*([0-9a-f]{64})", text)
     m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
     if not (m_sha and m_val) or m_sha.group(1) != sha:
         return None
@@ -309,9 +326,9 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     dom, us_launch, achieved, bytes_launch = max(cands, key=lambda c: c[1])
     traffic = None
     if dom.startswith("up_cols"):
-        traffic = committed_traffic("qs_gemv.hip", "up_cols_llama7b_relu2_b1_traffic.md")
+        traffic = committed_traffic("up_cols_llama7b_relu2_b1_traffic.md")
     elif dom.startswith("gather_sel"):
-        traffic = committed_traffic("qs_gemv.hip", "gather_sel_llama7b_relu2_b1_traffic.md")
+        traffic = committed_traffic("gather_sel_llama7b_relu2_b1_traffic.md")
     dom = dom.split(" ")[0]
 
     # ceiling reference: a plain streaming read of the same bytes per launch,
