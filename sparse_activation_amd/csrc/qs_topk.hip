@@ -1025,24 +1025,23 @@ hipError_t launch_desc31(const float* x, int64_t rows, int64_t d, int64_t k, uin
 
 namespace {
 
-// Many rows of bf16 x whose only output is X (.) M in bf16 (the operand of the
-// dense MFMA paths): one workgroup of 256 threads per row, E entries per
-// thread.  The top-k of the 15-bit magnitude keys comes from two LDS
+// Rows of bf16 x whose only output is X (.) M: in bf16 for many rows (the
+// operand of the dense MFMA paths), in fp32 for a few (the decode FFN's
+// gathers); one workgroup of NT threads per row, E entries per thread.  The top-k of the 15-bit magnitude keys comes from two LDS
 // histogram levels (8 high bits, then the 7 low bits of the boundary bin;
 // ties to the lower index, Q-Sparse news article, section "Sparsification
 // with the Top-K function"), without the candidate lists and digit loops of
-// the general kernel; then each thread writes its run of X (.) M.
+// the general kernel; then each thread writes its run of X (.) M (bf16, or
+// fp32 with F32), after the launch's side jobs (clear_side_buffers).
 constexpr int kS15NT = 256;
 
-template <int E>
-__global__ __launch_bounds__(kS15NT) void select15_xs_kernel(TopkArgs a) {
-    __shared__ rowsel::Sel15Lds<1, kS15NT / 64> L;
+template <int NT, int E, bool F32>
+__global__ __launch_bounds__(NT) void select15_xs_kernel(TopkArgs a) {
+    __shared__ rowsel::Sel15Lds<1, NT / 64> L;
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
     const int d = (int)a.d;
     const int nvalid = d - tid * E;
-    if (a.zero_ptr != nullptr && row == 0)
-        for (int i = tid; i < a.n_zero; i += kS15NT) a.zero_ptr[i] = 0;
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(reinterpret_cast<const void*>(reinterpret_cast<const uint16_t*>(a.x) + row * d)),
         (short)0, d * 2, 0x00020000);
@@ -1052,15 +1051,15 @@ __global__ __launch_bounds__(kS15NT) void select15_xs_kernel(TopkArgs a) {
         const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)((tid * E + 8 * q) * 2), 0, 0);
         xr16[4 * q] = v.x; xr16[4 * q + 1] = v.y; xr16[4 * q + 2] = v.z; xr16[4 * q + 3] = v.w;
     }
-    for (int i = tid; i < (int)(sizeof(L) / 4); i += kS15NT) reinterpret_cast<uint32_t*>(&L)[i] = 0;
+    clear_side_buffers<NT>(a, (int)row, tid);
+    for (int i = tid; i < (int)(sizeof(L) / 4); i += NT) reinterpret_cast<uint32_t*>(&L)[i] = 0;
     uint32_t key[1][E];
 #pragma unroll
     for (int e = 0; e < E; ++e)
         key[0][e] = e < nvalid ? (xr16[e / 2] >> (16 * (e % 2))) & 0x7FFFu : sel::kInvalid;
     __syncthreads();
     uint32_t selm[1];
-    rowsel::select15_masks<kS15NT, 1, E>(key, 1, a.k, L, tid, selm);
-    uint16_t* xs = reinterpret_cast<uint16_t*>(a.xs) + row * d;
+    rowsel::select15_masks<NT, 1, E>(key, 1, a.k, L, tid, selm);
 #pragma unroll
     for (int q = 0; q < E / 8; ++q) {
         if (tid * E + 8 * q >= d) break;   // (d % 8 == 0: whole runs)
@@ -1072,7 +1071,17 @@ __global__ __launch_bounds__(kS15NT) void select15_xs_kernel(TopkArgs a) {
             const uint32_t hi = (selm[0] >> (e + 1)) & 1u ? 0xFFFF0000u : 0u;
             w[i] = xr16[4 * q + i] & (lo | hi);
         }
-        *reinterpret_cast<uint4*>(xs + tid * E + 8 * q) = make_uint4(w[0], w[1], w[2], w[3]);
+        if constexpr (F32) {
+            // bf16 -> fp32 is exact: the bits move to the high half.
+            float* xs = reinterpret_cast<float*>(a.xs) + row * d + tid * E + 8 * q;
+            *reinterpret_cast<uint4*>(xs) = make_uint4(w[0] << 16, w[0] & 0xFFFF0000u,
+                                                       w[1] << 16, w[1] & 0xFFFF0000u);
+            *reinterpret_cast<uint4*>(xs + 4) = make_uint4(w[2] << 16, w[2] & 0xFFFF0000u,
+                                                           w[3] << 16, w[3] & 0xFFFF0000u);
+        } else {
+            uint16_t* xs = reinterpret_cast<uint16_t*>(a.xs) + row * d;
+            *reinterpret_cast<uint4*>(xs + tid * E + 8 * q) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
     }
 }
 
@@ -1095,16 +1104,26 @@ hipError_t launch_topk(int key_kind, int xs_kind, int64_t rows, const TopkArgs& 
         (xs_kind != XS_F32 || (key_kind != KEY_F32 && key_kind != KEY_BF16) || a.d % 8 != 0 ||
          a.d > 16384 || a.frag_groups != (a.d + 31) / 32))
         return hipErrorInvalidValue;
-    // Many rows of bf16 keys whose only output is X (.) M in bf16: the lean
-    // two-level selection (measured against the general kernel on the
-    // 2048 x 4096 prefill rows).
-    if (key_kind == KEY_BF16 && xs_kind == XS_BF16 && rows > 64 && rows <= 0x7FFFFFFF &&
-        a.d % 8 == 0 && a.d <= 16 * kS15NT && a.xs != nullptr && a.mask == nullptr &&
-        a.idx == nullptr && a.count == nullptr && a.tau == nullptr && a.cutoff == nullptr &&
-        a.zero_rows == nullptr && a.zero_rows2 == nullptr && a.xform == XF_NONE &&
-        a.frag == nullptr) {
-        if (a.d <= 8 * kS15NT) select15_xs_kernel<8><<<dim3((unsigned)rows), dim3(kS15NT), 0, stream>>>(a);
-        else select15_xs_kernel<16><<<dim3((unsigned)rows), dim3(kS15NT), 0, stream>>>(a);
+    // Rows of bf16 keys whose only output is X (.) M (besides the side jobs):
+    // the lean two-level selection.  Many rows written in bf16 (measured
+    // against the general kernel on the 2048 x 4096 prefill rows): 256
+    // threads per row; few rows written in fp32 (the 2-16 token decode FFN):
+    // 512 threads per row, for latency.
+    const bool lean = key_kind == KEY_BF16 && rows <= 0x7FFFFFFF && a.d % 8 == 0 &&
+                      a.xs != nullptr && a.mask == nullptr && a.idx == nullptr &&
+                      a.count == nullptr && a.tau == nullptr && a.cutoff == nullptr &&
+                      a.xform == XF_NONE && a.frag == nullptr;
+    if (lean && xs_kind == XS_BF16 && rows > 64 && a.d <= 16 * kS15NT &&
+        a.zero_rows == nullptr && a.zero_rows2 == nullptr) {
+        const dim3 g((unsigned)rows), b(kS15NT);
+        if (a.d <= 8 * kS15NT) select15_xs_kernel<kS15NT, 8, false><<<g, b, 0, stream>>>(a);
+        else select15_xs_kernel<kS15NT, 16, false><<<g, b, 0, stream>>>(a);
+        return hipGetLastError();
+    }
+    if (lean && xs_kind == XS_F32 && rows <= 64 && a.d <= 16 * 512) {
+        const dim3 g((unsigned)rows), b(512);
+        if (a.d <= 8 * 512) select15_xs_kernel<512, 8, true><<<g, b, 0, stream>>>(a);
+        else select15_xs_kernel<512, 16, true><<<g, b, 0, stream>>>(a);
         return hipGetLastError();
     }
     // Few rows (decode): one big workgroup per row; many rows: smaller ones.

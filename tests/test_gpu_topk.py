@@ -104,3 +104,24 @@ def test_topk_boundary_bin_sizes(gpu_lib, nbin):
     for k in sorted({big + 1, big + nbin // 3, big + nbin // 2, big + nbin - 1, big + nbin}):
         note(f"topk boundary bin nbin={nbin} k={k}")
         _check("f32", x, k, _run(gpu_lib, "f32", x, k))
+
+
+@pytest.mark.parametrize("rows,d", [(1, 8), (2, 4096), (3, 1000), (4, 4104), (2, 8192), (64, 512),
+                                    (2, 8200), (5, 1004), (65, 520)])
+@pytest.mark.parametrize("ties", [False, True])
+def test_topk_xs_only_bf16(gpu_lib, rows, d, ties):
+    """bf16 rows whose only output is X (.) M in fp32 (the decode FFN's
+    selection launch): a selected entry is the bf16 value widened exactly, an
+    unselected one +0.0, bit for bit; d % 8 == 0 with d <= 8192 and at most
+    64 rows take the lean two-level kernel, the other shapes the general one."""
+    import torch
+    x = _inputs("bf16", rows, d, seed=5000 + rows * 7 + d + ties, ties=ties)
+    xd = to_dev(x, torch.bfloat16)
+    for k in sorted({0, 1, d // 3, d // 2, d - 1, d}):
+        note(f"topk xs-only bf16 rows={rows} d={d} k={k} ties={ties}")
+        got = gpu_lib.qs_topk_mask(xd, k, want_mask=False, want_idx=False, want_desc=False,
+                                   want_xs=True)[4]
+        torch.cuda.synchronize()
+        m_ref = oracle.topk_select(oracle.magnitude(x.astype(np.float64)), k)[0].astype(bool)
+        ref = np.where(m_ref, x.astype(np.float32), np.float32(0.0)).astype(np.float32)
+        assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32))
