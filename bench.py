@@ -163,14 +163,18 @@ def sources_sha256(srcs=GEMV_SOURCES):
     return h.hexdigest()
 
 
-def committed_traffic(name: str, srcs=GEMV_SOURCES):
-    """Traffic per launch from profiles/<name>, if the hash of the sources it
-    was counted on matches the current sources (else the kernel changed since)."""
+def committed_traffic(name: str, row_pad: int, srcs=GEMV_SOURCES):
+    """Traffic per launch from profiles/<name>, if it was counted on weight
+    rows padded by `row_pad` elements and the hash of the sources it was
+    counted on matches the current sources (else the kernel changed since)."""
     path = os.path.join(ROOT, "profiles", name)
     sha = sources_sha256(srcs)
     if sha is None or not os.path.exists(path):
         return None
     text = open(path).read()
+    m_pad = re.search(r"weight_row_pad:\s*([0-9]+)", text)
+    if not m_pad or int(m_pad.group(1)) != row_pad:
+        return None
     m_sha = re.search(r"sources_sha256:\s*([0-9a-f]{64})", text)
     m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
     if not (m_sha and m_val) or m_sha.group(1) != sha:
@@ -326,9 +330,11 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
     dom, us_launch, achieved, bytes_launch = max(cands, key=lambda c: c[1])
     traffic = None
     if dom.startswith("up_cols"):
-        traffic = committed_traffic("up_cols_llama7b_relu2_b1_traffic.md")
+        traffic = committed_traffic("up_cols_llama7b_relu2_b1_traffic.md", pad)
     elif dom.startswith("gather_sel"):
-        traffic = committed_traffic("gather_sel_llama7b_relu2_b1_traffic.md")
+        traffic = committed_traffic("gather_sel_llama7b_relu2_b1_traffic.md", pad)
+    elif dom.startswith("gather_gemv") and not args.deterministic:
+        traffic = committed_traffic(f"gather_gemv_llama7b_relu2_b{B}_traffic.md", pad)
     dom = dom.split(" ")[0]
 
     # ceiling reference: a plain streaming read of the same bytes per launch,

@@ -30,7 +30,8 @@ def test_committed_traffic_follows_the_kernel_sources(tmp_path):
     bench = _load_bench()
     names = ("up_cols_llama7b_relu2_b1_traffic.md", "gather_sel_llama7b_relu2_b1_traffic.md")
     for n in names:
-        assert bench.committed_traffic(n) is not None, n   # the committed profiles match
+        assert bench.committed_traffic(n, 64) is not None, n   # the committed profiles match
+        assert bench.committed_traffic(n, 0) is None, n        # counted on padded rows only
     (tmp_path / "profiles").mkdir()
     csrc = tmp_path / "sparse_activation_amd" / "csrc"
     csrc.mkdir(parents=True)
@@ -39,10 +40,10 @@ def test_committed_traffic_follows_the_kernel_sources(tmp_path):
     for f in bench.GEMV_SOURCES:
         shutil.copy(os.path.join(ROOT, "sparse_activation_amd", "csrc", f), csrc / f)
     bench.ROOT = str(tmp_path)
-    assert bench.committed_traffic(names[0]) is not None
+    assert bench.committed_traffic(names[0], 64) is not None
     for f in bench.GEMV_SOURCES:   # an edit of any one of them voids the stored figure
         orig = (csrc / f).read_bytes()
         (csrc / f).write_bytes(orig + b"\n")
-        assert bench.committed_traffic(names[0]) is None, f
+        assert bench.committed_traffic(names[0], 64) is None, f
         (csrc / f).write_bytes(orig)
-    assert bench.committed_traffic(names[0]) is not None
+    assert bench.committed_traffic(names[0], 64) is not None
