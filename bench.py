@@ -315,7 +315,8 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
 
         def down_launch(i):
             gather(u2[i % N_XROT], wdns[i % n_copies], y=ydn, ws=ws_dn)
-        dn_name = "gather_gemv_kernel (down)"
+        # bf16 W_down^T: token tiles of 5-16 rows run the bf16 MFMA gather.
+        dn_name = "gather_bmfma_kernel (down)" if B > 4 else "gather_gemv_kernel (down)"
     cands = [(dn_name,) + timed(dn_name, down_launch, dn_bytes) + (dn_bytes,)]
     if B == 1:
         yup = torch.empty((B, ffn), dtype=torch.float32, device=dev)
