@@ -336,6 +336,8 @@ def run_c2(args, torch, np, qs, datagen, dev, stream):
         traffic = committed_traffic("gather_sel_llama7b_relu2_b1_traffic.md", pad)
     elif dom.startswith("gather_gemv") and not args.deterministic:
         traffic = committed_traffic(f"gather_gemv_llama7b_relu2_b{B}_traffic.md", pad)
+    elif dom.startswith("gather_bmfma") and not args.deterministic:
+        traffic = committed_traffic(f"gather_bmfma_down_llama7b_relu2_b{B}_traffic.md", pad)
     dom = dom.split(" ")[0]
 
     # ceiling reference: a plain streaming read of the same bytes per launch,
