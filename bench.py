@@ -149,6 +149,8 @@ def time_steps(args, torch, stream, fn, steps, warmup):
 # The sources a one-token FFN kernel is compiled from: the kernel file and the
 # headers it includes, in this order.
 GEMV_SOURCES = ("qs_gemv.hip", "qs_rowsel.h", "qs_select.h", "qs_internal.h")
+# The one-token dReLU FFN's: its gate/up kernel's file, then the down gather's.
+DRELU_SOURCES = ("qs_mfma.hip",) + GEMV_SOURCES
 
 
 def sources_sha256(srcs=GEMV_SOURCES):
@@ -501,7 +503,10 @@ def run_c5(args, torch, np, qs, datagen, dev, stream):
                    "zero_fraction_h": round(zero_frac, 4), "up_rows_read": g_pos,
                    "down_rows_read": nz},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": committed_traffic("mistral7b_drelu_ffn_b1_step_traffic.md", pad,
+                                                  DRELU_SOURCES)
+                     if B == 1 and not args.deterministic else None,
                      "kernel": "whole FFN step (gate/up + down)",
                      "algorithmic_bytes_per_step": round(float(step_bytes))},
         "timing": timing, "cpu_baseline": None,
@@ -748,7 +753,9 @@ def run_c2g(args, torch, np, qs, datagen, dev, stream):
                    "k_in": k_in, "k_mid": k_mid, "weight_row_pad": pad, "weight_copies": n_copies,
                    "x_rotations": N_XROT, "union_rows_in": u1, "union_rows_mid": u2},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": committed_traffic("llama7b_relu2glu_ffn_b1_step_traffic.md", pad)
+                     if B == 1 and not args.deterministic else None,
                      "kernel": "whole FFN step (gate, up, top-K of h, down)",
                      "algorithmic_bytes_per_step": round(float(step_bytes))},
         "timing": timing, "cpu_baseline": None,
